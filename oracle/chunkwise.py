@@ -1,0 +1,124 @@
+"""Chunkwise-parallel GSA / GLA in float64 numpy -- a second, independent
+implementation used only to pin the recurrent oracle.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Source: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling".
+* App. A.1 (chunkwise form, Eq. 14-16): the sequence is cut into N = ceil(T/C)
+  chunks; within a chunk the output is an inter-chunk term read from the state
+  at the chunk start plus an intra-chunk causal term, and the state is carried
+  to the next chunk.  Element-wise gating keeps this rearrangement exact.
+* App. B: GSA is two such GLA passes.  The first pass takes the queries and
+  keys with the slot write intensities I = 1 - A as its values; a softmax over
+  the slots of its output gives the queries of the second pass, whose keys are
+  I and values are V.  The per-slot decay sits on the value (slot) dimension in
+  the first pass and on the key (slot) dimension in the second, as in the
+  paper's listing.  The preprocessing step is the chunk-local cumulative sum
+  of log alpha.
+
+Every decay factor exp(G_j - G_r) is formed as the exponential of an explicit
+sum of log alpha over tokens r+1..j (never as a difference of two cumulative
+sums), so alpha = 0 (log alpha = -inf) is handled exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def log_sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+
+
+def _pair_logdecay(la):
+    """D[j, r, :] = sum of la[i] for r < i <= j (0 when r == j); -inf for r > j."""
+    L, d = la.shape
+    D = np.full((L, L, d), -np.inf)
+    for r in range(L):
+        D[r, r] = 0.0
+        if r + 1 < L:
+            D[r + 1:, r] = np.cumsum(la[r + 1:], axis=0)
+    return D
+
+
+def gla_key_decay(q, k, v, la, S0=None, C=64):
+    """One unit of GLA with decay on the key (row) dimension of S [dk, dv].
+    q, k, la: [T, dk]; v: [T, dv].  Returns (o [T, dv], S_final)."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for n0 in range(0, T, C):
+        sl = slice(n0, min(n0 + C, T))
+        qc, kc, vc, lc = q[sl], k[sl], v[sl], la[sl]
+        D = _pair_logdecay(lc)
+        Gf = np.cumsum(lc, axis=0)            # decay from the chunk start to j
+        inter = (qc * np.exp(Gf)) @ S
+        A = np.einsum("jc,rc,jrc->jr", qc, kc, np.exp(D))
+        o[sl] = inter + A @ vc
+        S = np.exp(Gf[-1])[:, None] * S + (kc * np.exp(D[-1])).T @ vc
+    return o, S
+
+
+def gla_value_decay(q, k, w, la, P0=None, C=64):
+    """One unit of GLA with decay on the value (column) dimension of P [dk, m].
+    q, k: [T, dk]; w, la: [T, m].  Returns (o [T, m], P_final)."""
+    T, dk = q.shape
+    m = w.shape[1]
+    P = np.zeros((dk, m)) if P0 is None else np.array(P0, dtype=np.float64)
+    o = np.zeros((T, m))
+    for n0 in range(0, T, C):
+        sl = slice(n0, min(n0 + C, T))
+        qc, kc, wc, lc = q[sl], k[sl], w[sl], la[sl]
+        D = _pair_logdecay(lc)
+        Gf = np.cumsum(lc, axis=0)
+        inter = np.exp(Gf) * (qc @ P)
+        A = qc @ kc.T
+        intra = np.einsum("jr,rc,jrc->jc", A, wc, np.exp(D))
+        o[sl] = inter + intra
+        P = P * np.exp(Gf[-1])[None, :] + kc.T @ (wc * np.exp(D[-1]))
+    return o, P
+
+
+def softmax_slots(x):
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0, C=64):
+    """One (b,h) unit of GSA as two chunked GLA passes.  Returns
+    (o, Kt_final [m,dk], Vt_final [m,dv], s [T,m])."""
+    la = log_sigmoid(g) / tau
+    w = -np.expm1(la)
+    P0 = None if k0 is None else np.asarray(k0, dtype=np.float64).T
+    ok, P = gla_value_decay(q, k, w, la, P0, C)
+    s = softmax_slots(ok)
+    o, Vf = gla_key_decay(s, w, v, la, v0, C)
+    return o, P.T, Vf, s
+
+
+def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, C=64):
+    B, H, T, dk = q.shape
+    m = g.shape[-1]
+    o = np.zeros(v.shape)
+    kf = np.zeros((B, H, m, dk))
+    vf = np.zeros((B, H, m, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], kf[b, h], vf[b, h], _ = gsa_unit(
+                q[b, h], k[b, h], v[b, h], g[b, h],
+                None if k0 is None else k0[b, h], None if v0 is None else v0[b, h], tau, C)
+    return o, kf, vf
+
+
+def gla_fwd(q, k, v, g, s0=None, tau=16.0, C=64):
+    B, H, T, dk = q.shape
+    o = np.zeros(v.shape)
+    sf = np.zeros((B, H, dk, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            la = log_sigmoid(g[b, h]) / tau
+            o[b, h], sf[b, h] = gla_key_decay(q[b, h], k[b, h], v[b, h], la,
+                                              None if s0 is None else s0[b, h], C)
+    return o, sf

@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the HIP-side
+tests/bench.
+
+This module holds random draws, scaling and dtype casts only -- none of the
+method's arithmetic -- so that the oracle and the HIP path can consume the very
+same stored arrays while sharing no code.
+
+Recipe (every workload): ``numpy.random.default_rng(seed)`` (PCG64), draws in
+float64 in the order q, k, v, g, then the initial key/value states (when the
+workload has them); each draw is then scaled/shifted and cast to its storage
+dtype.  bf16 storage rounds float64 -> float32 -> bfloat16, both steps
+round-to-nearest-even.  The float64 view the oracle consumes is the exact
+upcast of the stored values.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Stored", "bf16_bits", "bf16_to_f64", "stored", "gsa_inputs", "gla_inputs",
+    "decode_inputs", "WORKLOADS",
+]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (nearest-even, via float32) and return the raw uint16 bits."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(f)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@dataclasses.dataclass
+class Stored:
+    """A tensor as stored for the device: ``raw`` is float32 or uint16 (bf16 bits);
+    ``f64`` is its exact float64 upcast for the oracle."""
+    raw: np.ndarray
+    dtype: str  # "f32" | "bf16"
+
+    @property
+    def f64(self) -> np.ndarray:
+        if self.dtype == "bf16":
+            return bf16_to_f64(self.raw)
+        return self.raw.astype(np.float64)
+
+    @property
+    def shape(self):
+        return self.raw.shape
+
+
+def stored(x: np.ndarray, dtype: str) -> Stored:
+    if dtype == "bf16":
+        return Stored(bf16_bits(x), "bf16")
+    if dtype == "f32":
+        return Stored(np.ascontiguousarray(x, dtype=np.float32), "f32")
+    raise ValueError(dtype)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float64)
+
+
+def gsa_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
+               g_shift=0.0, init_std=None):
+    """q,k,v ~ N(0,1)*qkv_scale [B,H,T,d]; g ~ N(0,1)+g_shift [B,H,T,m];
+    optional K0 [B,H,m,dk], V0 [B,H,m,dv] ~ N(0, init_std) stored as float32."""
+    rng = np.random.default_rng(seed)
+    if qkv_scale is None:
+        qkv_scale = 1.0 / math.sqrt(dk)
+    q = _normal(rng, (B, H, T, dk)) * qkv_scale
+    k = _normal(rng, (B, H, T, dk)) * qkv_scale
+    v = _normal(rng, (B, H, T, dv)) * qkv_scale
+    g = _normal(rng, (B, H, T, m)) + g_shift
+    out = dict(q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
+               g=stored(g, dtype), k0=None, v0=None)
+    if init_std is not None:
+        out["k0"] = stored(_normal(rng, (B, H, m, dk)) * init_std, "f32")
+        out["v0"] = stored(_normal(rng, (B, H, m, dv)) * init_std, "f32")
+    return out
+
+
+def gla_inputs(B, H, T, dk, dv, dtype="bf16", seed=0, qkv_scale=None,
+               g_shift=0.0, init_std=None):
+    """q,k ~ N(0,1)*qkv_scale [B,H,T,dk]; v [B,H,T,dv]; g ~ N(0,1)+g_shift
+    [B,H,T,dk] (one logit per key dim); optional S0 [B,H,dk,dv] ~ N(0,init_std)."""
+    rng = np.random.default_rng(seed)
+    if qkv_scale is None:
+        qkv_scale = 1.0 / math.sqrt(dk)
+    q = _normal(rng, (B, H, T, dk)) * qkv_scale
+    k = _normal(rng, (B, H, T, dk)) * qkv_scale
+    v = _normal(rng, (B, H, T, dv)) * qkv_scale
+    g = _normal(rng, (B, H, T, dk)) + g_shift
+    out = dict(q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
+               g=stored(g, dtype), s0=None)
+    if init_std is not None:
+        out["s0"] = stored(_normal(rng, (B, H, dk, dv)) * init_std, "f32")
+    return out
+
+
+def decode_inputs(N, H, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
+                  state_std=0.1):
+    """Key/value slot states [N,H,m,d] ~ N(0,state_std) float32, then one token
+    per sequence: q,k,v ~ N(0,1)*qkv_scale [N,H,d], g ~ N(0,1) [N,H,m]."""
+    rng = np.random.default_rng(seed)
+    if qkv_scale is None:
+        qkv_scale = 1.0 / math.sqrt(dk)
+    q = _normal(rng, (N, H, dk)) * qkv_scale
+    k = _normal(rng, (N, H, dk)) * qkv_scale
+    v = _normal(rng, (N, H, dv)) * qkv_scale
+    g = _normal(rng, (N, H, m))
+    ks = _normal(rng, (N, H, m, dk)) * state_std
+    vs = _normal(rng, (N, H, m, dv)) * state_std
+    return dict(q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
+                g=stored(g, dtype), kstate=stored(ks, "f32"), vstate=stored(vs, "f32"))
+
+
+# The five workloads: sizes, dtypes and value distributions of the method's
+# configurations (GSA: tau = 8 per the paper's Sec. 3.3; the standalone GLA
+# case uses tau = 16).
+WORKLOADS = {
+    "gsa_f32_small": dict(op="gsa", B=1, H=2, T=256, dk=64, dv=64, m=32, C=64, tau=8.0,
+                          dtype="f32", qkv_scale=1 / 8.0, g_shift=0.0, init_std=None),
+    "gsa_bf16_train_T2048": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=64, C=64,
+                                 tau=8.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
+                                 g_shift=0.0, init_std=None),
+    "gla_bf16_T4096": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64, tau=16.0,
+                           dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
+                           init_std=None),
+    "gsa_bf16_long_T16384": dict(op="gsa", B=1, H=8, T=16384, dk=128, dv=128, m=64, C=64,
+                                 tau=8.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
+                                 g_shift=2.0, init_std=0.1),
+    "gsa_decode_N256": dict(op="decode", N=256, H=16, dk=128, dv=128, m=64, tau=8.0,
+                            dtype="bf16", qkv_scale=1 / math.sqrt(128), state_std=0.1),
+}

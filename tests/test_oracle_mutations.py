@@ -1,0 +1,125 @@
+"""The pins must have teeth: plant plausible mistakes in a private copy of the
+C oracle (compiled to a temporary library on the CPU) and check that every
+mutant fails at least one pin that the real oracle passes.  The committed
+oracle source is never modified."""
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import bruteforce, chunkwise
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "gsa_oracle.c")
+
+# (name, original text, planted mistake)
+MUTATIONS = [
+    ("write_not_coupled", "double w = -expm1(la);", "double w = 1.0;"),
+    ("write_is_alpha", "double w = -expm1(la);", "double w = a;"),
+    ("exclusive_read", "Kc[x] = a * Kc[x] + w * kt[x];\n            acc += Kc[x] * qt[x];",
+     "acc += Kc[x] * qt[x];\n            Kc[x] = a * Kc[x] + w * kt[x];"),
+    ("logsig_sign", "return (x < 0.0 ? x : 0.0) - log1p(exp(-fabs(x)));",
+     "return (x < 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));"),
+    ("tau_multiplies", "double la = log_sigmoid(gt[c]) / tau;",
+     "double la = log_sigmoid(gt[c]) * tau;"),
+    ("softmax_unnormalised", "s[c] /= sum;", "s[c] /= 1.0;"),
+    ("output_transposed", "acc += V[c * dv + x] * s[c];", "acc += V[x * dv + c] * s[c];"),
+    ("value_decay_skipped", "Vc[x] = a * Vc[x] + w * vt[x];", "Vc[x] = Vc[x] + w * vt[x];"),
+    ("gla_scalar_gate", "double a = exp(log_sigmoid(gt[x]) / tau);",
+     "double a = exp(log_sigmoid(gt[0]) / tau);"),
+    ("gla_read_before_write", "Sx[y] = a * Sx[y] + kt[x] * vt[y];",
+     "Sx[y] = a * Sx[y] + kt[x] * vt[y] * (t > 0);"),
+]
+
+
+def _build(tmp_path, text, name):
+    c = tmp_path / (name + ".c")
+    c.write_text(text)
+    so = tmp_path / (name + ".so")
+    subprocess.check_call(["gcc", "-O1", "-std=c99", "-fPIC", "-shared", "-o", str(so),
+                           str(c), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    P, L, D, I = ctypes.c_void_p, ctypes.c_long, ctypes.c_double, ctypes.c_int
+    lib.oracle_gsa_fwd.argtypes = [P] * 11 + [L] * 6 + [D, I]
+    lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
+    return lib
+
+
+def _p(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def _gsa(lib, q, k, v, g, k0=None, v0=None, tau=8.0):
+    B, H, T, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    o = np.empty((B, H, T, dv))
+    kf = np.empty((B, H, m, dk))
+    vf = np.empty((B, H, m, dv))
+    rc = lib.oracle_gsa_fwd(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
+                            _p(vf), None, None, B, H, T, dk, dv, m, tau, 1)
+    assert rc == 0
+    return o, kf, vf
+
+
+def _gla(lib, q, k, v, g, s0=None, tau=16.0):
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    o = np.empty((B, H, T, dv))
+    sf = np.empty((B, H, dk, dv))
+    assert lib.oracle_gla_fwd(_p(q), _p(k), _p(v), _p(g), _p(s0), _p(o), _p(sf),
+                              B, H, T, dk, dv, tau, 1) == 0
+    return o, sf
+
+
+def _rel(x, y):
+    d = np.max(np.abs(y))
+    return np.max(np.abs(x - y)) / (d if d > 0 else 1.0)
+
+
+def _pins_pass(lib):
+    """A compact run of the pins; True when all hold."""
+    r = np.random.default_rng(77)
+    T, d, m = 21, 6, 6          # m == dv keeps every planted index in bounds
+    q, k = r.standard_normal((2, 1, 1, T, d)) / 2
+    v = r.standard_normal((1, 1, T, d)) / 2
+    g = r.standard_normal((1, 1, T, m)) * 1.5
+    k0 = r.standard_normal((1, 1, m, d)) * 0.3
+    v0 = r.standard_normal((1, 1, m, d)) * 0.3
+    ok = True
+    o, kf, vf = _gsa(lib, q, k, v, g, k0, v0)
+    oc, kfc, vfc = chunkwise.gsa_fwd(q, k, v, g, k0, v0, tau=8.0, C=8)
+    ok &= _rel(o, oc) < 1e-12 and _rel(kf, kfc) < 1e-12 and _rel(vf, vfc) < 1e-12
+    ob = bruteforce.gsa_unit(q[0, 0, :6], k[0, 0, :6], v[0, 0, :6], g[0, 0, :6],
+                             k0[0, 0], v0[0, 0], tau=8.0)
+    o6, _, _ = _gsa(lib, q[:, :, :6].copy(), k[:, :, :6].copy(), v[:, :, :6].copy(),
+                    g[:, :, :6].copy(), k0, v0)
+    ok &= _rel(o6[0, 0], ob) < 1e-12
+    # alpha = 1 with a given state: o_t = V0^T softmax(K0 q_t)
+    ginf = np.full_like(g, np.inf)
+    o1, _, _ = _gsa(lib, q, k, v, ginf, k0, v0)
+    ok &= _rel(o1[0, 0], scipy.special.softmax(q[0, 0] @ k0[0, 0].T, -1) @ v0[0, 0]) < 1e-13
+    # GLA pins: chunkwise, brute force, alpha = 1 linear attention
+    gg = r.standard_normal((1, 1, T, d))
+    s0 = r.standard_normal((1, 1, d, d))
+    og, sfg = _gla(lib, q, k, v, gg, s0)
+    ogc, sfgc = chunkwise.gla_fwd(q, k, v, gg, s0, tau=16.0, C=8)
+    ok &= _rel(og, ogc) < 1e-12 and _rel(sfg, sfgc) < 1e-12
+    ola, _ = _gla(lib, q, k, v, np.full_like(gg, np.inf))
+    ok &= _rel(ola[0, 0], np.tril(q[0, 0] @ k[0, 0].T) @ v[0, 0]) < 1e-12
+    return bool(ok)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    assert _pins_pass(_build(tmp_path, open(SRC).read(), "orig"))
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, orig, mut):
+    text = open(SRC).read()
+    assert orig in text, "mutation anchor missing: " + name
+    lib = _build(tmp_path, text.replace(orig, mut, 1), name)
+    assert not _pins_pass(lib), "planted mistake not caught: " + name
