@@ -1,0 +1,128 @@
+/*
+ * libgsa -- Gated Slot Attention (GSA) and gated linear attention (GLA) on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * Method: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling"
+ * (arXiv 2409.07146).  For every independent (batch, head) unit and token t:
+ *   alpha_t = sigmoid(g_t)^(1/tau)                      (Sec. 3.3, footnote 2)
+ *   Kt_t = Diag(alpha_t) Kt_{t-1} + (1 - alpha_t) k_t^T  (Sec. 3.2, per slot)
+ *   s_t  = softmax over the m slots of (Kt_t q_t)         (Sec. 3.2, App. B)
+ *   Vt_t = Diag(alpha_t) Vt_{t-1} + (1 - alpha_t) v_t^T
+ *   o_t  = Vt_t^T s_t
+ * GLA (Sec. 2.3 with beta = 1): S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T,
+ * o_t = S_t^T q_t, with one gate per key dimension.  The state is updated with
+ * token t before it is read.  No normaliser, no softmax temperature.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are device pointers (HIP) unless stated.  All tensors are dense,
+ *    row-major, with the layouts given per argument; base pointers must be
+ *    16-byte aligned.
+ *  - dtype selects the storage type of q, k, v, g and o (GSA_DTYPE_F32 or
+ *    GSA_DTYPE_BF16).  Recurrent states are always float32 and all
+ *    accumulation is float32.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device memory, keeps no mutable global state and takes scratch space only
+ *    from the workspace argument (query its size first; NULL is allowed when
+ *    the query returns 0).
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous: they enqueue kernels and return.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is written and the status is returned.  A failed launch
+ *    returns GSA_ERR_HIP.
+ */
+#ifndef LIBGSA_GSA_H
+#define LIBGSA_GSA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSA_ABI_VERSION 1
+
+typedef enum {
+  GSA_OK = 0,
+  GSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  GSA_ERR_SHAPE = 2,       /* negative or zero size, bad tau */
+  GSA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+  GSA_ERR_UNSUPPORTED = 4, /* (dtype, dk, dv, m, C) not compiled */
+  GSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+  GSA_ERR_HIP = 6,         /* a kernel launch failed */
+  GSA_ERR_ALIAS = 7        /* an output overlaps an input or another output */
+} gsa_status;
+
+typedef enum { GSA_DTYPE_F32 = 0, GSA_DTYPE_BF16 = 1 } gsa_dtype;
+
+/* ABI version (GSA_ABI_VERSION of the built library). */
+int gsa_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* gsa_status_string(int status);
+
+/* 1 if the shape/dtype combination is compiled for the GPU, else 0.  The chunk
+ * length C of the chunkwise form (App. A.1) is fixed at 64 tokens in this
+ * build; the result of the method does not depend on C. */
+int gsa_fwd_supported(int dk, int dv, int m, int C, int dtype);
+int gla_fwd_supported(int dk, int dv, int C, int dtype);
+int gsa_decode_supported(int dk, int dv, int m, int dtype);
+
+/* Bytes of device workspace gsa_fwd / gla_fwd need for this problem (the
+ * segment state maps of the chunk-state scan).  chunks_per_segment = 0 picks
+ * the library's default split; (size_t)-1 on invalid arguments. */
+size_t gsa_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int C, int dtype,
+                               int chunks_per_segment);
+size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int dtype,
+                               int chunks_per_segment);
+
+/*
+ * GSA forward, chunkwise-parallel (Sec. 3.2 two-pass form; App. A.1 and B).
+ *   q, k     [B,H,T,dk]  dtype
+ *   v        [B,H,T,dv]  dtype
+ *   g        [B,H,T,m]   dtype   forget-gate logits; alpha = sigmoid(g)^(1/tau)
+ *   k0       [B,H,m,dk]  float32 initial key-slot state, NULL = zeros
+ *   v0       [B,H,m,dv]  float32 initial value-slot state, NULL = zeros
+ *   o        [B,H,T,dv]  dtype   output, must not overlap any input
+ *   k_final  [B,H,m,dk]  float32 final key-slot state, NULL = not wanted
+ *   v_final  [B,H,m,dv]  float32 final value-slot state, NULL = not wanted
+ *   tau      > 0 (8 in the paper)
+ *   chunks_per_segment: how many 64-token chunks one workgroup carries the
+ *            state across (0 = default); the workspace must be sized for it.
+ * k_final may equal k0 and v_final may equal v0 (in-place state advance).
+ */
+int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* k0,
+            const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T, int dk,
+            int dv, int m, int C, float tau, int dtype, void* workspace, size_t workspace_bytes,
+            int chunks_per_segment, void* stream);
+
+/*
+ * GLA forward, chunkwise-parallel (Sec. 2.3, App. A.1).
+ *   q, k, g  [B,H,T,dk]  dtype   g: one gate logit per key dimension
+ *   v        [B,H,T,dv]  dtype
+ *   s0       [B,H,dk,dv] float32 initial state, NULL = zeros
+ *   o        [B,H,T,dv]  dtype
+ *   s_final  [B,H,dk,dv] float32, NULL = not wanted (may equal s0)
+ */
+int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
+            float* s_final, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
+            void* workspace, size_t workspace_bytes, int chunks_per_segment, void* stream);
+
+/*
+ * One recurrent GSA step (Sec. 3.2 recurrent form) for N sequences x H heads.
+ *   q, k     [N,H,dk]    dtype
+ *   v        [N,H,dv]    dtype
+ *   g        [N,H,m]     dtype
+ *   k_state  [N,H,m,dk]  float32, advanced in place
+ *   v_state  [N,H,m,dv]  float32, advanced in place
+ *   o        [N,H,dv]    dtype
+ * The states must not overlap each other, the token inputs or o.
+ */
+int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* k_state,
+                    float* v_state, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGSA_GSA_H */

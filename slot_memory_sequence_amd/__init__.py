@@ -1,0 +1,191 @@
+"""libgsa: Gated Slot Attention / gated linear attention on MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in ``include/gsa.h``.  It only
+marshals arguments (device pointers, sizes, the current HIP stream) and
+allocates outputs/workspace through PyTorch; every step of the computation
+runs in the library's HIP kernels.  There is no CPU fallback: if the built
+library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["lib", "gsa_fwd", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH",
+           "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
+           "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgsa.so is not built (run __graft_entry__.build() or "
+                      "python slot_memory_sequence_amd/build.py): " + LIB_PATH)
+
+_P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+lib = ctypes.CDLL(LIB_PATH)
+lib.gsa_abi_version.restype = _I
+lib.gsa_status_string.restype = ctypes.c_char_p
+lib.gsa_status_string.argtypes = [_I]
+lib.gsa_fwd_supported.argtypes = [_I] * 5
+lib.gla_fwd_supported.argtypes = [_I] * 4
+lib.gsa_decode_supported.argtypes = [_I] * 4
+lib.gsa_fwd_workspace_bytes.restype = _S
+lib.gsa_fwd_workspace_bytes.argtypes = [_I] * 9
+lib.gla_fwd_workspace_bytes.restype = _S
+lib.gla_fwd_workspace_bytes.argtypes = [_I] * 8
+lib.gsa_fwd.restype = _I
+lib.gsa_fwd.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _P]
+lib.gla_fwd.restype = _I
+lib.gla_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _P]
+lib.gsa_decode_step.restype = _I
+lib.gsa_decode_step.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P]
+
+
+class GsaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s: status %d (%s)" % (fn, status, status_string(status)))
+
+
+def status_string(s: int) -> str:
+    return lib.gsa_status_string(int(s)).decode()
+
+
+def gsa_fwd_supported(dk, dv, m, C=64, dtype=DTYPE_BF16) -> bool:
+    return bool(lib.gsa_fwd_supported(dk, dv, m, C, dtype))
+
+
+def gla_fwd_supported(dk, dv, C=64, dtype=DTYPE_BF16) -> bool:
+    return bool(lib.gla_fwd_supported(dk, dv, C, dtype))
+
+
+def gsa_decode_supported(dk, dv, m, dtype=DTYPE_BF16) -> bool:
+    return bool(lib.gsa_decode_supported(dk, dv, m, dtype))
+
+
+def gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C=64, dtype=DTYPE_BF16, chunks_per_segment=0):
+    return int(lib.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C, dtype, chunks_per_segment))
+
+
+def gla_fwd_workspace_bytes(B, H, T, dk, dv, C=64, dtype=DTYPE_BF16, chunks_per_segment=0):
+    return int(lib.gla_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype, chunks_per_segment))
+
+
+# ------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError("q/k/v/g must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, dtype=None):
+    torch = _torch()
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
+            chunks_per_segment=0, out=None, k_final=None, v_final=None, workspace=None,
+            stream=None):
+    """Chunkwise GSA forward.  q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m] (gate
+    logits); optional float32 initial slot states k0 [B,H,m,dk], v0 [B,H,m,dv].
+    Returns (o, k_final, v_final) -- the finals are None unless final_state."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(k0, "k0", torch.float32)
+    _check(v0, "v0", torch.float32)
+    B, H, T, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state:
+        if k_final is None:
+            k_final = torch.empty((B, H, m, dk), dtype=torch.float32, device=q.device)
+        if v_final is None:
+            v_final = torch.empty((B, H, m, dv), dtype=torch.float32, device=q.device)
+    nbytes = gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C, dt, chunks_per_segment)
+    if nbytes == (1 << 64) - 1:
+        raise ValueError("invalid problem size")
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
+                     _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
+                     _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                     int(chunks_per_segment), _stream(stream))
+    if st:
+        raise GsaError("gsa_fwd", st)
+    return out, k_final, v_final
+
+
+def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
+            chunks_per_segment=0, out=None, s_final=None, workspace=None, stream=None):
+    """Chunkwise GLA forward.  q, k, g [B,H,T,dk]; v [B,H,T,dv]; optional float32
+    initial state s0 [B,H,dk,dv].  Returns (o, s_final or None)."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(s0, "s0", torch.float32)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dt(q)
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    if final_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    nbytes = gla_fwd_workspace_bytes(B, H, T, dk, dv, C, dt, chunks_per_segment)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out), _ptr(s_final),
+                     B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
+                     0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                     _stream(stream))
+    if st:
+        raise GsaError("gla_fwd", st)
+    return out, s_final
+
+
+def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=None):
+    """One recurrent GSA step.  q, k [N,H,dk]; v [N,H,dv]; g [N,H,m]; float32
+    k_state [N,H,m,dk] and v_state [N,H,m,dv] are advanced in place.  Returns o."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(k_state, "k_state", torch.float32)
+    _check(v_state, "v_state", torch.float32)
+    N, H, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib.gsa_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state), _ptr(v_state),
+                             _ptr(out), N, H, dk, dv, m, float(tau), _dt(q), _stream(stream))
+    if st:
+        raise GsaError("gsa_decode_step", st)
+    return out

@@ -1,0 +1,247 @@
+// C-ABI boundary of libgsa: argument validation, workspace sizing, dispatch.
+// Host code only; every step of the computation runs in the HIP kernels.
+#include "../../include/gsa.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <cmath>
+
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kChunk = 64;
+constexpr int kTargetWorkgroups = 256;  // one per CU on MI355X
+constexpr int kMaxUnits = 65535;        // grid y limit
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range rng(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) {
+  if (a.lo == 0 || b.lo == 0 || a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+size_t esize(int dtype) { return dtype == GSA_DTYPE_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == GSA_DTYPE_F32 || dtype == GSA_DTYPE_BF16; }
+
+int default_chunks_per_seg(long long units, int nchunks) {
+  if (nchunks <= 1 || units <= 0) return nchunks > 0 ? nchunks : 1;
+  long long p = kTargetWorkgroups / units;
+  if (p < 1) p = 1;
+  if (p > nchunks) p = nchunks;
+  return (int)((nchunks + p - 1) / p);
+}
+
+int resolve_cps(long long units, int T, int cps) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  if (cps <= 0) cps = default_chunks_per_seg(units, nchunks);
+  if (nchunks > 0 && cps > nchunks) cps = nchunks;
+  return cps < 1 ? 1 : cps;
+}
+
+size_t ws_bytes(long long units, int T, int cps, size_t state_elems, size_t dec_elems) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  if (nchunks == 0 || units == 0) return 0;
+  const long long P = (nchunks + cps - 1) / cps;
+  if (P <= 1) return 0;
+  const size_t st = (size_t)units * P * state_elems * 4;
+  const size_t dc = (size_t)units * P * dec_elems * 4;
+  return ((st + 255) & ~(size_t)255) + dc;
+}
+
+int hip_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? GSA_OK : GSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gsa_abi_version(void) { return GSA_ABI_VERSION; }
+
+const char* gsa_status_string(int s) {
+  switch (s) {
+    case GSA_OK: return "ok";
+    case GSA_ERR_NULL: return "a required pointer is NULL";
+    case GSA_ERR_SHAPE: return "invalid size or tau";
+    case GSA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case GSA_ERR_UNSUPPORTED: return "shape/dtype combination not compiled";
+    case GSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GSA_ERR_HIP: return "HIP launch failed";
+    case GSA_ERR_ALIAS: return "output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int gsa_fwd_supported(int dk, int dv, int m, int C, int dtype) {
+  if (C != kChunk || !dtype_ok(dtype)) return 0;
+  return gsa::gsa_dispatch(dtype, dk, dv, m, nullptr, true) > 0 ? 1 : 0;
+}
+
+int gla_fwd_supported(int dk, int dv, int C, int dtype) {
+  if (C != kChunk || !dtype_ok(dtype)) return 0;
+  return gsa::gla_dispatch(dtype, dk, dv, nullptr, true) > 0 ? 1 : 0;
+}
+
+int gsa_decode_supported(int dk, int dv, int m, int dtype) {
+  if (!dtype_ok(dtype)) return 0;
+  return gsa::decode_dispatch(dtype, dk, dv, m, nullptr, true) > 0 ? 1 : 0;
+}
+
+size_t gsa_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int C, int dtype,
+                               int cps) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !dtype_ok(dtype))
+    return (size_t)-1;
+  const long long units = (long long)B * H;
+  return ws_bytes(units, T, resolve_cps(units, T, cps), (size_t)m * (dk + dv), (size_t)m);
+}
+
+size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int dtype, int cps) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || C < 1 || !dtype_ok(dtype)) return (size_t)-1;
+  const long long units = (long long)B * H;
+  return ws_bytes(units, T, resolve_cps(units, T, cps), (size_t)dk * dv, (size_t)dk);
+}
+
+int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* k0,
+            const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk, int dv, int m,
+            int C, float tau, int dtype, void* workspace, size_t workspace_bytes, int cps,
+            void* stream) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !(tau > 0.f) ||
+      !std::isfinite(tau) || !dtype_ok(dtype))
+    return GSA_ERR_SHAPE;
+  if (!gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)B * H;
+  if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  if (units == 0) return GSA_OK;
+  if (T > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const size_t nt = (size_t)units * T;
+  const Range rq = rng(q, nt * dk * es), rk = rng(k, nt * dk * es), rv = rng(v, nt * dv * es),
+              rg = rng(g, nt * m * es), ro = rng(o, nt * dv * es);
+  const Range rk0 = rng(k0, (size_t)units * m * dk * 4), rv0 = rng(v0, (size_t)units * m * dv * 4);
+  const Range rkf = rng(kf, (size_t)units * m * dk * 4), rvf = rng(vf, (size_t)units * m * dv * 4);
+  const Range rws = rng(workspace, workspace_bytes);
+  for (Range in : {rq, rk, rv, rg, rk0, rv0, rkf, rvf, rws})
+    if (overlap(ro, in)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, ro, rws}) {
+    if (overlap(rkf, in) || overlap(rvf, in)) return GSA_ERR_ALIAS;
+  }
+  if (overlap(rkf, rvf) || overlap(rkf, rv0) || overlap(rvf, rk0)) return GSA_ERR_ALIAS;
+  if ((kf && k0 && kf != k0 && overlap(rkf, rk0)) || (vf && v0 && vf != v0 && overlap(rvf, rv0)))
+    return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, rk0, rv0})
+    if (overlap(rws, in)) return GSA_ERR_ALIAS;
+  const int c = resolve_cps(units, T, cps);
+  const size_t need = ws_bytes(units, T, c, (size_t)m * (dk + dv), (size_t)m);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
+
+  if (T == 0) {  // nothing to read: the final state is the initial state
+    gsa::state_copy(kf, k0, (size_t)units * m * dk, stream);
+    gsa::state_copy(vf, v0, (size_t)units * m * dv, stream);
+    return hip_status();
+  }
+  gsa::GsaLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.k0 = k0; a.v0 = v0; a.o = o; a.kf = kf; a.vf = vf;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const long long P = (nchunks + c - 1) / c;
+  a.ws_state = (float*)workspace;
+  a.ws_dec = workspace ? (float*)((char*)workspace +
+                                  (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
+                       : nullptr;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
+  (void)hipGetLastError();
+  if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
+            float* sf, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
+            void* workspace, size_t workspace_bytes, int cps, void* stream) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || C < 1 || !(tau > 0.f) ||
+      !std::isfinite(tau) || !dtype_ok(dtype))
+    return GSA_ERR_SHAPE;
+  if (!gla_fwd_supported(dk, dv, C, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)B * H;
+  if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  if (units == 0) return GSA_OK;
+  if (T > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, s0, o, sf, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const size_t nt = (size_t)units * T;
+  const Range rq = rng(q, nt * dk * es), rk = rng(k, nt * dk * es), rv = rng(v, nt * dv * es),
+              rg = rng(g, nt * dk * es), ro = rng(o, nt * dv * es);
+  const Range rs0 = rng(s0, (size_t)units * dk * dv * 4), rsf = rng(sf, (size_t)units * dk * dv * 4);
+  const Range rws = rng(workspace, workspace_bytes);
+  for (Range in : {rq, rk, rv, rg, rs0, rsf, rws})
+    if (overlap(ro, in)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, rws})
+    if (overlap(rsf, in)) return GSA_ERR_ALIAS;
+  if (sf && s0 && sf != s0 && overlap(rsf, rs0)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, rs0})
+    if (overlap(rws, in)) return GSA_ERR_ALIAS;
+  const int c = resolve_cps(units, T, cps);
+  const size_t need = ws_bytes(units, T, c, (size_t)dk * dv, (size_t)dk);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
+  if (T == 0) {
+    gsa::state_copy(sf, s0, (size_t)units * dk * dv, stream);
+    return hip_status();
+  }
+  gsa::GlaLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.sf = sf;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const long long P = (nchunks + c - 1) / c;
+  a.ws_state = (float*)workspace;
+  a.ws_dec = workspace ? (float*)((char*)workspace +
+                                  (((size_t)units * P * dk * dv * 4 + 255) & ~(size_t)255))
+                       : nullptr;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
+  (void)hipGetLastError();
+  if (gsa::gla_dispatch(dtype, dk, dv, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* ks,
+                    float* vs, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
+                    void* stream) {
+  if (N < 0 || H < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
+      !dtype_ok(dtype))
+    return GSA_ERR_SHAPE;
+  if (!gsa_decode_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)N * H;
+  if (units == 0) return GSA_OK;
+  if (units > 0x7fffffffLL) return GSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !ks || !vs || !o) return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, ks, vs, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const Range rq = rng(q, units * dk * es), rk = rng(k, units * dk * es), rv = rng(v, units * dv * es),
+              rg = rng(g, units * m * es), ro = rng(o, units * dv * es);
+  const Range rks = rng(ks, (size_t)units * m * dk * 4), rvs = rng(vs, (size_t)units * m * dv * 4);
+  if (overlap(rks, rvs)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, ro}) {
+    if (overlap(rks, in) || overlap(rvs, in)) return GSA_ERR_ALIAS;
+  }
+  for (Range in : {rq, rk, rv, rg})
+    if (overlap(ro, in)) return GSA_ERR_ALIAS;
+  gsa::DecodeLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs; a.o = o; a.N = N; a.H = H;
+  a.tau = tau; a.stream = stream;
+  (void)hipGetLastError();
+  if (gsa::decode_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// One recurrent GSA step for a batch of sequences (single-token decode).
+//
+// Method: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling",
+// Sec. 3.2 (per-slot gated RNN, recurrent form of Fig. 2) and Sec. 3.3 (forget
+// gate sigmoid(g)^(1/tau)).  For every (sequence, head), in place:
+//   Kt <- Diag(a) Kt + (1-a) k^T ;  s = softmax(Kt q) ;
+//   Vt <- Diag(a) Vt + (1-a) v^T ;  o = Vt^T s.
+// The step is bound by HBM traffic: the two fp32 slot states are read and
+// written once (2 * 2 * m * d * 4 bytes per unit) while the token I/O is tiny,
+// the reason the paper ties inference speed to state size (Sec. 4.1.4).
+//
+// Layout: one workgroup of 256 threads per unit; each thread owns NK float4 of
+// Kt and of Vt (row c = f / (DK/4)), all issued before any arithmetic so that
+// 64 KB per unit are in flight.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace gsa {
+
+constexpr int dNT = 256;
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* out);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* out) {
+  float4 x = *reinterpret_cast<const float4*>(p);
+  out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+}
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float* out) {
+  uint2 x = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(x.x << 16);
+  out[1] = __uint_as_float(x.x & 0xffff0000u);
+  out[2] = __uint_as_float(x.y << 16);
+  out[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float* v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
+  uint2 x;
+  x.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  x.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(p) = x;
+}
+
+template <typename T, int DK, int DV, int M>
+__global__ void __launch_bounds__(dNT)
+gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                  const T* __restrict__ g, float* __restrict__ ks, float* __restrict__ vs,
+                  T* __restrict__ o, float inv_tau) {
+  constexpr int LK = DK / 4, LV = DV / 4;        // float4 per state row
+  constexpr int NK = M * LK / dNT, NV = M * LV / dNT;
+  static_assert(NK >= 1 && NV >= 1 && (M * LK) % dNT == 0 && (M * LV) % dNT == 0, "shape");
+  static_assert(64 % LK == 0 && 64 % LV == 0, "row width must divide a wave");
+  __shared__ float sA[M], sW[M], sZ[M], sS[M];
+  __shared__ float sO[dNT / LV][DV];
+
+  const int tid = threadIdx.x;
+  const size_t u = blockIdx.x;
+  float4* kst = reinterpret_cast<float4*>(ks + u * M * DK);
+  float4* vst = reinterpret_cast<float4*>(vs + u * M * DV);
+
+  float4 kr[NK], vr[NV];
+#pragma unroll
+  for (int i = 0; i < NK; i++) kr[i] = kst[tid + dNT * i];
+#pragma unroll
+  for (int i = 0; i < NV; i++) vr[i] = vst[tid + dNT * i];
+
+  const int ck = tid % LK, cv = tid % LV;       // this thread's float4 column
+  float qf[4], kf[4], vf[4];
+  load4<T>(q + u * DK + 4 * ck, qf);
+  load4<T>(k + u * DK + 4 * ck, kf);
+  load4<T>(v + u * DV + 4 * cv, vf);
+  for (int c = tid; c < M; c += dNT) {
+    float a, w;
+    gate_alpha_w(Elem<T>::to_f(g[u * M + c]), inv_tau, a, w);
+    sA[c] = a;
+    sW[c] = w;
+  }
+  __syncthreads();
+
+  // pass 1: key state update and slot scores
+#pragma unroll
+  for (int i = 0; i < NK; i++) {
+    const int c = (tid + dNT * i) / LK;
+    const float a = sA[c], w = sW[c];
+    kr[i].x = a * kr[i].x + w * kf[0];
+    kr[i].y = a * kr[i].y + w * kf[1];
+    kr[i].z = a * kr[i].z + w * kf[2];
+    kr[i].w = a * kr[i].w + w * kf[3];
+    kst[tid + dNT * i] = kr[i];
+    float z = kr[i].x * qf[0] + kr[i].y * qf[1] + kr[i].z * qf[2] + kr[i].w * qf[3];
+#pragma unroll
+    for (int off = LK / 2; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+    if (tid % LK == 0) sZ[c] = z;
+  }
+  __syncthreads();
+  if (tid < 64) {  // slot softmax in wave 0
+    float z = -INFINITY;
+    for (int c = tid; c < M; c += 64) z = fmaxf(z, sZ[c]);
+    float mx = z;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    float sm = 0.f;
+    for (int c = tid; c < M; c += 64) sm += __expf(sZ[c] - mx);
+    sm = sum64(sm);
+    for (int c = tid; c < M; c += 64) sS[c] = __expf(sZ[c] - mx) / sm;
+  }
+  __syncthreads();
+
+  // pass 2: value state update and read-out
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int c = (tid + dNT * i) / LV;
+    const float a = sA[c], w = sW[c], s = sS[c];
+    vr[i].x = a * vr[i].x + w * vf[0];
+    vr[i].y = a * vr[i].y + w * vf[1];
+    vr[i].z = a * vr[i].z + w * vf[2];
+    vr[i].w = a * vr[i].w + w * vf[3];
+    vst[tid + dNT * i] = vr[i];
+    acc[0] += s * vr[i].x;
+    acc[1] += s * vr[i].y;
+    acc[2] += s * vr[i].z;
+    acc[3] += s * vr[i].w;
+  }
+  // threads with the same column: tid % LV equal; rows differ by tid / LV
+  const int grp = tid / LV;
+#pragma unroll
+  for (int e = 0; e < 4; e++) sO[grp][4 * cv + e] = acc[e];
+  __syncthreads();
+  if (tid < LV) {
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gi = 0; gi < dNT / LV; gi++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) r[e] += sO[gi][4 * tid + e];
+    }
+    store4<T>(o + u * DV + 4 * tid, r);
+  }
+}
+
+template <typename T, int DK, int DV, int M>
+static int launch_decode(const DecodeLaunch& a) {
+  const unsigned units = (unsigned)a.N * (unsigned)a.H;
+  hipLaunchKernelGGL((gsa_decode_kernel<T, DK, DV, M>), dim3(units), dim3(dNT), 0, (hipStream_t)a.stream,
+                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
+                     1.0f / a.tau);
+  return 0;
+}
+
+#define DEC_CASE(TT, DTC, DKC, DVC, MC)                                   \
+  if (dt == DTC && dk == DKC && dv == DVC && m == MC) {                 \
+    if (query) return 1;                                                 \
+    return launch_decode<TT, DKC, DVC, MC>(*a);                          \
+  }
+
+int decode_dispatch(int dt, int dk, int dv, int m, const DecodeLaunch* a, bool query) {
+  DEC_CASE(bf16_t, 1, 128, 128, 64)
+  DEC_CASE(bf16_t, 1, 128, 128, 32)
+  DEC_CASE(bf16_t, 1, 64, 64, 64)
+  DEC_CASE(bf16_t, 1, 64, 64, 32)
+  DEC_CASE(float, 0, 128, 128, 64)
+  DEC_CASE(float, 0, 128, 128, 32)
+  DEC_CASE(float, 0, 64, 64, 64)
+  DEC_CASE(float, 0, 64, 64, 32)
+  DEC_CASE(float, 0, 64, 64, 16)
+  return -1;
+}
+
+__global__ void state_copy_kernel(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = src ? src[i] : 0.f;
+}
+
+void state_copy(float* dst, const float* src, size_t n, void* stream) {
+  if (!dst || n == 0 || dst == src) return;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(state_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, dst, src, n);
+}
+
+}  // namespace gsa

@@ -1,0 +1,48 @@
+// Internal launch descriptors shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <stddef.h>
+
+namespace gsa {
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+struct GsaLaunch {
+  const void *q, *k, *v, *g;
+  const float *k0, *v0;
+  void* o;
+  float *kf, *vf;
+  float *ws_state, *ws_dec;
+  int B, H, T, chunks_per_seg;
+  float tau;
+  void* stream;
+};
+
+struct GlaLaunch {
+  const void *q, *k, *v, *g;
+  const float* s0;
+  void* o;
+  float* sf;
+  float *ws_state, *ws_dec;
+  int B, H, T, chunks_per_seg;
+  float tau;
+  void* stream;
+};
+
+struct DecodeLaunch {
+  const void *q, *k, *v, *g;
+  float *ks, *vs;
+  void* o;
+  int N, H;
+  float tau;
+  void* stream;
+};
+
+// query == true: return the phase-C LDS bytes (> 0) if the shape is compiled, else -1.
+// query == false: enqueue the launches and return 0, or -1 if not compiled.
+int gsa_dispatch(int dtype, int dk, int dv, int m, const GsaLaunch* a, bool query);
+int gla_dispatch(int dtype, int dk, int dv, const GlaLaunch* a, bool query);
+int decode_dispatch(int dtype, int dk, int dv, int m, const DecodeLaunch* a, bool query);
+// copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
+void state_copy(float* dst, const float* src, size_t n, void* stream);
+
+}  // namespace gsa

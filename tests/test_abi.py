@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every entry point include/gsa.h declares,
+and rejects bad arguments on the host before anything is enqueued (no GPU
+needed: every call here fails validation first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsa.h")
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    import slot_memory_sequence_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(gsa_\w+|gla_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_symbols_exported(gsa):
+    names = _declared()
+    assert {"gsa_fwd", "gla_fwd", "gsa_decode_step", "gsa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(gsa.lib, n), "missing export: " + n
+    assert gsa.lib.gsa_abi_version() == 1
+
+
+def test_status_strings(gsa):
+    for s in range(0, 8):
+        assert gsa.status_string(s) and gsa.status_string(s) != "unknown status"
+    assert gsa.status_string(99) == "unknown status"
+
+
+def test_supported_sets(gsa):
+    assert gsa.gsa_fwd_supported(128, 128, 64, 64, 1)
+    assert gsa.gsa_fwd_supported(64, 64, 32, 64, 0)
+    assert not gsa.gsa_fwd_supported(128, 128, 64, 32, 1)   # only C = 64 compiled
+    assert not gsa.gsa_fwd_supported(128, 64, 64, 64, 1)
+    assert not gsa.gsa_fwd_supported(128, 128, 64, 64, 7)
+    assert gsa.gla_fwd_supported(128, 128, 64, 1)
+    assert gsa.gsa_decode_supported(128, 128, 64, 1)
+    assert not gsa.gsa_decode_supported(96, 128, 64, 1)
+
+
+def test_workspace_query(gsa):
+    # one segment per unit needs no workspace
+    assert gsa.gsa_fwd_workspace_bytes(1, 1, 64, 128, 128, 64, 64, 1, 0) == 0
+    nb = gsa.gsa_fwd_workspace_bytes(8, 4, 2048, 128, 128, 64, 64, 1, 4)
+    P = 2048 // 64 // 4
+    state = 32 * P * 64 * 256 * 4
+    assert nb == ((state + 255) // 256) * 256 + 32 * P * 64 * 4
+    assert gsa.gsa_fwd_workspace_bytes(-1, 4, 16, 128, 128, 64, 64, 1, 0) == (1 << 64) - 1
+    assert gsa.gla_fwd_workspace_bytes(8, 16, 4096, 128, 128, 64, 1, 0) > 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation
+
+
+def _gsa_call(gsa, **over):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, g=FAKE + 0x300000, k0=None, v0=None,
+             o=FAKE + 0x400000, kf=None, vf=None, B=1, H=1, T=64, dk=128, dv=128, m=64, C=64,
+             tau=8.0, dtype=1, ws=None, wsb=0, cps=0)
+    a.update(over)
+    P = ctypes.c_void_p
+    return gsa.lib.gsa_fwd(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["k0"]), P(a["v0"]),
+                           P(a["o"]), P(a["kf"]), P(a["vf"]), a["B"], a["H"], a["T"], a["dk"],
+                           a["dv"], a["m"], a["C"], a["tau"], a["dtype"], P(a["ws"]), a["wsb"],
+                           a["cps"], None)
+
+
+def test_gsa_fwd_validation(gsa):
+    assert _gsa_call(gsa, B=-1) == 2
+    assert _gsa_call(gsa, tau=0.0) == 2
+    assert _gsa_call(gsa, tau=float("nan")) == 2
+    assert _gsa_call(gsa, dtype=3) == 2
+    assert _gsa_call(gsa, C=32) == 4
+    assert _gsa_call(gsa, m=48) == 4
+    assert _gsa_call(gsa, dk=64) == 4
+    assert _gsa_call(gsa, q=None) == 1
+    assert _gsa_call(gsa, o=None) == 1
+    assert _gsa_call(gsa, g=FAKE + 0x300008) == 3
+    assert _gsa_call(gsa, o=FAKE + 0x20) == 7            # output overlaps q
+    assert _gsa_call(gsa, kf=FAKE + 0x500000, vf=FAKE + 0x500000) == 7
+    # long sequence on one unit needs a workspace
+    assert _gsa_call(gsa, T=4096, cps=1) == 5
+    assert _gsa_call(gsa, T=4096, cps=1, ws=FAKE + 0x10000000, wsb=16) == 5
+    assert _gsa_call(gsa, B=70000) == 4
+
+
+def test_gla_and_decode_validation(gsa):
+    P = ctypes.c_void_p
+    f = gsa.lib.gla_fwd
+    base = [P(FAKE), P(FAKE + 0x100000), P(FAKE + 0x200000), P(FAKE + 0x300000), P(None),
+            P(FAKE + 0x400000), P(None)]
+    assert f(*base, 1, 1, 64, 128, 128, 64, 0.0, 1, None, 0, 0, None) == 2
+    assert f(*base, 1, 1, 64, 128, 96, 64, 16.0, 1, None, 0, 0, None) == 4
+    bad = list(base)
+    bad[5] = P(FAKE + 0x100010)   # o overlaps k
+    assert f(*bad, 1, 1, 64, 128, 128, 64, 16.0, 1, None, 0, 0, None) == 7
+    d = gsa.lib.gsa_decode_step
+    args = [P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000), P(FAKE + 0x3000), P(FAKE + 0x100000),
+            P(FAKE + 0x200000), P(FAKE + 0x4000)]
+    assert d(*args, 1, 1, 128, 128, 64, -1.0, 1, None) == 2
+    args2 = list(args)
+    args2[5] = P(FAKE + 0x100100)  # v_state overlaps k_state
+    assert d(*args2, 1, 1, 128, 128, 64, 8.0, 1, None) == 7
+    args3 = list(args)
+    args3[4] = None
+    assert d(*args3, 1, 1, 128, 128, 64, 8.0, 1, None) == 1
+
+
+def test_package_has_no_cpu_fallback():
+    """The product package never imports, loads or calls the oracle."""
+    pkg = os.path.join(ROOT, "slot_memory_sequence_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                for bad in ("import oracle", "from oracle", "liboracle", "oracle_gsa", "oracle_gla"):
+                    assert bad not in text, (f, bad)

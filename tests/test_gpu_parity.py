@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+the same seeded stored inputs.
+
+Bar (max |x - y| / max |y| per output tensor): 1e-4 for float32 inputs,
+2e-2 for bfloat16 inputs with float32 state and accumulation.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def gsa(torch):
+    import slot_memory_sequence_amd as m
+    return m
+
+
+def _run_gsa(gsa, torch, inp, tau, final=True, cps=0):
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    k0, v0 = to_dev(inp["k0"], torch), to_dev(inp["v0"], torch)
+    o, kf, vf = gsa.gsa_fwd(q, k, v, g, k0, v0, tau=tau, final_state=final, chunks_per_segment=cps)
+    torch.cuda.synchronize()
+    return o, kf, vf
+
+
+def _oracle_gsa(inp, tau, units=None):
+    f = lambda x: None if x is None else (x.f64 if units is None else x.f64.reshape(-1, *x.shape[2:])[units][:, None])
+    return oracle.gsa_fwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["g"]), f(inp["k0"]),
+                          f(inp["v0"]), tau=tau, nthreads=oracle.max_threads())
+
+
+def _check_gsa(gsa, torch, B, H, T, d, m, dtype, init=False, tau=8.0, cps=0, g_shift=0.0,
+               seed=0, mutate=None):
+    inp = synth.gsa_inputs(B, H, T, d, d, m, dtype=dtype, seed=seed, g_shift=g_shift,
+                           init_std=0.1 if init else None)
+    if mutate is not None:
+        mutate(inp)
+    o, kf, vf = _run_gsa(gsa, torch, inp, tau, final=True, cps=cps)
+    ref = _oracle_gsa(inp, tau)
+    tol = TOL[dtype]
+    eo, ek, ev = rel_err(to_np(o), ref["o"]), rel_err(to_np(kf), ref["kf"]), rel_err(to_np(vf), ref["vf"])
+    print("gsa B%d H%d T%d d%d m%d %s init=%s cps=%d: o %.2e kf %.2e vf %.2e" %
+          (B, H, T, d, m, dtype, init, cps, eo, ek, ev))
+    assert eo <= tol and ek <= tol and ev <= tol
+    return o
+
+
+# ----------------------------------------------------------------- GSA
+def test_gsa_f32_small_workload(gsa, torch):
+    """B1 H2 T256 d64 m32, float32, zero state, seed 0 (q,k,v scaled 1/8)."""
+    w = synth.WORKLOADS["gsa_f32_small"]
+    inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype="f32",
+                           seed=0, qkv_scale=w["qkv_scale"])
+    o, kf, vf = _run_gsa(gsa, torch, inp, w["tau"])
+    ref = _oracle_gsa(inp, w["tau"])
+    for x, y in ((o, ref["o"]), (kf, ref["kf"]), (vf, ref["vf"])):
+        assert rel_err(to_np(x), y) <= 1e-4
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200, 320])
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("f32", 64, 16), ("bf16", 128, 64),
+                                       ("bf16", 64, 32), ("bf16", 128, 32), ("f32", 128, 16),
+                                       ("bf16", 64, 64)])
+def test_gsa_shapes(gsa, torch, T, dtype, d, m):
+    _check_gsa(gsa, torch, 2, 2, T, d, m, dtype, init=(T % 2 == 1), seed=T)
+
+
+@pytest.mark.parametrize("cps", [1, 2, 3, 100])
+def test_gsa_segmentations(gsa, torch, cps):
+    """The chunk-state scan must give the same result for any segment split."""
+    _check_gsa(gsa, torch, 1, 3, 64 * 7 + 5, 128, 64, "bf16", init=True, cps=cps, seed=3)
+    _check_gsa(gsa, torch, 1, 2, 64 * 5 + 9, 64, 32, "f32", init=True, cps=cps, seed=4)
+
+
+def _extreme(inp):
+    g = inp["g"]
+    x = g.f64.copy()
+    x[..., 3, :] = -np.inf
+    x[..., 70:75, 2] = np.inf
+    x[..., 100, :5] = -30.0
+    x[..., 130:140, 7] = 30.0
+    x[..., 200:260, 1] = -np.inf
+    inp["g"] = synth.stored(x, g.dtype)
+
+
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_gsa_extreme_gates(gsa, torch, dtype, d, m):
+    """alpha = 0 / alpha = 1 tokens (g = -inf / +inf, +-30): chunks whose decay
+    product falls below e^-40 take the exact token recurrence."""
+    for cps in (0, 1):
+        _check_gsa(gsa, torch, 1, 2, 300, d, m, dtype, init=True, cps=cps, mutate=_extreme, seed=7)
+
+
+def test_gsa_split_handoff_and_inplace(gsa, torch):
+    """fwd over [0,T1) then [T1,T) from the handed-off state == fwd over [0,T);
+    the second call advances the state in place (k_final is k0)."""
+    inp = synth.gsa_inputs(2, 2, 333, 64, 64, 32, dtype="f32", seed=11, init_std=0.1)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    k0, v0 = to_dev(inp["k0"], torch), to_dev(inp["v0"], torch)
+    o_full, kf, vf = gsa.gsa_fwd(q, k, v, g, k0, v0, final_state=True, chunks_per_segment=1)
+    T1 = 130
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1, k1, v1 = gsa.gsa_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1), k0, v0,
+                             final_state=True)
+    o2, k2, v2 = gsa.gsa_fwd(sl(q, T1, 333), sl(k, T1, 333), sl(v, T1, 333), sl(g, T1, 333), k1, v1,
+                             final_state=True, k_final=k1, v_final=v1, chunks_per_segment=1)
+    torch.cuda.synchronize()
+    assert k2.data_ptr() == k1.data_ptr()
+    full = to_np(o_full)
+    assert rel_err(np.concatenate([to_np(o1), to_np(o2)], axis=2), full) <= 1e-5
+    assert rel_err(to_np(k2), to_np(kf)) <= 1e-5 and rel_err(to_np(v2), to_np(vf)) <= 1e-5
+
+
+def test_gsa_empty_and_tiny(gsa, torch):
+    inp = synth.gsa_inputs(1, 2, 0, 64, 64, 32, dtype="f32", seed=1, init_std=0.1)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    k0, v0 = to_dev(inp["k0"], torch), to_dev(inp["v0"], torch)
+    o, kf, vf = gsa.gsa_fwd(q, k, v, g, k0, v0, final_state=True)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert np.array_equal(to_np(kf), inp["k0"].f64) and np.array_equal(to_np(vf), inp["v0"].f64)
+    o, _, _ = gsa.gsa_fwd(q[:0], k[:0], v[:0], g[:0])   # B = 0
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+def test_gsa_deterministic(gsa, torch):
+    inp = synth.gsa_inputs(2, 4, 700, 128, 128, 64, dtype="bf16", seed=5)
+    a = _run_gsa(gsa, torch, inp, 8.0)[0]
+    b = _run_gsa(gsa, torch, inp, 8.0)[0]
+    assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------- GLA
+def _check_gla(gsa, torch, B, H, T, d, dtype, init=False, tau=16.0, cps=0, seed=0, mutate=None):
+    inp = synth.gla_inputs(B, H, T, d, d, dtype=dtype, seed=seed, init_std=0.1 if init else None)
+    if mutate is not None:
+        mutate(inp)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    o, sf = gsa.gla_fwd(q, k, v, g, to_dev(inp["s0"], torch), tau=tau, final_state=True,
+                        chunks_per_segment=cps)
+    torch.cuda.synchronize()
+    s0 = None if inp["s0"] is None else inp["s0"].f64
+    ref = oracle.gla_fwd(inp["q"].f64, inp["k"].f64, inp["v"].f64, inp["g"].f64, s0, tau=tau,
+                         nthreads=oracle.max_threads())
+    eo, es = rel_err(to_np(o), ref["o"]), rel_err(to_np(sf), ref["sf"])
+    print("gla B%d H%d T%d d%d %s cps=%d: o %.2e sf %.2e" % (B, H, T, d, dtype, cps, eo, es))
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("T", [1, 50, 64, 129, 300])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
+def test_gla_shapes(gsa, torch, T, dtype, d):
+    _check_gla(gsa, torch, 2, 2, T, d, dtype, init=(T % 2 == 0), seed=T)
+
+
+@pytest.mark.parametrize("cps", [1, 3])
+def test_gla_segmentations(gsa, torch, cps):
+    _check_gla(gsa, torch, 1, 2, 64 * 6 + 3, 128, "bf16", init=True, cps=cps, seed=2)
+
+
+def test_gla_extreme_gates(gsa, torch):
+    def mut(inp):
+        x = inp["g"].f64.copy()
+        x[..., 10, :] = -np.inf
+        x[..., 80:90, 5] = np.inf
+        x[..., 150:220, 3] = -np.inf
+        inp["g"] = synth.stored(x, inp["g"].dtype)
+    _check_gla(gsa, torch, 1, 2, 260, 64, "f32", init=True, mutate=mut, seed=9)
+    _check_gla(gsa, torch, 1, 2, 260, 128, "bf16", init=True, mutate=mut, seed=9, cps=1)
+
+
+# -------------------------------------------------------------- decode
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 64), ("f32", 64, 32), ("f32", 128, 64),
+                                       ("bf16", 64, 32), ("f32", 64, 16)])
+def test_decode_step(gsa, torch, dtype, d, m):
+    inp = synth.decode_inputs(3, 5, d, d, m, dtype=dtype, seed=m)
+    ks, vs = to_dev(inp["kstate"], torch), to_dev(inp["vstate"], torch)
+    o = gsa.gsa_decode_step(*(to_dev(inp[n], torch) for n in "qkvg"), ks, vs)
+    torch.cuda.synchronize()
+    ro, rk, rv = oracle.gsa_decode_step(inp["q"].f64, inp["k"].f64, inp["v"].f64, inp["g"].f64,
+                                        inp["kstate"].f64, inp["vstate"].f64)
+    tol = TOL[dtype]
+    assert rel_err(to_np(o), ro) <= tol
+    assert rel_err(to_np(ks), rk) <= 1e-5 and rel_err(to_np(vs), rv) <= 1e-5
+
+
+def test_decode_chain_equals_fwd(gsa, torch):
+    """T chained decode steps reproduce the chunkwise forward (float32)."""
+    inp = synth.gsa_inputs(2, 2, 70, 64, 64, 32, dtype="f32", seed=21, init_std=0.1)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    ks, vs = to_dev(inp["k0"], torch).clone(), to_dev(inp["v0"], torch).clone()
+    o_fwd, kf, vf = gsa.gsa_fwd(q, k, v, g, to_dev(inp["k0"], torch), to_dev(inp["v0"], torch),
+                                final_state=True)
+    outs = []
+    for t in range(70):
+        outs.append(gsa.gsa_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                        v[:, :, t].contiguous(), g[:, :, t].contiguous(), ks, vs))
+    torch.cuda.synchronize()
+    assert rel_err(np.stack([to_np(x) for x in outs], axis=2), to_np(o_fwd)) <= 1e-5
+    assert rel_err(to_np(ks), to_np(kf)) <= 1e-5 and rel_err(to_np(vs), to_np(vf)) <= 1e-5
