@@ -1,0 +1,362 @@
+"""Benchmark of the GSA hot path on one MI355X.
+
+A step is one chunkwise GSA forward (gate prep, both passes, slot softmax,
+state carry; all phases of the launch sequence) over one batch of the
+training-shape workload: B=8, H=4, T=2048, dk=dv=128, m=64 slots, C=64,
+bf16 inputs, fp32 state (seeded synthetic data).  `value` is B*T tokens/s
+with inputs resident in HBM, rotating over enough input copies that the
+256 MB last-level cache cannot hold them.  The dominant kernel's duration
+comes from HIP events recorded on the library's stream around it.
+
+Also reported: the standalone GLA forward (T=4096), the long-context GSA
+forward (T=16384, initial state), and the batched decode step (HBM GB/s),
+and the float64 CPU oracle timed on this host on the training-shape batch.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ HIP events
+class Events:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return float(f.value)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "slot_memory_sequence_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get("%s@%s" % (kernel, workload))
+    except Exception:
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------ workloads
+def gsa_alg(B, H, T, dk, dv, m, C, dtype_bytes, init_state=False, final_state=False):
+    th = B * H * T
+    flops = th * ((C + 1) * (dk + 2 * m + dv) + 4 * m * (dk + dv))
+    nbytes = th * (2 * dk + dv + m + dv) * dtype_bytes
+    if init_state:
+        nbytes += B * H * m * (dk + dv) * 4
+    if final_state:
+        nbytes += B * H * m * (dk + dv) * 4
+    return flops, nbytes
+
+
+def gla_alg(B, H, T, dk, dv, C, dtype_bytes):
+    th = B * H * T
+    return th * ((C + 1) * (dk + dv) + 4 * dk * dv), th * (3 * dk + 2 * dv) * dtype_bytes
+
+
+def dev_sets(torch, inp, names, nsets):
+    from tests.gpu_helpers import to_dev
+    base = {n: to_dev(inp[n], torch) for n in names if inp.get(n) is not None}
+    sets = [base]
+    for _ in range(nsets - 1):
+        sets.append({n: t.clone() for n, t in base.items()})
+    return sets
+
+
+def time_op(torch, ev, call, sets, steps, warmup):
+    """Run warmup + timed steps rotating over input sets; returns wall-clock
+    seconds for the timed steps and per-step phase times (ms)."""
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = ev.create(4 * steps)
+    for i in range(warmup):
+        call(sets[i % len(sets)], None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(sets[i % len(sets)], evs[4 * i: 4 * i + 4])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    phases = []
+    for i in range(steps):
+        e = evs[4 * i: 4 * i + 4]
+        phases.append((ev.ms(e[0], e[1]), ev.ms(e[1], e[2]), ev.ms(e[2], e[3]), ev.ms(e[0], e[3])))
+    return wall, phases
+
+
+def mean(xs):
+    return sum(xs) / len(xs)
+
+
+def roofline(bytes_alg, t_ms, kernel, workload):
+    achieved = bytes_alg / (t_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(kernel, workload),
+            "kernel": kernel}
+
+
+def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True):
+    import synth
+    inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                           seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
+                           init_std=w["init_std"])
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "k0", "v0"], nsets)
+    init = inp["k0"] is not None
+    B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
+    outs = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    kfs = [torch.empty((B, H, m, dk), dtype=torch.float32, device="cuda") for _ in sets] if init else None
+    vfs = [torch.empty((B, H, m, dv), dtype=torch.float32, device="cuda") for _ in sets] if init else None
+    nb = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def call(s, events):
+        i = next(j for j, x in enumerate(sets) if x is s)
+        gsa.gsa_fwd(s["q"], s["k"], s["v"], s["g"], s.get("k0"), s.get("v0"), tau=w["tau"],
+                    final_state=init, out=outs[i], k_final=kfs[i] if init else None,
+                    v_final=vfs[i] if init else None, workspace=ws, events=events)
+
+    wall, ph = time_op(torch, ev, call, sets, steps, warmup)
+    flops, nbytes = gsa_alg(B, H, T, dk, dv, m, w["C"], 2, init_state=init, final_state=init)
+    t_op = mean([p[3] for p in ph])
+    t_out = mean([p[2] for p in ph])
+    res = {
+        "tokens_per_s": B * T * steps / wall, "ms_per_step": wall / steps * 1e3,
+        "ms_phases": {"state_maps": round(mean([p[0] for p in ph]), 4),
+                      "scan": round(mean([p[1] for p in ph]), 4),
+                      "outputs": round(t_out, 4), "op": round(t_op, 4)},
+        "alg_flops": flops, "alg_bytes": nbytes,
+        "alg_tflops": flops / (t_op * 1e-3) / 1e12,
+        "roofline": roofline(nbytes, t_out, "gsa_seg_out", name),
+        "op_roofline": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
+                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "input_sets": nsets, "out": outs[0], "inp": inp,
+    }
+    res["mfma_frac_alg"] = res["alg_tflops"] / PEAK_BF16_TFLOPS
+    if warm_too:
+        wall_w, ph_w = time_op(torch, ev, call, sets[:1], steps, 2)
+        res["warm_tokens_per_s"] = B * T * steps / wall_w
+        res["warm_ms_op"] = round(mean([p[3] for p in ph_w]), 4)
+    return res
+
+
+def bench_gla(torch, gsa, ev, w, steps, warmup):
+    import synth
+    inp = synth.gla_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], dtype=w["dtype"], seed=0,
+                           qkv_scale=w["qkv_scale"])
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g"], 2)
+    B, H, T, dk, dv = w["B"], w["H"], w["T"], w["dk"], w["dv"]
+    outs = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    nb = gsa.gla_fwd_workspace_bytes(B, H, T, dk, dv, w["C"], 1, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def call(s, events):
+        i = next(j for j, x in enumerate(sets) if x is s)
+        gsa.gla_fwd(s["q"], s["k"], s["v"], s["g"], tau=w["tau"], out=outs[i], workspace=ws,
+                    events=events)
+
+    wall, ph = time_op(torch, ev, call, sets, steps, warmup)
+    flops, nbytes = gla_alg(B, H, T, dk, dv, w["C"], 2)
+    t_op, t_out = mean([p[3] for p in ph]), mean([p[2] for p in ph])
+    return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_step": round(wall / steps * 1e3, 4),
+            "ms_phases": {"state_maps": round(mean([p[0] for p in ph]), 4),
+                          "scan": round(mean([p[1] for p in ph]), 4), "outputs": round(t_out, 4),
+                          "op": round(t_op, 4)},
+            "alg_tflops": round(flops / (t_op * 1e-3) / 1e12, 2),
+            "mfma_frac_alg": round(flops / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline(nbytes, t_out, "gla_seg_out", "gla_bf16_T4096")}
+
+
+def bench_decode(torch, gsa, ev, w, steps, warmup):
+    import synth
+    from tests.gpu_helpers import to_dev
+    inp = synth.decode_inputs(w["N"], w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
+                              qkv_scale=w["qkv_scale"], state_std=w["state_std"])
+    tok = {n: to_dev(inp[n], torch) for n in "qkvg"}
+    states = [(to_dev(inp["kstate"], torch), to_dev(inp["vstate"], torch)) for _ in range(2)]
+    out = torch.empty((w["N"], w["H"], w["dv"]), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = ev.create(2 * steps)
+    for i in range(warmup):
+        ks, vs = states[i % 2]
+        gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ks, vs = states[i % 2]
+        ev.record(evs[2 * i], stream)
+        gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out)
+        ev.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])
+    units = w["N"] * w["H"]
+    nbytes = units * (4 * w["m"] * (w["dk"] + w["dv"]) + 2 * (2 * w["dk"] + 2 * w["dv"] + w["m"]))
+    r = roofline(nbytes, t, "gsa_decode_kernel", "gsa_decode_N256")
+    return {"value": r["achieved"], "unit": "GB/s", "ms_kernel": round(t, 4),
+            "steps_per_s": round(steps / wall, 1), "tokens_per_s": round(w["N"] * steps / wall, 1),
+            "roofline": r}
+
+
+def cpu_baseline(w, inp, budget_s):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    args = [inp[n].f64 for n in "qkvg"]
+    ref = None
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        ref = oracle.gsa_fwd(*args, tau=w["tau"], want_states=False, nthreads=threads)
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    tokens = w["B"] * w["T"] * runs
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "full %s batch (B=%d H=%d T=%d), %d run(s) in %.1f s, fp64 recurrence, "
+                      "OpenMP over (b,h) units" % ("training-shape", w["B"], w["H"], w["T"], runs, dt)}, ref
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=6, help="input copies rotated through (cache-cold)")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (the workload is one GPU's share; "
+              "nothing here uses collectives). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import slot_memory_sequence_amd as gsa
+    import synth
+    from tests.gpu_helpers import rel_err, to_np
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ev = Events()
+    wname = "gsa_bf16_train_T2048"
+    w = synth.WORKLOADS[wname]
+    log("bench: %s steps=%d warmup=%d sets=%d" % (wname, args.steps, args.warmup, args.sets))
+    main_res = bench_gsa(torch, gsa, ev, w, wname, args.steps, args.warmup, args.sets)
+    log("bench: main done %.3g tokens/s" % main_res["tokens_per_s"])
+
+    comps = {}
+    if not args.no_components:
+        wl = synth.WORKLOADS["gsa_bf16_long_T16384"]
+        r = bench_gsa(torch, gsa, ev, wl, "gsa_bf16_long_T16384", args.steps, args.warmup, 3,
+                      warm_too=False)
+        comps["gsa_bf16_long_T16384"] = {
+            "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(r["ms_per_step"], 4), "ms_phases": r["ms_phases"],
+            "alg_tflops": round(r["alg_tflops"], 2), "mfma_frac_alg": round(r["mfma_frac_alg"], 4),
+            "roofline": r["roofline"], "op_roofline": r["op_roofline"]}
+        del r
+        log("bench: long-context done")
+        comps["gla_bf16_T4096"] = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"],
+                                            args.steps, args.warmup)
+        log("bench: gla done")
+        comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
+                                                args.steps, args.warmup)
+        log("bench: decode done")
+        torch.cuda.empty_cache()
+
+    cpu, err = None, None
+    if not args.no_cpu:
+        cpu, ref = cpu_baseline(w, main_res["inp"], args.cpu_seconds)
+        err = rel_err(to_np(main_res["out"]), ref["o"])
+        log("bench: cpu baseline done, parity rel err %.3e" % err)
+
+    line = {
+        "metric": "GSA fwd tokens/s (B*T/s) at T=2048; % bf16 MFMA peak; decode HBM GB/s",
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q,k,v scaled 1/sqrt(128), gate logits N(0,1))",
+        "config": {"workload": wname, "B": w["B"], "H": w["H"], "T": w["T"], "dk": w["dk"],
+                   "dv": w["dv"], "m": w["m"], "C": w["C"], "tau": w["tau"],
+                   "input_sets_rotated": main_res["input_sets"]},
+        "roofline": main_res["roofline"],
+        "op_roofline": main_res["op_roofline"],
+        "ms_phases": main_res["ms_phases"],
+        "alg_tflops": round(main_res["alg_tflops"], 2),
+        "mfma_frac_alg": round(main_res["mfma_frac_alg"], 4),
+        "warm_cache_tokens_per_s": round(main_res.get("warm_tokens_per_s", 0.0), 1),
+        "decode_GBps": comps.get("gsa_decode_N256", {}).get("value"),
+        "components": comps,
+        "cpu_baseline": cpu,
+        "parity_rel_err": None if err is None else float("%.3e" % err),
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -108,6 +108,26 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
             void* workspace, size_t workspace_bytes, int chunks_per_segment, void* stream);
 
 /*
+ * gsa_fwd / gla_fwd with timing hooks, for benchmarks and profilers.  events
+ * is NULL or an array of 4 hipEvent_t (each entry nullable), recorded on the
+ * stream at the phase boundaries of the launch sequence:
+ *   [0] before the segment state-map pass, [1] before the segment scan,
+ *   [2] before the output pass, [3] after the output pass.
+ * When a problem needs a single segment the first two passes are skipped and
+ * [0]..[2] are recorded back to back.  Everything else is as for the plain
+ * entry points (which are these with events = NULL).
+ */
+int gsa_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* k0,
+                   const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T,
+                   int dk, int dv, int m, int C, float tau, int dtype, void* workspace,
+                   size_t workspace_bytes, int chunks_per_segment, void* stream,
+                   void* const* events);
+int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* s0,
+                   void* o, float* s_final, int B, int H, int T, int dk, int dv, int C, float tau,
+                   int dtype, void* workspace, size_t workspace_bytes, int chunks_per_segment,
+                   void* stream, void* const* events);
+
+/*
  * One recurrent GSA step (Sec. 3.2 recurrent form) for N sequences x H heads.
  *   q, k     [N,H,dk]    dtype
  *   v        [N,H,dv]    dtype

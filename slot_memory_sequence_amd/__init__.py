@@ -11,6 +11,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# Load PyTorch's HIP runtime first: libgsa links libamdhip64.so.7 by soname, so
+# the process then holds exactly one HIP runtime and torch's streams, events
+# and allocations are valid handles for the library.
+import torch as _torch_rt  # noqa: F401
+
 __all__ = ["lib", "gsa_fwd", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH",
            "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
            "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
@@ -38,6 +43,10 @@ lib.gsa_fwd.restype = _I
 lib.gsa_fwd.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _P]
 lib.gla_fwd.restype = _I
 lib.gla_fwd.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _P]
+lib.gsa_fwd_events.restype = _I
+lib.gsa_fwd_events.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _P, _P]
+lib.gla_fwd_events.restype = _I
+lib.gla_fwd_events.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_decode_step.restype = _I
 lib.gsa_decode_step.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P]
 
@@ -103,6 +112,14 @@ def _check(t, name, dtype=None):
         raise TypeError("%s must be %s" % (name, dtype))
 
 
+def _events(events):
+    """None, or 4 raw hipEvent_t handles (ints or None) -> void*[4]."""
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * 4)(*[None if e is None else int(e) for e in events])
+    return ctypes.cast(arr, ctypes.c_void_p)
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -112,7 +129,7 @@ def _stream(stream):
 
 def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
             chunks_per_segment=0, out=None, k_final=None, v_final=None, workspace=None,
-            stream=None):
+            stream=None, events=None):
     """Chunkwise GSA forward.  q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m] (gate
     logits); optional float32 initial slot states k0 [B,H,m,dk], v0 [B,H,m,dv].
     Returns (o, k_final, v_final) -- the finals are None unless final_state."""
@@ -136,17 +153,18 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
         raise ValueError("invalid problem size")
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.gsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
-                     _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
-                     _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                     int(chunks_per_segment), _stream(stream))
+    st = lib.gsa_fwd_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
+                            _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
+                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            int(chunks_per_segment), _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_fwd", st)
     return out, k_final, v_final
 
 
 def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
-            chunks_per_segment=0, out=None, s_final=None, workspace=None, stream=None):
+            chunks_per_segment=0, out=None, s_final=None, workspace=None, stream=None,
+            events=None):
     """Chunkwise GLA forward.  q, k, g [B,H,T,dk]; v [B,H,T,dv]; optional float32
     initial state s0 [B,H,dk,dv].  Returns (o, s_final or None)."""
     torch = _torch()
@@ -163,10 +181,10 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
     nbytes = gla_fwd_workspace_bytes(B, H, T, dk, dv, C, dt, chunks_per_segment)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out), _ptr(s_final),
-                     B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
-                     0 if workspace is None else workspace.numel(), int(chunks_per_segment),
-                     _stream(stream))
+    st = lib.gla_fwd_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out),
+                            _ptr(s_final), B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                            _stream(stream), _events(events))
     if st:
         raise GsaError("gla_fwd", st)
     return out, s_final

@@ -113,6 +113,14 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
             const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk, int dv, int m,
             int C, float tau, int dtype, void* workspace, size_t workspace_bytes, int cps,
             void* stream) {
+  return gsa_fwd_events(q, k, v, g, k0, v0, o, kf, vf, B, H, T, dk, dv, m, C, tau, dtype,
+                        workspace, workspace_bytes, cps, stream, nullptr);
+}
+
+int gsa_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* k0,
+                   const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk,
+                   int dv, int m, int C, float tau, int dtype, void* workspace,
+                   size_t workspace_bytes, int cps, void* stream, void* const* events) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !(tau > 0.f) ||
       !std::isfinite(tau) || !dtype_ok(dtype))
     return GSA_ERR_SHAPE;
@@ -159,6 +167,7 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
                                   (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
                        : nullptr;
   a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
+  a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();
@@ -167,6 +176,14 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
 int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
             float* sf, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
             void* workspace, size_t workspace_bytes, int cps, void* stream) {
+  return gla_fwd_events(q, k, v, g, s0, o, sf, B, H, T, dk, dv, C, tau, dtype, workspace,
+                        workspace_bytes, cps, stream, nullptr);
+}
+
+int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* s0,
+                   void* o, float* sf, int B, int H, int T, int dk, int dv, int C, float tau,
+                   int dtype, void* workspace, size_t workspace_bytes, int cps, void* stream,
+                   void* const* events) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || C < 1 || !(tau > 0.f) ||
       !std::isfinite(tau) || !dtype_ok(dtype))
     return GSA_ERR_SHAPE;
@@ -207,6 +224,7 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
                                   (((size_t)units * P * dk * dv * 4 + 255) & ~(size_t)255))
                        : nullptr;
   a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
+  a.events = events;
   (void)hipGetLastError();
   if (gsa::gla_dispatch(dtype, dk, dv, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();

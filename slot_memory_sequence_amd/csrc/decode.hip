@@ -179,6 +179,10 @@ __global__ void state_copy_kernel(float* __restrict__ dst, const float* __restri
   for (; i < n; i += stride) dst[i] = src ? src[i] : 0.f;
 }
 
+void record_event(void* const* events, int i, void* stream) {
+  if (events && events[i]) (void)hipEventRecord((hipEvent_t)events[i], (hipStream_t)stream);
+}
+
 void state_copy(float* dst, const float* src, size_t n, void* stream) {
   if (!dst || n == 0 || dst == src) return;
   size_t blocks = (n + 255) / 256;

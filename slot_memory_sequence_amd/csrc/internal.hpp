@@ -15,6 +15,7 @@ struct GsaLaunch {
   int B, H, T, chunks_per_seg;
   float tau;
   void* stream;
+  void* const* events;  // nullable: 4 hipEvent_t recorded at the phase boundaries
 };
 
 struct GlaLaunch {
@@ -26,7 +27,11 @@ struct GlaLaunch {
   int B, H, T, chunks_per_seg;
   float tau;
   void* stream;
+  void* const* events;  // nullable: 4 hipEvent_t recorded at the phase boundaries
 };
+
+// record events[i] on the stream when the event array and entry are non-null
+void record_event(void* const* events, int i, void* stream);
 
 struct DecodeLaunch {
   const void *q, *k, *v, *g;
