@@ -244,7 +244,8 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
     wall = time.perf_counter() - t0
     t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])
     units = w["N"] * w["H"]
-    nbytes = units * (4 * w["m"] * (w["dk"] + w["dv"]) + 2 * (2 * w["dk"] + 2 * w["dv"] + w["m"]))
+    # both fp32 states read and written once, plus the bf16 token I/O (q, k, v, g in, o out)
+    nbytes = units * (2 * 4 * w["m"] * (w["dk"] + w["dv"]) + 2 * (2 * w["dk"] + 2 * w["dv"] + w["m"]))
     r = roofline(nbytes, t, "gsa_decode_kernel", "gsa_decode_N256")
     return {"value": r["achieved"], "unit": "GB/s", "ms_kernel": round(t, 4),
             "steps_per_s": round(steps / wall, 1), "tokens_per_s": round(w["N"] * steps / wall, 1),

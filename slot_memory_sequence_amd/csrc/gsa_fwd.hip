@@ -757,11 +757,9 @@ constexpr bool gsa_fits() {
   }
 
 // Returns: query -> LDS bytes (>0) or -1 if unsupported; launch -> 0 or -1.
+// bf16 inputs take the kernels of gsa_fwd_bf16.hip; this file serves float32.
 int gsa_dispatch(int dt, int dk, int dv, int m, const GsaLaunch* a, bool query) {
-  GSA_CASE(bf16_t, 1, 128, 128, 64)
-  GSA_CASE(bf16_t, 1, 128, 128, 32)
-  GSA_CASE(bf16_t, 1, 64, 64, 64)
-  GSA_CASE(bf16_t, 1, 64, 64, 32)
+  if (dt == 1) return gsa_dispatch_bf16(dk, dv, m, a, query);
   GSA_CASE(float, 0, 64, 64, 64)
   GSA_CASE(float, 0, 64, 64, 32)
   GSA_CASE(float, 0, 64, 64, 16)

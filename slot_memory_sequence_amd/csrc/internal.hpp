@@ -45,6 +45,7 @@ struct DecodeLaunch {
 // query == true: return the phase-C LDS bytes (> 0) if the shape is compiled, else -1.
 // query == false: enqueue the launches and return 0, or -1 if not compiled.
 int gsa_dispatch(int dtype, int dk, int dv, int m, const GsaLaunch* a, bool query);
+int gsa_dispatch_bf16(int dk, int dv, int m, const GsaLaunch* a, bool query);
 int gla_dispatch(int dtype, int dk, int dv, const GlaLaunch* a, bool query);
 int decode_dispatch(int dtype, int dk, int dv, int m, const DecodeLaunch* a, bool query);
 // copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
