@@ -271,6 +271,41 @@ def cpu_baseline(w, inp, budget_s):
                       "OpenMP over (b,h) units" % ("training-shape", w["B"], w["H"], w["T"], runs, dt)}, ref
 
 
+def copy_calibration(torch, ev, steps):
+    """A plain device copy of known size (512 MiB read + 512 MiB written), the
+    reference for scaling the profiler's FETCH_SIZE / WRITE_SIZE counters."""
+    n = 512 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = ev.create(2 * steps)
+    for i in range(steps):
+        ev.record(evs[2 * i], stream)
+        dst.copy_(src)
+        ev.record(evs[2 * i + 1], stream)
+    torch.cuda.synchronize()
+    t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])
+    return {"workload": "copy_512MiB", "bytes_read": n, "bytes_written": n, "ms": round(t, 4),
+            "GBps": round(2 * n / (t * 1e-3) / 1e9, 1)}
+
+
+def run_only(args, torch, gsa, ev):
+    import synth
+    if args.only == "copy":
+        return copy_calibration(torch, ev, args.steps)
+    if args.only == "gsa":
+        r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], "gsa_bf16_train_T2048",
+                      args.steps, args.warmup, args.sets, warm_too=False)
+        return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "long":
+        r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
+                      args.steps, args.warmup, 3, warm_too=False)
+        return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "gla":
+        return bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"], args.steps, args.warmup)
+    return bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"], args.steps, args.warmup)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +315,8 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy"], default=None,
+                    help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU (the workload is one GPU's share; "
@@ -296,6 +333,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ev = Events()
+    if args.only is not None:
+        print(json.dumps(run_only(args, torch, gsa, ev)), flush=True)
+        return
     wname = "gsa_bf16_train_T2048"
     w = synth.WORKLOADS[wname]
     log("bench: %s steps=%d warmup=%d sets=%d" % (wname, args.steps, args.warmup, args.sets))

@@ -42,7 +42,8 @@ namespace bfk {
 constexpr int C = 64;   // chunk length
 constexpr int NW = 8;   // waves per workgroup
 constexpr int NT = NW * 64;
-constexpr float kFastMinLogDecay = -40.f;  // log of the smallest whole-chunk decay the factors allow
+// log2 of the smallest whole-chunk decay the factorised chunk form allows (e^-40)
+constexpr float kFastMinLog2Decay = -57.70780163555854f;
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
@@ -99,34 +100,39 @@ struct OutLds {
   static constexpr int oK = oQ + C * LDQ * 2;
   static constexpr int oV = oK + C * LDQ * 2;
   static constexpr int oR = oV + C * LDV * 2;          // region used differently by the two paths
-  // fast path
-  static constexpr int oW = oR;                        // bf16 copy of W [M][DK+DV]
-  static constexpr int oX = oW + M * LDW * 2;          // X [C][M] bf16
-  static constexpr int oZ = oX + C * LDX * 2;          // Z [C][M] bf16
-  static constexpr int oE = oZ + C * LDX * 2;          // E [C][M] fp32
-  static constexpr int szFast = oE + C * LDE * 4 - oR;
+  // fast path: bf16 copy of W, then two sets of chunk factors (this chunk's
+  // and the next one's, computed while this chunk is processed)
+  static constexpr int oW = oR;                        // bf16 W [M][DK+DV]
+  static constexpr int oF = oW + M * LDW * 2;
+  static constexpr int fX = 0;                         // X [C][M] bf16
+  static constexpr int fZ = fX + C * LDX * 2;          // Z [C][M] bf16
+  static constexpr int fE = fZ + C * LDX * 2;          // E [C][M] fp32
+  static constexpr int szF = fE + C * LDE * 4;         // one factor set
+  static constexpr int szFast = oF + 2 * szF - oR;
   // exact-recurrence path
   static constexpr int oWf = oR;                       // fp32 W [M][DK+DV]
   static constexpr int oLa = oWf + M * (DK + DV) * 4;  // log alpha [C][M] fp32
   static constexpr int oZs = oLa + C * M * 4;          // slot scores [M] fp32
   static constexpr int oOp = oZs + M * 4;              // output partials [NW][DV] fp32
   static constexpr int szSlow = oOp + NW * DV * 4 - oR;
-  static constexpr int oDec = oR + (szFast > szSlow ? szFast : szSlow);  // [M] fp32
-  static constexpr int total = oDec + M * 4;
-  static_assert(oK % 16 == 0 && oV % 16 == 0 && oW % 16 == 0 && oX % 16 == 0 && oZ % 16 == 0 &&
-                    oE % 16 == 0 && oLa % 16 == 0 && oOp % 16 == 0 && oDec % 16 == 0,
+  static constexpr int oDec = oR + (szFast > szSlow ? szFast : szSlow);  // 2 x [M] fp32
+  static constexpr int total = oDec + 2 * M * 4;
+  static_assert(oK % 16 == 0 && oV % 16 == 0 && oW % 16 == 0 && oF % 16 == 0 && szF % 16 == 0 &&
+                    fZ % 16 == 0 && fE % 16 == 0 && oLa % 16 == 0 && oOp % 16 == 0 && oDec % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
 };
 
 template <int DK, int DV, int M>
-struct StateLds {
+struct StateLds {  // two buffers of everything a chunk needs (software pipeline)
   static constexpr int PAD = 8;
   static constexpr int LDQ = DK + PAD, LDV = DV + PAD, LDX = M + PAD;
   static constexpr int oK = 0;
   static constexpr int oV = oK + C * LDQ * 2;
   static constexpr int oZ = oV + C * LDV * 2;
   static constexpr int oDec = oZ + C * LDX * 2;
-  static constexpr int total = oDec + M * 4;
+  static constexpr int szBuf = oDec + M * 4;
+  static constexpr int total = 2 * szBuf;
+  static_assert(oV % 16 == 0 && oZ % 16 == 0 && oDec % 16 == 0 && szBuf % 16 == 0, "alignment");
 };
 
 // ------------------------------------------------------- global tile I/O
@@ -137,23 +143,22 @@ struct Tile {
   static constexpr int NV = C * VPR / NT;
   static_assert(NV >= 1 && (C * VPR) % NT == 0, "tile/thread mismatch");
   uint4 r[NV];
-  // rows >= rows_valid (>= 1) read the last valid row and are then zeroed, so
-  // the loads need no branches
+  // rows >= rows_valid (>= 1) read the last valid row; store() zeroes them, so
+  // the loads are not waited for until the tile is stored
   __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int rows_valid, int tid) {
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       const int idx = tid + NT * i, row = idx / VPR, cv = idx % VPR;
-      const int rr = min(row, rows_valid - 1);
-      const uint4 x = *reinterpret_cast<const uint4*>(base + rr * D + cv * 8);
-      const bool ok = row < rows_valid;
-      r[i] = make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
+      r[i] = *reinterpret_cast<const uint4*>(base + min(row, rows_valid - 1) * D + cv * 8);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* dst, int ld, int tid) const {
+  __device__ __forceinline__ void store(bf16_t* dst, int ld, int rows_valid, int tid) const {
 #pragma unroll
     for (int i = 0; i < NV; i++) {
       const int idx = tid + NT * i, row = idx / VPR, cv = idx % VPR;
-      *reinterpret_cast<uint4*>(dst + row * ld + cv * 8) = r[i];
+      const bool ok = row < rows_valid;
+      *reinterpret_cast<uint4*>(dst + row * ld + cv * 8) =
+          make_uint4(ok ? r[i].x : 0u, ok ? r[i].y : 0u, ok ? r[i].z : 0u, ok ? r[i].w : 0u);
     }
   }
 };
@@ -161,95 +166,151 @@ struct Tile {
 // SPT gate logits of one token row (SPT = 4 or 8 bf16 = 8 or 16 bytes).
 template <int SPT>
 struct GateRow {
-  static_assert(SPT == 4 || SPT == 8, "gate row width");
-  typedef typename std::conditional<SPT == 8, uint4, uint2>::type V;
-  V r;
-  // p must point at a readable row even when !valid (the caller clamps it)
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ p, bool valid) {
-    const V x = *reinterpret_cast<const V*>(p);
-    r = valid ? x : V{};
+  static_assert(SPT >= 2 && SPT % 2 == 0, "gate row width");
+  uint32_t r[SPT / 2];
+  // p must point at a readable row, 4-byte aligned (the caller clamps the
+  // row); rows past the end are masked by the consumer
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+    if constexpr (SPT % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < SPT / 8; i++) {
+        const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+        r[4 * i] = x.x; r[4 * i + 1] = x.y; r[4 * i + 2] = x.z; r[4 * i + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPT / 2; i++) r[i] = reinterpret_cast<const uint32_t*>(p)[i];
+    }
   }
-  __device__ __forceinline__ float at(int s) const { return bf2f(reinterpret_cast<const bf16_t*>(&r)[s]); }
+  __device__ __forceinline__ float at(int s) const {
+    const uint32_t w = r[s >> 1];
+    return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  // an opaque redefinition: uses of the row (and the wait for its load) stay
+  // after this point
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int i = 0; i < SPT / 2; i++) asm volatile("" : "+v"(r[i]));
+  }
 };
 
-// Gates of SPT slots for token row = lane of a chunk, for the output pass:
-// w = 1 - alpha and G = chunk-local inclusive cumulative sum of log alpha (one
-// wave scan).  E_j = exp(G_j); the decay from token r to the chunk end is
-// exp(G_C - G_r).  Rows past the end of the sequence are identity steps
-// (log alpha = 0, write 0).  Only chunks with G_C >= -40 in every slot use
-// these factors, so every exponential below stays finite there.
+// ------------------------------------------------------------- gate math
+// All gate quantities are kept in base-2 logarithms so that the hardware
+// exp2 / log2 instructions apply directly.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float x) {  // DPP lane move, 0 where no source lane
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sums over the 64 lanes of a wave, for N independent
+// values per lane, step-major so that every step issues N independent
+// operations: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the last
+// lane of rows 0 / 2 into rows 1 / 3 and the last lane of row 1 into rows 2, 3.
+template <int N>
+__device__ __forceinline__ void wave_prefix_sums(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x111, 0xf>(x[i]);  // row_shr:1
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x112, 0xf>(x[i]);  // row_shr:2
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x114, 0xf>(x[i]);  // row_shr:4
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x118, 0xf>(x[i]);  // row_shr:8
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x142, 0xa>(x[i]);  // row_bcast:15 into rows 1, 3
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x143, 0xc>(x[i]);  // row_bcast:31 into rows 2, 3
+}
+
+// Value of the previous lane of the wave (a whole-wave shift by one lane);
+// lane 0 gets `first`.
+__device__ __forceinline__ float prev_lane(float x, float first) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x), 0x138, 0xf, 0xf, false));
+}
+
+// log2 alpha = log2(sigmoid(g)) / tau, clamped at -115 (alpha ~ 2.4e-35) so that
+// g = -inf gives a finite value.
+__device__ __forceinline__ float gate_log2(float g, float inv_tau) {
+  const float t = g * 1.4426950408889634f;  // g / ln 2
+  const float ls2 = fminf(t, 0.f) - __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(t)));
+  return fmaxf(ls2 * inv_tau, -115.f);
+}
+
+// Output-pass factors of SPT slots for token row = lane of a chunk, with
+// G = chunk-local inclusive cumulative sum of log2 alpha:
+//   E_j = exp2(G_j),  X_j = (1 - alpha_j) / E_j = 1/E_j - 1/E_{j-1}.
+// Rows past the end of the sequence are identity steps (log alpha = 0).
 template <int SPT>
 struct LogGates {
-  float w[SPT], G[SPT];
-  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau, int lane) {
+  float G[SPT], E[SPT], X[SPT];
+  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
+#pragma unroll
+    for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+    wave_prefix_sums<SPT>(G);
 #pragma unroll
     for (int s = 0; s < SPT; s++) {
-      const float x = g.at(s);
-      const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
-      G[s] = valid ? la : 0.f;
-      w[s] = valid ? -expm1f(la) : 0.f;
+      E[s] = __builtin_amdgcn_exp2f(G[s]);
+      X[s] = __builtin_amdgcn_exp2f(-G[s]);
     }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-      for (int s = 0; s < SPT; s++) {
-        const float up = __shfl_up(G[s], off, 64);
-        if (lane >= off) G[s] += up;
-      }
-    }
+    for (int s = 0; s < SPT; s++) X[s] -= prev_lane(X[s], 1.f);
   }
 };
 
-// Gates for the state-map pass: w = 1 - alpha and the exclusive suffix product
-// S_r = prod_{i>r} alpha_i (one wave scan, exact also for alpha = 0), plus the
-// whole-chunk product.
+// State-map factors: the decay from token r to the chunk end
+// S_r = prod_{i>r} alpha_i = exp2(G_C - G_r), the write term
+// Z_r = (1 - alpha_r) S_r = S_r - S_{r-1}, and the whole-chunk decay.
 template <int SPT>
 struct SuffixGates {
-  float w[SPT], S[SPT], dec[SPT];
-  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau, int lane) {
-    float a[SPT];
+  float Z[SPT], dec[SPT];
+  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
+    float G[SPT];
+#pragma unroll
+    for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+    wave_prefix_sums<SPT>(G);
 #pragma unroll
     for (int s = 0; s < SPT; s++) {
-      float av, wv;
-      gate_alpha_w(g.at(s), inv_tau, av, wv);
-      a[s] = valid ? av : 1.f;
-      w[s] = valid ? wv : 0.f;
-      S[s] = a[s];
+      const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
+      dec[s] = __builtin_amdgcn_exp2f(tot);
+      Z[s] = __builtin_amdgcn_exp2f(tot - G[s]);
     }
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-      for (int s = 0; s < SPT; s++) {
-        const float dn = __shfl_down(S[s], off, 64);
-        if (lane + off < 64) S[s] *= dn;
-      }
-    }
-    // S is now the inclusive suffix product; lane 0 holds the whole product
-#pragma unroll
-    for (int s = 0; s < SPT; s++) {
-      dec[s] = __shfl(S[s], 0, 64);
-      const float nx = __shfl_down(S[s], 1, 64);
-      S[s] = (lane == 63) ? 1.f : nx;
-    }
+    for (int s = 0; s < SPT; s++) Z[s] -= prev_lane(Z[s], dec[s]);
   }
 };
 
-// SPT consecutive floats -> SPT bf16 stored as one 8- or 16-byte vector
+// SPT consecutive floats -> bf16 / fp32 rows in LDS; dst is 4-byte (bf16) /
+// 8-byte (fp32) aligned at least, 16-byte when SPT is a multiple of 8 / 4.
 template <int SPT>
 __device__ __forceinline__ void store_bf16_row(bf16_t* dst, const float* v) {
-  if constexpr (SPT == 8) {
-    f32x8 x = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
-    *reinterpret_cast<bf16x8*>(dst) = __builtin_convertvector(x, bf16x8);
+  if constexpr (SPT % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < SPT; i += 8) {
+      f32x8 x = {v[i], v[i + 1], v[i + 2], v[i + 3], v[i + 4], v[i + 5], v[i + 6], v[i + 7]};
+      *reinterpret_cast<bf16x8*>(dst + i) = __builtin_convertvector(x, bf16x8);
+    }
   } else {
-    f32x4 x = {v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<bf16x4v*>(dst) = __builtin_convertvector(x, bf16x4v);
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+#pragma unroll
+    for (int i = 0; i < SPT; i += 2) {
+      f32x2 x = {v[i], v[i + 1]};
+      *reinterpret_cast<bf16x2*>(dst + i) = __builtin_convertvector(x, bf16x2);
+    }
   }
 }
 template <int SPT>
 __device__ __forceinline__ void store_f32_row(float* dst, const float* v) {
+  if constexpr (SPT % 4 == 0) {
 #pragma unroll
-  for (int s = 0; s < SPT; s += 4)
-    *reinterpret_cast<float4*>(dst + s) = make_float4(v[s], v[s + 1], v[s + 2], v[s + 3]);
+    for (int s = 0; s < SPT; s += 4)
+      *reinterpret_cast<float4*>(dst + s) = make_float4(v[s], v[s + 1], v[s + 2], v[s + 3]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < SPT; s += 2) *reinterpret_cast<float2*>(dst + s) = make_float2(v[s], v[s + 1]);
+  }
 }
 
 // ------------------------------------------------------------ state tiles
@@ -365,15 +426,46 @@ struct StateTiles {
   }
 };
 
+// ------------------------------------------------------ chunk factors
+// SPT slots from slot0 of one chunk (token row = lane): X = (1-alpha)/E,
+// Z = (1-alpha) prod_{i>r} alpha_i and E into one factor set, the whole-chunk
+// decay into dec.  Returns whether any of these slots decays below the range
+// of the factorised form in this chunk.
+template <int SPT, int LDX, int LDE>
+__device__ __forceinline__ bool chunk_factors(const GateRow<SPT>& g, bool valid, float inv_tau,
+                                              int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
+                                              float* sDec) {
+  LogGates<SPT> gt;
+  gt.compute(g, valid, inv_tau);
+  bool small = false;
+  float z[SPT];
+#pragma unroll
+  for (int s = 0; s < SPT; s++) {
+    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.G[s]), 63));
+    small |= !(gc >= kFastMinLog2Decay);
+    const float dc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.E[s]), 63));
+    z[s] = gt.X[s] * dc;
+    if (lane == 0) sDec[slot0 + s] = dc;
+  }
+  store_bf16_row<SPT>(sX + lane * LDX + slot0, gt.X);
+  store_bf16_row<SPT>(sZ + lane * LDX + slot0, z);
+  store_f32_row<SPT>(sE + lane * LDE + slot0, gt.E);
+  return small;
+}
+
 // -------------------------------------------------------- pass-wave chunk
-// Token rows 16J..16J+15 of the chunk: both passes, the slot softmax and the
-// output rows.  Reads sQ, sK, sV, sX, sE and the bf16 state copy sW.
-template <int DK, int DV, int M>
-__device__ __forceinline__ void pass_chunk(int J, int lane, const bf16_t* sQ, const bf16_t* sK,
+// Token rows 16J..16J+15 of the chunk: pass 1, the slot softmax, pass 2 and the
+// output rows.  Reads sQ, sK, sV, sX, sE and the bf16 state copy sW.  J is a
+// template parameter so that every loop is static and independent
+// accumulators can be interleaved.
+template <int DK, int DV, int M, int J>
+__device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf16_t* sK,
                                            const bf16_t* sV, const bf16_t* sW, const bf16_t* sX,
                                            const float* sE, bf16_t* __restrict__ orow, int rv) {
   using Lds = OutLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, NP = M / 32, NVT = DV / 16;
+  constexpr int NR = J + 1;         // score row tiles r <= j
+  constexpr int NPR = J / 2 + 1;    // r-tile pairs
   const int L = lane & 15, g = lane >> 4;
   const int j = 16 * J + L;  // this lane's token column
 
@@ -385,36 +477,38 @@ __device__ __forceinline__ void pass_chunk(int J, int lane, const bf16_t* sQ, co
   // A^T[r][j] = k_r . q_j for row tiles R <= J, causal mask on the diagonal tile
   f32x4 at[4];
 #pragma unroll
-  for (int R = 0; R < 4; R++) {
-    at[R] = zero4();
-    if (R <= J) {
+  for (int R = 0; R < 4; R++) at[R] = zero4();
 #pragma unroll
-      for (int s = 0; s < KQ; s++) at[R] = mma(ld_row(sK, Lds::LDQ, 16 * R, 32 * s, lane), qf[s], at[R]);
-      if (R == J) {
+  for (int s = 0; s < KQ; s++)
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-          if (4 * g + i > L) at[R][i] = 0.f;
-      }
-    }
-  }
-  const bf16x8 af0 = pack8(at[0], at[1]);
-  const bf16x8 af1 = pack8(at[2], at[3]);
-  const bool two = J >= 2;  // second r-pair needed
+    for (int R = 0; R < NR; R++) at[R] = mma(ld_row(sK, Lds::LDQ, 16 * R, 32 * s, lane), qf[s], at[R]);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (4 * g + i > L) at[J][i] = 0.f;
+  bf16x8 af[2];
+  af[0] = pack8(at[0], at[1]);
+  af[1] = pack8(at[2], at[3]);
 
   // pass 1: o'^T[c][j] = E[j][c] (Wk[c].q_j + sum_r X[r][c] A^T[r][j])
   f32x4 op[MT];
-  f32x4 ev[MT];
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) op[ct] = zero4();
+#pragma unroll
+  for (int s = 0; s < KQ; s++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) op[ct] = mma(ld_row(sW, Lds::LDW, 16 * ct, 32 * s, lane), qf[s], op[ct]);
+#pragma unroll
+  for (int pr = 0; pr < NPR; pr++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+      op[ct] = mma(ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), af[pr], op[ct]);
 #pragma unroll
   for (int ct = 0; ct < MT; ct++) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int s = 0; s < KQ; s++) acc = mma(ld_row(sW, Lds::LDW, 16 * ct, 32 * s, lane), qf[s], acc);
-    acc = mma(ld_col(sX, Lds::LDX, 16 * ct, 4 * g, 16 + 4 * g, lane), af0, acc);
-    if (two) acc = mma(ld_col(sX, Lds::LDX, 16 * ct, 32 + 4 * g, 48 + 4 * g, lane), af1, acc);
     const float4 e = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 16 * ct + 4 * g);
-    ev[ct] = f32x4{e.x, e.y, e.z, e.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) op[ct][i] = acc[i] * ev[ct][i];
+    op[ct][0] *= e.x;
+    op[ct][1] *= e.y;
+    op[ct][2] *= e.z;
+    op[ct][3] *= e.w;
   }
 
   // slot softmax of token j: over (ct, i) in-lane and the four lane groups
@@ -430,7 +524,7 @@ __device__ __forceinline__ void pass_chunk(int J, int lane, const bf16_t* sQ, co
   for (int ct = 0; ct < MT; ct++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      op[ct][i] = __expf(op[ct][i] - mx);
+      op[ct][i] = __builtin_amdgcn_exp2f((op[ct][i] - mx) * 1.4426950408889634f);
       sm += op[ct][i];
     }
   sm += __shfl_xor(sm, 16, 64);
@@ -440,45 +534,57 @@ __device__ __forceinline__ void pass_chunk(int J, int lane, const bf16_t* sQ, co
   bf16x8 sb[NP];
 #pragma unroll
   for (int p = 0; p < NP; p++) {
-    f32x4 a, b;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      a[i] = op[2 * p][i] * inv * ev[2 * p][i];
-      b[i] = op[2 * p + 1][i] * inv * ev[2 * p + 1][i];
-    }
+    const float4 ea = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 4 * g);
+    const float4 eb = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 16 + 4 * g);
+    const f32x4 a = {op[2 * p][0] * inv * ea.x, op[2 * p][1] * inv * ea.y, op[2 * p][2] * inv * ea.z,
+                     op[2 * p][3] * inv * ea.w};
+    const f32x4 b = {op[2 * p + 1][0] * inv * eb.x, op[2 * p + 1][1] * inv * eb.y,
+                     op[2 * p + 1][2] * inv * eb.z, op[2 * p + 1][3] * inv * eb.w};
     sb[p] = pack8(a, b);
   }
 
   // pass 2 scores: A2^T[r][j] = sum_c X[r][c] (s*E)[j][c], r tiles R <= J
   f32x4 a2[4];
 #pragma unroll
-  for (int R = 0; R < 4; R++) {
-    a2[R] = zero4();
-    if (R <= J) {
+  for (int R = 0; R < 4; R++) a2[R] = zero4();
 #pragma unroll
-      for (int p = 0; p < NP; p++)
-        a2[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], a2[R]);
-      if (R == J) {
+  for (int p = 0; p < NP; p++)
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-          if (4 * g + i > L) a2[R][i] = 0.f;
-      }
-    }
-  }
-  const bf16x8 a2f0 = pack8(a2[0], a2[1]);
-  const bf16x8 a2f1 = pack8(a2[2], a2[3]);
+    for (int R = 0; R < NR; R++)
+      a2[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], a2[R]);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (4 * g + i > L) a2[J][i] = 0.f;
+  bf16x8 a2f[2];
+  a2f[0] = pack8(a2[0], a2[1]);
+  a2f[1] = pack8(a2[2], a2[3]);
 
-  // o^T[n][j] = sum_c Wv[c][n] (s*E)[j][c] + sum_r V[r][n] A2^T[r][j]
+  // o^T[n][j] = sum_c Wv[c][n] (s*E)[j][c] + sum_r V[r][n] A2^T[r][j], in
+  // groups of four column tiles
   const bool store = j < rv;
+  constexpr int NG = NVT < 4 ? NVT : 4;
 #pragma unroll
-  for (int nt = 0; nt < NVT; nt++) {
-    f32x4 acc = zero4();
+  for (int n0 = 0; n0 < NVT; n0 += NG) {
+    f32x4 acc[NG];
+#pragma unroll
+    for (int u = 0; u < NG; u++) acc[u] = zero4();
 #pragma unroll
     for (int p = 0; p < NP; p++)
-      acc = mma(ld_col(sW + DK, Lds::LDW, 16 * nt, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], acc);
-    acc = mma(ld_col(sV, Lds::LDV, 16 * nt, 4 * g, 16 + 4 * g, lane), a2f0, acc);
-    if (two) acc = mma(ld_col(sV, Lds::LDV, 16 * nt, 32 + 4 * g, 48 + 4 * g, lane), a2f1, acc);
-    if (store) *reinterpret_cast<bf16x4v*>(orow + (size_t)j * DV + 16 * nt + 4 * g) = pack4(acc);
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = mma(ld_col(sW + DK, Lds::LDW, 16 * (n0 + u), 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane),
+                     sb[p], acc[u]);
+#pragma unroll
+    for (int pr = 0; pr < NPR; pr++)
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = mma(ld_col(sV, Lds::LDV, 16 * (n0 + u), 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane),
+                     a2f[pr], acc[u]);
+    if (store) {
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        *reinterpret_cast<bf16x4v*>(orow + (size_t)j * DV + 16 * (n0 + u) + 4 * g) = pack4(acc[u]);
+    }
   }
 }
 
@@ -489,12 +595,10 @@ __device__ __forceinline__ void pass_chunk(int J, int lane, const bf16_t* sQ, co
 // The state waves' accumulators W are written to LDS, advanced there by all
 // threads, and read back.  Contains workgroup barriers: all threads call it.
 template <int DK, int DV, int M>
-__device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, const GateRow<M / NW>& pg,
-                                            int rv, float inv_tau, unsigned char* smem,
+__device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
                                             const bf16_t* sQ, const bf16_t* sK, const bf16_t* sV,
                                             bf16_t* __restrict__ orow, int tid) {
   using Lds = OutLds<DK, DV, M>;
-  constexpr int SPT = M / NW;
   constexpr int TPS = NT / M;            // threads per slot
   constexpr int KPT = DK / TPS, VPT = DV / TPS;
   constexpr int SPW = 64 / TPS;          // slots per wave
@@ -507,15 +611,10 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, const G
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
 
-  // state and log-gates to LDS (the region held the fast path's factors and
-  // the bf16 state copy; all of their readers passed the last barrier)
+  // the state to LDS (the region held the fast path's factors and the bf16
+  // state copy, all of whose readers passed the last barrier); the caller has
+  // written this chunk's log alpha to sLa
   if (is_state) W.store_w(sWf, sw, lane);
-#pragma unroll
-  for (int s = 0; s < SPT; s++) {
-    const float x = pg.at(s);
-    const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
-    sLa[lane * M + wv * SPT + s] = lane < rv ? la : 0.f;
-  }
   __syncthreads();
   const int c = tid / TPS, p = tid % TPS;
   float wk[KPT], wvv[VPT];
@@ -576,6 +675,7 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, const G
   for (int i = 0; i < VPT; i++) sWf[c * (DK + DV) + DK + p * VPT + i] = wvv[i];
   __syncthreads();
   if (is_state) W.load_w(sWf, sw, lane);
+  __syncthreads();  // the region is reused by the next factor set
 }
 
 // ------------------------------------------------ phase A: segment maps
@@ -590,10 +690,10 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
   using Lds = StateLds<DK, DV, M>;
   constexpr int SPT = M / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  bf16_t* sK = reinterpret_cast<bf16_t*>(smem + Lds::oK);
-  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Lds::oV);
-  bf16_t* sZ = reinterpret_cast<bf16_t*>(smem + Lds::oZ);
-  float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
+  auto bK = [&](int b) { return reinterpret_cast<bf16_t*>(smem + b * Lds::szBuf + Lds::oK); };
+  auto bV = [&](int b) { return reinterpret_cast<bf16_t*>(smem + b * Lds::szBuf + Lds::oV); };
+  auto bZ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + b * Lds::szBuf + Lds::oZ); };
+  auto bDec = [&](int b) { return reinterpret_cast<float*>(smem + b * Lds::szBuf + Lds::oDec); };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int seg = blockIdx.x, unit = blockIdx.y;
@@ -609,38 +709,47 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
 #pragma unroll
   for (int s = 0; s < SPT; s++) segdec[s] = 1.f;
 
+  // stage chunk ch into buffer b: tiles from registers, gates from the logits
   Tile<DK> pk;
   Tile<DV> pv;
   GateRow<SPT> pg;
-  {
-    const int t0 = c_begin * C, rv = min(C, T_len - t0);
-    pk.load(kb + (size_t)t0 * DK, rv, tid);
-    pv.load(vb + (size_t)t0 * DV, rv, tid);
-    pg.load(gb + (size_t)(t0 + min(lane, rv - 1)) * M, lane < rv);
-  }
-  for (int ch = c_begin; ch < c_end; ch++) {
+  auto load_chunk = [&](int ch, int tid_, int lane_) {
     const int t0 = ch * C, rv = min(C, T_len - t0);
-    pk.store(sK, Lds::LDQ, tid);
-    pv.store(sV, Lds::LDV, tid);
+    pk.load(kb + (size_t)t0 * DK, rv, tid_);
+    pv.load(vb + (size_t)t0 * DV, rv, tid_);
+    pg.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
+  };
+  auto stage_chunk = [&](int ch, int b, bool count, int tid_, int lane_) {
+    const int rv = min(C, T_len - ch * C);
+    pk.store(bK(b), Lds::LDQ, rv, tid_);
+    pv.store(bV(b), Lds::LDV, rv, tid_);
     SuffixGates<SPT> gt;
-    gt.compute(pg, lane < rv, inv_tau, lane);
-    float z[SPT];
+    gt.compute(pg, lane_ < rv, inv_tau);
 #pragma unroll
     for (int s = 0; s < SPT; s++) {
-      z[s] = gt.w[s] * gt.S[s];
-      segdec[s] *= gt.dec[s];
-      if (lane == 0) sDec[wv * SPT + s] = gt.dec[s];
+      segdec[s] *= count ? gt.dec[s] : 1.f;
+      if (lane_ == 0) bDec(b)[wv * SPT + s] = gt.dec[s];
     }
-    store_bf16_row<SPT>(sZ + lane * Lds::LDX + wv * SPT, z);
-    if (ch + 1 < c_end) {
-      const int t1 = t0 + C, rv1 = min(C, T_len - t1);
-      pk.load(kb + (size_t)t1 * DK, rv1, tid);
-      pv.load(vb + (size_t)t1 * DV, rv1, tid);
-      pg.load(gb + (size_t)(t1 + min(lane, rv1 - 1)) * M, lane < rv1);
-    }
+    store_bf16_row<SPT>(bZ(b) + lane_ * Lds::LDX + wv * SPT, gt.Z);
+  };
+
+  load_chunk(c_begin, tid, lane);
+  stage_chunk(c_begin, 0, true, tid, lane);
+  load_chunk(min(c_begin + 1, c_end - 1), tid, lane);
+  __syncthreads();
+  int b = 0;
+  for (int ch = c_begin; ch < c_end; ch++) {
+    int lane_i = lane, tid_i = tid;  // re-derived per chunk (see the output kernel)
+    asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+    // next chunk into the other buffer (the last chunk's again at the end,
+    // into a buffer nobody reads), the one after into registers, this chunk's
+    // state update: all independent until the barrier
+    const int cn = min(ch + 1, c_end - 1);
+    stage_chunk(cn, b ^ 1, ch + 1 < c_end, tid_i, lane_i);
+    load_chunk(min(ch + 2, c_end - 1), tid_i, lane_i);
+    W.carry(bK(b), Lds::LDQ, bV(b), Lds::LDV, bZ(b), Lds::LDX, bDec(b), wv, lane_i);
     __syncthreads();
-    W.carry(sK, Lds::LDQ, sV, Lds::LDV, sZ, Lds::LDX, sDec, wv, lane);
-    __syncthreads();
+    b ^= 1;
   }
   W.store_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), wv, lane);
   if (lane == 0) {
@@ -701,21 +810,28 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              float* __restrict__ vf, int T_len, int S, int P, float inv_tau) {
   using Lds = OutLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
-  constexpr int SPT = M / NW;
-  constexpr int MT = M / 16;
+  // Who computes which slots' gates for the next chunk: each state wave SSL
+  // slots (after its state update), pass waves 0 and 1 PSL slots each (after
+  // their rows, which need the fewest contractions); waves 2 and 3 none.
+  constexpr int SSL = 3 * M / 16, PSL = M / 8;
+  static_assert(4 * SSL + 2 * PSL == M, "gate slots must cover the slots");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + Lds::oQ);
   bf16_t* sK = reinterpret_cast<bf16_t*>(smem + Lds::oK);
   bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Lds::oV);
   bf16_t* sW = reinterpret_cast<bf16_t*>(smem + Lds::oW);
-  bf16_t* sX = reinterpret_cast<bf16_t*>(smem + Lds::oX);
-  bf16_t* sZ = reinterpret_cast<bf16_t*>(smem + Lds::oZ);
-  float* sE = reinterpret_cast<float*>(smem + Lds::oE);
-  float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
+  float* sLa = reinterpret_cast<float*>(smem + Lds::oLa);
+  float* sDec0 = reinterpret_cast<float*>(smem + Lds::oDec);
+  // factor set b: X, Z, E, dec
+  auto fX = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fX); };
+  auto fZ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fZ); };
+  auto fE = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oF + b * Lds::szF + Lds::fE); };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
+  const bool gate_pass = wv < 2;
+  const int slot0 = is_state ? sw * SSL : 4 * SSL + wv * PSL;  // first gate slot (owners)
   const int seg = blockIdx.x, unit = blockIdx.y;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
@@ -723,78 +839,117 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
-  const bf16_t* gb = gg + ub * M + wv * SPT;
+  const bf16_t* gb = gg + ub * M + (is_state || gate_pass ? slot0 : 0);
   bf16_t* ob = oo + ub * DV;
 
-  ST W;
-  if (is_state) {
-    if (P > 1) W.load_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), sw, lane);
-    else W.load_kv(k0 ? k0 + (size_t)unit * M * DK : nullptr, v0 ? v0 + (size_t)unit * M * DV : nullptr, sw, lane);
-    W.store_copy(sW, Lds::LDW, sw, lane);
-  }
+  // Gate logits, one row per owner: loaded at the top of a chunk for the next
+  // chunk (after the exact path, if this chunk takes it, has read this
+  // chunk's row) and used after the contractions, when it has long arrived.
+  struct Rows {
+    GateRow<SSL> s;  // state waves
+    GateRow<PSL> p;  // pass waves 0, 1
+  };
+  Rows gr;
+  auto load_gates = [&](Rows& r, int t0, int rv, int lane_) {
+    const bf16_t* p = gb + (size_t)(t0 + min(lane_, rv - 1)) * M;
+    if (is_state) r.s.load(p);
+    else if (gate_pass) r.p.load(p);
+  };
+  // (the empty asm of pin() keeps the use of the logits, and so the wait for
+  // their load, at the call)
+  auto factors = [&](Rows& r, int rv, int fb, int lane_) -> bool {
+    if (is_state) {
+      r.s.pin();
+      return chunk_factors<SSL, Lds::LDX, Lds::LDE>(r.s, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+                                                     fE(fb), sDec0 + fb * M);
+    }
+    if (gate_pass) {
+      r.p.pin();
+      return chunk_factors<PSL, Lds::LDX, Lds::LDE>(r.p, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+                                                     fE(fb), sDec0 + fb * M);
+    }
+    return false;
+  };
+  auto log_alpha = [&](const Rows& r, int rv, int lane_) {  // natural log, exact path
+    auto put = [&](float x, int s) {
+      const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
+      sLa[lane_ * M + slot0 + s] = lane_ < rv ? la : 0.f;
+    };
+    if (is_state) {
+#pragma unroll
+      for (int s = 0; s < SSL; s++) put(r.s.at(s), s);
+    } else if (gate_pass) {
+#pragma unroll
+      for (int s = 0; s < PSL; s++) put(r.p.at(s), s);
+    }
+  };
+  auto rows_of = [&](int ch) { return min(C, T_len - ch * C); };
 
   Tile<DK> pq, pk;
   Tile<DV> pv;
-  GateRow<SPT> pg;
+  ST W;
+  bool slow;
   {
-    const int t0 = c_begin * C, rv = min(C, T_len - t0);
+    const int t0 = c_begin * C, rv = rows_of(c_begin);
     pq.load(qb + (size_t)t0 * DK, rv, tid);
     pk.load(kb + (size_t)t0 * DK, rv, tid);
     pv.load(vb + (size_t)t0 * DV, rv, tid);
-    pg.load(gb + (size_t)(t0 + min(lane, rv - 1)) * M, lane < rv);
+    load_gates(gr, t0, rv, lane);
+    if (is_state) {
+      if (P > 1) W.load_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), sw, lane);
+      else W.load_kv(k0 ? k0 + (size_t)unit * M * DK : nullptr, v0 ? v0 + (size_t)unit * M * DV : nullptr, sw, lane);
+      W.store_copy(sW, Lds::LDW, sw, lane);
+    }
+    slow = __syncthreads_or(factors(gr, rv, 0, lane)) != 0;
   }
 
+  int b = 0;  // factor set of the current chunk
   for (int ch = c_begin; ch < c_end; ch++) {
-    const int t0 = ch * C, rv = min(C, T_len - t0);
-    pq.store(sQ, Lds::LDQ, tid);
-    pk.store(sK, Lds::LDQ, tid);
-    pv.store(sV, Lds::LDV, tid);
-    bool small = false;
-    {
-      LogGates<SPT> gt;
-      gt.compute(pg, lane < rv, inv_tau, lane);
-      float x[SPT], z[SPT], e[SPT];
-#pragma unroll
-      for (int s = 0; s < SPT; s++) {
-        const float gc = __shfl(gt.G[s], 63, 64);
-        small |= !(gc >= kFastMinLogDecay);
-        e[s] = __expf(gt.G[s]);
-        x[s] = gt.w[s] * __expf(-gt.G[s]);
-        z[s] = gt.w[s] * __expf(gc - gt.G[s]);
-        if (lane == 0) sDec[wv * SPT + s] = __expf(gc);
-      }
-      // the fast-path factors; a slow chunk overwrites this region after the barrier
-      store_bf16_row<SPT>(sX + lane * Lds::LDX + wv * SPT, x);
-      store_bf16_row<SPT>(sZ + lane * Lds::LDX + wv * SPT, z);
-      store_f32_row<SPT>(sE + lane * Lds::LDE + wv * SPT, e);
-    }
-    GateRow<SPT> pg_next;  // the current row stays in pg for a slow chunk
-    if (ch + 1 < c_end) {  // prefetch the next chunk into registers
-      const int t1 = t0 + C, rv1 = min(C, T_len - t1);
-      pq.load(qb + (size_t)t1 * DK, rv1, tid);
-      pk.load(kb + (size_t)t1 * DK, rv1, tid);
-      pv.load(vb + (size_t)t1 * DV, rv1, tid);
-      pg_next.load(gb + (size_t)(t1 + min(lane, rv1 - 1)) * M, lane < rv1);
-    }
-    const bool slow = __syncthreads_or(small) != 0;
-
+    // lane / thread indices re-derived each chunk: keeps the compiler from
+    // holding every per-lane LDS address of the loop in registers across it
+    int lane_i = lane, tid_i = tid;
+    asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+    const int t0 = ch * C, rv = rows_of(ch);
+    const int cn = min(ch + 1, c_end - 1);  // next chunk (this one again at the end)
+    const int t1 = cn * C, rv1 = rows_of(cn);
+    pq.store(sQ, Lds::LDQ, rv, tid_i);
+    pk.store(sK, Lds::LDQ, rv, tid_i);
+    pv.store(sV, Lds::LDV, rv, tid_i);
+    if (slow) log_alpha(gr, rv, lane_i);
+    load_gates(gr, t1, rv1, lane_i);
+    __syncthreads();
+    // prefetch the next chunk's tiles into registers (unconditionally -- the
+    // last chunk reloads itself -- so that no branch blurs the load-count waits)
+    pq.load(qb + (size_t)t1 * DK, rv1, tid_i);
+    pk.load(kb + (size_t)t1 * DK, rv1, tid_i);
+    pv.load(vb + (size_t)t1 * DV, rv1, tid_i);
+    bool small;
     if (!slow) {
       if (!is_state) {
+        bf16_t* orow = ob + (size_t)t0 * DV;
         // pass waves hold no state: dropping it frees these registers for the passes
         W.zero();
-        pass_chunk<DK, DV, M>(wv, lane, sQ, sK, sV, sW, sX, sE, ob + (size_t)t0 * DV, rv);
+        switch (wv) {
+          case 0: pass_chunk<DK, DV, M, 0>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 1: pass_chunk<DK, DV, M, 1>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 2: pass_chunk<DK, DV, M, 2>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          default: pass_chunk<DK, DV, M, 3>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+        }
       } else {
-        W.carry(sK, Lds::LDQ, sV, Lds::LDV, sZ, Lds::LDX, sDec, sw, lane);
+        W.carry(sK, Lds::LDQ, sV, Lds::LDV, fZ(b), Lds::LDX, sDec0 + b * M, sw, lane_i);
       }
+      // the next chunk's factors (owners: the state waves and pass waves 0, 1)
+      small = factors(gr, rv1, b ^ 1, lane_i);
     } else {
       // ---- exact token recurrence (no division by a decay product), on an
       // fp32 copy of the state in LDS; thread t owns slot t / TPS and 1/TPS of
       // its columns for the whole chunk
-      exact_chunk<DK, DV, M>(W, pg, rv, inv_tau, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid);
+      exact_chunk<DK, DV, M>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid_i);
+      small = factors(gr, rv1, b ^ 1, lane_i);
     }
-    __syncthreads();
-    if (is_state) W.store_copy(sW, Lds::LDW, sw, lane);
-    pg = pg_next;
+    slow = __syncthreads_or(small) != 0;
+    if (is_state) W.store_copy(sW, Lds::LDW, sw, lane_i);
+    b ^= 1;
   }
 
   if (seg == P - 1 && is_state)
