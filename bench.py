@@ -6,7 +6,8 @@ training-shape workload: B=8, H=4, T=2048, dk=dv=128, m=64 slots, C=64,
 bf16 inputs, fp32 state (seeded synthetic data).  `value` is B*T tokens/s
 with inputs resident in HBM, rotating over enough input copies that the
 256 MB last-level cache cannot hold them.  The dominant kernel's duration
-comes from HIP events recorded on the library's stream around it.
+comes from HIP events that its own dispatch stamps (start and end) on the
+library's stream.
 
 Also reported: the standalone GLA forward (T=4096), the long-context GSA
 forward (T=16384, initial state), and the batched decode step (HBM GB/s),
@@ -178,7 +179,7 @@ def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True):
                       "outputs": round(t_out, 4), "op": round(t_op, 4)},
         "alg_flops": flops, "alg_bytes": nbytes,
         "alg_tflops": flops / (t_op * 1e-3) / 1e12,
-        "roofline": roofline(nbytes, t_out, "gsa_seg_out", name),
+        "roofline": roofline(nbytes, t_out, "gsa_bf16_out", name),
         "op_roofline": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
@@ -228,7 +229,6 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
     tok = {n: to_dev(inp[n], torch) for n in "qkvg"}
     states = [(to_dev(inp["kstate"], torch), to_dev(inp["vstate"], torch)) for _ in range(2)]
     out = torch.empty((w["N"], w["H"], w["dv"]), dtype=torch.bfloat16, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
     evs = ev.create(2 * steps)
     for i in range(warmup):
         ks, vs = states[i % 2]
@@ -237,9 +237,8 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
     t0 = time.perf_counter()
     for i in range(steps):
         ks, vs = states[i % 2]
-        ev.record(evs[2 * i], stream)
-        gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out)
-        ev.record(evs[2 * i + 1], stream)
+        gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out,
+                            events=evs[2 * i: 2 * i + 2])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])

@@ -109,13 +109,14 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
 
 /*
  * gsa_fwd / gla_fwd with timing hooks, for benchmarks and profilers.  events
- * is NULL or an array of 4 hipEvent_t (each entry nullable), recorded on the
- * stream at the phase boundaries of the launch sequence:
- *   [0] before the segment state-map pass, [1] before the segment scan,
- *   [2] before the output pass, [3] after the output pass.
- * When a problem needs a single segment the first two passes are skipped and
- * [0]..[2] are recorded back to back.  Everything else is as for the plain
- * entry points (which are these with events = NULL).
+ * is NULL or an array of 4 hipEvent_t (each entry nullable).  [0] and [1] take
+ * the start and end timestamps of the segment state-map kernel's dispatch,
+ * [2] and [3] those of the output kernel's dispatch, so [2] -> [3] is the
+ * output kernel's execution time, [1] -> [2] the segment scan with the gaps
+ * around it and [0] -> [3] the whole launch sequence.  When a problem needs a
+ * single segment the first two passes are skipped and [0], [1] are recorded
+ * on the stream just before the output kernel.  Everything else is as for the
+ * plain entry points (which are these with events = NULL).
  */
 int gsa_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* k0,
                    const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T,
@@ -140,6 +141,12 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
 int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* k_state,
                     float* v_state, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
                     void* stream);
+/* gsa_decode_step with a timing hook: events is NULL or 2 hipEvent_t (each
+ * nullable) that take the start and end timestamps of the decode kernel's
+ * dispatch.  gsa_decode_step is this with events = NULL. */
+int gsa_decode_step_events(const void* q, const void* k, const void* v, const void* g,
+                           float* k_state, float* v_state, void* o, int N, int H, int dk, int dv,
+                           int m, float tau, int dtype, void* stream, void* const* events);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,8 @@ lib.gla_fwd_events.restype = _I
 lib.gla_fwd_events.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_decode_step.restype = _I
 lib.gsa_decode_step.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P]
+lib.gsa_decode_step_events.restype = _I
+lib.gsa_decode_step_events.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -112,11 +114,13 @@ def _check(t, name, dtype=None):
         raise TypeError("%s must be %s" % (name, dtype))
 
 
-def _events(events):
-    """None, or 4 raw hipEvent_t handles (ints or None) -> void*[4]."""
+def _events(events, n=4):
+    """None, or n raw hipEvent_t handles (ints or None) -> void*[n]."""
     if events is None:
         return None
-    arr = (ctypes.c_void_p * 4)(*[None if e is None else int(e) for e in events])
+    if len(events) != n:
+        raise ValueError("expected %d event handles, got %d" % (n, len(events)))
+    arr = (ctypes.c_void_p * n)(*[None if e is None else int(e) for e in events])
     return ctypes.cast(arr, ctypes.c_void_p)
 
 
@@ -190,9 +194,11 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
     return out, s_final
 
 
-def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=None):
+def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=None,
+                    events=None):
     """One recurrent GSA step.  q, k [N,H,dk]; v [N,H,dv]; g [N,H,m]; float32
-    k_state [N,H,m,dk] and v_state [N,H,m,dv] are advanced in place.  Returns o."""
+    k_state [N,H,m,dk] and v_state [N,H,m,dv] are advanced in place.  Returns o.
+    events: None or two hipEvent_t handles that take the kernel's start and end."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _check(t, n, q.dtype)
@@ -202,8 +208,9 @@ def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=N
     dv, m = v.shape[-1], g.shape[-1]
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.gsa_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state), _ptr(v_state),
-                             _ptr(out), N, H, dk, dv, m, float(tau), _dt(q), _stream(stream))
+    st = lib.gsa_decode_step_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state),
+                                    _ptr(v_state), _ptr(out), N, H, dk, dv, m, float(tau), _dt(q),
+                                    _stream(stream), _events(events, 2))
     if st:
         raise GsaError("gsa_decode_step", st)
     return out

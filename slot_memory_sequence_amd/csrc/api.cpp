@@ -233,6 +233,12 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
 int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* ks,
                     float* vs, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
                     void* stream) {
+  return gsa_decode_step_events(q, k, v, g, ks, vs, o, N, H, dk, dv, m, tau, dtype, stream, nullptr);
+}
+
+int gsa_decode_step_events(const void* q, const void* k, const void* v, const void* g, float* ks,
+                           float* vs, void* o, int N, int H, int dk, int dv, int m, float tau,
+                           int dtype, void* stream, void* const* events) {
   if (N < 0 || H < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
       !dtype_ok(dtype))
     return GSA_ERR_SHAPE;
@@ -256,7 +262,7 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, 
     if (overlap(ro, in)) return GSA_ERR_ALIAS;
   gsa::DecodeLaunch a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs; a.o = o; a.N = N; a.H = H;
-  a.tau = tau; a.stream = stream;
+  a.tau = tau; a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::decode_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();

@@ -14,6 +14,7 @@
 // 64 KB per unit are in flight.
 #include "common.hpp"
 #include "internal.hpp"
+#include "launch.hpp"
 
 namespace gsa {
 
@@ -148,9 +149,9 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 template <typename T, int DK, int DV, int M>
 static int launch_decode(const DecodeLaunch& a) {
   const unsigned units = (unsigned)a.N * (unsigned)a.H;
-  hipLaunchKernelGGL((gsa_decode_kernel<T, DK, DV, M>), dim3(units), dim3(dNT), 0, (hipStream_t)a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
-                     1.0f / a.tau);
+  launch_timed(gsa_decode_kernel<T, DK, DV, M>, dim3(units), dim3(dNT), 0, a.stream, a.events, 0, 1,
+               (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
+               1.0f / a.tau);
   return 0;
 }
 

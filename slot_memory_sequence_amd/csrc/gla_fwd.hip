@@ -14,6 +14,7 @@
 // e^-40 in some key dimension.
 #include "common.hpp"
 #include "internal.hpp"
+#include "launch.hpp"
 
 namespace gsa {
 
@@ -483,21 +484,20 @@ static int launch_gla(const GlaLaunch& a) {
   const int P = (nchunks + S - 1) / S;
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
-  record_event(a.events, 0, a.stream);
   if (P > 1) {
-    hipLaunchKernelGGL((gla_seg_state<T, DK, DV>), dim3(P - 1, units), dim3(gNT), LS::total, st,
-                       (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ws_state, a.ws_dec, a.T, S, P, inv_tau);
-    record_event(a.events, 1, a.stream);
+    launch_timed(gla_seg_state<T, DK, DV>, dim3(P - 1, units), dim3(gNT), LS::total, a.stream, a.events,
+                 0, 1, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ws_state, a.ws_dec, a.T, S, P,
+                 inv_tau);
     const long long ne = (long long)units * DK * DV;
     hipLaunchKernelGGL((gla_seg_scan<DK, DV>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
                        a.ws_state, (const float*)a.ws_dec, a.s0, units, P);
+  } else {
+    record_event(a.events, 0, a.stream);
+    record_event(a.events, 1, a.stream);
   }
-  if (P <= 1) record_event(a.events, 1, a.stream);
-  record_event(a.events, 2, a.stream);
-  hipLaunchKernelGGL((gla_seg_out<T, DK, DV>), dim3(P, units), dim3(gNT), LO::total, st,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.s0,
-                     (const float*)a.ws_state, (T*)a.o, a.sf, a.T, S, P, inv_tau);
-  record_event(a.events, 3, a.stream);
+  launch_timed(gla_seg_out<T, DK, DV>, dim3(P, units), dim3(gNT), LO::total, a.stream, a.events, 2, 3,
+               (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.s0,
+               (const float*)a.ws_state, (T*)a.o, a.sf, a.T, S, P, inv_tau);
   return 0;
 }
 

@@ -35,6 +35,7 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+#include "launch.hpp"
 
 namespace gsa {
 namespace bfk {
@@ -975,23 +976,20 @@ static int launch(const GsaLaunch& a) {
     return true;
   }();
   (void)lds_set;
-  record_event(a.events, 0, a.stream);
   if (P > 1) {
-    hipLaunchKernelGGL((gsa_bf16_state<DK, DV, M>), dim3(P - 1, units), dim3(NT), LS::total, st,
-                       (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g, a.ws_state,
-                       a.ws_dec, a.T, S, P, inv_tau);
-    record_event(a.events, 1, a.stream);
+    launch_timed(gsa_bf16_state<DK, DV, M>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
+                 a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
+                 a.ws_state, a.ws_dec, a.T, S, P, inv_tau);
     const long long ne = (long long)units * M * (DK + DV);
     hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
                        a.ws_state, (const float*)a.ws_dec, a.k0, a.v0, units, P);
   } else {
+    record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  record_event(a.events, 2, a.stream);
-  hipLaunchKernelGGL((gsa_bf16_out<DK, DV, M>), dim3(P, units), dim3(NT), LO::total, st,
-                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
-                     a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, a.T, S, P, inv_tau);
-  record_event(a.events, 3, a.stream);
+  launch_timed(gsa_bf16_out<DK, DV, M>, dim3(P, units), dim3(NT), LO::total, a.stream, a.events, 2,
+               3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
+               a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, a.T, S, P, inv_tau);
   return 0;
 }
 

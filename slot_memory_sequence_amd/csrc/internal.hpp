@@ -15,7 +15,7 @@ struct GsaLaunch {
   int B, H, T, chunks_per_seg;
   float tau;
   void* stream;
-  void* const* events;  // nullable: 4 hipEvent_t recorded at the phase boundaries
+  void* const* events;  // nullable: 4 hipEvent_t, see gsa_fwd_events
 };
 
 struct GlaLaunch {
@@ -27,7 +27,7 @@ struct GlaLaunch {
   int B, H, T, chunks_per_seg;
   float tau;
   void* stream;
-  void* const* events;  // nullable: 4 hipEvent_t recorded at the phase boundaries
+  void* const* events;  // nullable: 4 hipEvent_t, see gla_fwd_events
 };
 
 // record events[i] on the stream when the event array and entry are non-null
@@ -40,6 +40,7 @@ struct DecodeLaunch {
   int N, H;
   float tau;
   void* stream;
+  void* const* events;  // nullable: 2 hipEvent_t, start and end of the kernel
 };
 
 // query == true: return the phase-C LDS bytes (> 0) if the shape is compiled, else -1.

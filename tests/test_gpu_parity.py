@@ -214,3 +214,60 @@ def test_decode_chain_equals_fwd(gsa, torch):
     torch.cuda.synchronize()
     assert rel_err(np.stack([to_np(x) for x in outs], axis=2), to_np(o_fwd)) <= 1e-5
     assert rel_err(to_np(ks), to_np(kf)) <= 1e-5 and rel_err(to_np(vs), to_np(vf)) <= 1e-5
+
+
+# ------------------------------------------------------------ timing hooks
+def _hip_events(n):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+
+    def ms(a, b):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return f.value
+
+    def free():
+        for e in evs:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    return evs, ms, free
+
+
+@pytest.mark.parametrize("dtype,cps", [("bf16", 2), ("bf16", 64), ("f32", 2)])
+def test_event_hooks_give_identical_results(gsa, torch, dtype, cps):
+    """The timed launches (dispatch-stamped events) compute exactly what the
+    plain ones do, and the stamps are ordered."""
+    inp = synth.gsa_inputs(2, 2, 300, 64, 64, 32, dtype=dtype, seed=7)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    o1, _, _ = gsa.gsa_fwd(q, k, v, g, tau=8.0, final_state=False, chunks_per_segment=cps)
+    evs, ms, free = _hip_events(4)
+    o2, _, _ = gsa.gsa_fwd(q, k, v, g, tau=8.0, final_state=False, chunks_per_segment=cps,
+                           events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    t = [ms(evs[0], evs[1]), ms(evs[1], evs[2]), ms(evs[2], evs[3]), ms(evs[0], evs[3])]
+    free()
+    assert t[2] > 0 and t[3] >= t[2] and min(t[0], t[1]) >= 0, t
+
+
+def test_decode_event_hooks(gsa, torch):
+    inp = synth.decode_inputs(8, 2, 128, 128, 64, dtype="bf16", seed=3)
+    tok = {n: to_dev(inp[n], torch) for n in "qkvg"}
+    ks1, vs1 = to_dev(inp["kstate"], torch), to_dev(inp["vstate"], torch)
+    ks2, vs2 = ks1.clone(), vs1.clone()
+    o1 = gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks1, vs1, tau=8.0)
+    evs, ms, free = _hip_events(2)
+    o2 = gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks2, vs2, tau=8.0, events=evs)
+    torch.cuda.synchronize()
+    t = ms(evs[0], evs[1])
+    free()
+    assert torch.equal(o1, o2) and torch.equal(ks1, ks2) and torch.equal(vs1, vs2)
+    assert t > 0
