@@ -218,7 +218,7 @@ def bench_gla(torch, gsa, ev, w, steps, warmup):
                           "op": round(t_op, 4)},
             "alg_tflops": round(flops / (t_op * 1e-3) / 1e12, 2),
             "mfma_frac_alg": round(flops / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline(nbytes, t_out, "gla_seg_out", "gla_bf16_T4096")}
+            "roofline": roofline(nbytes, t_out, "gla_bf16_out", "gla_bf16_T4096")}
 
 
 def bench_decode(torch, gsa, ev, w, steps, warmup):

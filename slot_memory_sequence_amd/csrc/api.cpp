@@ -45,13 +45,30 @@ int resolve_cps(long long units, int T, int cps) {
   return cps < 1 ? 1 : cps;
 }
 
-size_t ws_bytes(long long units, int T, int cps, size_t state_elems, size_t dec_elems) {
+// State-map sub-segments per output segment for the bf16 GLA path: enough
+// that the state-map pass has about kTargetWorkgroups workgroups (1 for the
+// other paths and for single-segment problems).
+int gla_state_split(long long units, int T, int cps, int dtype) {
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  if (dtype != GSA_DTYPE_BF16 || nchunks == 0 || units == 0) return 1;
+  const long long P = (nchunks + cps - 1) / cps;
+  if (P <= 1) return 1;
+  long long r = kTargetWorkgroups / ((P - 1) * units);
+  if (r > cps) r = cps;
+  return r < 1 ? 1 : (int)r;
+}
+
+// Workspace slots per unit: P segment start states, or (P-1) R maps if more.
+long long ws_slots(long long P, int R) { return (P - 1) * R > P ? (P - 1) * R : P; }
+
+size_t ws_bytes(long long units, int T, int cps, size_t state_elems, size_t dec_elems, int R = 1) {
   const int nchunks = (T + kChunk - 1) / kChunk;
   if (nchunks == 0 || units == 0) return 0;
   const long long P = (nchunks + cps - 1) / cps;
   if (P <= 1) return 0;
-  const size_t st = (size_t)units * P * state_elems * 4;
-  const size_t dc = (size_t)units * P * dec_elems * 4;
+  const long long NQ = ws_slots(P, R);
+  const size_t st = (size_t)units * NQ * state_elems * 4;
+  const size_t dc = (size_t)units * NQ * dec_elems * 4;
   return ((st + 255) & ~(size_t)255) + dc;
 }
 
@@ -106,7 +123,8 @@ size_t gsa_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int C
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int dtype, int cps) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || C < 1 || !dtype_ok(dtype)) return (size_t)-1;
   const long long units = (long long)B * H;
-  return ws_bytes(units, T, resolve_cps(units, T, cps), (size_t)dk * dv, (size_t)dk);
+  const int c = resolve_cps(units, T, cps);
+  return ws_bytes(units, T, c, (size_t)dk * dv, (size_t)dk, gla_state_split(units, T, c, dtype));
 }
 
 int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* k0,
@@ -209,7 +227,8 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
   for (Range in : {rq, rk, rv, rg, rs0})
     if (overlap(rws, in)) return GSA_ERR_ALIAS;
   const int c = resolve_cps(units, T, cps);
-  const size_t need = ws_bytes(units, T, c, (size_t)dk * dv, (size_t)dk);
+  const int R = gla_state_split(units, T, c, dtype);
+  const size_t need = ws_bytes(units, T, c, (size_t)dk * dv, (size_t)dk, R);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
   if (T == 0) {
     gsa::state_copy(sf, s0, (size_t)units * dk * dv, stream);
@@ -219,11 +238,12 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
   a.q = q; a.k = k; a.v = v; a.g = g; a.s0 = s0; a.o = o; a.sf = sf;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const long long P = (nchunks + c - 1) / c;
+  const long long NQ = ws_slots(P, R);
   a.ws_state = (float*)workspace;
   a.ws_dec = workspace ? (float*)((char*)workspace +
-                                  (((size_t)units * P * dk * dv * 4 + 255) & ~(size_t)255))
+                                  (((size_t)units * NQ * dk * dv * 4 + 255) & ~(size_t)255))
                        : nullptr;
-  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.state_split = R; a.tau = tau; a.stream = stream;
   a.events = events;
   (void)hipGetLastError();
   if (gsa::gla_dispatch(dtype, dk, dv, &a, false) != 0) return GSA_ERR_UNSUPPORTED;

@@ -1,0 +1,197 @@
+// bf16 building blocks shared by the chunkwise GSA and GLA kernels (gfx950):
+// MFMA wrappers and operand fragment loads from LDS, chunk tile I/O, raw
+// bf16 rows, wave-wide DPP scans and the log2-domain gate.
+#pragma once
+#include "common.hpp"
+
+namespace gsa {
+namespace bfk {
+
+constexpr int C = 64;   // chunk length
+constexpr int NW = 8;   // waves per workgroup
+constexpr int NT = NW * 64;
+// log2 of the smallest whole-chunk decay the factorised chunk form allows (e^-40)
+constexpr float kFastMinLog2Decay = -57.70780163555854f;
+
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// two accumulator quads -> one operand fragment (round to nearest even)
+__device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
+  f32x8 x = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_convertvector(x, bf16x8);
+}
+__device__ __forceinline__ bf16x4v pack4(const f32x4& a) { return __builtin_convertvector(a, bf16x4v); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row-major [row][k] tile: lane l gets 8 consecutive k at row row0 + l%16,
+// column k0 + 8*(l/16)  (MFMA operand order, standard k).
+__device__ __forceinline__ bf16x8 ld_row(const bf16_t* base, int ld, int row0, int k0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+
+// Row-major [row][k] tile, permuted k: lane l gets 4 consecutive k from klo and
+// 4 from khi (both already include the lane group's offset) at row row0 + l%16.
+__device__ __forceinline__ bf16x8 ld_row2(const bf16_t* base, int ld, int row0, int klo, int khi,
+                                          int lane) {
+  const bf16_t* p = base + (row0 + (lane & 15)) * ld;
+  bf16x4v lo = *reinterpret_cast<const bf16x4v*>(p + klo);
+  bf16x4v hi = *reinterpret_cast<const bf16x4v*>(p + khi);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Row-major [k][n] tile read column-wise with the LDS transpose read: lane l
+// gets tile[klo + jj][n0 + l%16] and tile[khi + jj][n0 + l%16], jj = 0..3,
+// where klo / khi already include the lane group's offset.
+__device__ __forceinline__ bf16x8 ld_col(const bf16_t* base, int ld, int n0, int klo, int khi,
+                                         int lane) {
+  const int L = lane & 15;
+  const bf16_t* p0 = base + (klo + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  const bf16_t* p1 = base + (khi + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GSA_LDS bf16x4_raw*)(p0));
+  bf16x4_raw hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GSA_LDS bf16x4_raw*)(p1));
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// ------------------------------------------------------- global tile I/O
+// [C][D] bf16 chunk tile moved as 16-byte vectors by the 512 threads.
+template <int D>
+struct Tile {
+  static constexpr int VPR = D / 8;
+  static constexpr int NV = C * VPR / NT;
+  static_assert(NV >= 1 && (C * VPR) % NT == 0, "tile/thread mismatch");
+  uint4 r[NV];
+  // rows >= rows_valid (>= 1) read the last valid row; store() zeroes them, so
+  // the loads are not waited for until the tile is stored
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int rows_valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int idx = tid + NT * i, row = idx / VPR, cv = idx % VPR;
+      r[i] = *reinterpret_cast<const uint4*>(base + min(row, rows_valid - 1) * D + cv * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* dst, int ld, int rows_valid, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int idx = tid + NT * i, row = idx / VPR, cv = idx % VPR;
+      const bool ok = row < rows_valid;
+      *reinterpret_cast<uint4*>(dst + row * ld + cv * 8) =
+          make_uint4(ok ? r[i].x : 0u, ok ? r[i].y : 0u, ok ? r[i].z : 0u, ok ? r[i].w : 0u);
+    }
+  }
+};
+
+// SPT gate logits of one token row (SPT = 4 or 8 bf16 = 8 or 16 bytes).
+template <int SPT>
+struct GateRow {
+  static_assert(SPT >= 2 && SPT % 2 == 0, "gate row width");
+  uint32_t r[SPT / 2];
+  // p must point at a readable row, 4-byte aligned (the caller clamps the
+  // row); rows past the end are masked by the consumer
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ p) {
+    if constexpr (SPT % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < SPT / 8; i++) {
+        const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+        r[4 * i] = x.x; r[4 * i + 1] = x.y; r[4 * i + 2] = x.z; r[4 * i + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPT / 2; i++) r[i] = reinterpret_cast<const uint32_t*>(p)[i];
+    }
+  }
+  __device__ __forceinline__ float at(int s) const {
+    const uint32_t w = r[s >> 1];
+    return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  // an opaque redefinition: uses of the row (and the wait for its load) stay
+  // after this point
+  __device__ __forceinline__ void pin() {
+#pragma unroll
+    for (int i = 0; i < SPT / 2; i++) asm volatile("" : "+v"(r[i]));
+  }
+};
+
+// ------------------------------------------------------------- gate math
+// All gate quantities are kept in base-2 logarithms so that the hardware
+// exp2 / log2 instructions apply directly.
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_zero(float x) {  // DPP lane move, 0 where no source lane
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sums over the 64 lanes of a wave, for N independent
+// values per lane, step-major so that every step issues N independent
+// operations: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the last
+// lane of rows 0 / 2 into rows 1 / 3 and the last lane of row 1 into rows 2, 3.
+template <int N>
+__device__ __forceinline__ void wave_prefix_sums(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x111, 0xf>(x[i]);  // row_shr:1
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x112, 0xf>(x[i]);  // row_shr:2
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x114, 0xf>(x[i]);  // row_shr:4
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x118, 0xf>(x[i]);  // row_shr:8
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x142, 0xa>(x[i]);  // row_bcast:15 into rows 1, 3
+#pragma unroll
+  for (int i = 0; i < N; i++) x[i] += dpp_zero<0x143, 0xc>(x[i]);  // row_bcast:31 into rows 2, 3
+}
+
+// Value of the previous lane of the wave (a whole-wave shift by one lane);
+// lane 0 gets `first`.
+__device__ __forceinline__ float prev_lane(float x, float first) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x), 0x138, 0xf, 0xf, false));
+}
+
+// log2 alpha = log2(sigmoid(g)) / tau, clamped at -115 (alpha ~ 2.4e-35) so that
+// g = -inf gives a finite value.
+__device__ __forceinline__ float gate_log2(float g, float inv_tau) {
+  const float t = g * 1.4426950408889634f;  // g / ln 2
+  const float ls2 = fminf(t, 0.f) - __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(t)));
+  return fmaxf(ls2 * inv_tau, -115.f);
+}
+
+// SPT consecutive floats -> bf16 / fp32 rows in LDS; dst is 4-byte (bf16) /
+// 8-byte (fp32) aligned at least, 16-byte when SPT is a multiple of 8 / 4.
+template <int SPT>
+__device__ __forceinline__ void store_bf16_row(bf16_t* dst, const float* v) {
+  if constexpr (SPT % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < SPT; i += 8) {
+      f32x8 x = {v[i], v[i + 1], v[i + 2], v[i + 3], v[i + 4], v[i + 5], v[i + 6], v[i + 7]};
+      *reinterpret_cast<bf16x8*>(dst + i) = __builtin_convertvector(x, bf16x8);
+    }
+  } else {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+#pragma unroll
+    for (int i = 0; i < SPT; i += 2) {
+      f32x2 x = {v[i], v[i + 1]};
+      *reinterpret_cast<bf16x2*>(dst + i) = __builtin_convertvector(x, bf16x2);
+    }
+  }
+}
+template <int SPT>
+__device__ __forceinline__ void store_f32_row(float* dst, const float* v) {
+  if constexpr (SPT % 4 == 0) {
+#pragma unroll
+    for (int s = 0; s < SPT; s += 4)
+      *reinterpret_cast<float4*>(dst + s) = make_float4(v[s], v[s + 1], v[s + 2], v[s + 3]);
+  } else {
+#pragma unroll
+    for (int s = 0; s < SPT; s += 2) *reinterpret_cast<float2*>(dst + s) = make_float2(v[s], v[s + 1]);
+  }
+}
+
+}  // namespace bfk
+}  // namespace gsa

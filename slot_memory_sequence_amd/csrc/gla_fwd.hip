@@ -518,8 +518,7 @@ constexpr bool gla_fits() { return GlaLds<T, DK, DV>::total <= kLdsBytes; }
   }
 
 int gla_dispatch(int dt, int dk, int dv, const GlaLaunch* a, bool query) {
-  GLA_CASE(bf16_t, 1, 128, 128)
-  GLA_CASE(bf16_t, 1, 64, 64)
+  if (dt == 1) return gla_dispatch_bf16(dk, dv, a, query);
   GLA_CASE(float, 0, 64, 64)
   GLA_CASE(float, 0, 128, 128)
   return -1;

@@ -25,6 +25,7 @@ struct GlaLaunch {
   float* sf;
   float *ws_state, *ws_dec;
   int B, H, T, chunks_per_seg;
+  int state_split;  // bf16: state-map sub-segments per output segment (>= 1)
   float tau;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gla_fwd_events
@@ -48,6 +49,7 @@ struct DecodeLaunch {
 int gsa_dispatch(int dtype, int dk, int dv, int m, const GsaLaunch* a, bool query);
 int gsa_dispatch_bf16(int dk, int dv, int m, const GsaLaunch* a, bool query);
 int gla_dispatch(int dtype, int dk, int dv, const GlaLaunch* a, bool query);
+int gla_dispatch_bf16(int dk, int dv, const GlaLaunch* a, bool query);
 int decode_dispatch(int dtype, int dk, int dv, int m, const DecodeLaunch* a, bool query);
 // copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
 void state_copy(float* dst, const float* src, size_t n, void* stream);

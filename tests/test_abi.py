@@ -58,6 +58,13 @@ def test_workspace_query(gsa):
     assert nb == ((state + 255) // 256) * 256 + 32 * P * 64 * 4
     assert gsa.gsa_fwd_workspace_bytes(-1, 4, 16, 128, 128, 64, 64, 1, 0) == (1 << 64) - 1
     assert gsa.gla_fwd_workspace_bytes(8, 16, 4096, 128, 128, 64, 1, 0) > 0
+    # bf16 GLA: 64 units, 2 output segments, each split into 4 state-map
+    # sub-segments -> max(P, (P-1)*4) = 4 slots per unit; fp32 keeps P = 2
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert gsa.gla_fwd_workspace_bytes(8, 8, 640, 64, 64, 64, 1, 5) == \
+        a256(64 * 4 * 64 * 64 * 4) + 64 * 4 * 64 * 4
+    assert gsa.gla_fwd_workspace_bytes(8, 8, 640, 64, 64, 64, 0, 5) == \
+        a256(64 * 2 * 64 * 64 * 4) + 64 * 2 * 64 * 4
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation

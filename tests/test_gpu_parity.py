@@ -174,6 +174,18 @@ def test_gla_segmentations(gsa, torch, cps):
     _check_gla(gsa, torch, 1, 2, 64 * 6 + 3, 128, "bf16", init=True, cps=cps, seed=2)
 
 
+def test_gla_state_split_with_empty_subsegment(gsa, torch):
+    # 64 units, 10 chunks, 5 per output segment: the bf16 state-map pass splits
+    # each segment into 4 sub-segments of 2 chunks, the last of them empty
+    _check_gla(gsa, torch, 8, 8, 640, 64, "bf16", init=True, cps=5, seed=4)
+
+
+@pytest.mark.parametrize("cps", [2, 7])
+def test_gla_bf16_split_ragged(gsa, torch, cps):
+    # few units: sub-segments of one chunk; ragged tail
+    _check_gla(gsa, torch, 1, 3, 64 * 9 + 17, 128, "bf16", init=True, cps=cps, seed=11)
+
+
 def test_gla_extreme_gates(gsa, torch):
     def mut(inp):
         x = inp["g"].f64.copy()
@@ -183,6 +195,8 @@ def test_gla_extreme_gates(gsa, torch):
         inp["g"] = synth.stored(x, inp["g"].dtype)
     _check_gla(gsa, torch, 1, 2, 260, 64, "f32", init=True, mutate=mut, seed=9)
     _check_gla(gsa, torch, 1, 2, 260, 128, "bf16", init=True, mutate=mut, seed=9, cps=1)
+    _check_gla(gsa, torch, 1, 2, 260, 64, "bf16", init=True, mutate=mut, seed=9, cps=2)
+    _check_gla(gsa, torch, 1, 2, 260, 128, "bf16", init=True, mutate=mut, seed=9)
 
 
 # -------------------------------------------------------------- decode
