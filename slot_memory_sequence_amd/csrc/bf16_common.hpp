@@ -161,6 +161,28 @@ __device__ __forceinline__ float gate_log2(float g, float inv_tau) {
   return fmaxf(ls2 * inv_tau, -115.f);
 }
 
+// gate_log2 of the token's logit, or exactly 0 (an identity step) for a row past
+// the end of the sequence.  The row is masked on the input (g = 1e30 gives
+// exp2(-|t|) = 0, log2(1) = 0), so the transcendentals run for every lane and
+// the compiler has no reason to branch around them.
+__device__ __forceinline__ float gate_log2_or_identity(float g, bool valid, float inv_tau) {
+  return gate_log2(valid ? g : 1e30f, inv_tau);
+}
+
+// Workgroup-wide OR of a wave-uniform flag: one LDS word per wave and one
+// barrier (cheaper than the library's reduction, which takes three barriers).
+// flags points at 2 x NW ints; round r uses half r & 1, so a round's writes
+// never meet the previous round's reads (every wave reads a round's flags
+// before it reaches the next round's barrier).
+__device__ __forceinline__ bool block_any(bool wave_flag, int* flags, int round, int lane, int wv) {
+  int* f = flags + (round & 1) * NW;
+  if (lane == 0) f[wv] = wave_flag ? 1 : 0;
+  __syncthreads();
+  const int4 a = *reinterpret_cast<const int4*>(f);
+  const int4 b = *reinterpret_cast<const int4*>(f + 4);
+  return (a.x | a.y | a.z | a.w | b.x | b.y | b.z | b.w) != 0;
+}
+
 // SPT consecutive floats -> bf16 / fp32 rows in LDS; dst is 4-byte (bf16) /
 // 8-byte (fp32) aligned at least, 16-byte when SPT is a multiple of 8 / 4.
 template <int SPT>

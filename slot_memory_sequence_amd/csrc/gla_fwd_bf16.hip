@@ -67,7 +67,8 @@ struct GlaOutLds {
   static constexpr int oOp = oGr + C * DK * 2;
   static constexpr int szSlow0 = DK * DV * 4, szSlow1 = oOp + NW * DV * 4 - oR;
   static constexpr int szSlow = szSlow0 > szSlow1 ? szSlow0 : szSlow1;
-  static constexpr int total = oR + (szFast > szSlow ? szFast : szSlow);
+  static constexpr int oFlag = oR + (szFast > szSlow ? szFast : szSlow);  // 2 x NW ints
+  static constexpr int total = oFlag + 2 * NW * 4;
   static_assert(szV % 16 == 0 && fK % 16 == 0 && fEc % 16 == 0 && szF % 16 == 0 && oS % 16 == 0 &&
                     oKr % 16 == 0 && oGr % 16 == 0 && oOp % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
@@ -188,7 +189,7 @@ __device__ __forceinline__ bool out_factors(const GateRow<SPT>& q, const GateRow
   const bool valid = lane < rv;
   float G[SPT];
 #pragma unroll
-  for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
   wave_prefix_sums<SPT>(G);
   bool small = false;
   float qt[SPT], kt[SPT], ec[SPT];
@@ -196,9 +197,10 @@ __device__ __forceinline__ bool out_factors(const GateRow<SPT>& q, const GateRow
   for (int s = 0; s < SPT; s++) {
     const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
     small |= !(gc >= kFastMinLog2Decay);
-    ec[s] = __builtin_amdgcn_exp2f(gc);
-    qt[s] = q.at(s) * __builtin_amdgcn_exp2f(G[s]);
-    kt[s] = valid ? k.at(s) * __builtin_amdgcn_exp2f(-G[s]) : 0.f;
+    const float e = __builtin_amdgcn_exp2f(G[s]);
+    ec[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 63));
+    qt[s] = q.at(s) * e;
+    kt[s] = (valid ? k.at(s) : 0.f) * __builtin_amdgcn_exp2f(-G[s]);
   }
   store_bf16_row<SPT>(sQt + lane * LDQ + d0, qt);
   store_bf16_row<SPT>(sKt + lane * LDQ + d0, kt);
@@ -215,14 +217,14 @@ __device__ __forceinline__ void map_factors(const GateRow<SPT>& k, const GateRow
   const bool valid = lane < rv;
   float G[SPT];
 #pragma unroll
-  for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
   wave_prefix_sums<SPT>(G);
   float kh[SPT], ec[SPT];
 #pragma unroll
   for (int s = 0; s < SPT; s++) {
     const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
     ec[s] = __builtin_amdgcn_exp2f(gc);
-    kh[s] = valid ? k.at(s) * __builtin_amdgcn_exp2f(gc - G[s]) : 0.f;
+    kh[s] = (valid ? k.at(s) : 0.f) * __builtin_amdgcn_exp2f(gc - G[s]);
     dec[s] *= count ? ec[s] : 1.f;
   }
   store_bf16_row<SPT>(sKh + lane * LDQ + d0, kh);
@@ -503,6 +505,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   auto fK = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fK); };
   auto fEc = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oF + b * Lds::szF + Lds::fEc); };
   bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
+  int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool is_state = wv >= 4;
@@ -553,7 +556,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   {
     const bool small = factors(c_begin, 0, tid, lane);
     load_rows(min(c_begin + 1, c_end - 1), tid, lane);
-    slow = __syncthreads_or(small) != 0;
+    slow = block_any(small, sFlag, 0, lane, wv);
   }
 
   int b = 0;  // factor set of the current chunk
@@ -587,7 +590,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     // blurs the load-count waits)
     const bool small = factors(cn, b ^ 1, tid_i, lane_i);
     load_rows(min(ch + 2, c_end - 1), tid_i, lane_i);
-    slow = __syncthreads_or(small) != 0;
+    slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
     if (is_state) W.store_copy(sS, Lds::LDS, sw, lane_i);
     __syncthreads();
     b ^= 1;

@@ -67,7 +67,8 @@ struct OutLds {
   static constexpr int oOp = oZs + M * 4;              // output partials [NW][DV] fp32
   static constexpr int szSlow = oOp + NW * DV * 4 - oR;
   static constexpr int oDec = oR + (szFast > szSlow ? szFast : szSlow);  // 2 x [M] fp32
-  static constexpr int total = oDec + 2 * M * 4;
+  static constexpr int oFlag = oDec + 2 * M * 4;                         // 2 x NW ints
+  static constexpr int total = oFlag + 2 * NW * 4;
   static_assert(oK % 16 == 0 && oV % 16 == 0 && oW % 16 == 0 && oF % 16 == 0 && szF % 16 == 0 &&
                     fZ % 16 == 0 && fE % 16 == 0 && oLa % 16 == 0 && oOp % 16 == 0 && oDec % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
@@ -95,7 +96,7 @@ struct LogGates {
   float G[SPT], E[SPT], X[SPT];
   __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
 #pragma unroll
-    for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+    for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
     wave_prefix_sums<SPT>(G);
 #pragma unroll
     for (int s = 0; s < SPT; s++) {
@@ -116,7 +117,7 @@ struct SuffixGates {
   __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
     float G[SPT];
 #pragma unroll
-    for (int s = 0; s < SPT; s++) G[s] = valid ? gate_log2(g.at(s), inv_tau) : 0.f;
+    for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
     wave_prefix_sums<SPT>(G);
 #pragma unroll
     for (int s = 0; s < SPT; s++) {
@@ -638,6 +639,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   bf16_t* sW = reinterpret_cast<bf16_t*>(smem + Lds::oW);
   float* sLa = reinterpret_cast<float*>(smem + Lds::oLa);
   float* sDec0 = reinterpret_cast<float*>(smem + Lds::oDec);
+  int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
   // factor set b: X, Z, E, dec
   auto fX = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fX); };
   auto fZ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fZ); };
@@ -716,7 +718,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       else W.load_kv(k0 ? k0 + (size_t)unit * M * DK : nullptr, v0 ? v0 + (size_t)unit * M * DV : nullptr, sw, lane);
       W.store_copy(sW, Lds::LDW, sw, lane);
     }
-    slow = __syncthreads_or(factors(gr, rv, 0, lane)) != 0;
+    slow = block_any(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
   }
 
   int b = 0;  // factor set of the current chunk
@@ -763,7 +765,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       exact_chunk<DK, DV, M>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid_i);
       small = factors(gr, rv1, b ^ 1, lane_i);
     }
-    slow = __syncthreads_or(small) != 0;
+    slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
     if (is_state) W.store_copy(sW, Lds::LDW, sw, lane_i);
     b ^= 1;
   }
