@@ -111,9 +111,10 @@ struct GateRow {
   }
   // an opaque redefinition: uses of the row (and the wait for its load) stay
   // after this point
+  template <int N = SPT>
   __device__ __forceinline__ void pin() {
 #pragma unroll
-    for (int i = 0; i < SPT / 2; i++) asm volatile("" : "+v"(r[i]));
+    for (int i = 0; i < N / 2; i++) asm volatile("" : "+v"(r[i]));
   }
 };
 
@@ -167,6 +168,31 @@ __device__ __forceinline__ float gate_log2(float g, float inv_tau) {
 // the compiler has no reason to branch around them.
 __device__ __forceinline__ float gate_log2_or_identity(float g, bool valid, float inv_tau) {
   return gate_log2(valid ? g : 1e30f, inv_tau);
+}
+
+// SPT consecutive bf16 of an LDS row -> floats (p 16-byte aligned when SPT is
+// a multiple of 8, else 4-byte aligned)
+template <int SPT>
+__device__ __forceinline__ void lds_row(const bf16_t* p, float* out) {
+  if constexpr (SPT % 8 == 0) {
+#pragma unroll
+    for (int i = 0; i < SPT; i += 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p + i);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        out[i + 2 * j] = __uint_as_float(w[j] << 16);
+        out[i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SPT; i += 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p + i);
+      out[i] = __uint_as_float(w << 16);
+      out[i + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+  }
 }
 
 // Workgroup-wide OR of a wave-uniform flag: one LDS word per wave and one

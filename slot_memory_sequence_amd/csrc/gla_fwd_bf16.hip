@@ -46,31 +46,31 @@ template <int DK, int DV>
 struct GlaOutLds {
   static constexpr int PAD = 8;
   static constexpr int LDQ = DK + PAD, LDV = DV + PAD, LDS = DV + PAD;
-  // raw V tiles of both factor sets (the exact path reads the current one)
+  // V tiles of both factor sets
   static constexpr int szV = C * LDV * 2;
   static constexpr int oV = 0;
-  static constexpr int oR = 2 * szV;  // region used differently by the two paths
-  // fast path: two factor sets {Qt, Kt [C][LDQ] bf16, E_C [DK] fp32}, the bf16 copy of S
-  static constexpr int fQ = 0;
-  static constexpr int fK = fQ + C * LDQ * 2;
-  static constexpr int fEc = fK + C * LDQ * 2;
-  static constexpr int szF = fEc + DK * 4;
-  static constexpr int oF = oR;
-  static constexpr int oS = oF + 2 * szF;  // S [DK][LDS] bf16
-  static constexpr int szFast = oS + DK * LDS * 2 - oR;
-  // exact path: fp32 S [DK][DV] for the change of layout, then (after it was
-  // read) raw q, k, g tiles [C][DK] bf16 and output partials [NW][DV] fp32
-  static constexpr int oSf = oR;
-  static constexpr int oQr = oR;
-  static constexpr int oKr = oQr + C * DK * 2;
-  static constexpr int oGr = oKr + C * DK * 2;
-  static constexpr int oOp = oGr + C * DK * 2;
-  static constexpr int szSlow0 = DK * DV * 4, szSlow1 = oOp + NW * DV * 4 - oR;
-  static constexpr int szSlow = szSlow0 > szSlow1 ? szSlow0 : szSlow1;
-  static constexpr int oFlag = oR + (szFast > szSlow ? szFast : szSlow);  // 2 x NW ints
+  // factor set b: Qt, Kt [C][LDQ] bf16 (raw q, k until the factor step turns
+  // them into Qt, Kt in place); the bf16 copy of S [DK][LDS] sits between the
+  // two sets so that either set and the copy form one contiguous region
+  static constexpr int szQK = 2 * C * LDQ * 2;
+  static constexpr int oF0 = 2 * szV;
+  static constexpr int oS = oF0 + szQK;
+  static constexpr int oF1 = oS + DK * LDS * 2;
+  static constexpr int fQ = 0, fK = C * LDQ * 2;
+  static constexpr int oEc = oF1 + szQK;                 // 2 x [DK] fp32
+  static constexpr int oG = oEc + 2 * DK * 4;            // raw gate logits [C][LDQ] bf16
+  static constexpr int oFlag = oG + C * LDQ * 2;         // 2 x NW ints
   static constexpr int total = oFlag + 2 * NW * 4;
-  static_assert(szV % 16 == 0 && fK % 16 == 0 && fEc % 16 == 0 && szF % 16 == 0 && oS % 16 == 0 &&
-                    oKr % 16 == 0 && oGr % 16 == 0 && oOp % 16 == 0,
+  // exact path, inside [set b | copy of S] (b = 0) or [copy of S | set 1]
+  // (b = 1): fp32 S [DK][DV] for the change of layout, then (after it was
+  // read) raw q, k, g tiles [C][DK] bf16 and output partials [NW][DV] fp32
+  static constexpr int szR = szQK + DK * LDS * 2;
+  static constexpr int xSf = 0, xQr = 0, xKr = C * DK * 2, xGr = 2 * C * DK * 2, xOp = 3 * C * DK * 2;
+  static_assert(DK * DV * 4 <= szR && xOp + NW * DV * 4 <= szR, "exact path must fit its region");
+  __device__ __forceinline__ static int oF(int b) { return b ? oF1 : oF0; }
+  __device__ __forceinline__ static int oX(int b) { return b ? oS : oF0; }
+  static_assert(szV % 16 == 0 && szQK % 16 == 0 && oS % 16 == 0 && oF1 % 16 == 0 && oEc % 16 == 0 &&
+                    oG % 16 == 0 && oFlag % 16 == 0 && xKr % 16 == 0 && xGr % 16 == 0 && xOp % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
 };
 
@@ -178,32 +178,35 @@ struct GlaTiles {
 
 // -------------------------------------------------------- chunk factors
 // Key dimensions d0..d0+SPT-1 of one chunk, token row = lane (rows >= rv are
-// identity steps): G = chunk-local cumulative log2 alpha.  Output-pass form:
-// Qt = q exp2(G), Kt = k exp2(-G) (0 on rows >= rv), E_C = exp2(G_C).
-// Returns whether any of these dimensions decays below the range of the
-// factorised form in this chunk.
+// identity steps): G = chunk-local cumulative log2 alpha.  Output-pass form,
+// from the raw q, k, g rows staged in LDS: Qt = q exp2(G) and Kt = k exp2(-G)
+// (0 on rows >= rv), written over q and k, and E_C = exp2(G_C).  Returns
+// whether any of these dimensions decays below the range of the factorised
+// form in this chunk.
 template <int SPT, int LDQ>
-__device__ __forceinline__ bool out_factors(const GateRow<SPT>& q, const GateRow<SPT>& k,
-                                            const GateRow<SPT>& g, int rv, float inv_tau, int lane,
-                                            int d0, bf16_t* sQt, bf16_t* sKt, float* sEc) {
+__device__ __forceinline__ bool out_factors(bf16_t* sQ, bf16_t* sK, const bf16_t* sG, int rv,
+                                            float inv_tau, int lane, int d0, float* sEc) {
   const bool valid = lane < rv;
-  float G[SPT];
+  float q[SPT], k[SPT], G[SPT];
+  lds_row<SPT>(sQ + lane * LDQ + d0, q);
+  lds_row<SPT>(sK + lane * LDQ + d0, k);
+  lds_row<SPT>(sG + lane * LDQ + d0, G);
 #pragma unroll
-  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(G[s], valid, inv_tau);
   wave_prefix_sums<SPT>(G);
   bool small = false;
-  float qt[SPT], kt[SPT], ec[SPT];
+  float ec[SPT];
 #pragma unroll
   for (int s = 0; s < SPT; s++) {
     const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
     small |= !(gc >= kFastMinLog2Decay);
     const float e = __builtin_amdgcn_exp2f(G[s]);
     ec[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), 63));
-    qt[s] = q.at(s) * e;
-    kt[s] = (valid ? k.at(s) : 0.f) * __builtin_amdgcn_exp2f(-G[s]);
+    q[s] *= e;
+    k[s] = (valid ? k[s] : 0.f) * __builtin_amdgcn_exp2f(-G[s]);
   }
-  store_bf16_row<SPT>(sQt + lane * LDQ + d0, qt);
-  store_bf16_row<SPT>(sKt + lane * LDQ + d0, kt);
+  store_bf16_row<SPT>(sQ + lane * LDQ + d0, q);
+  store_bf16_row<SPT>(sK + lane * LDQ + d0, k);
   if (lane == 0) store_f32_row<SPT>(sEc + d0, ec);
   return small;
 }
@@ -295,7 +298,7 @@ __device__ __forceinline__ void gla_pass_chunk(int lane, const bf16_t* sQt, cons
 // The state waves' accumulators go through LDS to and from that layout.
 // Contains workgroup barriers: all threads call it.
 template <int DK, int DV>
-__device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, unsigned char* smem,
+__device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, unsigned char* region,
                                                 const bf16_t* sV, const bf16_t* __restrict__ qc,
                                                 const bf16_t* __restrict__ kc,
                                                 const bf16_t* __restrict__ gc,
@@ -304,17 +307,18 @@ __device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, 
   constexpr int TPD = NT / DK;  // threads per key dimension
   constexpr int CPT = DV / TPD;  // value columns per thread
   static_assert(NT % DK == 0 && TPD <= 64 && CPT >= 1, "exact-path thread map");
-  float* sSf = reinterpret_cast<float*>(smem + Lds::oSf);
-  bf16_t* sQr = reinterpret_cast<bf16_t*>(smem + Lds::oQr);
-  bf16_t* sKr = reinterpret_cast<bf16_t*>(smem + Lds::oKr);
-  bf16_t* sGr = reinterpret_cast<bf16_t*>(smem + Lds::oGr);
-  float* sOp = reinterpret_cast<float*>(smem + Lds::oOp);
+  float* sSf = reinterpret_cast<float*>(region + Lds::xSf);
+  bf16_t* sQr = reinterpret_cast<bf16_t*>(region + Lds::xQr);
+  bf16_t* sKr = reinterpret_cast<bf16_t*>(region + Lds::xKr);
+  bf16_t* sGr = reinterpret_cast<bf16_t*>(region + Lds::xGr);
+  float* sOp = reinterpret_cast<float*>(region + Lds::xOp);
   const int lane = tid & 63, wv = tid >> 6;
   const bool is_state = wv >= 4;
   const int d = tid / TPD, p = tid % TPD;
 
-  // (the region held the factor sets and the bf16 state copy, all of whose
-  // readers passed the last barrier)
+  // (the region held this chunk's factor set and the bf16 state copy, all of
+  // whose readers passed the last barrier; the other set holds the next
+  // chunk's staged rows and is left alone)
   if (is_state) W.store(sSf, DV, wv - 4, lane);
   __syncthreads();
   float s[CPT];
@@ -367,7 +371,7 @@ __device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, 
   for (int i = 0; i < CPT; i++) sSf[d * DV + p * CPT + i] = s[i];
   __syncthreads();
   if (is_state) W.load(sSf, DV, wv - 4, lane);
-  __syncthreads();  // the region is reused by the next factor set
+  __syncthreads();  // the region is reused by the state copy and later rows
 }
 
 // ------------------------------------------------ phase A: state maps
@@ -489,6 +493,11 @@ gla_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec, co
 }
 
 // ------------------------------------------------------ phase C: outputs
+// Per chunk c (factor set b = c & 1): the contractions of chunk c; the factors
+// of chunk c+1 from its rows staged in set b^1; a barrier; the state copy and
+// the staging of chunk c+2's rows (loaded one chunk earlier as coalesced tiles)
+// into set b, the g tile and the V slot of set b; the loads of chunk c+3; a
+// barrier.
 template <int DK, int DV>
 __global__ void __launch_bounds__(NT, 1)
 gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
@@ -501,10 +510,11 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   constexpr int SPT = DK / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto fV = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oV + b * Lds::szV); };
-  auto fQ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fQ); };
-  auto fK = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fK); };
-  auto fEc = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oF + b * Lds::szF + Lds::fEc); };
+  auto fQ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF(b) + Lds::fQ); };
+  auto fK = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF(b) + Lds::fK); };
+  auto fEc = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oEc + b * DK * 4); };
   bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
+  bf16_t* sG = reinterpret_cast<bf16_t*>(smem + Lds::oG);
   int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -521,43 +531,45 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bf16_t* vb = vv + ub * DV;
   bf16_t* ob = oo + ub * DV;
   auto rows_of = [&](int ch) { return min(C, T_len - ch * C); };
+  auto clamp = [&](int ch) { return min(ch, c_end - 1); };
 
-  // the next chunk's rows (token = lane, this wave's key dimensions) and V tile
-  GateRow<SPT> rq, rk, rg;
+  // raw tiles of a later chunk in registers (coalesced loads)
+  Tile<DK> pq, pk, pg;
   Tile<DV> pv;
-  auto load_rows = [&](int ch, int tid_, int lane_) {
+  auto load_tiles = [&](int ch, int tid_) {
     const int t0 = ch * C, rv = rows_of(ch);
-    const size_t row = (size_t)(t0 + min(lane_, rv - 1)) * DK + d0;
-    rq.load(qb + row);
-    rk.load(kb + row);
-    rg.load(gb + row);
+    pq.load(qb + (size_t)t0 * DK, rv, tid_);
+    pk.load(kb + (size_t)t0 * DK, rv, tid_);
+    pg.load(gb + (size_t)t0 * DK, rv, tid_);
     pv.load(vb + (size_t)t0 * DV, rv, tid_);
   };
-  // (the empty asm of pin() keeps the uses of the rows, and so the wait for
-  // their loads, at the call)
-  auto factors = [&](int ch, int fb, int tid_, int lane_) -> bool {
+  auto stage_tiles = [&](int ch, int b, int tid_) {  // rows >= rv are zeroed
     const int rv = rows_of(ch);
-    rq.pin();
-    rk.pin();
-    rg.pin();
-    pv.store(fV(fb), Lds::LDV, rv, tid_);
-    return out_factors<SPT, Lds::LDQ>(rq, rk, rg, rv, inv_tau, lane_, d0, fQ(fb), fK(fb), fEc(fb));
+    pq.store(fQ(b), Lds::LDQ, rv, tid_);
+    pk.store(fK(b), Lds::LDQ, rv, tid_);
+    pg.store(sG, Lds::LDQ, rv, tid_);
+    pv.store(fV(b), Lds::LDV, rv, tid_);
+  };
+  auto factors = [&](int ch, int b, int lane_) -> bool {
+    return out_factors<SPT, Lds::LDQ>(fQ(b), fK(b), sG, rows_of(ch), inv_tau, lane_, d0, fEc(b));
   };
 
   ST W;
   bool slow;
-  load_rows(c_begin, tid, lane);
+  load_tiles(c_begin, tid);
   if (is_state) {
     const float* src = P > 1 ? ws_state + ((size_t)unit * NQ + seg) * DK * DV
                              : (s0 ? s0 + (size_t)unit * DK * DV : nullptr);
     W.load(src, DV, sw, lane);
     W.store_copy(sS, Lds::LDS, sw, lane);
   }
-  {
-    const bool small = factors(c_begin, 0, tid, lane);
-    load_rows(min(c_begin + 1, c_end - 1), tid, lane);
-    slow = block_any(small, sFlag, 0, lane, wv);
-  }
+  stage_tiles(c_begin, 0, tid);
+  load_tiles(clamp(c_begin + 1), tid);
+  __syncthreads();
+  slow = block_any(factors(c_begin, 0, lane), sFlag, 0, lane, wv);
+  stage_tiles(clamp(c_begin + 1), 1, tid);
+  load_tiles(clamp(c_begin + 2), tid);
+  __syncthreads();
 
   int b = 0;  // factor set of the current chunk
   for (int ch = c_begin; ch < c_end; ch++) {
@@ -566,7 +578,6 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     int lane_i = lane, tid_i = tid;
     asm volatile("" : "+v"(lane_i), "+v"(tid_i));
     const int t0 = ch * C, rv = rows_of(ch);
-    const int cn = min(ch + 1, c_end - 1);  // next chunk (this one again at the end)
     if (!slow) {
       if (!is_state) {
         bf16_t* orow = ob + (size_t)t0 * DV;
@@ -582,16 +593,19 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
         W.template carry<true>(fV(b), Lds::LDV, fK(b), Lds::LDQ, fEc(b), sw, lane_i);
       }
     } else {
-      gla_exact_chunk<DK, DV>(W, rv, smem, fV(b), qb + (size_t)t0 * DK, kb + (size_t)t0 * DK,
-                              gb + (size_t)t0 * DK, ob + (size_t)t0 * DV, tid_i, inv_tau);
+      gla_exact_chunk<DK, DV>(W, rv, smem + Lds::oX(b), fV(b), qb + (size_t)t0 * DK,
+                              kb + (size_t)t0 * DK, gb + (size_t)t0 * DK, ob + (size_t)t0 * DV, tid_i,
+                              inv_tau);
     }
-    // the next chunk's factors into the other set, then the rows after it
-    // (unconditionally -- the last chunk reloads itself -- so that no branch
-    // blurs the load-count waits)
-    const bool small = factors(cn, b ^ 1, tid_i, lane_i);
-    load_rows(min(ch + 2, c_end - 1), tid_i, lane_i);
+    // the next chunk's factors (this one again at the end, into a set nobody reads)
+    const bool small = factors(clamp(ch + 1), b ^ 1, lane_i);
     slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
     if (is_state) W.store_copy(sS, Lds::LDS, sw, lane_i);
+    // chunk ch+2's rows into this chunk's set (its readers passed the barrier),
+    // then the loads of chunk ch+3 (unconditional, clamped: no branch blurs the
+    // load-count waits)
+    stage_tiles(clamp(ch + 2), b, tid_i);
+    load_tiles(clamp(ch + 3), tid_i);
     __syncthreads();
     b ^= 1;
   }
@@ -614,9 +628,9 @@ static int launch_gla(const GlaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   static const bool lds_set = [] {  // once per instantiation and process
-    hipFuncSetAttribute((const void*)gla_bf16_out<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)gla_bf16_out<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         LO::total);
-    hipFuncSetAttribute((const void*)gla_bf16_state<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)gla_bf16_state<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         LS::total);
     return true;
   }();

@@ -786,9 +786,9 @@ static int launch(const GsaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   static const bool lds_set = [] {  // once per instantiation and process
-    hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LO::total);
-    hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
     return true;
   }();
