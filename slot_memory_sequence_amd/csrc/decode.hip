@@ -9,16 +9,15 @@
 // written once (2 * 2 * m * d * 4 bytes per unit) while the token I/O is tiny,
 // the reason the paper ties inference speed to state size (Sec. 4.1.4).
 //
-// Layout: one workgroup of 256 threads per unit; each thread owns NK float4 of
-// Kt and of Vt (row c = f / (DK/4)), all issued before any arithmetic so that
-// 64 KB per unit are in flight.
+// Layout: one workgroup per unit; each thread owns NK float4 of Kt and of Vt
+// (row c = f / (DK/4)), all loaded before any arithmetic so that the unit's
+// whole state (64 KB at m = 64, d = 128) is in flight at once.
 #include "common.hpp"
 #include "internal.hpp"
 #include "launch.hpp"
 
 namespace gsa {
 
-constexpr int dNT = 256;
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* out);
@@ -49,35 +48,63 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = x;
 }
 
-template <typename T, int DK, int DV, int M>
-__global__ void __launch_bounds__(dNT)
+// float4 of each state per thread (8: 256 threads for m = 64, d = 128) and
+// non-temporal state loads / stores: the fastest pair measured on MI355X for
+// this read-modify-write stream (about 6.1 TB/s, against 5.4 TB/s for plain
+// loads and stores and 5.3-6.0 TB/s for 512 or 1024 threads per unit)
+#ifndef GSA_DECODE_KPER
+#define GSA_DECODE_KPER 8
+#endif
+#ifndef GSA_DECODE_NT
+#define GSA_DECODE_NT 1
+#endif
+
+// The states are streamed once: non-temporal loads and stores keep them from
+// displacing anything in the caches.
+__device__ __forceinline__ f32x4 ld_state(const f32x4* p) {
+  if constexpr (GSA_DECODE_NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+__device__ __forceinline__ void st_state(f32x4* p, f32x4 x) {
+  if constexpr (GSA_DECODE_NT) __builtin_nontemporal_store(x, p);
+  else *p = x;
+}
+
+// Threads per unit: KPER float4 of Kt per thread (at most 1024 threads).
+template <int DK, int M>
+constexpr int decode_threads() {
+  return (M * DK / 4) / GSA_DECODE_KPER > 1024 ? 1024 : (M * DK / 4) / GSA_DECODE_KPER;
+}
+
+template <typename T, int DK, int DV, int M, int NTH>
+__global__ void __launch_bounds__(NTH)
 gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, float* __restrict__ ks, float* __restrict__ vs,
                   T* __restrict__ o, float inv_tau) {
   constexpr int LK = DK / 4, LV = DV / 4;        // float4 per state row
-  constexpr int NK = M * LK / dNT, NV = M * LV / dNT;
-  static_assert(NK >= 1 && NV >= 1 && (M * LK) % dNT == 0 && (M * LV) % dNT == 0, "shape");
+  constexpr int NK = M * LK / NTH, NV = M * LV / NTH;
+  static_assert(NK >= 1 && NV >= 1 && (M * LK) % NTH == 0 && (M * LV) % NTH == 0, "shape");
   static_assert(64 % LK == 0 && 64 % LV == 0, "row width must divide a wave");
   __shared__ float sA[M], sW[M], sZ[M], sS[M];
-  __shared__ float sO[dNT / LV][DV];
+  __shared__ float sO[NTH / LV][DV];
 
   const int tid = threadIdx.x;
   const size_t u = blockIdx.x;
-  float4* kst = reinterpret_cast<float4*>(ks + u * M * DK);
-  float4* vst = reinterpret_cast<float4*>(vs + u * M * DV);
+  f32x4* kst = reinterpret_cast<f32x4*>(ks + u * M * DK);
+  f32x4* vst = reinterpret_cast<f32x4*>(vs + u * M * DV);
 
-  float4 kr[NK], vr[NV];
+  f32x4 kr[NK], vr[NV];
 #pragma unroll
-  for (int i = 0; i < NK; i++) kr[i] = kst[tid + dNT * i];
+  for (int i = 0; i < NK; i++) kr[i] = ld_state(kst + tid + NTH * i);
 #pragma unroll
-  for (int i = 0; i < NV; i++) vr[i] = vst[tid + dNT * i];
+  for (int i = 0; i < NV; i++) vr[i] = ld_state(vst + tid + NTH * i);
 
   const int ck = tid % LK, cv = tid % LV;       // this thread's float4 column
   float qf[4], kf[4], vf[4];
   load4<T>(q + u * DK + 4 * ck, qf);
   load4<T>(k + u * DK + 4 * ck, kf);
   load4<T>(v + u * DV + 4 * cv, vf);
-  for (int c = tid; c < M; c += dNT) {
+  for (int c = tid; c < M; c += NTH) {
     float a, w;
     gate_alpha_w(Elem<T>::to_f(g[u * M + c]), inv_tau, a, w);
     sA[c] = a;
@@ -88,14 +115,12 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   // pass 1: key state update and slot scores
 #pragma unroll
   for (int i = 0; i < NK; i++) {
-    const int c = (tid + dNT * i) / LK;
+    const int c = (tid + NTH * i) / LK;
     const float a = sA[c], w = sW[c];
-    kr[i].x = a * kr[i].x + w * kf[0];
-    kr[i].y = a * kr[i].y + w * kf[1];
-    kr[i].z = a * kr[i].z + w * kf[2];
-    kr[i].w = a * kr[i].w + w * kf[3];
-    kst[tid + dNT * i] = kr[i];
-    float z = kr[i].x * qf[0] + kr[i].y * qf[1] + kr[i].z * qf[2] + kr[i].w * qf[3];
+#pragma unroll
+    for (int e = 0; e < 4; e++) kr[i][e] = a * kr[i][e] + w * kf[e];
+    st_state(kst + tid + NTH * i, kr[i]);
+    float z = kr[i][0] * qf[0] + kr[i][1] * qf[1] + kr[i][2] * qf[2] + kr[i][3] * qf[3];
 #pragma unroll
     for (int off = LK / 2; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
     if (tid % LK == 0) sZ[c] = z;
@@ -118,17 +143,14 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < NV; i++) {
-    const int c = (tid + dNT * i) / LV;
+    const int c = (tid + NTH * i) / LV;
     const float a = sA[c], w = sW[c], s = sS[c];
-    vr[i].x = a * vr[i].x + w * vf[0];
-    vr[i].y = a * vr[i].y + w * vf[1];
-    vr[i].z = a * vr[i].z + w * vf[2];
-    vr[i].w = a * vr[i].w + w * vf[3];
-    vst[tid + dNT * i] = vr[i];
-    acc[0] += s * vr[i].x;
-    acc[1] += s * vr[i].y;
-    acc[2] += s * vr[i].z;
-    acc[3] += s * vr[i].w;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      vr[i][e] = a * vr[i][e] + w * vf[e];
+      acc[e] += s * vr[i][e];
+    }
+    st_state(vst + tid + NTH * i, vr[i]);
   }
   // threads with the same column: tid % LV equal; rows differ by tid / LV
   const int grp = tid / LV;
@@ -138,7 +160,7 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   if (tid < LV) {
     float r[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int gi = 0; gi < dNT / LV; gi++) {
+    for (int gi = 0; gi < NTH / LV; gi++) {
 #pragma unroll
       for (int e = 0; e < 4; e++) r[e] += sO[gi][4 * tid + e];
     }
@@ -148,9 +170,10 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
 
 template <typename T, int DK, int DV, int M>
 static int launch_decode(const DecodeLaunch& a) {
+  constexpr int NTH = decode_threads<DK, M>();
   const unsigned units = (unsigned)a.N * (unsigned)a.H;
-  launch_timed(gsa_decode_kernel<T, DK, DV, M>, dim3(units), dim3(dNT), 0, a.stream, a.events, 0, 1,
-               (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
+  launch_timed(gsa_decode_kernel<T, DK, DV, M, NTH>, dim3(units), dim3(NTH), 0, a.stream, a.events, 0,
+               1, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
                1.0f / a.tau);
   return 0;
 }
