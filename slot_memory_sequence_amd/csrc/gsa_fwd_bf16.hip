@@ -94,7 +94,9 @@ struct StateLds {  // two buffers of everything a chunk needs (software pipeline
 template <int SPT>
 struct LogGates {
   float G[SPT], E[SPT], X[SPT];
-  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
+  // g: a gate row holding at least SPT values
+  template <class Row>
+  __device__ __forceinline__ void compute(const Row& g, bool valid, float inv_tau) {
 #pragma unroll
     for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
     wave_prefix_sums<SPT>(G);
@@ -248,8 +250,8 @@ struct StateTiles {
 // Z = (1-alpha) prod_{i>r} alpha_i and E into one factor set, the whole-chunk
 // decay into dec.  Returns whether any of these slots decays below the range
 // of the factorised form in this chunk.
-template <int SPT, int LDX, int LDE>
-__device__ __forceinline__ bool chunk_factors(const GateRow<SPT>& g, bool valid, float inv_tau,
+template <int SPT, int LDX, int LDE, class Row>
+__device__ __forceinline__ bool chunk_factors(const Row& g, bool valid, float inv_tau,
                                               int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
                                               float* sDec) {
   LogGates<SPT> gt;
@@ -649,7 +651,9 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
   const bool gate_pass = wv < 2;
-  const int slot0 = is_state ? sw * SSL : 4 * SSL + wv * PSL;  // first gate slot (owners)
+  // first gate slot (owners): pass waves 0, 1 own [0, 2 PSL), the state waves
+  // the rest, so that every owner's SSL-wide row read stays inside the row
+  const int slot0 = is_state ? 2 * PSL + sw * SSL : wv * PSL;
   const int seg = blockIdx.x, unit = blockIdx.y;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
@@ -663,42 +667,41 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   // Gate logits, one row per owner: loaded at the top of a chunk for the next
   // chunk (after the exact path, if this chunk takes it, has read this
   // chunk's row) and used after the contractions, when it has long arrived.
-  struct Rows {
-    GateRow<SSL> s;  // state waves
-    GateRow<PSL> p;  // pass waves 0, 1
-  };
-  Rows gr;
-  auto load_gates = [&](Rows& r, int t0, int rv, int lane_) {
-    const bf16_t* p = gb + (size_t)(t0 + min(lane_, rv - 1)) * M;
-    if (is_state) r.s.load(p);
-    else if (gate_pass) r.p.load(p);
+  // One row shape for both roles (pass waves 0, 1 read SSL values and use the
+  // first PSL): two shapes let the compiler merge the two loads into one with
+  // a runtime-chosen destination, which puts the row in scratch memory.
+  typedef GateRow<SSL> Row;
+  static_assert(PSL <= SSL && PSL + SSL <= 2 * PSL + 4 * SSL, "pass-wave rows are prefixes, in bounds");
+  Row gr;
+  auto load_gates = [&](Row& r, int t0, int rv, int lane_) {
+    if (is_state || gate_pass) r.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
   };
   // (the empty asm of pin() keeps the use of the logits, and so the wait for
   // their load, at the call)
-  auto factors = [&](Rows& r, int rv, int fb, int lane_) -> bool {
+  auto factors = [&](Row& r, int rv, int fb, int lane_) -> bool {
     if (is_state) {
-      r.s.pin();
-      return chunk_factors<SSL, Lds::LDX, Lds::LDE>(r.s, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+      r.pin();
+      return chunk_factors<SSL, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
                                                      fE(fb), sDec0 + fb * M);
     }
     if (gate_pass) {
-      r.p.pin();
-      return chunk_factors<PSL, Lds::LDX, Lds::LDE>(r.p, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+      r.template pin<PSL>();
+      return chunk_factors<PSL, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
                                                      fE(fb), sDec0 + fb * M);
     }
     return false;
   };
-  auto log_alpha = [&](const Rows& r, int rv, int lane_) {  // natural log, exact path
+  auto log_alpha = [&](const Row& r, int rv, int lane_) {  // natural log, exact path
     auto put = [&](float x, int s) {
       const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
       sLa[lane_ * M + slot0 + s] = lane_ < rv ? la : 0.f;
     };
     if (is_state) {
 #pragma unroll
-      for (int s = 0; s < SSL; s++) put(r.s.at(s), s);
+      for (int s = 0; s < SSL; s++) put(r.at(s), s);
     } else if (gate_pass) {
 #pragma unroll
-      for (int s = 0; s < PSL; s++) put(r.p.at(s), s);
+      for (int s = 0; s < PSL; s++) put(r.at(s), s);
     }
   };
   auto rows_of = [&](int ch) { return min(C, T_len - ch * C); };
