@@ -629,11 +629,10 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              float* __restrict__ vf, int T_len, int S, int P, float inv_tau) {
   using Lds = OutLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
-  // Who computes which slots' gates for the next chunk: each state wave SSL
-  // slots (after its state update), pass waves 0 and 1 PSL slots each (after
-  // their rows, which need the fewest contractions); waves 2 and 3 none.
-  constexpr int SSL = 3 * M / 16, PSL = M / 8;
-  static_assert(4 * SSL + 2 * PSL == M, "gate slots must cover the slots");
+  // Every wave computes the next chunk's gate factors of GPW slots (after its
+  // contractions): an even split measured faster than giving the state waves
+  // or the lighter pass waves more of them.
+  constexpr int GPW = M / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + Lds::oQ);
   bf16_t* sK = reinterpret_cast<bf16_t*>(smem + Lds::oK);
@@ -650,10 +649,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
-  const bool gate_pass = wv < 2;
-  // first gate slot (owners): pass waves 0, 1 own [0, 2 PSL), the state waves
-  // the rest, so that every owner's SSL-wide row read stays inside the row
-  const int slot0 = is_state ? 2 * PSL + sw * SSL : wv * PSL;
+  const int slot0 = wv * GPW;  // this wave's first gate slot
   const int seg = blockIdx.x, unit = blockIdx.y;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
@@ -661,47 +657,33 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
-  const bf16_t* gb = gg + ub * M + (is_state || gate_pass ? slot0 : 0);
+  const bf16_t* gb = gg + ub * M + slot0;
   bf16_t* ob = oo + ub * DV;
 
   // Gate logits, one row per owner: loaded at the top of a chunk for the next
   // chunk (after the exact path, if this chunk takes it, has read this
   // chunk's row) and used after the contractions, when it has long arrived.
-  // One row shape for both roles (pass waves 0, 1 read SSL values and use the
-  // first PSL): two shapes let the compiler merge the two loads into one with
-  // a runtime-chosen destination, which puts the row in scratch memory.
-  typedef GateRow<SSL> Row;
-  static_assert(PSL <= SSL && PSL + SSL <= 2 * PSL + 4 * SSL, "pass-wave rows are prefixes, in bounds");
+  // (one row type for every wave: rows of two widths here once let the
+  // compiler merge their loads into one with a runtime-chosen destination,
+  // which put the row in scratch memory)
+  typedef GateRow<GPW> Row;
   Row gr;
   auto load_gates = [&](Row& r, int t0, int rv, int lane_) {
-    if (is_state || gate_pass) r.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
+    r.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
   };
   // (the empty asm of pin() keeps the use of the logits, and so the wait for
   // their load, at the call)
   auto factors = [&](Row& r, int rv, int fb, int lane_) -> bool {
-    if (is_state) {
-      r.pin();
-      return chunk_factors<SSL, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
-                                                     fE(fb), sDec0 + fb * M);
-    }
-    if (gate_pass) {
-      r.template pin<PSL>();
-      return chunk_factors<PSL, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
-                                                     fE(fb), sDec0 + fb * M);
-    }
-    return false;
+    r.pin();
+    return chunk_factors<GPW, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+                                                   fE(fb), sDec0 + fb * M);
   };
   auto log_alpha = [&](const Row& r, int rv, int lane_) {  // natural log, exact path
-    auto put = [&](float x, int s) {
+#pragma unroll
+    for (int s = 0; s < GPW; s++) {
+      const float x = r.at(s);
       const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
       sLa[lane_ * M + slot0 + s] = lane_ < rv ? la : 0.f;
-    };
-    if (is_state) {
-#pragma unroll
-      for (int s = 0; s < SSL; s++) put(r.at(s), s);
-    } else if (gate_pass) {
-#pragma unroll
-      for (int s = 0; s < PSL; s++) put(r.at(s), s);
     }
   };
   auto rows_of = [&](int ch) { return min(C, T_len - ch * C); };
@@ -759,7 +741,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       } else {
         W.carry(sK, Lds::LDQ, sV, Lds::LDV, fZ(b), Lds::LDX, sDec0 + b * M, sw, lane_i);
       }
-      // the next chunk's factors (owners: the state waves and pass waves 0, 1)
+      // the next chunk's factors
       small = factors(gr, rv1, b ^ 1, lane_i);
     } else {
       // ---- exact token recurrence (no division by a decay product), on an
