@@ -285,3 +285,80 @@ def test_decode_event_hooks(gsa, torch):
     free()
     assert torch.equal(o1, o2) and torch.equal(ks1, ks2) and torch.equal(vs1, vs2)
     assert t > 0
+
+
+# ------------------------------------------------- decay regimes, hand-offs
+def _decay_chunks(chunks, value):
+    """Gate logit `value` on every token of the listed 64-token chunks."""
+    def mut(inp):
+        x = inp["g"].f64.copy()
+        for c in chunks:
+            x[..., 64 * c:64 * c + 64, :] = value
+        inp["g"] = synth.stored(x, inp["g"].dtype)
+    return mut
+
+
+def _shift_gates(shift):
+    def mut(inp):
+        inp["g"] = synth.stored(inp["g"].f64 + shift, inp["g"].dtype)
+    return mut
+
+
+@pytest.mark.parametrize("case", ["all", "mixed"])
+def test_gsa_bf16_strong_decay(gsa, torch, case):
+    # alpha = sigmoid(g)^(1/8).  "all": g ~ N(-8, 1) makes every 64-token decay
+    # product ~e^-64, below the e^-40 floor of the factorised form, so every
+    # chunk runs the exact recurrence.  "mixed": g = -12 on chunks 1 and 3
+    # (product ~e^-96) and N(0, 1) elsewhere.
+    mut = _shift_gates(-8.0) if case == "all" else _decay_chunks((1, 3), -12.0)
+    for cps in (0, 1):
+        _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, cps=cps, seed=21, mutate=mut)
+
+
+@pytest.mark.parametrize("case", ["all", "mixed"])
+def test_gla_bf16_strong_decay(gsa, torch, case):
+    # tau = 16: g ~ N(-12, 1) makes every 64-token product ~e^-48 (exact
+    # recurrence everywhere); "mixed": g = -12 on chunks 1 and 3 only
+    mut = _shift_gates(-12.0) if case == "all" else _decay_chunks((1, 3), -12.0)
+    for cps in (0, 1):
+        _check_gla(gsa, torch, 1, 3, 64 * 5 + 11, 128, "bf16", init=True, cps=cps, seed=22, mutate=mut)
+
+
+def test_gsa_bf16_split_handoff(gsa, torch):
+    """bf16: fwd over [0,T1) then [T1,T) from the handed-off fp32 state agrees
+    with one call over [0,T) and with the oracle."""
+    inp = synth.gsa_inputs(2, 2, 64 * 6 + 7, 128, 128, 64, dtype="bf16", seed=23, init_std=0.1)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    k0, v0 = to_dev(inp["k0"], torch), to_dev(inp["v0"], torch)
+    T, T1 = q.shape[2], 64 * 2 + 30
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1, k1, v1 = gsa.gsa_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1), k0, v0,
+                             final_state=True)
+    o2, k2, v2 = gsa.gsa_fwd(sl(q, T1, T), sl(k, T1, T), sl(v, T1, T), sl(g, T1, T), k1, v1,
+                             final_state=True)
+    torch.cuda.synchronize()
+    ref = _oracle_gsa(inp, 8.0)
+    o = np.concatenate([to_np(o1), to_np(o2)], axis=2)
+    assert rel_err(o, ref["o"]) <= TOL["bf16"]
+    assert rel_err(to_np(k2), ref["kf"]) <= TOL["bf16"] and rel_err(to_np(v2), ref["vf"]) <= TOL["bf16"]
+
+
+def test_gla_bf16_split_handoff_empty_and_deterministic(gsa, torch):
+    inp = synth.gla_inputs(1, 2, 64 * 5 + 3, 128, 128, dtype="bf16", seed=24, init_std=0.1)
+    q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
+    s0 = to_dev(inp["s0"], torch)
+    T, T1 = q.shape[2], 64 + 17
+    sl = lambda x, a, b: x[:, :, a:b].contiguous()
+    o1, s1 = gsa.gla_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1), s0, final_state=True)
+    o2, s2 = gsa.gla_fwd(sl(q, T1, T), sl(k, T1, T), sl(v, T1, T), sl(g, T1, T), s1, final_state=True)
+    oa, _ = gsa.gla_fwd(q, k, v, g, s0)
+    ob, _ = gsa.gla_fwd(q, k, v, g, s0)
+    # T = 0: the final state is the initial one
+    oz, sz = gsa.gla_fwd(sl(q, 0, 0), sl(k, 0, 0), sl(v, 0, 0), sl(g, 0, 0), s0, final_state=True)
+    torch.cuda.synchronize()
+    ref = oracle.gla_fwd(inp["q"].f64, inp["k"].f64, inp["v"].f64, inp["g"].f64, inp["s0"].f64,
+                         tau=16.0, nthreads=oracle.max_threads())
+    assert rel_err(np.concatenate([to_np(o1), to_np(o2)], axis=2), ref["o"]) <= TOL["bf16"]
+    assert rel_err(to_np(s2), ref["sf"]) <= TOL["bf16"]
+    assert torch.equal(oa, ob)
+    assert oz.numel() == 0 and np.array_equal(to_np(sz), inp["s0"].f64)
