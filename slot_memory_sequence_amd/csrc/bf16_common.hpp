@@ -154,6 +154,24 @@ __device__ __forceinline__ float prev_lane(float x, float first) {
       __builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x), 0x138, 0xf, 0xf, false));
 }
 
+// Max / sum of x over lanes l, l^16, l^32, l^48 (the four lane groups of a
+// 64-lane wave; every lane gets the result).  gfx950's half-wave and row
+// swaps (v_permlane32_swap, v_permlane16_swap), each with one register as both
+// operands, give every lane its partner's value in one of the two results,
+// so the exchange needs no LDS round trip.
+__device__ __forceinline__ float group4_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // log2 alpha = log2(sigmoid(g)) / tau, clamped at -115 (alpha ~ 2.4e-35) so that
 // g = -inf gives a finite value.
 __device__ __forceinline__ float gate_log2(float g, float inv_tau) {

@@ -336,8 +336,7 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
   for (int ct = 0; ct < MT; ct++)
 #pragma unroll
     for (int i = 0; i < 4; i++) mx = fmaxf(mx, op[ct][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = group4_max(mx);
   float sm = 0.f;
 #pragma unroll
   for (int ct = 0; ct < MT; ct++)
@@ -346,8 +345,7 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
       op[ct][i] = __builtin_amdgcn_exp2f((op[ct][i] - mx) * 1.4426950408889634f);
       sm += op[ct][i];
     }
-  sm += __shfl_xor(sm, 16, 64);
-  sm += __shfl_xor(sm, 32, 64);
+  sm = group4_sum(sm);
   const float inv = 1.f / sm;
   // (s*E)^T as B operands over slot pairs (permuted slot index)
   bf16x8 sb[NP];
