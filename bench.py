@@ -330,7 +330,7 @@ def main():
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU (the workload is one GPU's share; "
+        print("bench.py: the benchmark runs on exactly one GPU (the workload is one GPU's share; "
               "nothing here uses collectives). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
