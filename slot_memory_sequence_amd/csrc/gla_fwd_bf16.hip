@@ -578,6 +578,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     int lane_i = lane, tid_i = tid;
     asm volatile("" : "+v"(lane_i), "+v"(tid_i));
     const int t0 = ch * C, rv = rows_of(ch);
+    bool small = false;
     if (!slow) {
       if (!is_state) {
         bf16_t* orow = ob + (size_t)t0 * DV;
@@ -590,6 +591,9 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
           default: gla_pass_chunk<DK, DV, 3>(lane_i, fQ(b), fK(b), fV(b), sS, orow, rv); break;
         }
       } else {
+        // the state waves take the next chunk's factors first: their gate
+        // arithmetic then overlaps the pass waves' contractions on each SIMD
+        small = factors(clamp(ch + 1), b ^ 1, lane_i);
         W.template carry<true>(fV(b), Lds::LDV, fK(b), Lds::LDQ, fEc(b), sw, lane_i);
       }
     } else {
@@ -597,8 +601,9 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
                               kb + (size_t)t0 * DK, gb + (size_t)t0 * DK, ob + (size_t)t0 * DV, tid_i,
                               inv_tau);
     }
-    // the next chunk's factors (this one again at the end, into a set nobody reads)
-    const bool small = factors(clamp(ch + 1), b ^ 1, lane_i);
+    // the next chunk's factors (this one again at the end, into a set nobody
+    // reads), by the waves that have not computed them yet
+    if (slow || !is_state) small = factors(clamp(ch + 1), b ^ 1, lane_i);
     slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
     if (is_state) W.store_copy(sS, Lds::LDS, sw, lane_i);
     // chunk ch+2's rows into this chunk's set (its readers passed the barrier),
