@@ -12,6 +12,9 @@ constexpr int NW = 8;   // waves per workgroup
 constexpr int NT = NW * 64;
 // log2 of the smallest whole-chunk decay the factorised chunk form allows (e^-40)
 constexpr float kFastMinLog2Decay = -57.70780163555854f;
+// Up to this many segment maps before the last segment, the output workgroups
+// build their start states from the maps themselves (no scan launch).
+constexpr int kMaxFoldedMaps = 3;
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
@@ -257,6 +260,22 @@ __device__ __forceinline__ void store_f32_row(float* dst, const float* v) {
 #pragma unroll
     for (int s = 0; s < SPT; s += 2) *reinterpret_cast<float2*>(dst + s) = make_float2(v[s], v[s + 1]);
   }
+}
+
+// Output workgroup -> (segment, unit).  Consecutive workgroup ids are
+// dispatched to the eight XCDs in turn (id mod 8); when the unit count is a
+// multiple of 8, every segment of a unit is placed on one XCD (the ids
+// congruent to the unit mod 8), so that the segments of a unit that read the
+// maps of the segments before them can share them in that XCD's L2.
+struct SegUnit {
+  int seg, unit;
+};
+__device__ __forceinline__ SegUnit seg_unit(int id, int P, int units) {
+  if ((units & 7) == 0) {
+    const int k = id >> 3;
+    return {k % P, (id & 7) + 8 * (k / P)};
+  }
+  return {id % P, id / P};
 }
 
 }  // namespace bfk

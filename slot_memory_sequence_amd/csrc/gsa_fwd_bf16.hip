@@ -28,7 +28,10 @@
 //
 // Launches (no inter-workgroup waiting): state maps of the segments
 // (gsa_bf16_state), a per-unit fp32 scan over the segments (gsa_bf16_scan) and
-// the outputs (gsa_bf16_out).  A chunk whose decay product falls below e^-40
+// the outputs (gsa_bf16_out).  With at most kMaxFoldedMaps maps before the last
+// segment there is no scan launch: each output workgroup folds the maps before
+// its segment into its start state (a dependent launch costs more than a few
+// such reads).  A chunk whose decay product falls below e^-40
 // in some slot is run as the exact token recurrence instead (no division by a
 // decay product).
 #include <type_traits>
@@ -164,6 +167,30 @@ struct StateTiles {
             src + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane));
         st[n][ct] = f32x4{x.x, x.y, x.z, x.w};
       }
+  }
+  // one segment map (layout of load_w) into registers, and the segment step
+  // W <- Diag(dec) W + map with the scan kernel's operation order
+  typedef f32x4 MapRegs[NCW][MT];
+  __device__ __forceinline__ void load_map(MapRegs& x, const float* __restrict__ src, int sw,
+                                           int lane) const {
+#pragma unroll
+    for (int n = 0; n < NCW; n++)
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        const float4 v = *reinterpret_cast<const float4*>(
+            src + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane));
+        x[n][ct] = f32x4{v.x, v.y, v.z, v.w};
+      }
+  }
+  __device__ __forceinline__ void fold(const MapRegs& x, const float* __restrict__ dec, int lane) {
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const float d = dec[16 * ct + (lane & 15)];
+#pragma unroll
+      for (int n = 0; n < NCW; n++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) st[n][ct][i] = d * st[n][ct][i] + x[n][ct][i];
+    }
   }
   // k0 [M][DK], v0 [M][DV], each nullable (zeros)
   __device__ __forceinline__ void load_kv(const float* __restrict__ k0, const float* __restrict__ v0,
@@ -624,7 +651,8 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const bf16_t* __restrict__ vv, const bf16_t* __restrict__ gg,
              const float* __restrict__ k0, const float* __restrict__ v0,
              const float* __restrict__ ws_state, bf16_t* __restrict__ oo, float* __restrict__ kf,
-             float* __restrict__ vf, int T_len, int S, int P, float inv_tau) {
+             float* __restrict__ vf, const float* __restrict__ ws_dec, int T_len, int S, int P,
+             int units, int fold, float inv_tau) {
   using Lds = OutLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   // Every wave computes the next chunk's gate factors of GPW slots (after its
@@ -648,7 +676,8 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
   const int slot0 = wv * GPW;  // this wave's first gate slot
-  const int seg = blockIdx.x, unit = blockIdx.y;
+  const SegUnit su = seg_unit(blockIdx.x, P, units);
+  const int seg = su.seg, unit = su.unit;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
   const size_t ub = (size_t)unit * T_len;
@@ -697,8 +726,28 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     pv.load(vb + (size_t)t0 * DV, rv, tid);
     load_gates(gr, t0, rv, lane);
     if (is_state) {
-      if (P > 1) W.load_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), sw, lane);
-      else W.load_kv(k0 ? k0 + (size_t)unit * M * DK : nullptr, v0 ? v0 + (size_t)unit * M * DV : nullptr, sw, lane);
+      if (P > 1 && !fold) {
+        W.load_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), sw, lane);  // from the scan
+      } else {
+        W.load_kv(k0 ? k0 + (size_t)unit * M * DK : nullptr, v0 ? v0 + (size_t)unit * M * DV : nullptr, sw, lane);
+        // the start state as the segment recurrence over the maps of the
+        // segments before this one, one map loading while the last is folded
+        if (seg > 0) {
+          const float* mp = ws_state + (size_t)unit * P * M * (DK + DV);
+          const float* dp = ws_dec + (size_t)unit * P * M;
+          constexpr size_t MS = (size_t)M * (DK + DV);
+          typename ST::MapRegs xa, xb;
+          W.load_map(xa, mp, sw, lane);
+          for (int p = 0; p < seg; p += 2) {
+            if (p + 1 < seg) W.load_map(xb, mp + (p + 1) * MS, sw, lane);
+            W.fold(xa, dp + (size_t)p * M, lane);
+            if (p + 1 < seg) {
+              if (p + 2 < seg) W.load_map(xa, mp + (p + 2) * MS, sw, lane);
+              W.fold(xb, dp + (size_t)(p + 1) * M, lane);
+            }
+          }
+        }
+      }
       W.store_copy(sW, Lds::LDW, sw, lane);
     }
     slow = block_any(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
@@ -776,20 +825,28 @@ static int launch(const GsaLaunch& a) {
     return true;
   }();
   (void)lds_set;
+  // With few segments the output workgroups fold the maps of the segments
+  // before theirs into their start state themselves: that costs the last
+  // segment's workgroup P - 1 map reads, all through one CU, and saves the scan
+  // launch and its wait (measured: a gain at 1 and 3 maps, a loss at 7).
+  const int fold = P > 1 && P - 1 <= kMaxFoldedMaps;
   if (P > 1) {
     launch_timed(gsa_bf16_state<DK, DV, M>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
                  a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
                  a.ws_state, a.ws_dec, a.T, S, P, inv_tau);
-    const long long ne = (long long)units * M * (DK + DV);
-    hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
-                       a.ws_state, (const float*)a.ws_dec, a.k0, a.v0, units, P);
+    if (!fold) {
+      const long long ne = (long long)units * M * (DK + DV);
+      hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
+                         a.ws_state, (const float*)a.ws_dec, a.k0, a.v0, units, P);
+    }
   } else {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gsa_bf16_out<DK, DV, M>, dim3(P, units), dim3(NT), LO::total, a.stream, a.events, 2,
+  launch_timed(gsa_bf16_out<DK, DV, M>, dim3(P * units), dim3(NT), LO::total, a.stream, a.events, 2,
                3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
-               a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, a.T, S, P, inv_tau);
+               a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, (const float*)a.ws_dec,
+               a.T, S, P, units, fold, inv_tau);
   return 0;
 }
 

@@ -87,6 +87,15 @@ def test_gsa_segmentations(gsa, torch, cps):
     _check_gsa(gsa, torch, 1, 2, 64 * 5 + 9, 64, 32, "f32", init=True, cps=cps, seed=4)
 
 
+@pytest.mark.parametrize("cps", [1, 2, 3, 4])
+def test_gsa_bf16_segments_xcd_placement(gsa, torch, cps):
+    """8 units, so every segment of a unit runs on one XCD; 10 chunks with a
+    ragged tail and initial states.  cps 4 / 3: 3 / 4 segments, whose output
+    workgroups build their start states from 2 / 3 segment maps themselves;
+    cps 2 / 1: 5 / 10 segments, start states from the scan kernel."""
+    _check_gsa(gsa, torch, 2, 4, 64 * 9 + 13, 128, 64, "bf16", init=True, cps=cps, seed=31)
+
+
 def _extreme(inp):
     g = inp["g"]
     x = g.f64.copy()
