@@ -21,7 +21,9 @@
 // the start state of every output segment (gla_bf16_scan), and the outputs
 // (gla_bf16_out).  The state-map pass may split each output segment into
 // several sub-segments so that it fills the chip when there are few
-// (batch, head) units.
+// (batch, head) units.  With at most kMaxFoldedMaps maps before the last
+// segment the output workgroups fold them into their start states themselves
+// and there is no scan launch.
 //
 // Output kernel, per workgroup of 512 threads:
 //   waves 0..3 ("pass"): token rows 16J..16J+15 of the chunk (J = wave);
@@ -131,6 +133,30 @@ struct GlaTiles {
       for (int b = 0; b < NB; b++)
         *reinterpret_cast<float4*>(S + (size_t)(c_of(sw, b) + L) * ld + n_of(sw, a) + 4 * g) =
             make_float4(st[a][b][0], st[a][b][1], st[a][b][2], st[a][b][3]);
+  }
+  // one sub-segment map (layout of load) into registers, and the segment step
+  // S <- Diag(dec) S + map (rows = key dimensions) with the scan kernel's
+  // operation order
+  typedef f32x4 MapRegs[NA][NB];
+  __device__ __forceinline__ void load_map(MapRegs& x, const float* __restrict__ S, int sw, int lane) const {
+    const int L = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int a = 0; a < NA; a++)
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        const float4 v = *reinterpret_cast<const float4*>(S + (size_t)(c_of(sw, b) + L) * DV + n_of(sw, a) + 4 * g);
+        x[a][b] = f32x4{v.x, v.y, v.z, v.w};
+      }
+  }
+  __device__ __forceinline__ void fold(const MapRegs& x, const float* __restrict__ dec, int sw, int lane) {
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const float d = dec[c_of(sw, b) + (lane & 15)];
+#pragma unroll
+      for (int a = 0; a < NA; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) st[a][b][i] = d * st[a][b][i] + x[a][b][i];
+    }
   }
   // bf16 copy of S, row-major [DK][ld]
   __device__ __forceinline__ void store_copy(bf16_t* sS, int ld, int sw, int lane) const {
@@ -503,8 +529,8 @@ __global__ void __launch_bounds__(NT, 1)
 gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const bf16_t* __restrict__ vv, const bf16_t* __restrict__ gg,
              const float* __restrict__ s0, const float* __restrict__ ws_state,
-             bf16_t* __restrict__ oo, float* __restrict__ sf, int T_len, int S, int P, int NQ,
-             float inv_tau) {
+             bf16_t* __restrict__ oo, float* __restrict__ sf, const float* __restrict__ ws_dec,
+             int T_len, int S, int P, int NQ, int R, int fold, float inv_tau) {
   using Lds = GlaOutLds<DK, DV>;
   using ST = GlaTiles<DK, DV, 4>;
   constexpr int SPT = DK / NW;
@@ -558,9 +584,21 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   bool slow;
   load_tiles(c_begin, tid);
   if (is_state) {
-    const float* src = P > 1 ? ws_state + ((size_t)unit * NQ + seg) * DK * DV
-                             : (s0 ? s0 + (size_t)unit * DK * DV : nullptr);
-    W.load(src, DV, sw, lane);
+    if (P > 1 && !fold) {
+      W.load(ws_state + ((size_t)unit * NQ + seg) * DK * DV, DV, sw, lane);  // from the scan
+    } else {
+      W.load(s0 ? s0 + (size_t)unit * DK * DV : nullptr, DV, sw, lane);
+      // the start state as the segment recurrence over the sub-segment maps
+      // before this segment (one map at a time: the chunk's tiles are live)
+      const int nm = seg * R;
+      const float* mp = ws_state + (size_t)unit * NQ * DK * DV;
+      const float* dp = ws_dec + (size_t)unit * NQ * DK;
+      for (int p = 0; p < nm; p++) {
+        typename ST::MapRegs x;
+        W.load_map(x, mp + (size_t)p * DK * DV, sw, lane);
+        W.fold(x, dp + (size_t)p * DK, sw, lane);
+      }
+    }
     W.store_copy(sS, Lds::LDS, sw, lane);
   }
   stage_tiles(c_begin, 0, tid);
@@ -640,20 +678,27 @@ static int launch_gla(const GlaLaunch& a) {
     return true;
   }();
   (void)lds_set;
+  // As in the GSA forward: with at most kMaxFoldedMaps maps before the last
+  // segment, the output workgroups fold them into their start states (no scan
+  // launch), unless the final state is written over s0.
+  const int fold = P > 1 && Q <= kMaxFoldedMaps && !(a.sf && a.sf == a.s0);
   if (P > 1) {
     launch_timed(gla_bf16_state<DK, DV>, dim3(Q, units), dim3(NT), LS::total, a.stream, a.events, 0, 1,
                  (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g, a.ws_state, a.ws_dec, a.T,
                  S, R, NQ, inv_tau);
-    const long long ne = (long long)units * DK * DV;
-    hipLaunchKernelGGL((gla_bf16_scan<DK, DV>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
-                       a.ws_state, (const float*)a.ws_dec, a.s0, units, P, R, NQ);
+    if (!fold) {
+      const long long ne = (long long)units * DK * DV;
+      hipLaunchKernelGGL((gla_bf16_scan<DK, DV>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
+                         a.ws_state, (const float*)a.ws_dec, a.s0, units, P, R, NQ);
+    }
   } else {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
   launch_timed(gla_bf16_out<DK, DV>, dim3(P, units), dim3(NT), LO::total, a.stream, a.events, 2, 3,
                (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g, a.s0,
-               (const float*)a.ws_state, (bf16_t*)a.o, a.sf, a.T, S, P, NQ, inv_tau);
+               (const float*)a.ws_state, (bf16_t*)a.o, a.sf, (const float*)a.ws_dec, a.T, S, P, NQ, R,
+               fold, inv_tau);
   return 0;
 }
 

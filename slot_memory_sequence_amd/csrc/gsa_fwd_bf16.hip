@@ -828,8 +828,11 @@ static int launch(const GsaLaunch& a) {
   // With few segments the output workgroups fold the maps of the segments
   // before theirs into their start state themselves: that costs the last
   // segment's workgroup P - 1 map reads, all through one CU, and saves the scan
-  // launch and its wait (measured: a gain at 1 and 3 maps, a loss at 7).
-  const int fold = P > 1 && P - 1 <= kMaxFoldedMaps;
+  // launch and its wait (measured: a gain at 1 and 3 maps, a loss at 7).  Every
+  // output workgroup then reads k0 / v0, so not when the final state is written
+  // over them (the last segment could finish before another one has started).
+  const bool in_place = (a.kf && a.kf == a.k0) || (a.vf && a.vf == a.v0);
+  const int fold = P > 1 && P - 1 <= kMaxFoldedMaps && !in_place;
   if (P > 1) {
     launch_timed(gsa_bf16_state<DK, DV, M>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
                  a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,

@@ -195,6 +195,15 @@ def test_gla_bf16_split_ragged(gsa, torch, cps):
     _check_gla(gsa, torch, 1, 3, 64 * 9 + 17, 128, "bf16", init=True, cps=cps, seed=11)
 
 
+@pytest.mark.parametrize("cps", [1, 2, 3])
+def test_gla_bf16_folded_start_states(gsa, torch, cps):
+    """8 units, 4 chunks with a ragged tail, initial state.  cps 1: 4 segments
+    of one chunk (3 maps before the last); cps 2 / 3: 2 segments whose state
+    maps split into 2 / 3 sub-segments.  Few enough maps that the output
+    workgroups fold them into their start states themselves."""
+    _check_gla(gsa, torch, 2, 4, 64 * 3 + 17, 128, "bf16", init=True, cps=cps, seed=41)
+
+
 def test_gla_extreme_gates(gsa, torch):
     def mut(inp):
         x = inp["g"].f64.copy()
@@ -343,9 +352,11 @@ def test_gsa_bf16_split_handoff(gsa, torch):
     sl = lambda x, a, b: x[:, :, a:b].contiguous()
     o1, k1, v1 = gsa.gsa_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1), k0, v0,
                              final_state=True)
+    # the second call advances the state in place (4 chunks, one per segment)
     o2, k2, v2 = gsa.gsa_fwd(sl(q, T1, T), sl(k, T1, T), sl(v, T1, T), sl(g, T1, T), k1, v1,
-                             final_state=True)
+                             final_state=True, k_final=k1, v_final=v1, chunks_per_segment=1)
     torch.cuda.synchronize()
+    assert k2.data_ptr() == k1.data_ptr() and v2.data_ptr() == v1.data_ptr()
     ref = _oracle_gsa(inp, 8.0)
     o = np.concatenate([to_np(o1), to_np(o2)], axis=2)
     assert rel_err(o, ref["o"]) <= TOL["bf16"]
@@ -359,7 +370,9 @@ def test_gla_bf16_split_handoff_empty_and_deterministic(gsa, torch):
     T, T1 = q.shape[2], 64 + 17
     sl = lambda x, a, b: x[:, :, a:b].contiguous()
     o1, s1 = gsa.gla_fwd(sl(q, 0, T1), sl(k, 0, T1), sl(v, 0, T1), sl(g, 0, T1), s0, final_state=True)
-    o2, s2 = gsa.gla_fwd(sl(q, T1, T), sl(k, T1, T), sl(v, T1, T), sl(g, T1, T), s1, final_state=True)
+    # the second call advances the state in place (4 chunks, one per segment)
+    o2, s2 = gsa.gla_fwd(sl(q, T1, T), sl(k, T1, T), sl(v, T1, T), sl(g, T1, T), s1, final_state=True,
+                         s_final=s1, chunks_per_segment=1)
     oa, _ = gsa.gla_fwd(q, k, v, g, s0)
     ob, _ = gsa.gla_fwd(q, k, v, g, s0)
     # T = 0: the final state is the initial one
@@ -368,6 +381,6 @@ def test_gla_bf16_split_handoff_empty_and_deterministic(gsa, torch):
     ref = oracle.gla_fwd(inp["q"].f64, inp["k"].f64, inp["v"].f64, inp["g"].f64, inp["s0"].f64,
                          tau=16.0, nthreads=oracle.max_threads())
     assert rel_err(np.concatenate([to_np(o1), to_np(o2)], axis=2), ref["o"]) <= TOL["bf16"]
-    assert rel_err(to_np(s2), ref["sf"]) <= TOL["bf16"]
+    assert s2.data_ptr() == s1.data_ptr() and rel_err(to_np(s2), ref["sf"]) <= TOL["bf16"]
     assert torch.equal(oa, ob)
     assert oz.numel() == 0 and np.array_equal(to_np(sz), inp["s0"].f64)
