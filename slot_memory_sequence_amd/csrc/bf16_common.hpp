@@ -263,15 +263,16 @@ __device__ __forceinline__ void store_f32_row(float* dst, const float* v) {
 }
 
 // Output workgroup -> (segment, unit).  Consecutive workgroup ids are
-// dispatched to the eight XCDs in turn (id mod 8); when the unit count is a
-// multiple of 8, every segment of a unit is placed on one XCD (the ids
-// congruent to the unit mod 8), so that the segments of a unit that read the
-// maps of the segments before them can share them in that XCD's L2.
+// dispatched to the eight XCDs in turn (id mod 8).  When the output workgroups
+// fold segment maps (fold != 0) and the unit count is a multiple of 8, every
+// segment of a unit is placed on one XCD (the ids congruent to the unit mod 8),
+// so that the segments of a unit can share its maps in that XCD's L2;
+// otherwise the segments of a unit have consecutive ids.
 struct SegUnit {
   int seg, unit;
 };
-__device__ __forceinline__ SegUnit seg_unit(int id, int P, int units) {
-  if ((units & 7) == 0) {
+__device__ __forceinline__ SegUnit seg_unit(int id, int P, int units, int fold) {
+  if (fold && (units & 7) == 0) {
     const int k = id >> 3;
     return {k % P, (id & 7) + 8 * (k / P)};
   }

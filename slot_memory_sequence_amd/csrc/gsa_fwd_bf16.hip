@@ -676,7 +676,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bool is_state = wv >= 4;
   const int sw = wv - 4;
   const int slot0 = wv * GPW;  // this wave's first gate slot
-  const SegUnit su = seg_unit(blockIdx.x, P, units);
+  const SegUnit su = seg_unit(blockIdx.x, P, units, fold);
   const int seg = su.seg, unit = su.unit;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
