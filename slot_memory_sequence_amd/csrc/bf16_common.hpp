@@ -87,6 +87,28 @@ struct Tile {
           make_uint4(ok ? r[i].x : 0u, ok ? r[i].y : 0u, ok ? r[i].z : 0u, ok ? r[i].w : 0u);
     }
   }
+  // The same with a uniform branch for full tiles (no row clamp, no zeroing):
+  // fewer vector instructions, for kernels whose waits do not depend on the
+  // loads being branch-free (the output kernels' prefetches do).
+  __device__ __forceinline__ void load_branchy(const bf16_t* __restrict__ base, int rows_valid, int tid) {
+    if (rows_valid >= C) {
+#pragma unroll
+      for (int i = 0; i < NV; i++) r[i] = *reinterpret_cast<const uint4*>(base + (size_t)(tid + NT * i) * 8);
+    } else {
+      load(base, rows_valid, tid);
+    }
+  }
+  __device__ __forceinline__ void store_branchy(bf16_t* dst, int ld, int rows_valid, int tid) const {
+    if (rows_valid >= C) {
+#pragma unroll
+      for (int i = 0; i < NV; i++) {
+        const int idx = tid + NT * i, row = idx / VPR, cv = idx % VPR;
+        *reinterpret_cast<uint4*>(dst + row * ld + cv * 8) = r[i];
+      }
+    } else {
+      store(dst, ld, rows_valid, tid);
+    }
+  }
 };
 
 // SPT gate logits of one token row (SPT = 4 or 8 bf16 = 8 or 16 bytes).

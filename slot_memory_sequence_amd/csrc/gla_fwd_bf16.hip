@@ -449,11 +449,11 @@ gla_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
     const size_t row = (size_t)(t0 + min(lane_, rv - 1)) * DK;
     rk.load(kb + row);
     rg.load(gb + row);
-    pv.load(vb + (size_t)t0 * DV, rv, tid_);
+    pv.load_branchy(vb + (size_t)t0 * DV, rv, tid_);
   };
   auto stage_chunk = [&](int ch, int b, bool count, int tid_, int lane_) {
     const int rv = min(C, T_len - ch * C);
-    pv.store(bV(b), Lds::LDV, rv, tid_);
+    pv.store_branchy(bV(b), Lds::LDV, rv, tid_);
     map_factors<SPT, Lds::LDQ>(rk, rg, rv, inv_tau, lane_, d0, bK(b), bEc(b), dec, count);
   };
 
