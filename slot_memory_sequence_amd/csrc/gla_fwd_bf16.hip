@@ -48,20 +48,22 @@ template <int DK, int DV>
 struct GlaOutLds {
   static constexpr int PAD = 8;
   static constexpr int LDQ = DK + PAD, LDV = DV + PAD, LDS = DV + PAD;
-  // V tiles of both factor sets
+  // V tile of the current chunk (staged one chunk ahead, after the barrier
+  // that ends its readers)
   static constexpr int szV = C * LDV * 2;
   static constexpr int oV = 0;
   // factor set b: Qt, Kt [C][LDQ] bf16 (raw q, k until the factor step turns
   // them into Qt, Kt in place); the bf16 copy of S [DK][LDS] sits between the
   // two sets so that either set and the copy form one contiguous region
   static constexpr int szQK = 2 * C * LDQ * 2;
-  static constexpr int oF0 = 2 * szV;
+  static constexpr int oF0 = szV;
   static constexpr int oS = oF0 + szQK;
   static constexpr int oF1 = oS + DK * LDS * 2;
   static constexpr int fQ = 0, fK = C * LDQ * 2;
   static constexpr int oEc = oF1 + szQK;                 // 2 x [DK] fp32
-  static constexpr int oG = oEc + 2 * DK * 4;            // raw gate logits [C][LDQ] bf16
-  static constexpr int oFlag = oG + C * LDQ * 2;         // 2 x NW ints
+  static constexpr int szG = C * LDQ * 2;                // raw gate logits [C][LDQ] bf16
+  static constexpr int oG0 = oEc + 2 * DK * 4;           // of set 0, then of set 1
+  static constexpr int oFlag = oG0 + 2 * szG;            // 2 x NW ints
   static constexpr int total = oFlag + 2 * NW * 4;
   // exact path, inside [set b | copy of S] (b = 0) or [copy of S | set 1]
   // (b = 1): fp32 S [DK][DV] for the change of layout, then (after it was
@@ -70,9 +72,11 @@ struct GlaOutLds {
   static constexpr int xSf = 0, xQr = 0, xKr = C * DK * 2, xGr = 2 * C * DK * 2, xOp = 3 * C * DK * 2;
   static_assert(DK * DV * 4 <= szR && xOp + NW * DV * 4 <= szR, "exact path must fit its region");
   __device__ __forceinline__ static int oF(int b) { return b ? oF1 : oF0; }
+  __device__ __forceinline__ static int oG(int b) { return oG0 + b * szG; }
   __device__ __forceinline__ static int oX(int b) { return b ? oS : oF0; }
   static_assert(szV % 16 == 0 && szQK % 16 == 0 && oS % 16 == 0 && oF1 % 16 == 0 && oEc % 16 == 0 &&
-                    oG % 16 == 0 && oFlag % 16 == 0 && xKr % 16 == 0 && xGr % 16 == 0 && xOp % 16 == 0,
+                    oG0 % 16 == 0 && szG % 16 == 0 && oFlag % 16 == 0 && xKr % 16 == 0 &&
+                    xGr % 16 == 0 && xOp % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
 };
 
@@ -519,11 +523,12 @@ gla_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec, co
 }
 
 // ------------------------------------------------------ phase C: outputs
-// Per chunk c (factor set b = c & 1): the contractions of chunk c; the factors
-// of chunk c+1 from its rows staged in set b^1; a barrier; the state copy and
-// the staging of chunk c+2's rows (loaded one chunk earlier as coalesced tiles)
-// into set b, the g tile and the V slot of set b; the loads of chunk c+3; a
-// barrier.
+// Per chunk c (factor set b = c & 1): the contractions of chunk c (pass waves)
+// beside the state waves' share of chunk c+1's factors and their carry; a
+// barrier; the state copy, chunk c+1's v into the V slot and chunk c+2's q, k,
+// g rows (loaded one chunk earlier as coalesced tiles) into set b; the loads
+// of chunks c+3 and c+2; the pass waves' share of chunk c+1's factors (from
+// set b^1); a barrier that also combines the exact-path votes.
 template <int DK, int DV>
 __global__ void __launch_bounds__(NT, 1)
 gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
@@ -535,12 +540,12 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   using ST = GlaTiles<DK, DV, 4>;
   constexpr int SPT = DK / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  auto fV = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oV + b * Lds::szV); };
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Lds::oV);
   auto fQ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF(b) + Lds::fQ); };
   auto fK = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF(b) + Lds::fK); };
   auto fEc = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oEc + b * DK * 4); };
   bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
-  bf16_t* sG = reinterpret_cast<bf16_t*>(smem + Lds::oG);
+  auto fG = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oG(b)); };
   int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -559,30 +564,33 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   auto rows_of = [&](int ch) { return min(C, T_len - ch * C); };
   auto clamp = [&](int ch) { return min(ch, c_end - 1); };
 
-  // raw tiles of a later chunk in registers (coalesced loads)
+  // raw tiles of later chunks in registers (coalesced loads): q, k, g three
+  // chunks ahead (staged two ahead, into the factor set of their chunk), v two
+  // ahead (staged one ahead, into the single V slot)
   Tile<DK> pq, pk, pg;
   Tile<DV> pv;
-  auto load_tiles = [&](int ch, int tid_) {
+  auto load_qkg = [&](int ch, int tid_) {
     const int t0 = ch * C, rv = rows_of(ch);
     pq.load(qb + (size_t)t0 * DK, rv, tid_);
     pk.load(kb + (size_t)t0 * DK, rv, tid_);
     pg.load(gb + (size_t)t0 * DK, rv, tid_);
-    pv.load(vb + (size_t)t0 * DV, rv, tid_);
   };
-  auto stage_tiles = [&](int ch, int b, int tid_) {  // rows >= rv are zeroed
+  auto load_v = [&](int ch, int tid_) { pv.load(vb + (size_t)ch * C * DV, rows_of(ch), tid_); };
+  auto stage_qkg = [&](int ch, int b, int tid_) {  // rows >= rv are zeroed
     const int rv = rows_of(ch);
     pq.store(fQ(b), Lds::LDQ, rv, tid_);
     pk.store(fK(b), Lds::LDQ, rv, tid_);
-    pg.store(sG, Lds::LDQ, rv, tid_);
-    pv.store(fV(b), Lds::LDV, rv, tid_);
+    pg.store(fG(b), Lds::LDQ, rv, tid_);
   };
+  auto stage_v = [&](int ch, int tid_) { pv.store(sV, Lds::LDV, rows_of(ch), tid_); };
   auto factors = [&](int ch, int b, int lane_) -> bool {
-    return out_factors<SPT, Lds::LDQ>(fQ(b), fK(b), sG, rows_of(ch), inv_tau, lane_, d0, fEc(b));
+    return out_factors<SPT, Lds::LDQ>(fQ(b), fK(b), fG(b), rows_of(ch), inv_tau, lane_, d0, fEc(b));
   };
 
   ST W;
   bool slow;
-  load_tiles(c_begin, tid);
+  load_qkg(c_begin, tid);
+  load_v(c_begin, tid);
   if (is_state) {
     if (P > 1 && !fold) {
       W.load(ws_state + ((size_t)unit * NQ + seg) * DK * DV, DV, sw, lane);  // from the scan
@@ -601,12 +609,14 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     }
     W.store_copy(sS, Lds::LDS, sw, lane);
   }
-  stage_tiles(c_begin, 0, tid);
-  load_tiles(clamp(c_begin + 1), tid);
+  stage_qkg(c_begin, 0, tid);
+  stage_v(c_begin, tid);
+  load_qkg(clamp(c_begin + 1), tid);
+  load_v(clamp(c_begin + 1), tid);
   __syncthreads();
   slow = block_any(factors(c_begin, 0, lane), sFlag, 0, lane, wv);
-  stage_tiles(clamp(c_begin + 1), 1, tid);
-  load_tiles(clamp(c_begin + 2), tid);
+  stage_qkg(clamp(c_begin + 1), 1, tid);
+  load_qkg(clamp(c_begin + 2), tid);
   __syncthreads();
 
   int b = 0;  // factor set of the current chunk
@@ -623,33 +633,38 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
         // pass waves hold no state: dropping it frees these registers for the passes
         W.zero();
         switch (wv) {
-          case 0: gla_pass_chunk<DK, DV, 0>(lane_i, fQ(b), fK(b), fV(b), sS, orow, rv); break;
-          case 1: gla_pass_chunk<DK, DV, 1>(lane_i, fQ(b), fK(b), fV(b), sS, orow, rv); break;
-          case 2: gla_pass_chunk<DK, DV, 2>(lane_i, fQ(b), fK(b), fV(b), sS, orow, rv); break;
-          default: gla_pass_chunk<DK, DV, 3>(lane_i, fQ(b), fK(b), fV(b), sS, orow, rv); break;
+          case 0: gla_pass_chunk<DK, DV, 0>(lane_i, fQ(b), fK(b), sV, sS, orow, rv); break;
+          case 1: gla_pass_chunk<DK, DV, 1>(lane_i, fQ(b), fK(b), sV, sS, orow, rv); break;
+          case 2: gla_pass_chunk<DK, DV, 2>(lane_i, fQ(b), fK(b), sV, sS, orow, rv); break;
+          default: gla_pass_chunk<DK, DV, 3>(lane_i, fQ(b), fK(b), sV, sS, orow, rv); break;
         }
       } else {
         // the state waves take the next chunk's factors first: their gate
         // arithmetic then overlaps the pass waves' contractions on each SIMD
         small = factors(clamp(ch + 1), b ^ 1, lane_i);
-        W.template carry<true>(fV(b), Lds::LDV, fK(b), Lds::LDQ, fEc(b), sw, lane_i);
+        W.template carry<true>(sV, Lds::LDV, fK(b), Lds::LDQ, fEc(b), sw, lane_i);
       }
     } else {
-      gla_exact_chunk<DK, DV>(W, rv, smem + Lds::oX(b), fV(b), qb + (size_t)t0 * DK,
+      gla_exact_chunk<DK, DV>(W, rv, smem + Lds::oX(b), sV, qb + (size_t)t0 * DK,
                               kb + (size_t)t0 * DK, gb + (size_t)t0 * DK, ob + (size_t)t0 * DV, tid_i,
                               inv_tau);
     }
+    // every wave is done with the copy of S, the V slot and this chunk's set
+    __syncthreads();
+    if (is_state) W.store_copy(sS, Lds::LDS, sw, lane_i);
+    // the next chunk's v into the V slot, chunk ch+2's rows into this chunk's
+    // set, then the loads of chunks ch+3 (q, k, g) and ch+2 (v) (unconditional,
+    // clamped: no branch blurs the load-count waits)
+    stage_v(clamp(ch + 1), tid_i);
+    stage_qkg(clamp(ch + 2), b, tid_i);
+    load_qkg(clamp(ch + 3), tid_i);
+    load_v(clamp(ch + 2), tid_i);
     // the next chunk's factors (this one again at the end, into a set nobody
-    // reads), by the waves that have not computed them yet
+    // reads) by the waves that have not computed them yet: the pass waves'
+    // gate arithmetic runs here, beside the state waves' copy of S (the rows
+    // it reads, set b^1 and its g tile, are not written in this chunk)
     if (slow || !is_state) small = factors(clamp(ch + 1), b ^ 1, lane_i);
     slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
-    if (is_state) W.store_copy(sS, Lds::LDS, sw, lane_i);
-    // chunk ch+2's rows into this chunk's set (its readers passed the barrier),
-    // then the loads of chunk ch+3 (unconditional, clamped: no branch blurs the
-    // load-count waits)
-    stage_tiles(clamp(ch + 2), b, tid_i);
-    load_tiles(clamp(ch + 3), tid_i);
-    __syncthreads();
     b ^= 1;
   }
 
