@@ -32,7 +32,9 @@
 //   all waves: the next chunk's factors Qt, Kt, E_C (key dimensions
 //              [DK/8 w, DK/8 (w+1)) of every token, token = lane, so that the
 //              cumulative decay is a wave-wide prefix sum), into the second of
-//              two factor sets.
+//              two factor sets: the state waves before the chunk's first
+//              barrier (beside the pass waves' contractions), the pass waves
+//              after it (beside the state copy).
 // A chunk whose decay product falls below e^-40 in some key dimension runs as
 // the exact token recurrence instead (no division by a decay product).
 #include "bf16_common.hpp"
