@@ -18,6 +18,7 @@ constexpr int kMaxFoldedMaps = 3;
 
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -219,7 +219,18 @@ struct StateTiles {
       for (int ct = 0; ct < MT; ct++)
         *reinterpret_cast<float4*>(dst + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane)) =
             make_float4(st[n][ct][0], st[n][ct][1], st[n][ct][2], st[n][ct][3]);
+  }  // the same to global memory with streaming stores: a segment map is read
+  // only by the next launch, so its lines need not stay in L2 (less for the
+  // end of the kernel to write back)
+  __device__ __forceinline__ void store_w_nt(float* __restrict__ dst, int sw, int lane) const {
+#pragma unroll
+    for (int n = 0; n < NCW; n++)
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++)
+        __builtin_nontemporal_store(
+            st[n][ct], reinterpret_cast<f32x4*>(dst + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane)));
   }
+
   __device__ __forceinline__ void store_kv(float* __restrict__ kf, float* __restrict__ vf, int sw,
                                            int lane) const {
 #pragma unroll
@@ -427,7 +438,9 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
     if (store) {
 #pragma unroll
       for (int u = 0; u < NG; u++)
-        *reinterpret_cast<bf16x4v*>(orow + (size_t)j * DV + 16 * (n0 + u) + 4 * g) = pack4(acc[u]);
+        // streaming store: the outputs are not read again by this operation
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
+                                    reinterpret_cast<u32x2*>(orow + (size_t)j * DV + 16 * (n0 + u) + 4 * g));
     }
   }
 }
@@ -595,7 +608,7 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
     __syncthreads();
     b ^= 1;
   }
-  W.store_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), wv, lane);
+  W.store_w_nt(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), wv, lane);
   if (lane == 0) {
 #pragma unroll
     for (int s = 0; s < SPT; s++) ws_dec[((size_t)unit * P + seg) * M + wv * SPT + s] = segdec[s];
@@ -636,12 +649,12 @@ gsa_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
       if (p0 + i + 1 < P) {
-        st[(size_t)(p0 + i) * NE] = W;
+        __builtin_nontemporal_store(W, st + (size_t)(p0 + i) * NE);  // read only by the next launch
         W = d[i] * W + x[i];
       }
     }
   }
-  st[(size_t)(P - 1) * NE] = W;
+  __builtin_nontemporal_store(W, st + (size_t)(P - 1) * NE);
 }
 
 // ------------------------------------------------------ phase C: outputs
