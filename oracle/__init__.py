@@ -53,7 +53,10 @@ def _load():
         lib.oracle_gsa_fwd.argtypes = [P] * 11 + [L] * 6 + [D, I]
         lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
         lib.oracle_gsa_decode_step.argtypes = [P] * 7 + [L] * 5 + [D, I]
-        for f in (lib.oracle_gsa_fwd, lib.oracle_gla_fwd, lib.oracle_gsa_decode_step):
+        lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
+        lib.oracle_gsa_decode_step_nl.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
+        for f in (lib.oracle_gsa_fwd, lib.oracle_gla_fwd, lib.oracle_gsa_decode_step,
+                  lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl):
             f.restype = I
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -70,15 +73,29 @@ def _p(x):
     return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
 
 
+# Slot read non-linearity: the softmax over the slots (Sec. 3.2) or one of the
+# element-wise replacements of the ablation study (Table 2).
+NONLINEARITIES = {"softmax": 0, "identity": 1, "swish": 2, "relu": 3, "relu2": 4}
+
+
+def _nl(nonlinearity) -> int:
+    if isinstance(nonlinearity, str):
+        return NONLINEARITIES[nonlinearity]
+    if int(nonlinearity) not in NONLINEARITIES.values():
+        raise ValueError("unknown slot non-linearity %r" % (nonlinearity,))
+    return int(nonlinearity)
+
+
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
 
 def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, want_states=True,
-            want_scores=False, nthreads=1):
+            want_scores=False, nthreads=1, nonlinearity="softmax"):
     """Recurrent GSA forward.  q,k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m];
     k0 [B,H,m,dk], v0 [B,H,m,dv] optional.  Returns dict with o, and the final
-    states kf/vf, slot softmax s and raw slot scores z when asked for."""
+    states kf/vf, slot read weights s (the softmax unless another
+    nonlinearity is named) and raw slot scores z when asked for."""
     q, k, v, g, k0, v0 = map(_f64, (q, k, v, g, k0, v0))
     B, H, T, dk = q.shape
     dv = v.shape[-1]
@@ -93,9 +110,9 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, want_states=True,
     vf = np.empty((B, H, m, dv)) if want_states else None
     s = np.empty((B, H, T, m)) if want_scores else None
     z = np.empty((B, H, T, m)) if want_scores else None
-    rc = _load().oracle_gsa_fwd(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
-                                _p(vf), _p(s), _p(z), B, H, T, dk, dv, m, float(tau),
-                                int(nthreads))
+    rc = _load().oracle_gsa_fwd_nl(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
+                                   _p(vf), _p(s), _p(z), B, H, T, dk, dv, m, float(tau),
+                                   _nl(nonlinearity), int(nthreads))
     if rc:
         raise RuntimeError("oracle_gsa_fwd failed (%d)" % rc)
     return dict(o=o, kf=kf, vf=vf, s=s, z=z)
@@ -116,7 +133,7 @@ def gla_fwd(q, k, v, g, s0=None, tau=16.0, want_state=True, nthreads=1):
     return dict(o=o, sf=sf)
 
 
-def gsa_decode_step(q, k, v, g, kstate, vstate, tau=8.0, nthreads=1):
+def gsa_decode_step(q, k, v, g, kstate, vstate, tau=8.0, nthreads=1, nonlinearity="softmax"):
     """One recurrent GSA step.  q,k [N,H,dk]; v [N,H,dv]; g [N,H,m];
     kstate [N,H,m,dk], vstate [N,H,m,dv].  Returns (o, new_kstate, new_vstate);
     the inputs are not modified."""
@@ -128,8 +145,9 @@ def gsa_decode_step(q, k, v, g, kstate, vstate, tau=8.0, nthreads=1):
     m = g.shape[-1]
     assert ks.shape == (N, H, m, dk) and vs.shape == (N, H, m, dv)
     o = np.empty((N, H, dv))
-    rc = _load().oracle_gsa_decode_step(_p(q), _p(k), _p(v), _p(g), _p(ks), _p(vs), _p(o),
-                                        N, H, dk, dv, m, float(tau), int(nthreads))
+    rc = _load().oracle_gsa_decode_step_nl(_p(q), _p(k), _p(v), _p(g), _p(ks), _p(vs), _p(o),
+                                           N, H, dk, dv, m, float(tau), _nl(nonlinearity),
+                                           int(nthreads))
     if rc:
         raise RuntimeError("oracle_gsa_decode_step failed (%d)" % rc)
     return o, ks, vs

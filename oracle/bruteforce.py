@@ -21,7 +21,24 @@ def _alpha(g, tau):
     return (1.0 / (1.0 + np.exp(-g))) ** (1.0 / tau)
 
 
-def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0):
+def _read(z, nonlinearity):
+    """Slot read weights from the slot scores: softmax (Sec. 3.2) or one of the
+    element-wise ablations of Table 2, each written from its definition."""
+    if nonlinearity == "softmax":
+        e = np.exp(z - z.max())
+        return e / e.sum()
+    if nonlinearity == "identity":
+        return z
+    if nonlinearity == "swish":
+        return z / (1.0 + np.exp(-z))
+    if nonlinearity == "relu":
+        return np.maximum(z, 0.0)
+    if nonlinearity == "relu2":
+        return np.maximum(z, 0.0) ** 2
+    raise ValueError(nonlinearity)
+
+
+def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0, nonlinearity="softmax"):
     T, dk = q.shape
     m = g.shape[1]
     dv = v.shape[1]
@@ -37,9 +54,7 @@ def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0):
             Kt = Kt + f[:, None] * k[j][None, :]
             Vt = Vt + f[:, None] * v[j][None, :]
         z = Kt @ q[t]
-        e = np.exp(z - z.max())
-        s = e / e.sum()
-        o[t] = Vt.T @ s
+        o[t] = Vt.T @ _read(z, nonlinearity)
     return o
 
 

@@ -86,19 +86,36 @@ def softmax_slots(x):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0, C=64):
+def slot_read(x, nonlinearity="softmax"):
+    """The link between the two passes: the softmax over the slots (Sec. 3.2),
+    or an element-wise replacement from the ablation study (Table 2)."""
+    x = np.asarray(x, dtype=np.float64)
+    if nonlinearity == "softmax":
+        return softmax_slots(x)
+    if nonlinearity == "identity":
+        return x.copy()
+    if nonlinearity == "swish":
+        return x * (0.5 * (1.0 + np.tanh(0.5 * x)))   # sigmoid via tanh
+    if nonlinearity == "relu":
+        return np.where(x > 0.0, x, 0.0)
+    if nonlinearity == "relu2":
+        return np.where(x > 0.0, x * x, 0.0)
+    raise ValueError(nonlinearity)
+
+
+def gsa_unit(q, k, v, g, k0=None, v0=None, tau=8.0, C=64, nonlinearity="softmax"):
     """One (b,h) unit of GSA as two chunked GLA passes.  Returns
     (o, Kt_final [m,dk], Vt_final [m,dv], s [T,m])."""
     la = log_sigmoid(g) / tau
     w = -np.expm1(la)
     P0 = None if k0 is None else np.asarray(k0, dtype=np.float64).T
     ok, P = gla_value_decay(q, k, w, la, P0, C)
-    s = softmax_slots(ok)
+    s = slot_read(ok, nonlinearity)
     o, Vf = gla_key_decay(s, w, v, la, v0, C)
     return o, P.T, Vf, s
 
 
-def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, C=64):
+def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, C=64, nonlinearity="softmax"):
     B, H, T, dk = q.shape
     m = g.shape[-1]
     o = np.zeros(v.shape)
@@ -108,7 +125,8 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, C=64):
         for h in range(H):
             o[b, h], kf[b, h], vf[b, h], _ = gsa_unit(
                 q[b, h], k[b, h], v[b, h], g[b, h],
-                None if k0 is None else k0[b, h], None if v0 is None else v0[b, h], tau, C)
+                None if k0 is None else k0[b, h], None if v0 is None else v0[b, h], tau, C,
+                nonlinearity)
     return o, kf, vf
 
 

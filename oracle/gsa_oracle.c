@@ -22,6 +22,10 @@
  *     updated with token t before it is read (inclusive read).
  *   - No normaliser term and no temperature (Sec. 2.2 footnote 1; App. A
  *     footnote 8).
+ *   - Non-linearity ablations (Sec. 4.1.3, Table 2): the softmax may be
+ *     replaced by an element-wise function of each slot score z, s_t[c] =
+ *     f(z[c]): 1 = none (f(z) = z), 2 = Swish (z * sigmoid(z)), 3 = ReLU
+ *     (max(z, 0)), 4 = ReLU^2 (max(z, 0)^2); 0 is the softmax.
  *   - GLA (Sec. 2.3, with beta = 1): S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T,
  *     o_t = S_t^T q_t, alpha_t per key dimension.
  *
@@ -48,11 +52,26 @@ static double log_sigmoid(double x)
     return (x < 0.0 ? x : 0.0) - log1p(exp(-fabs(x)));
 }
 
+/* Element-wise slot read functions of the ablation study (Table 2). */
+static double slot_fn(double x, int act)
+{
+    switch (act) {
+    case 1:
+        return x;
+    case 2:
+        return x / (1.0 + exp(-x));
+    case 3:
+        return x > 0.0 ? x : 0.0;
+    default:
+        return x > 0.0 ? x * x : 0.0;
+    }
+}
+
 /* One GSA token step on one unit's slot states (Sec. 3.2). */
 static void gsa_token(const double *qt, const double *kt, const double *vt,
                       const double *gt, double *K, double *V, double *ot,
                       double *st, double *zt, double *z, double *s,
-                      long dk, long dv, long m, double tau)
+                      long dk, long dv, long m, double tau, int act)
 {
     long c, x;
     double zmax = -INFINITY, sum = 0.0;
@@ -72,12 +91,17 @@ static void gsa_token(const double *qt, const double *kt, const double *vt,
         if (acc > zmax)
             zmax = acc;
     }
-    for (c = 0; c < m; c++) {
-        s[c] = exp(z[c] - zmax);
-        sum += s[c];
+    if (act == 0) {
+        for (c = 0; c < m; c++) {
+            s[c] = exp(z[c] - zmax);
+            sum += s[c];
+        }
+        for (c = 0; c < m; c++)
+            s[c] /= sum;
+    } else {
+        for (c = 0; c < m; c++)
+            s[c] = slot_fn(z[c], act);
     }
-    for (c = 0; c < m; c++)
-        s[c] /= sum;
     for (x = 0; x < dv; x++) {
         double acc = 0.0;
         for (c = 0; c < m; c++)
@@ -92,18 +116,19 @@ static void gsa_token(const double *qt, const double *kt, const double *vt,
 
 /*
  * GSA forward over whole sequences.  k0/v0 nullable (zero initial state);
- * kf/vf nullable; s_out/z_out nullable [B,H,T,m] (slot softmax / raw scores).
+ * kf/vf nullable; s_out/z_out nullable [B,H,T,m] (slot read weights / raw
+ * scores).  act: 0 softmax, 1..4 the element-wise ablations above.
  */
-int oracle_gsa_fwd(const double *q, const double *k, const double *v,
-                   const double *g, const double *k0, const double *v0,
-                   double *o, double *kf, double *vf, double *s_out,
-                   double *z_out, long B, long H, long T, long dk, long dv,
-                   long m, double tau, int nthreads)
+int oracle_gsa_fwd_nl(const double *q, const double *k, const double *v,
+                      const double *g, const double *k0, const double *v0,
+                      double *o, double *kf, double *vf, double *s_out,
+                      double *z_out, long B, long H, long T, long dk, long dv,
+                      long m, double tau, int act, int nthreads)
 {
     long units = B * H, u;
     int err = 0;
     if (!q || !k || !v || !g || !o || B < 0 || H < 0 || T < 0 || dk < 1 ||
-        dv < 1 || m < 1 || !(tau > 0.0))
+        dv < 1 || m < 1 || !(tau > 0.0) || act < 0 || act > 4)
         return 1;
 #ifdef _OPENMP
     if (nthreads < 1)
@@ -127,7 +152,7 @@ int oracle_gsa_fwd(const double *q, const double *k, const double *v,
                 long row = u * T + t;
                 gsa_token(q + row * dk, k + row * dk, v + row * dv, g + row * m,
                           K, V, o + row * dv, s_out ? s_out + row * m : NULL,
-                          z_out ? z_out + row * m : NULL, z, s, dk, dv, m, tau);
+                          z_out ? z_out + row * m : NULL, z, s, dk, dv, m, tau, act);
             }
             if (kf)
                 memcpy(kf + u * m * dk, K, (size_t)(m * dk) * sizeof(double));
@@ -140,6 +165,17 @@ int oracle_gsa_fwd(const double *q, const double *k, const double *v,
         free(s);
     }
     return err;
+}
+
+/* The method as published: the softmax read. */
+int oracle_gsa_fwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *k0, const double *v0,
+                   double *o, double *kf, double *vf, double *s_out,
+                   double *z_out, long B, long H, long T, long dk, long dv,
+                   long m, double tau, int nthreads)
+{
+    return oracle_gsa_fwd_nl(q, k, v, g, k0, v0, o, kf, vf, s_out, z_out, B, H,
+                             T, dk, dv, m, tau, 0, nthreads);
 }
 
 /* GLA forward (Sec. 2.3, beta = 1): per key dimension decay, S in R^{dk x dv}. */
@@ -196,15 +232,15 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
  * One recurrent GSA step for N independent sequences x H heads; the slot states
  * [N,H,m,dk] / [N,H,m,dv] are advanced in place and o [N,H,dv] is written.
  */
-int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
-                           const double *g, double *kstate, double *vstate,
-                           double *o, long N, long H, long dk, long dv, long m,
-                           double tau, int nthreads)
+int oracle_gsa_decode_step_nl(const double *q, const double *k, const double *v,
+                              const double *g, double *kstate, double *vstate,
+                              double *o, long N, long H, long dk, long dv, long m,
+                              double tau, int act, int nthreads)
 {
     long units = N * H, u;
     int err = 0;
     if (!q || !k || !v || !g || !kstate || !vstate || !o || N < 0 || H < 0 ||
-        dk < 1 || dv < 1 || m < 1 || !(tau > 0.0))
+        dk < 1 || dv < 1 || m < 1 || !(tau > 0.0) || act < 0 || act > 4)
         return 1;
 #ifdef _OPENMP
     if (nthreads < 1)
@@ -219,12 +255,21 @@ int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
         } else {
             gsa_token(q + u * dk, k + u * dk, v + u * dv, g + u * m,
                       kstate + u * m * dk, vstate + u * m * dv, o + u * dv,
-                      NULL, NULL, z, s, dk, dv, m, tau);
+                      NULL, NULL, z, s, dk, dv, m, tau, act);
         }
         free(z);
         free(s);
     }
     return err;
+}
+
+int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
+                           const double *g, double *kstate, double *vstate,
+                           double *o, long N, long H, long dk, long dv, long m,
+                           double tau, int nthreads)
+{
+    return oracle_gsa_decode_step_nl(q, k, v, g, kstate, vstate, o, N, H, dk,
+                                     dv, m, tau, 0, nthreads);
 }
 
 int oracle_max_threads(void)

@@ -33,6 +33,12 @@ MUTATIONS = [
      "double a = exp(log_sigmoid(gt[0]) / tau);"),
     ("gla_read_before_write", "Sx[y] = a * Sx[y] + kt[x] * vt[y];",
      "Sx[y] = a * Sx[y] + kt[x] * vt[y] * (t > 0);"),
+    # slot read non-linearities of the ablation study (Table 2)
+    ("swish_sigmoid_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    ("relu_leaky", "return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : 0.01 * x;"),
+    ("relu2_not_squared", "return x > 0.0 ? x * x : 0.0;", "return x > 0.0 ? x : 0.0;"),
+    ("read_codes_shifted", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c], act + 1);"),
+    ("read_of_scaled_scores", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c] * 0.5, act);"),
 ]
 
 
@@ -46,6 +52,7 @@ def _build(tmp_path, text, name):
     P, L, D, I = ctypes.c_void_p, ctypes.c_long, ctypes.c_double, ctypes.c_int
     lib.oracle_gsa_fwd.argtypes = [P] * 11 + [L] * 6 + [D, I]
     lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
+    lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
     return lib
 
 
@@ -53,14 +60,18 @@ def _p(x):
     return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
 
 
-def _gsa(lib, q, k, v, g, k0=None, v0=None, tau=8.0):
+def _gsa(lib, q, k, v, g, k0=None, v0=None, tau=8.0, act=None):
     B, H, T, dk = q.shape
     dv, m = v.shape[-1], g.shape[-1]
     o = np.empty((B, H, T, dv))
     kf = np.empty((B, H, m, dk))
     vf = np.empty((B, H, m, dv))
-    rc = lib.oracle_gsa_fwd(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
-                            _p(vf), None, None, B, H, T, dk, dv, m, tau, 1)
+    if act is None:
+        rc = lib.oracle_gsa_fwd(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
+                                _p(vf), None, None, B, H, T, dk, dv, m, tau, 1)
+    else:
+        rc = lib.oracle_gsa_fwd_nl(_p(q), _p(k), _p(v), _p(g), _p(k0), _p(v0), _p(o), _p(kf),
+                                   _p(vf), None, None, B, H, T, dk, dv, m, tau, act, 1)
     assert rc == 0
     return o, kf, vf
 
@@ -110,6 +121,11 @@ def _pins_pass(lib):
     ok &= _rel(og, ogc) < 1e-12 and _rel(sfg, sfgc) < 1e-12
     ola, _ = _gla(lib, q, k, v, np.full_like(gg, np.inf))
     ok &= _rel(ola[0, 0], np.tril(q[0, 0] @ k[0, 0].T) @ v[0, 0]) < 1e-12
+    # the element-wise slot reads against the numpy chunk form
+    for act, name in ((1, "identity"), (2, "swish"), (3, "relu"), (4, "relu2")):
+        on, _, _ = _gsa(lib, q, k, v, g, k0, v0, act=act)
+        oc, _, _ = chunkwise.gsa_fwd(q, k, v, g, k0, v0, tau=8.0, C=8, nonlinearity=name)
+        ok &= _rel(on, oc) < 1e-12
     return bool(ok)
 
 
