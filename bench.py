@@ -156,7 +156,7 @@ def roofline(bytes_alg, t_ms, kernel, workload):
             "kernel": kernel}
 
 
-def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True):
+def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True, nonlinearity="softmax"):
     import synth
     inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
                            seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
@@ -174,7 +174,8 @@ def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True):
         i = next(j for j, x in enumerate(sets) if x is s)
         gsa.gsa_fwd(s["q"], s["k"], s["v"], s["g"], s.get("k0"), s.get("v0"), tau=w["tau"],
                     final_state=init, out=outs[i], k_final=kfs[i] if init else None,
-                    v_final=vfs[i] if init else None, workspace=ws, events=events)
+                    v_final=vfs[i] if init else None, workspace=ws, events=events,
+                    nonlinearity=nonlinearity)
 
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     flops, nbytes = gsa_alg(B, H, T, dk, dv, m, w["C"], 2, init_state=init, final_state=init)
@@ -300,6 +301,25 @@ def copy_calibration(torch, ev, steps):
             "GBps": round(2 * n / (t * 1e-3) / 1e9, 1)}
 
 
+def bench_ablations(torch, gsa, ev, steps, warmup, nsets):
+    """The training-shape GSA forward with each element-wise slot read of the
+    ablation study in place of the softmax (same launch sequence; only the
+    read inside the output kernel differs)."""
+    import synth
+    w = synth.WORKLOADS["gsa_bf16_train_T2048"]
+    out = {}
+    for nl in ("identity", "swish", "relu", "relu2"):
+        r = bench_gsa(torch, gsa, ev, w, "gsa_bf16_train_T2048", steps, warmup, nsets,
+                      warm_too=False, nonlinearity=nl)
+        rf = dict(r["roofline"])
+        rf["traffic"] = None  # counters are taken on the softmax kernel only
+        out[nl] = {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+                   "ms_per_step": round(r["ms_per_step"], 4), "ms_phases": r["ms_phases"],
+                   "roofline": rf}
+        del r
+    return out
+
+
 def run_only(args, torch, gsa, ev):
     import synth
     if args.only == "copy":
@@ -312,6 +332,8 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "ablations":
+        return bench_ablations(torch, gsa, ev, args.steps, args.warmup, args.sets)
     if args.only == "gla":
         return bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"], args.steps, args.warmup)
     return bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"], args.steps, args.warmup)
@@ -326,7 +348,7 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy", "ablations"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -371,6 +393,9 @@ def main():
         comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
                                                 args.steps, args.warmup)
         log("bench: decode done")
+        comps["gsa_bf16_train_T2048_read_ablations"] = bench_ablations(
+            torch, gsa, ev, max(1, args.steps // 2), args.warmup, args.sets)
+        log("bench: read ablations done")
         torch.cuda.empty_cache()
 
     cpu, err = None, None

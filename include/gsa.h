@@ -39,12 +39,12 @@
 extern "C" {
 #endif
 
-#define GSA_ABI_VERSION 1
+#define GSA_ABI_VERSION 2
 
 typedef enum {
   GSA_OK = 0,
   GSA_ERR_NULL = 1,        /* a required pointer is NULL */
-  GSA_ERR_SHAPE = 2,       /* negative or zero size, bad tau */
+  GSA_ERR_SHAPE = 2,       /* negative or zero size, bad tau, dtype or non-linearity code */
   GSA_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
   GSA_ERR_UNSUPPORTED = 4, /* (dtype, dk, dv, m, C) not compiled */
   GSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
@@ -53,6 +53,24 @@ typedef enum {
 } gsa_status;
 
 typedef enum { GSA_DTYPE_F32 = 0, GSA_DTYPE_BF16 = 1 } gsa_dtype;
+
+/* What turns the pass-1 slot scores o'_t = Kt_t q_t into the pass-2 read
+ * weights s_t.  GSA_SLOT_SOFTMAX is the method (Sec. 3.2): a softmax over the
+ * m slots.  The others are the non-linearity ablations of the paper's Table 2,
+ * applied element-wise to each slot score x in place of the softmax:
+ *   GSA_SLOT_IDENTITY  s = x                (no non-linearity, "-softmax")
+ *   GSA_SLOT_SWISH     s = x * sigmoid(x)
+ *   GSA_SLOT_RELU      s = max(x, 0)
+ *   GSA_SLOT_RELU2     s = max(x, 0)^2
+ * Everything else (gates, both state recurrences, o_t = Vt_t^T s_t) is
+ * unchanged. */
+typedef enum {
+  GSA_SLOT_SOFTMAX = 0,
+  GSA_SLOT_IDENTITY = 1,
+  GSA_SLOT_SWISH = 2,
+  GSA_SLOT_RELU = 3,
+  GSA_SLOT_RELU2 = 4
+} gsa_slot_nonlinearity;
 
 /* ABI version (GSA_ABI_VERSION of the built library). */
 int gsa_abi_version(void);
@@ -129,6 +147,19 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
                    void* stream, void* const* events);
 
 /*
+ * gsa_fwd with the slot read non-linearity chosen by the caller (a
+ * gsa_slot_nonlinearity code; any other value returns GSA_ERR_SHAPE) and the
+ * timing hooks of gsa_fwd_events.  gsa_fwd and gsa_fwd_events are this with
+ * GSA_SLOT_SOFTMAX.  Shapes, layouts, workspace, aliasing and errors are those
+ * of gsa_fwd; the same (dk, dv, m, dtype) combinations are compiled for every
+ * non-linearity.
+ */
+int gsa_fwd_ex(const void* q, const void* k, const void* v, const void* g, const float* k0,
+               const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T, int dk,
+               int dv, int m, int C, float tau, int dtype, void* workspace, size_t workspace_bytes,
+               int chunks_per_segment, int nonlinearity, void* stream, void* const* events);
+
+/*
  * One recurrent GSA step (Sec. 3.2 recurrent form) for N sequences x H heads.
  *   q, k     [N,H,dk]    dtype
  *   v        [N,H,dv]    dtype
@@ -147,6 +178,12 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, 
 int gsa_decode_step_events(const void* q, const void* k, const void* v, const void* g,
                            float* k_state, float* v_state, void* o, int N, int H, int dk, int dv,
                            int m, float tau, int dtype, void* stream, void* const* events);
+/* gsa_decode_step with the slot read non-linearity chosen by the caller (a
+ * gsa_slot_nonlinearity code, else GSA_ERR_SHAPE) and the timing hook of
+ * gsa_decode_step_events; everything else as for gsa_decode_step. */
+int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* g, float* k_state,
+                       float* v_state, void* o, int N, int H, int dk, int dv, int m, float tau,
+                       int dtype, int nonlinearity, void* stream, void* const* events);
 
 #ifdef __cplusplus
 }

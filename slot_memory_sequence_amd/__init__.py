@@ -16,12 +16,15 @@ import os
 # and allocations are valid handles for the library.
 import torch as _torch_rt  # noqa: F401
 
-__all__ = ["lib", "gsa_fwd", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH",
+__all__ = ["lib", "gsa_fwd", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH", "NONLINEARITIES",
            "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
            "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
+# gsa_slot_nonlinearity codes: the softmax read of GSA and the element-wise
+# ablations (none, Swish, ReLU, ReLU^2)
+NONLINEARITIES = {"softmax": 0, "identity": 1, "swish": 2, "relu": 3, "relu2": 4}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgsa.so is not built (run __graft_entry__.build() or "
@@ -51,6 +54,10 @@ lib.gsa_decode_step.restype = _I
 lib.gsa_decode_step.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P]
 lib.gsa_decode_step_events.restype = _I
 lib.gsa_decode_step_events.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P, _P]
+lib.gsa_fwd_ex.restype = _I
+lib.gsa_fwd_ex.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _I, _P, _P]
+lib.gsa_decode_step_ex.restype = _I
+lib.gsa_decode_step_ex.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _I, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -124,6 +131,15 @@ def _events(events, n=4):
     return ctypes.cast(arr, ctypes.c_void_p)
 
 
+def _nl(nonlinearity):
+    if isinstance(nonlinearity, str):
+        if nonlinearity not in NONLINEARITIES:
+            raise ValueError("unknown slot non-linearity %r (one of %s)"
+                             % (nonlinearity, ", ".join(NONLINEARITIES)))
+        return NONLINEARITIES[nonlinearity]
+    return int(nonlinearity)  # a raw code; the library validates it
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -133,9 +149,11 @@ def _stream(stream):
 
 def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
             chunks_per_segment=0, out=None, k_final=None, v_final=None, workspace=None,
-            stream=None, events=None):
+            stream=None, events=None, nonlinearity="softmax"):
     """Chunkwise GSA forward.  q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m] (gate
     logits); optional float32 initial slot states k0 [B,H,m,dk], v0 [B,H,m,dv].
+    nonlinearity: the slot read, "softmax" (GSA) or one of the element-wise
+    ablations "identity", "swish", "relu", "relu2".
     Returns (o, k_final, v_final) -- the finals are None unless final_state."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
@@ -157,10 +175,11 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
         raise ValueError("invalid problem size")
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.gsa_fwd_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
-                            _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
-                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                            int(chunks_per_segment), _stream(stream), _events(events))
+    st = lib.gsa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
+                        _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
+                        _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                        int(chunks_per_segment), _nl(nonlinearity), _stream(stream),
+                        _events(events))
     if st:
         raise GsaError("gsa_fwd", st)
     return out, k_final, v_final
@@ -195,10 +214,11 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
 
 
 def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=None,
-                    events=None):
+                    events=None, nonlinearity="softmax"):
     """One recurrent GSA step.  q, k [N,H,dk]; v [N,H,dv]; g [N,H,m]; float32
     k_state [N,H,m,dk] and v_state [N,H,m,dv] are advanced in place.  Returns o.
-    events: None or two hipEvent_t handles that take the kernel's start and end."""
+    events: None or two hipEvent_t handles that take the kernel's start and end.
+    nonlinearity: as for gsa_fwd."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _check(t, n, q.dtype)
@@ -208,9 +228,9 @@ def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=N
     dv, m = v.shape[-1], g.shape[-1]
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
-    st = lib.gsa_decode_step_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state),
-                                    _ptr(v_state), _ptr(out), N, H, dk, dv, m, float(tau), _dt(q),
-                                    _stream(stream), _events(events, 2))
+    st = lib.gsa_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state),
+                                _ptr(v_state), _ptr(out), N, H, dk, dv, m, float(tau), _dt(q),
+                                _nl(nonlinearity), _stream(stream), _events(events, 2))
     if st:
         raise GsaError("gsa_decode_step", st)
     return out

@@ -30,6 +30,8 @@ size_t esize(int dtype) { return dtype == GSA_DTYPE_BF16 ? 2 : 4; }
 
 bool dtype_ok(int dtype) { return dtype == GSA_DTYPE_F32 || dtype == GSA_DTYPE_BF16; }
 
+bool nonlinearity_ok(int nl) { return nl >= GSA_SLOT_SOFTMAX && nl <= GSA_SLOT_RELU2; }
+
 int default_chunks_per_seg(long long units, int nchunks) {
   if (nchunks <= 1 || units <= 0) return nchunks > 0 ? nchunks : 1;
   long long p = kTargetWorkgroups / units;
@@ -87,7 +89,7 @@ const char* gsa_status_string(int s) {
   switch (s) {
     case GSA_OK: return "ok";
     case GSA_ERR_NULL: return "a required pointer is NULL";
-    case GSA_ERR_SHAPE: return "invalid size or tau";
+    case GSA_ERR_SHAPE: return "invalid size, tau, dtype or non-linearity code";
     case GSA_ERR_ALIGN: return "pointer not 16-byte aligned";
     case GSA_ERR_UNSUPPORTED: return "shape/dtype combination not compiled";
     case GSA_ERR_WORKSPACE: return "workspace missing or too small";
@@ -131,16 +133,24 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
             const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk, int dv, int m,
             int C, float tau, int dtype, void* workspace, size_t workspace_bytes, int cps,
             void* stream) {
-  return gsa_fwd_events(q, k, v, g, k0, v0, o, kf, vf, B, H, T, dk, dv, m, C, tau, dtype,
-                        workspace, workspace_bytes, cps, stream, nullptr);
+  return gsa_fwd_ex(q, k, v, g, k0, v0, o, kf, vf, B, H, T, dk, dv, m, C, tau, dtype, workspace,
+                    workspace_bytes, cps, GSA_SLOT_SOFTMAX, stream, nullptr);
 }
 
 int gsa_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* k0,
                    const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk,
                    int dv, int m, int C, float tau, int dtype, void* workspace,
                    size_t workspace_bytes, int cps, void* stream, void* const* events) {
+  return gsa_fwd_ex(q, k, v, g, k0, v0, o, kf, vf, B, H, T, dk, dv, m, C, tau, dtype, workspace,
+                    workspace_bytes, cps, GSA_SLOT_SOFTMAX, stream, events);
+}
+
+int gsa_fwd_ex(const void* q, const void* k, const void* v, const void* g, const float* k0,
+               const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk, int dv,
+               int m, int C, float tau, int dtype, void* workspace, size_t workspace_bytes, int cps,
+               int nonlinearity, void* stream, void* const* events) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !(tau > 0.f) ||
-      !std::isfinite(tau) || !dtype_ok(dtype))
+      !std::isfinite(tau) || !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
     return GSA_ERR_SHAPE;
   if (!gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
@@ -184,8 +194,8 @@ int gsa_fwd_events(const void* q, const void* k, const void* v, const void* g, c
   a.ws_dec = workspace ? (float*)((char*)workspace +
                                   (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
                        : nullptr;
-  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.stream = stream;
-  a.events = events;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
+  a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();
@@ -253,14 +263,22 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
 int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* ks,
                     float* vs, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
                     void* stream) {
-  return gsa_decode_step_events(q, k, v, g, ks, vs, o, N, H, dk, dv, m, tau, dtype, stream, nullptr);
+  return gsa_decode_step_ex(q, k, v, g, ks, vs, o, N, H, dk, dv, m, tau, dtype, GSA_SLOT_SOFTMAX,
+                            stream, nullptr);
 }
 
 int gsa_decode_step_events(const void* q, const void* k, const void* v, const void* g, float* ks,
                            float* vs, void* o, int N, int H, int dk, int dv, int m, float tau,
                            int dtype, void* stream, void* const* events) {
+  return gsa_decode_step_ex(q, k, v, g, ks, vs, o, N, H, dk, dv, m, tau, dtype, GSA_SLOT_SOFTMAX,
+                            stream, events);
+}
+
+int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* g, float* ks,
+                       float* vs, void* o, int N, int H, int dk, int dv, int m, float tau, int dtype,
+                       int nonlinearity, void* stream, void* const* events) {
   if (N < 0 || H < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
-      !dtype_ok(dtype))
+      !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
     return GSA_ERR_SHAPE;
   if (!gsa_decode_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)N * H;
@@ -282,7 +300,7 @@ int gsa_decode_step_events(const void* q, const void* k, const void* v, const vo
     if (overlap(ro, in)) return GSA_ERR_ALIAS;
   gsa::DecodeLaunch a{};
   a.q = q; a.k = k; a.v = v; a.g = g; a.ks = ks; a.vs = vs; a.o = o; a.N = N; a.H = H;
-  a.tau = tau; a.stream = stream; a.events = events;
+  a.tau = tau; a.act = nonlinearity; a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::decode_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();

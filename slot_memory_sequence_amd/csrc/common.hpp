@@ -135,4 +135,26 @@ __device__ __forceinline__ float sum32(float x) {
 // whole-chunk decay product must stay >= e^-40 so that 1/prod stays <= e^40.
 constexpr float kFastMinDecay = 4.248354255291589e-18f;  // e^-40
 
+// ------------------------------------------------- slot read non-linearity
+// What turns the pass-1 slot scores o'_t into the pass-2 read weights s_t: the
+// softmax over the m slots (Sec. 3.2), or one of the element-wise functions
+// the ablation study puts in its place (Table 2: no non-linearity, Swish, ReLU,
+// ReLU^2).  The values match the GSA_SLOT_* codes of the C ABI.
+enum SlotAct : int { kActSoftmax = 0, kActIdentity = 1, kActSwish = 2, kActRelu = 3, kActRelu2 = 4 };
+
+// The element-wise replacements (not used for kActSoftmax, which needs the
+// whole slot row).  Swish(x) = x * sigmoid(x), formed as x / (1 + e^-x): for
+// x -> -inf the quotient goes to -0, never inf * 0.
+template <int ACT>
+__device__ __forceinline__ float slot_act(float x) {
+  static_assert(ACT >= kActIdentity && ACT <= kActRelu2, "element-wise slot non-linearity");
+  if constexpr (ACT == kActIdentity) return x;
+  else if constexpr (ACT == kActSwish) return x / (1.f + __expf(-x));
+  else if constexpr (ACT == kActRelu) return fmaxf(x, 0.f);
+  else {
+    const float r = fmaxf(x, 0.f);
+    return r * r;
+  }
+}
+
 }  // namespace gsa

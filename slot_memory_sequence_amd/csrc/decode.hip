@@ -5,6 +5,8 @@
 // gate sigmoid(g)^(1/tau)).  For every (sequence, head), in place:
 //   Kt <- Diag(a) Kt + (1-a) k^T ;  s = softmax(Kt q) ;
 //   Vt <- Diag(a) Vt + (1-a) v^T ;  o = Vt^T s.
+// The softmax may be replaced by one of the element-wise functions of the
+// paper's ablation study (Table 2), selected by the ACT template parameter.
 // The step is bound by HBM traffic: the two fp32 slot states are read and
 // written once (2 * 2 * m * d * 4 bytes per unit) while the token I/O is tiny,
 // the reason the paper ties inference speed to state size (Sec. 4.1.4).
@@ -76,7 +78,7 @@ constexpr int decode_threads() {
   return (M * DK / 4) / GSA_DECODE_KPER > 1024 ? 1024 : (M * DK / 4) / GSA_DECODE_KPER;
 }
 
-template <typename T, int DK, int DV, int M, int NTH>
+template <typename T, int DK, int DV, int M, int NTH, int ACT>
 __global__ void __launch_bounds__(NTH)
 gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   const T* __restrict__ g, float* __restrict__ ks, float* __restrict__ vs,
@@ -126,7 +128,9 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     if (tid % LK == 0) sZ[c] = z;
   }
   __syncthreads();
-  if (tid < 64) {  // slot softmax in wave 0
+  if constexpr (ACT != kActSoftmax) {  // element-wise read non-linearity (Table 2 ablations)
+    for (int c = tid; c < M; c += NTH) sS[c] = slot_act<ACT>(sZ[c]);
+  } else if (tid < 64) {  // slot softmax in wave 0
     float z = -INFINITY;
     for (int c = tid; c < M; c += 64) z = fmaxf(z, sZ[c]);
     float mx = z;
@@ -168,20 +172,32 @@ gsa_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   }
 }
 
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, int ACT>
 static int launch_decode(const DecodeLaunch& a) {
   constexpr int NTH = decode_threads<DK, M>();
   const unsigned units = (unsigned)a.N * (unsigned)a.H;
-  launch_timed(gsa_decode_kernel<T, DK, DV, M, NTH>, dim3(units), dim3(NTH), 0, a.stream, a.events, 0,
+  launch_timed(gsa_decode_kernel<T, DK, DV, M, NTH, ACT>, dim3(units), dim3(NTH), 0, a.stream, a.events, 0,
                1, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ks, a.vs, (T*)a.o,
                1.0f / a.tau);
   return 0;
 }
 
+template <typename T, int DK, int DV, int M>
+static int launch_decode_act(const DecodeLaunch& a) {
+  switch (a.act) {
+    case kActSoftmax: return launch_decode<T, DK, DV, M, kActSoftmax>(a);
+    case kActIdentity: return launch_decode<T, DK, DV, M, kActIdentity>(a);
+    case kActSwish: return launch_decode<T, DK, DV, M, kActSwish>(a);
+    case kActRelu: return launch_decode<T, DK, DV, M, kActRelu>(a);
+    case kActRelu2: return launch_decode<T, DK, DV, M, kActRelu2>(a);
+    default: return -1;
+  }
+}
+
 #define DEC_CASE(TT, DTC, DKC, DVC, MC)                                   \
   if (dt == DTC && dk == DKC && dv == DVC && m == MC) {                 \
     if (query) return 1;                                                 \
-    return launch_decode<TT, DKC, DVC, MC>(*a);                          \
+    return launch_decode_act<TT, DKC, DVC, MC>(*a);                      \
   }
 
 int decode_dispatch(int dt, int dk, int dv, int m, const DecodeLaunch* a, bool query) {

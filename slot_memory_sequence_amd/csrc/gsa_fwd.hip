@@ -317,7 +317,7 @@ gsa_seg_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
 }
 
 // ---------------------------------------------------- phase C: outputs
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, int ACT>
 __global__ void __launch_bounds__(kNT, 1)
 gsa_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
             const T* __restrict__ gg, const float* __restrict__ k0, const float* __restrict__ v0,
@@ -510,17 +510,20 @@ gsa_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
           for (int i = 0; i < 4; i++) {
             const int row = 16 * J + 4 * (lane >> 4) + i, col = 16 * ct + (lane & 15);
             a1[s][i] *= sE[row * L::LDE + col];
-            const float mx = max16(a1[s][i]);
-            if ((lane & 15) == 0) sRed[row * MT + ct] = mx;
+            if constexpr (ACT == kActSoftmax) {
+              const float mx = max16(a1[s][i]);
+              if ((lane & 15) == 0) sRed[row * MT + ct] = mx;
+            }
           }
         }
       }
       __syncthreads();
-      // ---- slot softmax: exp and row sums
+      // ---- slot softmax: exp and row sums (the element-wise ablation
+      // functions need neither)
 #pragma unroll
       for (int s = 0; s < T1W; s++) {
         const int t = wv + kNW * s;
-        if (t < NT1) {
+        if (ACT == kActSoftmax && t < NT1) {
           const int J = t / MT, ct = t % MT;
 #pragma unroll
           for (int i = 0; i < 4; i++) {
@@ -543,10 +546,15 @@ gsa_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
 #pragma unroll
           for (int i = 0; i < 4; i++) {
             const int row = 16 * J + 4 * (lane >> 4) + i, col = 16 * ct + (lane & 15);
-            float sm = 0.f;
+            float sv;
+            if constexpr (ACT == kActSoftmax) {
+              float sm = 0.f;
 #pragma unroll
-            for (int c2 = 0; c2 < MT; c2++) sm += sRed2[row * MT + c2];
-            const float sv = a1[s][i] / sm;
+              for (int c2 = 0; c2 < MT; c2++) sm += sRed2[row * MT + c2];
+              sv = a1[s][i] / sm;
+            } else {
+              sv = slot_act<ACT>(a1[s][i]);
+            }
             sSE[row * L::LDM + col] = Elem<T>::from_f(sv * sE[row * L::LDE + col]);
           }
         }
@@ -647,12 +655,16 @@ gsa_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
 #pragma unroll
             for (int nt = 0; nt < DK / 16; nt++) z += sZp[nt * M + lane];
           }
-          float mx = z;
+          if constexpr (ACT == kActSoftmax) {
+            float mx = z;
 #pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-          const float e = (lane < M) ? __expf(z - mx) : 0.f;
-          const float sm = sum64(e);
-          if (lane < M) sS[lane] = e / sm;
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const float e = (lane < M) ? __expf(z - mx) : 0.f;
+            const float sm = sum64(e);
+            if (lane < M) sS[lane] = e / sm;
+          } else {
+            if (lane < M) sS[lane] = slot_act<ACT>(z);
+          }
         }
         __syncthreads();
 #pragma unroll
@@ -705,7 +717,7 @@ gsa_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
 }
 
 // ------------------------------------------------------------ launcher
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, int ACT>
 static int launch_gsa(const GsaLaunch& a) {
   using LO = GsaLds<T, DK, DV, M>;
   using LS = GsaStateLds<T, DK, DV, M>;
@@ -726,17 +738,17 @@ static int launch_gsa(const GsaLaunch& a) {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gsa_seg_out<T, DK, DV, M>, dim3(P, units), dim3(kNT), LO::total, a.stream, a.events, 2,
+  launch_timed(gsa_seg_out<T, DK, DV, M, ACT>, dim3(P, units), dim3(kNT), LO::total, a.stream, a.events, 2,
                3, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.k0, a.v0,
                (const float*)a.ws_state, (T*)a.o, a.kf, a.vf, a.T, S, P, inv_tau);
   return 0;
 }
 
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, int ACT>
 static void set_lds_limits() {
-  hipFuncSetAttribute((const void*)gsa_seg_out<T, DK, DV, M>,
+  (void)hipFuncSetAttribute((const void*)gsa_seg_out<T, DK, DV, M, ACT>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, GsaLds<T, DK, DV, M>::total);
-  hipFuncSetAttribute((const void*)gsa_seg_state<T, DK, DV, M>,
+  (void)hipFuncSetAttribute((const void*)gsa_seg_state<T, DK, DV, M>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, GsaStateLds<T, DK, DV, M>::total);
 }
 
@@ -745,12 +757,28 @@ constexpr bool gsa_fits() {
   return GsaLds<T, DK, DV, M>::total <= kLdsBytes;
 }
 
+template <typename T, int DK, int DV, int M>
+static int launch_gsa_act(const GsaLaunch& a) {
+  switch (a.act) {
+#define GSA_ACT_CASE(A)               \
+  case A:                             \
+    set_lds_limits<T, DK, DV, M, A>(); \
+    return launch_gsa<T, DK, DV, M, A>(a);
+    GSA_ACT_CASE(kActSoftmax)
+    GSA_ACT_CASE(kActIdentity)
+    GSA_ACT_CASE(kActSwish)
+    GSA_ACT_CASE(kActRelu)
+    GSA_ACT_CASE(kActRelu2)
+#undef GSA_ACT_CASE
+    default: return -1;
+  }
+}
+
 #define GSA_CASE(TT, DTC, DKC, DVC, MC)                                                   \
   if (dt == DTC && dk == DKC && dv == DVC && m == MC) {                                 \
     if constexpr (gsa_fits<TT, DKC, DVC, MC>()) {                                        \
       if (query) return GsaLds<TT, DKC, DVC, MC>::total;                                 \
-      set_lds_limits<TT, DKC, DVC, MC>();                                                \
-      return launch_gsa<TT, DKC, DVC, MC>(*a);                                           \
+      return launch_gsa_act<TT, DKC, DVC, MC>(*a);                                       \
     }                                                                                    \
     return -1;                                                                           \
   }

@@ -311,11 +311,12 @@ __device__ __forceinline__ bool chunk_factors(const Row& g, bool valid, float in
 }
 
 // -------------------------------------------------------- pass-wave chunk
-// Token rows 16J..16J+15 of the chunk: pass 1, the slot softmax, pass 2 and the
+// Token rows 16J..16J+15 of the chunk: pass 1, the slot read non-linearity
+// (ACT: the softmax, or an element-wise ablation function), pass 2 and the
 // output rows.  Reads sQ, sK, sV, sX, sE and the bf16 state copy sW.  J is a
 // template parameter so that every loop is static and independent
 // accumulators can be interleaved.
-template <int DK, int DV, int M, int J>
+template <int DK, int DV, int M, int J, int ACT>
 __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf16_t* sK,
                                            const bf16_t* sV, const bf16_t* sW, const bf16_t* sX,
                                            const float* sE, bf16_t* __restrict__ orow, int rv) {
@@ -368,23 +369,32 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
     op[ct][3] *= e.w;
   }
 
-  // slot softmax of token j: over (ct, i) in-lane and the four lane groups
-  float mx = op[0][0];
+  float inv = 1.f;
+  if constexpr (ACT == kActSoftmax) {
+    // slot softmax of token j: over (ct, i) in-lane and the four lane groups
+    float mx = op[0][0];
 #pragma unroll
-  for (int ct = 0; ct < MT; ct++)
+    for (int ct = 0; ct < MT; ct++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) mx = fmaxf(mx, op[ct][i]);
-  mx = group4_max(mx);
-  float sm = 0.f;
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, op[ct][i]);
+    mx = group4_max(mx);
+    float sm = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < MT; ct++)
+    for (int ct = 0; ct < MT; ct++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      op[ct][i] = __builtin_amdgcn_exp2f((op[ct][i] - mx) * 1.4426950408889634f);
-      sm += op[ct][i];
-    }
-  sm = group4_sum(sm);
-  const float inv = 1.f / sm;
+      for (int i = 0; i < 4; i++) {
+        op[ct][i] = __builtin_amdgcn_exp2f((op[ct][i] - mx) * 1.4426950408889634f);
+        sm += op[ct][i];
+      }
+    sm = group4_sum(sm);
+    inv = 1.f / sm;
+  } else {
+    // element-wise replacement of the softmax (Table 2 ablations)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) op[ct][i] = slot_act<ACT>(op[ct][i]);
+  }
   // (s*E)^T as B operands over slot pairs (permuted slot index)
   bf16x8 sb[NP];
 #pragma unroll
@@ -447,11 +457,12 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
 
 // ------------------------------------------------ exact chunk recurrence
 // Runs one chunk token by token: Kt, Vt <- Diag(alpha) (.) + (1-alpha)[k|v]^T,
-// s = softmax over slots of Kt q, o = Vt^T s (Sec. 3.2 recurrent form).  Used
+// s = softmax over slots of Kt q (or the element-wise ACT), o = Vt^T s
+// (Sec. 3.2 recurrent form).  Used
 // for chunks whose decay product is too small for the factorised chunk form.
 // The state waves' accumulators W are written to LDS, advanced there by all
 // threads, and read back.  Contains workgroup barriers: all threads call it.
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int ACT>
 __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
                                             const bf16_t* sQ, const bf16_t* sK, const bf16_t* sV,
                                             bf16_t* __restrict__ orow, int tid) {
@@ -495,14 +506,19 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv,
 #pragma unroll
     for (int i = 0; i < VPT; i++) wvv[i] = a * wvv[i] + w * bf2f(sV[jt * Lds::LDV + p * VPT + i]);
     __syncthreads();
-    // slot softmax, computed by every wave; lane l < M holds slot l
-    const float zl = lane < M ? sZs[lane] : -INFINITY;
-    float mx = zl;
+    float sc;
+    if constexpr (ACT == kActSoftmax) {
+      // slot softmax, computed by every wave; lane l < M holds slot l
+      const float zl = lane < M ? sZs[lane] : -INFINITY;
+      float mx = zl;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    const float el = lane < M ? __expf(zl - mx) : 0.f;
-    const float sm = sum64(el);
-    const float sc = __shfl(el, c, 64) / sm;
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      const float el = lane < M ? __expf(zl - mx) : 0.f;
+      const float sm = sum64(el);
+      sc = __shfl(el, c, 64) / sm;
+    } else {
+      sc = slot_act<ACT>(sZs[c]);
+    }
     // o partials: reduce over the wave's slots (lanes with equal p), then over waves
     float op[VPT];
 #pragma unroll
@@ -658,7 +674,7 @@ gsa_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
 }
 
 // ------------------------------------------------------ phase C: outputs
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int ACT>
 __global__ void __launch_bounds__(NT, 1)
 gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const bf16_t* __restrict__ vv, const bf16_t* __restrict__ gg,
@@ -793,10 +809,10 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
         // pass waves hold no state: dropping it frees these registers for the passes
         W.zero();
         switch (wv) {
-          case 0: pass_chunk<DK, DV, M, 0>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          case 1: pass_chunk<DK, DV, M, 1>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          case 2: pass_chunk<DK, DV, M, 2>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          default: pass_chunk<DK, DV, M, 3>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 0: pass_chunk<DK, DV, M, 0, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 1: pass_chunk<DK, DV, M, 1, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 2: pass_chunk<DK, DV, M, 2, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          default: pass_chunk<DK, DV, M, 3, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
         }
       } else {
         W.carry(sK, Lds::LDQ, sV, Lds::LDV, fZ(b), Lds::LDX, sDec0 + b * M, sw, lane_i);
@@ -807,7 +823,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       // ---- exact token recurrence (no division by a decay product), on an
       // fp32 copy of the state in LDS; thread t owns slot t / TPS and 1/TPS of
       // its columns for the whole chunk
-      exact_chunk<DK, DV, M>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid_i);
+      exact_chunk<DK, DV, M, ACT>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid_i);
       small = factors(gr, rv1, b ^ 1, lane_i);
     }
     slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
@@ -820,7 +836,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
 }
 
 // ------------------------------------------------------------ launcher
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int ACT>
 static int launch(const GsaLaunch& a) {
   using LO = OutLds<DK, DV, M>;
   using LS = StateLds<DK, DV, M>;
@@ -831,7 +847,7 @@ static int launch(const GsaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   static const bool lds_set = [] {  // once per instantiation and process
-    (void)hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M, ACT>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LO::total);
     (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
@@ -859,11 +875,23 @@ static int launch(const GsaLaunch& a) {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gsa_bf16_out<DK, DV, M>, dim3(P * units), dim3(NT), LO::total, a.stream, a.events, 2,
+  launch_timed(gsa_bf16_out<DK, DV, M, ACT>, dim3(P * units), dim3(NT), LO::total, a.stream, a.events, 2,
                3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
                a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, (const float*)a.ws_dec,
                a.T, S, P, units, fold, inv_tau);
   return 0;
+}
+
+template <int DK, int DV, int M>
+static int launch_act(const GsaLaunch& a) {
+  switch (a.act) {
+    case kActSoftmax: return launch<DK, DV, M, kActSoftmax>(a);
+    case kActIdentity: return launch<DK, DV, M, kActIdentity>(a);
+    case kActSwish: return launch<DK, DV, M, kActSwish>(a);
+    case kActRelu: return launch<DK, DV, M, kActRelu>(a);
+    case kActRelu2: return launch<DK, DV, M, kActRelu2>(a);
+    default: return -1;
+  }
 }
 
 }  // namespace bfk
@@ -872,7 +900,7 @@ static int launch(const GsaLaunch& a) {
   if (dk == DKC && dv == DVC && m == MC) {                                \
     static_assert(bfk::OutLds<DKC, DVC, MC>::total <= kLdsBytes, "LDS"); \
     if (query) return bfk::OutLds<DKC, DVC, MC>::total;                   \
-    return bfk::launch<DKC, DVC, MC>(*a);                                 \
+    return bfk::launch_act<DKC, DVC, MC>(*a);                             \
   }
 
 // Returns: query -> LDS bytes (>0) or -1 if unsupported; launch -> 0 or -1.

@@ -14,6 +14,7 @@ struct GsaLaunch {
   float *ws_state, *ws_dec;
   int B, H, T, chunks_per_seg;
   float tau;
+  int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gsa_fwd_events
 };
@@ -40,6 +41,7 @@ struct DecodeLaunch {
   void* o;
   int N, H;
   float tau;
+  int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
   void* stream;
   void* const* events;  // nullable: 2 hipEvent_t, start and end of the kernel
 };

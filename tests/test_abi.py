@@ -29,7 +29,7 @@ def test_header_symbols_exported(gsa):
     assert {"gsa_fwd", "gla_fwd", "gsa_decode_step", "gsa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(gsa.lib, n), "missing export: " + n
-    assert gsa.lib.gsa_abi_version() == 1
+    assert gsa.lib.gsa_abi_version() == 2
 
 
 def test_status_strings(gsa):
@@ -121,6 +121,34 @@ def test_gla_and_decode_validation(gsa):
     args3 = list(args)
     args3[4] = None
     assert d(*args3, 1, 1, 128, 128, 64, 8.0, 1, None) == 1
+
+
+def test_nonlinearity_validation(gsa):
+    """The _ex entry points reject a code outside gsa_slot_nonlinearity with
+    GSA_ERR_SHAPE before looking at anything else, and take every listed code
+    as far as the (failing) pointer checks."""
+    P = ctypes.c_void_p
+    f = gsa.lib.gsa_fwd_ex
+    args = [P(FAKE), P(FAKE + 0x100000), P(FAKE + 0x200000), P(FAKE + 0x300000), P(None),
+            P(None), P(FAKE + 0x400000), P(None), P(None), 1, 1, 64, 128, 128, 64, 64, 8.0, 1,
+            None, 0, 0]
+    for bad in (-1, 5, 99):
+        assert f(*args, bad, None, None) == 2
+    unaligned = list(args)
+    unaligned[3] = P(FAKE + 0x300008)
+    for code in gsa.NONLINEARITIES.values():
+        assert f(*unaligned, code, None, None) == 3
+    d = gsa.lib.gsa_decode_step_ex
+    dargs = [P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000), P(FAKE + 0x3000), P(FAKE + 0x100000),
+             P(FAKE + 0x200000), P(FAKE + 0x4000), 1, 1, 128, 128, 64, 8.0, 1]
+    assert d(*dargs, 5, None, None) == 2
+    assert d(*dargs, -1, None, None) == 2
+    dbad = list(dargs)
+    dbad[4] = None
+    for code in gsa.NONLINEARITIES.values():
+        assert d(*dbad, code, None, None) == 1
+    with pytest.raises(ValueError):
+        gsa._nl("tanh")
 
 
 def test_package_has_no_cpu_fallback():
