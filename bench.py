@@ -301,6 +301,58 @@ def copy_calibration(torch, ev, steps):
             "GBps": round(2 * n / (t * 1e-3) / 1e9, 1)}
 
 
+def bench_serve(torch, gsa, ev, w, steps, warmup):
+    """The serving path: the prefill of 256 prompts of mixed lengths as one
+    packed variable-length call (final states written), then decode steps of
+    all 256 x H units from those states.  Prefill tokens/s counts prompt
+    tokens (sum of lengths) per second."""
+    import synth
+    from tests.gpu_helpers import to_dev
+    lengths = synth.varlen_lengths(w["N"], w["len_lo"], w["len_hi"], seed=0)
+    inp = synth.varlen_inputs(lengths, w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
+                              qkv_scale=w["qkv_scale"], g_shift=w["g_shift"])
+    cu = inp["cu_seqlens"]
+    n, H, dk, dv, m = w["N"], w["H"], w["dk"], w["dv"], w["m"]
+    total = int(cu[-1])
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g"], 2)
+    outs = [torch.empty((H, total, dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    kfs = [torch.empty((n, H, m, dk), dtype=torch.float32, device="cuda") for _ in sets]
+    vfs = [torch.empty((n, H, m, dv), dtype=torch.float32, device="cuda") for _ in sets]
+    nb = gsa.gsa_fwd_varlen_workspace_bytes(cu, H, dk, dv, m)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def call(s, events):
+        i = next(j for j, x in enumerate(sets) if x is s)
+        gsa.gsa_fwd_varlen(s["q"], s["k"], s["v"], s["g"], cu, tau=w["tau"], final_state=True,
+                           out=outs[i], k_final=kfs[i], v_final=vfs[i], workspace=ws, events=events)
+
+    wall, ph = time_op(torch, ev, call, sets, steps, warmup)
+    # each prompt token-head: q, k, v, g read and o written once; final states written once
+    nbytes = H * total * (2 * dk + 2 * dv + m) * 2 + n * H * m * (dk + dv) * 4
+    t_op, t_out = mean([p[3] for p in ph]), mean([p[2] for p in ph])
+    # decode steps from the prefill's final states (one new token per sequence)
+    tok = synth.decode_inputs(n, H, dk, dv, m, dtype=w["dtype"], seed=1, qkv_scale=w["qkv_scale"])
+    td = {x: to_dev(tok[x], torch) for x in "qkvg"}
+    ks, vs = kfs[0], vfs[0]
+    dout = torch.empty((n, H, dv), dtype=torch.bfloat16, device="cuda")
+    devs = ev.create(2 * steps)
+    for i in range(steps):
+        gsa.gsa_decode_step(td["q"], td["k"], td["v"], td["g"], ks, vs, tau=w["tau"], out=dout,
+                            events=devs[2 * i: 2 * i + 2])
+    torch.cuda.synchronize()
+    t_dec = mean([ev.ms(devs[2 * i], devs[2 * i + 1]) for i in range(steps)])
+    dec_bytes = n * H * (2 * 4 * m * (dk + dv) + 2 * (2 * dk + 2 * dv + m))
+    return {"value": round(total * steps / wall, 1), "unit": "prompt tokens/s",
+            "prompts": n, "H": H, "prompt_tokens": total, "len_min": min(lengths),
+            "len_max": max(lengths), "ms_per_prefill": round(wall / steps * 1e3, 4),
+            "ms_phases": {"state_maps": round(mean([p[0] for p in ph]), 4),
+                          "scan": round(mean([p[1] for p in ph]), 4), "outputs": round(t_out, 4),
+                          "op": round(t_op, 4)},
+            "roofline": roofline(nbytes, t_out, "gsa_bf16_out", "gsa_bf16_serve_N256"),
+            "decode_ms_kernel": round(t_dec, 4),
+            "decode_roofline": roofline(dec_bytes, t_dec, "gsa_decode_kernel", "gsa_decode_N256")}
+
+
 def bench_ablations(torch, gsa, ev, steps, warmup, nsets):
     """The training-shape GSA forward with each element-wise slot read of the
     ablation study in place of the softmax (same launch sequence; only the
@@ -332,6 +384,9 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "serve":
+        return bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
+                           args.warmup)
     if args.only == "ablations":
         return bench_ablations(torch, gsa, ev, args.steps, args.warmup, args.sets)
     if args.only == "gla":
@@ -348,7 +403,7 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy", "ablations"], default=None,
+    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy", "ablations", "serve"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -393,6 +448,10 @@ def main():
         comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
                                                 args.steps, args.warmup)
         log("bench: decode done")
+        comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
+                                                   max(1, args.steps // 2), args.warmup)
+        log("bench: serving prefill + decode done")
+        torch.cuda.empty_cache()
         comps["gsa_bf16_train_T2048_read_ablations"] = bench_ablations(
             torch, gsa, ev, max(1, args.steps // 2), args.warmup, args.sets)
         log("bench: read ablations done")

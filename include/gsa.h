@@ -114,6 +114,36 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
             int chunks_per_segment, void* stream);
 
 /*
+ * GSA forward over a packed batch of variable-length sequences (the prefill of
+ * a serving batch), with the chunkwise form above applied to every sequence
+ * independently.  The final states it writes are the decode states of
+ * gsa_decode_step for the same n_seqs x H units.
+ *   cu_seqlens  HOST int32 [n_seqs + 1]: cu_seqlens[0] = 0, non-decreasing;
+ *               sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1;
+ *               total = cu_seqlens[n_seqs].  Read during the call only.
+ *               Empty sequences are allowed (their final state is the
+ *               initial one, they have no outputs).  n_seqs <= 256.
+ *   q, k     [H, total, dk]  bf16   head-major packed tokens
+ *   v        [H, total, dv]  bf16
+ *   g        [H, total, m]   bf16   forget-gate logits
+ *   k0, v0   [n_seqs, H, m, dk|dv] float32 initial states, NULL = zeros
+ *   o        [H, total, dv]  bf16
+ *   k_final, v_final [n_seqs, H, m, dk|dv] float32, NULL = not wanted (may
+ *            equal k0 / v0)
+ * Only bf16 storage and the softmax read are compiled for this entry point
+ * (GSA_ERR_UNSUPPORTED otherwise); a bad cu_seqlens returns GSA_ERR_SHAPE.
+ * Workspace, aliasing, events and errors as for gsa_fwd_events; the workspace
+ * size comes from gsa_fwd_varlen_workspace_bytes with the same cu_seqlens.
+ */
+size_t gsa_fwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv,
+                                      int m, int C, int dtype, int chunks_per_segment);
+int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                   const int* cu_seqlens, int n_seqs, int H, const float* k0, const float* v0,
+                   void* o, float* k_final, float* v_final, int dk, int dv, int m, int C, float tau,
+                   int dtype, void* workspace, size_t workspace_bytes, int chunks_per_segment,
+                   void* stream, void* const* events);
+
+/*
  * GLA forward, chunkwise-parallel (Sec. 2.3, App. A.1).
  *   q, k, g  [B,H,T,dk]  dtype   g: one gate logit per key dimension
  *   v        [B,H,T,dv]  dtype

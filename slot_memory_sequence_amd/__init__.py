@@ -16,7 +16,8 @@ import os
 # and allocations are valid handles for the library.
 import torch as _torch_rt  # noqa: F401
 
-__all__ = ["lib", "gsa_fwd", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH", "NONLINEARITIES",
+__all__ = ["lib", "gsa_fwd", "gsa_fwd_varlen", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH",
+           "NONLINEARITIES", "gsa_fwd_varlen_workspace_bytes",
            "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
            "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
 
@@ -57,6 +58,10 @@ lib.gsa_decode_step_events.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P, _P]
 lib.gsa_fwd_ex.restype = _I
 lib.gsa_fwd_ex.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_decode_step_ex.restype = _I
+lib.gsa_fwd_varlen.restype = _I
+lib.gsa_fwd_varlen.argtypes = [_P] * 5 + [_I, _I] + [_P] * 5 + [_I] * 4 + [_F, _I, _P, _S, _I, _P, _P]
+lib.gsa_fwd_varlen_workspace_bytes.restype = _S
+lib.gsa_fwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 8
 lib.gsa_decode_step_ex.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _I, _P, _P]
 
 
@@ -88,6 +93,21 @@ def gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C=64, dtype=DTYPE_BF16, chunks_p
 
 def gla_fwd_workspace_bytes(B, H, T, dk, dv, C=64, dtype=DTYPE_BF16, chunks_per_segment=0):
     return int(lib.gla_fwd_workspace_bytes(B, H, T, dk, dv, C, dtype, chunks_per_segment))
+
+
+def _cu_array(cu_seqlens):
+    """Host int32 offsets [n + 1] as a ctypes array (kept alive by the caller)."""
+    vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if len(vals) < 1:
+        raise ValueError("cu_seqlens needs at least one entry (0)")
+    return (ctypes.c_int * len(vals))(*vals), len(vals) - 1
+
+
+def gsa_fwd_varlen_workspace_bytes(cu_seqlens, H, dk, dv, m, C=64, dtype=DTYPE_BF16,
+                                   chunks_per_segment=0):
+    arr, n = _cu_array(cu_seqlens)
+    return int(lib.gsa_fwd_varlen_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), n, H, dk, dv,
+                                                  m, C, dtype, chunks_per_segment))
 
 
 # ------------------------------------------------------------- marshalling
@@ -182,6 +202,49 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
                         _events(events))
     if st:
         raise GsaError("gsa_fwd", st)
+    return out, k_final, v_final
+
+
+def gsa_fwd_varlen(q, k, v, g, cu_seqlens, k0=None, v0=None, *, tau=8.0, C=64,
+                   final_state=False, chunks_per_segment=0, out=None, k_final=None,
+                   v_final=None, workspace=None, stream=None, events=None):
+    """GSA forward over a packed batch of variable-length sequences.  q, k
+    [H,total,dk]; v [H,total,dv]; g [H,total,m] (bf16, head-major packed);
+    cu_seqlens: host offsets [n+1] (list, numpy or CPU tensor), cu[0] = 0;
+    optional float32 initial states k0 [n,H,m,dk], v0 [n,H,m,dv].
+    Returns (o [H,total,dv], k_final, v_final) -- finals None unless
+    final_state; they are the decode states of gsa_decode_step."""
+    torch = _torch()
+    for nm, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, nm, q.dtype)
+    _check(k0, "k0", torch.float32)
+    _check(v0, "v0", torch.float32)
+    H, total, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    dt = _dt(q)
+    arr, n = _cu_array(cu_seqlens)
+    if arr[n] != total:
+        raise ValueError("cu_seqlens[-1] = %d but the arrays hold %d tokens" % (arr[n], total))
+    if out is None:
+        out = torch.empty((H, total, dv), dtype=q.dtype, device=q.device)
+    if final_state:
+        if k_final is None:
+            k_final = torch.empty((n, H, m, dk), dtype=torch.float32, device=q.device)
+        if v_final is None:
+            v_final = torch.empty((n, H, m, dv), dtype=torch.float32, device=q.device)
+    nbytes = int(lib.gsa_fwd_varlen_workspace_bytes(ctypes.cast(arr, ctypes.c_void_p), n, H, dk,
+                                                    dv, m, C, dt, chunks_per_segment))
+    if nbytes == (1 << 64) - 1:
+        raise ValueError("invalid cu_seqlens or problem size")
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), ctypes.cast(arr, ctypes.c_void_p),
+                            n, H, _ptr(k0), _ptr(v0), _ptr(out), _ptr(k_final), _ptr(v_final),
+                            dk, dv, m, C, float(tau), dt, _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                            _stream(stream), _events(events))
+    if st:
+        raise GsaError("gsa_fwd_varlen", st)
     return out, k_final, v_final
 
 

@@ -79,6 +79,90 @@ int hip_status() {
   return e == hipSuccess ? GSA_OK : GSA_ERR_HIP;
 }
 
+// A packed variable-length batch: cu (host) holds n + 1 non-decreasing token
+// offsets starting at 0.  Also gives the longest length and the chunk count
+// over all sequences (one head).
+bool varlen_ok(const int* cu, int n, int* tmax, long long* chunks) {
+  if (!cu || n < 0 || n > gsa::kMaxVarSeqs || cu[0] != 0) return false;
+  int mx = 0;
+  long long ch = 0;
+  for (int i = 0; i < n; i++) {
+    if (cu[i + 1] < cu[i]) return false;
+    const int len = cu[i + 1] - cu[i];
+    if (len > mx) mx = len;
+    ch += (len + kChunk - 1) / kChunk;
+  }
+  *tmax = mx;
+  *chunks = ch;
+  return true;
+}
+
+// Chunks per segment for a packed batch: enough segments over all non-empty
+// (sequence, head) units for about kTargetWorkgroups output workgroups (equal
+// lengths give the dense batch's split).
+int resolve_cps_var(int H, int tmax, long long chunks_per_head, int cps) {
+  const int nchunks = (tmax + kChunk - 1) / kChunk;
+  if (cps <= 0) {
+    const long long total = chunks_per_head * H;
+    cps = (int)((total + kTargetWorkgroups - 1) / kTargetWorkgroups);
+  }
+  if (nchunks > 0 && cps > nchunks) cps = nchunks;
+  return cps < 1 ? 1 : cps;
+}
+
+// Validation of pointers, aliasing and workspace, then the launches; shared by
+// the dense batch (cu == nullptr: B sequences of T tokens) and the packed
+// variable-length batch (B = n sequences, T = the longest, ntok rows in all).
+int gsa_run(const void* q, const void* k, const void* v, const void* g, const float* k0,
+            const float* v0, void* o, float* kf, float* vf, int B, int H, int T, size_t ntok, int c,
+            const int* cu, int dk, int dv, int m, float tau, int dtype, void* workspace,
+            size_t workspace_bytes, int nonlinearity, void* stream, void* const* events) {
+  const long long units = (long long)B * H;
+  if (ntok > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const size_t nt = ntok;
+  const Range rq = rng(q, nt * dk * es), rk = rng(k, nt * dk * es), rv = rng(v, nt * dv * es),
+              rg = rng(g, nt * m * es), ro = rng(o, nt * dv * es);
+  const Range rk0 = rng(k0, (size_t)units * m * dk * 4), rv0 = rng(v0, (size_t)units * m * dv * 4);
+  const Range rkf = rng(kf, (size_t)units * m * dk * 4), rvf = rng(vf, (size_t)units * m * dv * 4);
+  const Range rws = rng(workspace, workspace_bytes);
+  for (Range in : {rq, rk, rv, rg, rk0, rv0, rkf, rvf, rws})
+    if (overlap(ro, in)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, ro, rws}) {
+    if (overlap(rkf, in) || overlap(rvf, in)) return GSA_ERR_ALIAS;
+  }
+  if (overlap(rkf, rvf) || overlap(rkf, rv0) || overlap(rvf, rk0)) return GSA_ERR_ALIAS;
+  if ((kf && k0 && kf != k0 && overlap(rkf, rk0)) || (vf && v0 && vf != v0 && overlap(rvf, rv0)))
+    return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg, rk0, rv0})
+    if (overlap(rws, in)) return GSA_ERR_ALIAS;
+  const size_t need = ws_bytes(units, T, c, (size_t)m * (dk + dv), (size_t)m);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
+
+  if (T == 0) {  // nothing to read: the final state is the initial state
+    gsa::state_copy(kf, k0, (size_t)units * m * dk, stream);
+    gsa::state_copy(vf, v0, (size_t)units * m * dv, stream);
+    return hip_status();
+  }
+  gsa::GsaLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.k0 = k0; a.v0 = v0; a.o = o; a.kf = kf; a.vf = vf;
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const long long P = (nchunks + c - 1) / c;
+  a.ws_state = (float*)workspace;
+  a.ws_dec = workspace ? (float*)((char*)workspace +
+                                  (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
+                       : nullptr;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
+  a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
+  a.stream = stream; a.events = events;
+  (void)hipGetLastError();
+  if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,49 +240,41 @@ int gsa_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   const long long units = (long long)B * H;
   if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
   if (units == 0) return GSA_OK;
-  if (T > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return GSA_ERR_ALIGN;
-  const size_t es = esize(dtype);
-  const size_t nt = (size_t)units * T;
-  const Range rq = rng(q, nt * dk * es), rk = rng(k, nt * dk * es), rv = rng(v, nt * dv * es),
-              rg = rng(g, nt * m * es), ro = rng(o, nt * dv * es);
-  const Range rk0 = rng(k0, (size_t)units * m * dk * 4), rv0 = rng(v0, (size_t)units * m * dv * 4);
-  const Range rkf = rng(kf, (size_t)units * m * dk * 4), rvf = rng(vf, (size_t)units * m * dv * 4);
-  const Range rws = rng(workspace, workspace_bytes);
-  for (Range in : {rq, rk, rv, rg, rk0, rv0, rkf, rvf, rws})
-    if (overlap(ro, in)) return GSA_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, rg, ro, rws}) {
-    if (overlap(rkf, in) || overlap(rvf, in)) return GSA_ERR_ALIAS;
-  }
-  if (overlap(rkf, rvf) || overlap(rkf, rv0) || overlap(rvf, rk0)) return GSA_ERR_ALIAS;
-  if ((kf && k0 && kf != k0 && overlap(rkf, rk0)) || (vf && v0 && vf != v0 && overlap(rvf, rv0)))
-    return GSA_ERR_ALIAS;
-  for (Range in : {rq, rk, rv, rg, rk0, rv0})
-    if (overlap(rws, in)) return GSA_ERR_ALIAS;
-  const int c = resolve_cps(units, T, cps);
-  const size_t need = ws_bytes(units, T, c, (size_t)m * (dk + dv), (size_t)m);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
+  return gsa_run(q, k, v, g, k0, v0, o, kf, vf, B, H, T, (size_t)units * T,
+                 resolve_cps(units, T, cps), nullptr, dk, dv, m, tau, dtype, workspace,
+                 workspace_bytes, nonlinearity, stream, events);
+}
 
-  if (T == 0) {  // nothing to read: the final state is the initial state
-    gsa::state_copy(kf, k0, (size_t)units * m * dk, stream);
-    gsa::state_copy(vf, v0, (size_t)units * m * dv, stream);
-    return hip_status();
-  }
-  gsa::GsaLaunch a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.k0 = k0; a.v0 = v0; a.o = o; a.kf = kf; a.vf = vf;
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  const long long P = (nchunks + c - 1) / c;
-  a.ws_state = (float*)workspace;
-  a.ws_dec = workspace ? (float*)((char*)workspace +
-                                  (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
-                       : nullptr;
-  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
-  a.stream = stream; a.events = events;
-  (void)hipGetLastError();
-  if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
-  return hip_status();
+size_t gsa_fwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv,
+                                      int m, int C, int dtype, int cps) {
+  int tmax = 0;
+  long long total_chunks = 0;
+  if (H < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !dtype_ok(dtype) ||
+      !varlen_ok(cu_seqlens, n_seqs, &tmax, &total_chunks))
+    return (size_t)-1;
+  const long long units = (long long)n_seqs * H;
+  return ws_bytes(units, tmax, resolve_cps_var(H, tmax, total_chunks, cps), (size_t)m * (dk + dv),
+                  (size_t)m);
+}
+
+int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                   const int* cu_seqlens, int n_seqs, int H, const float* k0, const float* v0,
+                   void* o, float* kf, float* vf, int dk, int dv, int m, int C, float tau, int dtype,
+                   void* workspace, size_t workspace_bytes, int cps, void* stream,
+                   void* const* events) {
+  int tmax = 0;
+  long long total_chunks = 0;
+  if (H < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
+      !dtype_ok(dtype) || !varlen_ok(cu_seqlens, n_seqs, &tmax, &total_chunks))
+    return GSA_ERR_SHAPE;
+  if (dtype != GSA_DTYPE_BF16 || !gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)n_seqs * H;
+  if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  if (units == 0) return GSA_OK;
+  return gsa_run(q, k, v, g, k0, v0, o, kf, vf, n_seqs, H, tmax,
+                 (size_t)H * (size_t)cu_seqlens[n_seqs], resolve_cps_var(H, tmax, total_chunks, cps),
+                 cu_seqlens, dk, dv, m, tau, dtype, workspace, workspace_bytes, GSA_SLOT_SOFTMAX,
+                 stream, events);
 }
 
 int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,

@@ -3,6 +3,7 @@
 // bf16 rows, wave-wide DPP scans and the log2-domain gate.
 #pragma once
 #include "common.hpp"
+#include "internal.hpp"
 
 namespace gsa {
 namespace bfk {
@@ -301,6 +302,35 @@ __device__ __forceinline__ SegUnit seg_unit(int id, int P, int units, int fold) 
   }
   return {id % P, id / P};
 }
+
+// ------------------------------------------------------------ sequences
+// Where the tokens of unit u sit: rows [base, base + len) of the q, k, v, g and
+// o arrays, one row per token (row pitch d, so a chunk is one contiguous tile).
+struct Span {
+  size_t base;
+  int len;
+};
+
+// A dense batch [B, H, T, d]: unit u = b*H + h holds rows u*T .. u*T + T - 1.
+struct DenseSeqs {
+  static constexpr bool kVar = false;
+  int T;
+  __device__ __forceinline__ Span span(int unit) const { return {(size_t)unit * T, T}; }
+};
+
+// A packed batch of n variable-length sequences, head-major [H, total, d]:
+// sequence s of head h holds rows h*total + cu[s] .. h*total + cu[s+1] - 1 and
+// is unit u = s*H + h (the states stay [n, H, m, d]).  Passed by value, so the
+// offsets live in the kernel arguments and need no device memory.
+struct VarSeqs {
+  static constexpr bool kVar = true;
+  int H, total;
+  int cu[kMaxVarSeqs + 1];
+  __device__ __forceinline__ Span span(int unit) const {
+    const int s = unit / H, h = unit - s * H;
+    return {(size_t)h * total + cu[s], cu[s + 1] - cu[s]};
+  }
+};
 
 }  // namespace bfk
 }  // namespace gsa

@@ -554,12 +554,14 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv,
 // ------------------------------------------------ phase A: segment maps
 // grid (P-1, units).  Map of segment seg from a zero start:
 // D = sum over its tokens of Diag(prod_{i>r} alpha_i)(1-alpha_r)[k_r|v_r]^T and
-// the segment decay product.  All eight waves carry state columns.
-template <int DK, int DV, int M>
+// the segment decay product.  All eight waves carry state columns.  A segment
+// past the end of its sequence (variable-length batches) writes the identity
+// map (D = 0, decay 1).
+template <int DK, int DV, int M, class Seq>
 __global__ void __launch_bounds__(NT, 1)
 gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
                const bf16_t* __restrict__ gg, float* __restrict__ ws_state,
-               float* __restrict__ ws_dec, int T_len, int S, int P, float inv_tau) {
+               float* __restrict__ ws_dec, Seq seq, int S, int P, float inv_tau) {
   using Lds = StateLds<DK, DV, M>;
   constexpr int SPT = M / NW;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -570,11 +572,13 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int seg = blockIdx.x, unit = blockIdx.y;
+  const Span sp = seq.span(unit);
+  const int T_len = sp.len;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
-  const bf16_t* kb = kk + (size_t)unit * T_len * DK;
-  const bf16_t* vb = vv + (size_t)unit * T_len * DV;
-  const bf16_t* gb = gg + (size_t)unit * T_len * M + wv * SPT;
+  const bf16_t* kb = kk + sp.base * DK;
+  const bf16_t* vb = vv + sp.base * DV;
+  const bf16_t* gb = gg + sp.base * M + wv * SPT;
 
   StateTiles<DK, DV, M, NW> W;
   W.zero();
@@ -606,6 +610,9 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
     store_bf16_row<SPT>(bZ(b) + lane_ * Lds::LDX + wv * SPT, gt.Z);
   };
 
+  if (Seq::kVar && c_begin >= c_end) {
+    // no tokens: the identity map (W and segdec as initialised)
+  } else {
   load_chunk(c_begin, tid, lane);
   stage_chunk(c_begin, 0, true, tid, lane);
   load_chunk(min(c_begin + 1, c_end - 1), tid, lane);
@@ -623,6 +630,7 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
     W.carry(bK(b), Lds::LDQ, bV(b), Lds::LDV, bZ(b), Lds::LDX, bDec(b), wv, lane_i);
     __syncthreads();
     b ^= 1;
+  }
   }
   W.store_w_nt(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), wv, lane);
   if (lane == 0) {
@@ -674,13 +682,13 @@ gsa_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
 }
 
 // ------------------------------------------------------ phase C: outputs
-template <int DK, int DV, int M, int ACT>
+template <int DK, int DV, int M, int ACT, class Seq>
 __global__ void __launch_bounds__(NT, 1)
 gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const bf16_t* __restrict__ vv, const bf16_t* __restrict__ gg,
              const float* __restrict__ k0, const float* __restrict__ v0,
              const float* __restrict__ ws_state, bf16_t* __restrict__ oo, float* __restrict__ kf,
-             float* __restrict__ vf, const float* __restrict__ ws_dec, int T_len, int S, int P,
+             float* __restrict__ vf, const float* __restrict__ ws_dec, Seq seq, int S, int P,
              int units, int fold, float inv_tau) {
   using Lds = OutLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
@@ -707,9 +715,16 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const int slot0 = wv * GPW;  // this wave's first gate slot
   const SegUnit su = seg_unit(blockIdx.x, P, units, fold);
   const int seg = su.seg, unit = su.unit;
+  const Span sp = seq.span(unit);
+  const int T_len = sp.len;
   const int nchunks = (T_len + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
-  const size_t ub = (size_t)unit * T_len;
+  // a segment past the end of its sequence (variable-length batches only) has
+  // no tokens: it only hands its start state on as the final state when it is
+  // the unit's last segment
+  const bool empty = Seq::kVar && c_begin >= c_end;
+  if (empty && seg != P - 1) return;
+  const size_t ub = sp.base;
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
@@ -750,10 +765,12 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   bool slow;
   {
     const int t0 = c_begin * C, rv = rows_of(c_begin);
-    pq.load(qb + (size_t)t0 * DK, rv, tid);
-    pk.load(kb + (size_t)t0 * DK, rv, tid);
-    pv.load(vb + (size_t)t0 * DV, rv, tid);
-    load_gates(gr, t0, rv, lane);
+    if (!empty) {
+      pq.load(qb + (size_t)t0 * DK, rv, tid);
+      pk.load(kb + (size_t)t0 * DK, rv, tid);
+      pv.load(vb + (size_t)t0 * DV, rv, tid);
+      load_gates(gr, t0, rv, lane);
+    }
     if (is_state) {
       if (P > 1 && !fold) {
         W.load_w(ws_state + ((size_t)unit * P + seg) * M * (DK + DV), sw, lane);  // from the scan
@@ -779,7 +796,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       }
       W.store_copy(sW, Lds::LDW, sw, lane);
     }
-    slow = block_any(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
+    slow = empty ? false : block_any(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
   }
 
   int b = 0;  // factor set of the current chunk
@@ -836,8 +853,11 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
 }
 
 // ------------------------------------------------------------ launcher
-template <int DK, int DV, int M, int ACT>
-static int launch(const GsaLaunch& a) {
+// a.T is the sequence length (dense) or the longest one (variable-length);
+// the segment count P follows from it, and the segments of shorter sequences
+// past their end are empty.
+template <int DK, int DV, int M, int ACT, class Seq>
+static int launch(const GsaLaunch& a, const Seq& seq) {
   using LO = OutLds<DK, DV, M>;
   using LS = StateLds<DK, DV, M>;
   const int units = a.B * a.H;
@@ -847,9 +867,9 @@ static int launch(const GsaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   static const bool lds_set = [] {  // once per instantiation and process
-    (void)hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M, ACT>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_out<DK, DV, M, ACT, Seq>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LO::total);
-    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M, Seq>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
     return true;
   }();
@@ -863,9 +883,9 @@ static int launch(const GsaLaunch& a) {
   const bool in_place = (a.kf && a.kf == a.k0) || (a.vf && a.vf == a.v0);
   const int fold = P > 1 && P - 1 <= kMaxFoldedMaps && !in_place;
   if (P > 1) {
-    launch_timed(gsa_bf16_state<DK, DV, M>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
+    launch_timed(gsa_bf16_state<DK, DV, M, Seq>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
                  a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
-                 a.ws_state, a.ws_dec, a.T, S, P, inv_tau);
+                 a.ws_state, a.ws_dec, seq, S, P, inv_tau);
     if (!fold) {
       const long long ne = (long long)units * M * (DK + DV);
       hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
@@ -875,21 +895,30 @@ static int launch(const GsaLaunch& a) {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gsa_bf16_out<DK, DV, M, ACT>, dim3(P * units), dim3(NT), LO::total, a.stream, a.events, 2,
-               3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
-               a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf, (const float*)a.ws_dec,
-               a.T, S, P, units, fold, inv_tau);
+  launch_timed(gsa_bf16_out<DK, DV, M, ACT, Seq>, dim3(P * units), dim3(NT), LO::total, a.stream,
+               a.events, 2, 3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+               (const bf16_t*)a.g, a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf,
+               (const float*)a.ws_dec, seq, S, P, units, fold, inv_tau);
   return 0;
 }
 
 template <int DK, int DV, int M>
 static int launch_act(const GsaLaunch& a) {
+  if (a.cu_seqlens) {  // packed variable-length batch: the softmax read only
+    if (a.act != kActSoftmax || a.n_seqs < 0 || a.n_seqs > kMaxVarSeqs) return -1;
+    VarSeqs vs{};
+    vs.H = a.H;
+    vs.total = a.cu_seqlens[a.n_seqs];
+    for (int i = 0; i <= a.n_seqs; i++) vs.cu[i] = a.cu_seqlens[i];
+    return launch<DK, DV, M, kActSoftmax, VarSeqs>(a, vs);
+  }
+  const DenseSeqs ds{a.T};
   switch (a.act) {
-    case kActSoftmax: return launch<DK, DV, M, kActSoftmax>(a);
-    case kActIdentity: return launch<DK, DV, M, kActIdentity>(a);
-    case kActSwish: return launch<DK, DV, M, kActSwish>(a);
-    case kActRelu: return launch<DK, DV, M, kActRelu>(a);
-    case kActRelu2: return launch<DK, DV, M, kActRelu2>(a);
+    case kActSoftmax: return launch<DK, DV, M, kActSoftmax>(a, ds);
+    case kActIdentity: return launch<DK, DV, M, kActIdentity>(a, ds);
+    case kActSwish: return launch<DK, DV, M, kActSwish>(a, ds);
+    case kActRelu: return launch<DK, DV, M, kActRelu>(a, ds);
+    case kActRelu2: return launch<DK, DV, M, kActRelu2>(a, ds);
     default: return -1;
   }
 }

@@ -5,6 +5,7 @@
 namespace gsa {
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kMaxVarSeqs = 256;       // sequences per variable-length call
 
 struct GsaLaunch {
   const void *q, *k, *v, *g;
@@ -15,6 +16,11 @@ struct GsaLaunch {
   int B, H, T, chunks_per_seg;
   float tau;
   int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
+  // Packed variable-length batch (bf16 only): n_seqs sequences, host offsets
+  // cu_seqlens[0..n_seqs] (validated), T = the longest length, B = n_seqs.
+  // cu_seqlens == nullptr: the dense [B, H, T, d] batch.
+  const int* cu_seqlens;
+  int n_seqs;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gsa_fwd_events
 };

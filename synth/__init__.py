@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "Stored", "bf16_bits", "bf16_to_f64", "stored", "gsa_inputs", "gla_inputs",
-    "decode_inputs", "WORKLOADS",
+    "decode_inputs", "varlen_lengths", "varlen_inputs", "WORKLOADS",
 ]
 
 
@@ -123,6 +123,40 @@ def decode_inputs(N, H, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
                 g=stored(g, dtype), kstate=stored(ks, "f32"), vstate=stored(vs, "f32"))
 
 
+def varlen_lengths(n, lo, hi, seed=0):
+    """n sequence lengths, log-uniform in [lo, hi] (a prompt-length mix with
+    many short and few long sequences), from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return [int(round(math.exp(t))) for t in x]
+
+
+def varlen_inputs(lengths, H, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
+                  g_shift=0.0, init_std=None):
+    """A packed batch of len(lengths) sequences, head-major: cu_seqlens [n+1]
+    (int32 offsets, cu[0] = 0); q,k ~ N(0,1)*qkv_scale [H,total,dk]; v
+    [H,total,dv]; g ~ N(0,1)+g_shift [H,total,m]; optional K0 [n,H,m,dk],
+    V0 [n,H,m,dv] ~ N(0, init_std) stored as float32.  Draw order as for
+    gsa_inputs."""
+    rng = np.random.default_rng(seed)
+    if qkv_scale is None:
+        qkv_scale = 1.0 / math.sqrt(dk)
+    n = len(lengths)
+    cu = np.zeros(n + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    total = int(cu[-1])
+    q = _normal(rng, (H, total, dk)) * qkv_scale
+    k = _normal(rng, (H, total, dk)) * qkv_scale
+    v = _normal(rng, (H, total, dv)) * qkv_scale
+    g = _normal(rng, (H, total, m)) + g_shift
+    out = dict(cu_seqlens=cu, q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
+               g=stored(g, dtype), k0=None, v0=None)
+    if init_std is not None:
+        out["k0"] = stored(_normal(rng, (n, H, m, dk)) * init_std, "f32")
+        out["v0"] = stored(_normal(rng, (n, H, m, dv)) * init_std, "f32")
+    return out
+
+
 # The five workloads: sizes, dtypes and value distributions of the method's
 # configurations (GSA: tau = 8 per the paper's Sec. 3.3; the standalone GLA
 # case uses tau = 16).
@@ -140,4 +174,10 @@ WORKLOADS = {
                                  g_shift=2.0, init_std=0.1),
     "gsa_decode_N256": dict(op="decode", N=256, H=16, dk=128, dv=128, m=64, tau=8.0,
                             dtype="bf16", qkv_scale=1 / math.sqrt(128), state_std=0.1),
+    # serving: the prefill of the decode batch's 256 sequences (prompt lengths
+    # log-uniform in [16, 1024]) as one packed variable-length call, then decode
+    # steps from its final states
+    "gsa_bf16_serve_N256": dict(op="serve", N=256, H=16, dk=128, dv=128, m=64, C=64, tau=8.0,
+                                dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
+                                len_lo=16, len_hi=1024),
 }

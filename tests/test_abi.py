@@ -151,6 +151,39 @@ def test_nonlinearity_validation(gsa):
         gsa._nl("tanh")
 
 
+def test_varlen_validation(gsa):
+    """The packed variable-length forward checks its host offsets before
+    anything is enqueued."""
+    P = ctypes.c_void_p
+    f = gsa.lib.gsa_fwd_varlen
+
+    def call(cu, n=None, H=2, dtype=1, q=FAKE, dk=128):
+        arr = (ctypes.c_int * len(cu))(*cu)
+        n = len(cu) - 1 if n is None else n
+        return f(P(q), P(FAKE + 0x1000000), P(FAKE + 0x2000000), P(FAKE + 0x3000000),
+                 ctypes.cast(arr, P), n, H, None, None, P(FAKE + 0x4000000), None, None, dk, dk,
+                 64, 64, 8.0, dtype, None, 0, 0, None, None)
+
+    assert call([1, 5]) == 2                       # cu[0] != 0
+    assert call([0, 70, 60]) == 2                  # decreasing
+    assert call([0, 5], n=-1) == 2
+    assert call([0] * 258) == 2                    # more than 256 sequences
+    assert f(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 1, 2, None, None, P(FAKE), None, None,
+             128, 128, 64, 64, 8.0, 1, None, 0, 0, None, None) == 2   # no offsets
+    assert call([0, 5, 9], dtype=0) == 4           # bf16 only
+    assert call([0, 5, 9], dk=96) == 4
+    assert call([0, 5, 9], q=FAKE + 8) == 3
+    assert call([0, 5, 9], q=None) == 1
+    ws = gsa.gsa_fwd_varlen_workspace_bytes
+    # equal lengths split exactly like the dense batch
+    assert ws([0, 2048, 4096, 6144, 8192], 8, 128, 128, 64) == \
+        gsa.gsa_fwd_workspace_bytes(4, 8, 2048, 128, 128, 64, 64, 1, 0)
+    assert ws([0, 64] + [64] * 0, 1, 128, 128, 64) == 0
+    assert ws([0, 5, 3], 2, 128, 128, 64) == (1 << 64) - 1
+    with pytest.raises(ValueError):
+        ws([], 2, 128, 128, 64)
+
+
 def test_package_has_no_cpu_fallback():
     """The product package never imports, loads or calls the oracle."""
     pkg = os.path.join(ROOT, "slot_memory_sequence_amd")
