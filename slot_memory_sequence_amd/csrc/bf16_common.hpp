@@ -312,23 +312,32 @@ struct Span {
 };
 
 // A dense batch [B, H, T, d]: unit u = b*H + h holds rows u*T .. u*T + T - 1.
+// unit_of maps the launch order of the units to the units (here the identity).
 struct DenseSeqs {
   static constexpr bool kVar = false;
   int T;
   __device__ __forceinline__ Span span(int unit) const { return {(size_t)unit * T, T}; }
+  __device__ __forceinline__ int unit_of(int i) const { return i; }
 };
 
 // A packed batch of n variable-length sequences, head-major [H, total, d]:
 // sequence s of head h holds rows h*total + cu[s] .. h*total + cu[s+1] - 1 and
 // is unit u = s*H + h (the states stay [n, H, m, d]).  Passed by value, so the
-// offsets live in the kernel arguments and need no device memory.
+// offsets live in the kernel arguments and need no device memory.  The units
+// are launched longest sequence first (order[] = the sequences by decreasing
+// length), so that the short ones fill the tail of the grid.
 struct VarSeqs {
   static constexpr bool kVar = true;
   int H, total;
   int cu[kMaxVarSeqs + 1];
+  int order[kMaxVarSeqs];
   __device__ __forceinline__ Span span(int unit) const {
     const int s = unit / H, h = unit - s * H;
     return {(size_t)h * total + cu[s], cu[s + 1] - cu[s]};
+  }
+  __device__ __forceinline__ int unit_of(int i) const {
+    const int r = i / H;
+    return order[r] * H + (i - r * H);
   }
 };
 

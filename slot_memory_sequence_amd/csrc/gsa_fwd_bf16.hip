@@ -34,6 +34,7 @@
 // such reads).  A chunk whose decay product falls below e^-40
 // in some slot is run as the exact token recurrence instead (no division by a
 // decay product).
+#include <algorithm>
 #include <type_traits>
 
 #include "bf16_common.hpp"
@@ -571,7 +572,7 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
   auto bDec = [&](int b) { return reinterpret_cast<float*>(smem + b * Lds::szBuf + Lds::oDec); };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int seg = blockIdx.x, unit = blockIdx.y;
+  const int seg = blockIdx.x, unit = seq.unit_of(blockIdx.y);
   const Span sp = seq.span(unit);
   const int T_len = sp.len;
   const int nchunks = (T_len + C - 1) / C;
@@ -714,7 +715,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const int sw = wv - 4;
   const int slot0 = wv * GPW;  // this wave's first gate slot
   const SegUnit su = seg_unit(blockIdx.x, P, units, fold);
-  const int seg = su.seg, unit = su.unit;
+  const int seg = su.seg, unit = seq.unit_of(su.unit);
   const Span sp = seq.span(unit);
   const int T_len = sp.len;
   const int nchunks = (T_len + C - 1) / C;
@@ -910,6 +911,12 @@ static int launch_act(const GsaLaunch& a) {
     vs.H = a.H;
     vs.total = a.cu_seqlens[a.n_seqs];
     for (int i = 0; i <= a.n_seqs; i++) vs.cu[i] = a.cu_seqlens[i];
+    // longest first (stable: equal lengths keep their order, so equal-length
+    // batches launch exactly like the dense one)
+    for (int i = 0; i < a.n_seqs; i++) vs.order[i] = i;
+    std::stable_sort(vs.order, vs.order + a.n_seqs, [&](int x, int y) {
+      return vs.cu[x + 1] - vs.cu[x] > vs.cu[y + 1] - vs.cu[y];
+    });
     return launch<DK, DV, M, kActSoftmax, VarSeqs>(a, vs);
   }
   const DenseSeqs ds{a.T};
