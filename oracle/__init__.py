@@ -54,9 +54,10 @@ def _load():
         lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
         lib.oracle_gsa_decode_step.argtypes = [P] * 7 + [L] * 5 + [D, I]
         lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
+        lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
         lib.oracle_gsa_decode_step_nl.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
         for f in (lib.oracle_gsa_fwd, lib.oracle_gla_fwd, lib.oracle_gsa_decode_step,
-                  lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl):
+                  lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl, lib.oracle_gla_fwd_gm):
             f.restype = I
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -118,16 +119,21 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, want_states=True,
     return dict(o=o, kf=kf, vf=vf, s=s, z=z)
 
 
-def gla_fwd(q, k, v, g, s0=None, tau=16.0, want_state=True, nthreads=1):
-    """Recurrent GLA forward.  q,k,g [B,H,T,dk]; v [B,H,T,dv]; s0 [B,H,dk,dv]."""
+GATE_INPUTS = {"logit": 0, "log_decay": 1}
+
+
+def gla_fwd(q, k, v, g, s0=None, tau=16.0, want_state=True, nthreads=1, gate="logit"):
+    """Recurrent GLA forward.  q,k,g [B,H,T,dk]; v [B,H,T,dv]; s0 [B,H,dk,dv].
+    gate: "logit" (alpha = sigmoid(g)^(1/tau)) or "log_decay" (alpha =
+    exp(min(g, 0)), tau unused)."""
     q, k, v, g, s0 = map(_f64, (q, k, v, g, s0))
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     assert k.shape == q.shape and g.shape == q.shape and v.shape[:3] == (B, H, T)
     o = np.empty((B, H, T, dv))
     sf = np.empty((B, H, dk, dv)) if want_state else None
-    rc = _load().oracle_gla_fwd(_p(q), _p(k), _p(v), _p(g), _p(s0), _p(o), _p(sf),
-                                B, H, T, dk, dv, float(tau), int(nthreads))
+    rc = _load().oracle_gla_fwd_gm(_p(q), _p(k), _p(v), _p(g), _p(s0), _p(o), _p(sf),
+                                   B, H, T, dk, dv, float(tau), GATE_INPUTS[gate], int(nthreads))
     if rc:
         raise RuntimeError("oracle_gla_fwd failed (%d)" % rc)
     return dict(o=o, sf=sf)

@@ -27,7 +27,11 @@
  *     f(z[c]): 1 = none (f(z) = z), 2 = Swish (z * sigmoid(z)), 3 = ReLU
  *     (max(z, 0)), 4 = ReLU^2 (max(z, 0)^2); 0 is the softmax.
  *   - GLA (Sec. 2.3, with beta = 1): S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T,
- *     o_t = S_t^T q_t, alpha_t per key dimension.
+ *     o_t = S_t^T q_t, alpha_t per key dimension.  The gate is given either as
+ *     logits (alpha = sigmoid(g)^(1/tau), gate_mode 0) or as per-token
+ *     log-decays (alpha = exp(min(g, 0)), gate_mode 1): a gate vector computed
+ *     elsewhere, such as the rank-one gate of Lattice's simplified chunk
+ *     recurrence.
  *
  * All arithmetic is fp64.  log sigmoid uses the textbook stable split
  * min(x,0) - log1p(exp(-|x|)); 1 - alpha is formed as -expm1(log alpha) so
@@ -179,15 +183,15 @@ int oracle_gsa_fwd(const double *q, const double *k, const double *v,
 }
 
 /* GLA forward (Sec. 2.3, beta = 1): per key dimension decay, S in R^{dk x dv}. */
-int oracle_gla_fwd(const double *q, const double *k, const double *v,
-                   const double *g, const double *s0, double *o, double *sf,
-                   long B, long H, long T, long dk, long dv, double tau,
-                   int nthreads)
+int oracle_gla_fwd_gm(const double *q, const double *k, const double *v,
+                      const double *g, const double *s0, double *o, double *sf,
+                      long B, long H, long T, long dk, long dv, double tau,
+                      int gate_mode, int nthreads)
 {
     long units = B * H, u;
     int err = 0;
     if (!q || !k || !v || !g || !o || B < 0 || H < 0 || T < 0 || dk < 1 ||
-        dv < 1 || !(tau > 0.0))
+        dv < 1 || !(tau > 0.0) || gate_mode < 0 || gate_mode > 1)
         return 1;
 #ifdef _OPENMP
     if (nthreads < 1)
@@ -209,7 +213,8 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
             const double *vt = v + row * dv, *gt = g + row * dk;
             double *ot = o + row * dv;
             for (x = 0; x < dk; x++) {
-                double a = exp(log_sigmoid(gt[x]) / tau);
+                double a = gate_mode == 0 ? exp(log_sigmoid(gt[x]) / tau)
+                                          : exp(gt[x] < 0.0 ? gt[x] : 0.0);
                 double *Sx = S + x * dv;
                 for (y = 0; y < dv; y++)
                     Sx[y] = a * Sx[y] + kt[x] * vt[y];
@@ -226,6 +231,15 @@ int oracle_gla_fwd(const double *q, const double *k, const double *v,
         free(S);
     }
     return err;
+}
+
+int oracle_gla_fwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *s0, double *o, double *sf,
+                   long B, long H, long T, long dk, long dv, double tau,
+                   int nthreads)
+{
+    return oracle_gla_fwd_gm(q, k, v, g, s0, o, sf, B, H, T, dk, dv, tau, 0,
+                             nthreads);
 }
 
 /*

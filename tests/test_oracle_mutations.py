@@ -29,8 +29,12 @@ MUTATIONS = [
     ("softmax_unnormalised", "s[c] /= sum;", "s[c] /= 1.0;"),
     ("output_transposed", "acc += V[c * dv + x] * s[c];", "acc += V[x * dv + c] * s[c];"),
     ("value_decay_skipped", "Vc[x] = a * Vc[x] + w * vt[x];", "Vc[x] = Vc[x] + w * vt[x];"),
-    ("gla_scalar_gate", "double a = exp(log_sigmoid(gt[x]) / tau);",
-     "double a = exp(log_sigmoid(gt[0]) / tau);"),
+    ("gla_scalar_gate", "double a = gate_mode == 0 ? exp(log_sigmoid(gt[x]) / tau)",
+     "double a = gate_mode == 0 ? exp(log_sigmoid(gt[0]) / tau)"),
+    # GLA gate given as log-decays
+    ("gla_logdecay_sign", "exp(gt[x] < 0.0 ? gt[x] : 0.0)", "exp(gt[x] < 0.0 ? -gt[x] : 0.0)"),
+    ("gla_logdecay_unclamped", "exp(gt[x] < 0.0 ? gt[x] : 0.0)", "exp(gt[x])"),
+    ("gla_logdecay_as_logit", ": exp(gt[x] < 0.0 ? gt[x] : 0.0);", ": exp(log_sigmoid(gt[x]) / tau);"),
     ("gla_read_before_write", "Sx[y] = a * Sx[y] + kt[x] * vt[y];",
      "Sx[y] = a * Sx[y] + kt[x] * vt[y] * (t > 0);"),
     # slot read non-linearities of the ablation study (Table 2)
@@ -53,6 +57,7 @@ def _build(tmp_path, text, name):
     lib.oracle_gsa_fwd.argtypes = [P] * 11 + [L] * 6 + [D, I]
     lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
     lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
+    lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
     return lib
 
 
@@ -121,6 +126,18 @@ def _pins_pass(lib):
     ok &= _rel(og, ogc) < 1e-12 and _rel(sfg, sfgc) < 1e-12
     ola, _ = _gla(lib, q, k, v, np.full_like(gg, np.inf))
     ok &= _rel(ola[0, 0], np.tril(q[0, 0] @ k[0, 0].T) @ v[0, 0]) < 1e-12
+    # GLA with log-decays given directly (a few positive entries, taken as 0),
+    # against the numpy chunk form, which takes log-decays as they are
+    la = -np.abs(r.standard_normal((1, 1, T, d))) * 0.3
+    la[0, 0, 3, 1] = 0.2
+    la[0, 0, 9, :2] = -np.inf
+    ol = np.empty((1, 1, T, d))
+    sl = np.empty((1, 1, d, d))
+    assert lib.oracle_gla_fwd_gm(_p(q), _p(k), _p(v), _p(la), _p(s0), _p(ol), _p(sl), 1, 1, T, d, d,
+                                 16.0, 1, 1) == 0
+    olc, slc = chunkwise.gla_key_decay(q[0, 0], k[0, 0], v[0, 0], np.minimum(la[0, 0], 0.0),
+                                       s0[0, 0], C=8)
+    ok &= _rel(ol[0, 0], olc) < 1e-12 and _rel(sl[0, 0], slc) < 1e-12
     # the element-wise slot reads against the numpy chunk form
     for act, name in ((1, "identity"), (2, "swish"), (3, "relu"), (4, "relu2")):
         on, _, _ = _gsa(lib, q, k, v, g, k0, v0, act=act)
