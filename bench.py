@@ -202,10 +202,11 @@ def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True, nonl
     return res
 
 
-def bench_gla(torch, gsa, ev, w, steps, warmup):
+def bench_gla(torch, gsa, ev, w, steps, warmup, name="gla_bf16_T4096"):
     import synth
+    gate = "log_decay" if w.get("log_decay_scale") else "logit"
     inp = synth.gla_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], dtype=w["dtype"], seed=0,
-                           qkv_scale=w["qkv_scale"])
+                           qkv_scale=w["qkv_scale"], log_decay_scale=w.get("log_decay_scale"))
     sets = dev_sets(torch, inp, ["q", "k", "v", "g"], 2)
     B, H, T, dk, dv = w["B"], w["H"], w["T"], w["dk"], w["dv"]
     outs = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
@@ -215,7 +216,7 @@ def bench_gla(torch, gsa, ev, w, steps, warmup):
     def call(s, events):
         i = next(j for j, x in enumerate(sets) if x is s)
         gsa.gla_fwd(s["q"], s["k"], s["v"], s["g"], tau=w["tau"], out=outs[i], workspace=ws,
-                    events=events)
+                    events=events, gate=gate)
 
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     flops, nbytes = gla_alg(B, H, T, dk, dv, w["C"], 2)
@@ -227,7 +228,7 @@ def bench_gla(torch, gsa, ev, w, steps, warmup):
                           "op": round(t_op, 4)},
             "alg_tflops": round(flops / (t_op * 1e-3) / 1e12, 2),
             "mfma_frac_alg": round(flops / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline(nbytes, t_out, "gla_bf16_out", "gla_bf16_T4096")}
+            "roofline": roofline(nbytes, t_out, "gla_bf16_out", name)}
 
 
 def bench_decode(torch, gsa, ev, w, steps, warmup):
@@ -391,6 +392,9 @@ def run_only(args, torch, gsa, ev):
         return bench_ablations(torch, gsa, ev, args.steps, args.warmup, args.sets)
     if args.only == "gla":
         return bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"], args.steps, args.warmup)
+    if args.only == "gla_log_decay":
+        return bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096_log_decay"], args.steps,
+                         args.warmup, "gla_bf16_T4096_log_decay")
     return bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"], args.steps, args.warmup)
 
 
@@ -403,7 +407,7 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["gsa", "long", "gla", "decode", "copy", "ablations", "serve"], default=None,
+    ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -445,6 +449,10 @@ def main():
         comps["gla_bf16_T4096"] = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"],
                                             args.steps, args.warmup)
         log("bench: gla done")
+        comps["gla_bf16_T4096_log_decay"] = bench_gla(
+            torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096_log_decay"], max(1, args.steps // 2),
+            args.warmup, "gla_bf16_T4096_log_decay")
+        log("bench: gla with log-decay gates done")
         comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
                                                 args.steps, args.warmup)
         log("bench: decode done")

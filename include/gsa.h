@@ -176,6 +176,28 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
                    int dtype, void* workspace, size_t workspace_bytes, int chunks_per_segment,
                    void* stream, void* const* events);
 
+/* How gla_fwd_ex reads its gate tensor g [B,H,T,dk]. */
+typedef enum {
+  GSA_GATE_LOGIT = 0,     /* logits: alpha = sigmoid(g)^(1/tau), as gla_fwd (Sec. 2.3, 3.3) */
+  GSA_GATE_LOG_DECAY = 1  /* per-token log-decays given directly: alpha = exp(min(g, 0));
+                             tau is not read.  A per-token vector gate over the key
+                             dimension computed elsewhere, e.g. the rank-one gate
+                             1 gamma_t^T of Lattice's simplified chunk recurrence with
+                             g = log gamma_t */
+} gsa_gate_input;
+
+/*
+ * gla_fwd with the gate input chosen by the caller (a gsa_gate_input code,
+ * else GSA_ERR_SHAPE) and the timing hooks of gla_fwd_events; gla_fwd and
+ * gla_fwd_events are this with GSA_GATE_LOGIT.  Everything else as gla_fwd.
+ * With GSA_GATE_LOG_DECAY, g = -inf is alpha = 0 exactly and positive values
+ * are taken as 0 (alpha <= 1).
+ */
+int gla_fwd_ex(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
+               float* s_final, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
+               void* workspace, size_t workspace_bytes, int chunks_per_segment, int gate_input,
+               void* stream, void* const* events);
+
 /*
  * gsa_fwd with the slot read non-linearity chosen by the caller (a
  * gsa_slot_nonlinearity code; any other value returns GSA_ERR_SHAPE) and the

@@ -26,6 +26,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # gsa_slot_nonlinearity codes: the softmax read of GSA and the element-wise
 # ablations (none, Swish, ReLU, ReLU^2)
 NONLINEARITIES = {"softmax": 0, "identity": 1, "swish": 2, "relu": 3, "relu2": 4}
+# gsa_gate_input codes of gla_fwd_ex: logits, or per-token log-decays given directly
+GATE_INPUTS = {"logit": 0, "log_decay": 1}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libgsa.so is not built (run __graft_entry__.build() or "
@@ -58,6 +60,8 @@ lib.gsa_decode_step_events.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _P, _P]
 lib.gsa_fwd_ex.restype = _I
 lib.gsa_fwd_ex.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_decode_step_ex.restype = _I
+lib.gla_fwd_ex.restype = _I
+lib.gla_fwd_ex.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_fwd_varlen.restype = _I
 lib.gsa_fwd_varlen.argtypes = [_P] * 5 + [_I, _I] + [_P] * 5 + [_I] * 4 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_fwd_varlen_workspace_bytes.restype = _S
@@ -250,9 +254,11 @@ def gsa_fwd_varlen(q, k, v, g, cu_seqlens, k0=None, v0=None, *, tau=8.0, C=64,
 
 def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
             chunks_per_segment=0, out=None, s_final=None, workspace=None, stream=None,
-            events=None):
+            events=None, gate="logit"):
     """Chunkwise GLA forward.  q, k, g [B,H,T,dk]; v [B,H,T,dv]; optional float32
-    initial state s0 [B,H,dk,dv].  Returns (o, s_final or None)."""
+    initial state s0 [B,H,dk,dv].  gate: "logit" (alpha = sigmoid(g)^(1/tau))
+    or "log_decay" (g holds log alpha per token and key dimension; tau unused).
+    Returns (o, s_final or None)."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
         _check(t, n, q.dtype)
@@ -267,10 +273,12 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
     nbytes = gla_fwd_workspace_bytes(B, H, T, dk, dv, C, dt, chunks_per_segment)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.gla_fwd_events(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out),
-                            _ptr(s_final), B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
-                            0 if workspace is None else workspace.numel(), int(chunks_per_segment),
-                            _stream(stream), _events(events))
+    if gate not in GATE_INPUTS:
+        raise ValueError("gate must be one of %s" % ", ".join(GATE_INPUTS))
+    st = lib.gla_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out),
+                        _ptr(s_final), B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
+                        0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                        GATE_INPUTS[gate], _stream(stream), _events(events))
     if st:
         raise GsaError("gla_fwd", st)
     return out, s_final

@@ -280,16 +280,27 @@ int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
 int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
             float* sf, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
             void* workspace, size_t workspace_bytes, int cps, void* stream) {
-  return gla_fwd_events(q, k, v, g, s0, o, sf, B, H, T, dk, dv, C, tau, dtype, workspace,
-                        workspace_bytes, cps, stream, nullptr);
+  return gla_fwd_ex(q, k, v, g, s0, o, sf, B, H, T, dk, dv, C, tau, dtype, workspace,
+                    workspace_bytes, cps, GSA_GATE_LOGIT, stream, nullptr);
 }
 
 int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, const float* s0,
                    void* o, float* sf, int B, int H, int T, int dk, int dv, int C, float tau,
                    int dtype, void* workspace, size_t workspace_bytes, int cps, void* stream,
                    void* const* events) {
+  return gla_fwd_ex(q, k, v, g, s0, o, sf, B, H, T, dk, dv, C, tau, dtype, workspace,
+                    workspace_bytes, cps, GSA_GATE_LOGIT, stream, events);
+}
+
+int gla_fwd_ex(const void* q, const void* k, const void* v, const void* g, const float* s0, void* o,
+               float* sf, int B, int H, int T, int dk, int dv, int C, float tau, int dtype,
+               void* workspace, size_t workspace_bytes, int cps, int gate_input, void* stream,
+               void* const* events) {
+  // tau only scales logits; with log-decays it is not read (any value)
+  if (gate_input == GSA_GATE_LOG_DECAY) tau = 1.f;
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || C < 1 || !(tau > 0.f) ||
-      !std::isfinite(tau) || !dtype_ok(dtype))
+      !std::isfinite(tau) || !dtype_ok(dtype) ||
+      (gate_input != GSA_GATE_LOGIT && gate_input != GSA_GATE_LOG_DECAY))
     return GSA_ERR_SHAPE;
   if (!gla_fwd_supported(dk, dv, C, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
@@ -329,7 +340,8 @@ int gla_fwd_events(const void* q, const void* k, const void* v, const void* g, c
   a.ws_dec = workspace ? (float*)((char*)workspace +
                                   (((size_t)units * NQ * dk * dv * 4 + 255) & ~(size_t)255))
                        : nullptr;
-  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.state_split = R; a.tau = tau; a.stream = stream;
+  a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.state_split = R; a.tau = tau;
+  a.gate_mode = gate_input; a.stream = stream;
   a.events = events;
   (void)hipGetLastError();
   if (gsa::gla_dispatch(dtype, dk, dv, &a, false) != 0) return GSA_ERR_UNSUPPORTED;

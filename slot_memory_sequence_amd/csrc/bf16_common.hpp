@@ -215,6 +215,19 @@ __device__ __forceinline__ float gate_log2_or_identity(float g, bool valid, floa
   return gate_log2(valid ? g : 1e30f, inv_tau);
 }
 
+// The same for either gate input (GateMode): a logit as above, or a natural
+// log-decay taken as given (clamped to [-115 ln 2, 0], so alpha <= 1 and
+// -inf is finite); 0 for a row past the end.
+template <int GM>
+__device__ __forceinline__ float gate_log2_mode(float g, bool valid, float inv_tau) {
+  if constexpr (GM == kGateLogit) {
+    return gate_log2_or_identity(g, valid, inv_tau);
+  } else {
+    const float l2 = fmaxf(fminf(g, 0.f) * 1.4426950408889634f, -115.f);
+    return valid ? l2 : 0.f;
+  }
+}
+
 // SPT consecutive bf16 of an LDS row -> floats (p 16-byte aligned when SPT is
 // a multiple of 8, else 4-byte aligned)
 template <int SPT>

@@ -135,6 +135,13 @@ __device__ __forceinline__ float sum32(float x) {
 // whole-chunk decay product must stay >= e^-40 so that 1/prod stays <= e^40.
 constexpr float kFastMinDecay = 4.248354255291589e-18f;  // e^-40
 
+// ------------------------------------------------------------ gate input
+// How the GLA forward's gate tensor is given: as logits, alpha =
+// sigmoid(g)^(1/tau) (Sec. 2.3 / 3.3), or directly as per-token log-decays,
+// log alpha = min(g, 0) (a gate vector computed elsewhere).  The values match
+// the GSA_GATE_* codes of the C ABI.
+enum GateMode : int { kGateLogit = 0, kGateLogDecay = 1 };
+
 // ------------------------------------------------- slot read non-linearity
 // What turns the pass-1 slot scores o'_t into the pass-2 read weights s_t: the
 // softmax over the m slots (Sec. 3.2), or one of the element-wise functions

@@ -99,13 +99,15 @@ struct GRow {
   __device__ __forceinline__ float at(int s) const { return Elem<T>::to_f(reinterpret_cast<const T*>(r)[s]); }
 };
 
-template <int DPT>
+template <int DPT, int GM>
 struct GlaGates {
   float a[DPT], E[DPT], Sx[DPT];
   __device__ __forceinline__ void compute(const float* g, bool valid, float inv_tau, int lane) {
 #pragma unroll
     for (int s = 0; s < DPT; s++) {
-      a[s] = valid ? gate_alpha(g[s], inv_tau) : 1.f;
+      // a logit (alpha = sigmoid(g)^(1/tau)) or a log-decay given directly
+      const float al = GM == kGateLogit ? gate_alpha(g[s], inv_tau) : __expf(fminf(g[s], 0.f));
+      a[s] = valid ? al : 1.f;
       E[s] = a[s];
       Sx[s] = a[s];
     }
@@ -128,7 +130,7 @@ struct GlaGates {
 };
 
 // ------------------------------------------------------ phase A: state map
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int GM>
 __global__ void __launch_bounds__(gNT, 1)
 gla_seg_state(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ gg,
               float* __restrict__ ws_state, float* __restrict__ ws_dec, int T_len, int S, int P,
@@ -173,7 +175,7 @@ gla_seg_state(const T* __restrict__ kk, const T* __restrict__ vv, const T* __res
     float gv[DPT];
 #pragma unroll
     for (int s = 0; s < DPT; s++) gv[s] = pg.at(s);
-    GlaGates<DPT> gt;
+    GlaGates<DPT, GM> gt;
     gt.compute(gv, lane < rv, inv_tau, lane);
 #pragma unroll
     for (int s = 0; s < DPT; s++) {
@@ -244,7 +246,7 @@ gla_seg_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
 }
 
 // ---------------------------------------------------- phase C: outputs
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int GM>
 __global__ void __launch_bounds__(gNT, 1)
 gla_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
             const T* __restrict__ gg, const float* __restrict__ s0, const float* __restrict__ ws_state,
@@ -332,7 +334,7 @@ gla_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
     float gv[DPT];
 #pragma unroll
     for (int s = 0; s < DPT; s++) gv[s] = pg.at(s);
-    GlaGates<DPT> gt;
+    GlaGates<DPT, GM> gt;
     gt.compute(gv, lane < rv, inv_tau, lane);
     bool small = false;
 #pragma unroll
@@ -474,7 +476,7 @@ gla_seg_out(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restr
   }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int GM>
 static int launch_gla(const GlaLaunch& a) {
   using LO = GlaLds<T, DK, DV>;
   using LS = GlaStateLds<T, DK, DV>;
@@ -485,7 +487,7 @@ static int launch_gla(const GlaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   if (P > 1) {
-    launch_timed(gla_seg_state<T, DK, DV>, dim3(P - 1, units), dim3(gNT), LS::total, a.stream, a.events,
+    launch_timed(gla_seg_state<T, DK, DV, GM>, dim3(P - 1, units), dim3(gNT), LS::total, a.stream, a.events,
                  0, 1, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.ws_state, a.ws_dec, a.T, S, P,
                  inv_tau);
     const long long ne = (long long)units * DK * DV;
@@ -495,7 +497,7 @@ static int launch_gla(const GlaLaunch& a) {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gla_seg_out<T, DK, DV>, dim3(P, units), dim3(gNT), LO::total, a.stream, a.events, 2, 3,
+  launch_timed(gla_seg_out<T, DK, DV, GM>, dim3(P, units), dim3(gNT), LO::total, a.stream, a.events, 2, 3,
                (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.s0,
                (const float*)a.ws_state, (T*)a.o, a.sf, a.T, S, P, inv_tau);
   return 0;
@@ -504,15 +506,21 @@ static int launch_gla(const GlaLaunch& a) {
 template <typename T, int DK, int DV>
 constexpr bool gla_fits() { return GlaLds<T, DK, DV>::total <= kLdsBytes; }
 
+template <typename T, int DK, int DV, int GM>
+static int launch_gla_mode(const GlaLaunch& a) {
+  (void)hipFuncSetAttribute((const void*)gla_seg_out<T, DK, DV, GM>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GlaLds<T, DK, DV>::total);
+  (void)hipFuncSetAttribute((const void*)gla_seg_state<T, DK, DV, GM>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GlaStateLds<T, DK, DV>::total);
+  return launch_gla<T, DK, DV, GM>(a);
+}
+
 #define GLA_CASE(TT, DTC, DKC, DVC)                                                       \
   if (dt == DTC && dk == DKC && dv == DVC) {                                            \
     if constexpr (gla_fits<TT, DKC, DVC>()) {                                            \
       if (query) return GlaLds<TT, DKC, DVC>::total;                                     \
-      hipFuncSetAttribute((const void*)gla_seg_out<TT, DKC, DVC>,                        \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, GlaLds<TT, DKC, DVC>::total); \
-      hipFuncSetAttribute((const void*)gla_seg_state<TT, DKC, DVC>,                      \
-                          hipFuncAttributeMaxDynamicSharedMemorySize, GlaStateLds<TT, DKC, DVC>::total); \
-      return launch_gla<TT, DKC, DVC>(*a);                                               \
+      return a->gate_mode == kGateLogit ? launch_gla_mode<TT, DKC, DVC, kGateLogit>(*a)  \
+                                        : launch_gla_mode<TT, DKC, DVC, kGateLogDecay>(*a); \
     }                                                                                    \
     return -1;                                                                           \
   }

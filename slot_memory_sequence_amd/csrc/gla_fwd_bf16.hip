@@ -215,7 +215,7 @@ struct GlaTiles {
 // (0 on rows >= rv), written over q and k, and E_C = exp2(G_C).  Returns
 // whether any of these dimensions decays below the range of the factorised
 // form in this chunk.
-template <int SPT, int LDQ>
+template <int SPT, int LDQ, int GM>
 __device__ __forceinline__ bool out_factors(bf16_t* sQ, bf16_t* sK, const bf16_t* sG, int rv,
                                             float inv_tau, int lane, int d0, float* sEc) {
   const bool valid = lane < rv;
@@ -224,7 +224,7 @@ __device__ __forceinline__ bool out_factors(bf16_t* sQ, bf16_t* sK, const bf16_t
   lds_row<SPT>(sK + lane * LDQ + d0, k);
   lds_row<SPT>(sG + lane * LDQ + d0, G);
 #pragma unroll
-  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(G[s], valid, inv_tau);
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_mode<GM>(G[s], valid, inv_tau);
   wave_prefix_sums<SPT>(G);
   bool small = false;
   float ec[SPT];
@@ -245,14 +245,14 @@ __device__ __forceinline__ bool out_factors(bf16_t* sQ, bf16_t* sK, const bf16_t
 
 // State-map form (any decay): Kh = k exp2(G_C - G) (0 on rows >= rv) and
 // E_C = exp2(G_C), which also multiplies into the running decay product.
-template <int SPT, int LDQ>
+template <int SPT, int LDQ, int GM>
 __device__ __forceinline__ void map_factors(const GateRow<SPT>& k, const GateRow<SPT>& g, int rv,
                                             float inv_tau, int lane, int d0, bf16_t* sKh, float* sEc,
                                             float (&dec)[SPT], bool count) {
   const bool valid = lane < rv;
   float G[SPT];
 #pragma unroll
-  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_mode<GM>(g.at(s), valid, inv_tau);
   wave_prefix_sums<SPT>(G);
   float kh[SPT], ec[SPT];
 #pragma unroll
@@ -329,7 +329,7 @@ __device__ __forceinline__ void gla_pass_chunk(int lane, const bf16_t* sQt, cons
 // state: thread t owns key dimension t / TPD and DV / TPD of its value columns.
 // The state waves' accumulators go through LDS to and from that layout.
 // Contains workgroup barriers: all threads call it.
-template <int DK, int DV>
+template <int DK, int DV, int GM>
 __device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, unsigned char* region,
                                                 const bf16_t* sV, const bf16_t* __restrict__ qc,
                                                 const bf16_t* __restrict__ kc,
@@ -370,7 +370,8 @@ __device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, 
   __syncthreads();
   for (int jt = 0; jt < rv; jt++) {
     const float x = bf2f(sGr[jt * DK + d]);
-    const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
+    const float la = GM == kGateLogit ? (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau
+                                      : fminf(x, 0.f);
     const float a = __expf(la);
     const float kd = bf2f(sKr[jt * DK + d]), qd = bf2f(sQr[jt * DK + d]);
     float op[CPT];
@@ -410,7 +411,7 @@ __device__ __forceinline__ void gla_exact_chunk(GlaTiles<DK, DV, 4>& W, int rv, 
 // grid (Q, units) with Q = (P-1) R: map i covers sub-segment i % R of output
 // segment i / R, from a zero start: S^T Diag(E_C) + V^T Kh per chunk, and the
 // product of the chunk decays.  All eight waves carry state tiles.
-template <int DK, int DV>
+template <int DK, int DV, int GM>
 __global__ void __launch_bounds__(NT, 2)
 gla_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
                const bf16_t* __restrict__ gg, float* __restrict__ ws_state,
@@ -460,7 +461,7 @@ gla_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
   auto stage_chunk = [&](int ch, int b, bool count, int tid_, int lane_) {
     const int rv = min(C, T_len - ch * C);
     pv.store_branchy(bV(b), Lds::LDV, rv, tid_);
-    map_factors<SPT, Lds::LDQ>(rk, rg, rv, inv_tau, lane_, d0, bK(b), bEc(b), dec, count);
+    map_factors<SPT, Lds::LDQ, GM>(rk, rg, rv, inv_tau, lane_, d0, bK(b), bEc(b), dec, count);
   };
 
   load_chunk(c_begin, tid, lane);
@@ -531,7 +532,7 @@ gla_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec, co
 // g rows (loaded one chunk earlier as coalesced tiles) into set b; the loads
 // of chunks c+3 and c+2; the pass waves' share of chunk c+1's factors (from
 // set b^1); a barrier that also combines the exact-path votes.
-template <int DK, int DV>
+template <int DK, int DV, int GM>
 __global__ void __launch_bounds__(NT, 1)
 gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const bf16_t* __restrict__ vv, const bf16_t* __restrict__ gg,
@@ -586,7 +587,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   };
   auto stage_v = [&](int ch, int tid_) { pv.store(sV, Lds::LDV, rows_of(ch), tid_); };
   auto factors = [&](int ch, int b, int lane_) -> bool {
-    return out_factors<SPT, Lds::LDQ>(fQ(b), fK(b), fG(b), rows_of(ch), inv_tau, lane_, d0, fEc(b));
+    return out_factors<SPT, Lds::LDQ, GM>(fQ(b), fK(b), fG(b), rows_of(ch), inv_tau, lane_, d0, fEc(b));
   };
 
   ST W;
@@ -647,7 +648,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
         W.template carry<true>(sV, Lds::LDV, fK(b), Lds::LDQ, fEc(b), sw, lane_i);
       }
     } else {
-      gla_exact_chunk<DK, DV>(W, rv, smem + Lds::oX(b), sV, qb + (size_t)t0 * DK,
+      gla_exact_chunk<DK, DV, GM>(W, rv, smem + Lds::oX(b), sV, qb + (size_t)t0 * DK,
                               kb + (size_t)t0 * DK, gb + (size_t)t0 * DK, ob + (size_t)t0 * DV, tid_i,
                               inv_tau);
     }
@@ -674,7 +675,7 @@ gla_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
 }
 
 // ------------------------------------------------------------ launcher
-template <int DK, int DV>
+template <int DK, int DV, int GM>
 static int launch_gla(const GlaLaunch& a) {
   using LO = GlaOutLds<DK, DV>;
   using LS = GlaStateLds<DK, DV>;
@@ -688,9 +689,9 @@ static int launch_gla(const GlaLaunch& a) {
   const float inv_tau = 1.0f / a.tau;
   hipStream_t st = (hipStream_t)a.stream;
   static const bool lds_set = [] {  // once per instantiation and process
-    (void)hipFuncSetAttribute((const void*)gla_bf16_out<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)gla_bf16_out<DK, DV, GM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         LO::total);
-    (void)hipFuncSetAttribute((const void*)gla_bf16_state<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)gla_bf16_state<DK, DV, GM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         LS::total);
     return true;
   }();
@@ -700,7 +701,7 @@ static int launch_gla(const GlaLaunch& a) {
   // launch), unless the final state is written over s0.
   const int fold = P > 1 && Q <= kMaxFoldedMaps && !(a.sf && a.sf == a.s0);
   if (P > 1) {
-    launch_timed(gla_bf16_state<DK, DV>, dim3(Q, units), dim3(NT), LS::total, a.stream, a.events, 0, 1,
+    launch_timed(gla_bf16_state<DK, DV, GM>, dim3(Q, units), dim3(NT), LS::total, a.stream, a.events, 0, 1,
                  (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g, a.ws_state, a.ws_dec, a.T,
                  S, R, NQ, inv_tau);
     if (!fold) {
@@ -712,7 +713,7 @@ static int launch_gla(const GlaLaunch& a) {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
   }
-  launch_timed(gla_bf16_out<DK, DV>, dim3(P, units), dim3(NT), LO::total, a.stream, a.events, 2, 3,
+  launch_timed(gla_bf16_out<DK, DV, GM>, dim3(P, units), dim3(NT), LO::total, a.stream, a.events, 2, 3,
                (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g, a.s0,
                (const float*)a.ws_state, (bf16_t*)a.o, a.sf, (const float*)a.ws_dec, a.T, S, P, NQ, R,
                fold, inv_tau);
@@ -725,7 +726,8 @@ static int launch_gla(const GlaLaunch& a) {
   if (dk == DKC && dv == DVC) {                                      \
     static_assert(bfk::GlaOutLds<DKC, DVC>::total <= kLdsBytes, "LDS"); \
     if (query) return bfk::GlaOutLds<DKC, DVC>::total;               \
-    return bfk::launch_gla<DKC, DVC>(*a);                            \
+    return a->gate_mode == kGateLogit ? bfk::launch_gla<DKC, DVC, kGateLogit>(*a)           \
+                                      : bfk::launch_gla<DKC, DVC, kGateLogDecay>(*a);       \
   }
 
 // Returns: query -> LDS bytes (>0) or -1 if unsupported; launch -> 0 or -1.

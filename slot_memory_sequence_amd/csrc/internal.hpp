@@ -34,6 +34,7 @@ struct GlaLaunch {
   int B, H, T, chunks_per_seg;
   int state_split;  // bf16: state-map sub-segments per output segment (>= 1)
   float tau;
+  int gate_mode;  // how g is given: a GSA_GATE_* code (GateMode)
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gla_fwd_events
 };

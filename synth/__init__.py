@@ -89,16 +89,19 @@ def gsa_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
 
 
 def gla_inputs(B, H, T, dk, dv, dtype="bf16", seed=0, qkv_scale=None,
-               g_shift=0.0, init_std=None):
+               g_shift=0.0, init_std=None, log_decay_scale=None):
     """q,k ~ N(0,1)*qkv_scale [B,H,T,dk]; v [B,H,T,dv]; g ~ N(0,1)+g_shift
-    [B,H,T,dk] (one logit per key dim); optional S0 [B,H,dk,dv] ~ N(0,init_std)."""
+    [B,H,T,dk] (one logit per key dim); optional S0 [B,H,dk,dv] ~ N(0,init_std).
+    With log_decay_scale, g is instead -|N(0,1)| * log_decay_scale (gates given
+    as log-decays: non-positive, half-normal)."""
     rng = np.random.default_rng(seed)
     if qkv_scale is None:
         qkv_scale = 1.0 / math.sqrt(dk)
     q = _normal(rng, (B, H, T, dk)) * qkv_scale
     k = _normal(rng, (B, H, T, dk)) * qkv_scale
     v = _normal(rng, (B, H, T, dv)) * qkv_scale
-    g = _normal(rng, (B, H, T, dk)) + g_shift
+    g = _normal(rng, (B, H, T, dk))
+    g = -np.abs(g) * log_decay_scale if log_decay_scale is not None else g + g_shift
     out = dict(q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
                g=stored(g, dtype), s0=None)
     if init_std is not None:
@@ -169,6 +172,11 @@ WORKLOADS = {
     "gla_bf16_T4096": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64, tau=16.0,
                            dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                            init_std=None),
+    # the same GLA with the gate given as per-token log-decays, half-normal with
+    # mean -0.048 (the tau = 16 logit gate's mean log-decay is -0.050)
+    "gla_bf16_T4096_log_decay": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64,
+                                     tau=16.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
+                                     g_shift=0.0, init_std=None, log_decay_scale=0.06),
     "gsa_bf16_long_T16384": dict(op="gsa", B=1, H=8, T=16384, dk=128, dv=128, m=64, C=64,
                                  tau=8.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
                                  g_shift=2.0, init_std=0.1),
