@@ -199,11 +199,15 @@ __device__ __forceinline__ float group4_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// log2 alpha = log2(sigmoid(g)) / tau, clamped at -115 (alpha ~ 2.4e-35) so that
-// g = -inf gives a finite value.
+// log2 alpha = log2(sigmoid(g)) / tau = -log2(1 + 2^-t) / tau with t = g / ln 2,
+// clamped at -115 (alpha ~ 2.4e-35) so that g = -inf gives a finite value.
+// For t << 0, 2^-t overflows to inf and the clamp applies; for t >> 0 the sum
+// rounds to 1 and the result is 0, which is what the split form
+// min(t, 0) - log2(1 + 2^-|t|) also gives in fp32 (1 + 2^-|t| rounds the
+// same way), at three VALU operations more per gate.
 __device__ __forceinline__ float gate_log2(float g, float inv_tau) {
   const float t = g * 1.4426950408889634f;  // g / ln 2
-  const float ls2 = fminf(t, 0.f) - __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(t)));
+  const float ls2 = -__builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-t));
   return fmaxf(ls2 * inv_tau, -115.f);
 }
 
