@@ -102,3 +102,19 @@ def test_gla_worked_example():
     for T in (1, 2):
         rt = oracle.gla_fwd(q[:, :, :T], k[:, :, :T], v[:, :, :T], g[:, :, :T], tau=ex["tau"])
         _close(rt["sf"][0, 0], _arr(ex["S_after"])[T - 1])
+
+
+@pytest.mark.parametrize("nl", ["identity", "relu", "relu2", "swish"])
+def test_gsa_worked_example_read_ablations(nl):
+    """The oracle's element-wise reads against the hand-derived outputs (the
+    exact rationals for none / ReLU / ReLU^2, Swish formed from the stated
+    scores and states)."""
+    ex, q, k, v, g = _gsa_inputs()
+    ref = oracle.gsa_fwd(q, k, v, g, tau=ex["tau"], want_scores=True, nonlinearity=nl)
+    if nl == "swish":
+        z, V = _arr(ex["z"]), _arr(ex["V_after"])
+        expect = np.stack([(z[t] / (1.0 + np.exp(-z[t]))) @ V[t] for t in range(3)])
+    else:
+        expect = _arr(ex["o_" + nl])
+    _close(ref["o"][0, 0], expect)
+    _close(ref["z"][0, 0], _arr(ex["z"]))
