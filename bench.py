@@ -279,9 +279,24 @@ def cpu_baseline(w, inp, budget_s):
             break
     dt = time.perf_counter() - t0
     tokens = w["B"] * w["T"] * runs
+    # one thread on one (batch, head) unit of the same batch, scaled to the
+    # batch's tokens/s (every unit costs the same)
+    one = [a[:1, :1].copy() for a in args]
+    t1 = time.perf_counter()
+    runs1 = 0
+    while True:
+        oracle.gsa_fwd(*one, tau=w["tau"], want_states=False, nthreads=1)
+        runs1 += 1
+        if time.perf_counter() - t1 >= min(2.0, budget_s):
+            break
+    dt1 = time.perf_counter() - t1
+    single = {"value": round(w["T"] * runs1 / dt1 / (w["B"] * w["H"]) * w["B"], 1), "cores": 1,
+              "sample": "one (b,h) unit of the batch (T=%d), %d run(s) in %.1f s, scaled to B*T tokens "
+                        "over B*H units" % (w["T"], runs1, dt1)}
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "full %s batch (B=%d H=%d T=%d), %d run(s) in %.1f s, fp64 recurrence, "
-                      "OpenMP over (b,h) units" % ("training-shape", w["B"], w["H"], w["T"], runs, dt)}, ref
+                      "OpenMP over (b,h) units" % ("training-shape", w["B"], w["H"], w["T"], runs, dt),
+            "single_thread": single}, ref
 
 
 def copy_calibration(torch, ev, steps):
