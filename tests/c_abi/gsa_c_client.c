@@ -1,0 +1,139 @@
+/*
+ * A plain C client of libgsa: no Python, no PyTorch.  It allocates device
+ * buffers with the HIP runtime, calls gsa_fwd (and gsa_decode_step on the
+ * resulting states) through include/gsa.h, and writes the results to a file,
+ * so that a test can compare them with the fp64 oracle on the same inputs.
+ *
+ * Usage: gsa_c_client <in.bin> <out.bin>
+ *   in.bin : int32 B, H, T, dk, dv, m; then float32 q[B,H,T,dk], k[B,H,T,dk],
+ *            v[B,H,T,dv], g[B,H,T,m], and one decode token per unit:
+ *            q1[B,H,dk], k1[B,H,dk], v1[B,H,dv], g1[B,H,m]
+ *   out.bin: float32 o[B,H,T,dv], k_final[B,H,m,dk], v_final[B,H,m,dv],
+ *            o1[B,H,dv], and the states after the decode step.
+ * Exit status 0 on success; any library or runtime error is printed.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/gsa.h"
+
+#define HIP_OK(x)                                                               \
+  do {                                                                          \
+    hipError_t e_ = (x);                                                        \
+    if (e_ != hipSuccess) {                                                     \
+      fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));           \
+      return 2;                                                                 \
+    }                                                                           \
+  } while (0)
+
+static float* read_floats(FILE* f, size_t n) {
+  float* p = (float*)malloc(n * sizeof(float) + 1);
+  if (p && fread(p, sizeof(float), n, f) != n) {
+    free(p);
+    return NULL;
+  }
+  return p;
+}
+
+static int to_device(float** d, const float* h, size_t n) {
+  if (hipMalloc((void**)d, n * sizeof(float) + 16) != hipSuccess) return 1;
+  if (n && hipMemcpy(*d, h, n * sizeof(float), hipMemcpyHostToDevice) != hipSuccess) return 1;
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc != 3) {
+    fprintf(stderr, "usage: %s in.bin out.bin\n", argv[0]);
+    return 1;
+  }
+  FILE* fi = fopen(argv[1], "rb");
+  if (!fi) return 1;
+  int hdr[6];
+  if (fread(hdr, sizeof(int), 6, fi) != 6) return 1;
+  const int B = hdr[0], H = hdr[1], T = hdr[2], dk = hdr[3], dv = hdr[4], m = hdr[5];
+  const size_t U = (size_t)B * H;
+  const size_t nq = U * T * dk, nv = U * T * dv, ng = U * T * m;
+  float* hq = read_floats(fi, nq);
+  float* hk = read_floats(fi, nq);
+  float* hv = read_floats(fi, nv);
+  float* hg = read_floats(fi, ng);
+  float* hq1 = read_floats(fi, U * dk);
+  float* hk1 = read_floats(fi, U * dk);
+  float* hv1 = read_floats(fi, U * dv);
+  float* hg1 = read_floats(fi, U * m);
+  fclose(fi);
+  if (!hq || !hk || !hv || !hg || !hq1 || !hk1 || !hv1 || !hg1) {
+    fprintf(stderr, "short input file\n");
+    return 1;
+  }
+  if (gsa_abi_version() != GSA_ABI_VERSION) {
+    fprintf(stderr, "ABI version mismatch: library %d, header %d\n", gsa_abi_version(),
+            GSA_ABI_VERSION);
+    return 1;
+  }
+  if (!gsa_fwd_supported(dk, dv, m, 64, GSA_DTYPE_F32)) {
+    fprintf(stderr, "shape not compiled\n");
+    return 1;
+  }
+
+  float *q, *k, *v, *g, *o, *kf, *vf, *q1, *k1, *v1, *g1, *o1;
+  if (to_device(&q, hq, nq) || to_device(&k, hk, nq) || to_device(&v, hv, nv) ||
+      to_device(&g, hg, ng) || to_device(&q1, hq1, U * dk) || to_device(&k1, hk1, U * dk) ||
+      to_device(&v1, hv1, U * dv) || to_device(&g1, hg1, U * m)) {
+    fprintf(stderr, "device allocation or copy failed\n");
+    return 2;
+  }
+  HIP_OK(hipMalloc((void**)&o, nv * sizeof(float) + 16));
+  HIP_OK(hipMalloc((void**)&kf, U * m * dk * sizeof(float)));
+  HIP_OK(hipMalloc((void**)&vf, U * m * dv * sizeof(float)));
+  HIP_OK(hipMalloc((void**)&o1, U * dv * sizeof(float)));
+
+  hipStream_t st;
+  HIP_OK(hipStreamCreate(&st));
+  const size_t wsb = gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, 64, GSA_DTYPE_F32, 0);
+  void* ws = NULL;
+  if (wsb == (size_t)-1) return 1;
+  if (wsb) HIP_OK(hipMalloc(&ws, wsb));
+
+  int s = gsa_fwd(q, k, v, g, NULL, NULL, o, kf, vf, B, H, T, dk, dv, m, 64, 8.0f, GSA_DTYPE_F32,
+                  ws, wsb, 0, st);
+  if (s != GSA_OK) {
+    fprintf(stderr, "gsa_fwd: %s\n", gsa_status_string(s));
+    return 3;
+  }
+  /* an error is reported on the host before anything runs */
+  if (gsa_fwd(q, k, v, g, NULL, NULL, o, kf, vf, B, H, T, dk, dv, m, 64, -1.0f, GSA_DTYPE_F32, ws,
+              wsb, 0, st) != GSA_ERR_SHAPE) {
+    fprintf(stderr, "bad tau was not rejected\n");
+    return 3;
+  }
+  HIP_OK(hipStreamSynchronize(st));
+
+  FILE* fo = fopen(argv[2], "wb");
+  if (!fo) return 1;
+  float* buf = (float*)malloc((nv > U * m * (dk + dv) ? nv : U * m * (dk + dv)) * sizeof(float));
+  if (!buf) return 1;
+#define DUMP(dptr, n)                                                            \
+  do {                                                                           \
+    HIP_OK(hipMemcpy(buf, dptr, (n) * sizeof(float), hipMemcpyDeviceToHost));   \
+    if (fwrite(buf, sizeof(float), (n), fo) != (n)) return 1;                    \
+  } while (0)
+  DUMP(o, nv);
+  DUMP(kf, U * m * dk);
+  DUMP(vf, U * m * dv);
+
+  /* one decode step from the final states, in place */
+  s = gsa_decode_step(q1, k1, v1, g1, kf, vf, o1, B, H, dk, dv, m, 8.0f, GSA_DTYPE_F32, st);
+  if (s != GSA_OK) {
+    fprintf(stderr, "gsa_decode_step: %s\n", gsa_status_string(s));
+    return 3;
+  }
+  HIP_OK(hipStreamSynchronize(st));
+  DUMP(o1, U * dv);
+  DUMP(kf, U * m * dk);
+  DUMP(vf, U * m * dv);
+  fclose(fo);
+  printf("gsa_c_client ok: B=%d H=%d T=%d dk=%d dv=%d m=%d workspace=%zu\n", B, H, T, dk, dv, m, wsb);
+  return 0;
+}
