@@ -122,7 +122,9 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
  *               sequence s holds tokens cu_seqlens[s] .. cu_seqlens[s+1] - 1;
  *               total = cu_seqlens[n_seqs].  Read during the call only.
  *               Empty sequences are allowed (their final state is the
- *               initial one, they have no outputs).  n_seqs <= 256.
+ *               initial one, they have no outputs).  Any n_seqs >= 0: the
+ *               library launches groups of up to 256 sequences in turn on
+ *               the stream, so H * min(n_seqs, 256) <= 65535.
  *   q, k     [H, total, dk]  bf16   head-major packed tokens
  *   v        [H, total, dv]  bf16
  *   g        [H, total, m]   bf16   forget-gate logits
@@ -134,6 +136,9 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
  * (GSA_ERR_UNSUPPORTED otherwise); a bad cu_seqlens returns GSA_ERR_SHAPE.
  * Workspace, aliasing, events and errors as for gsa_fwd_events; the workspace
  * size comes from gsa_fwd_varlen_workspace_bytes with the same cu_seqlens.
+ * With more than 256 sequences the timing hooks stamp the whole call: events
+ * [0] and [1] are recorded before the first launch, [2] and [3] after the
+ * last.
  */
 size_t gsa_fwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv,
                                       int m, int C, int dtype, int chunks_per_segment);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "internal.hpp"
@@ -83,7 +84,7 @@ int hip_status() {
 // offsets starting at 0.  Also gives the longest length and the chunk count
 // over all sequences (one head).
 bool varlen_ok(const int* cu, int n, int* tmax, long long* chunks) {
-  if (!cu || n < 0 || n > gsa::kMaxVarSeqs || cu[0] != 0) return false;
+  if (!cu || n < 0 || cu[0] != 0) return false;
   int mx = 0;
   long long ch = 0;
   for (int i = 0; i < n; i++) {
@@ -118,6 +119,8 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
             const int* cu, int dk, int dv, int m, float tau, int dtype, void* workspace,
             size_t workspace_bytes, int nonlinearity, void* stream, void* const* events) {
   const long long units = (long long)B * H;
+  // units of one launch sequence (a packed batch runs in groups of sequences)
+  const long long ws_units = cu ? (long long)std::min(B, gsa::kMaxVarSeqs) * H : units;
   if (ntok > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
   const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace};
   for (const void* p : ptrs)
@@ -139,7 +142,7 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
     return GSA_ERR_ALIAS;
   for (Range in : {rq, rk, rv, rg, rk0, rv0})
     if (overlap(rws, in)) return GSA_ERR_ALIAS;
-  const size_t need = ws_bytes(units, T, c, (size_t)m * (dk + dv), (size_t)m);
+  const size_t need = ws_bytes(ws_units, T, c, (size_t)m * (dk + dv), (size_t)m);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
 
   if (T == 0) {  // nothing to read: the final state is the initial state
@@ -153,7 +156,7 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
   const long long P = (nchunks + c - 1) / c;
   a.ws_state = (float*)workspace;
   a.ws_dec = workspace ? (float*)((char*)workspace +
-                                  (((size_t)units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
+                                  (((size_t)ws_units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
                        : nullptr;
   a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
   a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
@@ -252,9 +255,9 @@ size_t gsa_fwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, 
   if (H < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !dtype_ok(dtype) ||
       !varlen_ok(cu_seqlens, n_seqs, &tmax, &total_chunks))
     return (size_t)-1;
-  const long long units = (long long)n_seqs * H;
-  return ws_bytes(units, tmax, resolve_cps_var(H, tmax, total_chunks, cps), (size_t)m * (dk + dv),
-                  (size_t)m);
+  const long long ws_units = (long long)std::min(n_seqs, gsa::kMaxVarSeqs) * H;
+  return ws_bytes(ws_units, tmax, resolve_cps_var(H, tmax, total_chunks, cps),
+                  (size_t)m * (dk + dv), (size_t)m);
 }
 
 int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -269,7 +272,7 @@ int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
     return GSA_ERR_SHAPE;
   if (dtype != GSA_DTYPE_BF16 || !gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)n_seqs * H;
-  if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  if ((long long)std::min(n_seqs, gsa::kMaxVarSeqs) * H > kMaxUnits) return GSA_ERR_UNSUPPORTED;
   if (units == 0) return GSA_OK;
   return gsa_run(q, k, v, g, k0, v0, o, kf, vf, n_seqs, H, tmax,
                  (size_t)H * (size_t)cu_seqlens[n_seqs], resolve_cps_var(H, tmax, total_chunks, cps),

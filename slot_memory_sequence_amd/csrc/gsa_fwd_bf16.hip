@@ -906,18 +906,50 @@ static int launch(const GsaLaunch& a, const Seq& seq) {
 template <int DK, int DV, int M>
 static int launch_act(const GsaLaunch& a) {
   if (a.cu_seqlens) {  // packed variable-length batch: the softmax read only
-    if (a.act != kActSoftmax || a.n_seqs < 0 || a.n_seqs > kMaxVarSeqs) return -1;
-    VarSeqs vs{};
-    vs.H = a.H;
-    vs.total = a.cu_seqlens[a.n_seqs];
-    for (int i = 0; i <= a.n_seqs; i++) vs.cu[i] = a.cu_seqlens[i];
-    // longest first (stable: equal lengths keep their order, so equal-length
-    // batches launch exactly like the dense one)
-    for (int i = 0; i < a.n_seqs; i++) vs.order[i] = i;
-    std::stable_sort(vs.order, vs.order + a.n_seqs, [&](int x, int y) {
-      return vs.cu[x + 1] - vs.cu[x] > vs.cu[y + 1] - vs.cu[y];
-    });
-    return launch<DK, DV, M, kActSoftmax, VarSeqs>(a, vs);
+    if (a.act != kActSoftmax || a.n_seqs < 0) return -1;
+    // Groups of at most kMaxVarSeqs sequences, one launch sequence each (a
+    // group's offsets travel in the kernel arguments); the groups run one
+    // after the other on the stream and share the workspace.
+    const int groups = (a.n_seqs + kMaxVarSeqs - 1) / kMaxVarSeqs;
+    if (groups > 1) {
+      record_event(a.events, 0, a.stream);
+      record_event(a.events, 1, a.stream);
+    }
+    const size_t MK = (size_t)a.H * M * DK, MV = (size_t)a.H * M * DV;
+    for (int g0 = 0; g0 < a.n_seqs; g0 += kMaxVarSeqs) {
+      const int ng = min(kMaxVarSeqs, a.n_seqs - g0);
+      VarSeqs vs{};
+      vs.H = a.H;
+      vs.total = a.cu_seqlens[a.n_seqs];
+      int tmax = 0;
+      for (int i = 0; i <= ng; i++) vs.cu[i] = a.cu_seqlens[g0 + i];
+      for (int i = 0; i < ng; i++) tmax = max(tmax, vs.cu[i + 1] - vs.cu[i]);
+      GsaLaunch b = a;
+      b.B = ng;
+      b.T = tmax;
+      b.k0 = a.k0 ? a.k0 + g0 * MK : nullptr;
+      b.v0 = a.v0 ? a.v0 + g0 * MV : nullptr;
+      b.kf = a.kf ? a.kf + g0 * MK : nullptr;
+      b.vf = a.vf ? a.vf + g0 * MV : nullptr;
+      b.events = groups == 1 ? a.events : nullptr;
+      if (tmax == 0) {  // only empty sequences: the final states are the initial ones
+        state_copy(b.kf, b.k0, (size_t)ng * MK, a.stream);
+        state_copy(b.vf, b.v0, (size_t)ng * MV, a.stream);
+        continue;
+      }
+      // longest first (stable: equal lengths keep their order, so equal-length
+      // batches launch exactly like the dense one)
+      for (int i = 0; i < ng; i++) vs.order[i] = i;
+      std::stable_sort(vs.order, vs.order + ng, [&](int x, int y) {
+        return vs.cu[x + 1] - vs.cu[x] > vs.cu[y + 1] - vs.cu[y];
+      });
+      if (launch<DK, DV, M, kActSoftmax, VarSeqs>(b, vs) != 0) return -1;
+    }
+    if (groups > 1) {
+      record_event(a.events, 2, a.stream);
+      record_event(a.events, 3, a.stream);
+    }
+    return 0;
   }
   const DenseSeqs ds{a.T};
   switch (a.act) {

@@ -5,7 +5,7 @@
 namespace gsa {
 
 constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kMaxVarSeqs = 256;       // sequences per variable-length call
+constexpr int kMaxVarSeqs = 256;       // sequences per launch of a variable-length batch
 
 struct GsaLaunch {
   const void *q, *k, *v, *g;
@@ -17,7 +17,9 @@ struct GsaLaunch {
   float tau;
   int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
   // Packed variable-length batch (bf16 only): n_seqs sequences, host offsets
-  // cu_seqlens[0..n_seqs] (validated), T = the longest length, B = n_seqs.
+  // cu_seqlens[0..n_seqs] (validated), T = the longest length, B = n_seqs;
+  // launched in groups of at most kMaxVarSeqs sequences, whose workspace is
+  // sized for min(n_seqs, kMaxVarSeqs) * H units.
   // cu_seqlens == nullptr: the dense [B, H, T, d] batch.
   const int* cu_seqlens;
   int n_seqs;

@@ -167,7 +167,7 @@ def test_varlen_validation(gsa):
     assert call([1, 5]) == 2                       # cu[0] != 0
     assert call([0, 70, 60]) == 2                  # decreasing
     assert call([0, 5], n=-1) == 2
-    assert call([0] * 258) == 2                    # more than 256 sequences
+    assert call([0] * 258, H=300) == 4             # a group of 256 x 300 units exceeds the grid
     assert f(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 1, 2, None, None, P(FAKE), None, None,
              128, 128, 64, 64, 8.0, 1, None, 0, 0, None, None) == 2   # no offsets
     assert call([0, 5, 9], dtype=0) == 4           # bf16 only
@@ -180,6 +180,12 @@ def test_varlen_validation(gsa):
         gsa.gsa_fwd_workspace_bytes(4, 8, 2048, 128, 128, 64, 64, 1, 0)
     assert ws([0, 64] + [64] * 0, 1, 128, 128, 64) == 0
     assert ws([0, 5, 3], 2, 128, 128, 64) == (1 << 64) - 1
+    # more than 256 sequences: the workspace of one group of 256
+    many = [64 * i for i in range(601)]
+    assert ws(many, 2, 128, 128, 64, chunks_per_segment=0) == 0          # one chunk each: P = 1
+    long_ = [0] + [64 * 40 * (i + 1) for i in range(600)]
+    assert ws(long_, 2, 128, 128, 64, chunks_per_segment=20) == \
+        gsa.gsa_fwd_varlen_workspace_bytes(long_[:257], 2, 128, 128, 64, chunks_per_segment=20)
     with pytest.raises(ValueError):
         ws([], 2, 128, 128, 64)
 

@@ -140,3 +140,14 @@ def test_softmax_code_matches_plain_entry_point(gsa, torch):
     o3, _, _ = gsa.gsa_fwd(q, k, v, g, nonlinearity="relu")
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and not torch.equal(o1, o3)
+
+
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 64), ("f32", 64, 32)])
+def test_gsa_data_independent_decay(gsa, torch, dtype, d, m):
+    """Table 2's data-independent decay: one gate per (head, slot), the same at
+    every token (an input pattern of the same kernels)."""
+    inp = synth.gsa_inputs(2, 2, 200, d, d, m, dtype=dtype, seed=17, init_std=0.1)
+    x = inp["g"].f64.copy()
+    x[:] = x[:, :, :1, :]          # the first token's logits for every token
+    inp["g"] = synth.stored(x, inp["g"].dtype)
+    _check(gsa, torch, inp, "softmax", dtype, label="data-independent decay")

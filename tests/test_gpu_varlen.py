@@ -172,3 +172,19 @@ def test_serving_workload_sampled(gsa, torch):
                     rel_err(vn[s], r["vf"][0]))
     print("serving prefill sampled sequences %s: worst rel err %.2e" % (picks, worst))
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cps", [0, 1])
+def test_varlen_more_than_256_sequences(gsa, torch, cps):
+    """600 sequences run as three groups of up to 256; the middle group holds
+    only empty sequences (its final states are the initial ones)."""
+    r = np.random.default_rng(31)
+    lengths = list(r.integers(1, 151, size=256)) + [0] * 256 + list(r.integers(0, 151, size=88))
+    lengths = [int(x) for x in lengths]
+    inp = synth.varlen_inputs(lengths, 2, 128, 128, 64, dtype="bf16", seed=32, init_std=0.1)
+    o, kf, vf = _run(gsa, torch, inp, cps)
+    ro, rk, rv = _oracle_each(inp)
+    errs = [rel_err(to_np(o), ro), rel_err(to_np(kf), rk), rel_err(to_np(vf), rv)]
+    print("600 sequences cps=%d: o %.2e kf %.2e vf %.2e" % (cps, *errs))
+    assert max(errs) <= TOL["bf16"]
+    assert np.array_equal(to_np(kf)[256:512], inp["k0"].f64[256:512])
