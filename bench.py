@@ -388,10 +388,62 @@ def bench_ablations(torch, gsa, ev, steps, warmup, nsets):
     return out
 
 
+def measure_peaks(torch, gsa, ev, reps=20):
+    """What this GPU sustains, with the library's own calibration kernels: a
+    streaming copy of 1 GiB and an in-place update of 1 GiB (bytes read +
+    written per second; the forward kernels read their inputs and write
+    elsewhere, the decode step updates its states in place), and a
+    register-only bf16 MFMA loop (dense flops per second).  Median and best of
+    `reps` event-timed runs after warm-up."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, args in (("copy", (dst, src)), ("update", (dst,))):
+        evs = ev.create(2 * reps)
+        for _ in range(5):
+            gsa.measure_hbm(*args)
+        for i in range(reps):
+            gsa.measure_hbm(*args, events=evs[2 * i: 2 * i + 2])
+        torch.cuda.synchronize()
+        t = sorted(ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(reps))
+        out["hbm_%s_GBps" % name] = round(2 * n / (t[len(t) // 2] * 1e-3) / 1e9, 1)
+        out["hbm_%s_GBps_best" % name] = round(2 * n / (t[0] * 1e-3) / 1e9, 1)
+    del src, dst
+    out["hbm_GBps"] = max(out["hbm_copy_GBps"], out["hbm_update_GBps"])
+    iters = 10000
+    sink, flops = gsa.measure_mfma_bf16(iters)
+    for _ in range(3):
+        gsa.measure_mfma_bf16(iters, sink=sink)
+    evm = ev.create(2 * reps)
+    for i in range(reps):
+        gsa.measure_mfma_bf16(iters, sink=sink, events=evm[2 * i: 2 * i + 2])
+    torch.cuda.synchronize()
+    tm = sorted(ev.ms(evm[2 * i], evm[2 * i + 1]) for i in range(reps))
+    out["mfma_bf16_TFLOPs"] = round(flops / (tm[len(tm) // 2] * 1e-3) / 1e12, 1)
+    out["mfma_bf16_TFLOPs_best"] = round(flops / (tm[0] * 1e-3) / 1e12, 1)
+    out["mfma_check"] = bool(torch.all(sink == 1024.0 * iters + 496.0).item())
+    out["kernels"] = ("gsa_measure_hbm (1 GiB copy / in-place update, non-temporal float4, 32 KB "
+                      "per workgroup), gsa_measure_mfma_bf16 (16x16x32, 8 chains/wave, 4 waves/SIMD)")
+    torch.cuda.empty_cache()
+    return out
+
+
+def with_measured(rf, peaks):
+    """A roofline record with the fraction of the measured peak beside the
+    published one's."""
+    if rf and peaks and rf.get("unit") == "GB/s":
+        rf = dict(rf)
+        rf["frac_of_measured"] = round(rf["achieved"] / peaks["hbm_GBps"], 4)
+    return rf
+
+
 def run_only(args, torch, gsa, ev):
     import synth
     if args.only == "copy":
         return copy_calibration(torch, ev, args.steps)
+    if args.only == "peaks":
+        return measure_peaks(torch, gsa, ev)
     if args.only == "gsa":
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], "gsa_bf16_train_T2048",
                       args.steps, args.warmup, args.sets, warm_too=False)
@@ -422,7 +474,8 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve"], default=None,
+    ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
+                             "peaks"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -480,6 +533,18 @@ def main():
         log("bench: read ablations done")
         torch.cuda.empty_cache()
 
+    peaks = measure_peaks(torch, gsa, ev)
+    log("bench: measured peaks %s" % peaks)
+    main_res["roofline"] = with_measured(main_res["roofline"], peaks)
+    main_res["op_roofline"] = with_measured(main_res["op_roofline"], peaks)
+    for c in comps.values():
+        for key in ("roofline", "op_roofline", "decode_roofline"):
+            if key in c:
+                c[key] = with_measured(c[key], peaks)
+        if "identity" in c:  # the read ablations
+            for v in c.values():
+                v["roofline"] = with_measured(v["roofline"], peaks)
+
     cpu, err = None, None
     if not args.no_cpu:
         cpu, ref = cpu_baseline(w, main_res["inp"], args.cpu_seconds)
@@ -509,6 +574,7 @@ def main():
         "mfma_frac_alg": round(main_res["mfma_frac_alg"], 4),
         "warm_cache_tokens_per_s": round(main_res.get("warm_tokens_per_s", 0.0), 1),
         "decode_GBps": comps.get("gsa_decode_N256", {}).get("value"),
+        "measured_peaks": peaks,
         "components": comps,
         "cpu_baseline": cpu,
         "parity_rel_err": None if err is None else float("%.3e" % err),

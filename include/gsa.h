@@ -242,6 +242,29 @@ int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* 
                        float* v_state, void* o, int N, int H, int dk, int dv, int m, float tau,
                        int dtype, int nonlinearity, void* stream, void* const* events);
 
+/*
+ * Calibration kernels for measurements: what this GPU sustains, reported by
+ * the benchmark beside the published peaks.  Not part of the method.
+ *
+ * gsa_measure_hbm: streams bytes (a multiple of 16, > 0) through HBM: mode 0
+ *   copies src to dst (device, 16-byte aligned, not overlapping); mode 1 adds
+ *   1.0f to every float of dst in place (src unused, may be NULL).  Either way
+ *   2 * bytes move.  events: NULL or 2 hipEvent_t (each nullable) stamped at
+ *   the start and end of the kernel's dispatch.
+ * gsa_measure_mfma_bf16: runs `iterations` rounds of bf16 MFMA 16x16x32 on
+ *   register operands (all ones) in GSA_MEASURE_MFMA_WORKGROUPS workgroups of
+ *   four waves, eight independent accumulators per wave; *flops (nullable)
+ *   receives the dense flop count.  sink: device, GSA_MEASURE_MFMA_WORKGROUPS
+ *   floats, each set to 1024 * iterations + 496 (exact for iterations <= 16000).
+ *   events as above.
+ * Both validate on the host and return a gsa_status.
+ */
+#define GSA_MEASURE_MFMA_WORKGROUPS 1024
+int gsa_measure_hbm(const void* src, void* dst, size_t bytes, int mode, void* stream,
+                    void* const* events);
+int gsa_measure_mfma_bf16(float* sink, int iterations, double* flops, void* stream,
+                          void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,11 @@ lib.gsa_fwd_ex.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_decode_step_ex.restype = _I
 lib.gla_fwd_ex.restype = _I
 lib.gla_fwd_ex.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _I, _P, _P]
+lib.gsa_measure_hbm.restype = _I
+lib.gsa_measure_hbm.argtypes = [_P, _P, _S, _I, _P, _P]
+lib.gsa_measure_mfma_bf16.restype = _I
+lib.gsa_measure_mfma_bf16.argtypes = [_P, _I, ctypes.POINTER(ctypes.c_double), _P, _P]
+MEASURE_MFMA_WORKGROUPS = 1024
 lib.gsa_fwd_varlen.restype = _I
 lib.gsa_fwd_varlen.argtypes = [_P] * 5 + [_I, _I] + [_P] * 5 + [_I] * 4 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_fwd_varlen_workspace_bytes.restype = _S
@@ -305,3 +310,39 @@ def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=N
     if st:
         raise GsaError("gsa_decode_step", st)
     return out
+
+
+# ------------------------------------------------------------ calibration
+def measure_hbm(dst, src=None, *, stream=None, events=None):
+    """Stream dst's bytes through HBM: copy src -> dst (equal byte sizes, a
+    multiple of 16), or with src None add 1.0 to every float of dst in place.
+    Returns the bytes moved (2 * nbytes).  events: None or two hipEvent_t
+    handles stamped at the kernel's start and end."""
+    _check(dst, "dst")
+    if src is not None:
+        _check(src, "src")
+    nb = dst.numel() * dst.element_size()
+    if src is not None and src.numel() * src.element_size() != nb:
+        raise ValueError("src and dst sizes differ")
+    st = lib.gsa_measure_hbm(_ptr(src), _ptr(dst), nb, 0 if src is not None else 1, _stream(stream),
+                             _events(events, 2))
+    if st:
+        raise GsaError("gsa_measure_hbm", st)
+    return 2 * nb
+
+
+def measure_mfma_bf16(iterations, *, sink=None, stream=None, events=None):
+    """The bf16 MFMA calibration loop; returns (sink, dense flops).  Every sink
+    entry ends at 1024 * iterations + 496."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(MEASURE_MFMA_WORKGROUPS, dtype=torch.float32, device="cuda")
+    _check(sink, "sink", torch.float32)
+    if sink.numel() < MEASURE_MFMA_WORKGROUPS:
+        raise ValueError("sink needs %d floats" % MEASURE_MFMA_WORKGROUPS)
+    fl = ctypes.c_double()
+    st = lib.gsa_measure_mfma_bf16(_ptr(sink), int(iterations), ctypes.byref(fl), _stream(stream),
+                                   _events(events, 2))
+    if st:
+        raise GsaError("gsa_measure_mfma_bf16", st)
+    return sink, fl.value

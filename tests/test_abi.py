@@ -190,6 +190,23 @@ def test_varlen_validation(gsa):
         ws([], 2, 128, 128, 64)
 
 
+def test_measure_validation(gsa):
+    """The calibration entry points reject bad arguments on the host."""
+    P = ctypes.c_void_p
+    c = gsa.lib.gsa_measure_hbm
+    assert c(None, P(FAKE), 64, 0, None, None) == 1
+    assert c(P(FAKE), None, 64, 1, None, None) == 1
+    assert c(P(FAKE), P(FAKE + 0x10000), 64, 2, None, None) == 2
+    assert c(P(FAKE), P(FAKE + 0x10000), 0, 0, None, None) == 2
+    assert c(P(FAKE), P(FAKE + 0x10000), 24, 0, None, None) == 2
+    assert c(P(FAKE + 4), P(FAKE + 0x10000), 64, 0, None, None) == 3
+    assert c(P(FAKE), P(FAKE + 32), 64, 0, None, None) == 7
+    f = gsa.lib.gsa_measure_mfma_bf16
+    assert f(None, 10, None, None, None) == 1
+    assert f(P(FAKE), 0, None, None, None) == 2
+    assert f(P(FAKE + 4), 10, None, None, None) == 3
+
+
 def test_package_has_no_cpu_fallback():
     """The product package never imports, loads or calls the oracle."""
     pkg = os.path.join(ROOT, "slot_memory_sequence_amd")
