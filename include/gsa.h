@@ -254,16 +254,18 @@ int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* 
  * gsa_measure_mfma_bf16: runs `iterations` rounds of bf16 MFMA 16x16x32 on
  *   register operands (all ones) in GSA_MEASURE_MFMA_WORKGROUPS workgroups of
  *   four waves, eight independent accumulators per wave; *flops (nullable)
- *   receives the dense flop count.  sink: device, GSA_MEASURE_MFMA_WORKGROUPS
- *   floats, each set to 1024 * iterations + 496 (exact for iterations <= 16000).
+ *   receives the dense flop count.  sink: device, sink_floats >=
+ *   GSA_MEASURE_MFMA_WORKGROUPS floats (else GSA_ERR_WORKSPACE); its first
+ *   GSA_MEASURE_MFMA_WORKGROUPS entries are set to 1024 * iterations + 496
+ *   (exact for iterations <= 16000).
  *   events as above.
  * Both validate on the host and return a gsa_status.
  */
 #define GSA_MEASURE_MFMA_WORKGROUPS 1024
 int gsa_measure_hbm(const void* src, void* dst, size_t bytes, int mode, void* stream,
                     void* const* events);
-int gsa_measure_mfma_bf16(float* sink, int iterations, double* flops, void* stream,
-                          void* const* events);
+int gsa_measure_mfma_bf16(float* sink, size_t sink_floats, int iterations, double* flops,
+                          void* stream, void* const* events);
 
 #ifdef __cplusplus
 }

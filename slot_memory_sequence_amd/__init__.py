@@ -65,7 +65,7 @@ lib.gla_fwd_ex.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_measure_hbm.restype = _I
 lib.gsa_measure_hbm.argtypes = [_P, _P, _S, _I, _P, _P]
 lib.gsa_measure_mfma_bf16.restype = _I
-lib.gsa_measure_mfma_bf16.argtypes = [_P, _I, ctypes.POINTER(ctypes.c_double), _P, _P]
+lib.gsa_measure_mfma_bf16.argtypes = [_P, _S, _I, ctypes.POINTER(ctypes.c_double), _P, _P]
 MEASURE_MFMA_WORKGROUPS = 1024
 lib.gsa_fwd_varlen.restype = _I
 lib.gsa_fwd_varlen.argtypes = [_P] * 5 + [_I, _I] + [_P] * 5 + [_I] * 4 + [_F, _I, _P, _S, _I, _P, _P]
@@ -341,8 +341,8 @@ def measure_mfma_bf16(iterations, *, sink=None, stream=None, events=None):
     if sink.numel() < MEASURE_MFMA_WORKGROUPS:
         raise ValueError("sink needs %d floats" % MEASURE_MFMA_WORKGROUPS)
     fl = ctypes.c_double()
-    st = lib.gsa_measure_mfma_bf16(_ptr(sink), int(iterations), ctypes.byref(fl), _stream(stream),
-                                   _events(events, 2))
+    st = lib.gsa_measure_mfma_bf16(_ptr(sink), sink.numel(), int(iterations), ctypes.byref(fl),
+                                   _stream(stream), _events(events, 2))
     if st:
         raise GsaError("gsa_measure_mfma_bf16", st)
     return sink, fl.value

@@ -108,10 +108,11 @@ int gsa_measure_hbm(const void* src, void* dst, size_t bytes, int mode, void* st
   return hipGetLastError() == hipSuccess ? GSA_OK : GSA_ERR_HIP;
 }
 
-int gsa_measure_mfma_bf16(float* sink, int iterations, double* flops, void* stream,
-                          void* const* events) {
+int gsa_measure_mfma_bf16(float* sink, size_t sink_floats, int iterations, double* flops,
+                          void* stream, void* const* events) {
   if (!sink) return GSA_ERR_NULL;
   if (iterations < 1) return GSA_ERR_SHAPE;
+  if (sink_floats < GSA_MEASURE_MFMA_WORKGROUPS) return GSA_ERR_WORKSPACE;
   if ((uintptr_t)sink & 15u) return GSA_ERR_ALIGN;
   (void)hipGetLastError();
   gsa::launch_timed(gsa::mfma_bf16_kernel, dim3(GSA_MEASURE_MFMA_WORKGROUPS), dim3(gsa::kMfmaThreads),

@@ -202,9 +202,10 @@ def test_measure_validation(gsa):
     assert c(P(FAKE + 4), P(FAKE + 0x10000), 64, 0, None, None) == 3
     assert c(P(FAKE), P(FAKE + 32), 64, 0, None, None) == 7
     f = gsa.lib.gsa_measure_mfma_bf16
-    assert f(None, 10, None, None, None) == 1
-    assert f(P(FAKE), 0, None, None, None) == 2
-    assert f(P(FAKE + 4), 10, None, None, None) == 3
+    assert f(None, 1024, 10, None, None, None) == 1
+    assert f(P(FAKE), 1024, 0, None, None, None) == 2
+    assert f(P(FAKE), 1023, 10, None, None, None) == 5
+    assert f(P(FAKE + 4), 1024, 10, None, None, None) == 3
 
 
 def test_package_has_no_cpu_fallback():
