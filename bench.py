@@ -265,6 +265,38 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
             "roofline": r}
 
 
+def bench_gla_decode(torch, gsa, ev, steps, warmup):
+    """The recurrent GLA step at the decode batch's shape (256 sequences x 16
+    heads, d = 128, tau = 16): one fp32 state of 64 KB per unit read and
+    written once, in place."""
+    import synth
+    from tests.gpu_helpers import to_dev
+    N, H, d = 256, 16, 128
+    inp = synth.gla_inputs(N, H, 1, d, d, dtype="bf16", seed=0, init_std=0.1)
+    tok = {n: to_dev(inp[n], torch)[:, :, 0].contiguous() for n in "qkvg"}
+    states = [to_dev(inp["s0"], torch) for _ in range(2)]
+    out = torch.empty((N, H, d), dtype=torch.bfloat16, device="cuda")
+    evs = ev.create(2 * steps)
+    for i in range(warmup):
+        gsa.gla_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], states[i % 2], out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        gsa.gla_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], states[i % 2], out=out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(steps):
+        gsa.gla_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], states[i % 2], out=out,
+                            events=evs[2 * i: 2 * i + 2])
+    torch.cuda.synchronize()
+    t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])
+    units = N * H
+    nbytes = units * (2 * 4 * d * d + 2 * (4 * d))
+    r = roofline(nbytes, t, "gla_decode_kernel", "gla_decode_N256")
+    return {"value": r["achieved"], "unit": "GB/s", "ms_kernel": round(t, 4),
+            "steps_per_s": round(steps / wall, 1), "roofline": r}
+
+
 def cpu_baseline(w, inp, budget_s):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -452,6 +484,8 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "gla_decode":
+        return bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
     if args.only == "serve":
         return bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
                            args.warmup)
@@ -475,7 +509,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks"], default=None,
+                             "peaks", "gla_decode"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -524,6 +558,8 @@ def main():
         comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
                                                 args.steps, args.warmup)
         log("bench: decode done")
+        comps["gla_decode_N256"] = bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
+        log("bench: GLA decode done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)
         log("bench: serving prefill + decode done")

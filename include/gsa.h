@@ -243,6 +243,25 @@ int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* 
                        int dtype, int nonlinearity, void* stream, void* const* events);
 
 /*
+ * One recurrent GLA step (Sec. 2.3 recurrent form, beta = 1) for N sequences x
+ * H heads: S <- Diag(alpha) S + k v^T, o = S^T q, alpha per key dimension, read
+ * from g as gate_input says (a gsa_gate_input code; tau is read only for
+ * logits).  The decode counterpart of gla_fwd / gla_fwd_ex, whose s_final it
+ * continues.
+ *   q, k, g  [N,H,dk]     dtype
+ *   v        [N,H,dv]     dtype
+ *   s        [N,H,dk,dv]  float32, advanced in place (must not overlap the
+ *                         token inputs or o)
+ *   o        [N,H,dv]     dtype
+ * events: NULL or 2 hipEvent_t stamped at the kernel's start and end.
+ * Compiled for dk = dv in {64, 128}, float32 and bf16.
+ */
+int gla_decode_supported(int dk, int dv, int dtype);
+int gla_decode_step(const void* q, const void* k, const void* v, const void* g, float* s, void* o,
+                    int N, int H, int dk, int dv, float tau, int dtype, int gate_input, void* stream,
+                    void* const* events);
+
+/*
  * Calibration kernels for measurements: what this GPU sustains, reported by
  * the benchmark beside the published peaks.  Not part of the method.
  *

@@ -16,7 +16,8 @@ import os
 # and allocations are valid handles for the library.
 import torch as _torch_rt  # noqa: F401
 
-__all__ = ["lib", "gsa_fwd", "gsa_fwd_varlen", "gla_fwd", "gsa_decode_step", "GsaError", "LIB_PATH",
+__all__ = ["lib", "gsa_fwd", "gsa_fwd_varlen", "gla_fwd", "gsa_decode_step", "gla_decode_step",
+           "GsaError", "LIB_PATH",
            "NONLINEARITIES", "gsa_fwd_varlen_workspace_bytes",
            "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
            "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
@@ -62,6 +63,9 @@ lib.gsa_fwd_ex.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _P, _S, _I, _I, _P, _P]
 lib.gsa_decode_step_ex.restype = _I
 lib.gla_fwd_ex.restype = _I
 lib.gla_fwd_ex.argtypes = [_P] * 7 + [_I] * 6 + [_F, _I, _P, _S, _I, _I, _P, _P]
+lib.gla_decode_supported.argtypes = [_I] * 3
+lib.gla_decode_step.restype = _I
+lib.gla_decode_step.argtypes = [_P] * 6 + [_I] * 4 + [_F, _I, _I, _P, _P]
 lib.gsa_measure_hbm.restype = _I
 lib.gsa_measure_hbm.argtypes = [_P, _P, _S, _I, _P, _P]
 lib.gsa_measure_mfma_bf16.restype = _I
@@ -309,6 +313,29 @@ def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=N
                                 _nl(nonlinearity), _stream(stream), _events(events, 2))
     if st:
         raise GsaError("gsa_decode_step", st)
+    return out
+
+
+def gla_decode_step(q, k, v, g, s_state, *, tau=16.0, gate="logit", out=None, stream=None,
+                    events=None):
+    """One recurrent GLA step.  q, k, g [N,H,dk]; v [N,H,dv]; float32 s_state
+    [N,H,dk,dv] advanced in place (e.g. gla_fwd's s_final).  gate as for
+    gla_fwd.  Returns o [N,H,dv]."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _check(t, n, q.dtype)
+    _check(s_state, "s_state", torch.float32)
+    if gate not in GATE_INPUTS:
+        raise ValueError("gate must be one of %s" % ", ".join(GATE_INPUTS))
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    st = lib.gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s_state), _ptr(out), N, H, dk,
+                             dv, float(tau), _dt(q), GATE_INPUTS[gate], _stream(stream),
+                             _events(events, 2))
+    if st:
+        raise GsaError("gla_decode_step", st)
     return out
 
 

@@ -397,4 +397,40 @@ int gsa_decode_step_ex(const void* q, const void* k, const void* v, const void* 
   return hip_status();
 }
 
+int gla_decode_supported(int dk, int dv, int dtype) {
+  if (!dtype_ok(dtype)) return 0;
+  return gsa::gla_decode_dispatch(dtype, dk, dv, nullptr, true) > 0 ? 1 : 0;
+}
+
+int gla_decode_step(const void* q, const void* k, const void* v, const void* g, float* s, void* o,
+                    int N, int H, int dk, int dv, float tau, int dtype, int gate_input, void* stream,
+                    void* const* events) {
+  if (gate_input == GSA_GATE_LOG_DECAY) tau = 1.f;  // not read
+  if (N < 0 || H < 0 || dk < 1 || dv < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
+      !dtype_ok(dtype) || (gate_input != GSA_GATE_LOGIT && gate_input != GSA_GATE_LOG_DECAY))
+    return GSA_ERR_SHAPE;
+  if (!gla_decode_supported(dk, dv, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)N * H;
+  if (units == 0) return GSA_OK;
+  if (units > 0x7fffffffLL) return GSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !s || !o) return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, s, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const Range rq = rng(q, units * dk * es), rk = rng(k, units * dk * es), rv = rng(v, units * dv * es),
+              rg = rng(g, units * dk * es), ro = rng(o, units * dv * es);
+  const Range rs = rng(s, (size_t)units * dk * dv * 4);
+  for (Range in : {rq, rk, rv, rg, ro})
+    if (overlap(rs, in)) return GSA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rg})
+    if (overlap(ro, in)) return GSA_ERR_ALIAS;
+  gsa::GlaDecodeLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.o = o; a.N = N; a.H = H; a.tau = tau;
+  a.gate_mode = gate_input; a.stream = stream; a.events = events;
+  (void)hipGetLastError();
+  if (gsa::gla_decode_dispatch(dtype, dk, dv, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
 }  // extern "C"

@@ -213,6 +213,91 @@ int decode_dispatch(int dt, int dk, int dv, int m, const DecodeLaunch* a, bool q
   return -1;
 }
 
+// ------------------------------------------------------------- GLA step
+// One recurrent GLA step (Sec. 2.3, beta = 1) per (sequence, head), in place:
+//   S <- Diag(alpha) S + k v^T,  o = S^T q,  alpha per key dimension (GM: from
+// a logit, or a log-decay given directly).  S [dk][dv] fp32 is streamed once:
+// thread t owns float4 column c = t % (dv/4) of rows t / (dv/4) + RG j, all its
+// rows loaded (non-temporal) before any arithmetic; the partial outputs of
+// the RG row groups are summed through LDS.
+template <typename T, int DK, int DV, int GM>
+__global__ void __launch_bounds__(256)
+gla_decode_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                  const T* __restrict__ g, float* __restrict__ ss, T* __restrict__ o, float inv_tau) {
+  constexpr int NTH = 256, CPR = DV / 4, RG = NTH / CPR, RPT = DK / RG;
+  static_assert(NTH % CPR == 0 && DK % RG == 0 && RPT >= 1, "shape");
+  __shared__ float sA[DK], sK[DK], sQ[DK];
+  __shared__ float sO[RG][DV];
+  const int tid = threadIdx.x;
+  const size_t u = blockIdx.x;
+  f32x4* st = reinterpret_cast<f32x4*>(ss + u * DK * DV);
+  const int c = tid % CPR, r0 = tid / CPR;
+  f32x4 sr[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; j++) sr[j] = ld_state(st + (size_t)(r0 + RG * j) * CPR + c);
+  float vf[4];
+  load4<T>(v + u * DV + 4 * c, vf);
+  for (int x = tid; x < DK; x += NTH) {
+    const float gx = Elem<T>::to_f(g[u * DK + x]);
+    sA[x] = GM == kGateLogit ? gate_alpha(gx, inv_tau) : __expf(fminf(gx, 0.f));
+    sK[x] = Elem<T>::to_f(k[u * DK + x]);
+    sQ[x] = Elem<T>::to_f(q[u * DK + x]);
+  }
+  __syncthreads();
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RPT; j++) {
+    const int x = r0 + RG * j;
+    const float a = sA[x], kx = sK[x], qx = sQ[x];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      sr[j][e] = a * sr[j][e] + kx * vf[e];
+      acc[e] += qx * sr[j][e];
+    }
+    st_state(st + (size_t)x * CPR + c, sr[j]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; e++) sO[r0][4 * c + e] = acc[e];
+  __syncthreads();
+  if (tid < CPR) {
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int gi = 0; gi < RG; gi++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) r[e] += sO[gi][4 * tid + e];
+    }
+    store4<T>(o + u * DV + 4 * tid, r);
+  }
+}
+
+template <typename T, int DK, int DV>
+static int launch_gla_decode(const GlaDecodeLaunch& a) {
+  const unsigned units = (unsigned)a.N * (unsigned)a.H;
+  const float inv_tau = 1.0f / a.tau;
+  if (a.gate_mode == kGateLogit)
+    launch_timed(gla_decode_kernel<T, DK, DV, kGateLogit>, dim3(units), dim3(256), 0, a.stream, a.events,
+                 0, 1, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.s, (T*)a.o, inv_tau);
+  else
+    launch_timed(gla_decode_kernel<T, DK, DV, kGateLogDecay>, dim3(units), dim3(256), 0, a.stream,
+                 a.events, 0, 1, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.g, a.s,
+                 (T*)a.o, inv_tau);
+  return 0;
+}
+
+#define GLA_DEC_CASE(TT, DTC, DKC, DVC)                    \
+  if (dt == DTC && dk == DKC && dv == DVC) {               \
+    if (query) return 1;                                    \
+    return launch_gla_decode<TT, DKC, DVC>(*a);             \
+  }
+
+int gla_decode_dispatch(int dt, int dk, int dv, const GlaDecodeLaunch* a, bool query) {
+  GLA_DEC_CASE(bf16_t, 1, 128, 128)
+  GLA_DEC_CASE(bf16_t, 1, 64, 64)
+  GLA_DEC_CASE(float, 0, 128, 128)
+  GLA_DEC_CASE(float, 0, 64, 64)
+  return -1;
+}
+
 __global__ void state_copy_kernel(float* __restrict__ dst, const float* __restrict__ src, size_t n) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;

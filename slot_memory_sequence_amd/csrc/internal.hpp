@@ -55,6 +55,17 @@ struct DecodeLaunch {
   void* const* events;  // nullable: 2 hipEvent_t, start and end of the kernel
 };
 
+struct GlaDecodeLaunch {
+  const void *q, *k, *v, *g;
+  float* s;
+  void* o;
+  int N, H;
+  float tau;
+  int gate_mode;  // a GSA_GATE_* code (GateMode)
+  void* stream;
+  void* const* events;  // nullable: 2 hipEvent_t, start and end of the kernel
+};
+
 // query == true: return the phase-C LDS bytes (> 0) if the shape is compiled, else -1.
 // query == false: enqueue the launches and return 0, or -1 if not compiled.
 int gsa_dispatch(int dtype, int dk, int dv, int m, const GsaLaunch* a, bool query);
@@ -62,6 +73,7 @@ int gsa_dispatch_bf16(int dk, int dv, int m, const GsaLaunch* a, bool query);
 int gla_dispatch(int dtype, int dk, int dv, const GlaLaunch* a, bool query);
 int gla_dispatch_bf16(int dk, int dv, const GlaLaunch* a, bool query);
 int decode_dispatch(int dtype, int dk, int dv, int m, const DecodeLaunch* a, bool query);
+int gla_decode_dispatch(int dtype, int dk, int dv, const GlaDecodeLaunch* a, bool query);
 // copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
 void state_copy(float* dst, const float* src, size_t n, void* stream);
 

@@ -208,6 +208,24 @@ def test_measure_validation(gsa):
     assert f(P(FAKE + 4), 1024, 10, None, None, None) == 3
 
 
+def test_gla_decode_validation(gsa):
+    P = ctypes.c_void_p
+    d = gsa.lib.gla_decode_step
+    args = [P(FAKE), P(FAKE + 0x1000), P(FAKE + 0x2000), P(FAKE + 0x3000), P(FAKE + 0x100000),
+            P(FAKE + 0x4000)]
+    assert d(*args, 1, 1, 128, 128, 16.0, 1, 2, None, None) == 2       # bad gate code
+    assert d(*args, 1, 1, 128, 128, -1.0, 1, 0, None, None) == 2       # bad tau with logits
+    assert d(*args, 1, 1, 96, 96, 16.0, 1, 0, None, None) == 4
+    bad = list(args)
+    bad[4] = P(FAKE + 0x1010)                                          # state overlaps k
+    assert d(*bad, 1, 1, 128, 128, 16.0, 1, 0, None, None) == 7
+    bad = list(args)
+    bad[5] = None
+    assert d(*bad, 1, 1, 128, 128, -1.0, 1, 1, None, None) == 1       # tau unused with log-decays
+    assert gsa.lib.gla_decode_supported(128, 128, 1) == 1
+    assert gsa.lib.gla_decode_supported(64, 128, 1) == 0
+
+
 def test_package_has_no_cpu_fallback():
     """The product package never imports, loads or calls the oracle."""
     pkg = os.path.join(ROOT, "slot_memory_sequence_amd")
