@@ -641,45 +641,48 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
 }
 
 // ----------------------------------------------------- phase B: scan
-// One thread per (unit, state element), serial over the segments; the loads of
-// a batch of maps are issued before any of the batch's stores.  Slot p holds
-// segment p's map on entry (p < P-1) and its start state on exit.
+// One thread per (unit, four consecutive state elements of one slot row),
+// serial over the segments; the loads of a batch of maps are issued before any
+// of the batch's stores.  Slot p holds segment p's map on entry (p < P-1) and
+// its start state on exit.
 template <int DK, int DV, int M>
 __global__ void __launch_bounds__(256)
 gsa_bf16_scan(float* __restrict__ ws_state, const float* __restrict__ ws_dec,
               const float* __restrict__ k0, const float* __restrict__ v0, int units, int P) {
   constexpr int NE = M * (DK + DV);
   constexpr int BATCH = 8;
+  static_assert(DK % 4 == 0 && DV % 4 == 0, "float4 rows");
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long long)units * NE) return;
-  const int unit = (int)(gid / NE), e = (int)(gid % NE);
+  if (gid >= (long long)units * (NE / 4)) return;
+  const int unit = (int)(gid / (NE / 4)), e = 4 * (int)(gid % (NE / 4));
   const int c = e / (DK + DV), cl = e % (DK + DV);
-  float W = 0.f;
+  f32x4 W = {0.f, 0.f, 0.f, 0.f};
   if (cl < DK) {
-    if (k0) W = k0[((size_t)unit * M + c) * DK + cl];
+    if (k0) W = *reinterpret_cast<const f32x4*>(k0 + ((size_t)unit * M + c) * DK + cl);
   } else {
-    if (v0) W = v0[((size_t)unit * M + c) * DV + cl - DK];
+    if (v0) W = *reinterpret_cast<const f32x4*>(v0 + ((size_t)unit * M + c) * DV + cl - DK);
   }
-  float* st = ws_state + (size_t)unit * P * NE + e;
+  f32x4* st = reinterpret_cast<f32x4*>(ws_state + (size_t)unit * P * NE + e);
   const float* dc = ws_dec + (size_t)unit * P * M + c;
   for (int p0 = 0; p0 + 1 < P; p0 += BATCH) {
-    float x[BATCH], d[BATCH];
+    f32x4 x[BATCH];
+    float d[BATCH];
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
       if (p0 + i + 1 < P) {
-        x[i] = st[(size_t)(p0 + i) * NE];
+        x[i] = st[(size_t)(p0 + i) * (NE / 4)];
         d[i] = dc[(size_t)(p0 + i) * M];
       }
     }
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
       if (p0 + i + 1 < P) {
-        __builtin_nontemporal_store(W, st + (size_t)(p0 + i) * NE);  // read only by the next launch
+        __builtin_nontemporal_store(W, st + (size_t)(p0 + i) * (NE / 4));  // read only by the next launch
         W = d[i] * W + x[i];
       }
     }
   }
-  __builtin_nontemporal_store(W, st + (size_t)(P - 1) * NE);
+  __builtin_nontemporal_store(W, st + (size_t)(P - 1) * (NE / 4));
 }
 
 // ------------------------------------------------------ phase C: outputs
@@ -888,7 +891,7 @@ static int launch(const GsaLaunch& a, const Seq& seq) {
                  a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
                  a.ws_state, a.ws_dec, seq, S, P, inv_tau);
     if (!fold) {
-      const long long ne = (long long)units * M * (DK + DV);
+      const long long ne = (long long)units * M * (DK + DV) / 4;  // float4 per thread
       hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
                          a.ws_state, (const float*)a.ws_dec, a.k0, a.v0, units, P);
     }
