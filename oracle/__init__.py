@@ -8,7 +8,9 @@ Three independent implementations, all float64:
 
 * ``gsa_fwd`` / ``gla_fwd`` / ``gsa_decode_step`` -- the plain token-by-token
   recurrences, in C (``gsa_oracle.c``), the reference everything is measured
-  against;
+  against; ``gsa_bwd``, the gradients of ``gsa_fwd`` by reverse-mode
+  differentiation of that recurrence (pinned by central differences of the
+  forward);
 * ``chunkwise`` -- the chunk decomposition of the paper's App. A.1 / App. B,
   written in numpy, used only to pin the recurrence;
 * ``bruteforce`` -- explicitly unrolled sums for tiny T, likewise a pin.
@@ -56,8 +58,10 @@ def _load():
         lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
         lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
         lib.oracle_gsa_decode_step_nl.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
+        lib.oracle_gsa_bwd.argtypes = [P] * 15 + [L] * 6 + [D, I]
         for f in (lib.oracle_gsa_fwd, lib.oracle_gla_fwd, lib.oracle_gsa_decode_step,
-                  lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl, lib.oracle_gla_fwd_gm):
+                  lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl, lib.oracle_gla_fwd_gm,
+                  lib.oracle_gsa_bwd):
             f.restype = I
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -117,6 +121,32 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, want_states=True,
     if rc:
         raise RuntimeError("oracle_gsa_fwd failed (%d)" % rc)
     return dict(o=o, kf=kf, vf=vf, s=s, z=z)
+
+
+def gsa_bwd(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, nthreads=1):
+    """Gradients of the recurrent GSA forward (softmax read) by reverse-mode
+    differentiation of the token recurrence.  do [B,H,T,dv] is the gradient of
+    the outputs; dkf [B,H,m,dk] / dvf [B,H,m,dv] (optional) those of the final
+    states.  Returns dict with dq, dk, dv, dg (shaped like q, k, v, g) and
+    dk0 / dv0, the gradients of the initial states (zero states when k0 / v0
+    are not given)."""
+    q, k, v, g, do, k0, v0, dkf, dvf = map(_f64, (q, k, v, g, do, k0, v0, dkf, dvf))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    m = g.shape[-1]
+    assert k.shape == q.shape and v.shape[:3] == (B, H, T) and g.shape[:3] == (B, H, T)
+    assert do.shape == v.shape
+    for x, d in ((k0, dk), (dkf, dk), (v0, dv), (dvf, dv)):
+        if x is not None:
+            assert x.shape == (B, H, m, d)
+    out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v), dg=np.empty_like(g),
+               dk0=np.empty((B, H, m, dk)), dv0=np.empty((B, H, m, dv)))
+    rc = _load().oracle_gsa_bwd(_p(q), _p(k), _p(v), _p(g), _p(do), _p(k0), _p(v0), _p(dkf),
+                                _p(dvf), *(_p(out[n]) for n in ("dq", "dk", "dv", "dg", "dk0", "dv0")),
+                                B, H, T, dk, dv, m, float(tau), int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_gsa_bwd failed (%d)" % rc)
+    return out
 
 
 GATE_INPUTS = {"logit": 0, "log_decay": 1}

@@ -32,6 +32,9 @@
  *     log-decays (alpha = exp(min(g, 0)), gate_mode 1): a gate vector computed
  *     elsewhere, such as the rank-one gate of Lattice's simplified chunk
  *     recurrence.
+ *   - Backward (App. B trains the model; the gradient itself is that of the
+ *     recurrence above): oracle_gsa_bwd differentiates the token recurrence in
+ *     reverse mode, keeping every state of the forward sweep.
  *
  * All arithmetic is fp64.  log sigmoid uses the textbook stable split
  * min(x,0) - log1p(exp(-|x|)); 1 - alpha is formed as -expm1(log alpha) so
@@ -284,6 +287,160 @@ int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
 {
     return oracle_gsa_decode_step_nl(q, k, v, g, kstate, vstate, o, N, H, dk,
                                      dv, m, tau, 0, nthreads);
+}
+
+/*
+ * Gradients of the GSA forward (softmax read) with respect to q, k, v, the
+ * gate logits g and the initial states, given the gradient dO of the outputs
+ * and (nullable) the gradients dkf / dvf of the final states.  This is the
+ * plain definition: reverse-mode differentiation of the token recurrence
+ * (Sec. 3.2-3.3), with every state of the forward sweep kept.  (App. B trains
+ * the same function; how its kernels save and recompute states is a matter of
+ * memory, not of the result.)
+ *
+ * Reverse sweep, per unit, t = T-1 .. 0, with dK, dV the adjoints of the
+ * states after token t (starting from dkf, dvf):
+ *   ds[c] = Vt[c,:] . dO_t              (o_t = Vt^T s_t)
+ *   dV[c,:] += s_t[c] dO_t
+ *   dz = s_t * (ds - s_t . ds)          (softmax Jacobian)
+ *   dq_t = Kt^T dz,   dK[c,:] += dz[c] q_t
+ *   dk_t = dK^T w_t,  dv_t = dV^T w_t    (w_t = 1 - alpha_t)
+ *   dalpha[c] = dK[c,:] . (K_{t-1}[c,:] - k_t) + dV[c,:] . (V_{t-1}[c,:] - v_t)
+ *   dg_t[c] = dalpha[c] * alpha_t[c] * sigmoid(-g_t[c]) / tau
+ *   dK[c,:] *= alpha_t[c], dV[c,:] *= alpha_t[c]   (adjoints of K_{t-1}, V_{t-1})
+ * dk0 / dv0 (nullable) receive the adjoints left after t = 0.
+ * Layouts as for oracle_gsa_fwd; dO and dv [B,H,T,dv], dg [B,H,T,m].
+ */
+int oracle_gsa_bwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *dO, const double *k0,
+                   const double *v0, const double *dkf, const double *dvf,
+                   double *dq, double *dk, double *dv, double *dg, double *dk0,
+                   double *dv0, long B, long H, long T, long d_k, long d_v,
+                   long m, double tau, int nthreads)
+{
+    long units = B * H, u;
+    int err = 0;
+    if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || B < 0 ||
+        H < 0 || T < 0 || d_k < 1 || d_v < 1 || m < 1 || !(tau > 0.0))
+        return 1;
+#ifdef _OPENMP
+    if (nthreads < 1)
+        nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : err)
+#endif
+    for (u = 0; u < units; u++) {
+        /* Ks[t] / Vs[t]: the states before token t (t = 0 .. T) */
+        double *Ks = malloc((size_t)((T + 1) * m * d_k) * sizeof(double));
+        double *Vs = malloc((size_t)((T + 1) * m * d_v) * sizeof(double));
+        double *S = malloc((size_t)((T > 0 ? T : 1) * m) * sizeof(double));
+        double *dK = calloc((size_t)(m * d_k), sizeof(double));
+        double *dV = calloc((size_t)(m * d_v), sizeof(double));
+        double *ds = malloc((size_t)m * sizeof(double));
+        double *dz = malloc((size_t)m * sizeof(double));
+        long t, c, x;
+        if (!Ks || !Vs || !S || !dK || !dV || !ds || !dz) {
+            err |= 2;
+        } else {
+            /* forward sweep: the states and the slot read weights */
+            for (c = 0; c < m * d_k; c++)
+                Ks[c] = k0 ? k0[u * m * d_k + c] : 0.0;
+            for (c = 0; c < m * d_v; c++)
+                Vs[c] = v0 ? v0[u * m * d_v + c] : 0.0;
+            for (t = 0; t < T; t++) {
+                long row = u * T + t;
+                const double *qt = q + row * d_k, *kt = k + row * d_k;
+                const double *vt = v + row * d_v, *gt = g + row * m;
+                const double *Kp = Ks + t * m * d_k, *Vp = Vs + t * m * d_v;
+                double *Kn = Ks + (t + 1) * m * d_k, *Vn = Vs + (t + 1) * m * d_v;
+                double *st = S + t * m, zmax = -INFINITY, sum = 0.0;
+                for (c = 0; c < m; c++) {
+                    double la = log_sigmoid(gt[c]) / tau;
+                    double a = exp(la), w = -expm1(la), acc = 0.0;
+                    for (x = 0; x < d_k; x++) {
+                        Kn[c * d_k + x] = a * Kp[c * d_k + x] + w * kt[x];
+                        acc += Kn[c * d_k + x] * qt[x];
+                    }
+                    for (x = 0; x < d_v; x++)
+                        Vn[c * d_v + x] = a * Vp[c * d_v + x] + w * vt[x];
+                    st[c] = acc;
+                    if (acc > zmax)
+                        zmax = acc;
+                }
+                for (c = 0; c < m; c++) {
+                    st[c] = exp(st[c] - zmax);
+                    sum += st[c];
+                }
+                for (c = 0; c < m; c++)
+                    st[c] /= sum;
+            }
+            /* reverse sweep */
+            if (dkf)
+                memcpy(dK, dkf + u * m * d_k, (size_t)(m * d_k) * sizeof(double));
+            if (dvf)
+                memcpy(dV, dvf + u * m * d_v, (size_t)(m * d_v) * sizeof(double));
+            for (t = T - 1; t >= 0; t--) {
+                long row = u * T + t;
+                const double *qt = q + row * d_k, *kt = k + row * d_k;
+                const double *vt = v + row * d_v, *gt = g + row * m;
+                const double *dOt = dO + row * d_v, *st = S + t * m;
+                const double *Kp = Ks + t * m * d_k, *Vp = Vs + t * m * d_v;
+                const double *Kn = Ks + (t + 1) * m * d_k, *Vn = Vs + (t + 1) * m * d_v;
+                double sds = 0.0;
+                for (c = 0; c < m; c++) {
+                    double acc = 0.0;
+                    for (x = 0; x < d_v; x++)
+                        acc += Vn[c * d_v + x] * dOt[x];
+                    ds[c] = acc;
+                    sds += st[c] * acc;
+                    for (x = 0; x < d_v; x++)
+                        dV[c * d_v + x] += st[c] * dOt[x];
+                }
+                for (c = 0; c < m; c++)
+                    dz[c] = st[c] * (ds[c] - sds);
+                for (x = 0; x < d_k; x++) {
+                    double acc = 0.0;
+                    for (c = 0; c < m; c++)
+                        acc += Kn[c * d_k + x] * dz[c];
+                    dq[row * d_k + x] = acc;
+                }
+                for (c = 0; c < m; c++)
+                    for (x = 0; x < d_k; x++)
+                        dK[c * d_k + x] += dz[c] * qt[x];
+                for (x = 0; x < d_k; x++)
+                    dk[row * d_k + x] = 0.0;
+                for (x = 0; x < d_v; x++)
+                    dv[row * d_v + x] = 0.0;
+                for (c = 0; c < m; c++) {
+                    double la = log_sigmoid(gt[c]) / tau;
+                    double a = exp(la), w = -expm1(la), da = 0.0;
+                    double sig_neg = exp(log_sigmoid(-gt[c]));
+                    for (x = 0; x < d_k; x++) {
+                        dk[row * d_k + x] += w * dK[c * d_k + x];
+                        da += dK[c * d_k + x] * (Kp[c * d_k + x] - kt[x]);
+                        dK[c * d_k + x] *= a;
+                    }
+                    for (x = 0; x < d_v; x++) {
+                        dv[row * d_v + x] += w * dV[c * d_v + x];
+                        da += dV[c * d_v + x] * (Vp[c * d_v + x] - vt[x]);
+                        dV[c * d_v + x] *= a;
+                    }
+                    dg[row * m + c] = da * a * sig_neg / tau;
+                }
+            }
+            if (dk0)
+                memcpy(dk0 + u * m * d_k, dK, (size_t)(m * d_k) * sizeof(double));
+            if (dv0)
+                memcpy(dv0 + u * m * d_v, dV, (size_t)(m * d_v) * sizeof(double));
+        }
+        free(Ks);
+        free(Vs);
+        free(S);
+        free(dK);
+        free(dV);
+        free(ds);
+        free(dz);
+    }
+    return err;
 }
 
 int oracle_max_threads(void)

@@ -12,6 +12,7 @@ import pytest
 import scipy.special
 
 from oracle import bruteforce, chunkwise
+from tests import test_oracle_bwd
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                    "oracle", "gsa_oracle.c")
@@ -43,6 +44,14 @@ MUTATIONS = [
     ("relu2_not_squared", "return x > 0.0 ? x * x : 0.0;", "return x > 0.0 ? x : 0.0;"),
     ("read_codes_shifted", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c], act + 1);"),
     ("read_of_scaled_scores", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c] * 0.5, act);"),
+    ("bwd_softmax_jacobian_unshifted", "dz[c] = st[c] * (ds[c] - sds);", "dz[c] = st[c] * ds[c];"),
+    ("bwd_read_of_previous_state", "acc += Vn[c * d_v + x] * dOt[x];", "acc += Vp[c * d_v + x] * dOt[x];"),
+    ("bwd_gate_of_new_state", "da += dK[c * d_k + x] * (Kp[c * d_k + x] - kt[x]);",
+     "da += dK[c * d_k + x] * (Kn[c * d_k + x] - kt[x]);"),
+    ("bwd_adjoint_decayed_by_write", "dK[c * d_k + x] *= a;", "dK[c * d_k + x] *= w;"),
+    ("bwd_gate_chain_without_alpha", "dg[row * m + c] = da * a * sig_neg / tau;",
+     "dg[row * m + c] = da * sig_neg / tau;"),
+    ("bwd_value_adjoint_after_read", "dV[c * d_v + x] += st[c] * dOt[x];", "dV[c * d_v + x] += 0.0;"),
 ]
 
 
@@ -58,6 +67,7 @@ def _build(tmp_path, text, name):
     lib.oracle_gla_fwd.argtypes = [P] * 7 + [L] * 5 + [D, I]
     lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
     lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
+    lib.oracle_gsa_bwd.argtypes = [P] * 15 + [L] * 6 + [D, I]
     return lib
 
 
@@ -143,7 +153,29 @@ def _pins_pass(lib):
         on, _, _ = _gsa(lib, q, k, v, g, k0, v0, act=act)
         oc, _, _ = chunkwise.gsa_fwd(q, k, v, g, k0, v0, tau=8.0, C=8, nonlinearity=name)
         ok &= _rel(on, oc) < 1e-12
+    # the backward against central differences of this library's forward
+    ok &= _bwd_pin(lib)
     return bool(ok)
+
+
+def _bwd_pin(lib):
+    def fwd(x, tau):
+        return _gsa(lib, x["q"], x["k"], x["v"], x["g"], x["k0"], x["v0"], tau=tau)
+
+    ok = True
+    for seed, T in ((3, 9), (4, 1)):
+        x, w = test_oracle_bwd.draw(1, 1, T, 5, 5, 4, seed=seed)
+        B, H, _, dk = x["q"].shape
+        dv, m = x["v"].shape[-1], x["g"].shape[-1]
+        gr = {n: np.empty_like(x[n]) for n in test_oracle_bwd.NAMES}
+        rc = lib.oracle_gsa_bwd(*(_p(x[n]) for n in "qkvg"), _p(w["o"]), _p(x["k0"]), _p(x["v0"]),
+                                _p(w["kf"]), _p(w["vf"]),
+                                *(_p(gr[n]) for n in test_oracle_bwd.NAMES), B, H, T, dk, dv, m,
+                                8.0, 1)
+        ok &= rc == 0
+        errs = test_oracle_bwd.directional_errors(fwd, gr, x, w, 8.0, seed=seed)
+        ok &= max(errs.values()) < 1e-7
+    return ok
 
 
 def test_unmutated_copy_passes(tmp_path):
