@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define GSA_ABI_VERSION 2
+#define GSA_ABI_VERSION 3
 
 typedef enum {
   GSA_OK = 0,
@@ -260,6 +260,39 @@ int gla_decode_supported(int dk, int dv, int dtype);
 int gla_decode_step(const void* q, const void* k, const void* v, const void* g, float* s, void* o,
                     int N, int H, int dk, int dv, float tau, int dtype, int gate_input, void* stream,
                     void* const* events);
+
+/*
+ * GSA backward (softmax read): the gradients of gsa_fwd's outputs (and final
+ * states) with respect to its inputs.  GSA Sec. 3.2-3.3 define the function;
+ * App. B the training scheme followed here: the two gated passes are
+ * differentiated in reverse order, the write intensity 1 - alpha collects the
+ * gradient of both passes, and the forget-gate gradient is a reversed
+ * cumulative sum over tokens of (pass outputs x their gradients - pass inputs
+ * x theirs); states are recomputed per chunk of 64 tokens, not stored.
+ *   q, k, g, v, k0, v0, tau, dtype   as for gsa_fwd (tau the same value)
+ *   d_o        [B,H,T,dv]   dtype    gradient of o
+ *   d_kf, d_vf [B,H,m,dk] / [B,H,m,dv] float32, nullable (zero): gradients
+ *              of the final states
+ *   d_q, d_k, d_v, d_g   like q, k, v, g   dtype   (written)
+ *   d_k0, d_v0 [B,H,m,dk] / [B,H,m,dv] float32, nullable: gradients of the
+ *              initial states (written when given)
+ *   workspace  device scratch of at least gsa_bwd_workspace_bytes(B, H, T,
+ *              dk, dv, m) bytes (else GSA_ERR_WORKSPACE), caller-owned; its
+ *              contents on entry do not matter.
+ * No output may overlap an input, the workspace or another output
+ * (GSA_ERR_ALIAS).  B * H <= 65535.  Compiled for (dk = dv, m) in {(128, 64),
+ * (128, 32), (64, 64), (64, 32)}, float32 and bf16 (gsa_bwd_supported).
+ * events: NULL or 4 hipEvent_t: [0, 1] stamp the forward token-walk kernel's
+ * dispatch, [2, 3] the reverse token-walk kernel's.
+ * Asynchronous on stream; status as for gsa_fwd.
+ */
+int gsa_bwd_supported(int dk, int dv, int m, int dtype);
+size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m);
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+            const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+            void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+            int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+            void* stream, void* const* events);
 
 /*
  * Calibration kernels for measurements: what this GPU sustains, reported by

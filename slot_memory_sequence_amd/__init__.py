@@ -76,6 +76,10 @@ lib.gsa_fwd_varlen.argtypes = [_P] * 5 + [_I, _I] + [_P] * 5 + [_I] * 4 + [_F, _
 lib.gsa_fwd_varlen_workspace_bytes.restype = _S
 lib.gsa_fwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 8
 lib.gsa_decode_step_ex.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _I, _P, _P]
+lib.gsa_bwd_supported.argtypes = [_I] * 4
+lib.gsa_bwd_workspace_bytes.argtypes = [_I] * 6
+lib.gsa_bwd_workspace_bytes.restype = _S
+lib.gsa_bwd.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -337,6 +341,45 @@ def gla_decode_step(q, k, v, g, s_state, *, tau=16.0, gate="logit", out=None, st
     if st:
         raise GsaError("gla_decode_step", st)
     return out
+
+
+def gsa_bwd_supported(dk, dv, m, dtype=DTYPE_BF16) -> bool:
+    return bool(lib.gsa_bwd_supported(dk, dv, m, dtype))
+
+
+def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m) -> int:
+    return int(lib.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m))
+
+
+def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
+            state_grads=False, workspace=None, stream=None, events=None):
+    """GSA backward (softmax read): the gradients of gsa_fwd(q, k, v, g, k0,
+    v0, tau=tau) given d_o [B,H,T,dv] (the gradient of o) and optional float32
+    d_kf [B,H,m,dk] / d_vf [B,H,m,dv] (those of the final states).
+    Returns (d_q, d_k, d_v, d_g, d_k0, d_v0); d_k0 / d_v0 (float32) are None
+    unless state_grads."""
+    torch = _torch()
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
+        _check(t, n, q.dtype)
+    for n, t in (("k0", k0), ("v0", v0), ("d_kf", d_kf), ("d_vf", d_vf)):
+        _check(t, n, torch.float32)
+    B, H, T, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    outs = [torch.empty_like(x) for x in (q, k, v, g)]
+    sg = [None, None]
+    if state_grads:
+        sg = [torch.empty((B, H, m, d), dtype=torch.float32, device=q.device) for d in (dk, dv)]
+    nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0), _ptr(d_kf),
+                     _ptr(d_vf), *(_ptr(x) for x in outs), _ptr(sg[0]), _ptr(sg[1]), B, H, T, dk,
+                     dv, m, float(tau), _dt(q), _ptr(workspace),
+                     0 if workspace is None else workspace.numel(), _stream(stream),
+                     _events(events))
+    if st:
+        raise GsaError("gsa_bwd", st)
+    return (*outs, sg[0], sg[1])
 
 
 # ------------------------------------------------------------ calibration

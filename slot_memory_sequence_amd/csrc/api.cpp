@@ -433,4 +433,62 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
   return hip_status();
 }
 
+size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1) return 0;
+  return gsa::gsa_bwd_ws_bytes((size_t)B * H, (size_t)T, dk, dv, m);
+}
+
+int gsa_bwd_supported(int dk, int dv, int m, int dtype) {
+  if (!dtype_ok(dtype)) return 0;
+  return gsa::gsa_bwd_dispatch(dtype, dk, dv, m, nullptr, true) == 0;
+}
+
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+            const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+            void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+            int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+            void* stream, void* const* events) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) ||
+      !std::isfinite(tau) || !dtype_ok(dtype))
+    return GSA_ERR_SHAPE;
+  if (!gsa_bwd_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)B * H;
+  if (units == 0) return GSA_OK;
+  if (units > 65535) return GSA_ERR_UNSUPPORTED;  // one grid row per unit
+  const size_t ntok = (size_t)units * T;
+  if (ntok > 0 && (!q || !k || !v || !g || !d_o || !d_q || !d_k || !d_v || !d_g))
+    return GSA_ERR_NULL;
+  const void* ptrs[] = {q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return GSA_ERR_ALIGN;
+  const size_t es = esize(dtype);
+  const size_t sk = (size_t)units * m * dk * 4, sv = (size_t)units * m * dv * 4;
+  const Range rq = rng(q, ntok * dk * es), rk = rng(k, ntok * dk * es), rv = rng(v, ntok * dv * es),
+              rg = rng(g, ntok * m * es), rdo = rng(d_o, ntok * dv * es);
+  const Range rk0 = rng(k0, sk), rv0 = rng(v0, sv), rkf = rng(d_kf, sk), rvf = rng(d_vf, sv);
+  const Range rdq = rng(d_q, ntok * dk * es), rdk = rng(d_k, ntok * dk * es),
+              rdv = rng(d_v, ntok * dv * es), rdg = rng(d_g, ntok * m * es);
+  const Range rdk0 = rng(d_k0, sk), rdv0 = rng(d_v0, sv);
+  const size_t need = T > 0 ? gsa::gsa_bwd_ws_bytes((size_t)units, (size_t)T, dk, dv, m) : 0;
+  const Range rws = rng(workspace, need);
+  const Range outs[] = {rdq, rdk, rdv, rdg, rdk0, rdv0, rws};
+  const Range ins[] = {rq, rk, rv, rg, rdo, rk0, rv0, rkf, rvf};
+  for (int i = 0; i < 7; i++) {
+    for (Range in : ins)
+      if (overlap(outs[i], in)) return GSA_ERR_ALIAS;
+    for (int j = i + 1; j < 7; j++)
+      if (overlap(outs[i], outs[j])) return GSA_ERR_ALIAS;
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
+  gsa::GsaBwdLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.d_o = d_o;
+  a.k0 = k0; a.v0 = v0; a.dkf = d_kf; a.dvf = d_vf;
+  a.dq = d_q; a.dk = d_k; a.dv = d_v; a.dg = d_g; a.dk0 = d_k0; a.dv0 = d_v0;
+  a.ws = (float*)workspace;
+  a.B = B; a.H = H; a.T = T; a.tau = tau; a.stream = stream; a.events = events;
+  (void)hipGetLastError();
+  if (gsa::gsa_bwd_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
+  return hip_status();
+}
+
 }  // extern "C"

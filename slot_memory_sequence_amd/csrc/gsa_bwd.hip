@@ -1,0 +1,611 @@
+// GSA backward: gradients of the chunked forward with respect to q, k, v, the
+// gate logits g and the initial slot states, given dO (and, optionally, the
+// gradients of the final states).
+//
+// Method: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling",
+// Sec. 3.2-3.3 (the per-slot gated recurrence and its gate) and App. B (the
+// training scheme: two GLA passes whose backward runs in reverse order, the
+// gradient of the shared write intensity summed over both passes, and the
+// forget-gate gradient formed from the products of each pass's inputs and
+// outputs with their gradients by a reversed cumulative sum; states are
+// recomputed rather than stored).
+//
+// Per unit (b, h), with alpha_t = sigmoid(g_t)^(1/tau), i_t = 1 - alpha_t,
+// z_t = Kt q_t (pass-1 output), s_t = softmax(z_t), o_t = Vt^T s_t:
+//   ds_t = Vt dO_t,  dz_t = s_t * (ds_t - s_t . ds_t),  dq_t = Kt^T dz_t
+//   adjoints (reverse in t): dVt = alpha_{t+1} dV_{t+1} + s_t dO_t^T,
+//                            dKt = alpha_{t+1} dK_{t+1} + dz_t q_t^T
+//   dk_t = dKt^T i_t,  dv_t = dVt^T i_t,  di_t = dKt k_t + dVt v_t
+//   with G_t = sum_{r<=t} log alpha_r, the loss depends on G_t through
+//   e^{G_t} on the reads of token t and e^{-G_t} on its writes, so
+//   dL/dG_t = z_t dz_t + s_t ds_t - i_t di_t (+ the final-state term at T),
+//   d log alpha_t = sum_{r>=t} dL/dG_r - alpha_t di_t,
+//   dg_t = d log alpha_t * sigmoid(-g_t) / tau.
+//
+// Five launches, chunks of C = 64 tokens, one workgroup per (chunk, unit):
+//   1. bwd_map       chunk state maps (the state a chunk builds from zero)
+//                    and chunk decays, by the token recurrence in fp32;
+//   2. bwd_scan<0>   chunk start states (forward scan of the maps);
+//   3. bwd_walk_fwd  per chunk from its start state, token by token:
+//                    z, s, ds, dz, dq, the reverse map of the chunk (what its
+//                    reads add to the adjoint of its start state), and the
+//                    per-token gate terms;
+//   4. bwd_scan<1>   adjoints at chunk ends (reverse scan of the reverse maps
+//                    from the final-state gradients); its carry out of chunk 0
+//                    is the gradient of the initial states;
+//   5. bwd_walk_rev  per chunk from its end adjoint, tokens in reverse: dk, dv
+//                    and the chunk-local reversed sums of dL/dG;
+//   6. bwd_gate      adds each chunk's carry (later chunks' sums and the
+//                    final-state term) and applies the gate's derivative.
+// The token walks keep both states (or both adjoints) of a unit in registers:
+// thread (slot group sg, column group cg) of a 16 x 16 grid owns M/16 slot
+// rows x D/16 columns of each, so that per-slot dot products are 16-lane row
+// reductions inside a wave and per-column sums over slots run over the four
+// slot groups of a wave and then, through LDS, over the four waves.
+#include "../../include/gsa.h"
+#include "common.hpp"
+#include "internal.hpp"
+#include "launch.hpp"
+
+namespace gsa {
+namespace bwd {
+
+constexpr int C = 64;    // chunk length
+constexpr int NT = 256;  // threads per workgroup: 4 waves, 16 x 16 thread grid
+
+template <int DK, int DV, int M>
+struct Shape {
+  static constexpr int SPT = M / 16;  // slot rows per thread
+  static constexpr int CK = DK / 16;  // key columns per thread
+  static constexpr int CV = DV / 16;  // value columns per thread
+  static constexpr int NE = M * (DK + DV);
+  static_assert(M % 16 == 0 && DK % 64 == 0 && DV % 64 == 0, "shape");
+};
+
+// N consecutive elements (N = 2, 4 or 8; 4 N-byte aligned for bf16, 4 N for
+// float) into fp32 registers
+template <int N>
+__device__ __forceinline__ void ldn(const float* p, float* o) {
+  if constexpr (N == 2) {
+    float2 x = *reinterpret_cast<const float2*>(p);
+    o[0] = x.x; o[1] = x.y;
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; j += 4) {
+      float4 x = *reinterpret_cast<const float4*>(p + j);
+      o[j] = x.x; o[j + 1] = x.y; o[j + 2] = x.z; o[j + 3] = x.w;
+    }
+  }
+}
+template <int N>
+__device__ __forceinline__ void ldn(const bf16_t* p, float* o) {
+  if constexpr (N == 2) {
+    uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __uint_as_float(x << 16); o[1] = __uint_as_float(x & 0xffff0000u);
+  } else if constexpr (N == 4) {
+    uint2 x = *reinterpret_cast<const uint2*>(p);
+    o[0] = __uint_as_float(x.x << 16); o[1] = __uint_as_float(x.x & 0xffff0000u);
+    o[2] = __uint_as_float(x.y << 16); o[3] = __uint_as_float(x.y & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; j += 8) {
+      uint4 x = *reinterpret_cast<const uint4*>(p + j);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        o[j + 2 * e] = __uint_as_float(w[e] << 16);
+        o[j + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+// sum over the four slot groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float sum_sg4(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float max_sg4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+struct Thread {
+  int l, w, cg, sg;
+  __device__ Thread() {
+    l = threadIdx.x & 63;
+    w = threadIdx.x >> 6;
+    cg = l & 15;
+    sg = w * 4 + (l >> 4);
+  }
+};
+
+// ------------------------------------------------------------ 1. maps
+// The state chunk p builds from a zero start, and its decay prod alpha.
+template <typename T, int DK, int DV, int M>
+__global__ void __launch_bounds__(NT)
+bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ gg,
+        float* __restrict__ st, float* __restrict__ dec, int T_, int P, float inv_tau) {
+  using S = Shape<DK, DV, M>;
+  const Thread th;
+  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  float K[S::SPT][S::CK], V[S::SPT][S::CV], cum[S::SPT];
+#pragma unroll
+  for (int i = 0; i < S::SPT; i++) {
+    cum[i] = 1.f;
+#pragma unroll
+    for (int j = 0; j < S::CK; j++) K[i][j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < S::CV; j++) V[i][j] = 0.f;
+  }
+  const int t0 = p * C, t1 = min(T_, t0 + C);
+  for (int t = t0; t < t1; t++) {
+    const size_t row = (size_t)u * T_ + t;
+    float gv[S::SPT], kv[S::CK], vv_[S::CV];
+    ldn<S::SPT>(gg + row * M + c0, gv);
+    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      float a, w;
+      gate_alpha_w(gv[i], inv_tau, a, w);
+      cum[i] *= a;
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) K[i][j] = a * K[i][j] + w * kv[j];
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) V[i][j] = a * V[i][j] + w * vv_[j];
+    }
+  }
+  float* base = st + ((size_t)u * P + p) * S::NE;
+#pragma unroll
+  for (int i = 0; i < S::SPT; i++) {
+    float* r = base + (size_t)(c0 + i) * (DK + DV);
+#pragma unroll
+    for (int j = 0; j < S::CK; j += 4)
+      *reinterpret_cast<f32x4*>(r + th.cg * S::CK + j) = f32x4{K[i][j], K[i][j + 1], K[i][j + 2], K[i][j + 3]};
+#pragma unroll
+    for (int j = 0; j < S::CV; j += 4)
+      *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
+          f32x4{V[i][j], V[i][j + 1], V[i][j + 2], V[i][j + 3]};
+    if (th.cg == 0) dec[((size_t)u * P + p) * M + c0 + i] = cum[i];
+  }
+}
+
+// ------------------------------------------------------------ 2./4. scans
+// One thread per (unit, float4 of a slot row), serial over the chunks.
+// REV = 0: slot p holds chunk p's map on entry and its start state on exit
+// (W starts at the initial states ka / va, nullable = zero).
+// REV = 1: slot p holds chunk p's reverse map on entry and, on exit, the
+// adjoint of the state at chunk p's end from later tokens (W starts at the
+// final-state gradients ka / va, nullable = zero); what is carried out of
+// chunk 0 is written to kout / vout (nullable).
+template <int DK, int DV, int M, int REV>
+__global__ void __launch_bounds__(256)
+bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __restrict__ ka,
+         const float* __restrict__ va, float* __restrict__ kout, float* __restrict__ vout, int units, int P) {
+  constexpr int NE = M * (DK + DV), BATCH = 8;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)units * (NE / 4)) return;
+  const int unit = (int)(gid / (NE / 4)), e = 4 * (int)(gid % (NE / 4));
+  const int c = e / (DK + DV), cl = e % (DK + DV);
+  const size_t ko = ((size_t)unit * M + c) * DK + cl, vo = ((size_t)unit * M + c) * DV + cl - DK;
+  f32x4 W = {0.f, 0.f, 0.f, 0.f};
+  if (cl < DK) {
+    if (ka) W = *reinterpret_cast<const f32x4*>(ka + ko);
+  } else {
+    if (va) W = *reinterpret_cast<const f32x4*>(va + vo);
+  }
+  f32x4* sl = reinterpret_cast<f32x4*>(ws + (size_t)unit * P * NE + e);
+  const float* dc = dec + (size_t)unit * P * M + c;
+  for (int n0 = 0; n0 < P; n0 += BATCH) {
+    f32x4 x[BATCH];
+    float d[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+      if (n0 + i < P) {
+        const int p = REV ? P - 1 - (n0 + i) : n0 + i;
+        x[i] = sl[(size_t)p * (NE / 4)];
+        d[i] = dc[(size_t)p * M];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+      if (n0 + i < P) {
+        const int p = REV ? P - 1 - (n0 + i) : n0 + i;
+        sl[(size_t)p * (NE / 4)] = W;
+        W = d[i] * W + x[i];
+      }
+    }
+  }
+  if (REV) {
+    if (cl < DK) {
+      if (kout) *reinterpret_cast<f32x4*>(kout + ko) = W;
+    } else {
+      if (vout) *reinterpret_cast<f32x4*>(vout + vo) = W;
+    }
+  }
+}
+
+// ------------------------------------------------------------ 3. forward walk
+// From chunk p's start state, token by token: the reads z, s, ds, dz, dq, the
+// reverse map (sum over the chunk of e^{G_t} dz_t q_t^T and e^{G_t} s_t dO_t^T,
+// G from the chunk start), and per token s, dz and z dz + s ds.  The chunk
+// holding the last token also forms the final-state term dkf . K_T + dvf . V_T
+// per slot (zero without final-state gradients).
+template <typename T, int DK, int DV, int M>
+__global__ void __launch_bounds__(NT)
+bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
+             const T* __restrict__ gg, const T* __restrict__ dOo, const float* __restrict__ st,
+             const float* __restrict__ dkf, const float* __restrict__ dvf, T* __restrict__ dq,
+             float* __restrict__ xu, float* __restrict__ sw, float* __restrict__ dzw,
+             float* __restrict__ hw, float* __restrict__ fs, int T_, int P, float inv_tau) {
+  using S = Shape<DK, DV, M>;
+  __shared__ float red[2][4][3];
+  __shared__ float dqb[2][4][DK];
+  const Thread th;
+  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  float K[S::SPT][S::CK], V[S::SPT][S::CV], XK[S::SPT][S::CK], XV[S::SPT][S::CV], cum[S::SPT];
+  {
+    const float* base = st + ((size_t)u * P + p) * S::NE;
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      const float* r = base + (size_t)(c0 + i) * (DK + DV);
+      ldn<S::CK>(r + th.cg * S::CK, K[i]);
+      ldn<S::CV>(r + DK + th.cg * S::CV, V[i]);
+      cum[i] = 1.f;
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) XK[i][j] = 0.f;
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) XV[i][j] = 0.f;
+    }
+  }
+  const int t0 = p * C, t1 = min(T_, t0 + C);
+  int n = 0;
+  for (int t = t0; t < t1; t++, n++) {
+    const int b = n & 1;
+    const size_t row = (size_t)u * T_ + t;
+    float gv[S::SPT], qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
+    ldn<S::SPT>(gg + row * M + c0, gv);
+    ldn<S::CK>(qq + row * DK + th.cg * S::CK, qv);
+    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
+    ldn<S::CV>(dOo + row * DV + th.cg * S::CV, dov);
+    float z[S::SPT], ds[S::SPT];
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      float a, w;
+      gate_alpha_w(gv[i], inv_tau, a, w);
+      cum[i] *= a;
+      float zp = 0.f, dp = 0.f;
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) {
+        K[i][j] = a * K[i][j] + w * kv[j];
+        zp += K[i][j] * qv[j];
+      }
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) {
+        V[i][j] = a * V[i][j] + w * vv_[j];
+        dp += V[i][j] * dov[j];
+      }
+      z[i] = sum16(zp);
+      ds[i] = sum16(dp);
+    }
+    // softmax statistics of this wave's slots: max, sum of e^{z - max}, and
+    // sum of e^{z - max} ds; then combined over the four waves
+    float mx = z[0];
+#pragma unroll
+    for (int i = 1; i < S::SPT; i++) mx = fmaxf(mx, z[i]);
+    mx = max_sg4(mx);
+    float se = 0.f, sd = 0.f;
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      const float e = __expf(z[i] - mx);
+      se += e;
+      sd += e * ds[i];
+    }
+    se = sum_sg4(se);
+    sd = sum_sg4(sd);
+    if (th.l == 0) {
+      red[b][th.w][0] = mx;
+      red[b][th.w][1] = se;
+      red[b][th.w][2] = sd;
+    }
+    __syncthreads();
+    if (n > 0 && threadIdx.x < DK) {  // dq of the previous token
+      const float x = dqb[b ^ 1][0][threadIdx.x] + dqb[b ^ 1][1][threadIdx.x] + dqb[b ^ 1][2][threadIdx.x] +
+                      dqb[b ^ 1][3][threadIdx.x];
+      dq[(row - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
+    }
+    float Mx = red[b][0][0];
+#pragma unroll
+    for (int x = 1; x < 4; x++) Mx = fmaxf(Mx, red[b][x][0]);
+    float Se = 0.f, Sd = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; x++) {
+      const float f = __expf(red[b][x][0] - Mx);
+      Se += red[b][x][1] * f;
+      Sd += red[b][x][2] * f;
+    }
+    const float inv = 1.f / Se, dbar = Sd * inv;
+    float s[S::SPT], dz[S::SPT];
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      s[i] = __expf(z[i] - Mx) * inv;
+      dz[i] = s[i] * (ds[i] - dbar);
+    }
+    // dq partial sums over this wave's slots
+#pragma unroll
+    for (int j = 0; j < S::CK; j++) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) x += dz[i] * K[i][j];
+      x = sum_sg4(x);
+      if ((th.l >> 4) == 0) dqb[b][th.w][th.cg * S::CK + j] = x;
+    }
+    if (th.cg == 0) {
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) {
+        sw[row * M + c0 + i] = s[i];
+        dzw[row * M + c0 + i] = dz[i];
+        hw[row * M + c0 + i] = z[i] * dz[i] + s[i] * ds[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      const float xs = cum[i] * dz[i], xv = cum[i] * s[i];
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) XK[i][j] += xs * qv[j];
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) XV[i][j] += xv * dov[j];
+    }
+  }
+  __syncthreads();
+  if (n > 0 && threadIdx.x < DK) {
+    const int b = (n - 1) & 1;
+    const float x = dqb[b][0][threadIdx.x] + dqb[b][1][threadIdx.x] + dqb[b][2][threadIdx.x] + dqb[b][3][threadIdx.x];
+    dq[((size_t)u * T_ + t1 - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
+  }
+  float* base = xu + ((size_t)u * P + p) * S::NE;
+#pragma unroll
+  for (int i = 0; i < S::SPT; i++) {
+    float* r = base + (size_t)(c0 + i) * (DK + DV);
+#pragma unroll
+    for (int j = 0; j < S::CK; j += 4)
+      *reinterpret_cast<f32x4*>(r + th.cg * S::CK + j) = f32x4{XK[i][j], XK[i][j + 1], XK[i][j + 2], XK[i][j + 3]};
+#pragma unroll
+    for (int j = 0; j < S::CV; j += 4)
+      *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
+          f32x4{XV[i][j], XV[i][j + 1], XV[i][j + 2], XV[i][j + 3]};
+  }
+  if (p == P - 1) {
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      float x = 0.f;
+      if (dkf) {
+        float d[S::CK];
+        ldn<S::CK>(dkf + ((size_t)u * M + c0 + i) * DK + th.cg * S::CK, d);
+#pragma unroll
+        for (int j = 0; j < S::CK; j++) x += d[j] * K[i][j];
+      }
+      if (dvf) {
+        float d[S::CV];
+        ldn<S::CV>(dvf + ((size_t)u * M + c0 + i) * DV + th.cg * S::CV, d);
+#pragma unroll
+        for (int j = 0; j < S::CV; j++) x += d[j] * V[i][j];
+      }
+      x = sum16(x);
+      if (th.cg == 0) fs[(size_t)u * M + c0 + i] = x;
+    }
+  }
+}
+
+// ------------------------------------------------------------ 5. reverse walk
+// From the adjoint at chunk p's end, tokens in reverse: dk, dv, and per token
+// the chunk-local reversed sum of dL/dG minus alpha di (written over z dz +
+// s ds); the chunk's total goes to tot.
+template <typename T, int DK, int DV, int M>
+__global__ void __launch_bounds__(NT)
+bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
+             const T* __restrict__ gg, const T* __restrict__ dOo, const float* __restrict__ xu,
+             const float* __restrict__ sw, const float* __restrict__ dzw, float* __restrict__ hw,
+             float* __restrict__ tot, T* __restrict__ dk, T* __restrict__ dv, int T_, int P, float inv_tau) {
+  using S = Shape<DK, DV, M>;
+  __shared__ float kvb[2][4][DK + DV];
+  const Thread th;
+  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  float AK[S::SPT][S::CK], AV[S::SPT][S::CV], R[S::SPT];
+  {
+    const float* base = xu + ((size_t)u * P + p) * S::NE;
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      const float* r = base + (size_t)(c0 + i) * (DK + DV);
+      ldn<S::CK>(r + th.cg * S::CK, AK[i]);
+      ldn<S::CV>(r + DK + th.cg * S::CV, AV[i]);
+      R[i] = 0.f;
+    }
+  }
+  const int t0 = p * C, t1 = min(T_, t0 + C);
+  int n = 0;
+  for (int t = t1 - 1; t >= t0; t--, n++) {
+    const int b = n & 1;
+    const size_t row = (size_t)u * T_ + t;
+    float gv[S::SPT], sv[S::SPT], dzv[S::SPT], hv[S::SPT];
+    float qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
+    ldn<S::SPT>(gg + row * M + c0, gv);
+    ldn<S::SPT>(sw + row * M + c0, sv);
+    ldn<S::SPT>(dzw + row * M + c0, dzv);
+    ldn<S::SPT>(hw + row * M + c0, hv);
+    ldn<S::CK>(qq + row * DK + th.cg * S::CK, qv);
+    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
+    ldn<S::CV>(dOo + row * DV + th.cg * S::CV, dov);
+    float a[S::SPT], w[S::SPT], di[S::SPT];
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      gate_alpha_w(gv[i], inv_tau, a[i], w[i]);
+      float pk = 0.f, pv = 0.f;
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) {
+        AK[i][j] += dzv[i] * qv[j];
+        pk += AK[i][j] * kv[j];
+      }
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) {
+        AV[i][j] += sv[i] * dov[j];
+        pv += AV[i][j] * vv_[j];
+      }
+      di[i] = sum16(pk) + sum16(pv);
+    }
+#pragma unroll
+    for (int j = 0; j < S::CK; j++) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) x += w[i] * AK[i][j];
+      x = sum_sg4(x);
+      if ((th.l >> 4) == 0) kvb[b][th.w][th.cg * S::CK + j] = x;
+    }
+#pragma unroll
+    for (int j = 0; j < S::CV; j++) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) x += w[i] * AV[i][j];
+      x = sum_sg4(x);
+      if ((th.l >> 4) == 0) kvb[b][th.w][DK + th.cg * S::CV + j] = x;
+    }
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+#pragma unroll
+      for (int j = 0; j < S::CK; j++) AK[i][j] *= a[i];
+#pragma unroll
+      for (int j = 0; j < S::CV; j++) AV[i][j] *= a[i];
+      R[i] += hv[i] - w[i] * di[i];
+    }
+    if (th.cg == 0) {
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) hw[row * M + c0 + i] = R[i] - a[i] * di[i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < DK + DV; e += NT) {
+      const float x = kvb[b][0][e] + kvb[b][1][e] + kvb[b][2][e] + kvb[b][3][e];
+      if (e < DK) dk[row * DK + e] = Elem<T>::from_f(x);
+      else dv[row * DV + e - DK] = Elem<T>::from_f(x);
+    }
+  }
+  if (th.cg == 0) {
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) tot[((size_t)u * P + p) * M + c0 + i] = R[i];
+  }
+}
+
+// ------------------------------------------------------------ 6. gate
+// dg = (chunk-local reversed sum + carry) * sigmoid(-g) / tau, the carry of
+// chunk p being the final-state term plus the totals of chunks p+1 .. P-1.
+template <typename T, int M>
+__global__ void __launch_bounds__(256)
+bwd_gate(const T* __restrict__ gg, const float* __restrict__ hw, const float* __restrict__ tot,
+         const float* __restrict__ fs, T* __restrict__ dg, int T_, int P, float inv_tau) {
+  __shared__ float carry[M];
+  const int p = blockIdx.x, u = blockIdx.y;
+  if (threadIdx.x < M) {
+    float c = fs[(size_t)u * M + threadIdx.x];
+    const float* tp = tot + (size_t)u * P * M + threadIdx.x;
+#pragma unroll 8
+    for (int x = p + 1; x < P; x++) c += tp[(size_t)x * M];
+    carry[threadIdx.x] = c;
+  }
+  __syncthreads();
+  const int t0 = p * C, n = min(C, T_ - t0) * M;
+  const size_t base = ((size_t)u * T_ + t0) * M;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int c = e % M;
+    const float gv = Elem<T>::to_f(gg[base + e]);
+    const float sneg = 1.f / (1.f + __expf(gv));  // sigmoid(-g): 0 at +inf, 1 at -inf
+    dg[base + e] = Elem<T>::from_f((hw[base + e] + carry[c]) * sneg * inv_tau);
+  }
+}
+
+// ------------------------------------------------------------ host side
+struct Ws {
+  float *st, *xu, *dec, *sw, *dzw, *hw, *tot, *fs;
+};
+
+// floats of workspace for U units of T tokens
+inline size_t ws_floats(size_t U, size_t T, int dk, int dv, int m) {
+  const size_t P = (T + C - 1) / C;
+  return 2 * U * P * (size_t)m * (dk + dv) + 2 * U * P * m + 3 * U * T * m + U * m;
+}
+
+inline Ws carve(float* w, size_t U, size_t T, int dk, int dv, int m) {
+  const size_t P = (T + C - 1) / C, NE = (size_t)m * (dk + dv);
+  Ws s;
+  s.st = w;
+  s.xu = s.st + U * P * NE;
+  s.dec = s.xu + U * P * NE;
+  s.tot = s.dec + U * P * m;
+  s.sw = s.tot + U * P * m;
+  s.dzw = s.sw + U * T * m;
+  s.hw = s.dzw + U * T * m;
+  s.fs = s.hw + U * T * m;
+  return s;
+}
+
+template <typename T, int DK, int DV, int M>
+int launch(const GsaBwdLaunch& a) {
+  const int U = a.B * a.H, Tn = a.T, P = (Tn + C - 1) / C;
+  const float inv_tau = 1.0f / a.tau;
+  if (Tn == 0) {  // no tokens: the initial states' gradients are the final ones'
+    state_copy(a.dk0, a.dkf, (size_t)U * M * DK, a.stream);
+    state_copy(a.dv0, a.dvf, (size_t)U * M * DV, a.stream);
+    record_event(a.events, 0, a.stream);
+    record_event(a.events, 1, a.stream);
+    record_event(a.events, 2, a.stream);
+    record_event(a.events, 3, a.stream);
+    return 0;
+  }
+  const Ws w = carve(a.ws, U, Tn, DK, DV, M);
+  const T *q = (const T*)a.q, *k = (const T*)a.k, *v = (const T*)a.v, *g = (const T*)a.g,
+          *dO = (const T*)a.d_o;
+  hipStream_t s = (hipStream_t)a.stream;
+  const dim3 grid(P, U);
+  const long long ne = (long long)U * M * (DK + DV) / 4;
+  const dim3 sgrid((unsigned)((ne + 255) / 256));
+  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), 0, s, k, v, g, w.st, w.dec, Tn, P, inv_tau);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, a.k0, a.v0,
+                     (float*)nullptr, (float*)nullptr, U, P);
+  launch_timed(bwd_walk_fwd<T, DK, DV, M>, grid, dim3(NT), 0, a.stream, a.events, 0, 1, q, k, v, g, dO,
+               (const float*)w.st, a.dkf, a.dvf, (T*)a.dq, w.xu, w.sw, w.dzw, w.hw, w.fs, Tn, P, inv_tau);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, a.dkf, a.dvf,
+                     a.dk0, a.dv0, U, P);
+  launch_timed(bwd_walk_rev<T, DK, DV, M>, grid, dim3(NT), 0, a.stream, a.events, 2, 3, q, k, v, g, dO,
+               (const float*)w.xu, (const float*)w.sw, (const float*)w.dzw, w.hw, w.tot, (T*)a.dk, (T*)a.dv,
+               Tn, P, inv_tau);
+  hipLaunchKernelGGL((bwd_gate<T, M>), grid, dim3(256), 0, s, g, (const float*)w.hw, (const float*)w.tot,
+                     (const float*)w.fs, (T*)a.dg, Tn, P, inv_tau);
+  return 0;
+}
+
+}  // namespace bwd
+
+size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m) {
+  return bwd::ws_floats(units, T, dk, dv, m) * sizeof(float);
+}
+
+#define GSA_BWD_CASE(TY, DT, DK_, DV_, M_)                                    \
+  if (dtype == DT && dk == DK_ && dv == DV_ && m == M_)                       \
+    return query ? 0 : bwd::launch<TY, DK_, DV_, M_>(*a);
+
+int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query) {
+  GSA_BWD_CASE(bf16_t, 1, 128, 128, 64)
+  GSA_BWD_CASE(bf16_t, 1, 64, 64, 32)
+  GSA_BWD_CASE(bf16_t, 1, 128, 128, 32)
+  GSA_BWD_CASE(bf16_t, 1, 64, 64, 64)
+  GSA_BWD_CASE(float, 0, 128, 128, 64)
+  GSA_BWD_CASE(float, 0, 64, 64, 32)
+  GSA_BWD_CASE(float, 0, 128, 128, 32)
+  GSA_BWD_CASE(float, 0, 64, 64, 64)
+  return -1;
+}
+
+}  // namespace gsa

@@ -77,4 +77,21 @@ int gla_decode_dispatch(int dtype, int dk, int dv, const GlaDecodeLaunch* a, boo
 // copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
 void state_copy(float* dst, const float* src, size_t n, void* stream);
 
+// GSA backward (softmax read): gradients of q, k, v, g (I/O dtype) and of the
+// initial states (fp32, nullable), given d_o and the nullable final-state
+// gradients dkf / dvf.  ws: gsa_bwd_ws_bytes(B * H, T, dk, dv, m) bytes.
+struct GsaBwdLaunch {
+  const void *q, *k, *v, *g, *d_o;
+  const float *k0, *v0, *dkf, *dvf;
+  void *dq, *dk, *dv, *dg;
+  float *dk0, *dv0;
+  float* ws;
+  int B, H, T;
+  float tau;
+  void* stream;
+  void* const* events;  // nullable: 4 hipEvent_t around the two token-walk kernels
+};
+size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m);
+int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query);
+
 }  // namespace gsa

@@ -88,6 +88,18 @@ def gsa_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
     return out
 
 
+def gsa_grad_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, final_std=None):
+    """Upstream gradients for a GSA backward: dO ~ N(0,1) [B,H,T,dv] in dtype;
+    optional final-state gradients dKf [B,H,m,dk], dVf [B,H,m,dv] ~ N(0,
+    final_std) stored as float32."""
+    rng = np.random.default_rng(seed)
+    out = dict(do=stored(_normal(rng, (B, H, T, dv)), dtype), dkf=None, dvf=None)
+    if final_std is not None:
+        out["dkf"] = stored(_normal(rng, (B, H, m, dk)) * final_std, "f32")
+        out["dvf"] = stored(_normal(rng, (B, H, m, dv)) * final_std, "f32")
+    return out
+
+
 def gla_inputs(B, H, T, dk, dv, dtype="bf16", seed=0, qkv_scale=None,
                g_shift=0.0, init_std=None, log_decay_scale=None):
     """q,k ~ N(0,1)*qkv_scale [B,H,T,dk]; v [B,H,T,dv]; g ~ N(0,1)+g_shift

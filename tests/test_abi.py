@@ -29,7 +29,7 @@ def test_header_symbols_exported(gsa):
     assert {"gsa_fwd", "gla_fwd", "gsa_decode_step", "gsa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(gsa.lib, n), "missing export: " + n
-    assert gsa.lib.gsa_abi_version() == 2
+    assert gsa.lib.gsa_abi_version() == 3
 
 
 def test_status_strings(gsa):
@@ -235,3 +235,39 @@ def test_package_has_no_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 for bad in ("import oracle", "from oracle", "liboracle", "oracle_gsa", "oracle_gla"):
                     assert bad not in text, (f, bad)
+
+
+def test_bwd_validation(gsa):
+    """gsa_bwd: shape, support, null, alignment, aliasing and workspace checks."""
+    f = gsa.lib.gsa_bwd
+    P = ctypes.c_void_p
+    ws = FAKE + 0x10000000
+    need = gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64)
+    assert need > 0 and gsa.gsa_bwd_workspace_bytes(1, 1, 0, 128, 128, 64) > 0
+    assert gsa.gsa_bwd_workspace_bytes(-1, 1, 64, 128, 128, 64) == 0
+    assert gsa.gsa_bwd_supported(128, 128, 64, 1) and gsa.gsa_bwd_supported(64, 64, 32, 0)
+    assert not gsa.gsa_bwd_supported(96, 96, 64, 1) and not gsa.gsa_bwd_supported(128, 128, 48, 1)
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, g=FAKE + 0x300000,
+                 do=FAKE + 0x400000, k0=None, v0=None, dkf=None, dvf=None, dq=FAKE + 0x500000,
+                 dk=FAKE + 0x600000, dv=FAKE + 0x700000, dg=FAKE + 0x800000, dk0=None, dv0=None,
+                 B=1, H=1, T=64, d_k=128, d_v=128, m=64, tau=8.0, dtype=1, ws=ws, wsb=need)
+        a.update(kw)
+        return f(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["do"]), P(a["k0"]), P(a["v0"]),
+                 P(a["dkf"]), P(a["dvf"]), P(a["dq"]), P(a["dk"]), P(a["dv"]), P(a["dg"]),
+                 P(a["dk0"]), P(a["dv0"]), a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["m"],
+                 a["tau"], a["dtype"], P(a["ws"]), a["wsb"], None, None)
+
+    assert call(tau=0.0) == 2 and call(tau=float("inf")) == 2 and call(T=-1) == 2
+    assert call(dtype=5) == 2
+    assert call(d_k=96, d_v=96) == 4
+    assert call(B=65536) == 4
+    assert call(B=0) == 0                               # nothing to do
+    assert call(q=None) == 1 and call(do=None) == 1 and call(dg=None) == 1
+    assert call(dq=FAKE + 0x500008) == 3
+    assert call(dq=FAKE + 0x20) == 7                    # d_q overlaps q
+    assert call(dk=FAKE + 0x500000) == 7                # d_k overlaps d_q
+    assert call(dk0=FAKE + 0x10) == 7                   # d_k0 overlaps q
+    assert call(ws=FAKE + 0x400000) == 7                # workspace overlaps d_o
+    assert call(wsb=need - 16) == 5 and call(ws=None) == 5

@@ -1,0 +1,174 @@
+"""GPU parity of the GSA backward (gsa_bwd, through the C ABI) against the
+float64 oracle's reverse-mode differentiation of the token recurrence, on the
+same seeded stored inputs.
+
+Bar (max |x - y| / max |y| per gradient tensor): 1e-4 for float32 inputs,
+2e-2 for bfloat16 inputs (fp32 states and accumulation, bf16 gradients out);
+the initial-state gradients (always float32) are held to the input dtype's
+bar as well.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dg", "dk0", "dv0")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def gsa(torch):
+    import slot_memory_sequence_amd as m
+    return m
+
+
+def _opt(x):
+    return None if x is None else x.f64
+
+
+def _run(gsa, torch, inp, gi, tau):
+    dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
+    ddev = {n: to_dev(gi[n], torch) for n in ("do", "dkf", "dvf")}
+    out = gsa.gsa_bwd(dev["q"], dev["k"], dev["v"], dev["g"], ddev["do"], dev["k0"], dev["v0"],
+                      ddev["dkf"], ddev["dvf"], tau=tau, state_grads=True)
+    torch.cuda.synchronize()
+    return dict(zip(GRADS, out))
+
+
+def _ref(inp, gi, tau, units=None):
+    """The oracle on all units, or on the listed flat unit indices."""
+    def sel(x):
+        if x is None:
+            return None
+        a = x.f64
+        if units is None:
+            return a
+        return a.reshape(-1, *a.shape[2:])[units][:, None]
+    return oracle.gsa_bwd(*(sel(inp[n]) for n in "qkvg"), sel(gi["do"]), sel(inp["k0"]),
+                          sel(inp["v0"]), sel(gi["dkf"]), sel(gi["dvf"]), tau=tau,
+                          nthreads=oracle.max_threads())
+
+
+def _compare(got, ref, dtype, label, units=None):
+    errs = {}
+    for n in GRADS:
+        x = to_np(got[n])
+        if units is not None:
+            x = x.reshape(-1, *x.shape[2:])[units][:, None]
+        errs[n] = rel_err(x, ref[n])
+    print("gsa_bwd %s: %s" % (label, " ".join("%s %.2e" % kv for kv in errs.items())))
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+def _check(gsa, torch, B, H, T, d, m, dtype, init, final, tau=8.0, seed=0, edit=None):
+    inp = synth.gsa_inputs(B, H, T, d, d, m, dtype=dtype, seed=seed,
+                           init_std=0.1 if init else None)
+    if edit:
+        edit(inp)
+    gi = synth.gsa_grad_inputs(B, H, T, d, d, m, dtype=dtype, seed=seed + 1000,
+                               final_std=1.0 if final else None)
+    got = _run(gsa, torch, inp, gi, tau)
+    _compare(got, _ref(inp, gi, tau), dtype,
+             "B%d H%d T%d d%d m%d %s init=%s final=%s" % (B, H, T, d, m, dtype, init, final))
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_bwd_lengths(gsa, torch, T, dtype, d, m):
+    """One token, a partial chunk, an exact chunk, a ragged tail, several chunks."""
+    _check(gsa, torch, 2, 2, T, d, m, dtype, init=True, final=True, seed=T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,m", [(128, 64), (64, 32), (128, 32), (64, 64)])
+def test_bwd_shapes(gsa, torch, dtype, d, m):
+    _check(gsa, torch, 1, 3, 150, d, m, dtype, init=True, final=True, seed=d + m)
+
+
+@pytest.mark.parametrize("init,final", [(False, False), (True, False), (False, True)])
+def test_bwd_optional_states(gsa, torch, init, final):
+    """Zero initial states and / or no final-state gradients."""
+    _check(gsa, torch, 2, 2, 130, 128, 64, "bf16", init=init, final=final, seed=7)
+
+
+@pytest.mark.parametrize("tau", [1.0, 16.0])
+def test_bwd_tau(gsa, torch, tau):
+    _check(gsa, torch, 1, 2, 100, 64, 32, "f32", init=True, final=True, tau=tau, seed=9)
+
+
+def _extreme(inp):
+    x = inp["g"].f64.copy()
+    x[..., 3, :] = -np.inf          # reset: alpha = 0
+    x[..., 70:75, 2] = np.inf       # frozen slot: alpha = 1, nothing written
+    x[..., 100, :5] = -30.0
+    x[..., 130:140, 7] = 30.0
+    x[..., 200:260, 1] = -np.inf
+    inp["g"] = synth.stored(x, inp["g"].dtype)
+
+
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_bwd_extreme_gates(gsa, torch, dtype, d, m):
+    """Gates at +-inf and +-30: resets, frozen slots and near-saturated
+    decays inside and across chunks."""
+    _check(gsa, torch, 1, 2, 300, d, m, dtype, init=True, final=True, seed=13, edit=_extreme)
+
+
+def test_bwd_empty_sequence(gsa, torch):
+    """T = 0: the initial-state gradients are the final-state gradients."""
+    B, H, d, m = 2, 3, 128, 64
+    gi = synth.gsa_grad_inputs(B, H, 1, d, d, m, dtype="bf16", seed=3, final_std=1.0)
+    empty = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    ge = torch.empty((B, H, 0, m), dtype=torch.bfloat16, device="cuda")
+    dkf, dvf = to_dev(gi["dkf"], torch), to_dev(gi["dvf"], torch)
+    out = gsa.gsa_bwd(empty, empty, empty, ge, empty, None, None, dkf, dvf, state_grads=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[4], dkf) and torch.equal(out[5], dvf)
+
+
+def test_bwd_matches_chunkwise_forward_outputs(gsa, torch):
+    """The backward recomputes the forward from chunk states of its own; the
+    gradient of <dO, o> along q must equal what the forward kernels give by a
+    central difference in float32 (a check independent of the oracle's
+    backward)."""
+    B, H, T, d, m = 1, 2, 200, 64, 32
+    inp = synth.gsa_inputs(B, H, T, d, d, m, dtype="f32", seed=17, init_std=0.1)
+    gi = synth.gsa_grad_inputs(B, H, T, d, d, m, dtype="f32", seed=18)
+    dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
+    do = to_dev(gi["do"], torch)
+    dq = gsa.gsa_bwd(dev["q"], dev["k"], dev["v"], dev["g"], do, dev["k0"], dev["v0"])[0]
+    u = torch.randn(dev["q"].shape, generator=torch.Generator(device="cuda").manual_seed(1),
+                    device="cuda")
+    eps = 1e-2
+
+    def L(qx):
+        o = gsa.gsa_fwd(qx, dev["k"], dev["v"], dev["g"], dev["k0"], dev["v0"])[0]
+        return float((o.double() * do.double()).sum())
+    num = (L(dev["q"] + eps * u) - L(dev["q"] - eps * u)) / (2 * eps)
+    ana = float((dq.double() * u.double()).sum())
+    print("directional dq: %.6e vs %.6e" % (ana, num))
+    assert abs(ana - num) <= 5e-3 * abs(num)
+
+
+def test_bwd_training_shape_sampled(gsa, torch):
+    """The training-shape workload (B8 H4 T2048 d128 m64, bf16) in the launch
+    configuration the benchmark times; five units against the oracle."""
+    w = synth.WORKLOADS["gsa_bf16_train_T2048"]
+    inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                           seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
+                           init_std=w["init_std"])
+    gi = synth.gsa_grad_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                               seed=1)
+    got = _run(gsa, torch, inp, gi, w["tau"])
+    units = [0, 7, 13, 22, w["B"] * w["H"] - 1]
+    _compare(got, _ref(inp, gi, w["tau"], units), "bf16", "B8 H4 T2048 sampled", units)
