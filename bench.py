@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_VALU_TFLOPS = 157.3
 
 
 def log(*a):
@@ -107,6 +108,17 @@ def gsa_alg(B, H, T, dk, dv, m, C, dtype_bytes, init_state=False, final_state=Fa
 def gla_alg(B, H, T, dk, dv, C, dtype_bytes):
     th = B * H * T
     return th * ((C + 1) * (dk + dv) + 4 * dk * dv), th * (3 * dk + 2 * dv) * dtype_bytes
+
+
+def gsa_bwd_alg(B, H, T, dk, dv, m, dtype_bytes):
+    """Per launch: fp32 vector flops of the forward token walk (state
+    updates, the two reads, dq and the reverse maps: 2 m (4 dk + 3 dv) per
+    token and head) and of the reverse walk (adjoint updates, the two gate
+    dots, dk, dv, the decay: 7 m (dk + dv)); and the backward's algorithmic
+    HBM bytes: q, k, v, g, dO read and dq, dk, dv, dg written once."""
+    th = B * H * T
+    return (th * 2 * m * (4 * dk + 3 * dv), th * 7 * m * (dk + dv),
+            th * (4 * dk + 3 * dv + 2 * m) * dtype_bytes)
 
 
 def dev_sets(torch, inp, names, nsets):
@@ -297,6 +309,43 @@ def bench_gla_decode(torch, gsa, ev, steps, warmup):
             "steps_per_s": round(steps / wall, 1), "roofline": r}
 
 
+def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd"):
+    """The GSA backward at the training shape (B8 H4 T2048, bf16), zero
+    initial states and no final-state gradients, dO ~ N(0, 1); two input sets
+    rotated."""
+    import synth
+    B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
+    inp = synth.gsa_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=0, qkv_scale=w["qkv_scale"],
+                           g_shift=w["g_shift"], init_std=w["init_std"])
+    inp["do"] = synth.gsa_grad_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=1)["do"]
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do"], 2)
+    outs = [tuple(torch.empty_like(s[n]) for n in "qkvg") for s in sets]
+    ws = torch.empty(gsa.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m), dtype=torch.uint8, device="cuda")
+
+    def call(s, events):
+        i = next(j for j, x in enumerate(sets) if x is s)
+        gsa.gsa_bwd(s["q"], s["k"], s["v"], s["g"], s["do"], tau=w["tau"], out=outs[i], workspace=ws,
+                    events=events)
+
+    wall, ph = time_op(torch, ev, call, sets, steps, warmup)
+    t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
+    f_f, f_r, nbytes = gsa_bwd_alg(B, H, T, dk, dv, m, 2)
+    kern, fl, t = ("bwd_walk_fwd", f_f, t_f) if t_f >= t_r else ("bwd_walk_rev", f_r, t_r)
+    ach = fl / (t * 1e-3) / 1e12
+    t_op = wall / steps * 1e3
+    return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
+            "ms_per_step": round(t_op, 4),
+            "ms_kernels": {"bwd_walk_fwd": round(t_f, 4), "bwd_walk_rev": round(t_r, 4)},
+            "walk_tflops": {"bwd_walk_fwd": round(f_f / (t_f * 1e-3) / 1e12, 2),
+                            "bwd_walk_rev": round(f_r / (t_r * 1e-3) / 1e12, 2)},
+            "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 4),
+                         "traffic": load_traffic(kern, name), "kernel": kern},
+            "op_hbm": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
+                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
+
+
 def cpu_baseline(w, inp, budget_s):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -484,6 +533,9 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "bwd":
+        return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps,
+                         args.warmup)
     if args.only == "gla_decode":
         return bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
     if args.only == "serve":
@@ -509,7 +561,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode"], default=None,
+                             "peaks", "gla_decode", "bwd"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -560,6 +612,9 @@ def main():
         log("bench: decode done")
         comps["gla_decode_N256"] = bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
         log("bench: GLA decode done")
+        comps["gsa_bf16_train_T2048_bwd"] = bench_bwd(torch, gsa, ev, w, max(1, args.steps // 4),
+                                                      args.warmup)
+        log("bench: backward done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)
         log("bench: serving prefill + decode done")

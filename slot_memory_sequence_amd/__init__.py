@@ -352,12 +352,12 @@ def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m) -> int:
 
 
 def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
-            state_grads=False, workspace=None, stream=None, events=None):
+            state_grads=False, out=None, workspace=None, stream=None, events=None):
     """GSA backward (softmax read): the gradients of gsa_fwd(q, k, v, g, k0,
     v0, tau=tau) given d_o [B,H,T,dv] (the gradient of o) and optional float32
     d_kf [B,H,m,dk] / d_vf [B,H,m,dv] (those of the final states).
     Returns (d_q, d_k, d_v, d_g, d_k0, d_v0); d_k0 / d_v0 (float32) are None
-    unless state_grads."""
+    unless state_grads.  out: optional (d_q, d_k, d_v, d_g) to write into."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
         _check(t, n, q.dtype)
@@ -365,7 +365,14 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
         _check(t, n, torch.float32)
     B, H, T, dk = q.shape
     dv, m = v.shape[-1], g.shape[-1]
-    outs = [torch.empty_like(x) for x in (q, k, v, g)]
+    if out is None:
+        outs = [torch.empty_like(x) for x in (q, k, v, g)]
+    else:
+        outs = list(out)
+        for n, t, x in zip(("d_q", "d_k", "d_v", "d_g"), outs, (q, k, v, g)):
+            _check(t, n, q.dtype)
+            if t.shape != x.shape:
+                raise ValueError("%s must have shape %s" % (n, tuple(x.shape)))
     sg = [None, None]
     if state_grads:
         sg = [torch.empty((B, H, m, d), dtype=torch.float32, device=q.device) for d in (dk, dv)]

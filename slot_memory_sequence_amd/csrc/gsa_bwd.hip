@@ -100,6 +100,16 @@ __device__ __forceinline__ void ldn(const bf16_t* p, float* o) {
   }
 }
 
+template <int N>
+__device__ __forceinline__ void stn(float* p, const float* v) {
+  if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; j += 4) *reinterpret_cast<float4*>(p + j) = make_float4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+  }
+}
+
 // sum over the four slot groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
 __device__ __forceinline__ float sum_sg4(float x) {
   x += __shfl_xor(x, 16, 64);
@@ -122,12 +132,43 @@ struct Thread {
   }
 };
 
+// Chunk inputs staged in LDS: rows t0 .. t1-1 of q, k (DK), v and dO (DV) in
+// the I/O type, copied with 16-byte loads that are all in flight before the
+// token loop (which then reads only LDS).
+template <typename T, int DK, int DV, int M>
+struct Stage {
+  static constexpr int Q = 0, K = C * DK, V = 2 * C * DK, DO = 2 * C * DK + C * DV;
+  static constexpr int elems = 2 * C * DK + 2 * C * DV;
+  static constexpr unsigned bytes = elems * sizeof(T);
+};
+
+template <typename T>
+__device__ __forceinline__ void copy_rows(T* __restrict__ dst, const T* __restrict__ src, int n_elems) {
+  constexpr int V = 16 / sizeof(T);
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  for (int i = threadIdx.x; i < n_elems / V; i += blockDim.x) d[i] = s[i];
+}
+
+template <typename T, int DK, int DV, int M>
+__device__ __forceinline__ void stage_chunk(T* lds, const T* qq, const T* kk, const T* vv, const T* dOo,
+                                            size_t row0, int rows) {
+  using SG = Stage<T, DK, DV, M>;
+  copy_rows(lds + SG::Q, qq + row0 * DK, rows * DK);
+  copy_rows(lds + SG::K, kk + row0 * DK, rows * DK);
+  copy_rows(lds + SG::V, vv + row0 * DV, rows * DV);
+  copy_rows(lds + SG::DO, dOo + row0 * DV, rows * DV);
+}
+
 // ------------------------------------------------------------ 1. maps
-// The state chunk p builds from a zero start, and its decay prod alpha.
+// The state chunk p builds from a zero start, and its decay prod alpha; also
+// every token's alpha and write intensity 1 - alpha (fp32 [units, T, M] each),
+// read by both token walks.
 template <typename T, int DK, int DV, int M>
 __global__ void __launch_bounds__(NT)
 bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ gg,
-        float* __restrict__ st, float* __restrict__ dec, int T_, int P, float inv_tau) {
+        float* __restrict__ st, float* __restrict__ dec, float* __restrict__ al,
+        float* __restrict__ wr, int T_, int P, float inv_tau) {
   using S = Shape<DK, DV, M>;
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
@@ -141,21 +182,27 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
     for (int j = 0; j < S::CV; j++) V[i][j] = 0.f;
   }
   const int t0 = p * C, t1 = min(T_, t0 + C);
+#pragma unroll 4
   for (int t = t0; t < t1; t++) {
     const size_t row = (size_t)u * T_ + t;
     float gv[S::SPT], kv[S::CK], vv_[S::CV];
     ldn<S::SPT>(gg + row * M + c0, gv);
     ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
     ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
+    float av[S::SPT], wv[S::SPT];
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
-      float a, w;
-      gate_alpha_w(gv[i], inv_tau, a, w);
+      gate_alpha_w(gv[i], inv_tau, av[i], wv[i]);
+      const float a = av[i], w = wv[i];
       cum[i] *= a;
 #pragma unroll
       for (int j = 0; j < S::CK; j++) K[i][j] = a * K[i][j] + w * kv[j];
 #pragma unroll
       for (int j = 0; j < S::CV; j++) V[i][j] = a * V[i][j] + w * vv_[j];
+    }
+    if (th.cg == 0) {
+      stn<S::SPT>(al + row * M + c0, av);
+      stn<S::SPT>(wr + row * M + c0, wv);
     }
   }
   float* base = st + ((size_t)u * P + p) * S::NE;
@@ -237,15 +284,21 @@ bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __r
 template <typename T, int DK, int DV, int M>
 __global__ void __launch_bounds__(NT)
 bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
-             const T* __restrict__ gg, const T* __restrict__ dOo, const float* __restrict__ st,
+             const float* __restrict__ al, const float* __restrict__ wr, const T* __restrict__ dOo,
+             const float* __restrict__ st,
              const float* __restrict__ dkf, const float* __restrict__ dvf, T* __restrict__ dq,
              float* __restrict__ xu, float* __restrict__ sw, float* __restrict__ dzw,
-             float* __restrict__ hw, float* __restrict__ fs, int T_, int P, float inv_tau) {
+             float* __restrict__ hw, float* __restrict__ fs, int T_, int P) {
   using S = Shape<DK, DV, M>;
+  using SG = Stage<T, DK, DV, M>;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T* lds = reinterpret_cast<T*>(lds_raw);
   __shared__ float red[2][4][3];
   __shared__ float dqb[2][4][DK];
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int t0 = p * C, t1 = min(T_, t0 + C);
+  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, (size_t)u * T_ + t0, t1 - t0);
   float K[S::SPT][S::CK], V[S::SPT][S::CV], XK[S::SPT][S::CK], XV[S::SPT][S::CV], cum[S::SPT];
   {
     const float* base = st + ((size_t)u * P + p) * S::NE;
@@ -261,22 +314,33 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       for (int j = 0; j < S::CV; j++) XV[i][j] = 0.f;
     }
   }
-  const int t0 = p * C, t1 = min(T_, t0 + C);
+  // this thread's slots' alpha and 1 - alpha, one token ahead
+  float a_n[S::SPT], w_n[S::SPT];
+  ldn<S::SPT>(al + ((size_t)u * T_ + t0) * M + c0, a_n);
+  ldn<S::SPT>(wr + ((size_t)u * T_ + t0) * M + c0, w_n);
+  __syncthreads();
   int n = 0;
   for (int t = t0; t < t1; t++, n++) {
     const int b = n & 1;
     const size_t row = (size_t)u * T_ + t;
-    float gv[S::SPT], qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
-    ldn<S::SPT>(gg + row * M + c0, gv);
-    ldn<S::CK>(qq + row * DK + th.cg * S::CK, qv);
-    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
-    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
-    ldn<S::CV>(dOo + row * DV + th.cg * S::CV, dov);
+    float av[S::SPT], wv[S::SPT], qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
+      av[i] = a_n[i];
+      wv[i] = w_n[i];
+    }
+    if (t + 1 < t1) {
+      ldn<S::SPT>(al + (row + 1) * M + c0, a_n);
+      ldn<S::SPT>(wr + (row + 1) * M + c0, w_n);
+    }
+    ldn<S::CK>(lds + SG::Q + n * DK + th.cg * S::CK, qv);
+    ldn<S::CK>(lds + SG::K + n * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(lds + SG::V + n * DV + th.cg * S::CV, vv_);
+    ldn<S::CV>(lds + SG::DO + n * DV + th.cg * S::CV, dov);
     float z[S::SPT], ds[S::SPT];
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
-      float a, w;
-      gate_alpha_w(gv[i], inv_tau, a, w);
+      const float a = av[i], w = wv[i];
       cum[i] *= a;
       float zp = 0.f, dp = 0.f;
 #pragma unroll
@@ -408,13 +472,19 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
 template <typename T, int DK, int DV, int M>
 __global__ void __launch_bounds__(NT)
 bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
-             const T* __restrict__ gg, const T* __restrict__ dOo, const float* __restrict__ xu,
+             const float* __restrict__ al, const float* __restrict__ wr, const T* __restrict__ dOo,
+             const float* __restrict__ xu,
              const float* __restrict__ sw, const float* __restrict__ dzw, float* __restrict__ hw,
-             float* __restrict__ tot, T* __restrict__ dk, T* __restrict__ dv, int T_, int P, float inv_tau) {
+             float* __restrict__ tot, T* __restrict__ dk, T* __restrict__ dv, int T_, int P) {
   using S = Shape<DK, DV, M>;
+  using SG = Stage<T, DK, DV, M>;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T* lds = reinterpret_cast<T*>(lds_raw);
   __shared__ float kvb[2][4][DK + DV];
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int t0 = p * C, t1 = min(T_, t0 + C);
+  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, (size_t)u * T_ + t0, t1 - t0);
   float AK[S::SPT][S::CK], AV[S::SPT][S::CV], R[S::SPT];
   {
     const float* base = xu + ((size_t)u * P + p) * S::NE;
@@ -426,25 +496,45 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       R[i] = 0.f;
     }
   }
-  const int t0 = p * C, t1 = min(T_, t0 + C);
+  // per-token s, dz, z dz + s ds, alpha and 1 - alpha of this thread's slots,
+  // one token ahead
+  float sv_n[S::SPT], dzv_n[S::SPT], hv_n[S::SPT], a_n[S::SPT], w_n[S::SPT];
+  {
+    const size_t r = (size_t)u * T_ + t1 - 1;
+    ldn<S::SPT>(sw + r * M + c0, sv_n);
+    ldn<S::SPT>(dzw + r * M + c0, dzv_n);
+    ldn<S::SPT>(hw + r * M + c0, hv_n);
+    ldn<S::SPT>(al + r * M + c0, a_n);
+    ldn<S::SPT>(wr + r * M + c0, w_n);
+  }
+  __syncthreads();
   int n = 0;
   for (int t = t1 - 1; t >= t0; t--, n++) {
-    const int b = n & 1;
+    const int b = n & 1, lt = t - t0;
     const size_t row = (size_t)u * T_ + t;
-    float gv[S::SPT], sv[S::SPT], dzv[S::SPT], hv[S::SPT];
+    float sv[S::SPT], dzv[S::SPT], hv[S::SPT], a[S::SPT], w[S::SPT], di[S::SPT];
     float qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
-    ldn<S::SPT>(gg + row * M + c0, gv);
-    ldn<S::SPT>(sw + row * M + c0, sv);
-    ldn<S::SPT>(dzw + row * M + c0, dzv);
-    ldn<S::SPT>(hw + row * M + c0, hv);
-    ldn<S::CK>(qq + row * DK + th.cg * S::CK, qv);
-    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
-    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
-    ldn<S::CV>(dOo + row * DV + th.cg * S::CV, dov);
-    float a[S::SPT], w[S::SPT], di[S::SPT];
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
-      gate_alpha_w(gv[i], inv_tau, a[i], w[i]);
+      sv[i] = sv_n[i];
+      dzv[i] = dzv_n[i];
+      hv[i] = hv_n[i];
+      a[i] = a_n[i];
+      w[i] = w_n[i];
+    }
+    if (t > t0) {
+      ldn<S::SPT>(sw + (row - 1) * M + c0, sv_n);
+      ldn<S::SPT>(dzw + (row - 1) * M + c0, dzv_n);
+      ldn<S::SPT>(hw + (row - 1) * M + c0, hv_n);
+      ldn<S::SPT>(al + (row - 1) * M + c0, a_n);
+      ldn<S::SPT>(wr + (row - 1) * M + c0, w_n);
+    }
+    ldn<S::CK>(lds + SG::Q + lt * DK + th.cg * S::CK, qv);
+    ldn<S::CK>(lds + SG::K + lt * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(lds + SG::V + lt * DV + th.cg * S::CV, vv_);
+    ldn<S::CV>(lds + SG::DO + lt * DV + th.cg * S::CV, dov);
+#pragma unroll
+    for (int i = 0; i < S::SPT; i++) {
       float pk = 0.f, pv = 0.f;
 #pragma unroll
       for (int j = 0; j < S::CK; j++) {
@@ -528,13 +618,13 @@ bwd_gate(const T* __restrict__ gg, const float* __restrict__ hw, const float* __
 
 // ------------------------------------------------------------ host side
 struct Ws {
-  float *st, *xu, *dec, *sw, *dzw, *hw, *tot, *fs;
+  float *st, *xu, *dec, *sw, *dzw, *hw, *al, *wr, *tot, *fs;
 };
 
 // floats of workspace for U units of T tokens
 inline size_t ws_floats(size_t U, size_t T, int dk, int dv, int m) {
   const size_t P = (T + C - 1) / C;
-  return 2 * U * P * (size_t)m * (dk + dv) + 2 * U * P * m + 3 * U * T * m + U * m;
+  return 2 * U * P * (size_t)m * (dk + dv) + 2 * U * P * m + 5 * U * T * m + U * m;
 }
 
 inline Ws carve(float* w, size_t U, size_t T, int dk, int dv, int m) {
@@ -547,7 +637,9 @@ inline Ws carve(float* w, size_t U, size_t T, int dk, int dv, int m) {
   s.sw = s.tot + U * P * m;
   s.dzw = s.sw + U * T * m;
   s.hw = s.dzw + U * T * m;
-  s.fs = s.hw + U * T * m;
+  s.al = s.hw + U * T * m;
+  s.wr = s.al + U * T * m;
+  s.fs = s.wr + U * T * m;
   return s;
 }
 
@@ -568,19 +660,31 @@ int launch(const GsaBwdLaunch& a) {
   const T *q = (const T*)a.q, *k = (const T*)a.k, *v = (const T*)a.v, *g = (const T*)a.g,
           *dO = (const T*)a.d_o;
   hipStream_t s = (hipStream_t)a.stream;
+  using SG = Stage<T, DK, DV, M>;
+  static const bool lds_set = [] {  // once per instantiation and process
+    (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
+    (void)hipFuncSetAttribute((const void*)bwd_walk_rev<T, DK, DV, M>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
+    return true;
+  }();
+  (void)lds_set;
   const dim3 grid(P, U);
   const long long ne = (long long)U * M * (DK + DV) / 4;
   const dim3 sgrid((unsigned)((ne + 255) / 256));
-  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), 0, s, k, v, g, w.st, w.dec, Tn, P, inv_tau);
+  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), 0, s, k, v, g, w.st, w.dec, w.al, w.wr, Tn, P,
+                     inv_tau);
   hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, a.k0, a.v0,
                      (float*)nullptr, (float*)nullptr, U, P);
-  launch_timed(bwd_walk_fwd<T, DK, DV, M>, grid, dim3(NT), 0, a.stream, a.events, 0, 1, q, k, v, g, dO,
-               (const float*)w.st, a.dkf, a.dvf, (T*)a.dq, w.xu, w.sw, w.dzw, w.hw, w.fs, Tn, P, inv_tau);
+  launch_timed(bwd_walk_fwd<T, DK, DV, M>, grid, dim3(NT), SG::bytes, a.stream, a.events, 0, 1, q, k, v,
+               (const float*)w.al, (const float*)w.wr, dO,
+               (const float*)w.st, a.dkf, a.dvf, (T*)a.dq, w.xu, w.sw, w.dzw, w.hw, w.fs, Tn, P);
   hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, a.dkf, a.dvf,
                      a.dk0, a.dv0, U, P);
-  launch_timed(bwd_walk_rev<T, DK, DV, M>, grid, dim3(NT), 0, a.stream, a.events, 2, 3, q, k, v, g, dO,
+  launch_timed(bwd_walk_rev<T, DK, DV, M>, grid, dim3(NT), SG::bytes, a.stream, a.events, 2, 3, q, k, v,
+               (const float*)w.al, (const float*)w.wr, dO,
                (const float*)w.xu, (const float*)w.sw, (const float*)w.dzw, w.hw, w.tot, (T*)a.dk, (T*)a.dv,
-               Tn, P, inv_tau);
+               Tn, P);
   hipLaunchKernelGGL((bwd_gate<T, M>), grid, dim3(256), 0, s, g, (const float*)w.hw, (const float*)w.tot,
                      (const float*)w.fs, (T*)a.dg, Tn, P, inv_tau);
   return 0;
