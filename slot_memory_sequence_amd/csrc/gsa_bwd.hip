@@ -110,6 +110,22 @@ __device__ __forceinline__ void stn(float* p, const float* v) {
   }
 }
 
+// sum over the 16 lanes of a row (the column groups of one slot group) with
+// DPP moves: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror.  Every step adds a commuting pair, so all 16 lanes end with the
+// same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x;
+}
+
 // sum over the four slot groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
 __device__ __forceinline__ float sum_sg4(float x) {
   x += __shfl_xor(x, 16, 64);
@@ -163,15 +179,40 @@ __device__ __forceinline__ void stage_chunk(T* lds, const T* qq, const T* kk, co
 // ------------------------------------------------------------ 1. maps
 // The state chunk p builds from a zero start, and its decay prod alpha; also
 // every token's alpha and write intensity 1 - alpha (fp32 [units, T, M] each),
-// read by both token walks.
+// read by both token walks.  The chunk's k and v are staged in LDS and its
+// C x M gates evaluated once each, cooperatively, before the token loop.
+template <typename T, int DK, int DV, int M>
+struct MapLds {
+  static constexpr unsigned kv_bytes = C * (DK + DV) * sizeof(T);
+  static constexpr unsigned bytes = kv_bytes + 2 * C * M * sizeof(float);
+};
+
 template <typename T, int DK, int DV, int M>
 __global__ void __launch_bounds__(NT)
 bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ gg,
         float* __restrict__ st, float* __restrict__ dec, float* __restrict__ al,
         float* __restrict__ wr, int T_, int P, float inv_tau) {
   using S = Shape<DK, DV, M>;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  T* sk = reinterpret_cast<T*>(lds_raw);
+  T* sv = sk + C * DK;
+  float* sa = reinterpret_cast<float*>(lds_raw + C * (DK + DV) * sizeof(T));
+  float* sw_ = sa + C * M;
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int t0 = p * C, t1 = min(T_, t0 + C), rows = t1 - t0;
+  const size_t row0 = (size_t)u * T_ + t0;
+  copy_rows(sk, kk + row0 * DK, rows * DK);
+  copy_rows(sv, vv + row0 * DV, rows * DV);
+  for (int e = threadIdx.x; e < rows * M; e += NT) {
+    float a, w;
+    gate_alpha_w(Elem<T>::to_f(gg[row0 * M + e]), inv_tau, a, w);
+    sa[e] = a;
+    sw_[e] = w;
+    al[row0 * M + e] = a;
+    wr[row0 * M + e] = w;
+  }
+  __syncthreads();
   float K[S::SPT][S::CK], V[S::SPT][S::CV], cum[S::SPT];
 #pragma unroll
   for (int i = 0; i < S::SPT; i++) {
@@ -181,28 +222,19 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
 #pragma unroll
     for (int j = 0; j < S::CV; j++) V[i][j] = 0.f;
   }
-  const int t0 = p * C, t1 = min(T_, t0 + C);
-#pragma unroll 4
-  for (int t = t0; t < t1; t++) {
-    const size_t row = (size_t)u * T_ + t;
-    float gv[S::SPT], kv[S::CK], vv_[S::CV];
-    ldn<S::SPT>(gg + row * M + c0, gv);
-    ldn<S::CK>(kk + row * DK + th.cg * S::CK, kv);
-    ldn<S::CV>(vv + row * DV + th.cg * S::CV, vv_);
-    float av[S::SPT], wv[S::SPT];
+  for (int n = 0; n < rows; n++) {
+    float av[S::SPT], wv[S::SPT], kv[S::CK], vv_[S::CV];
+    ldn<S::SPT>(sa + n * M + c0, av);
+    ldn<S::SPT>(sw_ + n * M + c0, wv);
+    ldn<S::CK>(sk + n * DK + th.cg * S::CK, kv);
+    ldn<S::CV>(sv + n * DV + th.cg * S::CV, vv_);
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
-      gate_alpha_w(gv[i], inv_tau, av[i], wv[i]);
-      const float a = av[i], w = wv[i];
-      cum[i] *= a;
+      cum[i] *= av[i];
 #pragma unroll
-      for (int j = 0; j < S::CK; j++) K[i][j] = a * K[i][j] + w * kv[j];
+      for (int j = 0; j < S::CK; j++) K[i][j] = av[i] * K[i][j] + wv[i] * kv[j];
 #pragma unroll
-      for (int j = 0; j < S::CV; j++) V[i][j] = a * V[i][j] + w * vv_[j];
-    }
-    if (th.cg == 0) {
-      stn<S::SPT>(al + row * M + c0, av);
-      stn<S::SPT>(wr + row * M + c0, wv);
+      for (int j = 0; j < S::CV; j++) V[i][j] = av[i] * V[i][j] + wv[i] * vv_[j];
     }
   }
   float* base = st + ((size_t)u * P + p) * S::NE;
@@ -353,8 +385,8 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
         V[i][j] = a * V[i][j] + w * vv_[j];
         dp += V[i][j] * dov[j];
       }
-      z[i] = sum16(zp);
-      ds[i] = sum16(dp);
+      z[i] = row_sum16(zp);
+      ds[i] = row_sum16(dp);
     }
     // softmax statistics of this wave's slots: max, sum of e^{z - max}, and
     // sum of e^{z - max} ds; then combined over the four waves
@@ -459,7 +491,7 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
 #pragma unroll
         for (int j = 0; j < S::CV; j++) x += d[j] * V[i][j];
       }
-      x = sum16(x);
+      x = row_sum16(x);
       if (th.cg == 0) fs[(size_t)u * M + c0 + i] = x;
     }
   }
@@ -546,7 +578,7 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
         AV[i][j] += sv[i] * dov[j];
         pv += AV[i][j] * vv_[j];
       }
-      di[i] = sum16(pk) + sum16(pv);
+      di[i] = row_sum16(pk) + row_sum16(pv);
     }
 #pragma unroll
     for (int j = 0; j < S::CK; j++) {
@@ -662,6 +694,8 @@ int launch(const GsaBwdLaunch& a) {
   hipStream_t s = (hipStream_t)a.stream;
   using SG = Stage<T, DK, DV, M>;
   static const bool lds_set = [] {  // once per instantiation and process
+    (void)hipFuncSetAttribute((const void*)bwd_map<T, DK, DV, M>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, MapLds<T, DK, DV, M>::bytes);
     (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
     (void)hipFuncSetAttribute((const void*)bwd_walk_rev<T, DK, DV, M>,
@@ -672,7 +706,8 @@ int launch(const GsaBwdLaunch& a) {
   const dim3 grid(P, U);
   const long long ne = (long long)U * M * (DK + DV) / 4;
   const dim3 sgrid((unsigned)((ne + 255) / 256));
-  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), 0, s, k, v, g, w.st, w.dec, w.al, w.wr, Tn, P,
+  constexpr unsigned map_lds = MapLds<T, DK, DV, M>::bytes;
+  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), map_lds, s, k, v, g, w.st, w.dec, w.al, w.wr, Tn, P,
                      inv_tau);
   hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, a.k0, a.v0,
                      (float*)nullptr, (float*)nullptr, U, P);
