@@ -172,3 +172,17 @@ def test_bwd_training_shape_sampled(gsa, torch):
     got = _run(gsa, torch, inp, gi, w["tau"])
     units = [0, 7, 13, 22, w["B"] * w["H"] - 1]
     _compare(got, _ref(inp, gi, w["tau"], units), "bf16", "B8 H4 T2048 sampled", units)
+
+
+def test_bwd_long_context_sampled(gsa, torch):
+    """The long-context shape (B1 H8 T16384, 256 chunks per unit) with initial
+    states and final-state gradients; two units against the oracle."""
+    w = synth.WORKLOADS["gsa_bf16_long_T16384"]
+    inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                           seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
+                           init_std=w["init_std"])
+    gi = synth.gsa_grad_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                               seed=2, final_std=1.0)
+    got = _run(gsa, torch, inp, gi, w["tau"])
+    units = [0, w["B"] * w["H"] - 1]
+    _compare(got, _ref(inp, gi, w["tau"], units), "bf16", "B1 H8 T16384 sampled", units)

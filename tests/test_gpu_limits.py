@@ -1,6 +1,7 @@
 """GPU parity at the size limits: the largest unit count the launch grid takes
 (65535 (batch, head) units), tensors of more than 2^31 elements (64-bit
-offsets everywhere), and a decode batch of 131072 units.  The inputs are drawn
+offsets everywhere), and a decode batch of 131072 units; the same limits for
+the backward.  The inputs are drawn
 on the device with a seeded torch generator; sampled units are copied back and
 checked against the float64 oracle run on exactly those stored values.
 
@@ -128,3 +129,37 @@ def test_decode_131072_units(gsa, torch):
     del q, k, v, g, ks, vs, o
     torch.cuda.empty_cache()
     assert worst <= TOL["bf16"]
+
+
+def _bwd_sampled(gsa, torch, B, H, T, d, m, units, seed):
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    sc = 1.0 / np.sqrt(d)
+    q = _randn(torch, gen, (B, H, T, d), sc)
+    k = _randn(torch, gen, (B, H, T, d), sc)
+    v = _randn(torch, gen, (B, H, T, d), sc)
+    g = _randn(torch, gen, (B, H, T, m), 1.0)
+    do = _randn(torch, gen, (B, H, T, d), 1.0)
+    grads = gsa.gsa_bwd(q, k, v, g, do)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for u in units:
+        ref = oracle.gsa_bwd(_unit(q, u), _unit(k, u), _unit(v, u), _unit(g, u), _unit(do, u), tau=8.0)
+        for name, x in zip(("dq", "dk", "dv", "dg"), grads[:4]):
+            worst = max(worst, rel_err(_unit(x, u), ref[name]))
+    print("gsa_bwd B%d H%d T%d d%d m%d units %s: worst rel err %.2e (%d elements per input)"
+          % (B, H, T, d, m, list(units), worst, q.numel()))
+    del q, k, v, g, do, grads
+    torch.cuda.empty_cache()
+    return worst
+
+
+def test_bwd_max_units(gsa, torch):
+    B = 65535
+    assert _bwd_sampled(gsa, torch, B, 1, 70, 64, 32, [0, 1, 32768, B - 1], seed=5) <= TOL["bf16"]
+
+
+def test_bwd_over_2g_elements(gsa, torch):
+    """q, k, v, dO and the gradients of 2^31 + elements each (about 90 GB of
+    device memory with the workspace)."""
+    B, H, T = 64, 16, 16385
+    assert _bwd_sampled(gsa, torch, B, H, T, 128, 64, [0, 517, B * H - 1], seed=6) <= TOL["bf16"]
