@@ -424,22 +424,26 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       Se += red[b][x][1] * f;
       Sd += red[b][x][2] * f;
     }
-    const float inv = 1.f / Se, dbar = Sd * inv;
+    const float inv = __builtin_amdgcn_rcpf(Se), dbar = Sd * inv;
     float s[S::SPT], dz[S::SPT];
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
       s[i] = __expf(z[i] - Mx) * inv;
       dz[i] = s[i] * (ds[i] - dbar);
     }
-    // dq partial sums over this wave's slots
+    // dq partial sums over this wave's slots: all shuffles first, then one
+    // store block (so that the cross-lane moves are in flight together)
+    float dqp[S::CK];
 #pragma unroll
     for (int j = 0; j < S::CK; j++) {
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < S::SPT; i++) x += dz[i] * K[i][j];
-      x = sum_sg4(x);
-      if ((th.l >> 4) == 0) dqb[b][th.w][th.cg * S::CK + j] = x;
+      dqp[j] = x;
     }
+#pragma unroll
+    for (int j = 0; j < S::CK; j++) dqp[j] = sum_sg4(dqp[j]);
+    if ((th.l >> 4) == 0) stn<S::CK>(&dqb[b][th.w][th.cg * S::CK], dqp);
     if (th.cg == 0) {
 #pragma unroll
       for (int i = 0; i < S::SPT; i++) {
@@ -580,21 +584,30 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       }
       di[i] = row_sum16(pk) + row_sum16(pv);
     }
+    // dk, dv partial sums over this wave's slots: all shuffles first, then
+    // one store block
+    float pk_[S::CK], pv_[S::CV];
 #pragma unroll
     for (int j = 0; j < S::CK; j++) {
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < S::SPT; i++) x += w[i] * AK[i][j];
-      x = sum_sg4(x);
-      if ((th.l >> 4) == 0) kvb[b][th.w][th.cg * S::CK + j] = x;
+      pk_[j] = x;
     }
 #pragma unroll
     for (int j = 0; j < S::CV; j++) {
       float x = 0.f;
 #pragma unroll
       for (int i = 0; i < S::SPT; i++) x += w[i] * AV[i][j];
-      x = sum_sg4(x);
-      if ((th.l >> 4) == 0) kvb[b][th.w][DK + th.cg * S::CV + j] = x;
+      pv_[j] = x;
+    }
+#pragma unroll
+    for (int j = 0; j < S::CK; j++) pk_[j] = sum_sg4(pk_[j]);
+#pragma unroll
+    for (int j = 0; j < S::CV; j++) pv_[j] = sum_sg4(pv_[j]);
+    if ((th.l >> 4) == 0) {
+      stn<S::CK>(&kvb[b][th.w][th.cg * S::CK], pk_);
+      stn<S::CV>(&kvb[b][th.w][DK + th.cg * S::CV], pv_);
     }
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
