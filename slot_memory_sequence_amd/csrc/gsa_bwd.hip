@@ -43,6 +43,7 @@
 // reductions inside a wave and per-column sums over slots run over the four
 // slot groups of a wave and then, through LDS, over the four waves.
 #include "../../include/gsa.h"
+#include "bf16_common.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 #include "launch.hpp"
@@ -126,17 +127,11 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// sum over the four slot groups of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float sum_sg4(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
-}
-__device__ __forceinline__ float max_sg4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
-}
+// sum / max over the four slot groups of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48): gfx950's permlane swaps, no LDS round trip; every lane gets the
+// same bits
+__device__ __forceinline__ float sum_sg4(float x) { return bfk::group4_sum(x); }
+__device__ __forceinline__ float max_sg4(float x) { return bfk::group4_max(x); }
 
 struct Thread {
   int l, w, cg, sg;
