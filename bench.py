@@ -309,7 +309,27 @@ def bench_gla_decode(torch, gsa, ev, steps, warmup):
             "steps_per_s": round(steps / wall, 1), "roofline": r}
 
 
-def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd"):
+def bwd_cpu_oracle(w, inp, budget_s=3.0):
+    """The oracle's backward (fp64, reverse-mode through the recurrence) on
+    one thread over one (batch, head) unit of the batch, scaled to the batch's
+    tokens/s (every unit costs the same)."""
+    import oracle
+    one = {n: inp[n].f64[:1, :1].copy() for n in ("q", "k", "v", "g", "do")}
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        oracle.gsa_bwd(one["q"], one["k"], one["v"], one["g"], one["do"], tau=w["tau"], nthreads=1)
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(w["T"] * runs / dt / (w["B"] * w["H"]) * w["B"], 1), "unit": "tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "one (b,h) unit of the batch (T=%d), %d run(s) in %.1f s, scaled to B*T tokens "
+                      "over B*H units" % (w["T"], runs, dt)}
+
+
+def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd", cpu=True):
     """The GSA backward at the training shape (B8 H4 T2048, bf16), zero
     initial states and no final-state gradients, dO ~ N(0, 1); two input sets
     rotated."""
@@ -343,7 +363,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd")
                          "traffic": load_traffic(kern, name), "kernel": kern},
             "op_hbm": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
+                       "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None}
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -535,7 +556,7 @@ def run_only(args, torch, gsa, ev):
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
     if args.only == "bwd":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps,
-                         args.warmup)
+                         args.warmup, cpu=False)
     if args.only == "gla_decode":
         return bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
     if args.only == "serve":
@@ -613,7 +634,7 @@ def main():
         comps["gla_decode_N256"] = bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
         log("bench: GLA decode done")
         comps["gsa_bf16_train_T2048_bwd"] = bench_bwd(torch, gsa, ev, w, max(1, args.steps // 4),
-                                                      args.warmup)
+                                                      args.warmup, cpu=not args.no_cpu)
         log("bench: backward done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)

@@ -174,12 +174,16 @@ __device__ __forceinline__ void stage_chunk(T* lds, const T* qq, const T* kk, co
 // ------------------------------------------------------------ 1. maps
 // The state chunk p builds from a zero start, and its decay prod alpha; also
 // every token's alpha and write intensity 1 - alpha (fp32 [units, T, M] each),
-// read by both token walks.  The chunk's k and v are staged in LDS and its
-// C x M gates evaluated once each, cooperatively, before the token loop.
+// read by both token walks.  The map is the sum over the chunk's tokens j of
+// Diag(prod_{r>j} alpha_r) i_j [k_j | v_j]^T: a product over the chunk with
+// weights in [0, 1].  Thread (slot c, part) evaluates the gates of 16
+// consecutive tokens of slot c, forms their suffix products, and the four
+// parts of a slot combine their products through LDS; then every thread
+// accumulates its slot rows x columns of the map from the LDS-staged k, v.
 template <typename T, int DK, int DV, int M>
 struct MapLds {
   static constexpr unsigned kv_bytes = C * (DK + DV) * sizeof(T);
-  static constexpr unsigned bytes = kv_bytes + 2 * C * M * sizeof(float);
+  static constexpr unsigned bytes = kv_bytes + C * M * sizeof(float) + (NT / M) * M * sizeof(float);
 };
 
 template <typename T, int DK, int DV, int M>
@@ -188,48 +192,67 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
         float* __restrict__ st, float* __restrict__ dec, float* __restrict__ al,
         float* __restrict__ wr, int T_, int P, float inv_tau) {
   using S = Shape<DK, DV, M>;
+  constexpr int PARTS = NT / M, TPP = C / PARTS;  // parts per slot, tokens per part
+  static_assert(NT % M == 0 && C % PARTS == 0, "gate split");
   extern __shared__ __align__(16) unsigned char lds_raw[];
   T* sk = reinterpret_cast<T*>(lds_raw);
   T* sv = sk + C * DK;
-  float* sa = reinterpret_cast<float*>(lds_raw + C * (DK + DV) * sizeof(T));
-  float* sw_ = sa + C * M;
+  float* sA = reinterpret_cast<float*>(lds_raw + C * (DK + DV) * sizeof(T));  // [C][M] weights
+  float* ptot = sA + C * M;                                                     // [PARTS][M]
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
   const int t0 = p * C, t1 = min(T_, t0 + C), rows = t1 - t0;
   const size_t row0 = (size_t)u * T_ + t0;
   copy_rows(sk, kk + row0 * DK, rows * DK);
   copy_rows(sv, vv + row0 * DV, rows * DV);
-  for (int e = threadIdx.x; e < rows * M; e += NT) {
-    float a, w;
-    gate_alpha_w(Elem<T>::to_f(gg[row0 * M + e]), inv_tau, a, w);
-    sa[e] = a;
-    sw_[e] = w;
-    al[row0 * M + e] = a;
-    wr[row0 * M + e] = w;
+  {
+    const int c = threadIdx.x % M, part = threadIdx.x / M, j0 = part * TPP;
+    float av[TPP], wv[TPP];
+#pragma unroll
+    for (int x = 0; x < TPP; x++) {
+      av[x] = 1.f;
+      wv[x] = 0.f;
+      if (j0 + x < rows) {
+        const size_t e = (row0 + j0 + x) * M + c;
+        gate_alpha_w(Elem<T>::to_f(gg[e]), inv_tau, av[x], wv[x]);
+        al[e] = av[x];
+        wr[e] = wv[x];
+      }
+    }
+    float prod = 1.f;  // suffix product inside the part
+#pragma unroll
+    for (int x = TPP - 1; x >= 0; x--) {
+      wv[x] *= prod;
+      prod *= av[x];
+    }
+    ptot[part * M + c] = prod;
+    __syncthreads();
+    float after = 1.f;  // product of the later parts
+    for (int q = part + 1; q < PARTS; q++) after *= ptot[q * M + c];
+#pragma unroll
+    for (int x = 0; x < TPP; x++) sA[(j0 + x) * M + c] = wv[x] * after;
+    if (part == 0) dec[((size_t)u * P + p) * M + c] = prod * after;
   }
   __syncthreads();
-  float K[S::SPT][S::CK], V[S::SPT][S::CV], cum[S::SPT];
+  float K[S::SPT][S::CK], V[S::SPT][S::CV];
 #pragma unroll
   for (int i = 0; i < S::SPT; i++) {
-    cum[i] = 1.f;
 #pragma unroll
     for (int j = 0; j < S::CK; j++) K[i][j] = 0.f;
 #pragma unroll
     for (int j = 0; j < S::CV; j++) V[i][j] = 0.f;
   }
   for (int n = 0; n < rows; n++) {
-    float av[S::SPT], wv[S::SPT], kv[S::CK], vv_[S::CV];
-    ldn<S::SPT>(sa + n * M + c0, av);
-    ldn<S::SPT>(sw_ + n * M + c0, wv);
+    float wt[S::SPT], kv[S::CK], vv_[S::CV];
+    ldn<S::SPT>(sA + n * M + c0, wt);
     ldn<S::CK>(sk + n * DK + th.cg * S::CK, kv);
     ldn<S::CV>(sv + n * DV + th.cg * S::CV, vv_);
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
-      cum[i] *= av[i];
 #pragma unroll
-      for (int j = 0; j < S::CK; j++) K[i][j] = av[i] * K[i][j] + wv[i] * kv[j];
+      for (int j = 0; j < S::CK; j++) K[i][j] += wt[i] * kv[j];
 #pragma unroll
-      for (int j = 0; j < S::CV; j++) V[i][j] = av[i] * V[i][j] + wv[i] * vv_[j];
+      for (int j = 0; j < S::CV; j++) V[i][j] += wt[i] * vv_[j];
     }
   }
   float* base = st + ((size_t)u * P + p) * S::NE;
@@ -243,7 +266,6 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
     for (int j = 0; j < S::CV; j += 4)
       *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
           f32x4{V[i][j], V[i][j + 1], V[i][j + 2], V[i][j + 3]};
-    if (th.cg == 0) dec[((size_t)u * P + p) * M + c0 + i] = cum[i];
   }
 }
 
