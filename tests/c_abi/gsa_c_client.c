@@ -1,15 +1,18 @@
 /*
  * A plain C client of libgsa: no Python, no PyTorch.  It allocates device
- * buffers with the HIP runtime, calls gsa_fwd (and gsa_decode_step on the
- * resulting states) through include/gsa.h, and writes the results to a file,
- * so that a test can compare them with the fp64 oracle on the same inputs.
+ * buffers with the HIP runtime, calls gsa_fwd, gsa_bwd on the same inputs and
+ * gsa_decode_step on the forward's final states through include/gsa.h, and
+ * writes the results to a file, so that a test can compare them with the fp64
+ * oracle on the same inputs.
  *
  * Usage: gsa_c_client <in.bin> <out.bin>
  *   in.bin : int32 B, H, T, dk, dv, m; then float32 q[B,H,T,dk], k[B,H,T,dk],
  *            v[B,H,T,dv], g[B,H,T,m], and one decode token per unit:
- *            q1[B,H,dk], k1[B,H,dk], v1[B,H,dv], g1[B,H,m]
+ *            q1[B,H,dk], k1[B,H,dk], v1[B,H,dv], g1[B,H,m]; then the output
+ *            gradient d_o[B,H,T,dv]
  *   out.bin: float32 o[B,H,T,dv], k_final[B,H,m,dk], v_final[B,H,m,dv],
- *            o1[B,H,dv], and the states after the decode step.
+ *            o1[B,H,dv], the states after the decode step, and the
+ *            gradients d_q, d_k [B,H,T,dk], d_v [B,H,T,dv], d_g [B,H,T,m].
  * Exit status 0 on success; any library or runtime error is printed.
  */
 #include <hip/hip_runtime_api.h>
@@ -62,8 +65,9 @@ int main(int argc, char** argv) {
   float* hk1 = read_floats(fi, U * dk);
   float* hv1 = read_floats(fi, U * dv);
   float* hg1 = read_floats(fi, U * m);
+  float* hdo = read_floats(fi, nv);
   fclose(fi);
-  if (!hq || !hk || !hv || !hg || !hq1 || !hk1 || !hv1 || !hg1) {
+  if (!hq || !hk || !hv || !hg || !hq1 || !hk1 || !hv1 || !hg1 || !hdo) {
     fprintf(stderr, "short input file\n");
     return 1;
   }
@@ -72,15 +76,15 @@ int main(int argc, char** argv) {
             GSA_ABI_VERSION);
     return 1;
   }
-  if (!gsa_fwd_supported(dk, dv, m, 64, GSA_DTYPE_F32)) {
+  if (!gsa_fwd_supported(dk, dv, m, 64, GSA_DTYPE_F32) || !gsa_bwd_supported(dk, dv, m, GSA_DTYPE_F32)) {
     fprintf(stderr, "shape not compiled\n");
     return 1;
   }
 
-  float *q, *k, *v, *g, *o, *kf, *vf, *q1, *k1, *v1, *g1, *o1;
+  float *q, *k, *v, *g, *o, *kf, *vf, *q1, *k1, *v1, *g1, *o1, *d_o, *gq, *gk, *gv, *gg;
   if (to_device(&q, hq, nq) || to_device(&k, hk, nq) || to_device(&v, hv, nv) ||
       to_device(&g, hg, ng) || to_device(&q1, hq1, U * dk) || to_device(&k1, hk1, U * dk) ||
-      to_device(&v1, hv1, U * dv) || to_device(&g1, hg1, U * m)) {
+      to_device(&v1, hv1, U * dv) || to_device(&g1, hg1, U * m) || to_device(&d_o, hdo, nv)) {
     fprintf(stderr, "device allocation or copy failed\n");
     return 2;
   }
@@ -88,6 +92,10 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc((void**)&kf, U * m * dk * sizeof(float)));
   HIP_OK(hipMalloc((void**)&vf, U * m * dv * sizeof(float)));
   HIP_OK(hipMalloc((void**)&o1, U * dv * sizeof(float)));
+  HIP_OK(hipMalloc((void**)&gq, nq * sizeof(float) + 16));
+  HIP_OK(hipMalloc((void**)&gk, nq * sizeof(float) + 16));
+  HIP_OK(hipMalloc((void**)&gv, nv * sizeof(float) + 16));
+  HIP_OK(hipMalloc((void**)&gg, ng * sizeof(float) + 16));
 
   hipStream_t st;
   HIP_OK(hipStreamCreate(&st));
@@ -112,7 +120,10 @@ int main(int argc, char** argv) {
 
   FILE* fo = fopen(argv[2], "wb");
   if (!fo) return 1;
-  float* buf = (float*)malloc((nv > U * m * (dk + dv) ? nv : U * m * (dk + dv)) * sizeof(float));
+  size_t nbuf = nv > U * m * (dk + dv) ? nv : U * m * (dk + dv);
+  if (nq > nbuf) nbuf = nq;
+  if (ng > nbuf) nbuf = ng;
+  float* buf = (float*)malloc(nbuf * sizeof(float));
   if (!buf) return 1;
 #define DUMP(dptr, n)                                                            \
   do {                                                                           \
@@ -122,6 +133,23 @@ int main(int argc, char** argv) {
   DUMP(o, nv);
   DUMP(kf, U * m * dk);
   DUMP(vf, U * m * dv);
+
+  /* the backward of the same forward (zero initial states, no final-state
+     gradients), with a workspace of its own */
+  const size_t wsb2 = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m);
+  void* ws2 = NULL;
+  if (wsb2) HIP_OK(hipMalloc(&ws2, wsb2));
+  s = gsa_bwd(q, k, v, g, d_o, NULL, NULL, NULL, NULL, gq, gk, gv, gg, NULL, NULL, B, H, T, dk, dv,
+              m, 8.0f, GSA_DTYPE_F32, ws2, wsb2, st, NULL);
+  if (s != GSA_OK) {
+    fprintf(stderr, "gsa_bwd: %s\n", gsa_status_string(s));
+    return 3;
+  }
+  if (gsa_bwd(q, k, v, g, d_o, NULL, NULL, NULL, NULL, gq, gk, gv, gg, NULL, NULL, B, H, T, dk, dv,
+              m, 8.0f, GSA_DTYPE_F32, ws2, wsb2 - 16, st, NULL) != GSA_ERR_WORKSPACE) {
+    fprintf(stderr, "short backward workspace was not rejected\n");
+    return 3;
+  }
 
   /* one decode step from the final states, in place */
   s = gsa_decode_step(q1, k1, v1, g1, kf, vf, o1, B, H, dk, dv, m, 8.0f, GSA_DTYPE_F32, st);
@@ -133,6 +161,10 @@ int main(int argc, char** argv) {
   DUMP(o1, U * dv);
   DUMP(kf, U * m * dk);
   DUMP(vf, U * m * dv);
+  DUMP(gq, nq);
+  DUMP(gk, nq);
+  DUMP(gv, nv);
+  DUMP(gg, ng);
   fclose(fo);
   printf("gsa_c_client ok: B=%d H=%d T=%d dk=%d dv=%d m=%d workspace=%zu\n", B, H, T, dk, dv, m, wsb);
   return 0;

@@ -1,8 +1,8 @@
 """The C ABI from plain C: tests/c_abi/gsa_c_client (no Python, no PyTorch in
-its process) allocates device memory with the HIP runtime, runs gsa_fwd and a
-gsa_decode_step on the final states, and writes the results; they are checked
-here against the float64 oracle on the same float32 inputs (bar 1e-4, the
-float32 path's; the decode states 1e-5)."""
+its process) allocates device memory with the HIP runtime, runs gsa_fwd, the
+backward gsa_bwd of the same call and a gsa_decode_step on the final states,
+and writes the results; they are checked here against the float64 oracle on
+the same float32 inputs (bar 1e-4, the float32 path's)."""
 import os
 import subprocess
 
@@ -25,10 +25,11 @@ def test_c_client_forward_and_decode(tmp_path):
     B, H, T, d, m = 2, 3, 200, 64, 32
     inp = synth.gsa_inputs(B, H, T, d, d, m, dtype="f32", seed=11)
     tok = synth.decode_inputs(B, H, d, d, m, dtype="f32", seed=12)
+    do = synth.gsa_grad_inputs(B, H, T, d, d, m, dtype="f32", seed=13)["do"]
     src = tmp_path / "in.bin"
     with open(src, "wb") as f:
         f.write(np.array([B, H, T, d, d, m], dtype=np.int32).tobytes())
-        for x in (inp["q"], inp["k"], inp["v"], inp["g"], tok["q"], tok["k"], tok["v"], tok["g"]):
+        for x in (inp["q"], inp["k"], inp["v"], inp["g"], tok["q"], tok["k"], tok["v"], tok["g"], do):
             f.write(np.ascontiguousarray(x.raw, dtype=np.float32).tobytes())
     dst = tmp_path / "out.bin"
     print("running the C client: B%d H%d T%d d%d m%d" % (B, H, T, d, m), flush=True)
@@ -37,10 +38,11 @@ def test_c_client_forward_and_decode(tmp_path):
     assert r.returncode == 0, r.stderr
     out = np.fromfile(dst, dtype=np.float32).astype(np.float64)
     U = B * H
-    sizes = [U * T * d, U * m * d, U * m * d, U * d, U * m * d, U * m * d]
+    sizes = [U * T * d, U * m * d, U * m * d, U * d, U * m * d, U * m * d,
+             U * T * d, U * T * d, U * T * d, U * T * m]
     assert out.size == sum(sizes)
     parts = np.split(out, np.cumsum(sizes)[:-1])
-    o, kf, vf, o1, kf1, vf1 = parts
+    o, kf, vf, o1, kf1, vf1, gq, gk, gv, gg = parts
     ref = oracle.gsa_fwd(*(inp[n].f64 for n in "qkvg"), tau=8.0)
     assert rel_err(o.reshape(B, H, T, d), ref["o"]) <= 1e-4
     assert rel_err(kf.reshape(B, H, m, d), ref["kf"]) <= 1e-4
@@ -48,3 +50,9 @@ def test_c_client_forward_and_decode(tmp_path):
     ro, rk, rv = oracle.gsa_decode_step(*(tok[n].f64 for n in "qkvg"), ref["kf"], ref["vf"])
     assert rel_err(o1.reshape(B, H, d), ro) <= 1e-4
     assert rel_err(kf1.reshape(B, H, m, d), rk) <= 1e-4 and rel_err(vf1.reshape(B, H, m, d), rv) <= 1e-4
+    gref = oracle.gsa_bwd(*(inp[n].f64 for n in "qkvg"), do.f64, tau=8.0)
+    for name, x, shape in (("dq", gq, (B, H, T, d)), ("dk", gk, (B, H, T, d)),
+                           ("dv", gv, (B, H, T, d)), ("dg", gg, (B, H, T, m))):
+        err = rel_err(x.reshape(shape), gref[name])
+        print("C client gsa_bwd %s rel err %.2e" % (name, err))
+        assert err <= 1e-4, name
