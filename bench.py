@@ -350,6 +350,24 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
     f_f, f_r, nbytes = gsa_bwd_alg(B, H, T, dk, dv, m, 2)
+    # one training step of the op: the forward, then its backward (same inputs)
+    o_buf = [torch.empty_like(s_["v"]) for s_ in sets]
+    nbf = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1, 0)
+    wsf = torch.empty(max(nbf, 1), dtype=torch.uint8, device="cuda")
+
+    def train_step(i):
+        s_ = sets[i % len(sets)]
+        gsa.gsa_fwd(s_["q"], s_["k"], s_["v"], s_["g"], tau=w["tau"], out=o_buf[i % len(sets)], workspace=wsf)
+        call(s_, None)
+
+    for i in range(warmup):
+        train_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        train_step(i)
+    torch.cuda.synchronize()
+    wall_train = time.perf_counter() - t0
     kern, fl, t = ("bwd_walk_fwd", f_f, t_f) if t_f >= t_r else ("bwd_walk_rev", f_r, t_r)
     ach = fl / (t * 1e-3) / 1e12
     t_op = wall / steps * 1e3
@@ -364,6 +382,9 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
             "op_hbm": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                        "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "train_step": {"value": round(B * T * steps / wall_train, 1), "unit": "tokens/s",
+                           "ms_per_step": round(wall_train / steps * 1e3, 4),
+                           "what": "gsa_fwd then gsa_bwd on the same batch, per step"},
             "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None}
 
 
