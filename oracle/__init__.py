@@ -59,9 +59,10 @@ def _load():
         lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
         lib.oracle_gsa_decode_step_nl.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
         lib.oracle_gsa_bwd.argtypes = [P] * 15 + [L] * 6 + [D, I]
+        lib.oracle_gsa_bwd_nl.argtypes = [P] * 15 + [L] * 6 + [D, I, I]
         for f in (lib.oracle_gsa_fwd, lib.oracle_gla_fwd, lib.oracle_gsa_decode_step,
                   lib.oracle_gsa_fwd_nl, lib.oracle_gsa_decode_step_nl, lib.oracle_gla_fwd_gm,
-                  lib.oracle_gsa_bwd):
+                  lib.oracle_gsa_bwd, lib.oracle_gsa_bwd_nl):
             f.restype = I
         lib.oracle_max_threads.restype = I
         _lib = lib
@@ -123,8 +124,10 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, tau=8.0, want_states=True,
     return dict(o=o, kf=kf, vf=vf, s=s, z=z)
 
 
-def gsa_bwd(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, nthreads=1):
-    """Gradients of the recurrent GSA forward (softmax read) by reverse-mode
+def gsa_bwd(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, nthreads=1,
+            nonlinearity="softmax"):
+    """Gradients of the recurrent GSA forward (with the slot read named by
+    nonlinearity, as for gsa_fwd) by reverse-mode
     differentiation of the token recurrence.  do [B,H,T,dv] is the gradient of
     the outputs; dkf [B,H,m,dk] / dvf [B,H,m,dv] (optional) those of the final
     states.  Returns dict with dq, dk, dv, dg (shaped like q, k, v, g) and
@@ -141,9 +144,9 @@ def gsa_bwd(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, nthre
             assert x.shape == (B, H, m, d)
     out = dict(dq=np.empty_like(q), dk=np.empty_like(k), dv=np.empty_like(v), dg=np.empty_like(g),
                dk0=np.empty((B, H, m, dk)), dv0=np.empty((B, H, m, dv)))
-    rc = _load().oracle_gsa_bwd(_p(q), _p(k), _p(v), _p(g), _p(do), _p(k0), _p(v0), _p(dkf),
-                                _p(dvf), *(_p(out[n]) for n in ("dq", "dk", "dv", "dg", "dk0", "dv0")),
-                                B, H, T, dk, dv, m, float(tau), int(nthreads))
+    rc = _load().oracle_gsa_bwd_nl(_p(q), _p(k), _p(v), _p(g), _p(do), _p(k0), _p(v0), _p(dkf),
+                                   _p(dvf), *(_p(out[n]) for n in ("dq", "dk", "dv", "dg", "dk0", "dv0")),
+                                   B, H, T, dk, dv, m, float(tau), _nl(nonlinearity), int(nthreads))
     if rc:
         raise RuntimeError("oracle_gsa_bwd failed (%d)" % rc)
     return out

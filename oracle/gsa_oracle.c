@@ -74,6 +74,23 @@ static double slot_fn(double x, int act)
     }
 }
 
+/* Derivatives of the element-wise slot reads (act 1..4). */
+static double slot_grad(double x, int act)
+{
+    switch (act) {
+    case 1:
+        return 1.0;
+    case 2: {
+        double sg = 1.0 / (1.0 + exp(-x));
+        return sg * (1.0 + x * (1.0 - sg));
+    }
+    case 3:
+        return x > 0.0 ? 1.0 : 0.0;
+    default:
+        return x > 0.0 ? 2.0 * x : 0.0;
+    }
+}
+
 /* One GSA token step on one unit's slot states (Sec. 3.2). */
 static void gsa_token(const double *qt, const double *kt, const double *vt,
                       const double *gt, double *K, double *V, double *ot,
@@ -290,7 +307,7 @@ int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
 }
 
 /*
- * Gradients of the GSA forward (softmax read) with respect to q, k, v, the
+ * Gradients of the GSA forward with respect to q, k, v, the
  * gate logits g and the initial states, given the gradient dO of the outputs
  * and (nullable) the gradients dkf / dvf of the final states.  This is the
  * plain definition: reverse-mode differentiation of the token recurrence
@@ -302,7 +319,8 @@ int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
  * states after token t (starting from dkf, dvf):
  *   ds[c] = Vt[c,:] . dO_t              (o_t = Vt^T s_t)
  *   dV[c,:] += s_t[c] dO_t
- *   dz = s_t * (ds - s_t . ds)          (softmax Jacobian)
+ *   dz = s_t * (ds - s_t . ds)          (softmax Jacobian; for an element-wise
+ *                                        read s = f(z): dz = f'(z) * ds)
  *   dq_t = Kt^T dz,   dK[c,:] += dz[c] q_t
  *   dk_t = dK^T w_t,  dv_t = dV^T w_t    (w_t = 1 - alpha_t)
  *   dalpha[c] = dK[c,:] . (K_{t-1}[c,:] - k_t) + dV[c,:] . (V_{t-1}[c,:] - v_t)
@@ -311,17 +329,19 @@ int oracle_gsa_decode_step(const double *q, const double *k, const double *v,
  * dk0 / dv0 (nullable) receive the adjoints left after t = 0.
  * Layouts as for oracle_gsa_fwd; dO and dv [B,H,T,dv], dg [B,H,T,m].
  */
-int oracle_gsa_bwd(const double *q, const double *k, const double *v,
-                   const double *g, const double *dO, const double *k0,
-                   const double *v0, const double *dkf, const double *dvf,
-                   double *dq, double *dk, double *dv, double *dg, double *dk0,
-                   double *dv0, long B, long H, long T, long d_k, long d_v,
-                   long m, double tau, int nthreads)
+int oracle_gsa_bwd_nl(const double *q, const double *k, const double *v,
+                      const double *g, const double *dO, const double *k0,
+                      const double *v0, const double *dkf, const double *dvf,
+                      double *dq, double *dk, double *dv, double *dg,
+                      double *dk0, double *dv0, long B, long H, long T,
+                      long d_k, long d_v, long m, double tau, int act,
+                      int nthreads)
 {
     long units = B * H, u;
     int err = 0;
     if (!q || !k || !v || !g || !dO || !dq || !dk || !dv || !dg || B < 0 ||
-        H < 0 || T < 0 || d_k < 1 || d_v < 1 || m < 1 || !(tau > 0.0))
+        H < 0 || T < 0 || d_k < 1 || d_v < 1 || m < 1 || !(tau > 0.0) ||
+        act < 0 || act > 4)
         return 1;
 #ifdef _OPENMP
     if (nthreads < 1)
@@ -333,12 +353,13 @@ int oracle_gsa_bwd(const double *q, const double *k, const double *v,
         double *Ks = malloc((size_t)((T + 1) * m * d_k) * sizeof(double));
         double *Vs = malloc((size_t)((T + 1) * m * d_v) * sizeof(double));
         double *S = malloc((size_t)((T > 0 ? T : 1) * m) * sizeof(double));
+        double *Z = malloc((size_t)((T > 0 ? T : 1) * m) * sizeof(double));
         double *dK = calloc((size_t)(m * d_k), sizeof(double));
         double *dV = calloc((size_t)(m * d_v), sizeof(double));
         double *ds = malloc((size_t)m * sizeof(double));
         double *dz = malloc((size_t)m * sizeof(double));
         long t, c, x;
-        if (!Ks || !Vs || !S || !dK || !dV || !ds || !dz) {
+        if (!Ks || !Vs || !S || !Z || !dK || !dV || !ds || !dz) {
             err |= 2;
         } else {
             /* forward sweep: the states and the slot read weights */
@@ -362,16 +383,21 @@ int oracle_gsa_bwd(const double *q, const double *k, const double *v,
                     }
                     for (x = 0; x < d_v; x++)
                         Vn[c * d_v + x] = a * Vp[c * d_v + x] + w * vt[x];
-                    st[c] = acc;
+                    Z[t * m + c] = acc;
                     if (acc > zmax)
                         zmax = acc;
                 }
-                for (c = 0; c < m; c++) {
-                    st[c] = exp(st[c] - zmax);
-                    sum += st[c];
+                if (act == 0) {
+                    for (c = 0; c < m; c++) {
+                        st[c] = exp(Z[t * m + c] - zmax);
+                        sum += st[c];
+                    }
+                    for (c = 0; c < m; c++)
+                        st[c] /= sum;
+                } else {
+                    for (c = 0; c < m; c++)
+                        st[c] = slot_fn(Z[t * m + c], act);
                 }
-                for (c = 0; c < m; c++)
-                    st[c] /= sum;
             }
             /* reverse sweep */
             if (dkf)
@@ -396,7 +422,8 @@ int oracle_gsa_bwd(const double *q, const double *k, const double *v,
                         dV[c * d_v + x] += st[c] * dOt[x];
                 }
                 for (c = 0; c < m; c++)
-                    dz[c] = st[c] * (ds[c] - sds);
+                    dz[c] = act == 0 ? st[c] * (ds[c] - sds)
+                                     : slot_grad(Z[t * m + c], act) * ds[c];
                 for (x = 0; x < d_k; x++) {
                     double acc = 0.0;
                     for (c = 0; c < m; c++)
@@ -435,12 +462,25 @@ int oracle_gsa_bwd(const double *q, const double *k, const double *v,
         free(Ks);
         free(Vs);
         free(S);
+        free(Z);
         free(dK);
         free(dV);
         free(ds);
         free(dz);
     }
     return err;
+}
+
+/* The method as published: the softmax read. */
+int oracle_gsa_bwd(const double *q, const double *k, const double *v,
+                   const double *g, const double *dO, const double *k0,
+                   const double *v0, const double *dkf, const double *dvf,
+                   double *dq, double *dk, double *dv, double *dg, double *dk0,
+                   double *dv0, long B, long H, long T, long d_k, long d_v,
+                   long m, double tau, int nthreads)
+{
+    return oracle_gsa_bwd_nl(q, k, v, g, dO, k0, v0, dkf, dvf, dq, dk, dv, dg,
+                             dk0, dv0, B, H, T, d_k, d_v, m, tau, 0, nthreads);
 }
 
 int oracle_max_threads(void)

@@ -1,4 +1,5 @@
-"""Pins for the oracle's GSA backward (CPU only).
+"""Pins for the oracle's GSA backward (CPU only), for the softmax read and the
+element-wise reads of the ablation study (Table 2).
 
 The backward is the gradient of the forward, so it is pinned against
 numerical differentiation of the forward oracle (which its own pins tie to the
@@ -40,14 +41,15 @@ def loss(fwd, x, w, tau):
     return L
 
 
-def fwd_oracle(x, tau):
-    r = oracle.gsa_fwd(x["q"], x["k"], x["v"], x["g"], x["k0"], x["v0"], tau=tau)
+def fwd_oracle(x, tau, nonlinearity="softmax"):
+    r = oracle.gsa_fwd(x["q"], x["k"], x["v"], x["g"], x["k0"], x["v0"], tau=tau,
+                       nonlinearity=nonlinearity)
     return r["o"], r["kf"], r["vf"]
 
 
-def bwd_oracle(x, w, tau):
+def bwd_oracle(x, w, tau, nonlinearity="softmax"):
     r = oracle.gsa_bwd(x["q"], x["k"], x["v"], x["g"], w["o"], x["k0"], x["v0"], w["kf"], w["vf"],
-                       tau=tau)
+                       tau=tau, nonlinearity=nonlinearity)
     return {n: r["d" + n] for n in NAMES}
 
 
@@ -142,3 +144,26 @@ def test_batch_units_are_independent():
             part = bwd_oracle(xs, ws, 8.0)
             for n in NAMES:
                 assert np.array_equal(part[n][0, 0], full[n][b, h]), n
+
+
+@pytest.mark.parametrize("nl", ["identity", "swish", "relu", "relu2"])
+@pytest.mark.parametrize("T", [1, 13])
+def test_directional_derivatives_elementwise_reads(nl, T):
+    """The backward of each element-wise read against central differences of
+    the forward with that read."""
+    x, w = draw(1, 2, T, 5, 4, 3, seed=40 + T)
+
+    def fwd(xx, tau):
+        return fwd_oracle(xx, tau, nl)
+    errs = directional_errors(fwd, bwd_oracle(x, w, 8.0, nl), x, w, 8.0, seed=T + 1)
+    assert max(errs.values()) < 1e-7, (nl, errs)
+
+
+def test_identity_read_gradient_of_q_is_linear_map():
+    """With no non-linearity and alpha = 1 (frozen states K0, V0) the output
+    is o_t = V0^T K0 q_t, so dq_t = K0^T V0 dO_t exactly."""
+    x, w = draw(1, 1, 7, 5, 4, 3, seed=50)
+    x["g"][:] = np.inf
+    gr = bwd_oracle(x, w, 8.0, "identity")
+    K0, V0 = x["k0"][0, 0], x["v0"][0, 0]
+    assert np.allclose(gr["q"][0, 0], w["o"][0, 0] @ V0.T @ K0, rtol=1e-13, atol=1e-13)

@@ -44,7 +44,10 @@ MUTATIONS = [
     ("relu2_not_squared", "return x > 0.0 ? x * x : 0.0;", "return x > 0.0 ? x : 0.0;"),
     ("read_codes_shifted", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c], act + 1);"),
     ("read_of_scaled_scores", "s[c] = slot_fn(z[c], act);", "s[c] = slot_fn(z[c] * 0.5, act);"),
-    ("bwd_softmax_jacobian_unshifted", "dz[c] = st[c] * (ds[c] - sds);", "dz[c] = st[c] * ds[c];"),
+    ("bwd_softmax_jacobian_unshifted", "st[c] * (ds[c] - sds)", "st[c] * ds[c]"),
+    ("bwd_swish_grad_without_product_rule", "return sg * (1.0 + x * (1.0 - sg));", "return sg;"),
+    ("bwd_relu2_grad_halved", "return x > 0.0 ? 2.0 * x : 0.0;", "return x > 0.0 ? x : 0.0;"),
+    ("bwd_elementwise_read_grad_as_softmax", ": slot_grad(Z[t * m + c], act) * ds[c];", ": st[c] * ds[c];"),
     ("bwd_read_of_previous_state", "acc += Vn[c * d_v + x] * dOt[x];", "acc += Vp[c * d_v + x] * dOt[x];"),
     ("bwd_gate_of_new_state", "da += dK[c * d_k + x] * (Kp[c * d_k + x] - kt[x]);",
      "da += dK[c * d_k + x] * (Kn[c * d_k + x] - kt[x]);"),
@@ -68,6 +71,7 @@ def _build(tmp_path, text, name):
     lib.oracle_gsa_fwd_nl.argtypes = [P] * 11 + [L] * 6 + [D, I, I]
     lib.oracle_gla_fwd_gm.argtypes = [P] * 7 + [L] * 5 + [D, I, I]
     lib.oracle_gsa_bwd.argtypes = [P] * 15 + [L] * 6 + [D, I]
+    lib.oracle_gsa_bwd_nl.argtypes = [P] * 15 + [L] * 6 + [D, I, I]
     return lib
 
 
@@ -159,22 +163,24 @@ def _pins_pass(lib):
 
 
 def _bwd_pin(lib):
-    def fwd(x, tau):
-        return _gsa(lib, x["q"], x["k"], x["v"], x["g"], x["k0"], x["v0"], tau=tau)
-
     ok = True
-    for seed, T in ((3, 9), (4, 1)):
-        x, w = test_oracle_bwd.draw(1, 1, T, 5, 5, 4, seed=seed)
-        B, H, _, dk = x["q"].shape
-        dv, m = x["v"].shape[-1], x["g"].shape[-1]
-        gr = {n: np.empty_like(x[n]) for n in test_oracle_bwd.NAMES}
-        rc = lib.oracle_gsa_bwd(*(_p(x[n]) for n in "qkvg"), _p(w["o"]), _p(x["k0"]), _p(x["v0"]),
-                                _p(w["kf"]), _p(w["vf"]),
-                                *(_p(gr[n]) for n in test_oracle_bwd.NAMES), B, H, T, dk, dv, m,
-                                8.0, 1)
-        ok &= rc == 0
-        errs = test_oracle_bwd.directional_errors(fwd, gr, x, w, 8.0, seed=seed)
-        ok &= max(errs.values()) < 1e-7
+    for act in (0, 1, 2, 3, 4):
+        def fwd(x, tau):
+            return _gsa(lib, x["q"], x["k"], x["v"], x["g"], x["k0"], x["v0"], tau=tau,
+                        act=None if act == 0 else act)
+
+        for seed, T in ((3, 9), (4, 1)):
+            x, w = test_oracle_bwd.draw(1, 1, T, 5, 5, 4, seed=seed)
+            B, H, _, dk = x["q"].shape
+            dv, m = x["v"].shape[-1], x["g"].shape[-1]
+            gr = {n: np.empty_like(x[n]) for n in test_oracle_bwd.NAMES}
+            rc = lib.oracle_gsa_bwd_nl(*(_p(x[n]) for n in "qkvg"), _p(w["o"]), _p(x["k0"]),
+                                       _p(x["v0"]), _p(w["kf"]), _p(w["vf"]),
+                                       *(_p(gr[n]) for n in test_oracle_bwd.NAMES), B, H, T, dk,
+                                       dv, m, 8.0, act, 1)
+            ok &= rc == 0
+            errs = test_oracle_bwd.directional_errors(fwd, gr, x, w, 8.0, seed=seed)
+            ok &= max(errs.values()) < 1e-7
     return ok
 
 
