@@ -262,7 +262,8 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
                     void* const* events);
 
 /*
- * GSA backward (softmax read): the gradients of gsa_fwd's outputs (and final
+ * GSA backward (softmax read; gsa_bwd_ex below for the other reads): the
+ * gradients of gsa_fwd's outputs (and final
  * states) with respect to its inputs.  GSA Sec. 3.2-3.3 define the function;
  * App. B the training scheme followed here: the two gated passes are
  * differentiated in reverse order, the write intensity 1 - alpha collects the
@@ -293,6 +294,17 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const vo
             void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
             int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
             void* stream, void* const* events);
+/* gsa_bwd for the forward with the slot read chosen by the caller (a
+ * gsa_slot_nonlinearity code, else GSA_ERR_SHAPE): the gradients of gsa_fwd_ex
+ * with that code.  For an element-wise read s = f(z) the softmax Jacobian is
+ * replaced by f'(z) (Swish: sigmoid(z) (1 + z (1 - sigmoid(z))); ReLU: the
+ * step z > 0; ReLU^2: 2 max(z, 0)).  Everything else as for gsa_bwd, which is
+ * this with GSA_SLOT_SOFTMAX. */
+int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+               const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+               void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+               int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+               int nonlinearity, void* stream, void* const* events);
 
 /*
  * Calibration kernels for measurements: what this GPU sustains, reported by

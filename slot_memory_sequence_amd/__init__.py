@@ -80,6 +80,7 @@ lib.gsa_bwd_supported.argtypes = [_I] * 4
 lib.gsa_bwd_workspace_bytes.argtypes = [_I] * 6
 lib.gsa_bwd_workspace_bytes.restype = _S
 lib.gsa_bwd.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _P, _P]
+lib.gsa_bwd_ex.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -352,12 +353,15 @@ def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m) -> int:
 
 
 def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
-            state_grads=False, out=None, workspace=None, stream=None, events=None):
+            state_grads=False, out=None, workspace=None, stream=None, events=None,
+            nonlinearity="softmax"):
     """GSA backward (softmax read): the gradients of gsa_fwd(q, k, v, g, k0,
     v0, tau=tau) given d_o [B,H,T,dv] (the gradient of o) and optional float32
     d_kf [B,H,m,dk] / d_vf [B,H,m,dv] (those of the final states).
     Returns (d_q, d_k, d_v, d_g, d_k0, d_v0); d_k0 / d_v0 (float32) are None
-    unless state_grads.  out: optional (d_q, d_k, d_v, d_g) to write into."""
+    unless state_grads.  out: optional (d_q, d_k, d_v, d_g) to write into.
+    nonlinearity: the slot read of the forward being differentiated, as for
+    gsa_fwd."""
     torch = _torch()
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
         _check(t, n, q.dtype)
@@ -379,11 +383,11 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
     nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.gsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0), _ptr(d_kf),
-                     _ptr(d_vf), *(_ptr(x) for x in outs), _ptr(sg[0]), _ptr(sg[1]), B, H, T, dk,
-                     dv, m, float(tau), _dt(q), _ptr(workspace),
-                     0 if workspace is None else workspace.numel(), _stream(stream),
-                     _events(events))
+    st = lib.gsa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0),
+                        _ptr(d_kf), _ptr(d_vf), *(_ptr(x) for x in outs), _ptr(sg[0]), _ptr(sg[1]),
+                        B, H, T, dk, dv, m, float(tau), _dt(q), _ptr(workspace),
+                        0 if workspace is None else workspace.numel(), _nl(nonlinearity),
+                        _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_bwd", st)
     return (*outs, sg[0], sg[1])

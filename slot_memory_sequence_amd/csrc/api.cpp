@@ -443,13 +443,13 @@ int gsa_bwd_supported(int dk, int dv, int m, int dtype) {
   return gsa::gsa_bwd_dispatch(dtype, dk, dv, m, nullptr, true) == 0;
 }
 
-int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,
-            const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
-            void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
-            int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
-            void* stream, void* const* events) {
+int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+               const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+               void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+               int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+               int nonlinearity, void* stream, void* const* events) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) ||
-      !std::isfinite(tau) || !dtype_ok(dtype))
+      !std::isfinite(tau) || !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
     return GSA_ERR_SHAPE;
   if (!gsa_bwd_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
@@ -485,10 +485,20 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const vo
   a.k0 = k0; a.v0 = v0; a.dkf = d_kf; a.dvf = d_vf;
   a.dq = d_q; a.dk = d_k; a.dv = d_v; a.dg = d_g; a.dk0 = d_k0; a.dv0 = d_v0;
   a.ws = (float*)workspace;
-  a.B = B; a.H = H; a.T = T; a.tau = tau; a.stream = stream; a.events = events;
+  a.B = B; a.H = H; a.T = T; a.tau = tau; a.act = nonlinearity; a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_bwd_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();
+}
+
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+            const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+            void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+            int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+            void* stream, void* const* events) {
+  return gsa_bwd_ex(q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, B, H, T,
+                    dk, dv, m, tau, dtype, workspace, workspace_bytes, GSA_SLOT_SOFTMAX, stream,
+                    events);
 }
 
 }  // extern "C"

@@ -164,4 +164,17 @@ __device__ __forceinline__ float slot_act(float x) {
   }
 }
 
+// Their derivatives (the backward's dz = f'(z) ds): 1; sigmoid(x) (1 + x (1 -
+// sigmoid(x))); the step x > 0; 2 max(x, 0).
+template <int ACT>
+__device__ __forceinline__ float slot_act_grad(float x) {
+  static_assert(ACT >= kActIdentity && ACT <= kActRelu2, "element-wise slot non-linearity");
+  if constexpr (ACT == kActIdentity) return 1.f;
+  else if constexpr (ACT == kActSwish) {
+    const float sg = 1.f / (1.f + __expf(-x));
+    return sg * (1.f + x * (1.f - sg));
+  } else if constexpr (ACT == kActRelu) return x > 0.f ? 1.f : 0.f;
+  else return x > 0.f ? 2.f * x : 0.f;
+}
+
 }  // namespace gsa

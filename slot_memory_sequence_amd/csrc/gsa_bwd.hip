@@ -329,8 +329,9 @@ bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __r
 // reverse map (sum over the chunk of e^{G_t} dz_t q_t^T and e^{G_t} s_t dO_t^T,
 // G from the chunk start), and per token s, dz and z dz + s ds.  The chunk
 // holding the last token also forms the final-state term dkf . K_T + dvf . V_T
-// per slot (zero without final-state gradients).
-template <typename T, int DK, int DV, int M>
+// per slot (zero without final-state gradients).  ACT: the slot read, the
+// softmax (dz = s (ds - s . ds)) or an element-wise f (s = f(z), dz = f'(z) ds).
+template <typename T, int DK, int DV, int M, int ACT>
 __global__ void __launch_bounds__(NT)
 bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
              const float* __restrict__ al, const float* __restrict__ wr, const T* __restrict__ dOo,
@@ -406,24 +407,27 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       ds[i] = row_sum16(dp);
     }
     // softmax statistics of this wave's slots: max, sum of e^{z - max}, and
-    // sum of e^{z - max} ds; then combined over the four waves
-    float mx = z[0];
+    // sum of e^{z - max} ds; then combined over the four waves (the barrier
+    // also publishes the previous token's dq partial sums)
+    if constexpr (ACT == kActSoftmax) {
+      float mx = z[0];
 #pragma unroll
-    for (int i = 1; i < S::SPT; i++) mx = fmaxf(mx, z[i]);
-    mx = max_sg4(mx);
-    float se = 0.f, sd = 0.f;
+      for (int i = 1; i < S::SPT; i++) mx = fmaxf(mx, z[i]);
+      mx = max_sg4(mx);
+      float se = 0.f, sd = 0.f;
 #pragma unroll
-    for (int i = 0; i < S::SPT; i++) {
-      const float e = __expf(z[i] - mx);
-      se += e;
-      sd += e * ds[i];
-    }
-    se = sum_sg4(se);
-    sd = sum_sg4(sd);
-    if (th.l == 0) {
-      red[b][th.w][0] = mx;
-      red[b][th.w][1] = se;
-      red[b][th.w][2] = sd;
+      for (int i = 0; i < S::SPT; i++) {
+        const float e = __expf(z[i] - mx);
+        se += e;
+        sd += e * ds[i];
+      }
+      se = sum_sg4(se);
+      sd = sum_sg4(sd);
+      if (th.l == 0) {
+        red[b][th.w][0] = mx;
+        red[b][th.w][1] = se;
+        red[b][th.w][2] = sd;
+      }
     }
     __syncthreads();
     if (n > 0 && threadIdx.x < DK) {  // dq of the previous token
@@ -431,22 +435,30 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
                       dqb[b ^ 1][3][threadIdx.x];
       dq[(row - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
     }
-    float Mx = red[b][0][0];
-#pragma unroll
-    for (int x = 1; x < 4; x++) Mx = fmaxf(Mx, red[b][x][0]);
-    float Se = 0.f, Sd = 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; x++) {
-      const float f = __expf(red[b][x][0] - Mx);
-      Se += red[b][x][1] * f;
-      Sd += red[b][x][2] * f;
-    }
-    const float inv = __builtin_amdgcn_rcpf(Se), dbar = Sd * inv;
     float s[S::SPT], dz[S::SPT];
+    if constexpr (ACT == kActSoftmax) {
+      float Mx = red[b][0][0];
 #pragma unroll
-    for (int i = 0; i < S::SPT; i++) {
-      s[i] = __expf(z[i] - Mx) * inv;
-      dz[i] = s[i] * (ds[i] - dbar);
+      for (int x = 1; x < 4; x++) Mx = fmaxf(Mx, red[b][x][0]);
+      float Se = 0.f, Sd = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; x++) {
+        const float f = __expf(red[b][x][0] - Mx);
+        Se += red[b][x][1] * f;
+        Sd += red[b][x][2] * f;
+      }
+      const float inv = __builtin_amdgcn_rcpf(Se), dbar = Sd * inv;
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) {
+        s[i] = __expf(z[i] - Mx) * inv;
+        dz[i] = s[i] * (ds[i] - dbar);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::SPT; i++) {
+        s[i] = slot_act<ACT>(z[i]);
+        dz[i] = slot_act_grad<ACT>(z[i]) * ds[i];
+      }
     }
     // dq partial sums over this wave's slots: all shuffles first, then one
     // store block (so that the cross-lane moves are in flight together)
@@ -705,7 +717,7 @@ inline Ws carve(float* w, size_t U, size_t T, int dk, int dv, int m) {
   return s;
 }
 
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, int ACT>
 int launch(const GsaBwdLaunch& a) {
   const int U = a.B * a.H, Tn = a.T, P = (Tn + C - 1) / C;
   const float inv_tau = 1.0f / a.tau;
@@ -726,7 +738,7 @@ int launch(const GsaBwdLaunch& a) {
   static const bool lds_set = [] {  // once per instantiation and process
     (void)hipFuncSetAttribute((const void*)bwd_map<T, DK, DV, M>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, MapLds<T, DK, DV, M>::bytes);
-    (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M, ACT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
     (void)hipFuncSetAttribute((const void*)bwd_walk_rev<T, DK, DV, M>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
@@ -741,7 +753,7 @@ int launch(const GsaBwdLaunch& a) {
                      inv_tau);
   hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, a.k0, a.v0,
                      (float*)nullptr, (float*)nullptr, U, P);
-  launch_timed(bwd_walk_fwd<T, DK, DV, M>, grid, dim3(NT), SG::bytes, a.stream, a.events, 0, 1, q, k, v,
+  launch_timed(bwd_walk_fwd<T, DK, DV, M, ACT>, grid, dim3(NT), SG::bytes, a.stream, a.events, 0, 1, q, k, v,
                (const float*)w.al, (const float*)w.wr, dO,
                (const float*)w.st, a.dkf, a.dvf, (T*)a.dq, w.xu, w.sw, w.dzw, w.hw, w.fs, Tn, P);
   hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, a.dkf, a.dvf,
@@ -755,6 +767,18 @@ int launch(const GsaBwdLaunch& a) {
   return 0;
 }
 
+template <typename T, int DK, int DV, int M>
+int launch_act(const GsaBwdLaunch& a) {
+  switch (a.act) {
+    case kActSoftmax: return launch<T, DK, DV, M, kActSoftmax>(a);
+    case kActIdentity: return launch<T, DK, DV, M, kActIdentity>(a);
+    case kActSwish: return launch<T, DK, DV, M, kActSwish>(a);
+    case kActRelu: return launch<T, DK, DV, M, kActRelu>(a);
+    case kActRelu2: return launch<T, DK, DV, M, kActRelu2>(a);
+    default: return -1;
+  }
+}
+
 }  // namespace bwd
 
 size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m) {
@@ -763,7 +787,7 @@ size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m) {
 
 #define GSA_BWD_CASE(TY, DT, DK_, DV_, M_)                                    \
   if (dtype == DT && dk == DK_ && dv == DV_ && m == M_)                       \
-    return query ? 0 : bwd::launch<TY, DK_, DV_, M_>(*a);
+    return query ? 0 : bwd::launch_act<TY, DK_, DV_, M_>(*a);
 
 int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query) {
   GSA_BWD_CASE(bf16_t, 1, 128, 128, 64)

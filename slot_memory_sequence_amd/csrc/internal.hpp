@@ -88,6 +88,7 @@ struct GsaBwdLaunch {
   float* ws;
   int B, H, T;
   float tau;
+  int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t around the two token-walk kernels
 };

@@ -271,3 +271,18 @@ def test_bwd_validation(gsa):
     assert call(dk0=FAKE + 0x10) == 7                   # d_k0 overlaps q
     assert call(ws=FAKE + 0x400000) == 7                # workspace overlaps d_o
     assert call(wsb=need - 16) == 5 and call(ws=None) == 5
+
+
+def test_bwd_ex_nonlinearity_validation(gsa):
+    f = gsa.lib.gsa_bwd_ex
+    P = ctypes.c_void_p
+    need = gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64)
+    args = [P(FAKE), P(FAKE + 0x100000), P(FAKE + 0x200000), P(FAKE + 0x300000), P(FAKE + 0x400000),
+            None, None, None, None, P(FAKE + 0x500000), P(FAKE + 0x600000), P(FAKE + 0x700000),
+            P(FAKE + 0x800000), None, None, 1, 1, 64, 128, 128, 64, 8.0, 1,
+            P(FAKE + 0x10000000), need]
+    assert f(*args, 5, None, None) == 2 and f(*args, -1, None, None) == 2
+    bad = list(args)
+    bad[9] = P(FAKE + 0x10)             # d_q overlaps q: the codes 0..4 pass the shape check
+    for code in range(5):
+        assert f(*bad, code, None, None) == 7

@@ -37,16 +37,16 @@ def _opt(x):
     return None if x is None else x.f64
 
 
-def _run(gsa, torch, inp, gi, tau):
+def _run(gsa, torch, inp, gi, tau, nl="softmax"):
     dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
     ddev = {n: to_dev(gi[n], torch) for n in ("do", "dkf", "dvf")}
     out = gsa.gsa_bwd(dev["q"], dev["k"], dev["v"], dev["g"], ddev["do"], dev["k0"], dev["v0"],
-                      ddev["dkf"], ddev["dvf"], tau=tau, state_grads=True)
+                      ddev["dkf"], ddev["dvf"], tau=tau, state_grads=True, nonlinearity=nl)
     torch.cuda.synchronize()
     return dict(zip(GRADS, out))
 
 
-def _ref(inp, gi, tau, units=None):
+def _ref(inp, gi, tau, units=None, nl="softmax"):
     """The oracle on all units, or on the listed flat unit indices."""
     def sel(x):
         if x is None:
@@ -57,7 +57,7 @@ def _ref(inp, gi, tau, units=None):
         return a.reshape(-1, *a.shape[2:])[units][:, None]
     return oracle.gsa_bwd(*(sel(inp[n]) for n in "qkvg"), sel(gi["do"]), sel(inp["k0"]),
                           sel(inp["v0"]), sel(gi["dkf"]), sel(gi["dvf"]), tau=tau,
-                          nthreads=oracle.max_threads())
+                          nthreads=oracle.max_threads(), nonlinearity=nl)
 
 
 def _compare(got, ref, dtype, label, units=None):
@@ -71,16 +71,17 @@ def _compare(got, ref, dtype, label, units=None):
     assert max(errs.values()) <= TOL[dtype], errs
 
 
-def _check(gsa, torch, B, H, T, d, m, dtype, init, final, tau=8.0, seed=0, edit=None):
+def _check(gsa, torch, B, H, T, d, m, dtype, init, final, tau=8.0, seed=0, edit=None,
+           nl="softmax"):
     inp = synth.gsa_inputs(B, H, T, d, d, m, dtype=dtype, seed=seed,
                            init_std=0.1 if init else None)
     if edit:
         edit(inp)
     gi = synth.gsa_grad_inputs(B, H, T, d, d, m, dtype=dtype, seed=seed + 1000,
                                final_std=1.0 if final else None)
-    got = _run(gsa, torch, inp, gi, tau)
-    _compare(got, _ref(inp, gi, tau), dtype,
-             "B%d H%d T%d d%d m%d %s init=%s final=%s" % (B, H, T, d, m, dtype, init, final))
+    got = _run(gsa, torch, inp, gi, tau, nl)
+    _compare(got, _ref(inp, gi, tau, nl=nl), dtype,
+             "B%d H%d T%d d%d m%d %s init=%s final=%s %s" % (B, H, T, d, m, dtype, init, final, nl))
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
@@ -186,3 +187,31 @@ def test_bwd_long_context_sampled(gsa, torch):
     got = _run(gsa, torch, inp, gi, w["tau"])
     units = [0, w["B"] * w["H"] - 1]
     _compare(got, _ref(inp, gi, w["tau"], units), "bf16", "B1 H8 T16384 sampled", units)
+
+
+ELEMENTWISE = ["identity", "swish", "relu", "relu2"]
+
+
+@pytest.mark.parametrize("nl", ELEMENTWISE)
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
+def test_bwd_elementwise_reads(gsa, torch, nl, dtype, d, m):
+    """The backward of the forward with each element-wise read of Table 2."""
+    _check(gsa, torch, 2, 2, 130, d, m, dtype, init=True, final=True, seed=60, nl=nl)
+
+
+@pytest.mark.parametrize("nl", ["swish", "relu2"])
+def test_bwd_elementwise_reads_extreme_gates(gsa, torch, nl):
+    _check(gsa, torch, 1, 2, 300, 128, 64, "bf16", init=True, final=True, seed=61, edit=_extreme,
+           nl=nl)
+
+
+def test_bwd_elementwise_read_training_shape_sampled(gsa, torch):
+    w = synth.WORKLOADS["gsa_bf16_train_T2048"]
+    inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                           seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
+                           init_std=w["init_std"])
+    gi = synth.gsa_grad_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                               seed=3)
+    got = _run(gsa, torch, inp, gi, w["tau"], "swish")
+    units = [3, w["B"] * w["H"] - 2]
+    _compare(got, _ref(inp, gi, w["tau"], units, "swish"), "bf16", "B8 H4 T2048 swish sampled", units)
