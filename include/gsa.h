@@ -307,6 +307,28 @@ int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const
                int nonlinearity, void* stream, void* const* events);
 
 /*
+ * gsa_bwd over a packed batch of n_seqs variable-length sequences laid out as
+ * for gsa_fwd_varlen: the gradients of gsa_fwd_varlen (softmax read).
+ *   q, k, d_q, d_k [H, total, dk]; v, d_o, d_v [H, total, dv]; g, d_g
+ *   [H, total, m] (dtype), total = cu_seqlens[n_seqs]; cu_seqlens (host,
+ *   n_seqs + 1 ints: 0, non-decreasing, else GSA_ERR_SHAPE);
+ *   k0, v0, d_kf, d_vf, d_k0, d_v0 [n_seqs, H, m, d] float32, nullable as for
+ *   gsa_bwd.  Each sequence is an independent run: an empty sequence's
+ *   initial-state gradients are its final-state gradients.
+ *   workspace: at least gsa_bwd_varlen_workspace_bytes(cu_seqlens, n_seqs, H,
+ *   dk, dv, m) bytes.  Runs in groups of at most 256 sequences one after the
+ *   other on the stream (min(n_seqs, 256) * H <= 65535); events as for
+ *   gsa_bwd when there is one group, else they stamp the whole call.
+ * Other arguments, errors and shapes as for gsa_bwd.
+ */
+size_t gsa_bwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv, int m);
+int gsa_bwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+                   const int* cu_seqlens, int n_seqs, int H, const float* k0, const float* v0,
+                   const float* d_kf, const float* d_vf, void* d_q, void* d_k, void* d_v, void* d_g,
+                   float* d_k0, float* d_v0, int dk, int dv, int m, float tau, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
+/*
  * Calibration kernels for measurements: what this GPU sustains, reported by
  * the benchmark beside the published peaks.  Not part of the method.
  *

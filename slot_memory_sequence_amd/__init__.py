@@ -81,6 +81,9 @@ lib.gsa_bwd_workspace_bytes.argtypes = [_I] * 6
 lib.gsa_bwd_workspace_bytes.restype = _S
 lib.gsa_bwd.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _P, _P]
 lib.gsa_bwd_ex.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
+lib.gsa_bwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 5
+lib.gsa_bwd_varlen_workspace_bytes.restype = _S
+lib.gsa_bwd_varlen.argtypes = [_P] * 5 + [_P, _I, _I] + [_P] * 10 + [_I] * 3 + [_F, _I, _P, _S, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -390,6 +393,42 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
                         _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_bwd", st)
+    return (*outs, sg[0], sg[1])
+
+
+def gsa_bwd_varlen_workspace_bytes(cu_seqlens, H, dk, dv, m) -> int:
+    arr, n = _cu_array(cu_seqlens)
+    return int(lib.gsa_bwd_varlen_workspace_bytes(ctypes.cast(arr, _P), n, H, dk, dv, m))
+
+
+def gsa_bwd_varlen(q, k, v, g, d_o, cu_seqlens, k0=None, v0=None, d_kf=None, d_vf=None, *,
+                   tau=8.0, state_grads=False, workspace=None, stream=None, events=None):
+    """GSA backward over a packed batch (layout of gsa_fwd_varlen: q, k, g, d_o
+    [H, total, d]; host offsets cu_seqlens; states [n, H, m, d]).  Returns
+    (d_q, d_k, d_v, d_g, d_k0, d_v0); the state gradients are None unless
+    state_grads."""
+    torch = _torch()
+    for nm, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
+        _check(t, nm, q.dtype)
+    for nm, t in (("k0", k0), ("v0", v0), ("d_kf", d_kf), ("d_vf", d_vf)):
+        _check(t, nm, torch.float32)
+    arr, n = _cu_array(cu_seqlens)
+    H, _, dk = q.shape
+    dv, m = v.shape[-1], g.shape[-1]
+    outs = [torch.empty_like(x) for x in (q, k, v, g)]
+    sg = [None, None]
+    if state_grads:
+        sg = [torch.empty((n, H, m, d), dtype=torch.float32, device=q.device) for d in (dk, dv)]
+    nbytes = int(lib.gsa_bwd_varlen_workspace_bytes(ctypes.cast(arr, _P), n, H, dk, dv, m))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), ctypes.cast(arr, _P), n, H,
+                            _ptr(k0), _ptr(v0), _ptr(d_kf), _ptr(d_vf), *(_ptr(x) for x in outs),
+                            _ptr(sg[0]), _ptr(sg[1]), dk, dv, m, float(tau), _dt(q), _ptr(workspace),
+                            0 if workspace is None else workspace.numel(), _stream(stream),
+                            _events(events))
+    if st:
+        raise GsaError("gsa_bwd_varlen", st)
     return (*outs, sg[0], sg[1])
 
 

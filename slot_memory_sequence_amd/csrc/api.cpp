@@ -435,7 +435,17 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
 
 size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m) {
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1) return 0;
-  return gsa::gsa_bwd_ws_bytes((size_t)B * H, (size_t)T, dk, dv, m);
+  const size_t units = (size_t)B * H;
+  return gsa::gsa_bwd_ws_bytes(units, ((size_t)T + kChunk - 1) / kChunk, units * T, dk, dv, m);
+}
+
+size_t gsa_bwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv, int m) {
+  int tmax = 0;
+  long long chunks = 0;
+  if (H < 0 || dk < 1 || dv < 1 || m < 1 || !varlen_ok(cu_seqlens, n_seqs, &tmax, &chunks)) return 0;
+  return gsa::gsa_bwd_ws_bytes((size_t)std::min(n_seqs, gsa::kMaxVarSeqs) * H,
+                               ((size_t)tmax + kChunk - 1) / kChunk,
+                               (size_t)H * (size_t)cu_seqlens[n_seqs], dk, dv, m);
 }
 
 int gsa_bwd_supported(int dk, int dv, int m, int dtype) {
@@ -443,19 +453,21 @@ int gsa_bwd_supported(int dk, int dv, int m, int dtype) {
   return gsa::gsa_bwd_dispatch(dtype, dk, dv, m, nullptr, true) == 0;
 }
 
-int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* d_o,
-               const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
-               void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
-               int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
-               int nonlinearity, void* stream, void* const* events) {
-  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) ||
-      !std::isfinite(tau) || !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
-    return GSA_ERR_SHAPE;
+// Validation and launch shared by the dense batch (cu == nullptr: B sequences
+// of T tokens) and the packed variable-length batch (B = n sequences, T = the
+// longest, ntok rows in all).
+static int bwd_run(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+                   const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+                   void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+                   size_t ntok, const int* cu, int dk, int dv, int m, float tau, int dtype,
+                   void* workspace, size_t workspace_bytes, int nonlinearity, void* stream,
+                   void* const* events) {
   if (!gsa_bwd_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
   if (units == 0) return GSA_OK;
-  if (units > 65535) return GSA_ERR_UNSUPPORTED;  // one grid row per unit
-  const size_t ntok = (size_t)units * T;
+  // one grid row per unit of a launch sequence (a packed batch launches groups)
+  const long long launch_units = cu ? (long long)std::min(B, gsa::kMaxVarSeqs) * H : units;
+  if (launch_units > 65535) return GSA_ERR_UNSUPPORTED;
   if (ntok > 0 && (!q || !k || !v || !g || !d_o || !d_q || !d_k || !d_v || !d_g))
     return GSA_ERR_NULL;
   const void* ptrs[] = {q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, workspace};
@@ -469,7 +481,9 @@ int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const
   const Range rdq = rng(d_q, ntok * dk * es), rdk = rng(d_k, ntok * dk * es),
               rdv = rng(d_v, ntok * dv * es), rdg = rng(d_g, ntok * m * es);
   const Range rdk0 = rng(d_k0, sk), rdv0 = rng(d_v0, sv);
-  const size_t need = T > 0 ? gsa::gsa_bwd_ws_bytes((size_t)units, (size_t)T, dk, dv, m) : 0;
+  const size_t need = T > 0 ? gsa::gsa_bwd_ws_bytes((size_t)launch_units, ((size_t)T + kChunk - 1) / kChunk,
+                                                    ntok, dk, dv, m)
+                            : 0;
   const Range rws = rng(workspace, need);
   const Range outs[] = {rdq, rdk, rdv, rdg, rdk0, rdv0, rws};
   const Range ins[] = {rq, rk, rv, rg, rdo, rk0, rv0, rkf, rvf};
@@ -485,10 +499,40 @@ int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const
   a.k0 = k0; a.v0 = v0; a.dkf = d_kf; a.dvf = d_vf;
   a.dq = d_q; a.dk = d_k; a.dv = d_v; a.dg = d_g; a.dk0 = d_k0; a.dv0 = d_v0;
   a.ws = (float*)workspace;
-  a.B = B; a.H = H; a.T = T; a.tau = tau; a.act = nonlinearity; a.stream = stream; a.events = events;
+  a.B = B; a.H = H; a.T = T; a.tau = tau; a.act = nonlinearity;
+  a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
+  a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_bwd_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
   return hip_status();
+}
+
+int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+               const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+               void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+               int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+               int nonlinearity, void* stream, void* const* events) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) ||
+      !std::isfinite(tau) || !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
+    return GSA_ERR_SHAPE;
+  return bwd_run(q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, B, H, T,
+                 (size_t)B * H * T, nullptr, dk, dv, m, tau, dtype, workspace, workspace_bytes,
+                 nonlinearity, stream, events);
+}
+
+int gsa_bwd_varlen(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+                   const int* cu_seqlens, int n_seqs, int H, const float* k0, const float* v0,
+                   const float* d_kf, const float* d_vf, void* d_q, void* d_k, void* d_v, void* d_g,
+                   float* d_k0, float* d_v0, int dk, int dv, int m, float tau, int dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  int tmax = 0;
+  long long chunks = 0;
+  if (H < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
+      !dtype_ok(dtype) || !varlen_ok(cu_seqlens, n_seqs, &tmax, &chunks))
+    return GSA_ERR_SHAPE;
+  return bwd_run(q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, n_seqs, H, tmax,
+                 (size_t)H * (size_t)cu_seqlens[n_seqs], cu_seqlens, dk, dv, m, tau, dtype, workspace,
+                 workspace_bytes, GSA_SLOT_SOFTMAX, stream, events);
 }
 
 int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,

@@ -186,11 +186,11 @@ struct MapLds {
   static constexpr unsigned bytes = kv_bytes + C * M * sizeof(float) + (NT / M) * M * sizeof(float);
 };
 
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, class Seq>
 __global__ void __launch_bounds__(NT)
 bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict__ gg,
         float* __restrict__ st, float* __restrict__ dec, float* __restrict__ al,
-        float* __restrict__ wr, int T_, int P, float inv_tau) {
+        float* __restrict__ wr, Seq seq, int P, float inv_tau) {
   using S = Shape<DK, DV, M>;
   constexpr int PARTS = NT / M, TPP = C / PARTS;  // parts per slot, tokens per part
   static_assert(NT % M == 0 && C % PARTS == 0, "gate split");
@@ -201,8 +201,9 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
   float* ptot = sA + C * M;                                                     // [PARTS][M]
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
-  const int t0 = p * C, t1 = min(T_, t0 + C), rows = t1 - t0;
-  const size_t row0 = (size_t)u * T_ + t0;
+  const bfk::Span sp = seq.span(u);
+  const int t0 = p * C, rows = max(0, min(sp.len, t0 + C) - t0);  // 0: past the sequence's end
+  const size_t row0 = sp.base + t0;
   copy_rows(sk, kk + row0 * DK, rows * DK);
   copy_rows(sv, vv + row0 * DV, rows * DV);
   {
@@ -331,14 +332,14 @@ bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __r
 // holding the last token also forms the final-state term dkf . K_T + dvf . V_T
 // per slot (zero without final-state gradients).  ACT: the slot read, the
 // softmax (dz = s (ds - s . ds)) or an element-wise f (s = f(z), dz = f'(z) ds).
-template <typename T, int DK, int DV, int M, int ACT>
+template <typename T, int DK, int DV, int M, int ACT, class Seq>
 __global__ void __launch_bounds__(NT)
 bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
              const float* __restrict__ al, const float* __restrict__ wr, const T* __restrict__ dOo,
              const float* __restrict__ st,
              const float* __restrict__ dkf, const float* __restrict__ dvf, T* __restrict__ dq,
              float* __restrict__ xu, float* __restrict__ sw, float* __restrict__ dzw,
-             float* __restrict__ hw, float* __restrict__ fs, int T_, int P) {
+             float* __restrict__ hw, float* __restrict__ fs, Seq seq, int P) {
   using S = Shape<DK, DV, M>;
   using SG = Stage<T, DK, DV, M>;
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -347,8 +348,9 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   __shared__ float dqb[2][4][DK];
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
-  const int t0 = p * C, t1 = min(T_, t0 + C);
-  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, (size_t)u * T_ + t0, t1 - t0);
+  const bfk::Span sp = seq.span(u);
+  const int t0 = p * C, t1 = max(t0, min(sp.len, t0 + C));  // t1 = t0: past the sequence's end
+  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, sp.base + t0, t1 - t0);
   float K[S::SPT][S::CK], V[S::SPT][S::CV], XK[S::SPT][S::CK], XV[S::SPT][S::CV], cum[S::SPT];
   {
     const float* base = st + ((size_t)u * P + p) * S::NE;
@@ -366,13 +368,15 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   }
   // this thread's slots' alpha and 1 - alpha, one token ahead
   float a_n[S::SPT], w_n[S::SPT];
-  ldn<S::SPT>(al + ((size_t)u * T_ + t0) * M + c0, a_n);
-  ldn<S::SPT>(wr + ((size_t)u * T_ + t0) * M + c0, w_n);
+  if (t1 > t0) {
+    ldn<S::SPT>(al + (sp.base + t0) * M + c0, a_n);
+    ldn<S::SPT>(wr + (sp.base + t0) * M + c0, w_n);
+  }
   __syncthreads();
   int n = 0;
   for (int t = t0; t < t1; t++, n++) {
     const int b = n & 1;
-    const size_t row = (size_t)u * T_ + t;
+    const size_t row = sp.base + t;
     float av[S::SPT], wv[S::SPT], qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
@@ -494,7 +498,7 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   if (n > 0 && threadIdx.x < DK) {
     const int b = (n - 1) & 1;
     const float x = dqb[b][0][threadIdx.x] + dqb[b][1][threadIdx.x] + dqb[b][2][threadIdx.x] + dqb[b][3][threadIdx.x];
-    dq[((size_t)u * T_ + t1 - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
+    dq[(sp.base + t1 - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
   }
   float* base = xu + ((size_t)u * P + p) * S::NE;
 #pragma unroll
@@ -508,7 +512,8 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
           f32x4{XV[i][j], XV[i][j + 1], XV[i][j + 2], XV[i][j + 3]};
   }
-  if (p == P - 1) {
+  // the chunk holding the sequence's last token (chunk 0 of an empty one)
+  if ((t1 > t0 && t1 == sp.len) || (sp.len == 0 && p == 0)) {
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
       float x = 0.f;
@@ -534,13 +539,13 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
 // From the adjoint at chunk p's end, tokens in reverse: dk, dv, and per token
 // the chunk-local reversed sum of dL/dG minus alpha di (written over z dz +
 // s ds); the chunk's total goes to tot.
-template <typename T, int DK, int DV, int M>
+template <typename T, int DK, int DV, int M, class Seq>
 __global__ void __launch_bounds__(NT)
 bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __restrict__ vv,
              const float* __restrict__ al, const float* __restrict__ wr, const T* __restrict__ dOo,
              const float* __restrict__ xu,
              const float* __restrict__ sw, const float* __restrict__ dzw, float* __restrict__ hw,
-             float* __restrict__ tot, T* __restrict__ dk, T* __restrict__ dv, int T_, int P) {
+             float* __restrict__ tot, T* __restrict__ dk, T* __restrict__ dv, Seq seq, int P) {
   using S = Shape<DK, DV, M>;
   using SG = Stage<T, DK, DV, M>;
   extern __shared__ __align__(16) unsigned char lds_raw[];
@@ -548,8 +553,9 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   __shared__ float kvb[2][4][DK + DV];
   const Thread th;
   const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
-  const int t0 = p * C, t1 = min(T_, t0 + C);
-  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, (size_t)u * T_ + t0, t1 - t0);
+  const bfk::Span sp = seq.span(u);
+  const int t0 = p * C, t1 = max(t0, min(sp.len, t0 + C));  // t1 = t0: past the sequence's end
+  stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, sp.base + t0, t1 - t0);
   float AK[S::SPT][S::CK], AV[S::SPT][S::CV], R[S::SPT];
   {
     const float* base = xu + ((size_t)u * P + p) * S::NE;
@@ -564,8 +570,8 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   // per-token s, dz, z dz + s ds, alpha and 1 - alpha of this thread's slots,
   // one token ahead
   float sv_n[S::SPT], dzv_n[S::SPT], hv_n[S::SPT], a_n[S::SPT], w_n[S::SPT];
-  {
-    const size_t r = (size_t)u * T_ + t1 - 1;
+  if (t1 > t0) {
+    const size_t r = sp.base + t1 - 1;
     ldn<S::SPT>(sw + r * M + c0, sv_n);
     ldn<S::SPT>(dzw + r * M + c0, dzv_n);
     ldn<S::SPT>(hw + r * M + c0, hv_n);
@@ -576,7 +582,7 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   int n = 0;
   for (int t = t1 - 1; t >= t0; t--, n++) {
     const int b = n & 1, lt = t - t0;
-    const size_t row = (size_t)u * T_ + t;
+    const size_t row = sp.base + t;
     float sv[S::SPT], dzv[S::SPT], hv[S::SPT], a[S::SPT], w[S::SPT], di[S::SPT];
     float qv[S::CK], kv[S::CK], vv_[S::CV], dov[S::CV];
 #pragma unroll
@@ -666,10 +672,10 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
 // ------------------------------------------------------------ 6. gate
 // dg = (chunk-local reversed sum + carry) * sigmoid(-g) / tau, the carry of
 // chunk p being the final-state term plus the totals of chunks p+1 .. P-1.
-template <typename T, int M>
+template <typename T, int M, class Seq>
 __global__ void __launch_bounds__(256)
 bwd_gate(const T* __restrict__ gg, const float* __restrict__ hw, const float* __restrict__ tot,
-         const float* __restrict__ fs, T* __restrict__ dg, int T_, int P, float inv_tau) {
+         const float* __restrict__ fs, T* __restrict__ dg, Seq seq, int P, float inv_tau) {
   __shared__ float carry[M];
   const int p = blockIdx.x, u = blockIdx.y;
   if (threadIdx.x < M) {
@@ -680,8 +686,9 @@ bwd_gate(const T* __restrict__ gg, const float* __restrict__ hw, const float* __
     carry[threadIdx.x] = c;
   }
   __syncthreads();
-  const int t0 = p * C, n = min(C, T_ - t0) * M;
-  const size_t base = ((size_t)u * T_ + t0) * M;
+  const bfk::Span sp = seq.span(u);
+  const int t0 = p * C, n = max(0, min(C, sp.len - t0)) * M;
+  const size_t base = (sp.base + t0) * M;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int c = e % M;
     const float gv = Elem<T>::to_f(gg[base + e]);
@@ -695,52 +702,45 @@ struct Ws {
   float *st, *xu, *dec, *sw, *dzw, *hw, *al, *wr, *tot, *fs;
 };
 
-// floats of workspace for U units of T tokens
-inline size_t ws_floats(size_t U, size_t T, int dk, int dv, int m) {
-  const size_t P = (T + C - 1) / C;
-  return 2 * U * P * (size_t)m * (dk + dv) + 2 * U * P * m + 5 * U * T * m + U * m;
+// floats of workspace for U units of P chunks each (one launch sequence) over
+// `rows` token rows in all (the per-token arrays are indexed by token row)
+inline size_t ws_floats(size_t U, size_t P, size_t rows, int dk, int dv, int m) {
+  return 2 * U * P * (size_t)m * (dk + dv) + 2 * U * P * m + 5 * rows * m + U * m;
 }
 
-inline Ws carve(float* w, size_t U, size_t T, int dk, int dv, int m) {
-  const size_t P = (T + C - 1) / C, NE = (size_t)m * (dk + dv);
+inline Ws carve(float* w, size_t U, size_t P, size_t rows, int dk, int dv, int m) {
+  const size_t NE = (size_t)m * (dk + dv);
   Ws s;
   s.st = w;
   s.xu = s.st + U * P * NE;
   s.dec = s.xu + U * P * NE;
   s.tot = s.dec + U * P * m;
   s.sw = s.tot + U * P * m;
-  s.dzw = s.sw + U * T * m;
-  s.hw = s.dzw + U * T * m;
-  s.al = s.hw + U * T * m;
-  s.wr = s.al + U * T * m;
-  s.fs = s.wr + U * T * m;
+  s.dzw = s.sw + rows * m;
+  s.hw = s.dzw + rows * m;
+  s.al = s.hw + rows * m;
+  s.wr = s.al + rows * m;
+  s.fs = s.wr + rows * m;
   return s;
 }
 
-template <typename T, int DK, int DV, int M, int ACT>
-int launch(const GsaBwdLaunch& a) {
-  const int U = a.B * a.H, Tn = a.T, P = (Tn + C - 1) / C;
+// One launch sequence over U units of P chunks each, the units' rows placed by
+// seq; k0 .. dv0 point at these units' states.
+template <typename T, int DK, int DV, int M, int ACT, class Seq>
+void launch_seq(const GsaBwdLaunch& a, const Seq& seq, int U, int P, const Ws& w, const float* k0,
+                const float* v0, const float* dkf, const float* dvf, float* dk0, float* dv0,
+                void* const* events) {
   const float inv_tau = 1.0f / a.tau;
-  if (Tn == 0) {  // no tokens: the initial states' gradients are the final ones'
-    state_copy(a.dk0, a.dkf, (size_t)U * M * DK, a.stream);
-    state_copy(a.dv0, a.dvf, (size_t)U * M * DV, a.stream);
-    record_event(a.events, 0, a.stream);
-    record_event(a.events, 1, a.stream);
-    record_event(a.events, 2, a.stream);
-    record_event(a.events, 3, a.stream);
-    return 0;
-  }
-  const Ws w = carve(a.ws, U, Tn, DK, DV, M);
   const T *q = (const T*)a.q, *k = (const T*)a.k, *v = (const T*)a.v, *g = (const T*)a.g,
           *dO = (const T*)a.d_o;
   hipStream_t s = (hipStream_t)a.stream;
   using SG = Stage<T, DK, DV, M>;
   static const bool lds_set = [] {  // once per instantiation and process
-    (void)hipFuncSetAttribute((const void*)bwd_map<T, DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)bwd_map<T, DK, DV, M, Seq>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, MapLds<T, DK, DV, M>::bytes);
-    (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M, ACT>,
+    (void)hipFuncSetAttribute((const void*)bwd_walk_fwd<T, DK, DV, M, ACT, Seq>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
-    (void)hipFuncSetAttribute((const void*)bwd_walk_rev<T, DK, DV, M>,
+    (void)hipFuncSetAttribute((const void*)bwd_walk_rev<T, DK, DV, M, Seq>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, SG::bytes);
     return true;
   }();
@@ -749,21 +749,81 @@ int launch(const GsaBwdLaunch& a) {
   const long long ne = (long long)U * M * (DK + DV) / 4;
   const dim3 sgrid((unsigned)((ne + 255) / 256));
   constexpr unsigned map_lds = MapLds<T, DK, DV, M>::bytes;
-  hipLaunchKernelGGL((bwd_map<T, DK, DV, M>), grid, dim3(NT), map_lds, s, k, v, g, w.st, w.dec, w.al, w.wr, Tn, P,
-                     inv_tau);
-  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, a.k0, a.v0,
+  hipLaunchKernelGGL((bwd_map<T, DK, DV, M, Seq>), grid, dim3(NT), map_lds, s, k, v, g, w.st, w.dec, w.al, w.wr,
+                     seq, P, inv_tau);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, k0, v0,
                      (float*)nullptr, (float*)nullptr, U, P);
-  launch_timed(bwd_walk_fwd<T, DK, DV, M, ACT>, grid, dim3(NT), SG::bytes, a.stream, a.events, 0, 1, q, k, v,
-               (const float*)w.al, (const float*)w.wr, dO,
-               (const float*)w.st, a.dkf, a.dvf, (T*)a.dq, w.xu, w.sw, w.dzw, w.hw, w.fs, Tn, P);
-  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, a.dkf, a.dvf,
-                     a.dk0, a.dv0, U, P);
-  launch_timed(bwd_walk_rev<T, DK, DV, M>, grid, dim3(NT), SG::bytes, a.stream, a.events, 2, 3, q, k, v,
-               (const float*)w.al, (const float*)w.wr, dO,
-               (const float*)w.xu, (const float*)w.sw, (const float*)w.dzw, w.hw, w.tot, (T*)a.dk, (T*)a.dv,
-               Tn, P);
-  hipLaunchKernelGGL((bwd_gate<T, M>), grid, dim3(256), 0, s, g, (const float*)w.hw, (const float*)w.tot,
-                     (const float*)w.fs, (T*)a.dg, Tn, P, inv_tau);
+  launch_timed(bwd_walk_fwd<T, DK, DV, M, ACT, Seq>, grid, dim3(NT), SG::bytes, a.stream, events, 0, 1, q, k,
+               v, (const float*)w.al, (const float*)w.wr, dO, (const float*)w.st, dkf, dvf, (T*)a.dq, w.xu,
+               w.sw, w.dzw, w.hw, w.fs, seq, P);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, dkf, dvf,
+                     dk0, dv0, U, P);
+  launch_timed(bwd_walk_rev<T, DK, DV, M, Seq>, grid, dim3(NT), SG::bytes, a.stream, events, 2, 3, q, k, v,
+               (const float*)w.al, (const float*)w.wr, dO, (const float*)w.xu, (const float*)w.sw,
+               (const float*)w.dzw, w.hw, w.tot, (T*)a.dk, (T*)a.dv, seq, P);
+  hipLaunchKernelGGL((bwd_gate<T, M, Seq>), grid, dim3(256), 0, s, g, (const float*)w.hw, (const float*)w.tot,
+                     (const float*)w.fs, (T*)a.dg, seq, P, inv_tau);
+}
+
+template <typename T, int DK, int DV, int M, int ACT>
+int launch(const GsaBwdLaunch& a) {
+  const size_t MK = (size_t)a.H * M * DK, MV = (size_t)a.H * M * DV;  // states per batch entry
+  if (!a.cu_seqlens) {
+    const int U = a.B * a.H, P = (a.T + C - 1) / C;
+    if (a.T == 0) {  // no tokens: the initial states' gradients are the final ones'
+      state_copy(a.dk0, a.dkf, (size_t)a.B * MK, a.stream);
+      state_copy(a.dv0, a.dvf, (size_t)a.B * MV, a.stream);
+      for (int e = 0; e < 4; e++) record_event(a.events, e, a.stream);
+      return 0;
+    }
+    const Ws w = carve(a.ws, U, P, (size_t)U * a.T, DK, DV, M);
+    launch_seq<T, DK, DV, M, ACT>(a, bfk::DenseSeqs{a.T}, U, P, w, a.k0, a.v0, a.dkf, a.dvf, a.dk0, a.dv0,
+                                  a.events);
+    return 0;
+  }
+  // A packed batch of variable-length sequences: groups of at most
+  // kMaxVarSeqs sequences, one launch sequence each (a group's offsets travel
+  // in the kernel arguments), one after the other on the stream.  They share
+  // the workspace: its chunk arrays are sized for the largest group and the
+  // longest sequence, its per-token arrays cover every packed row.
+  const int n = a.n_seqs, total = a.cu_seqlens[n];
+  int tmax = 0;
+  for (int i = 0; i < n; i++) tmax = max(tmax, a.cu_seqlens[i + 1] - a.cu_seqlens[i]);
+  const Ws w = carve(a.ws, (size_t)min(n, kMaxVarSeqs) * a.H, (tmax + C - 1) / C, (size_t)a.H * total, DK, DV, M);
+  const int groups = (n + kMaxVarSeqs - 1) / kMaxVarSeqs;
+  if (groups > 1) {
+    record_event(a.events, 0, a.stream);
+    record_event(a.events, 1, a.stream);
+  }
+  for (int g0 = 0; g0 < n; g0 += kMaxVarSeqs) {
+    const int ng = min(kMaxVarSeqs, n - g0);
+    bfk::VarSeqs vs{};
+    vs.H = a.H;
+    vs.total = total;
+    int tg = 0;
+    for (int i = 0; i <= ng; i++) vs.cu[i] = a.cu_seqlens[g0 + i];
+    for (int i = 0; i < ng; i++) {
+      vs.order[i] = i;
+      tg = max(tg, vs.cu[i + 1] - vs.cu[i]);
+    }
+    const float* k0 = a.k0 ? a.k0 + g0 * MK : nullptr;
+    const float* v0 = a.v0 ? a.v0 + g0 * MV : nullptr;
+    const float* dkf = a.dkf ? a.dkf + g0 * MK : nullptr;
+    const float* dvf = a.dvf ? a.dvf + g0 * MV : nullptr;
+    float* dk0 = a.dk0 ? a.dk0 + g0 * MK : nullptr;
+    float* dv0 = a.dv0 ? a.dv0 + g0 * MV : nullptr;
+    if (tg == 0) {  // only empty sequences
+      state_copy(dk0, dkf, (size_t)ng * MK, a.stream);
+      state_copy(dv0, dvf, (size_t)ng * MV, a.stream);
+      continue;
+    }
+    launch_seq<T, DK, DV, M, ACT>(a, vs, ng * a.H, (tg + C - 1) / C, w, k0, v0, dkf, dvf, dk0, dv0,
+                                  groups == 1 ? a.events : nullptr);
+  }
+  if (groups > 1) {
+    record_event(a.events, 2, a.stream);
+    record_event(a.events, 3, a.stream);
+  }
   return 0;
 }
 
@@ -781,8 +841,8 @@ int launch_act(const GsaBwdLaunch& a) {
 
 }  // namespace bwd
 
-size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m) {
-  return bwd::ws_floats(units, T, dk, dv, m) * sizeof(float);
+size_t gsa_bwd_ws_bytes(size_t units, size_t chunks, size_t rows, int dk, int dv, int m) {
+  return bwd::ws_floats(units, chunks, rows, dk, dv, m) * sizeof(float);
 }
 
 #define GSA_BWD_CASE(TY, DT, DK_, DV_, M_)                                    \

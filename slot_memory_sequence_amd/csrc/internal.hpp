@@ -77,9 +77,8 @@ int gla_decode_dispatch(int dtype, int dk, int dv, const GlaDecodeLaunch* a, boo
 // copy (src != null) or zero-fill n floats on the stream (T == 0 state hand-off)
 void state_copy(float* dst, const float* src, size_t n, void* stream);
 
-// GSA backward (softmax read): gradients of q, k, v, g (I/O dtype) and of the
-// initial states (fp32, nullable), given d_o and the nullable final-state
-// gradients dkf / dvf.  ws: gsa_bwd_ws_bytes(B * H, T, dk, dv, m) bytes.
+// GSA backward: gradients of q, k, v, g (I/O dtype) and of the initial states
+// (fp32, nullable), given d_o and the nullable final-state gradients dkf / dvf.
 struct GsaBwdLaunch {
   const void *q, *k, *v, *g, *d_o;
   const float *k0, *v0, *dkf, *dvf;
@@ -89,10 +88,16 @@ struct GsaBwdLaunch {
   int B, H, T;
   float tau;
   int act;  // slot read non-linearity, a GSA_SLOT_* code (SlotAct)
+  // packed variable-length batch (nullable): host offsets cu_seqlens[0..n_seqs]
+  // (validated), B = n_seqs, T = the longest length, rows [H, total, d]
+  const int* cu_seqlens;
+  int n_seqs;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t around the two token-walk kernels
 };
-size_t gsa_bwd_ws_bytes(size_t units, size_t T, int dk, int dv, int m);
+// workspace of one launch sequence of `units` units of `chunks` chunks over
+// `rows` token rows in all
+size_t gsa_bwd_ws_bytes(size_t units, size_t chunks, size_t rows, int dk, int dv, int m);
 int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query);
 
 }  // namespace gsa

@@ -172,6 +172,19 @@ def varlen_inputs(lengths, H, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
     return out
 
 
+def varlen_grad_inputs(lengths, H, dk, dv, m, dtype="bf16", seed=0, final_std=None):
+    """Upstream gradients for the backward of a packed batch: dO ~ N(0,1)
+    [H,total,dv] in dtype; optional dKf [n,H,m,dk], dVf [n,H,m,dv] ~ N(0,
+    final_std) stored as float32."""
+    rng = np.random.default_rng(seed)
+    n, total = len(lengths), int(np.sum(np.asarray(lengths, dtype=np.int64)))
+    out = dict(do=stored(_normal(rng, (H, total, dv)), dtype), dkf=None, dvf=None)
+    if final_std is not None:
+        out["dkf"] = stored(_normal(rng, (n, H, m, dk)) * final_std, "f32")
+        out["dvf"] = stored(_normal(rng, (n, H, m, dv)) * final_std, "f32")
+    return out
+
+
 # The five workloads: sizes, dtypes and value distributions of the method's
 # configurations (GSA: tau = 8 per the paper's Sec. 3.3; the standalone GLA
 # case uses tau = 16).

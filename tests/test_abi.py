@@ -286,3 +286,29 @@ def test_bwd_ex_nonlinearity_validation(gsa):
     bad[9] = P(FAKE + 0x10)             # d_q overlaps q: the codes 0..4 pass the shape check
     for code in range(5):
         assert f(*bad, code, None, None) == 7
+
+
+def test_bwd_varlen_validation(gsa):
+    """Every call here fails validation on the host (nothing is launched)."""
+    f = gsa.lib.gsa_bwd_varlen
+    P = ctypes.c_void_p
+
+    def call(cu, n=None, H=2, dtype=1, dq=FAKE + 0x5000000, dk=128, ws=FAKE + 0x40000000, wsb=None):
+        arr = (ctypes.c_int * len(cu))(*cu)
+        n = len(cu) - 1 if n is None else n
+        if wsb is None:
+            wsb = gsa.lib.gsa_bwd_varlen_workspace_bytes(ctypes.cast(arr, P), n, H, dk, dk, 64)
+        return f(P(FAKE), P(FAKE + 0x1000000), P(FAKE + 0x2000000), P(FAKE + 0x3000000),
+                 P(FAKE + 0x4000000), ctypes.cast(arr, P), n, H, None, None, None, None,
+                 P(dq), P(FAKE + 0x6000000), P(FAKE + 0x7000000), P(FAKE + 0x8000000),
+                 None, None, dk, dk, 64, 8.0, dtype, P(ws), wsb, None, None)
+
+    assert call([0, 5, 3]) == 2                       # decreasing offsets
+    assert call([1, 5]) == 2                          # cu[0] != 0
+    assert call([0, 5], dtype=9) == 2
+    assert call([0, 5], dk=96) == 4
+    assert call([0, 70, 200], dq=FAKE + 0x10) == 7    # d_q overlaps q
+    assert call([0, 70, 200], wsb=16) == 5
+    arr = (ctypes.c_int * 3)(0, 70, 200)
+    assert gsa.lib.gsa_bwd_varlen_workspace_bytes(ctypes.cast(arr, P), 2, 2, 128, 128, 64) > 0
+    assert gsa.lib.gsa_bwd_varlen_workspace_bytes(None, 2, 2, 128, 128, 64) == 0
