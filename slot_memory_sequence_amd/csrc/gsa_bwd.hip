@@ -11,8 +11,10 @@
 // recomputed rather than stored).
 //
 // Per unit (b, h), with alpha_t = sigmoid(g_t)^(1/tau), i_t = 1 - alpha_t,
-// z_t = Kt q_t (pass-1 output), s_t = softmax(z_t), o_t = Vt^T s_t:
-//   ds_t = Vt dO_t,  dz_t = s_t * (ds_t - s_t . ds_t),  dq_t = Kt^T dz_t
+// z_t = Kt q_t (pass-1 output), s_t = softmax(z_t) (or an element-wise read
+// f(z_t), Table 2), o_t = Vt^T s_t:
+//   ds_t = Vt dO_t,  dz_t = s_t * (ds_t - s_t . ds_t) (or f'(z_t) ds_t),
+//   dq_t = Kt^T dz_t
 //   adjoints (reverse in t): dVt = alpha_{t+1} dV_{t+1} + s_t dO_t^T,
 //                            dKt = alpha_{t+1} dK_{t+1} + dz_t q_t^T
 //   dk_t = dKt^T i_t,  dv_t = dVt^T i_t,  di_t = dKt k_t + dVt v_t
@@ -22,9 +24,10 @@
 //   d log alpha_t = sum_{r>=t} dL/dG_r - alpha_t di_t,
 //   dg_t = d log alpha_t * sigmoid(-g_t) / tau.
 //
-// Five launches, chunks of C = 64 tokens, one workgroup per (chunk, unit):
-//   1. bwd_map       chunk state maps (the state a chunk builds from zero)
-//                    and chunk decays, by the token recurrence in fp32;
+// Six launches, chunks of C = 64 tokens, one workgroup per (chunk, unit) for
+// all but the scans:
+//   1. bwd_map       chunk state maps (the state a chunk builds from zero, as
+//                    a weighted sum over its tokens) and chunk decays, fp32;
 //   2. bwd_scan<0>   chunk start states (forward scan of the maps);
 //   3. bwd_walk_fwd  per chunk from its start state, token by token:
 //                    z, s, ds, dz, dq, the reverse map of the chunk (what its
@@ -41,7 +44,9 @@
 // thread (slot group sg, column group cg) of a 16 x 16 grid owns M/16 slot
 // rows x D/16 columns of each, so that per-slot dot products are 16-lane row
 // reductions inside a wave and per-column sums over slots run over the four
-// slot groups of a wave and then, through LDS, over the four waves.
+// slot groups of a wave and then, through LDS, over the four waves.  A unit's
+// rows are placed by the sequence layout (a dense batch, or a packed batch of
+// variable-length sequences whose chunks past a sequence's end are empty).
 #include "../../include/gsa.h"
 #include "bf16_common.hpp"
 #include "common.hpp"
