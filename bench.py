@@ -388,6 +388,40 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
             "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None}
 
 
+def bench_bwd_varlen(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_serve_N256_bwd"):
+    """The backward over the serving workload's packed batch (256 sequences x
+    H16, log-uniform lengths), dO ~ N(0, 1): training on packed sequences of
+    mixed lengths.  Tokens/s counts sequence tokens (sum of lengths)."""
+    import synth
+    lengths = synth.varlen_lengths(w["N"], w["len_lo"], w["len_hi"], seed=0)
+    inp = synth.varlen_inputs(lengths, w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
+                              qkv_scale=w["qkv_scale"], g_shift=w["g_shift"])
+    inp["do"] = synth.varlen_grad_inputs(lengths, w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
+                                         seed=1)["do"]
+    cu = inp["cu_seqlens"]
+    H, dk, dv, m = w["H"], w["dk"], w["dv"], w["m"]
+    total = int(cu[-1])
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do"], 2)
+    ws = torch.empty(gsa.gsa_bwd_varlen_workspace_bytes(cu, H, dk, dv, m), dtype=torch.uint8, device="cuda")
+
+    def call(s_, events):
+        gsa.gsa_bwd_varlen(s_["q"], s_["k"], s_["v"], s_["g"], s_["do"], cu, tau=w["tau"], workspace=ws,
+                           events=events)
+
+    wall, ph = time_op(torch, ev, call, sets, steps, warmup)
+    t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
+    # per token-head the same work as the dense backward (one sequence's tokens)
+    f_f, f_r, nbytes = gsa_bwd_alg(1, H, total, dk, dv, m, 2)
+    kern, fl, t = ("bwd_walk_fwd", f_f, t_f) if t_f >= t_r else ("bwd_walk_rev", f_r, t_r)
+    ach = fl / (t * 1e-3) / 1e12
+    return {"value": round(total * steps / wall, 1), "unit": "tokens/s", "sequences": w["N"], "H": H,
+            "tokens": total, "ms_per_step": round(wall / steps * 1e3, 4),
+            "ms_kernels": {"bwd_walk_fwd": round(t_f, 4), "bwd_walk_rev": round(t_r, 4)},
+            "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 4),
+                         "traffic": load_traffic(kern, name), "kernel": kern}}
+
+
 def cpu_baseline(w, inp, budget_s):
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -575,6 +609,9 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "bwd_serve":
+        return bench_bwd_varlen(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
+                                args.warmup)
     if args.only == "bwd":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps,
                          args.warmup, cpu=False)
@@ -603,7 +640,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -657,6 +694,9 @@ def main():
         comps["gsa_bf16_train_T2048_bwd"] = bench_bwd(torch, gsa, ev, w, max(1, args.steps // 4),
                                                       args.warmup, cpu=not args.no_cpu)
         log("bench: backward done")
+        comps["gsa_bf16_serve_N256_bwd"] = bench_bwd_varlen(
+            torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], max(1, args.steps // 4), args.warmup)
+        log("bench: packed-batch backward done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)
         log("bench: serving prefill + decode done")

@@ -281,7 +281,8 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
  *              dk, dv, m) bytes (else GSA_ERR_WORKSPACE), caller-owned; its
  *              contents on entry do not matter.
  * No output may overlap an input, the workspace or another output
- * (GSA_ERR_ALIAS).  B * H <= 65535.  Compiled for (dk = dv, m) in {(128, 64),
+ * (GSA_ERR_ALIAS).  B * H <= 65535 and T <= 65535 * 64 (else
+ * GSA_ERR_UNSUPPORTED).  Compiled for (dk = dv, m) in {(128, 64),
  * (128, 32), (64, 64), (64, 32)}, float32 and bf16 (gsa_bwd_supported).
  * events: NULL or 4 hipEvent_t: [0, 1] stamp the forward token-walk kernel's
  * dispatch, [2, 3] the reverse token-walk kernel's.

@@ -24,7 +24,7 @@
 //   d log alpha_t = sum_{r>=t} dL/dG_r - alpha_t di_t,
 //   dg_t = d log alpha_t * sigmoid(-g_t) / tau.
 //
-// Six launches, chunks of C = 64 tokens, one workgroup per (chunk, unit) for
+// Six launches, chunks of C = 64 tokens, one workgroup per (unit, chunk) for
 // all but the scans:
 //   1. bwd_map       chunk state maps (the state a chunk builds from zero, as
 //                    a weighted sum over its tokens) and chunk decays, fp32;
@@ -46,7 +46,8 @@
 // reductions inside a wave and per-column sums over slots run over the four
 // slot groups of a wave and then, through LDS, over the four waves.  A unit's
 // rows are placed by the sequence layout (a dense batch, or a packed batch of
-// variable-length sequences whose chunks past a sequence's end are empty).
+// variable-length sequences; a unit has ceil(len / C) chunks, the workgroups
+// of the grid's chunks past that return at once and the scans stop there).
 #include "../../include/gsa.h"
 #include "bf16_common.hpp"
 #include "common.hpp"
@@ -205,9 +206,10 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
   float* sA = reinterpret_cast<float*>(lds_raw + C * (DK + DV) * sizeof(T));  // [C][M] weights
   float* ptot = sA + C * M;                                                     // [PARTS][M]
   const Thread th;
-  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int p = blockIdx.y, u = blockIdx.x, c0 = th.sg * S::SPT;
   const bfk::Span sp = seq.span(u);
-  const int t0 = p * C, rows = max(0, min(sp.len, t0 + C) - t0);  // 0: past the sequence's end
+  const int t0 = p * C, rows = min(sp.len, t0 + C) - t0;
+  if (rows <= 0) return;  // past the sequence's end: no chunk (the scans stop before it)
   const size_t row0 = sp.base + t0;
   copy_rows(sk, kk + row0 * DK, rows * DK);
   copy_rows(sv, vv + row0 * DV, rows * DV);
@@ -283,15 +285,17 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
 // adjoint of the state at chunk p's end from later tokens (W starts at the
 // final-state gradients ka / va, nullable = zero); what is carried out of
 // chunk 0 is written to kout / vout (nullable).
-template <int DK, int DV, int M, int REV>
+template <int DK, int DV, int M, int REV, class Seq>
 __global__ void __launch_bounds__(256)
 bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __restrict__ ka,
-         const float* __restrict__ va, float* __restrict__ kout, float* __restrict__ vout, int units, int P) {
+         const float* __restrict__ va, float* __restrict__ kout, float* __restrict__ vout, Seq seq,
+         int units, int P) {
   constexpr int NE = M * (DK + DV), BATCH = 8;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long long)units * (NE / 4)) return;
   const int unit = (int)(gid / (NE / 4)), e = 4 * (int)(gid % (NE / 4));
   const int c = e / (DK + DV), cl = e % (DK + DV);
+  const int Pu = (seq.span(unit).len + C - 1) / C;  // this unit's chunks (P for a dense batch)
   const size_t ko = ((size_t)unit * M + c) * DK + cl, vo = ((size_t)unit * M + c) * DV + cl - DK;
   f32x4 W = {0.f, 0.f, 0.f, 0.f};
   if (cl < DK) {
@@ -301,21 +305,21 @@ bwd_scan(float* __restrict__ ws, const float* __restrict__ dec, const float* __r
   }
   f32x4* sl = reinterpret_cast<f32x4*>(ws + (size_t)unit * P * NE + e);
   const float* dc = dec + (size_t)unit * P * M + c;
-  for (int n0 = 0; n0 < P; n0 += BATCH) {
+  for (int n0 = 0; n0 < Pu; n0 += BATCH) {
     f32x4 x[BATCH];
     float d[BATCH];
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
-      if (n0 + i < P) {
-        const int p = REV ? P - 1 - (n0 + i) : n0 + i;
+      if (n0 + i < Pu) {
+        const int p = REV ? Pu - 1 - (n0 + i) : n0 + i;
         x[i] = sl[(size_t)p * (NE / 4)];
         d[i] = dc[(size_t)p * M];
       }
     }
 #pragma unroll
     for (int i = 0; i < BATCH; i++) {
-      if (n0 + i < P) {
-        const int p = REV ? P - 1 - (n0 + i) : n0 + i;
+      if (n0 + i < Pu) {
+        const int p = REV ? Pu - 1 - (n0 + i) : n0 + i;
         sl[(size_t)p * (NE / 4)] = W;
         W = d[i] * W + x[i];
       }
@@ -352,9 +356,10 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   __shared__ float red[2][4][3];
   __shared__ float dqb[2][4][DK];
   const Thread th;
-  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int p = blockIdx.y, u = blockIdx.x, c0 = th.sg * S::SPT;
   const bfk::Span sp = seq.span(u);
-  const int t0 = p * C, t1 = max(t0, min(sp.len, t0 + C));  // t1 = t0: past the sequence's end
+  const int t0 = p * C, t1 = min(sp.len, t0 + C);
+  if (t1 <= t0) return;  // past the sequence's end: no chunk
   stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, sp.base + t0, t1 - t0);
   float K[S::SPT][S::CK], V[S::SPT][S::CV], XK[S::SPT][S::CK], XV[S::SPT][S::CV], cum[S::SPT];
   {
@@ -373,10 +378,8 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   }
   // this thread's slots' alpha and 1 - alpha, one token ahead
   float a_n[S::SPT], w_n[S::SPT];
-  if (t1 > t0) {
-    ldn<S::SPT>(al + (sp.base + t0) * M + c0, a_n);
-    ldn<S::SPT>(wr + (sp.base + t0) * M + c0, w_n);
-  }
+  ldn<S::SPT>(al + (sp.base + t0) * M + c0, a_n);
+  ldn<S::SPT>(wr + (sp.base + t0) * M + c0, w_n);
   __syncthreads();
   int n = 0;
   for (int t = t0; t < t1; t++, n++) {
@@ -500,7 +503,7 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
     }
   }
   __syncthreads();
-  if (n > 0 && threadIdx.x < DK) {
+  if (threadIdx.x < DK) {
     const int b = (n - 1) & 1;
     const float x = dqb[b][0][threadIdx.x] + dqb[b][1][threadIdx.x] + dqb[b][2][threadIdx.x] + dqb[b][3][threadIdx.x];
     dq[(sp.base + t1 - 1) * DK + threadIdx.x] = Elem<T>::from_f(x);
@@ -517,8 +520,7 @@ bwd_walk_fwd(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
       *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
           f32x4{XV[i][j], XV[i][j + 1], XV[i][j + 2], XV[i][j + 3]};
   }
-  // the chunk holding the sequence's last token (chunk 0 of an empty one)
-  if ((t1 > t0 && t1 == sp.len) || (sp.len == 0 && p == 0)) {
+  if (t1 == sp.len) {  // the chunk holding the sequence's last token
 #pragma unroll
     for (int i = 0; i < S::SPT; i++) {
       float x = 0.f;
@@ -557,9 +559,10 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   T* lds = reinterpret_cast<T*>(lds_raw);
   __shared__ float kvb[2][4][DK + DV];
   const Thread th;
-  const int p = blockIdx.x, u = blockIdx.y, c0 = th.sg * S::SPT;
+  const int p = blockIdx.y, u = blockIdx.x, c0 = th.sg * S::SPT;
   const bfk::Span sp = seq.span(u);
-  const int t0 = p * C, t1 = max(t0, min(sp.len, t0 + C));  // t1 = t0: past the sequence's end
+  const int t0 = p * C, t1 = min(sp.len, t0 + C);
+  if (t1 <= t0) return;  // past the sequence's end: no chunk
   stage_chunk<T, DK, DV, M>(lds, qq, kk, vv, dOo, sp.base + t0, t1 - t0);
   float AK[S::SPT][S::CK], AV[S::SPT][S::CV], R[S::SPT];
   {
@@ -575,7 +578,7 @@ bwd_walk_rev(const T* __restrict__ qq, const T* __restrict__ kk, const T* __rest
   // per-token s, dz, z dz + s ds, alpha and 1 - alpha of this thread's slots,
   // one token ahead
   float sv_n[S::SPT], dzv_n[S::SPT], hv_n[S::SPT], a_n[S::SPT], w_n[S::SPT];
-  if (t1 > t0) {
+  {
     const size_t r = sp.base + t1 - 1;
     ldn<S::SPT>(sw + r * M + c0, sv_n);
     ldn<S::SPT>(dzw + r * M + c0, dzv_n);
@@ -682,17 +685,19 @@ __global__ void __launch_bounds__(256)
 bwd_gate(const T* __restrict__ gg, const float* __restrict__ hw, const float* __restrict__ tot,
          const float* __restrict__ fs, T* __restrict__ dg, Seq seq, int P, float inv_tau) {
   __shared__ float carry[M];
-  const int p = blockIdx.x, u = blockIdx.y;
+  const int p = blockIdx.y, u = blockIdx.x;
+  const bfk::Span sp = seq.span(u);
+  const int t0 = p * C, Pu = (sp.len + C - 1) / C;
+  if (p >= Pu) return;  // past the sequence's end: no chunk
   if (threadIdx.x < M) {
     float c = fs[(size_t)u * M + threadIdx.x];
     const float* tp = tot + (size_t)u * P * M + threadIdx.x;
 #pragma unroll 8
-    for (int x = p + 1; x < P; x++) c += tp[(size_t)x * M];
+    for (int x = p + 1; x < Pu; x++) c += tp[(size_t)x * M];
     carry[threadIdx.x] = c;
   }
   __syncthreads();
-  const bfk::Span sp = seq.span(u);
-  const int t0 = p * C, n = max(0, min(C, sp.len - t0)) * M;
+  const int n = min(C, sp.len - t0) * M;
   const size_t base = (sp.base + t0) * M;
   for (int e = threadIdx.x; e < n; e += 256) {
     const int c = e % M;
@@ -750,19 +755,24 @@ void launch_seq(const GsaBwdLaunch& a, const Seq& seq, int U, int P, const Ws& w
     return true;
   }();
   (void)lds_set;
-  const dim3 grid(P, U);
+  // units along x: consecutive workgroups (which the dispatcher deals round
+  // robin to the eight XCDs) are different units' chunk p, so every XCD gets
+  // an even share of every chunk index (with chunks along x, chunk p of every
+  // unit would land on XCD p mod 8, and a packed batch's late chunks, which
+  // only long sequences have, on a few XCDs)
+  const dim3 grid(U, P);
   const long long ne = (long long)U * M * (DK + DV) / 4;
   const dim3 sgrid((unsigned)((ne + 255) / 256));
   constexpr unsigned map_lds = MapLds<T, DK, DV, M>::bytes;
   hipLaunchKernelGGL((bwd_map<T, DK, DV, M, Seq>), grid, dim3(NT), map_lds, s, k, v, g, w.st, w.dec, w.al, w.wr,
                      seq, P, inv_tau);
-  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, k0, v0,
-                     (float*)nullptr, (float*)nullptr, U, P);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 0, Seq>), sgrid, dim3(256), 0, s, w.st, (const float*)w.dec, k0, v0,
+                     (float*)nullptr, (float*)nullptr, seq, U, P);
   launch_timed(bwd_walk_fwd<T, DK, DV, M, ACT, Seq>, grid, dim3(NT), SG::bytes, a.stream, events, 0, 1, q, k,
                v, (const float*)w.al, (const float*)w.wr, dO, (const float*)w.st, dkf, dvf, (T*)a.dq, w.xu,
                w.sw, w.dzw, w.hw, w.fs, seq, P);
-  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, dkf, dvf,
-                     dk0, dv0, U, P);
+  hipLaunchKernelGGL((bwd_scan<DK, DV, M, 1, Seq>), sgrid, dim3(256), 0, s, w.xu, (const float*)w.dec, dkf, dvf,
+                     dk0, dv0, seq, U, P);
   launch_timed(bwd_walk_rev<T, DK, DV, M, Seq>, grid, dim3(NT), SG::bytes, a.stream, events, 2, 3, q, k, v,
                (const float*)w.al, (const float*)w.wr, dO, (const float*)w.xu, (const float*)w.sw,
                (const float*)w.dzw, w.hw, w.tot, (T*)a.dk, (T*)a.dv, seq, P);

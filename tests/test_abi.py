@@ -263,6 +263,7 @@ def test_bwd_validation(gsa):
     assert call(dtype=5) == 2
     assert call(d_k=96, d_v=96) == 4
     assert call(B=65536) == 4
+    assert call(T=65535 * 64 + 1) == 4                  # more chunks than the grid takes
     assert call(B=0) == 0                               # nothing to do
     assert call(q=None) == 1 and call(do=None) == 1 and call(dg=None) == 1
     assert call(dq=FAKE + 0x500008) == 3
