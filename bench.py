@@ -330,22 +330,25 @@ def bwd_cpu_oracle(w, inp, budget_s=3.0):
 
 
 def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd", cpu=True):
-    """The GSA backward at the training shape (B8 H4 T2048, bf16), zero
-    initial states and no final-state gradients, dO ~ N(0, 1); two input sets
-    rotated."""
+    """The GSA backward at a workload's shape (the training shape B8 H4 T2048
+    bf16 with zero states, or the long-context one with initial states and
+    final-state gradients), dO ~ N(0, 1); two input sets rotated."""
     import synth
     B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
     inp = synth.gsa_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=0, qkv_scale=w["qkv_scale"],
                            g_shift=w["g_shift"], init_std=w["init_std"])
-    inp["do"] = synth.gsa_grad_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=1)["do"]
-    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do"], 2)
+    states = inp["k0"] is not None
+    gi = synth.gsa_grad_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=1,
+                               final_std=1.0 if states else None)
+    inp["do"], inp["dkf"], inp["dvf"] = gi["do"], gi["dkf"], gi["dvf"]
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do", "k0", "v0", "dkf", "dvf"], 2)
     outs = [tuple(torch.empty_like(s[n]) for n in "qkvg") for s in sets]
     ws = torch.empty(gsa.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m), dtype=torch.uint8, device="cuda")
 
     def call(s, events):
         i = next(j for j, x in enumerate(sets) if x is s)
-        gsa.gsa_bwd(s["q"], s["k"], s["v"], s["g"], s["do"], tau=w["tau"], out=outs[i], workspace=ws,
-                    events=events)
+        gsa.gsa_bwd(s["q"], s["k"], s["v"], s["g"], s["do"], s.get("k0"), s.get("v0"), s.get("dkf"),
+                    s.get("dvf"), tau=w["tau"], out=outs[i], workspace=ws, events=events)
 
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
@@ -357,7 +360,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
 
     def train_step(i):
         s_ = sets[i % len(sets)]
-        gsa.gsa_fwd(s_["q"], s_["k"], s_["v"], s_["g"], tau=w["tau"], out=o_buf[i % len(sets)], workspace=wsf)
+        gsa.gsa_fwd(s_["q"], s_["k"], s_["v"], s_["g"], s_.get("k0"), s_.get("v0"), tau=w["tau"],
+                    out=o_buf[i % len(sets)], workspace=wsf)
         call(s_, None)
 
     for i in range(warmup):
@@ -609,6 +613,9 @@ def run_only(args, torch, gsa, ev):
         r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], "gsa_bf16_long_T16384",
                       args.steps, args.warmup, 3, warm_too=False)
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "bwd_long":
+        return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], args.steps,
+                         args.warmup, name="gsa_bf16_long_T16384_bwd", cpu=False)
     if args.only == "bwd_serve":
         return bench_bwd_varlen(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
                                 args.warmup)
@@ -640,7 +647,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd", "bwd_serve"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -697,6 +704,10 @@ def main():
         comps["gsa_bf16_serve_N256_bwd"] = bench_bwd_varlen(
             torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], max(1, args.steps // 4), args.warmup)
         log("bench: packed-batch backward done")
+        comps["gsa_bf16_long_T16384_bwd"] = bench_bwd(
+            torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], max(1, args.steps // 4), args.warmup,
+            name="gsa_bf16_long_T16384_bwd", cpu=False)
+        log("bench: long-context backward done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)
         log("bench: serving prefill + decode done")
