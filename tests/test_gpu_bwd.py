@@ -215,3 +215,27 @@ def test_bwd_elementwise_read_training_shape_sampled(gsa, torch):
     got = _run(gsa, torch, inp, gi, w["tau"], "swish")
     units = [3, w["B"] * w["H"] - 2]
     _compare(got, _ref(inp, gi, w["tau"], units, "swish"), "bf16", "B8 H4 T2048 swish sampled", units)
+
+
+def test_bwd_event_hooks_and_repeatability(gsa, torch):
+    """The dispatch-stamped launches give the plain launches' bits; a second
+    call on a reused (dirty) workspace gives the same bits; the stamps of the
+    two token walks are ordered."""
+    from tests.test_gpu_parity import _hip_events
+    inp = synth.gsa_inputs(2, 2, 300, 128, 128, 64, dtype="bf16", seed=70, init_std=0.1)
+    gi = synth.gsa_grad_inputs(2, 2, 300, 128, 128, 64, dtype="bf16", seed=71, final_std=1.0)
+    dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
+    ddev = {n: to_dev(gi[n], torch) for n in ("do", "dkf", "dvf")}
+    ws = torch.empty(gsa.gsa_bwd_workspace_bytes(2, 2, 300, 128, 128, 64), dtype=torch.uint8,
+                     device="cuda")
+    args = (dev["q"], dev["k"], dev["v"], dev["g"], ddev["do"], dev["k0"], dev["v0"], ddev["dkf"],
+            ddev["dvf"])
+    a = gsa.gsa_bwd(*args, state_grads=True, workspace=ws)
+    evs, ms, free = _hip_events(4)
+    b = gsa.gsa_bwd(*args, state_grads=True, workspace=ws, events=evs)
+    torch.cuda.synchronize()
+    t = [ms(evs[0], evs[1]), ms(evs[2], evs[3]), ms(evs[0], evs[3])]
+    free()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert t[0] > 0 and t[1] > 0 and t[2] >= t[0] + t[1], t
