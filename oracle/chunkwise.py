@@ -140,3 +140,112 @@ def gla_fwd(q, k, v, g, s0=None, tau=16.0, C=64):
             o[b, h], sf[b, h] = gla_key_decay(q[b, h], k[b, h], v[b, h], la,
                                               None if s0 is None else s0[b, h], C)
     return o, sf
+
+
+# ----------------------------------------------------------------- backward
+# App. B's training scheme in chunk form: the two GLA passes are differentiated
+# in reverse order (pass 2 first), the write intensity I = 1 - alpha collects
+# the gradient of both passes, and the forget-gate gradient is the reversed
+# cumulative sum over tokens of each pass's "scaled-by-e^G" products minus its
+# "scaled-by-e^-G" products (pass 2: Q.dQ - K.dK with its query s and key I;
+# pass 1: O.dO - V.dV with its output o' and value I), plus the final-state
+# terms.  Chunk start states come from the forward recurrence, chunk-end
+# adjoints from the reverse one; within a chunk every decay is exp of an
+# explicit sum of log alpha, as in the forward.
+
+def _chunks(T, C):
+    return [slice(n0, min(n0 + C, T)) for n0 in range(0, T, C)]
+
+
+def gla_key_decay_bwd(q, k, v, la, S0, do, dSf, C=64):
+    """Backward of gla_key_decay (S [dk, dv], decay on rows).  Returns
+    (dq, dk, dv, dG, dS0) with dG[t, c] = dL/dG_t[c], G the running sum of la."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    starts = []
+    for sl in _chunks(T, C):          # forward: chunk start states
+        starts.append(S.copy())
+        lc, kc, vc = la[sl], k[sl], v[sl]
+        D = _pair_logdecay(lc)
+        S = np.exp(np.cumsum(lc, axis=0)[-1])[:, None] * S + (kc * np.exp(D[-1])).T @ vc
+    dq, dkk, dvv, dG = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros((T, dk))
+    U = np.zeros((dk, dv)) if dSf is None else np.array(dSf, dtype=np.float64)
+    if dSf is not None and T > 0:
+        dG[T - 1] += np.sum(U * S, axis=1)        # the final state carries e^{G_T}
+    for i in reversed(range(len(starts))):
+        sl = _chunks(T, C)[i]
+        qc, kc, vc, lc, dc = q[sl], k[sl], v[sl], la[sl], do[sl]
+        D = np.exp(_pair_logdecay(lc))                # D[j, r] = decay from r to j
+        Gf = np.exp(np.cumsum(lc, axis=0))
+        A = dc @ vc.T                                 # dO_j . v_r
+        dq[sl] = Gf * (dc @ starts[i].T) + np.einsum("jr,rc,jrc->jc", A, kc, D)
+        dkk[sl] = np.einsum("tj,tc,tjc->jc", A, qc, D) + D[-1] * (vc @ U.T)
+        Bm = np.einsum("tc,jc,tjc->tj", qc, kc, D)
+        dvv[sl] = Bm.T @ dc + (kc * D[-1]) @ U
+        dG[sl] += qc * dq[sl] - kc * dkk[sl]
+        U = Gf[-1][:, None] * U + (qc * Gf).T @ dc
+    return dq, dkk, dvv, dG, U
+
+
+def gla_value_decay_bwd(q, k, w, la, P0, do, dPf, C=64):
+    """Backward of gla_value_decay (P [dk, m], decay on columns).  Returns
+    (dq, dk, dw, dG, dP0)."""
+    T, dk = q.shape
+    m = w.shape[1]
+    P = np.zeros((dk, m)) if P0 is None else np.array(P0, dtype=np.float64)
+    starts, outs = [], np.zeros((T, m))
+    for sl in _chunks(T, C):
+        starts.append(P.copy())
+        qc, kc, wc, lc = q[sl], k[sl], w[sl], la[sl]
+        D = np.exp(_pair_logdecay(lc))
+        Gf = np.exp(np.cumsum(lc, axis=0))
+        outs[sl] = Gf * (qc @ P) + np.einsum("jr,rc,jrc->jc", qc @ kc.T, wc, D)
+        P = P * Gf[-1][None, :] + kc.T @ (wc * D[-1])
+    dq, dkk, dw, dG = np.zeros_like(q), np.zeros_like(k), np.zeros_like(w), np.zeros((T, m))
+    U = np.zeros((dk, m)) if dPf is None else np.array(dPf, dtype=np.float64)
+    if dPf is not None and T > 0:
+        dG[T - 1] += np.sum(U * P, axis=0)
+    for i in reversed(range(len(starts))):
+        sl = _chunks(T, C)[i]
+        qc, kc, wc, lc, dc = q[sl], k[sl], w[sl], la[sl], do[sl]
+        D = np.exp(_pair_logdecay(lc))
+        Gf = np.exp(np.cumsum(lc, axis=0))
+        dq[sl] = (dc * Gf) @ starts[i].T + np.einsum("jc,rc,jrc->jr", dc, wc, D) @ kc
+        E = np.einsum("tc,jc,tjc->tj", dc, wc, D)
+        dkk[sl] = E.T @ qc + (wc * D[-1]) @ U.T
+        dw[sl] = np.einsum("tj,tc,tjc->jc", qc @ kc.T, dc, D) + D[-1] * (kc @ U)
+        dG[sl] += outs[sl] * dc - wc * dw[sl]
+        U = U * Gf[-1][None, :] + qc.T @ (dc * Gf)
+    return dq, dkk, dw, dG, U
+
+
+def gsa_bwd_unit(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, C=64):
+    """Gradients of one (b,h) unit of GSA (softmax read) through the two chunked
+    GLA passes.  Returns (dq, dk, dv, dg, dk0, dv0)."""
+    la = log_sigmoid(g) / tau
+    w = -np.expm1(la)
+    P0 = None if k0 is None else np.asarray(k0, dtype=np.float64).T
+    z, _ = gla_value_decay(q, k, w, la, P0, C)
+    s = softmax_slots(z)
+    ds, dw2, dv, dG2, dv0 = gla_key_decay_bwd(s, w, v, la, v0, do, dvf, C)      # pass 2
+    dz = s * (ds - np.sum(s * ds, axis=-1, keepdims=True))                       # softmax
+    dPf = None if dkf is None else np.asarray(dkf, dtype=np.float64).T
+    dq, dk, dw1, dG1, dP0 = gla_value_decay_bwd(q, k, w, la, P0, dz, dPf, C)    # pass 1
+    dI = dw1 + dw2
+    dG = dG1 + dG2
+    dla = np.cumsum(dG[::-1], axis=0)[::-1] - np.exp(la) * dI                   # reversed cumsum
+    dg = dla * np.exp(log_sigmoid(-np.asarray(g, dtype=np.float64))) / tau
+    return dq, dk, dv, dg, dP0.T, dv0
+
+
+def gsa_bwd(q, k, v, g, do, k0=None, v0=None, dkf=None, dvf=None, tau=8.0, C=64):
+    """[B,H,...] wrapper of gsa_bwd_unit; returns a dict like oracle.gsa_bwd."""
+    B, H = q.shape[:2]
+    out = {n: [] for n in ("dq", "dk", "dv", "dg", "dk0", "dv0")}
+    opt = lambda x, b, h: None if x is None else x[b, h]
+    res = [[gsa_bwd_unit(q[b, h], k[b, h], v[b, h], g[b, h], do[b, h], opt(k0, b, h), opt(v0, b, h),
+                         opt(dkf, b, h), opt(dvf, b, h), tau, C) for h in range(H)] for b in range(B)]
+    for i, n in enumerate(("dq", "dk", "dv", "dg", "dk0", "dv0")):
+        out[n] = np.array([[res[b][h][i] for h in range(H)] for b in range(B)])
+    return out

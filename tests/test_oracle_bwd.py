@@ -167,3 +167,36 @@ def test_identity_read_gradient_of_q_is_linear_map():
     gr = bwd_oracle(x, w, 8.0, "identity")
     K0, V0 = x["k0"][0, 0], x["v0"][0, 0]
     assert np.allclose(gr["q"][0, 0], w["o"][0, 0] @ V0.T @ K0, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 64])
+@pytest.mark.parametrize("T", [1, 7, 20, 70])
+def test_chunk_form_backward_equals_recurrent(C, T):
+    """App. B's chunk-form backward (two GLA backward passes in reverse order,
+    dI summed over both, the gate gradient as a reversed cumsum) gives the
+    recurrent reverse-mode gradients."""
+    from oracle import chunkwise
+    x, w = draw(1, 2, T, 5, 4, 3, seed=80 + T + C)
+    ref = bwd_oracle(x, w, 8.0)
+    got = chunkwise.gsa_bwd(x["q"], x["k"], x["v"], x["g"], w["o"], x["k0"], x["v0"], w["kf"],
+                            w["vf"], tau=8.0, C=C)
+    for n in NAMES:
+        den = max(np.max(np.abs(ref[n])), 1e-300)
+        assert np.max(np.abs(got["d" + n] - ref[n])) / den < 1e-11, (n, C, T)
+
+
+def test_chunk_form_backward_extreme_gates():
+    """Gates at -inf / +inf inside and across chunks: the chunk form's decays
+    are sums of log alpha, never differences of running sums."""
+    from oracle import chunkwise
+    x, w = draw(1, 1, 40, 5, 4, 3, seed=90, init=True, final=True)
+    x["g"][..., 5, :] = -np.inf
+    x["g"][..., 12:15, 1] = np.inf
+    x["g"][..., 30, 0] = -np.inf
+    ref = bwd_oracle(x, w, 8.0)
+    got = chunkwise.gsa_bwd(x["q"], x["k"], x["v"], x["g"], w["o"], x["k0"], x["v0"], w["kf"],
+                            w["vf"], tau=8.0, C=8)
+    for n in NAMES:
+        den = max(np.max(np.abs(ref[n])), 1e-300)
+        assert np.all(np.isfinite(got["d" + n])), n
+        assert np.max(np.abs(got["d" + n] - ref[n])) / den < 1e-11, n
