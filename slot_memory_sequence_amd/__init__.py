@@ -432,6 +432,50 @@ def gsa_bwd_varlen(q, k, v, g, d_o, cu_seqlens, k0=None, v0=None, d_kf=None, d_v
     return (*outs, sg[0], sg[1])
 
 
+def _autograd_function():
+    torch = _torch()
+
+    class GsaFunction(torch.autograd.Function):
+        """gsa_fwd (final states returned) with gsa_bwd as its backward."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, k0, v0, tau, nonlinearity):
+            ctx.set_materialize_grads(False)
+            o, kf, vf = gsa_fwd(q, k, v, g, k0, v0, tau=tau, final_state=True,
+                                nonlinearity=nonlinearity)
+            ctx.save_for_backward(q, k, v, g, k0, v0)
+            ctx.tau, ctx.nonlinearity = tau, nonlinearity
+            return o, kf, vf
+
+        @staticmethod
+        def backward(ctx, d_o, d_kf, d_vf):
+            q, k, v, g, k0, v0 = ctx.saved_tensors
+            if d_o is None:
+                d_o = torch.zeros_like(v)
+            grads = gsa_bwd(q, k, v, g, d_o.contiguous(), k0, v0,
+                            None if d_kf is None else d_kf.contiguous(),
+                            None if d_vf is None else d_vf.contiguous(), tau=ctx.tau,
+                            state_grads=True, nonlinearity=ctx.nonlinearity)
+            dk0 = grads[4] if k0 is not None and ctx.needs_input_grad[4] else None
+            dv0 = grads[5] if v0 is not None and ctx.needs_input_grad[5] else None
+            return grads[0], grads[1], grads[2], grads[3], dk0, dv0, None, None
+
+    return GsaFunction
+
+
+_GSA_FUNCTION = None
+
+
+def gsa_autograd(q, k, v, g, k0=None, v0=None, *, tau=8.0, nonlinearity="softmax"):
+    """Differentiable GSA: returns (o, k_final, v_final) like gsa_fwd with
+    final_state=True, and back-propagates through gsa_bwd (all the kernels of
+    this library; the function only routes tensors)."""
+    global _GSA_FUNCTION
+    if _GSA_FUNCTION is None:
+        _GSA_FUNCTION = _autograd_function()
+    return _GSA_FUNCTION.apply(q, k, v, g, k0, v0, float(tau), nonlinearity)
+
+
 # ------------------------------------------------------------ calibration
 def measure_hbm(dst, src=None, *, stream=None, events=None):
     """Stream dst's bytes through HBM: copy src -> dst (equal byte sizes, a

@@ -239,3 +239,24 @@ def test_bwd_event_hooks_and_repeatability(gsa, torch):
     for x, y in zip(a, b):
         assert torch.equal(x, y)
     assert t[0] > 0 and t[1] > 0 and t[2] >= t[0] + t[1], t
+
+
+def test_autograd_function(gsa, torch):
+    """gsa_autograd: torch.autograd through gsa_fwd / gsa_bwd gives the direct
+    backward's bits and the oracle's gradients, for a loss on o and on the
+    final states."""
+    inp = synth.gsa_inputs(2, 2, 130, 128, 128, 64, dtype="bf16", seed=75, init_std=0.1)
+    gi = synth.gsa_grad_inputs(2, 2, 130, 128, 128, 64, dtype="bf16", seed=76, final_std=1.0)
+    leaves = {n: to_dev(inp[n], torch).requires_grad_(True) for n in ("q", "k", "v", "g", "k0", "v0")}
+    W, A, Bv = (to_dev(gi[n], torch) for n in ("do", "dkf", "dvf"))
+    o, kf, vf = gsa.gsa_autograd(*(leaves[n] for n in ("q", "k", "v", "g", "k0", "v0")), tau=8.0)
+    loss = (o.float() * W.float()).sum() + (kf * A).sum() + (vf * Bv).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    direct = gsa.gsa_bwd(*(leaves[n].detach() for n in ("q", "k", "v", "g")), W,
+                         leaves["k0"].detach(), leaves["v0"].detach(), A, Bv, state_grads=True)
+    for n, d in zip(("q", "k", "v", "g", "k0", "v0"), direct):
+        assert torch.equal(leaves[n].grad, d), n
+    ref = _ref(inp, gi, 8.0)
+    _compare(dict(zip(GRADS, (leaves[n].grad for n in ("q", "k", "v", "g", "k0", "v0")))), ref,
+             "bf16", "autograd B2 H2 T130")
