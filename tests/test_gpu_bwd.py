@@ -260,3 +260,20 @@ def test_autograd_function(gsa, torch):
     ref = _ref(inp, gi, 8.0)
     _compare(dict(zip(GRADS, (leaves[n].grad for n in ("q", "k", "v", "g", "k0", "v0")))), ref,
              "bf16", "autograd B2 H2 T130")
+
+
+@pytest.mark.parametrize("nl", ["softmax", "relu2"])
+def test_autograd_function_without_states(gsa, torch, nl):
+    """No initial states and a loss on o only (the final-state gradients
+    arrive as None), with the softmax read and an element-wise one."""
+    inp = synth.gsa_inputs(1, 3, 100, 64, 64, 32, dtype="f32", seed=77)
+    gi = synth.gsa_grad_inputs(1, 3, 100, 64, 64, 32, dtype="f32", seed=78)
+    leaves = {n: to_dev(inp[n], torch).requires_grad_(True) for n in "qkvg"}
+    W = to_dev(gi["do"], torch)
+    o, _, _ = gsa.gsa_autograd(*(leaves[n] for n in "qkvg"), tau=8.0, nonlinearity=nl)
+    (o * W).sum().backward()
+    torch.cuda.synchronize()
+    ref = oracle.gsa_bwd(*(inp[n].f64 for n in "qkvg"), gi["do"].f64, tau=8.0, nonlinearity=nl)
+    errs = {n: rel_err(to_np(leaves[n].grad), ref["d" + n]) for n in "qkvg"}
+    print("autograd %s no states: %s" % (nl, errs))
+    assert max(errs.values()) <= TOL["f32"], errs
