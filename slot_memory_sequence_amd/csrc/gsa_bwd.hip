@@ -184,8 +184,8 @@ __device__ __forceinline__ void stage_chunk(T* lds, const T* qq, const T* kk, co
 // Diag(prod_{r>j} alpha_r) i_j [k_j | v_j]^T: a product over the chunk with
 // weights in [0, 1].  Thread (slot c, part) evaluates the gates of 16
 // consecutive tokens of slot c, forms their suffix products, and the four
-// parts of a slot combine their products through LDS; then every thread
-// accumulates its slot rows x columns of the map from the LDS-staged k, v.
+// parts of a slot combine their products through LDS; the product itself runs
+// on the matrix cores in fp32 from the LDS-staged weights and k, v.
 template <typename T, int DK, int DV, int M>
 struct MapLds {
   static constexpr unsigned kv_bytes = C * (DK + DV) * sizeof(T);
@@ -205,14 +205,15 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
   T* sv = sk + C * DK;
   float* sA = reinterpret_cast<float*>(lds_raw + C * (DK + DV) * sizeof(T));  // [C][M] weights
   float* ptot = sA + C * M;                                                     // [PARTS][M]
-  const Thread th;
-  const int p = blockIdx.y, u = blockIdx.x, c0 = th.sg * S::SPT;
+  const int p = blockIdx.y, u = blockIdx.x;
   const bfk::Span sp = seq.span(u);
   const int t0 = p * C, rows = min(sp.len, t0 + C) - t0;
   if (rows <= 0) return;  // past the sequence's end: no chunk (the scans stop before it)
   const size_t row0 = sp.base + t0;
   copy_rows(sk, kk + row0 * DK, rows * DK);
   copy_rows(sv, vv + row0 * DV, rows * DV);
+  for (int i = rows * DK + threadIdx.x; i < C * DK; i += NT) sk[i] = Elem<T>::from_f(0.f);  // past the end
+  for (int i = rows * DV + threadIdx.x; i < C * DV; i += NT) sv[i] = Elem<T>::from_f(0.f);
   {
     const int c = threadIdx.x % M, part = threadIdx.x / M, j0 = part * TPP;
     float av[TPP], wv[TPP];
@@ -242,38 +243,34 @@ bwd_map(const T* __restrict__ kk, const T* __restrict__ vv, const T* __restrict_
     if (part == 0) dec[((size_t)u * P + p) * M + c] = prod * after;
   }
   __syncthreads();
-  float K[S::SPT][S::CK], V[S::SPT][S::CV];
+  // the map A^T [k | v] on fp32 matrix cores (16x16x4 tiles, fp32 products):
+  // A = sA [token][slot] is the transposed left operand, the staged k, v rows
+  // the right one; the four waves share the (M/16) x ((DK+DV)/16) output tiles
+  constexpr int NCOL = (DK + DV) / 16, TPW = (M / 16) * NCOL / 4;
+  static_assert((M / 16) * NCOL % 4 == 0, "tiles per wave");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int i = 0; i < S::SPT; i++) {
+  for (int t = 0; t < TPW; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int kend = (rows + 3) & ~3;
+  for (int k0 = 0; k0 < kend; k0 += 4) {
+    const int j = k0 + (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < S::CK; j++) K[i][j] = 0.f;
-#pragma unroll
-    for (int j = 0; j < S::CV; j++) V[i][j] = 0.f;
-  }
-  for (int n = 0; n < rows; n++) {
-    float wt[S::SPT], kv[S::CK], vv_[S::CV];
-    ldn<S::SPT>(sA + n * M + c0, wt);
-    ldn<S::CK>(sk + n * DK + th.cg * S::CK, kv);
-    ldn<S::CV>(sv + n * DV + th.cg * S::CV, vv_);
-#pragma unroll
-    for (int i = 0; i < S::SPT; i++) {
-#pragma unroll
-      for (int j = 0; j < S::CK; j++) K[i][j] += wt[i] * kv[j];
-#pragma unroll
-      for (int j = 0; j < S::CV; j++) V[i][j] += wt[i] * vv_[j];
+    for (int t = 0; t < TPW; t++) {
+      const int tile = wave * TPW + t, cb = tile / NCOL, nt = tile % NCOL;
+      const float a = sA[j * M + 16 * cb + (lane & 15)];
+      const int col = 16 * nt + (lane & 15);
+      const float b = col < DK ? Elem<T>::to_f(sk[j * DK + col]) : Elem<T>::to_f(sv[j * DV + col - DK]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
     }
   }
   float* base = st + ((size_t)u * P + p) * S::NE;
 #pragma unroll
-  for (int i = 0; i < S::SPT; i++) {
-    float* r = base + (size_t)(c0 + i) * (DK + DV);
+  for (int t = 0; t < TPW; t++) {
+    const int tile = wave * TPW + t, cb = tile / NCOL, nt = tile % NCOL;
 #pragma unroll
-    for (int j = 0; j < S::CK; j += 4)
-      *reinterpret_cast<f32x4*>(r + th.cg * S::CK + j) = f32x4{K[i][j], K[i][j + 1], K[i][j + 2], K[i][j + 3]};
-#pragma unroll
-    for (int j = 0; j < S::CV; j += 4)
-      *reinterpret_cast<f32x4*>(r + DK + th.cg * S::CV + j) =
-          f32x4{V[i][j], V[i][j + 1], V[i][j + 2], V[i][j + 3]};
+    for (int i = 0; i < 4; i++)
+      base[(size_t)(16 * cb + 4 * (lane >> 4) + i) * (DK + DV) + 16 * nt + (lane & 15)] = acc[t][i];
   }
 }
 
