@@ -329,6 +329,18 @@ def bwd_cpu_oracle(w, inp, budget_s=3.0):
                       "over B*H units" % (w["T"], runs, dt)}
 
 
+def bwd_parity(torch, w, inp, grads):
+    """Max over dq, dk, dv, dg of max |x - y| / max |y| on (batch, head)
+    unit 0 of the benched call against the oracle's backward."""
+    import oracle
+    from tests.gpu_helpers import rel_err, to_np
+    torch.cuda.synchronize()
+    one = {n: inp[n].f64[:1, :1] for n in ("q", "k", "v", "g", "do")}
+    ref = oracle.gsa_bwd(one["q"], one["k"], one["v"], one["g"], one["do"], tau=w["tau"])
+    return float("%.3e" % max(rel_err(to_np(x[:1, :1]), ref[n])
+                               for x, n in zip(grads, ("dq", "dk", "dv", "dg"))))
+
+
 def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd", cpu=True):
     """The GSA backward at a workload's shape (the training shape B8 H4 T2048
     bf16 with zero states, or the long-context one with initial states and
@@ -389,7 +401,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
             "train_step": {"value": round(B * T * steps / wall_train, 1), "unit": "tokens/s",
                            "ms_per_step": round(wall_train / steps * 1e3, 4),
                            "what": "gsa_fwd then gsa_bwd on the same batch, per step"},
-            "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None}
+            "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None,
+            "parity_rel_err": bwd_parity(torch, w, inp, outs[0]) if cpu else None}
 
 
 def bench_bwd_varlen(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_serve_N256_bwd"):
