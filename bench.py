@@ -121,8 +121,20 @@ def gsa_bwd_alg(B, H, T, dk, dv, m, dtype_bytes):
             th * (4 * dk + 3 * dv + 2 * m) * dtype_bytes)
 
 
+def rel_err(x, y):
+    """max |x - y| / max |y| over one tensor (y the oracle)."""
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    den = float(np.max(np.abs(y))) if y.size else 0.0
+    num = float(np.max(np.abs(x - y))) if y.size else 0.0
+    return num / den if den > 0 else num
+
+
 def dev_sets(torch, inp, names, nsets):
-    from tests.gpu_helpers import to_dev
+    from synth import to_dev
     base = {n: to_dev(inp[n], torch) for n in names if inp.get(n) is not None}
     sets = [base]
     for _ in range(nsets - 1):
@@ -161,25 +173,70 @@ def mean(xs):
     return sum(xs) / len(xs)
 
 
+def stats(xs):
+    """Mean, median, p10 and p90 (nearest rank) of per-step times in ms."""
+    ys = sorted(xs)
+    n = len(ys)
+
+    def q(f):
+        return ys[min(n - 1, max(0, int(round(f * (n - 1)))))]
+    return {"mean": round(mean(ys), 4), "median": round(q(0.5), 4), "p10": round(q(0.1), 4),
+            "p90": round(q(0.9), 4), "n": n}
+
+
+def cpu_threads():
+    """Host threads the oracle runs on: the CPUs this process may use (the
+    GPU machine's CPU share), and os.cpu_count() beside it."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, avail), os.cpu_count()
+
+
+def timed_runs(fn, budget_s):
+    """Run fn until budget_s seconds have passed (at least once): (runs, s)."""
+    t0 = time.perf_counter()
+    runs = 0
+    while True:
+        fn()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            return runs, dt
+
+
+def op_roofline(bytes_alg, t_ms):
+    """The whole op against HBM: algorithmic bytes over the wall-clock step
+    (every launch of the sequence and the gaps between them)."""
+    a = bytes_alg / (t_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBPS, 4), "basis": "wall-clock ms_per_step"}
+
+
 def roofline(bytes_alg, t_ms, kernel, workload):
     achieved = bytes_alg / (t_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": load_traffic(kernel, workload),
-            "kernel": kernel}
+            "kernel": kernel, "basis": "the workload's algorithmic bytes over this kernel's "
+                                       "mean dispatch time"}
 
 
 def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True, nonlinearity="softmax"):
     import synth
     inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
                            seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
-                           init_std=w["init_std"])
+                           init_std=w["init_std"], fast_slots=w.get("fast_slots", 0),
+                           fast_shift=w.get("fast_shift", 0.0))
     sets = dev_sets(torch, inp, ["q", "k", "v", "g", "k0", "v0"], nsets)
     init = inp["k0"] is not None
     B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
-    outs = [torch.empty((B, H, T, dv), dtype=torch.bfloat16, device="cuda") for _ in sets]
+    bf16 = w["dtype"] == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    outs = [torch.empty((B, H, T, dv), dtype=tdt, device="cuda") for _ in sets]
     kfs = [torch.empty((B, H, m, dk), dtype=torch.float32, device="cuda") for _ in sets] if init else None
     vfs = [torch.empty((B, H, m, dv), dtype=torch.float32, device="cuda") for _ in sets] if init else None
-    nb = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1, 0)
+    nb = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1 if bf16 else 0, 0)
     ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
 
     def call(s, events):
@@ -190,20 +247,22 @@ def bench_gsa(torch, gsa, ev, w, name, steps, warmup, nsets, warm_too=True, nonl
                     nonlinearity=nonlinearity)
 
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
-    flops, nbytes = gsa_alg(B, H, T, dk, dv, m, w["C"], 2, init_state=init, final_state=init)
+    flops, nbytes = gsa_alg(B, H, T, dk, dv, m, w["C"], 2 if bf16 else 4, init_state=init,
+                            final_state=init)
     t_op = mean([p[3] for p in ph])
     t_out = mean([p[2] for p in ph])
+    t_wall = wall / steps * 1e3
     res = {
-        "tokens_per_s": B * T * steps / wall, "ms_per_step": wall / steps * 1e3,
+        "tokens_per_s": B * T * steps / wall, "ms_per_step": t_wall,
         "ms_phases": {"state_maps": round(mean([p[0] for p in ph]), 4),
                       "scan": round(mean([p[1] for p in ph]), 4),
                       "outputs": round(t_out, 4), "op": round(t_op, 4)},
+        "ms_op_stamped": stats([p[3] for p in ph]),
+        "ms_out_kernel": stats([p[2] for p in ph]),
         "alg_flops": flops, "alg_bytes": nbytes,
-        "alg_tflops": flops / (t_op * 1e-3) / 1e12,
-        "roofline": roofline(nbytes, t_out, "gsa_bf16_out", name),
-        "op_roofline": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
-                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "alg_tflops": flops / (t_wall * 1e-3) / 1e12,
+        "roofline": roofline(nbytes, t_out, "gsa_bf16_out" if bf16 else "gsa_seg_out", name),
+        "op_roofline": op_roofline(nbytes, t_wall),
         "input_sets": nsets, "out": outs[0], "inp": inp,
     }
     res["mfma_frac_alg"] = res["alg_tflops"] / PEAK_BF16_TFLOPS
@@ -233,19 +292,24 @@ def bench_gla(torch, gsa, ev, w, steps, warmup, name="gla_bf16_T4096"):
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     flops, nbytes = gla_alg(B, H, T, dk, dv, w["C"], 2)
     t_op, t_out = mean([p[3] for p in ph]), mean([p[2] for p in ph])
+    t_wall = wall / steps * 1e3
     return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
-            "ms_per_step": round(wall / steps * 1e3, 4),
+            "ms_per_step": round(t_wall, 4),
             "ms_phases": {"state_maps": round(mean([p[0] for p in ph]), 4),
                           "scan": round(mean([p[1] for p in ph]), 4), "outputs": round(t_out, 4),
                           "op": round(t_op, 4)},
-            "alg_tflops": round(flops / (t_op * 1e-3) / 1e12, 2),
-            "mfma_frac_alg": round(flops / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "roofline": roofline(nbytes, t_out, "gla_bf16_out", name)}
+            "ms_op_stamped": stats([p[3] for p in ph]),
+            "ms_out_kernel": stats([p[2] for p in ph]),
+            "alg_tflops": round(flops / (t_wall * 1e-3) / 1e12, 2),
+            "mfma_frac_alg": round(flops / (t_wall * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "roofline": roofline(nbytes, t_out, "gla_bf16_out", name),
+            "op_roofline": op_roofline(nbytes, t_wall),
+            "_inp": inp, "_out": outs[0]}
 
 
 def bench_decode(torch, gsa, ev, w, steps, warmup):
     import synth
-    from tests.gpu_helpers import to_dev
+    from synth import to_dev
     inp = synth.decode_inputs(w["N"], w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
                               qkv_scale=w["qkv_scale"], state_std=w["state_std"])
     tok = {n: to_dev(inp[n], torch) for n in "qkvg"}
@@ -267,14 +331,15 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
         gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out,
                             events=evs[2 * i: 2 * i + 2])
     torch.cuda.synchronize()
-    t = mean([ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)])
+    tk = [ev.ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)]
+    t = mean(tk)
     units = w["N"] * w["H"]
     # both fp32 states read and written once, plus the bf16 token I/O (q, k, v, g in, o out)
     nbytes = units * (2 * 4 * w["m"] * (w["dk"] + w["dv"]) + 2 * (2 * w["dk"] + 2 * w["dv"] + w["m"]))
     r = roofline(nbytes, t, "gsa_decode_kernel", "gsa_decode_N256")
     return {"value": r["achieved"], "unit": "GB/s", "ms_kernel": round(t, 4),
-            "steps_per_s": round(steps / wall, 1), "tokens_per_s": round(w["N"] * steps / wall, 1),
-            "roofline": r}
+            "ms_kernel_stats": stats(tk), "steps_per_s": round(steps / wall, 1),
+            "tokens_per_s": round(w["N"] * steps / wall, 1), "roofline": r, "_inp": inp}
 
 
 def bench_gla_decode(torch, gsa, ev, steps, warmup):
@@ -282,7 +347,7 @@ def bench_gla_decode(torch, gsa, ev, steps, warmup):
     heads, d = 128, tau = 16): one fp32 state of 64 KB per unit read and
     written once, in place."""
     import synth
-    from tests.gpu_helpers import to_dev
+    from synth import to_dev
     N, H, d = 256, 16, 128
     inp = synth.gla_inputs(N, H, 1, d, d, dtype="bf16", seed=0, init_std=0.1)
     tok = {n: to_dev(inp[n], torch)[:, :, 0].contiguous() for n in "qkvg"}
@@ -333,7 +398,7 @@ def bwd_parity(torch, w, inp, grads):
     """Max over dq, dk, dv, dg of max |x - y| / max |y| on (batch, head)
     unit 0 of the benched call against the oracle's backward."""
     import oracle
-    from tests.gpu_helpers import rel_err, to_np
+    from synth import to_np
     torch.cuda.synchronize()
     one = {n: inp[n].f64[:1, :1] for n in ("q", "k", "v", "g", "do")}
     ref = oracle.gsa_bwd(one["q"], one["k"], one["v"], one["g"], one["do"], tau=w["tau"])
@@ -441,7 +506,7 @@ def bench_bwd_varlen(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_serve_N256
 
 def cpu_baseline(w, inp, budget_s):
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, host_cpus = cpu_threads()
     args = [inp[n].f64 for n in "qkvg"]
     ref = None
     t0 = time.perf_counter()
@@ -467,10 +532,124 @@ def cpu_baseline(w, inp, budget_s):
     single = {"value": round(w["T"] * runs1 / dt1 / (w["B"] * w["H"]) * w["B"], 1), "cores": 1,
               "sample": "one (b,h) unit of the batch (T=%d), %d run(s) in %.1f s, scaled to B*T tokens "
                         "over B*H units" % (w["T"], runs1, dt1)}
-    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+            "host_cpu_count": host_cpus, "kind": "oracle",
             "sample": "full %s batch (B=%d H=%d T=%d), %d run(s) in %.1f s, fp64 recurrence, "
-                      "OpenMP over (b,h) units" % ("training-shape", w["B"], w["H"], w["T"], runs, dt),
+                      "OpenMP over (b,h) units on the %d CPUs this process may use" % (
+                          "training-shape", w["B"], w["H"], w["T"], runs, dt, threads),
             "single_thread": single}, ref
+
+
+def oracle_gsa_sample(w, inp, out, budget_s):
+    """The oracle's forward on one thread over (batch, head) unit 0 of a GSA
+    workload (its initial state included), scaled to the batch's tokens/s
+    (every unit costs the same); and the device output of that unit against
+    it."""
+    import oracle
+    from synth import to_np
+    one = {n: (None if inp[n] is None else inp[n].f64[:1, :1].copy()) for n in ("q", "k", "v", "g", "k0", "v0")}
+    ref = {}
+
+    def run():
+        ref["o"] = oracle.gsa_fwd(one["q"], one["k"], one["v"], one["g"], one["k0"], one["v0"],
+                                  tau=w["tau"], want_states=False, nthreads=1)["o"]
+    runs, dt = timed_runs(run, budget_s)
+    return {"value": round(w["T"] * runs / dt / (w["B"] * w["H"]) * w["B"], 1), "unit": "tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "one (b,h) unit (T=%d) on one thread, %d run(s) in %.1f s, scaled to B*T tokens "
+                      "over B*H units" % (w["T"], runs, dt),
+            "parity_rel_err_unit0": float("%.3e" % rel_err(to_np(out[:1, :1]), ref["o"]))}
+
+
+def oracle_gla_sample(w, inp, out, budget_s):
+    """As oracle_gsa_sample for the GLA workload."""
+    import oracle
+    from synth import to_np
+    one = {n: inp[n].f64[:1, :1].copy() for n in "qkvg"}
+    gate = "log_decay" if w.get("log_decay_scale") else "logit"
+    ref = {}
+
+    def run():
+        ref["o"] = oracle.gla_fwd(one["q"], one["k"], one["v"], one["g"], tau=w["tau"],
+                                  want_state=False, nthreads=1, gate=gate)["o"]
+    runs, dt = timed_runs(run, budget_s)
+    return {"value": round(w["T"] * runs / dt / (w["B"] * w["H"]) * w["B"], 1), "unit": "tokens/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "one (b,h) unit (T=%d) on one thread, %d run(s) in %.1f s, scaled to B*T tokens "
+                      "over B*H units" % (w["T"], runs, dt),
+            "parity_rel_err_unit0": float("%.3e" % rel_err(to_np(out[:1, :1]), ref["o"]))}
+
+
+def oracle_decode_sample(w, inp, budget_s, nseq=4):
+    """The oracle's decode step on one thread over the first nseq sequences
+    (x all heads) of the decode batch, scaled to whole-batch steps/s."""
+    import oracle
+    sl = {n: inp[n].f64[:nseq].copy() for n in ("q", "k", "v", "g", "kstate", "vstate")}
+
+    def run():
+        oracle.gsa_decode_step(sl["q"], sl["k"], sl["v"], sl["g"], sl["kstate"], sl["vstate"],
+                               tau=w["tau"], nthreads=1)
+    runs, dt = timed_runs(run, budget_s)
+    return {"value": round(runs / dt * nseq / w["N"], 2), "unit": "steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d of %d sequences x H%d on one thread, %d run(s) in %.1f s, scaled to the "
+                      "whole batch" % (nseq, w["N"], w["H"], runs, dt)}
+
+
+def bench_small_f32(torch, gsa, ev, steps, warmup, budget_s):
+    """The small float32 workload (B1 H2 T256 d64 m32): launch-latency bound,
+    timed for completeness with the full-batch oracle beside it."""
+    import oracle
+    import synth
+    from synth import to_np
+    w = synth.WORKLOADS["gsa_f32_small"]
+    r = bench_gsa(torch, gsa, ev, w, "gsa_f32_small", steps, warmup, 2, warm_too=False)
+    args = [r["inp"][n].f64 for n in "qkvg"]
+    ref = {}
+
+    def run():
+        ref["o"] = oracle.gsa_fwd(*args, tau=w["tau"], want_states=False, nthreads=1)["o"]
+    runs, dt = timed_runs(run, budget_s)
+    return {"value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+            "ms_per_step": round(r["ms_per_step"], 4), "ms_op_stamped": r["ms_op_stamped"],
+            "note": "launch-latency bound: no roofline claim",
+            "parity_rel_err": float("%.3e" % rel_err(to_np(r["out"]), ref["o"])),
+            "cpu_oracle": {"value": round(w["B"] * w["T"] * runs / dt, 1), "unit": "tokens/s",
+                           "cores": 1, "kind": "oracle",
+                           "sample": "the full batch, %d run(s) in %.1f s" % (runs, dt)}}
+
+
+def environment(torch):
+    """Where the numbers were taken: GPU arch, ROCm/HIP, torch, and the
+    sources (git commit when a checkout is present, else a content hash)."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            rocm = open(path).read().strip()
+            break
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        sha = None
+    return {"gpu": props.name, "gfx_arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "rocm": rocm, "hip": torch.version.hip,
+            "torch": torch.__version__, "git_sha": sha, "source_sha": source_sha()}
+
+
+def source_sha():
+    """Hash of the committed sources this run executes (kernels, ABI header,
+    binding, bench)."""
+    h = hashlib.sha256()
+    paths = [os.path.join(ROOT, "include", "gsa.h"), os.path.join(ROOT, "bench.py"),
+             os.path.join(ROOT, "slot_memory_sequence_amd", "__init__.py")]
+    csrc = os.path.join(ROOT, "slot_memory_sequence_amd", "csrc")
+    paths += [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    for pth in paths:
+        h.update(open(pth, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def copy_calibration(torch, ev, steps):
@@ -497,7 +676,7 @@ def bench_serve(torch, gsa, ev, w, steps, warmup):
     all 256 x H units from those states.  Prefill tokens/s counts prompt
     tokens (sum of lengths) per second."""
     import synth
-    from tests.gpu_helpers import to_dev
+    from synth import to_dev
     lengths = synth.varlen_lengths(w["N"], w["len_lo"], w["len_hi"], seed=0)
     inp = synth.varlen_inputs(lengths, w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
                               qkv_scale=w["qkv_scale"], g_shift=w["g_shift"])
@@ -672,7 +851,7 @@ def main():
     import torch
     import slot_memory_sequence_amd as gsa
     import synth
-    from tests.gpu_helpers import rel_err, to_np
+    from synth import to_np
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -688,6 +867,7 @@ def main():
     log("bench: main done %.3g tokens/s" % main_res["tokens_per_s"])
 
     comps = {}
+    ocpu = 0.0 if args.no_cpu else max(1.0, args.cpu_seconds / 5)  # per sampled oracle timing
     if not args.no_components:
         wl = synth.WORKLOADS["gsa_bf16_long_T16384"]
         r = bench_gsa(torch, gsa, ev, wl, "gsa_bf16_long_T16384", args.steps, args.warmup, 3,
@@ -695,20 +875,44 @@ def main():
         comps["gsa_bf16_long_T16384"] = {
             "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
             "ms_per_step": round(r["ms_per_step"], 4), "ms_phases": r["ms_phases"],
+            "ms_op_stamped": r["ms_op_stamped"],
             "alg_tflops": round(r["alg_tflops"], 2), "mfma_frac_alg": round(r["mfma_frac_alg"], 4),
-            "roofline": r["roofline"], "op_roofline": r["op_roofline"]}
+            "roofline": r["roofline"], "op_roofline": r["op_roofline"],
+            "cpu_oracle": oracle_gsa_sample(wl, r["inp"], r["out"], ocpu) if ocpu else None}
         del r
         log("bench: long-context done")
-        comps["gla_bf16_T4096"] = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"],
-                                            args.steps, args.warmup)
+        wf = synth.WORKLOADS["gsa_bf16_train_T2048_fast_forget"]
+        r = bench_gsa(torch, gsa, ev, wf, "gsa_bf16_train_T2048_fast_forget", args.steps,
+                      args.warmup, args.sets, warm_too=False)
+        comps["gsa_bf16_train_T2048_fast_forget"] = {
+            "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+            "vs_headline": round(r["tokens_per_s"] / main_res["tokens_per_s"], 4),
+            "what": "the training shape with 8 of 64 slots at gate logits N(-6, 1)",
+            "ms_per_step": round(r["ms_per_step"], 4), "ms_phases": r["ms_phases"],
+            "ms_op_stamped": r["ms_op_stamped"], "roofline": r["roofline"],
+            "op_roofline": r["op_roofline"],
+            "cpu_oracle": oracle_gsa_sample(wf, r["inp"], r["out"], ocpu) if ocpu else None}
+        del r
+        log("bench: fast-forgetting slots done")
+        r = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"], args.steps, args.warmup)
+        gi, go = r.pop("_inp"), r.pop("_out")
+        r["cpu_oracle"] = oracle_gla_sample(synth.WORKLOADS["gla_bf16_T4096"], gi, go, ocpu) if ocpu else None
+        comps["gla_bf16_T4096"] = r
+        del gi, go
         log("bench: gla done")
-        comps["gla_bf16_T4096_log_decay"] = bench_gla(
-            torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096_log_decay"], max(1, args.steps // 2),
-            args.warmup, "gla_bf16_T4096_log_decay")
+        r = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096_log_decay"],
+                      max(1, args.steps // 2), args.warmup, "gla_bf16_T4096_log_decay")
+        r.pop("_inp"), r.pop("_out")
+        comps["gla_bf16_T4096_log_decay"] = r
         log("bench: gla with log-decay gates done")
-        comps["gsa_decode_N256"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"],
-                                                args.steps, args.warmup)
+        r = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256"], args.steps, args.warmup)
+        di = r.pop("_inp")
+        r["cpu_oracle"] = oracle_decode_sample(synth.WORKLOADS["gsa_decode_N256"], di, ocpu) if ocpu else None
+        comps["gsa_decode_N256"] = r
+        del di
         log("bench: decode done")
+        comps["gsa_f32_small"] = bench_small_f32(torch, gsa, ev, args.steps, args.warmup, ocpu or 0.2)
+        log("bench: small fp32 done")
         comps["gla_decode_N256"] = bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
         log("bench: GLA decode done")
         comps["gsa_bf16_train_T2048_bwd"] = bench_bwd(torch, gsa, ev, w, max(1, args.steps // 4),
@@ -767,8 +971,13 @@ def main():
         "roofline": main_res["roofline"],
         "op_roofline": main_res["op_roofline"],
         "ms_phases": main_res["ms_phases"],
+        "ms_op_stamped": main_res["ms_op_stamped"],
+        "ms_out_kernel": main_res["ms_out_kernel"],
         "alg_tflops": round(main_res["alg_tflops"], 2),
         "mfma_frac_alg": round(main_res["mfma_frac_alg"], 4),
+        "mfma": {"alg_tflops": round(main_res["alg_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(main_res["mfma_frac_alg"], 4),
+                 "basis": "algorithmic flops (causal halves) over the wall-clock step"},
         "warm_cache_tokens_per_s": round(main_res.get("warm_tokens_per_s", 0.0), 1),
         "decode_GBps": comps.get("gsa_decode_N256", {}).get("value"),
         "measured_peaks": peaks,
@@ -776,6 +985,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_rel_err": None if err is None else float("%.3e" % err),
         "kernel_source_sha": kernel_source_sha(),
+        "environment": environment(torch),
     }
     print(json.dumps(line), flush=True)
 

@@ -162,6 +162,31 @@ def _check(t, name, dtype=None):
         raise TypeError("%s must be %s" % (name, dtype))
 
 
+def _shape(t, name, shape):
+    """Raise ValueError unless t (nullable) has exactly this shape.  Runs on
+    the tensors' metadata only, before anything reaches the library: the C ABI
+    takes bare pointers, so a tensor of the wrong shape would otherwise be
+    indexed past its end by the kernels."""
+    if t is None:
+        return
+    if not hasattr(t, "shape"):
+        raise TypeError("%s must be a tensor" % name)
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(int(x) for x in shape),
+                                                          tuple(t.shape)))
+
+
+def _ndim(t, name, n):
+    if not hasattr(t, "shape"):
+        raise TypeError("%s must be a tensor" % name)
+    if len(t.shape) != n:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, n, tuple(t.shape)))
+
+
+def _wsbytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def _events(events, n=4):
     """None, or n raw hipEvent_t handles (ints or None) -> void*[n]."""
     if events is None:
@@ -197,12 +222,19 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
     ablations "identity", "swish", "relu", "relu2".
     Returns (o, k_final, v_final) -- the finals are None unless final_state."""
     torch = _torch()
-    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
-        _check(t, n, q.dtype)
-    _check(k0, "k0", torch.float32)
-    _check(v0, "v0", torch.float32)
+    _ndim(q, "q", 4)
     B, H, T, dk = q.shape
+    _ndim(v, "v", 4)
+    _ndim(g, "g", 4)
     dv, m = v.shape[-1], g.shape[-1]
+    for n, t, sh in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)), ("g", g, (B, H, T, m)),
+                     ("k0", k0, (B, H, m, dk)), ("v0", v0, (B, H, m, dv)), ("out", out, (B, H, T, dv)),
+                     ("k_final", k_final, (B, H, m, dk)), ("v_final", v_final, (B, H, m, dv))):
+        _shape(t, n, sh)
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        _check(t, n, q.dtype)
+    for n, t in (("k0", k0), ("v0", v0), ("k_final", k_final), ("v_final", v_final)):
+        _check(t, n, torch.float32)
     dt = _dt(q)
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
@@ -218,7 +250,7 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     st = lib.gsa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
                         _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), dt,
-                        _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                        _ptr(workspace), _wsbytes(workspace),
                         int(chunks_per_segment), _nl(nonlinearity), _stream(stream),
                         _events(events))
     if st:
@@ -236,16 +268,23 @@ def gsa_fwd_varlen(q, k, v, g, cu_seqlens, k0=None, v0=None, *, tau=8.0, C=64,
     Returns (o [H,total,dv], k_final, v_final) -- finals None unless
     final_state; they are the decode states of gsa_decode_step."""
     torch = _torch()
-    for nm, t in (("q", q), ("k", k), ("v", v), ("g", g)):
-        _check(t, nm, q.dtype)
-    _check(k0, "k0", torch.float32)
-    _check(v0, "v0", torch.float32)
+    _ndim(q, "q", 3)
     H, total, dk = q.shape
+    _ndim(v, "v", 3)
+    _ndim(g, "g", 3)
     dv, m = v.shape[-1], g.shape[-1]
-    dt = _dt(q)
     arr, n = _cu_array(cu_seqlens)
     if arr[n] != total:
         raise ValueError("cu_seqlens[-1] = %d but the arrays hold %d tokens" % (arr[n], total))
+    for nm, t, sh in (("k", k, (H, total, dk)), ("v", v, (H, total, dv)), ("g", g, (H, total, m)),
+                      ("k0", k0, (n, H, m, dk)), ("v0", v0, (n, H, m, dv)), ("out", out, (H, total, dv)),
+                      ("k_final", k_final, (n, H, m, dk)), ("v_final", v_final, (n, H, m, dv))):
+        _shape(t, nm, sh)
+    for nm, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        _check(t, nm, q.dtype)
+    for nm, t in (("k0", k0), ("v0", v0), ("k_final", k_final), ("v_final", v_final)):
+        _check(t, nm, torch.float32)
+    dt = _dt(q)
     if out is None:
         out = torch.empty((H, total, dv), dtype=q.dtype, device=q.device)
     if final_state:
@@ -262,7 +301,7 @@ def gsa_fwd_varlen(q, k, v, g, cu_seqlens, k0=None, v0=None, *, tau=8.0, C=64,
     st = lib.gsa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), ctypes.cast(arr, ctypes.c_void_p),
                             n, H, _ptr(k0), _ptr(v0), _ptr(out), _ptr(k_final), _ptr(v_final),
                             dk, dv, m, C, float(tau), dt, _ptr(workspace),
-                            0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                            _wsbytes(workspace), int(chunks_per_segment),
                             _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_fwd_varlen", st)
@@ -277,11 +316,18 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
     or "log_decay" (g holds log alpha per token and key dimension; tau unused).
     Returns (o, s_final or None)."""
     torch = _torch()
-    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
-        _check(t, n, q.dtype)
-    _check(s0, "s0", torch.float32)
+    _ndim(q, "q", 4)
     B, H, T, dk = q.shape
+    _ndim(v, "v", 4)
     dv = v.shape[-1]
+    for n, t, sh in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)), ("g", g, (B, H, T, dk)),
+                     ("s0", s0, (B, H, dk, dv)), ("out", out, (B, H, T, dv)),
+                     ("s_final", s_final, (B, H, dk, dv))):
+        _shape(t, n, sh)
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        _check(t, n, q.dtype)
+    for n, t in (("s0", s0), ("s_final", s_final)):
+        _check(t, n, torch.float32)
     dt = _dt(q)
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
@@ -294,7 +340,7 @@ def gla_fwd(q, k, v, g, s0=None, *, tau=16.0, C=64, final_state=False,
         raise ValueError("gate must be one of %s" % ", ".join(GATE_INPUTS))
     st = lib.gla_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s0), _ptr(out),
                         _ptr(s_final), B, H, T, dk, dv, C, float(tau), dt, _ptr(workspace),
-                        0 if workspace is None else workspace.numel(), int(chunks_per_segment),
+                        _wsbytes(workspace), int(chunks_per_segment),
                         GATE_INPUTS[gate], _stream(stream), _events(events))
     if st:
         raise GsaError("gla_fwd", st)
@@ -308,12 +354,21 @@ def gsa_decode_step(q, k, v, g, k_state, v_state, *, tau=8.0, out=None, stream=N
     events: None or two hipEvent_t handles that take the kernel's start and end.
     nonlinearity: as for gsa_fwd."""
     torch = _torch()
-    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+    _ndim(q, "q", 3)
+    N, H, dk = q.shape
+    _ndim(v, "v", 3)
+    _ndim(g, "g", 3)
+    dv, m = v.shape[-1], g.shape[-1]
+    for n, t, sh in (("k", k, (N, H, dk)), ("v", v, (N, H, dv)), ("g", g, (N, H, m)),
+                     ("k_state", k_state, (N, H, m, dk)), ("v_state", v_state, (N, H, m, dv)),
+                     ("out", out, (N, H, dv))):
+        _shape(t, n, sh)
+    if k_state is None or v_state is None:
+        raise TypeError("k_state and v_state are required")
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
         _check(t, n, q.dtype)
     _check(k_state, "k_state", torch.float32)
     _check(v_state, "v_state", torch.float32)
-    N, H, dk = q.shape
-    dv, m = v.shape[-1], g.shape[-1]
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     st = lib.gsa_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k_state),
@@ -330,13 +385,20 @@ def gla_decode_step(q, k, v, g, s_state, *, tau=16.0, gate="logit", out=None, st
     [N,H,dk,dv] advanced in place (e.g. gla_fwd's s_final).  gate as for
     gla_fwd.  Returns o [N,H,dv]."""
     torch = _torch()
-    for n, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+    _ndim(q, "q", 3)
+    N, H, dk = q.shape
+    _ndim(v, "v", 3)
+    dv = v.shape[-1]
+    for n, t, sh in (("k", k, (N, H, dk)), ("v", v, (N, H, dv)), ("g", g, (N, H, dk)),
+                     ("s_state", s_state, (N, H, dk, dv)), ("out", out, (N, H, dv))):
+        _shape(t, n, sh)
+    if s_state is None:
+        raise TypeError("s_state is required")
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
         _check(t, n, q.dtype)
     _check(s_state, "s_state", torch.float32)
     if gate not in GATE_INPUTS:
         raise ValueError("gate must be one of %s" % ", ".join(GATE_INPUTS))
-    N, H, dk = q.shape
-    dv = v.shape[-1]
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     st = lib.gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s_state), _ptr(out), N, H, dk,
@@ -366,12 +428,21 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
     nonlinearity: the slot read of the forward being differentiated, as for
     gsa_fwd."""
     torch = _torch()
+    _ndim(q, "q", 4)
+    B, H, T, dk = q.shape
+    _ndim(v, "v", 4)
+    _ndim(g, "g", 4)
+    dv, m = v.shape[-1], g.shape[-1]
+    for n, t, sh in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)), ("g", g, (B, H, T, m)),
+                     ("d_o", d_o, (B, H, T, dv)), ("k0", k0, (B, H, m, dk)), ("v0", v0, (B, H, m, dv)),
+                     ("d_kf", d_kf, (B, H, m, dk)), ("d_vf", d_vf, (B, H, m, dv))):
+        _shape(t, n, sh)
+    if d_o is None:
+        raise TypeError("d_o is required")
     for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
         _check(t, n, q.dtype)
     for n, t in (("k0", k0), ("v0", v0), ("d_kf", d_kf), ("d_vf", d_vf)):
         _check(t, n, torch.float32)
-    B, H, T, dk = q.shape
-    dv, m = v.shape[-1], g.shape[-1]
     if out is None:
         outs = [torch.empty_like(x) for x in (q, k, v, g)]
     else:
@@ -389,7 +460,7 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
     st = lib.gsa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0),
                         _ptr(d_kf), _ptr(d_vf), *(_ptr(x) for x in outs), _ptr(sg[0]), _ptr(sg[1]),
                         B, H, T, dk, dv, m, float(tau), _dt(q), _ptr(workspace),
-                        0 if workspace is None else workspace.numel(), _nl(nonlinearity),
+                        _wsbytes(workspace), _nl(nonlinearity),
                         _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_bwd", st)
@@ -408,13 +479,24 @@ def gsa_bwd_varlen(q, k, v, g, d_o, cu_seqlens, k0=None, v0=None, d_kf=None, d_v
     (d_q, d_k, d_v, d_g, d_k0, d_v0); the state gradients are None unless
     state_grads."""
     torch = _torch()
+    _ndim(q, "q", 3)
+    H, total, dk = q.shape
+    _ndim(v, "v", 3)
+    _ndim(g, "g", 3)
+    dv, m = v.shape[-1], g.shape[-1]
+    arr, n = _cu_array(cu_seqlens)
+    if arr[n] != total:
+        raise ValueError("cu_seqlens[-1] = %d but the arrays hold %d tokens" % (arr[n], total))
+    for nm, t, sh in (("k", k, (H, total, dk)), ("v", v, (H, total, dv)), ("g", g, (H, total, m)),
+                      ("d_o", d_o, (H, total, dv)), ("k0", k0, (n, H, m, dk)), ("v0", v0, (n, H, m, dv)),
+                      ("d_kf", d_kf, (n, H, m, dk)), ("d_vf", d_vf, (n, H, m, dv))):
+        _shape(t, nm, sh)
+    if d_o is None:
+        raise TypeError("d_o is required")
     for nm, t in (("q", q), ("k", k), ("v", v), ("g", g), ("d_o", d_o)):
         _check(t, nm, q.dtype)
     for nm, t in (("k0", k0), ("v0", v0), ("d_kf", d_kf), ("d_vf", d_vf)):
         _check(t, nm, torch.float32)
-    arr, n = _cu_array(cu_seqlens)
-    H, _, dk = q.shape
-    dv, m = v.shape[-1], g.shape[-1]
     outs = [torch.empty_like(x) for x in (q, k, v, g)]
     sg = [None, None]
     if state_grads:
@@ -425,7 +507,7 @@ def gsa_bwd_varlen(q, k, v, g, d_o, cu_seqlens, k0=None, v0=None, d_kf=None, d_v
     st = lib.gsa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), ctypes.cast(arr, _P), n, H,
                             _ptr(k0), _ptr(v0), _ptr(d_kf), _ptr(d_vf), *(_ptr(x) for x in outs),
                             _ptr(sg[0]), _ptr(sg[1]), dk, dv, m, float(tau), _dt(q), _ptr(workspace),
-                            0 if workspace is None else workspace.numel(), _stream(stream),
+                            _wsbytes(workspace), _stream(stream),
                             _events(events))
     if st:
         raise GsaError("gsa_bwd_varlen", st)
@@ -448,6 +530,7 @@ def _autograd_function():
             return o, kf, vf
 
         @staticmethod
+        @torch.autograd.function.once_differentiable
         def backward(ctx, d_o, d_kf, d_vf):
             q, k, v, g, k0, v0 = ctx.saved_tensors
             if d_o is None:

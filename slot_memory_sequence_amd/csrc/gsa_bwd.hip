@@ -827,6 +827,8 @@ int launch(const GsaBwdLaunch& a) {
     if (tg == 0) {  // only empty sequences
       state_copy(dk0, dkf, (size_t)ng * MK, a.stream);
       state_copy(dv0, dvf, (size_t)ng * MV, a.stream);
+      if (groups == 1)  // the call's only group: its events still stamp the (empty) work
+        for (int e = 0; e < 4; e++) record_event(a.events, e, a.stream);
       continue;
     }
     launch_seq<T, DK, DV, M, ACT>(a, vs, ng * a.H, (tg + C - 1) / C, w, k0, v0, dkf, dvf, dk0, dv0,

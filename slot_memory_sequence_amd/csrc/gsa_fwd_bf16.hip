@@ -938,6 +938,7 @@ static int launch_act(const GsaLaunch& a) {
       if (tmax == 0) {  // only empty sequences: the final states are the initial ones
         state_copy(b.kf, b.k0, (size_t)ng * MK, a.stream);
         state_copy(b.vf, b.v0, (size_t)ng * MV, a.stream);
+        for (int e = 0; e < 4; e++) record_event(b.events, e, a.stream);  // only with one group
         continue;
       }
       // longest first (stable: equal lengths keep their order, so equal-length

@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "Stored", "bf16_bits", "bf16_to_f64", "stored", "gsa_inputs", "gla_inputs",
-    "decode_inputs", "varlen_lengths", "varlen_inputs", "WORKLOADS",
+    "decode_inputs", "varlen_lengths", "varlen_inputs", "WORKLOADS", "to_dev", "to_np",
 ]
 
 
@@ -70,9 +70,11 @@ def _normal(rng, shape):
 
 
 def gsa_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
-               g_shift=0.0, init_std=None):
+               g_shift=0.0, init_std=None, fast_slots=0, fast_shift=0.0):
     """q,k,v ~ N(0,1)*qkv_scale [B,H,T,d]; g ~ N(0,1)+g_shift [B,H,T,m];
-    optional K0 [B,H,m,dk], V0 [B,H,m,dv] ~ N(0, init_std) stored as float32."""
+    optional K0 [B,H,m,dk], V0 [B,H,m,dv] ~ N(0, init_std) stored as float32.
+    fast_slots > 0: the logits of the first fast_slots slots are shifted by
+    fast_shift in addition (a set of fast-forgetting slots)."""
     rng = np.random.default_rng(seed)
     if qkv_scale is None:
         qkv_scale = 1.0 / math.sqrt(dk)
@@ -80,6 +82,8 @@ def gsa_inputs(B, H, T, dk, dv, m, dtype="bf16", seed=0, qkv_scale=None,
     k = _normal(rng, (B, H, T, dk)) * qkv_scale
     v = _normal(rng, (B, H, T, dv)) * qkv_scale
     g = _normal(rng, (B, H, T, m)) + g_shift
+    if fast_slots:
+        g[..., :fast_slots] += fast_shift
     out = dict(q=stored(q, dtype), k=stored(k, dtype), v=stored(v, dtype),
                g=stored(g, dtype), k0=None, v0=None)
     if init_std is not None:
@@ -194,6 +198,12 @@ WORKLOADS = {
     "gsa_bf16_train_T2048": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=64, C=64,
                                  tau=8.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
                                  g_shift=0.0, init_std=None),
+    # the training shape with 8 of the 64 slots forgetting fast (logits
+    # N(-6, 1): log alpha ~ -0.75 per token, about -48 over a 64-token chunk)
+    "gsa_bf16_train_T2048_fast_forget": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=64,
+                                             C=64, tau=8.0, dtype="bf16",
+                                             qkv_scale=1 / math.sqrt(128), g_shift=0.0,
+                                             init_std=None, fast_slots=8, fast_shift=-6.0),
     "gla_bf16_T4096": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64, tau=16.0,
                            dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                            init_std=None),
@@ -214,3 +224,20 @@ WORKLOADS = {
                                 dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                                 len_lo=16, len_hi=1024),
 }
+
+
+def to_dev(st, torch):
+    """Stored -> device tensor with identical stored bits (data movement only)."""
+    if st is None:
+        return None
+    if st.dtype == "bf16":
+        t = torch.from_numpy(st.raw.view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(st.raw, dtype=np.float32))
+    return t.to("cuda")
+
+
+def to_np(t):
+    """Device tensor -> float64 numpy array (exact upcast)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)

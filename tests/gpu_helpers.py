@@ -2,21 +2,7 @@
 and compare device results with the oracle."""
 import numpy as np
 
-
-def to_dev(st, torch):
-    """synth.Stored -> device tensor with identical stored bits."""
-    if st is None:
-        return None
-    if st.dtype == "bf16":
-        t = torch.from_numpy(st.raw.view(np.int16).copy()).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(np.ascontiguousarray(st.raw, dtype=np.float32))
-    return t.to("cuda")
-
-
-def to_np(t):
-    import torch
-    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+from synth import to_dev, to_np  # noqa: F401  (re-exported for the tests)
 
 
 def rel_err(x, y):
@@ -31,3 +17,32 @@ def rel_err(x, y):
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+class RawEvents:
+    """hipEvent_t handles created through the process's HIP runtime (the one
+    torch loaded), for the entry points' timing hooks; elapsed() fails unless
+    both events were recorded."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = self.ct.c_void_p()
+            assert self.hip.hipEventCreate(self.ct.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed(self, a, b):
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        assert rc == 0, "hipEventElapsedTime failed (%d): an event was not recorded" % rc
+        return float(f.value)

@@ -277,3 +277,14 @@ def test_autograd_function_without_states(gsa, torch, nl):
     errs = {n: rel_err(to_np(leaves[n].grad), ref["d" + n]) for n in "qkvg"}
     print("autograd %s no states: %s" % (nl, errs))
     assert max(errs.values()) <= TOL["f32"], errs
+
+
+def test_autograd_double_backward_raises(gsa, torch):
+    """The backward is not itself differentiable: asking for a gradient of a
+    gradient raises instead of silently dropping the second-order terms."""
+    inp = synth.gsa_inputs(1, 1, 40, 64, 64, 32, dtype="f32", seed=79)
+    leaves = {n: to_dev(inp[n], torch).requires_grad_(True) for n in "qkvg"}
+    o, _, _ = gsa.gsa_autograd(*(leaves[n] for n in "qkvg"), tau=8.0)
+    (gq,) = torch.autograd.grad(o.sum(), leaves["q"], create_graph=True)
+    with pytest.raises(RuntimeError):
+        torch.autograd.grad(gq.sum(), leaves["k"])

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import RawEvents, TOL, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -127,6 +127,11 @@ def test_bwd_varlen_all_empty(gsa, torch):
     e = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
     eg = torch.empty((2, 0, 64), dtype=torch.bfloat16, device="cuda")
     dkf, dvf = to_dev(gi["dkf"], torch), to_dev(gi["dvf"], torch)
-    out = gsa.gsa_bwd_varlen(e, e, e, eg, e, [0, 0, 0, 0], None, None, dkf, dvf, state_grads=True)
+    ev = RawEvents()
+    evs = ev.create(4)
+    out = gsa.gsa_bwd_varlen(e, e, e, eg, e, [0, 0, 0, 0], None, None, dkf, dvf, state_grads=True,
+                             events=evs)
     torch.cuda.synchronize()
     assert torch.equal(out[4], dkf) and torch.equal(out[5], dvf)
+    for a, b in ((0, 1), (2, 3), (0, 3)):  # every timing hook was recorded
+        assert ev.elapsed(evs[a], evs[b]) >= 0.0

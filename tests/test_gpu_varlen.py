@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import RawEvents, TOL, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +105,21 @@ def test_varlen_in_place_state_advance(gsa, torch):
 def test_varlen_all_empty_and_single(gsa, torch):
     _check(gsa, torch, [0, 0, 0], 2, 128, 64, init=True, seed=6)
     _check(gsa, torch, [777], 4, 128, 64, init=True, seed=7)
+
+
+def test_varlen_all_empty_records_events(gsa, torch):
+    """A call whose only group holds empty sequences still records its four
+    timing hooks (a caller timing it needs every event recorded)."""
+    ev = RawEvents()
+    evs = ev.create(4)
+    e = torch.empty((2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    eg = torch.empty((2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    k0 = torch.randn((3, 2, 64, 128), device="cuda")
+    _, kf, _ = gsa.gsa_fwd_varlen(e, e, e, eg, [0, 0, 0, 0], k0, None, final_state=True, events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(kf, k0)
+    for a, b in ((0, 1), (2, 3), (0, 3)):
+        assert ev.elapsed(evs[a], evs[b]) >= 0.0
 
 
 def test_varlen_equal_lengths_is_the_dense_call(gsa, torch):
