@@ -148,6 +148,7 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
   if (T == 0) {  // nothing to read: the final state is the initial state
     gsa::state_copy(kf, k0, (size_t)units * m * dk, stream);
     gsa::state_copy(vf, v0, (size_t)units * m * dv, stream);
+    for (int e = 0; e < 4; e++) gsa::record_event(events, e, stream);  // every hook still stamps
     return hip_status();
   }
   gsa::GsaLaunch a{};
@@ -332,6 +333,7 @@ int gla_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
   if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
   if (T == 0) {
     gsa::state_copy(sf, s0, (size_t)units * dk * dv, stream);
+    for (int e = 0; e < 4; e++) gsa::record_event(events, e, stream);
     return hip_status();
   }
   gsa::GlaLaunch a{};
