@@ -21,9 +21,12 @@
  *    GSA_DTYPE_BF16).  Recurrent states are always float32 and all
  *    accumulation is float32.
  *  - The caller owns every buffer.  The library never allocates or frees
- *    device memory, keeps no mutable global state and takes scratch space only
- *    from the workspace argument (query its size first; NULL is allowed when
- *    the query returns 0).
+ *    device memory and takes scratch space only from the workspace argument
+ *    (query its size first; NULL is allowed when the query returns 0).  The
+ *    one exception is gsa_fwd_noalloc, for callers that cannot allocate: it
+ *    uses a fixed scratch array of the library's own code object (placed on
+ *    each GPU by the code-object loader) and caches that array's address per
+ *    device; no other entry point keeps mutable global state.
  *  - stream is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous: they enqueue kernels and return.
  *  - Arguments are validated on the host before anything is enqueued; on any
@@ -39,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GSA_ABI_VERSION 3
+#define GSA_ABI_VERSION 4
 
 typedef enum {
   GSA_OK = 0,
@@ -49,7 +52,9 @@ typedef enum {
   GSA_ERR_UNSUPPORTED = 4, /* (dtype, dk, dv, m, C) not compiled */
   GSA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
   GSA_ERR_HIP = 6,         /* a kernel launch failed */
-  GSA_ERR_ALIAS = 7        /* an output overlaps an input or another output */
+  GSA_ERR_ALIAS = 7,       /* an output overlaps an input or another output */
+  GSA_ERR_SCRATCH_LIMIT = 8 /* the problem needs more than the library's fixed scratch
+                               (gsa_fwd_noalloc) */
 } gsa_status;
 
 typedef enum { GSA_DTYPE_F32 = 0, GSA_DTYPE_BF16 = 1 } gsa_dtype;
@@ -215,6 +220,37 @@ int gsa_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
                const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T, int dk,
                int dv, int m, int C, float tau, int dtype, void* workspace, size_t workspace_bytes,
                int chunks_per_segment, int nonlinearity, void* stream, void* const* events);
+
+/*
+ * gsa_fwd_ex for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * scratch space that gsa_fwd takes from its workspace argument (segment state
+ * maps, start states and decay products) comes instead from a fixed array of
+ * GSA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on, from the first call on that GPU until the process ends.  No other
+ * memory is allocated or freed, by the library or anything it calls.
+ *   Arguments, shapes, aliasing, events and the result: those of gsa_fwd_ex
+ *   with the same arguments (the same kernels, segment split and scratch
+ *   layout, so the same bits).
+ *   Returns GSA_ERR_SCRATCH_LIMIT, before anything is enqueued, when
+ *   gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C, dtype, chunks_per_segment)
+ *   exceeds GSA_NOALLOC_SCRATCH_BYTES (32 MiB: e.g. 32 (batch, head) units x
+ *   T = 2048 need 17 MB, 8 units x T = 16384 need 17 MB); GSA_ERR_HIP when the
+ *   stream's device cannot be determined or the array's address cannot be
+ *   looked up.
+ *   Concurrency: every call on one GPU uses the same array.  Calls that may
+ *   overlap on one GPU (on different streams, or from different host threads
+ *   without ordering) race and give wrong results; calls ordered on one
+ *   stream do not.  Nothing needs clearing between calls (every word of the
+ *   scratch a call reads it has written first).
+ * gsa_fwd_noalloc_scratch_bytes() returns GSA_NOALLOC_SCRATCH_BYTES.
+ */
+#define GSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+size_t gsa_fwd_noalloc_scratch_bytes(void);
+int gsa_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const float* k0,
+                    const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T,
+                    int dk, int dv, int m, int C, float tau, int dtype, int chunks_per_segment,
+                    int nonlinearity, void* stream, void* const* events);
 
 /*
  * One recurrent GSA step (Sec. 3.2 recurrent form) for N sequences x H heads.

@@ -84,6 +84,10 @@ lib.gsa_bwd_ex.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_bwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 5
 lib.gsa_bwd_varlen_workspace_bytes.restype = _S
 lib.gsa_bwd_varlen.argtypes = [_P] * 5 + [_P, _I, _I] + [_P] * 10 + [_I] * 3 + [_F, _I, _P, _S, _P, _P]
+lib.gsa_fwd_noalloc_scratch_bytes.restype = _S
+lib.gsa_fwd_noalloc_scratch_bytes.argtypes = []
+lib.gsa_fwd_noalloc.restype = _I
+lib.gsa_fwd_noalloc.argtypes = [_P] * 9 + [_I] * 7 + [_F, _I, _I, _I, _P, _P]
 
 
 class GsaError(RuntimeError):
@@ -255,6 +259,38 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
                         _events(events))
     if st:
         raise GsaError("gsa_fwd", st)
+    return out, k_final, v_final
+
+
+def gsa_fwd_noalloc(q, k, v, g, k0=None, v0=None, *, out, k_final=None, v_final=None, tau=8.0,
+                    C=64, chunks_per_segment=0, stream=None, events=None, nonlinearity="softmax"):
+    """gsa_fwd without a workspace: the scratch space comes from the
+    library's fixed per-GPU array (gsa_fwd_noalloc_scratch_bytes() bytes), so
+    nothing is allocated, here or in the library -- the caller passes every
+    output buffer.  Calls that overlap on one GPU race (they share the
+    array).  Returns (out, k_final, v_final)."""
+    torch = _torch()
+    _ndim(q, "q", 4)
+    B, H, T, dk = q.shape
+    _ndim(v, "v", 4)
+    _ndim(g, "g", 4)
+    dv, m = v.shape[-1], g.shape[-1]
+    if out is None:
+        raise TypeError("out is required (nothing is allocated)")
+    for n, t, sh in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)), ("g", g, (B, H, T, m)),
+                     ("k0", k0, (B, H, m, dk)), ("v0", v0, (B, H, m, dv)), ("out", out, (B, H, T, dv)),
+                     ("k_final", k_final, (B, H, m, dk)), ("v_final", v_final, (B, H, m, dv))):
+        _shape(t, n, sh)
+    for n, t in (("q", q), ("k", k), ("v", v), ("g", g), ("out", out)):
+        _check(t, n, q.dtype)
+    for n, t in (("k0", k0), ("v0", v0), ("k_final", k_final), ("v_final", v_final)):
+        _check(t, n, torch.float32)
+    st = lib.gsa_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
+                             _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, C, float(tau), _dt(q),
+                             int(chunks_per_segment), _nl(nonlinearity), _stream(stream),
+                             _events(events))
+    if st:
+        raise GsaError("gsa_fwd_noalloc", st)
     return out, k_final, v_final
 
 

@@ -183,6 +183,7 @@ const char* gsa_status_string(int s) {
     case GSA_ERR_WORKSPACE: return "workspace missing or too small";
     case GSA_ERR_HIP: return "HIP launch failed";
     case GSA_ERR_ALIAS: return "output overlaps an input or another output";
+    case GSA_ERR_SCRATCH_LIMIT: return "problem needs more than the library's fixed scratch";
     default: return "unknown status";
   }
 }

@@ -29,11 +29,11 @@ def test_header_symbols_exported(gsa):
     assert {"gsa_fwd", "gla_fwd", "gsa_decode_step", "gsa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(gsa.lib, n), "missing export: " + n
-    assert gsa.lib.gsa_abi_version() == 3
+    assert gsa.lib.gsa_abi_version() == 4
 
 
 def test_status_strings(gsa):
-    for s in range(0, 8):
+    for s in range(0, 9):
         assert gsa.status_string(s) and gsa.status_string(s) != "unknown status"
     assert gsa.status_string(99) == "unknown status"
 
@@ -313,3 +313,23 @@ def test_bwd_varlen_validation(gsa):
     arr = (ctypes.c_int * 3)(0, 70, 200)
     assert gsa.lib.gsa_bwd_varlen_workspace_bytes(ctypes.cast(arr, P), 2, 2, 128, 128, 64) > 0
     assert gsa.lib.gsa_bwd_varlen_workspace_bytes(None, 2, 2, 128, 128, 64) == 0
+
+
+def test_noalloc_rejects_before_touching_the_device(gsa):
+    """gsa_fwd_noalloc refuses problems whose scratch exceeds its fixed array
+    (GSA_ERR_SCRATCH_LIMIT) and invalid sizes (GSA_ERR_SHAPE) on the host,
+    before it looks up a device or enqueues anything -- so these calls run
+    without a GPU."""
+    P = ctypes.c_void_p
+    f = gsa.lib.gsa_fwd_noalloc
+    cap = gsa.lib.gsa_fwd_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    args = [P(FAKE), P(FAKE + 0x100000), P(FAKE + 0x200000), P(FAKE + 0x300000), P(None), P(None),
+            P(FAKE + 0x400000), P(None), P(None)]
+    # 64 units x 16384 tokens, one chunk per segment: 64 * 256 maps of 64 KB
+    B, H, T = 16, 4, 16384
+    need = gsa.gsa_fwd_workspace_bytes(B, H, T, 128, 128, 64, 64, 1, 1)
+    assert need > cap
+    assert f(*args, B, H, T, 128, 128, 64, 64, 8.0, 1, 1, 0, None, None) == 8
+    assert gsa.status_string(8) != "unknown status"
+    assert f(*args, -1, H, T, 128, 128, 64, 64, 8.0, 1, 0, 0, None, None) == 2
