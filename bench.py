@@ -133,6 +133,26 @@ def rel_err(x, y):
     return num / den if den > 0 else num
 
 
+def gsa_bwd_chunk_alg(B, H, T, dk, dv, m, C, dtype_bytes):
+    """The chunk-form backward on the matrix cores, per launch.  Algorithmic
+    flops (causal halves only, 2 per multiply-add) of the forward sweep (z,
+    ds, dq with their intra-chunk scores, the state carry, the reverse map)
+    and of the reverse sweep (the two score sets, A_dq / A_2, dk and dv inter
+    and intra, di inter and intra, the adjoint update); and algorithmic bytes:
+    forward sweep q, k, v, g, dO read and dq written, reverse sweep the same
+    reads and dk, dv, dg written, the whole backward each input read and each
+    gradient written once."""
+    th = B * H * T
+    h = (C + 1) / 2.0
+    fwd = (m * dk + h * dk + h * m) + (m * dv + h * dv + h * m) + (m * dk + h * m + h * dk) + 2 * m * (dk + dv)
+    rev = (h * (dk + dv) + 2 * h * m + m * (dk + dv) + h * (dk + dv) + m * (dk + dv) + 2 * h * m +
+           m * (dk + dv))
+    reads = (2 * dk + 2 * dv + m) * dtype_bytes
+    return {"flops_fwd": 2 * fwd * th, "flops_rev": 2 * rev * th,
+            "bytes_fwd": th * (reads + dk * dtype_bytes), "bytes_rev": th * (reads + (dk + dv + m) * dtype_bytes),
+            "bytes": th * (4 * dk + 3 * dv + 2 * m) * dtype_bytes}
+
+
 def dev_sets(torch, inp, names, nsets):
     from synth import to_dev
     base = {n: to_dev(inp[n], torch) for n in names if inp.get(n) is not None}
@@ -420,7 +440,7 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     inp["do"], inp["dkf"], inp["dvf"] = gi["do"], gi["dkf"], gi["dvf"]
     sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do", "k0", "v0", "dkf", "dvf"], 2)
     outs = [tuple(torch.empty_like(s[n]) for n in "qkvg") for s in sets]
-    ws = torch.empty(gsa.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(gsa.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, 1), dtype=torch.uint8, device="cuda")
 
     def call(s, events):
         i = next(j for j, x in enumerate(sets) if x is s)
@@ -429,7 +449,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
 
     wall, ph = time_op(torch, ev, call, sets, steps, warmup)
     t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
-    f_f, f_r, nbytes = gsa_bwd_alg(B, H, T, dk, dv, m, 2)
+    al = gsa_bwd_chunk_alg(B, H, T, dk, dv, m, w["C"], 2)
+    nbytes = al["bytes"]
     # one training step of the op: the forward, then its backward (same inputs)
     o_buf = [torch.empty_like(s_["v"]) for s_ in sets]
     nbf = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1, 0)
@@ -449,20 +470,23 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
         train_step(i)
     torch.cuda.synchronize()
     wall_train = time.perf_counter() - t0
-    kern, fl, t = ("bwd_walk_fwd", f_f, t_f) if t_f >= t_r else ("bwd_walk_rev", f_r, t_r)
-    ach = fl / (t * 1e-3) / 1e12
+    kern, kb, t = ("bwd_bf16_fwd", al["bytes_fwd"], t_f) if t_f >= t_r else ("bwd_bf16_rev", al["bytes_rev"], t_r)
     t_op = wall / steps * 1e3
+    fl = al["flops_fwd"] + al["flops_rev"]
     return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
             "ms_per_step": round(t_op, 4),
-            "ms_kernels": {"bwd_walk_fwd": round(t_f, 4), "bwd_walk_rev": round(t_r, 4)},
-            "walk_tflops": {"bwd_walk_fwd": round(f_f / (t_f * 1e-3) / 1e12, 2),
-                            "bwd_walk_rev": round(f_r / (t_r * 1e-3) / 1e12, 2)},
-            "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_VALU_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_VALU_TFLOPS, 4),
-                         "traffic": load_traffic(kern, name), "kernel": kern},
-            "op_hbm": {"bound": "hbm", "achieved": round(nbytes / (t_op * 1e-3) / 1e9, 1),
-                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": round(nbytes / (t_op * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+            "ms_kernels": {"bwd_bf16_fwd": round(t_f, 4), "bwd_bf16_rev": round(t_r, 4)},
+            "ms_kernel_stats": {"bwd_bf16_fwd": stats([p[0] for p in ph]),
+                                "bwd_bf16_rev": stats([p[2] for p in ph])},
+            "kernel_alg_tflops": {"bwd_bf16_fwd": round(al["flops_fwd"] / (t_f * 1e-3) / 1e12, 2),
+                                  "bwd_bf16_rev": round(al["flops_rev"] / (t_r * 1e-3) / 1e12, 2)},
+            "roofline": dict(roofline(kb, t, kern, name),
+                             basis="this kernel's algorithmic bytes (q, k, v, g, dO read and its gradients "
+                                   "written once) over its mean dispatch time"),
+            "op_roofline": op_roofline(nbytes, t_op),
+            "mfma": {"alg_tflops": round(fl / (t_op * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fl / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "basis": "the chunk form's algorithmic flops (causal halves) over the wall-clock step"},
             "train_step": {"value": round(B * T * steps / wall_train, 1), "unit": "tokens/s",
                            "ms_per_step": round(wall_train / steps * 1e3, 4),
                            "what": "gsa_fwd then gsa_bwd on the same batch, per step"},

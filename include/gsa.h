@@ -325,6 +325,16 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
  * Asynchronous on stream; status as for gsa_fwd.
  */
 int gsa_bwd_supported(int dk, int dv, int m, int dtype);
+/* Workspace bytes of gsa_bwd / gsa_bwd_ex for this dtype and slot read (a
+ * gsa_slot_nonlinearity code; 0 on invalid arguments or T = 0).  bf16 with
+ * any read but ReLU runs the chunk form on the matrix cores and keeps
+ * per-segment states, reverse maps and bf16 per-token read weights (59 MB at
+ * B8 H4 T2048 d128 m64); float32, and bf16 with the ReLU read (whose
+ * derivative, a step at 0, needs fp32 scores), run fp32 token walks that
+ * keep per-chunk states and five fp32 per-token arrays. */
+size_t gsa_bwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int m, int dtype,
+                                  int nonlinearity);
+/* The largest need over dtypes and reads (enough for any call). */
 size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m);
 int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,
             const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,

@@ -79,6 +79,8 @@ lib.gsa_decode_step_ex.argtypes = [_P] * 7 + [_I] * 5 + [_F, _I, _I, _P, _P]
 lib.gsa_bwd_supported.argtypes = [_I] * 4
 lib.gsa_bwd_workspace_bytes.argtypes = [_I] * 6
 lib.gsa_bwd_workspace_bytes.restype = _S
+lib.gsa_bwd_workspace_bytes_ex.argtypes = [_I] * 8
+lib.gsa_bwd_workspace_bytes_ex.restype = _S
 lib.gsa_bwd.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _P, _P]
 lib.gsa_bwd_ex.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_bwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 5
@@ -449,8 +451,12 @@ def gsa_bwd_supported(dk, dv, m, dtype=DTYPE_BF16) -> bool:
     return bool(lib.gsa_bwd_supported(dk, dv, m, dtype))
 
 
-def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m) -> int:
-    return int(lib.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m))
+def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, dtype=None, nonlinearity="softmax") -> int:
+    """Workspace bytes of gsa_bwd for this storage type (DTYPE_F32 /
+    DTYPE_BF16) and slot read; without a dtype, enough for any call."""
+    if dtype is None:
+        return int(lib.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m))
+    return int(lib.gsa_bwd_workspace_bytes_ex(B, H, T, dk, dv, m, int(dtype), _nl(nonlinearity)))
 
 
 def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
@@ -490,7 +496,7 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
     sg = [None, None]
     if state_grads:
         sg = [torch.empty((B, H, m, d), dtype=torch.float32, device=q.device) for d in (dk, dv)]
-    nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m)
+    nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, _dt(q), nonlinearity)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     st = lib.gsa_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0),

@@ -436,10 +436,21 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
   return hip_status();
 }
 
-size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m) {
-  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1) return 0;
+size_t gsa_bwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int m, int dtype, int nonlinearity) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !dtype_ok(dtype) ||
+      !nonlinearity_ok(nonlinearity))
+    return 0;
+  if (T == 0) return 0;
   const size_t units = (size_t)B * H;
-  return gsa::gsa_bwd_ws_bytes(units, ((size_t)T + kChunk - 1) / kChunk, units * T, dk, dv, m);
+  return gsa::gsa_bwd_need_bytes(dtype, nonlinearity, false, units, ((size_t)T + kChunk - 1) / kChunk,
+                                 units * T, T, dk, dv, m);
+}
+
+size_t gsa_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m) {
+  // enough for either storage type and any read (the token-walk path's need
+  // is the larger)
+  return std::max(gsa_bwd_workspace_bytes_ex(B, H, T, dk, dv, m, GSA_DTYPE_F32, GSA_SLOT_SOFTMAX),
+                  gsa_bwd_workspace_bytes_ex(B, H, T, dk, dv, m, GSA_DTYPE_BF16, GSA_SLOT_SOFTMAX));
 }
 
 size_t gsa_bwd_varlen_workspace_bytes(const int* cu_seqlens, int n_seqs, int H, int dk, int dv, int m) {
@@ -485,8 +496,8 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
   const Range rdq = rng(d_q, ntok * dk * es), rdk = rng(d_k, ntok * dk * es),
               rdv = rng(d_v, ntok * dv * es), rdg = rng(d_g, ntok * m * es);
   const Range rdk0 = rng(d_k0, sk), rdv0 = rng(d_v0, sv);
-  const size_t need = T > 0 ? gsa::gsa_bwd_ws_bytes((size_t)launch_units, ((size_t)T + kChunk - 1) / kChunk,
-                                                    ntok, dk, dv, m)
+  const size_t need = T > 0 ? gsa::gsa_bwd_need_bytes(dtype, nonlinearity, cu != nullptr, (size_t)launch_units,
+                                                      ((size_t)T + kChunk - 1) / kChunk, ntok, T, dk, dv, m)
                             : 0;
   const Range rws = rng(workspace, need);
   const Range outs[] = {rdq, rdk, rdv, rdg, rdk0, rdv0, rws};

@@ -48,6 +48,8 @@
 // rows are placed by the sequence layout (a dense batch, or a packed batch of
 // variable-length sequences; a unit has ceil(len / C) chunks, the workgroups
 // of the grid's chunks past that return at once and the scans stop there).
+#include <type_traits>
+
 #include "../../include/gsa.h"
 #include "bf16_common.hpp"
 #include "common.hpp"
@@ -788,6 +790,8 @@ int launch(const GsaBwdLaunch& a) {
       for (int e = 0; e < 4; e++) record_event(a.events, e, a.stream);
       return 0;
     }
+    if constexpr (std::is_same<T, bf16_t>::value && ACT != kActRelu)  // the chunk form on the matrix cores
+      return gsa_bwd_bf16_dispatch(DK, DV, M, &a, false, (size_t)U, a.T) == 0 ? 0 : -1;
     const Ws w = carve(a.ws, U, P, (size_t)U * a.T, DK, DV, M);
     launch_seq<T, DK, DV, M, ACT>(a, bfk::DenseSeqs{a.T}, U, P, w, a.k0, a.v0, a.dkf, a.dvf, a.dk0, a.dv0,
                                   a.events);
@@ -857,6 +861,15 @@ int launch_act(const GsaBwdLaunch& a) {
 
 size_t gsa_bwd_ws_bytes(size_t units, size_t chunks, size_t rows, int dk, int dv, int m) {
   return bwd::ws_floats(units, chunks, rows, dk, dv, m) * sizeof(float);
+}
+
+size_t gsa_bwd_need_bytes(int dtype, int act, bool packed, size_t units, size_t chunks, size_t rows, int T,
+                          int dk, int dv, int m) {
+  if (gsa_bwd_on_mfma(dtype, act, packed)) {
+    const long long b = gsa_bwd_bf16_dispatch(dk, dv, m, nullptr, true, units, T);
+    if (b >= 0) return (size_t)b;
+  }
+  return gsa_bwd_ws_bytes(units, chunks, rows, dk, dv, m);
 }
 
 #define GSA_BWD_CASE(TY, DT, DK_, DV_, M_)                                    \

@@ -1,0 +1,1339 @@
+// GSA backward on gfx950, bf16 inputs: the chunk form on the matrix cores.
+//
+// Method: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling",
+// Sec. 3.2-3.3 (the function) and App. B (training: the two GLA passes are
+// differentiated in reverse order, the write intensity 1 - alpha collects
+// the gradient of both, the forget-gate gradient is a reversed cumulative sum
+// over tokens, states are recomputed rather than stored); App. A.1 (the chunk
+// form: a read of the chunk-start state plus a causal intra-chunk term).
+//
+// Per chunk of C = 64 tokens, with the chunk-local cumulative decay E (per
+// slot), X = (1 - alpha) / E, Z = (1 - alpha) E_C / E, the state W = [Kt | Vt]
+// at the chunk start and its adjoint dW at the chunk end:
+//   z^T  = E^T * (Wk Q^T  + X^T mask(K Q^T))        pass-1 read        [m x C]
+//   ds^T = E^T * (Wv dO^T + X^T mask(V dO^T))       pass-1 read of dO
+//   s = softmax(z) (or f(z)),  dz = s (ds - s.ds)  (or f'(z) ds)
+//   dq^T = Wk^T (dz*E)^T + K^T mask(X (dz*E)^T)     pass-2 read
+//   dk   = Z dWk + mask(X (dz*E)^T)^T Q,  dv = Z dWv + mask(X (s*E)^T)^T dO
+//   di   = (1/E) * (E_C dW [k|v]^T + mask(K Q^T)^T (dz*E) + mask(V dO^T)^T (s*E))
+//   reverse map of the chunk: [Q | dO]^T [dz*E | s*E]  (what its reads add
+//   to the adjoint of its start state); dW at the chunk start =
+//   Diag(E_C) dW + that map.
+// The gate: with G_t = sum_{r<=t} log alpha_r, dL/dG_t = z dz + s ds - i di
+// on the reads and writes of token t, and d log alpha_t = sum_{r>=t} dL/dG_r -
+// alpha_t di_t.  The sum over all tokens after a point t0 equals
+// <dW_{t0}, W_{t0}> per slot (the adjoint of the state at t0 times that state:
+// scaling every later decay by e^eps scales exactly the state carried over
+// t0), so each workgroup takes its carry from later chunks from that dot at
+// its segment end and sums only inside its own segment.
+//
+// Launches (one workgroup per (segment, unit); segments of S chunks):
+//   1. gsa_bf16_state + gsa_bf16_scan (the forward's): segment start states;
+//   2. bwd_bf16_fwd: per segment, chunks in order from its start state: the
+//      state carry and the reverse map in MFMA accumulators (state waves),
+//      z, ds, s, dz, h = z dz + s ds and dq (pass waves); s, dz, h are kept
+//      per token (bf16) for the reverse sweep; the segment's end state is
+//      written over its start state, its reverse map and decay beside it;
+//   3. bwd_bf16_rscan: the end adjoint of every segment (reverse scan of the
+//      reverse maps from the final-state gradients) and the initial-state
+//      gradients;
+//   4. bwd_bf16_rev: per segment, chunks in reverse from its end adjoint:
+//      the adjoint update (state waves), dk, dv, di and dg (pass waves).
+// A chunk where some slot's decay product falls below e^-40 (the factorised
+// forms divide by E) runs as an exact token walk of the state waves over the
+// fp32 state / adjoint they hold in their accumulators.
+#include <type_traits>
+
+#include "../../include/gsa.h"
+#include "bf16_common.hpp"
+#include "bf16_state.hpp"
+#include "common.hpp"
+#include "internal.hpp"
+#include "launch.hpp"
+
+namespace gsa {
+namespace bfb {
+
+using namespace bfk;
+
+// --------------------------------------------------------------- LDS plan
+// Shared by both sweeps: the chunk's q, k, v, dO tiles, a bf16 copy of the
+// state (forward sweep) or of its adjoint (reverse sweep), one set of chunk
+// factors, and two bf16 [C][M] operand tiles (forward sweep: s*E*D and
+// dz*E*D for the reverse map, D the decay from the segment start; reverse
+// sweep: s*E and dz*E).  The exact path keeps log alpha [C][M] fp32 over X
+// and Z, and its reductions in the operand tiles' place.
+template <int DK, int DV, int M>
+struct BwdLds {
+  static constexpr int PAD = 8;
+  static constexpr int LDQ = DK + PAD, LDV = DV + PAD, LDW = DK + DV + PAD, LDX = M + PAD, LDE = M + 4;
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + C * LDQ * 2;
+  static constexpr int oV = oK + C * LDQ * 2;
+  static constexpr int oDo = oV + C * LDV * 2;
+  static constexpr int oW = oDo + C * LDV * 2;    // bf16 [M][LDW]
+  static constexpr int oX = oW + M * LDW * 2;     // X [C][LDX] bf16 | exact: log alpha [C][M] fp32
+  static constexpr int oZ = oX + C * LDX * 2;     // Z [C][LDX] bf16
+  static constexpr int oE = oZ + C * LDX * 2;     // E [C][LDE] fp32
+  static constexpr int oS = oE + C * LDE * 4;     // s operand [C][LDX] bf16 | exact: reductions
+  static constexpr int oDZ = oS + C * LDX * 2;    // dz operand [C][LDX] bf16
+  static constexpr int oDec = oDZ + C * LDX * 2;  // chunk decay E_C [M] fp32
+  static constexpr int oAux = oDec + M * 4;       // fwd: decay from the segment start [M]; rev: carry [2][M]
+  static constexpr int oWt = oAux + 2 * M * 4;    // rev: per pass wave gate sums [4][M] fp32
+  static constexpr int oFlag = oWt + 4 * M * 4;   // 2 x NW ints
+  static constexpr int total = oFlag + 2 * NW * 4;
+  static_assert(C * M * 4 <= 2 * C * LDX * 2, "log alpha fits over X and Z");
+  static_assert(2 * 4 * M * 4 <= C * LDX * 2 && 6 * M * 4 <= C * LDE * 4, "exact-path reductions fit");
+  static_assert(oK % 16 == 0 && oV % 16 == 0 && oDo % 16 == 0 && oW % 16 == 0 && oX % 16 == 0 &&
+                    oZ % 16 == 0 && oE % 16 == 0 && oS % 16 == 0 && oDZ % 16 == 0 && oDec % 16 == 0,
+                "LDS tiles must stay 16-byte aligned");
+  static_assert(total <= kLdsBytes, "LDS");
+};
+
+// The chunk's factors for GPW slots from slot0 (token row = lane): X, Z (bf16),
+// E (fp32), E_C; E is also returned.  Returns whether any of these slots
+// decays below the factorised form's range in this chunk.
+template <int GPW, int LDX, int LDE, class Row>
+__device__ __forceinline__ bool bwd_factors(const Row& g, bool valid, float inv_tau, int lane, int slot0,
+                                            bf16_t* sX, bf16_t* sZ, float* sE, float* sDec,
+                                            float (&E)[GPW]) {
+  LogGates<GPW> gt;
+  gt.compute(g, valid, inv_tau);
+  bool small = false;
+  float z[GPW];
+#pragma unroll
+  for (int s = 0; s < GPW; s++) {
+    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.G[s]), 63));
+    small |= !(gc >= kFastMinLog2Decay);
+    const float dc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.E[s]), 63));
+    z[s] = gt.X[s] * dc;
+    E[s] = gt.E[s];
+    if (lane == 0) sDec[slot0 + s] = dc;
+  }
+  store_bf16_row<GPW>(sX + lane * LDX + slot0, gt.X);
+  store_bf16_row<GPW>(sZ + lane * LDX + slot0, z);
+  store_f32_row<GPW>(sE + lane * LDE + slot0, gt.E);
+  return small;
+}
+
+// Natural log alpha of GPW slots of one token row (the exact path); 0 for a
+// row past the end of the sequence.
+template <int GPW, class Row>
+__device__ __forceinline__ void log_alpha_row(const Row& g, bool valid, float inv_tau, float* dst) {
+#pragma unroll
+  for (int s = 0; s < GPW; s++) {
+    const float x = g.at(s);
+    const float la = (fminf(x, 0.f) - log1pf(__expf(-fabsf(x)))) * inv_tau;
+    dst[s] = valid ? la : 0.f;
+  }
+}
+
+// Gate terms of a logit: alpha, 1 - alpha and sigmoid(-g) / tau (hardware
+// exp2 / log2; g = +inf gives (1, 0, 0), g = -inf gives (~0, 1, 1/tau)).
+__device__ __forceinline__ void gate_terms(float g, float inv_tau, float& a, float& w, float& sn) {
+  const float t = g * 1.4426950408889634f;
+  const float l2 = fmaxf(-__builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-t)) * inv_tau, -115.f);
+  a = __builtin_amdgcn_exp2f(l2);
+  w = 1.f - a;
+  sn = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(t)) * inv_tau;
+}
+
+// sum over the 16 lanes of a row (DPP quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror); every lane of the row gets the same bits
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
+  const f32x4 x = {a, b, c, d};
+  *reinterpret_cast<bf16x4v*>(p) = pack4(x);
+}
+__device__ __forceinline__ float4 ld_bf16x4(const bf16_t* p) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
+
+// A [C][D] bf16 chunk tile moved as 16-byte vectors by the NTH threads
+// 0 .. NTH-1 (the pass waves alone in the forward sweep, so that the state
+// waves hold no prefetch registers beside their two accumulator sets).  Rows
+// >= rows_valid read the last valid row on load and are written as zeros.
+template <int D, int NTH>
+struct TileN {
+  static constexpr int VPR = D / 8;
+  static constexpr int NV = C * VPR / NTH;
+  static_assert(NV >= 1 && (C * VPR) % NTH == 0, "tile/thread mismatch");
+  uint4 r[NV];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ base, int rows_valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int idx = tid + NTH * i, row = idx / VPR, cv = idx % VPR;
+      r[i] = *reinterpret_cast<const uint4*>(base + min(row, rows_valid - 1) * D + cv * 8);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* dst, int ld, int rows_valid, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NV; i++) {
+      const int idx = tid + NTH * i, row = idx / VPR, cv = idx % VPR;
+      const bool ok = row < rows_valid;
+      *reinterpret_cast<uint4*>(dst + row * ld + cv * 8) =
+          make_uint4(ok ? r[i].x : 0u, ok ? r[i].y : 0u, ok ? r[i].z : 0u, ok ? r[i].w : 0u);
+    }
+  }
+};
+
+// ======================================================== forward sweep
+// Pass waves, first half (before the mid-chunk barrier): token rows 16J ..
+// 16J+15.  z and ds, the slot read, dz and h; s, dz and h to the per-token
+// workspace (rows < rv); s*E*D and dz*E*D rows to LDS for the reverse map;
+// (dz*E)^T as operands for the second half.
+template <int DK, int DV, int M, int J, int ACT>
+__device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, bf16_t* sS, bf16_t* sDZ,
+                                          const float* sSeg, bf16_t* __restrict__ s_rows,
+                                          bf16_t* __restrict__ dz_rows, bf16_t* __restrict__ h_rows,
+                                          int rv, bf16x8 (&dzb)[M / 32]) {
+  using Lds = BwdLds<DK, DV, M>;
+  constexpr int MT = M / 16, KQ = DK / 32, KV = DV / 32, NP = M / 32;
+  constexpr int NR = J + 1, NPR = J / 2 + 1;
+  const bf16_t* sQ = reinterpret_cast<const bf16_t*>(smem + Lds::oQ);
+  const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
+  const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Lds::oV);
+  const bf16_t* sDo = reinterpret_cast<const bf16_t*>(smem + Lds::oDo);
+  const bf16_t* sW = reinterpret_cast<const bf16_t*>(smem + Lds::oW);
+  const bf16_t* sX = reinterpret_cast<const bf16_t*>(smem + Lds::oX);
+  const float* sE = reinterpret_cast<const float*>(smem + Lds::oE);
+  const int L = lane & 15, g = lane >> 4;
+  const int j = 16 * J + L;
+
+  bf16x8 qf[KQ], df[KV];
+#pragma unroll
+  for (int s = 0; s < KQ; s++) qf[s] = ld_row(sQ, Lds::LDQ, 16 * J, 32 * s, lane);
+#pragma unroll
+  for (int s = 0; s < KV; s++) df[s] = ld_row(sDo, Lds::LDV, 16 * J, 32 * s, lane);
+
+  // A^T[r][j] = k_r . q_j, B^T[r][j] = v_r . dO_j for row tiles R <= J (causal)
+  f32x4 at[4], bt[4];
+#pragma unroll
+  for (int R = 0; R < 4; R++) at[R] = bt[R] = zero4();
+#pragma unroll
+  for (int s = 0; s < KQ; s++)
+#pragma unroll
+    for (int R = 0; R < NR; R++) at[R] = mma(ld_row(sK, Lds::LDQ, 16 * R, 32 * s, lane), qf[s], at[R]);
+#pragma unroll
+  for (int s = 0; s < KV; s++)
+#pragma unroll
+    for (int R = 0; R < NR; R++) bt[R] = mma(ld_row(sV, Lds::LDV, 16 * R, 32 * s, lane), df[s], bt[R]);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (4 * g + i > L) at[J][i] = bt[J][i] = 0.f;
+  bf16x8 af[2], bfr[2];
+  af[0] = pack8(at[0], at[1]);
+  af[1] = pack8(at[2], at[3]);
+  bfr[0] = pack8(bt[0], bt[1]);
+  bfr[1] = pack8(bt[2], bt[3]);
+
+  // z^T[c][j] = E[j][c] (Wk[c].q_j + sum_r X[r][c] A^T[r][j]); ds^T likewise
+  f32x4 z[MT], ds[MT];
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) z[ct] = ds[ct] = zero4();
+#pragma unroll
+  for (int s = 0; s < KQ; s++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) z[ct] = mma(ld_row(sW, Lds::LDW, 16 * ct, 32 * s, lane), qf[s], z[ct]);
+#pragma unroll
+  for (int s = 0; s < KV; s++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+      ds[ct] = mma(ld_row(sW + DK, Lds::LDW, 16 * ct, 32 * s, lane), df[s], ds[ct]);
+#pragma unroll
+  for (int pr = 0; pr < NPR; pr++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const bf16x8 xa = ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane);
+      z[ct] = mma(xa, af[pr], z[ct]);
+      ds[ct] = mma(xa, bfr[pr], ds[ct]);
+    }
+  float e[MT][4];
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    const float4 ev = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 16 * ct + 4 * g);
+    e[ct][0] = ev.x; e[ct][1] = ev.y; e[ct][2] = ev.z; e[ct][3] = ev.w;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      z[ct][i] *= e[ct][i];
+      ds[ct][i] *= e[ct][i];
+    }
+  }
+
+  // the slot read of token j (over (ct, i) in-lane and the four lane groups)
+  f32x4 s[MT], dz[MT];
+  if constexpr (ACT == kActSoftmax) {
+    float mx = z[0][0];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, z[ct][i]);
+    mx = group4_max(mx);
+    float sm = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s[ct][i] = __builtin_amdgcn_exp2f((z[ct][i] - mx) * 1.4426950408889634f);
+        sm += s[ct][i];
+      }
+    const float inv = 1.f / group4_sum(sm);
+    float db = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s[ct][i] *= inv;
+        db += s[ct][i] * ds[ct][i];
+      }
+    db = group4_sum(db);
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) dz[ct][i] = s[ct][i] * (ds[ct][i] - db);
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s[ct][i] = slot_act<ACT>(z[ct][i]);
+        dz[ct][i] = slot_act_grad<ACT>(z[ct][i]) * ds[ct][i];
+      }
+  }
+  const bool valid = j < rv;
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    const int c = 16 * ct + 4 * g;
+    const float4 dd = *reinterpret_cast<const float4*>(sSeg + c);
+    const float d4[4] = {dd.x, dd.y, dd.z, dd.w};
+    float h[4], sed[4], dzed[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      h[i] = z[ct][i] * dz[ct][i] + s[ct][i] * ds[ct][i];
+      sed[i] = s[ct][i] * e[ct][i] * d4[i];
+      dzed[i] = dz[ct][i] * e[ct][i] * d4[i];
+    }
+    if (valid) {
+      store_bf16x4(s_rows + (size_t)j * M + c, s[ct][0], s[ct][1], s[ct][2], s[ct][3]);
+      store_bf16x4(dz_rows + (size_t)j * M + c, dz[ct][0], dz[ct][1], dz[ct][2], dz[ct][3]);
+      store_bf16x4(h_rows + (size_t)j * M + c, h[0], h[1], h[2], h[3]);
+    }
+    store_bf16x4(sS + j * Lds::LDX + c, sed[0], sed[1], sed[2], sed[3]);
+    store_bf16x4(sDZ + j * Lds::LDX + c, dzed[0], dzed[1], dzed[2], dzed[3]);
+  }
+  // (dz*E)^T as B operands over slot pairs (the permuted slot order of pass 2)
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const f32x4 a = {dz[2 * p][0] * e[2 * p][0], dz[2 * p][1] * e[2 * p][1], dz[2 * p][2] * e[2 * p][2],
+                     dz[2 * p][3] * e[2 * p][3]};
+    const f32x4 b = {dz[2 * p + 1][0] * e[2 * p + 1][0], dz[2 * p + 1][1] * e[2 * p + 1][1],
+                     dz[2 * p + 1][2] * e[2 * p + 1][2], dz[2 * p + 1][3] * e[2 * p + 1][3]};
+    dzb[p] = pack8(a, b);
+  }
+}
+
+// Pass waves, second half: dq^T[n][j] = sum_c Wk[c][n] (dz*E)[j][c] +
+// sum_{r<=j} K[r][n] A3^T[r][j], A3^T[r][j] = sum_c X[r][c] (dz*E)[j][c].
+template <int DK, int DV, int M, int J>
+__device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, const bf16x8 (&dzb)[M / 32],
+                                          bf16_t* __restrict__ dq_rows, int rv) {
+  using Lds = BwdLds<DK, DV, M>;
+  constexpr int NP = M / 32, NKT = DK / 16;
+  constexpr int NR = J + 1, NPR = J / 2 + 1;
+  const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
+  const bf16_t* sW = reinterpret_cast<const bf16_t*>(smem + Lds::oW);
+  const bf16_t* sX = reinterpret_cast<const bf16_t*>(smem + Lds::oX);
+  const int L = lane & 15, g = lane >> 4;
+  const int j = 16 * J + L;
+  f32x4 a3[4];
+#pragma unroll
+  for (int R = 0; R < 4; R++) a3[R] = zero4();
+#pragma unroll
+  for (int p = 0; p < NP; p++)
+#pragma unroll
+    for (int R = 0; R < NR; R++)
+      a3[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), dzb[p], a3[R]);
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (4 * g + i > L) a3[J][i] = 0.f;
+  bf16x8 a3f[2];
+  a3f[0] = pack8(a3[0], a3[1]);
+  a3f[1] = pack8(a3[2], a3[3]);
+  const bool store = j < rv;
+  constexpr int NG = NKT < 4 ? NKT : 4;
+#pragma unroll
+  for (int n0 = 0; n0 < NKT; n0 += NG) {
+    f32x4 acc[NG];
+#pragma unroll
+    for (int u = 0; u < NG; u++) acc[u] = zero4();
+#pragma unroll
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = mma(ld_col(sW, Lds::LDW, 16 * (n0 + u), 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), dzb[p],
+                     acc[u]);
+#pragma unroll
+    for (int pr = 0; pr < NPR; pr++)
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = mma(ld_col(sK, Lds::LDQ, 16 * (n0 + u), 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane),
+                     a3f[pr], acc[u]);
+    if (store) {
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
+                                    reinterpret_cast<u32x2*>(dq_rows + (size_t)j * DK + 16 * (n0 + u) + 4 * g));
+    }
+  }
+}
+
+// Exact forward-sweep chunk (some slot's decay product below the factorised
+// range): the state waves walk the tokens on the fp32 state in their
+// accumulators (Kt, Vt <- Diag(alpha)(.) + (1 - alpha)[k | v]^T, then the
+// reads) and add each token's dq; pass wave 0 takes the slot read of each
+// token and writes its reverse-map operand rows (s and dz times the decay
+// from the segment start through the token) into the operand tiles, which the
+// state waves then contract on the matrix cores as in the factorised path --
+// no division by a decay product anywhere.  log alpha of the chunk is in LDS
+// (over X, Z), the reductions over E.  Two workgroup barriers per token in
+// both halves (fwd_exact_state for the state waves, fwd_exact_pass for the
+// others).
+template <int DK, int DV, int M>
+__device__ __forceinline__ void fwd_exact_state(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
+                                                bf16_t* __restrict__ dq_rows, int lane, int sw) {
+  using Lds = BwdLds<DK, DV, M>;
+  using ST = StateTiles<DK, DV, M, 4>;
+  constexpr int MT = M / 16, NCW = ST::NCW;
+  const bf16_t* sQ = reinterpret_cast<const bf16_t*>(smem + Lds::oQ);
+  const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
+  const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Lds::oV);
+  const bf16_t* sDo = reinterpret_cast<const bf16_t*>(smem + Lds::oDo);
+  const float* sLa = reinterpret_cast<const float*>(smem + Lds::oX);
+  float* part = reinterpret_cast<float*>(smem + Lds::oE);  // [4][M] scores per state wave
+  const float* rDZ = part + 5 * M;                         // [M] dz of the token
+  const int L = lane & 15, g = lane >> 4;
+  const bool khalf = 16 * (sw * NCW) < DK;  // this wave holds Kt columns (else Vt)
+  for (int jt = 0; jt < rv; jt++) {
+    float a[MT], w[MT];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const float la = sLa[jt * M + 16 * ct + L];
+      a[ct] = __expf(la);
+      w[ct] = -expm1f(la);
+    }
+    float p[MT];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) p[ct] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NCW; n++) {
+      const int c0 = W.col(sw, n, lane);
+      const float4 kv = khalf ? ld_bf16x4(sK + jt * Lds::LDQ + c0) : ld_bf16x4(sV + jt * Lds::LDV + c0 - DK);
+      const float4 rd = khalf ? ld_bf16x4(sQ + jt * Lds::LDQ + c0) : ld_bf16x4(sDo + jt * Lds::LDV + c0 - DK);
+      const float k4[4] = {kv.x, kv.y, kv.z, kv.w}, q4[4] = {rd.x, rd.y, rd.z, rd.w};
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          W.st[n][ct][i] = a[ct] * W.st[n][ct][i] + w[ct] * k4[i];
+          p[ct] += W.st[n][ct][i] * q4[i];
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) p[ct] = group4_sum(p[ct]);
+    if (g == 0) {
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) part[sw * M + 16 * ct + L] = p[ct];
+    }
+    __syncthreads();  // the token's scores are in LDS
+    __syncthreads();  // its read weights are in LDS
+    if (khalf) {      // dq of token jt over this wave's Kt columns
+      float dz[MT];
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) dz[ct] = rDZ[16 * ct + L];
+#pragma unroll
+      for (int n = 0; n < NCW; n++) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          float acc = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < MT; ct++) acc += W.st[n][ct][i] * dz[ct];
+          x[i] = row_sum16(acc);
+        }
+        if (L == 0) store_bf16x4(dq_rows + (size_t)jt * DK + W.col(sw, n, lane), x[0], x[1], x[2], x[3]);
+      }
+    }
+  }
+}
+
+template <int DK, int DV, int M, int ACT>
+__device__ __forceinline__ void fwd_exact_pass(int rv, unsigned char* smem, const float* sSeg,
+                                               bf16_t* __restrict__ s_rows, bf16_t* __restrict__ dz_rows,
+                                               bf16_t* __restrict__ h_rows, int lane, int wv) {
+  using Lds = BwdLds<DK, DV, M>;
+  const float* sLa = reinterpret_cast<const float*>(smem + Lds::oX);
+  const float* part = reinterpret_cast<const float*>(smem + Lds::oE);
+  float* rDZ = reinterpret_cast<float*>(smem + Lds::oE) + 5 * M;
+  bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
+  bf16_t* sDZ = reinterpret_cast<bf16_t*>(smem + Lds::oDZ);
+  const int tid = wv * 64 + lane;
+  // operand rows past the end stay zero (the contraction runs over all C rows)
+  for (int e = rv * M + tid; e < C * M; e += 4 * 64) {
+    sS[(e / M) * Lds::LDX + e % M] = 0;
+    sDZ[(e / M) * Lds::LDX + e % M] = 0;
+  }
+  const bool on = wv == 0 && lane < M;
+  float eseg = on ? sSeg[lane] : 0.f;  // decay from the segment start through the token
+  for (int jt = 0; jt < rv; jt++) {
+    __syncthreads();  // the token's scores are in LDS
+    if (wv == 0) {    // the read of token jt: slot = lane
+      const float z = on ? part[lane] + part[M + lane] : 0.f;
+      const float ds = on ? part[2 * M + lane] + part[3 * M + lane] : 0.f;
+      float s, dz;
+      if constexpr (ACT == kActSoftmax) {
+        const float mx = wave_max(on ? z : -INFINITY);
+        const float e = on ? __expf(z - mx) : 0.f;
+        s = e / sum64(e);
+        const float db = sum64(s * ds);
+        dz = s * (ds - db);
+      } else {
+        s = slot_act<ACT>(z);
+        dz = slot_act_grad<ACT>(z) * ds;
+      }
+      if (on) {
+        eseg *= __expf(sLa[jt * M + lane]);
+        rDZ[lane] = dz;
+        s_rows[(size_t)jt * M + lane] = f2bf(s);
+        dz_rows[(size_t)jt * M + lane] = f2bf(dz);
+        h_rows[(size_t)jt * M + lane] = f2bf(z * dz + s * ds);
+        sS[jt * Lds::LDX + lane] = f2bf(s * eseg);
+        sDZ[jt * Lds::LDX + lane] = f2bf(dz * eseg);
+      }
+    }
+    __syncthreads();  // its read weights are in LDS
+  }
+}
+
+// One workgroup per (segment, unit).  The state waves and the pass waves run
+// separate loops (so that neither holds the other's registers) with the same
+// sequence of workgroup barriers: A (chunk staged), M (reverse-map operands
+// written), B (chunk done); an exact chunk replaces M by its per-token ones.
+template <int DK, int DV, int M, int ACT>
+__global__ void __launch_bounds__(NT, 1)
+bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
+             const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, float* __restrict__ st,
+             float* __restrict__ rm, float* __restrict__ rdec, bf16_t* __restrict__ dq,
+             bf16_t* __restrict__ s_ws, bf16_t* __restrict__ dz_ws, bf16_t* __restrict__ h_ws, int T, int S,
+             int P, float inv_tau) {
+  using Lds = BwdLds<DK, DV, M>;
+  using ST = StateTiles<DK, DV, M, 4>;
+  constexpr int GPW = M / NW;
+  constexpr int NP = M / 32;
+  constexpr size_t NE = (size_t)M * (DK + DV);
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + Lds::oQ);
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem + Lds::oK);
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Lds::oV);
+  bf16_t* sDo = reinterpret_cast<bf16_t*>(smem + Lds::oDo);
+  bf16_t* sW = reinterpret_cast<bf16_t*>(smem + Lds::oW);
+  bf16_t* sX = reinterpret_cast<bf16_t*>(smem + Lds::oX);
+  bf16_t* sZ = reinterpret_cast<bf16_t*>(smem + Lds::oZ);
+  float* sE = reinterpret_cast<float*>(smem + Lds::oE);
+  bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
+  bf16_t* sDZ = reinterpret_cast<bf16_t*>(smem + Lds::oDZ);
+  float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
+  float* sSeg = reinterpret_cast<float*>(smem + Lds::oAux);
+  float* sLa = reinterpret_cast<float*>(smem + Lds::oX);
+  int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool is_state = wv >= 4;
+  const int sw = wv - 4;
+  const int slot0 = wv * GPW;
+  const int seg = blockIdx.x % P, unit = blockIdx.x / P;
+  const int nchunks = (T + C - 1) / C;
+  const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
+  const size_t ub = (size_t)unit * T;
+  const bf16_t* qb = qq + ub * DK;
+  const bf16_t* kb = kk + ub * DK;
+  const bf16_t* vb = vv + ub * DV;
+  const bf16_t* db = dOo + ub * DV;
+  const bf16_t* gb = gg + ub * M + slot0;
+  float* stp = st + ((size_t)unit * P + seg) * NE;
+  float* rmp = rm + ((size_t)unit * P + seg) * NE;
+  auto rows_of = [&](int ch) { return min(C, T - ch * C); };
+
+  typedef GateRow<GPW> Row;
+  Row gr;
+  // the chunk tiles go through the pass waves' registers only (threads 0 .. 255)
+  TileN<DK, 256> pq, pk;
+  TileN<DV, 256> pv, pd;
+  auto load_tiles = [&](int ch, int tid_) {
+    const int t0 = ch * C, rv = rows_of(ch);
+    pq.load(qb + (size_t)t0 * DK, rv, tid_);
+    pk.load(kb + (size_t)t0 * DK, rv, tid_);
+    pv.load(vb + (size_t)t0 * DV, rv, tid_);
+    pd.load(db + (size_t)t0 * DV, rv, tid_);
+  };
+  auto load_gates = [&](int ch, int lane_) {
+    gr.load(gb + (size_t)(ch * C + min(lane_, rows_of(ch) - 1)) * M);
+  };
+  // stage chunk ch (the pass waves its tiles, every wave its factors),
+  // barrier A, log alpha for an exact chunk, the loads of the next chunk
+  // (this one again at the end); returns whether ch is exact
+  auto stage = [&](auto pass, int ch, int it, int lane_, int tid_) -> bool {
+    const int rv = rows_of(ch);
+    if constexpr (decltype(pass)::value) {
+      pq.store(sQ, Lds::LDQ, rv, tid_);
+      pk.store(sK, Lds::LDQ, rv, tid_);
+      pv.store(sV, Lds::LDV, rv, tid_);
+      pd.store(sDo, Lds::LDV, rv, tid_);
+    }
+    gr.pin();
+    float E[GPW];
+    const bool small =
+        bwd_factors<GPW, Lds::LDX, Lds::LDE>(gr, lane_ < rv, inv_tau, lane_, slot0, sX, sZ, sE, sDec, E);
+    const bool slow = block_any(small, sFlag, it, lane_, wv);
+    if (slow) {  // every factor reader is past barrier A
+      float la[GPW];
+      log_alpha_row<GPW>(gr, lane_ < rv, inv_tau, la);
+      store_f32_row<GPW>(sLa + lane_ * M + slot0, la);
+    }
+    const int cn = min(ch + 1, c_end - 1);
+    load_gates(cn, lane_);
+    if constexpr (decltype(pass)::value) load_tiles(cn, tid_);
+    return slow;
+  };
+  using Pass = std::integral_constant<bool, true>;
+  using State = std::integral_constant<bool, false>;
+
+  load_gates(c_begin, lane);
+  if (tid < M) sSeg[tid] = 1.f;
+  if (is_state) {
+    ST W, R;
+    W.load_w(stp, sw, lane);
+    R.zero();
+    for (int ch = c_begin; ch < c_end; ch++) {
+      int lane_i = lane, tid_i = tid;
+      asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+      const int rv = rows_of(ch);
+      W.store_copy(sW, Lds::LDW, sw, lane_i);  // the chunk's start state for the pass waves
+      const bool slow = stage(State{}, ch, ch - c_begin, lane_i, tid_i);
+      if (!slow) {
+        W.carry(sK, Lds::LDQ, sV, Lds::LDV, sZ, Lds::LDX, sDec, sw, lane_i);
+        __syncthreads();  // M: the reverse-map operands are in LDS
+      } else {
+        __syncthreads();  // log alpha is in LDS
+        fwd_exact_state<DK, DV, M>(W, rv, smem, dq + (ub + ch * C) * DK, lane_i, sw);
+      }
+      // the chunk's reverse map (operand rows from the passes or the walk)
+      R.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, nullptr, sw, lane_i);
+      __syncthreads();  // B: every reader of this chunk's tiles, factors and copies is done
+    }
+    // the segment's end state over its start state (only this workgroup reads
+    // that slot), its reverse map beside it
+    W.store_w(stp, sw, lane);
+    R.store_w(rmp, sw, lane);
+  } else {
+    load_tiles(c_begin, tid);
+    bf16x8 dzb[NP];
+    for (int ch = c_begin; ch < c_end; ch++) {
+      int lane_i = lane, tid_i = tid;
+      asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+      const int t0 = ch * C, rv = rows_of(ch);
+      const bool slow = stage(Pass{}, ch, ch - c_begin, lane_i, tid_i);
+      bf16_t* srow = s_ws + (ub + t0) * M;
+      bf16_t* dzrow = dz_ws + (ub + t0) * M;
+      bf16_t* hrow = h_ws + (ub + t0) * M;
+      if (!slow) {
+        switch (wv) {
+          case 0: fwd_pass1<DK, DV, M, 0, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
+          case 1: fwd_pass1<DK, DV, M, 1, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
+          case 2: fwd_pass1<DK, DV, M, 2, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
+          default: fwd_pass1<DK, DV, M, 3, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
+        }
+        __syncthreads();  // M
+        // the decay from the segment start, advanced past this chunk (its
+        // readers are all before M; E_C is rewritten only after B)
+        if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];
+        bf16_t* dqrow = dq + (ub + t0) * DK;
+        switch (wv) {
+          case 0: fwd_pass2<DK, DV, M, 0>(lane_i, smem, dzb, dqrow, rv); break;
+          case 1: fwd_pass2<DK, DV, M, 1>(lane_i, smem, dzb, dqrow, rv); break;
+          case 2: fwd_pass2<DK, DV, M, 2>(lane_i, smem, dzb, dqrow, rv); break;
+          default: fwd_pass2<DK, DV, M, 3>(lane_i, smem, dzb, dqrow, rv); break;
+        }
+      } else {
+        __syncthreads();  // log alpha is in LDS
+        fwd_exact_pass<DK, DV, M, ACT>(rv, smem, sSeg, srow, dzrow, hrow, lane_i, wv);
+        if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];  // read by the walk before its first barrier
+      }
+      __syncthreads();  // B
+    }
+  }
+  __syncthreads();
+  if (tid < M) rdec[((size_t)unit * P + seg) * M + tid] = sSeg[tid];
+}
+
+// ======================================================== reverse scan
+// One thread per (unit, four consecutive elements of a slot row), serial
+// over the segments from the last: slot p of rm holds segment p's reverse map
+// on entry and on exit the adjoint of the state at segment p's end (from the
+// tokens after it and the final-state gradients dkf / dvf, nullable = zero);
+// what is carried out of segment 0 is the gradient of the initial states.
+template <int DK, int DV, int M>
+__global__ void __launch_bounds__(256)
+bwd_bf16_rscan(float* __restrict__ rm, const float* __restrict__ rdec, const float* __restrict__ dkf,
+               const float* __restrict__ dvf, float* __restrict__ dk0, float* __restrict__ dv0, int units,
+               int P) {
+  constexpr int NE = M * (DK + DV), BATCH = 8;
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)units * (NE / 4)) return;
+  const int unit = (int)(gid / (NE / 4)), e = 4 * (int)(gid % (NE / 4));
+  const int c = e / (DK + DV), cl = e % (DK + DV);
+  const size_t ko = ((size_t)unit * M + c) * DK + cl, vo = ((size_t)unit * M + c) * DV + cl - DK;
+  f32x4 W = zero4();
+  if (cl < DK) {
+    if (dkf) W = *reinterpret_cast<const f32x4*>(dkf + ko);
+  } else {
+    if (dvf) W = *reinterpret_cast<const f32x4*>(dvf + vo);
+  }
+  f32x4* sl = reinterpret_cast<f32x4*>(rm + (size_t)unit * P * NE + e);
+  const float* dc = rdec + (size_t)unit * P * M + c;
+  for (int n0 = 0; n0 < P; n0 += BATCH) {
+    f32x4 x[BATCH];
+    float d[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+      if (n0 + i < P) {
+        const int p = P - 1 - (n0 + i);
+        x[i] = sl[(size_t)p * (NE / 4)];
+        d[i] = dc[(size_t)p * M];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+      if (n0 + i < P) {
+        const int p = P - 1 - (n0 + i);
+        sl[(size_t)p * (NE / 4)] = W;
+        W = d[i] * W + x[i];
+      }
+    }
+  }
+  if (cl < DK) {
+    if (dk0) *reinterpret_cast<f32x4*>(dk0 + ko) = W;
+  } else {
+    if (dv0) *reinterpret_cast<f32x4*>(dv0 + vo) = W;
+  }
+}
+
+// ======================================================== reverse sweep
+// Pass waves: write-token rows j = 16J .. 16J+15 of the chunk, from the bf16
+// copy of the adjoint at the chunk end.  dk and dv rows are written; di and
+// the gate terms give each (token, slot) its part of d log alpha: the sum
+// over the wave's rows from j on (pre), the wave's total per slot (sWt[J]).
+// The rest (later waves' totals and the carry from later chunks) is added
+// after the next barrier by rev_pass_finish.
+template <int DK, int DV, int M, int J>
+__device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, float* sWt,
+                                         const bf16_t* __restrict__ h_rows, const bf16_t* __restrict__ g_rows,
+                                         bf16_t* __restrict__ dk_rows, bf16_t* __restrict__ dv_rows, int rv,
+                                         float inv_tau, float (&pre)[M / 16][4], float (&sn)[M / 16][4]) {
+  using Lds = BwdLds<DK, DV, M>;
+  constexpr int MT = M / 16, KQ = DK / 32, KV = DV / 32, NP = M / 32, NKT = DK / 16, NVT = DV / 16;
+  constexpr int PR0 = J / 2;  // first read-row tile pair at or after this wave's rows
+  const bf16_t* sQ = reinterpret_cast<const bf16_t*>(smem + Lds::oQ);
+  const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
+  const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Lds::oV);
+  const bf16_t* sDo = reinterpret_cast<const bf16_t*>(smem + Lds::oDo);
+  const bf16_t* sW = reinterpret_cast<const bf16_t*>(smem + Lds::oW);
+  const bf16_t* sX = reinterpret_cast<const bf16_t*>(smem + Lds::oX);
+  const bf16_t* sZ = reinterpret_cast<const bf16_t*>(smem + Lds::oZ);
+  const float* sE = reinterpret_cast<const float*>(smem + Lds::oE);
+  const bf16_t* sS = reinterpret_cast<const bf16_t*>(smem + Lds::oS);
+  const bf16_t* sDZ = reinterpret_cast<const bf16_t*>(smem + Lds::oDZ);
+  const float* sDec = reinterpret_cast<const float*>(smem + Lds::oDec);
+  const int L = lane & 15, g = lane >> 4;
+  const int j = 16 * J + L;
+  const bool valid = j < rv;
+  const int jr = valid ? j : rv - 1;  // rows past the end read the last valid row (masked below)
+
+  // this lane's h and gate logits (token j, slots 16ct + 4g + 0..3), issued first
+  float4 hv[MT], gv[MT];
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    hv[ct] = ld_bf16x4(h_rows + (size_t)jr * M + 16 * ct + 4 * g);
+    gv[ct] = ld_bf16x4(g_rows + (size_t)jr * M + 16 * ct + 4 * g);
+  }
+
+  bf16x8 kf[KQ], vf[KV];
+#pragma unroll
+  for (int s = 0; s < KQ; s++) kf[s] = ld_row(sK, Lds::LDQ, 16 * J, 32 * s, lane);
+#pragma unroll
+  for (int s = 0; s < KV; s++) vf[s] = ld_row(sV, Lds::LDV, 16 * J, 32 * s, lane);
+
+  // S1[t'][j] = q_t' . k_j, S2[t'][j] = dO_t' . v_j for read rows t' >= j
+  f32x4 s1[4], s2[4];
+#pragma unroll
+  for (int T = 0; T < 4; T++) s1[T] = s2[T] = zero4();
+#pragma unroll
+  for (int s = 0; s < KQ; s++)
+#pragma unroll
+    for (int T = J; T < 4; T++) s1[T] = mma(ld_row(sQ, Lds::LDQ, 16 * T, 32 * s, lane), kf[s], s1[T]);
+#pragma unroll
+  for (int s = 0; s < KV; s++)
+#pragma unroll
+    for (int T = J; T < 4; T++) s2[T] = mma(ld_row(sDo, Lds::LDV, 16 * T, 32 * s, lane), vf[s], s2[T]);
+  // A_dq[t'][j] = sum_c dzE[t'][c] X[j][c], A2[t'][j] = sum_c sE[t'][c] X[j][c]
+  bf16x8 xb[NP];
+#pragma unroll
+  for (int p = 0; p < NP; p++) xb[p] = ld_row2(sX, Lds::LDX, 16 * J, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane);
+  f32x4 ad[4], a2[4];
+#pragma unroll
+  for (int T = 0; T < 4; T++) ad[T] = a2[T] = zero4();
+#pragma unroll
+  for (int p = 0; p < NP; p++)
+#pragma unroll
+    for (int T = J; T < 4; T++) {
+      ad[T] = mma(ld_row2(sDZ, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], ad[T]);
+      a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], a2[T]);
+    }
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    if (4 * g + i < L) s1[J][i] = s2[J][i] = ad[J][i] = a2[J][i] = 0.f;  // causal: t' >= j
+  bf16x8 s1f[2], s2f[2], adf[2], a2f[2];
+#pragma unroll
+  for (int pr = 0; pr < 2; pr++) {
+    s1f[pr] = pack8(s1[2 * pr], s1[2 * pr + 1]);
+    s2f[pr] = pack8(s2[2 * pr], s2[2 * pr + 1]);
+    adf[pr] = pack8(ad[2 * pr], ad[2 * pr + 1]);
+    a2f[pr] = pack8(a2[2 * pr], a2[2 * pr + 1]);
+  }
+
+  // dk^T[n][j] = sum_c dWk[c][n] Z[j][c] + sum_t' Q[t'][n] A_dq[t'][j]; dv^T likewise
+  bf16x8 zb[NP];
+#pragma unroll
+  for (int p = 0; p < NP; p++) zb[p] = ld_row2(sZ, Lds::LDX, 16 * J, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane);
+  constexpr int NG = 4;
+  static_assert(NKT % NG == 0 && NVT % NG == 0, "column groups");
+#pragma unroll
+  for (int n0 = 0; n0 < NKT + NVT; n0 += NG) {
+    const bool kpart = n0 < NKT;
+    const int nb = kpart ? n0 : n0 - NKT;
+    f32x4 acc[NG];
+#pragma unroll
+    for (int u = 0; u < NG; u++) acc[u] = zero4();
+#pragma unroll
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = mma(ld_col(sW + (kpart ? 0 : DK), Lds::LDW, 16 * (nb + u), 32 * p + 4 * g, 32 * p + 16 + 4 * g,
+                            lane),
+                     zb[p], acc[u]);
+#pragma unroll
+    for (int pr = PR0; pr < 2; pr++)
+#pragma unroll
+      for (int u = 0; u < NG; u++)
+        acc[u] = kpart ? mma(ld_col(sQ, Lds::LDQ, 16 * (nb + u), 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane),
+                             adf[pr], acc[u])
+                       : mma(ld_col(sDo, Lds::LDV, 16 * (nb + u), 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane),
+                             a2f[pr], acc[u]);
+    if (valid) {
+#pragma unroll
+      for (int u = 0; u < NG; u++) {
+        bf16_t* dst = kpart ? dk_rows + (size_t)j * DK : dv_rows + (size_t)j * DV;
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
+                                    reinterpret_cast<u32x2*>(dst + 16 * (nb + u) + 4 * g));
+      }
+    }
+  }
+
+  // di^T[c][j] = (E_C[c] sum_n dW[c][n] [k|v]_j[n] + sum_t' (dzE[t'][c] S1[t'][j] +
+  // sE[t'][c] S2[t'][j])) / E[j][c]
+  f32x4 di[MT];
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) di[ct] = zero4();
+#pragma unroll
+  for (int s = 0; s < KQ; s++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) di[ct] = mma(ld_row(sW, Lds::LDW, 16 * ct, 32 * s, lane), kf[s], di[ct]);
+#pragma unroll
+  for (int s = 0; s < KV; s++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+      di[ct] = mma(ld_row(sW + DK, Lds::LDW, 16 * ct, 32 * s, lane), vf[s], di[ct]);
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    const float4 d = *reinterpret_cast<const float4*>(sDec + 16 * ct + 4 * g);
+    di[ct][0] *= d.x;
+    di[ct][1] *= d.y;
+    di[ct][2] *= d.z;
+    di[ct][3] *= d.w;
+  }
+#pragma unroll
+  for (int pr = PR0; pr < 2; pr++)
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      di[ct] = mma(ld_col(sDZ, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s1f[pr], di[ct]);
+      di[ct] = mma(ld_col(sS, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s2f[pr], di[ct]);
+    }
+
+  // gate: u = h - (1 - alpha) di; sums over the wave's rows from j on (DPP
+  // row shifts towards lower lanes), pre = that sum - alpha di
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    const float4 e = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 16 * ct + 4 * g);
+    const float ev[4] = {e.x, e.y, e.z, e.w};
+    const float hh[4] = {hv[ct].x, hv[ct].y, hv[ct].z, hv[ct].w};
+    const float gl[4] = {gv[ct].x, gv[ct].y, gv[ct].z, gv[ct].w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float d = di[ct][i] * __builtin_amdgcn_rcpf(ev[i]);
+      float a, w;
+      gate_terms(gl[i], inv_tau, a, w, sn[ct][i]);
+      float x = valid ? hh[i] - w * d : 0.f;
+      x += dpp_zero<0x101, 0xf>(x);  // row_shl:1
+      x += dpp_zero<0x102, 0xf>(x);  // row_shl:2
+      x += dpp_zero<0x104, 0xf>(x);  // row_shl:4
+      x += dpp_zero<0x108, 0xf>(x);  // row_shl:8
+      pre[ct][i] = x - a * d;
+      if (L == 0) sWt[J * M + 16 * ct + 4 * g + i] = x;
+    }
+  }
+}
+
+// After the barrier that publishes every wave's totals: d log alpha = pre +
+// the totals of the later waves of this chunk + the carry from later chunks;
+// dg = that * sigmoid(-g) / tau.
+template <int M, int J>
+__device__ __forceinline__ void rev_pass_finish(int lane, const float* sWt, const float* carry,
+                                                bf16_t* __restrict__ dg_rows, int rv,
+                                                const float (&pre)[M / 16][4], const float (&sn)[M / 16][4]) {
+  constexpr int MT = M / 16;
+  const int L = lane & 15, g = lane >> 4, j = 16 * J + L;
+#pragma unroll
+  for (int ct = 0; ct < MT; ct++) {
+    const int c = 16 * ct + 4 * g;
+    float4 add = *reinterpret_cast<const float4*>(carry + c);
+#pragma unroll
+    for (int J2 = J + 1; J2 < 4; J2++) {
+      const float4 t = *reinterpret_cast<const float4*>(sWt + J2 * M + c);
+      add.x += t.x; add.y += t.y; add.z += t.z; add.w += t.w;
+    }
+    if (j < rv)
+      store_bf16x4(dg_rows + (size_t)j * M + c, (pre[ct][0] + add.x) * sn[ct][0], (pre[ct][1] + add.y) * sn[ct][1],
+                   (pre[ct][2] + add.z) * sn[ct][2], (pre[ct][3] + add.w) * sn[ct][3]);
+  }
+}
+
+// Exact reverse-sweep chunk: the state waves walk the tokens backwards on the
+// fp32 adjoint in their accumulators (dW += [dz q^T | s dO^T] of the token,
+// dk, dv and di from it, then dW *= alpha), pass wave 0 forms each token's
+// gate gradient; s, dz and h come unscaled from the per-token workspace.  On
+// return the state waves' accumulators hold the adjoint at the chunk start
+// and sWt[0] the chunk's total of the gate terms (sWt[1..3] = 0).  One
+// workgroup barrier per token in both halves.
+template <int DK, int DV, int M>
+__device__ __forceinline__ void rev_exact_state(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
+                                                const bf16_t* __restrict__ s_rows,
+                                                const bf16_t* __restrict__ dz_rows, bf16_t* __restrict__ dk_rows,
+                                                bf16_t* __restrict__ dv_rows, int lane, int sw) {
+  using Lds = BwdLds<DK, DV, M>;
+  using ST = StateTiles<DK, DV, M, 4>;
+  constexpr int MT = M / 16, NCW = ST::NCW;
+  const bf16_t* sQ = reinterpret_cast<const bf16_t*>(smem + Lds::oQ);
+  const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
+  const bf16_t* sV = reinterpret_cast<const bf16_t*>(smem + Lds::oV);
+  const bf16_t* sDo = reinterpret_cast<const bf16_t*>(smem + Lds::oDo);
+  const float* sLa = reinterpret_cast<const float*>(smem + Lds::oX);
+  float* dpart = reinterpret_cast<float*>(smem + Lds::oS);  // [2][4][M]: di partials per state wave
+  const int L = lane & 15, g = lane >> 4;
+  const bool khalf = 16 * (sw * NCW) < DK;
+  for (int jt = rv - 1, n = 0; jt >= 0; jt--, n++) {
+    float* dp = dpart + (n & 1) * 4 * M;
+    float a[MT], w[MT], rd[MT];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const float la = sLa[jt * M + 16 * ct + L];
+      a[ct] = __expf(la);
+      w[ct] = -expm1f(la);
+      rd[ct] = bf2f(khalf ? dz_rows[(size_t)jt * M + 16 * ct + L] : s_rows[(size_t)jt * M + 16 * ct + L]);
+    }
+    float p[MT];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) p[ct] = 0.f;
+#pragma unroll
+    for (int n2 = 0; n2 < NCW; n2++) {
+      const int c0 = W.col(sw, n2, lane);
+      const float4 kv = khalf ? ld_bf16x4(sK + jt * Lds::LDQ + c0) : ld_bf16x4(sV + jt * Lds::LDV + c0 - DK);
+      const float4 qv = khalf ? ld_bf16x4(sQ + jt * Lds::LDQ + c0) : ld_bf16x4(sDo + jt * Lds::LDV + c0 - DK);
+      const float k4[4] = {kv.x, kv.y, kv.z, kv.w}, q4[4] = {qv.x, qv.y, qv.z, qv.w};
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) {
+          W.st[n2][ct][i] += rd[ct] * q4[i];
+          acc += w[ct] * W.st[n2][ct][i];
+          p[ct] += W.st[n2][ct][i] * k4[i];
+        }
+        x[i] = row_sum16(acc);
+      }
+      if (L == 0) {
+        bf16_t* dst = khalf ? dk_rows + (size_t)jt * DK + c0 : dv_rows + (size_t)jt * DV + c0 - DK;
+        store_bf16x4(dst, x[0], x[1], x[2], x[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) W.st[n2][ct][i] *= a[ct];
+    }
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) p[ct] = group4_sum(p[ct]);
+    if (g == 0) {
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) dp[sw * M + 16 * ct + L] = p[ct];
+    }
+    __syncthreads();  // the token's di partials are in LDS
+  }
+}
+
+template <int M>
+__device__ __forceinline__ void rev_exact_pass(int rv, const unsigned char* smem, int oS, const float* carry,
+                                               float* sWt, const bf16_t* __restrict__ h_rows,
+                                               const bf16_t* __restrict__ g_rows, bf16_t* __restrict__ dg_rows,
+                                               float inv_tau, int lane, int wv) {
+  const float* dpart = reinterpret_cast<const float*>(smem + oS);
+  float run = 0.f;  // wave 0: the sum of the gate terms of the chunk's tokens from jt on
+  for (int jt = rv - 1, n = 0; jt >= 0; jt--, n++) {
+    __syncthreads();  // the token's di partials are in LDS
+    if (wv == 0 && lane < M) {
+      const float* dp = dpart + (n & 1) * 4 * M;
+      const float d = dp[lane] + dp[M + lane] + dp[2 * M + lane] + dp[3 * M + lane];
+      float a, w, sn;
+      gate_terms(bf2f(g_rows[(size_t)jt * M + lane]), inv_tau, a, w, sn);
+      run += bf2f(h_rows[(size_t)jt * M + lane]) - w * d;
+      dg_rows[(size_t)jt * M + lane] = f2bf((run + carry[lane] - a * d) * sn);
+    }
+  }
+  if (wv == 0 && lane < M) {
+    sWt[lane] = run;
+    sWt[M + lane] = sWt[2 * M + lane] = sWt[3 * M + lane] = 0.f;
+  }
+}
+
+// One workgroup per (segment, unit), chunks from the segment's end.  As in the
+// forward sweep the two roles run separate loops with the same barriers: A
+// (chunk staged), B (chunk done, its gate totals published); an exact chunk
+// adds one barrier per token.
+template <int DK, int DV, int M>
+__global__ void __launch_bounds__(NT, 1)
+bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
+             const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, const float* __restrict__ st,
+             const float* __restrict__ rm, const bf16_t* __restrict__ s_ws, const bf16_t* __restrict__ dz_ws,
+             const bf16_t* __restrict__ h_ws, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+             bf16_t* __restrict__ dg, int T, int S, int P, float inv_tau) {
+  using Lds = BwdLds<DK, DV, M>;
+  using ST = StateTiles<DK, DV, M, 4>;
+  constexpr int GPW = M / NW;
+  constexpr int MT = M / 16;
+  constexpr size_t NE = (size_t)M * (DK + DV);
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + Lds::oQ);
+  bf16_t* sK = reinterpret_cast<bf16_t*>(smem + Lds::oK);
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem + Lds::oV);
+  bf16_t* sDo = reinterpret_cast<bf16_t*>(smem + Lds::oDo);
+  bf16_t* sW = reinterpret_cast<bf16_t*>(smem + Lds::oW);
+  bf16_t* sX = reinterpret_cast<bf16_t*>(smem + Lds::oX);
+  bf16_t* sZ = reinterpret_cast<bf16_t*>(smem + Lds::oZ);
+  float* sE = reinterpret_cast<float*>(smem + Lds::oE);
+  bf16_t* sS = reinterpret_cast<bf16_t*>(smem + Lds::oS);
+  bf16_t* sDZ = reinterpret_cast<bf16_t*>(smem + Lds::oDZ);
+  float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
+  float* sCarry = reinterpret_cast<float*>(smem + Lds::oAux);  // [2][M]
+  float* sWt = reinterpret_cast<float*>(smem + Lds::oWt);      // [4][M]
+  float* sLa = reinterpret_cast<float*>(smem + Lds::oX);
+  int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool is_state = wv >= 4;
+  const int sw = wv - 4;
+  const int slot0 = wv * GPW;
+  const int seg = blockIdx.x % P, unit = blockIdx.x / P;
+  const int nchunks = (T + C - 1) / C;
+  const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
+  const size_t ub = (size_t)unit * T;
+  const bf16_t* qb = qq + ub * DK;
+  const bf16_t* kb = kk + ub * DK;
+  const bf16_t* vb = vv + ub * DV;
+  const bf16_t* db = dOo + ub * DV;
+  auto rows_of = [&](int ch) { return min(C, T - ch * C); };
+
+  typedef GateRow<GPW> Row;
+  Row gr, sr, zr;  // gate logits, s and dz of token row = lane, this wave's slots
+  Tile<DK> pq, pk;
+  Tile<DV> pv, pd;
+  auto load_chunk = [&](int ch, int lane_, int tid_) {
+    const int t0 = ch * C, rv = rows_of(ch);
+    pq.load(qb + (size_t)t0 * DK, rv, tid_);
+    pk.load(kb + (size_t)t0 * DK, rv, tid_);
+    pv.load(vb + (size_t)t0 * DV, rv, tid_);
+    pd.load(db + (size_t)t0 * DV, rv, tid_);
+    const size_t r = (ub + t0 + min(lane_, rv - 1)) * M + slot0;
+    gr.load(gg + r);
+    sr.load(s_ws + r);
+    zr.load(dz_ws + r);
+  };
+  // stage chunk ch: tiles, factors, s*E and dz*E (zero past the end); barrier
+  // A; log alpha for an exact chunk; the loads of the chunk before
+  auto stage = [&](int ch, int it, int lane_, int tid_) -> bool {
+    const int rv = rows_of(ch);
+    pq.store(sQ, Lds::LDQ, rv, tid_);
+    pk.store(sK, Lds::LDQ, rv, tid_);
+    pv.store(sV, Lds::LDV, rv, tid_);
+    pd.store(sDo, Lds::LDV, rv, tid_);
+    gr.pin();
+    sr.pin();
+    zr.pin();
+    float E[GPW];
+    const bool ok = lane_ < rv;
+    const bool small = bwd_factors<GPW, Lds::LDX, Lds::LDE>(gr, ok, inv_tau, lane_, slot0, sX, sZ, sE, sDec, E);
+    float se[GPW], ze[GPW];
+#pragma unroll
+    for (int s = 0; s < GPW; s++) {
+      se[s] = ok ? sr.at(s) * E[s] : 0.f;
+      ze[s] = ok ? zr.at(s) * E[s] : 0.f;
+    }
+    store_bf16_row<GPW>(sS + lane_ * Lds::LDX + slot0, se);
+    store_bf16_row<GPW>(sDZ + lane_ * Lds::LDX + slot0, ze);
+    const bool slow = block_any(small, sFlag, it, lane_, wv);
+    if (slow) {
+      float la[GPW];
+      log_alpha_row<GPW>(gr, ok, inv_tau, la);
+      store_f32_row<GPW>(sLa + lane_ * M + slot0, la);
+    }
+    load_chunk(max(ch - 1, c_begin), lane_, tid_);  // the chunk before (this one again at the end)
+    return slow;
+  };
+
+  load_chunk(c_end - 1, lane, tid);
+  if (is_state) {
+    ST W;  // the adjoint of the state at the end of the current chunk
+    {
+      // carry from the tokens after this segment: <dW_end, W_end> per slot
+      const size_t o = ((size_t)unit * P + seg) * NE;
+      W.load_w(rm + o, sw, lane);
+      typename ST::MapRegs we;
+      W.load_map(we, st + o, sw, lane);
+      float p[MT];
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        p[ct] = 0.f;
+#pragma unroll
+        for (int n = 0; n < ST::NCW; n++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) p[ct] += W.st[n][ct][i] * we[n][ct][i];
+        p[ct] = group4_sum(p[ct]);
+      }
+      if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) sWt[sw * M + 16 * ct + (lane & 15)] = p[ct];
+      }
+    }
+    __syncthreads();  // the carry's partial dots
+    if (sw == 0 && lane < M) sCarry[lane] = sWt[lane] + sWt[M + lane] + sWt[2 * M + lane] + sWt[3 * M + lane];
+    for (int ch = c_end - 1, it = 0; ch >= c_begin; ch--, it++) {
+      int lane_i = lane, tid_i = tid;
+      asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+      const int t0 = ch * C, rv = rows_of(ch);
+      W.store_copy(sW, Lds::LDW, sw, lane_i);  // the adjoint at the chunk end, for the pass waves
+      const bool slow = stage(ch, it, lane_i, tid_i);
+      if (!slow) {
+        // the adjoint at the chunk start: Diag(E_C) dW + [Q | dO]^T [dz*E | s*E]
+        W.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sw, lane_i);
+      } else {
+        __syncthreads();  // log alpha is in LDS
+        rev_exact_state<DK, DV, M>(W, rv, smem, s_ws + (ub + t0) * M, dz_ws + (ub + t0) * M,
+                                   dk + (ub + t0) * DK, dv + (ub + t0) * DV, lane_i, sw);
+      }
+      __syncthreads();  // B
+      if (sw == 0 && lane_i < M) {  // the carry into the chunk before
+        const float* carry = sCarry + (it & 1) * M;
+        sCarry[((it + 1) & 1) * M + lane_i] = carry[lane_i] + sWt[lane_i] + sWt[M + lane_i] +
+                                              sWt[2 * M + lane_i] + sWt[3 * M + lane_i];
+      }
+    }
+  } else {
+    __syncthreads();  // the carry's partial dots
+    float pre[MT][4], sn[MT][4];
+    for (int ch = c_end - 1, it = 0; ch >= c_begin; ch--, it++) {
+      int lane_i = lane, tid_i = tid;
+      asm volatile("" : "+v"(lane_i), "+v"(tid_i));
+      const int t0 = ch * C, rv = rows_of(ch);
+      const float* carry = sCarry + (it & 1) * M;
+      const bool slow = stage(ch, it, lane_i, tid_i);
+      const bf16_t* hrow = h_ws + (ub + t0) * M;
+      const bf16_t* grow = gg + (ub + t0) * M;
+      bf16_t* dkrow = dk + (ub + t0) * DK;
+      bf16_t* dvrow = dv + (ub + t0) * DV;
+      bf16_t* dgrow = dg + (ub + t0) * M;
+      if (!slow) {
+        switch (wv) {
+          case 0: rev_pass<DK, DV, M, 0>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          case 1: rev_pass<DK, DV, M, 1>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          case 2: rev_pass<DK, DV, M, 2>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          default: rev_pass<DK, DV, M, 3>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+        }
+      } else {
+        __syncthreads();  // log alpha is in LDS
+        rev_exact_pass<M>(rv, smem, Lds::oS, carry, sWt, hrow, grow, dgrow, inv_tau, lane_i, wv);
+      }
+      __syncthreads();  // B: every wave's gate totals are in LDS
+      if (!slow) {
+        switch (wv) {
+          case 0: rev_pass_finish<M, 0>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          case 1: rev_pass_finish<M, 1>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          case 2: rev_pass_finish<M, 2>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          default: rev_pass_finish<M, 3>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ host side
+// Chunks per segment: about 256 workgroups over the units (the forward's
+// split), and at most kMaxSegChunks.  The gate sums inside a segment add up
+// bf16-rounded per-token terms (h) and MFMA-formed di; between segments the
+// carry is the exact per-slot dot of adjoint and state, so capping the
+// segment bounds how many rounded terms any gate gradient sums (measured:
+// 257-chunk segments, at 1024 units of 16385 tokens, reached 3.7e-2 of
+// max |dg|).
+constexpr int kMaxSegChunks = 8;
+inline int chunks_per_segment(long long units, int nchunks) {
+  if (nchunks <= 1 || units <= 0) return nchunks > 0 ? nchunks : 1;
+  long long p = 256 / units;
+  if (p < 1) p = 1;
+  if (p > nchunks) p = nchunks;
+  const int s = (int)((nchunks + p - 1) / p);
+  return s < kMaxSegChunks ? s : kMaxSegChunks;
+}
+
+struct Ws {
+  float *st, *dec, *rm, *rdec;
+  bf16_t *s, *dz, *h;
+};
+
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the dense bf16 backward (bytes) and its carving: segment
+// start/end states and reverse maps (fp32), segment decays, and s, dz, h per
+// token (bf16).
+inline size_t ws_bytes(size_t U, int T, int dk, int dv, int m, Ws* w = nullptr, void* base = nullptr) {
+  const int nchunks = (T + C - 1) / C;
+  const int S = chunks_per_segment((long long)U, nchunks);
+  const size_t P = (size_t)((nchunks + S - 1) / S);
+  const size_t NE = (size_t)m * (dk + dv);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += a256(bytes);
+    return o;
+  };
+  const size_t o_st = take(U * P * NE * 4), o_dec = take(U * P * m * 4), o_rm = take(U * P * NE * 4),
+               o_rdec = take(U * P * m * 4), o_s = take(U * T * (size_t)m * 2),
+               o_dz = take(U * T * (size_t)m * 2), o_h = take(U * T * (size_t)m * 2);
+  if (w) {
+    char* b = (char*)base;
+    w->st = (float*)(b + o_st);
+    w->dec = (float*)(b + o_dec);
+    w->rm = (float*)(b + o_rm);
+    w->rdec = (float*)(b + o_rdec);
+    w->s = (bf16_t*)(b + o_s);
+    w->dz = (bf16_t*)(b + o_dz);
+    w->h = (bf16_t*)(b + o_h);
+  }
+  return off;
+}
+
+template <int DK, int DV, int M, int ACT>
+int launch(const GsaBwdLaunch& a) {
+  using Lds = BwdLds<DK, DV, M>;
+  const int U = a.B * a.H, T = a.T;
+  const int nchunks = (T + C - 1) / C;
+  const int S = chunks_per_segment(U, nchunks);
+  const int P = (nchunks + S - 1) / S;
+  Ws w;
+  ws_bytes((size_t)U, T, DK, DV, M, &w, a.ws);
+  const float inv_tau = 1.0f / a.tau;
+  static const bool lds_set = [] {
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_fwd<DK, DV, M, ACT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Lds::total);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_rev<DK, DV, M>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              Lds::total);
+    return true;
+  }();
+  (void)lds_set;
+  if (gsa_bf16_segment_states(DK, DV, M, a.k, a.v, a.g, a.k0, a.v0, w.st, w.dec, U, T, S, P, a.tau, a.stream) != 0)
+    return -1;
+  const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v, *g = (const bf16_t*)a.g,
+               *dO = (const bf16_t*)a.d_o;
+  launch_timed(bwd_bf16_fwd<DK, DV, M, ACT>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 0, 1, q, k, v,
+               g, dO, w.st, w.rm, w.rdec, (bf16_t*)a.dq, w.s, w.dz, w.h, T, S, P, inv_tau);
+  const long long ne = (long long)U * M * (DK + DV) / 4;
+  hipLaunchKernelGGL((bwd_bf16_rscan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)a.stream, w.rm, (const float*)w.rdec, a.dkf, a.dvf, a.dk0, a.dv0, U, P);
+  launch_timed(bwd_bf16_rev<DK, DV, M>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 2, 3, q, k, v, g,
+               dO, (const float*)w.st, (const float*)w.rm, (const bf16_t*)w.s, (const bf16_t*)w.dz,
+               (const bf16_t*)w.h, (bf16_t*)a.dk, (bf16_t*)a.dv, (bf16_t*)a.dg, T, S, P, inv_tau);
+  return 0;
+}
+
+template <int DK, int DV, int M>
+int launch_act(const GsaBwdLaunch& a) {
+  switch (a.act) {
+    case kActSoftmax: return launch<DK, DV, M, kActSoftmax>(a);
+    case kActIdentity: return launch<DK, DV, M, kActIdentity>(a);
+    case kActSwish: return launch<DK, DV, M, kActSwish>(a);
+    case kActRelu: return launch<DK, DV, M, kActRelu>(a);
+    case kActRelu2: return launch<DK, DV, M, kActRelu2>(a);
+    default: return -1;
+  }
+}
+
+}  // namespace bfb
+
+// The dense bf16 backward on the matrix cores: returns the workspace bytes
+// (query) or launches (0); -1 if (dk, dv, m) is not compiled for it.
+long long gsa_bwd_bf16_dispatch(int dk, int dv, int m, const GsaBwdLaunch* a, bool query, size_t units, int T) {
+#define BWD_BF16_CASE(DKC, DVC, MC)                                                        \
+  if (dk == DKC && dv == DVC && m == MC)                                                   \
+    return query ? (long long)bfb::ws_bytes(units, T, DKC, DVC, MC) : bfb::launch_act<DKC, DVC, MC>(*a);
+  BWD_BF16_CASE(128, 128, 64)
+  BWD_BF16_CASE(128, 128, 32)
+  BWD_BF16_CASE(64, 64, 64)
+  BWD_BF16_CASE(64, 64, 32)
+#undef BWD_BF16_CASE
+  return -1;
+}
+
+}  // namespace gsa

@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "bf16_common.hpp"
+#include "bf16_state.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 #include "launch.hpp"
@@ -90,226 +91,6 @@ struct StateLds {  // two buffers of everything a chunk needs (software pipeline
   static constexpr int total = 2 * szBuf;
   static_assert(oV % 16 == 0 && oZ % 16 == 0 && oDec % 16 == 0 && szBuf % 16 == 0, "alignment");
 };
-
-// Output-pass factors of SPT slots for token row = lane of a chunk, with
-// G = chunk-local inclusive cumulative sum of log2 alpha:
-//   E_j = exp2(G_j),  X_j = (1 - alpha_j) / E_j = 1/E_j - 1/E_{j-1}.
-// Rows past the end of the sequence are identity steps (log alpha = 0).
-template <int SPT>
-struct LogGates {
-  float G[SPT], E[SPT], X[SPT];
-  // g: a gate row holding at least SPT values
-  template <class Row>
-  __device__ __forceinline__ void compute(const Row& g, bool valid, float inv_tau) {
-#pragma unroll
-    for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
-    wave_prefix_sums<SPT>(G);
-#pragma unroll
-    for (int s = 0; s < SPT; s++) {
-      E[s] = __builtin_amdgcn_exp2f(G[s]);
-      X[s] = __builtin_amdgcn_exp2f(-G[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < SPT; s++) X[s] -= prev_lane(X[s], 1.f);
-  }
-};
-
-// State-map factors: the decay from token r to the chunk end
-// S_r = prod_{i>r} alpha_i = exp2(G_C - G_r), the write term
-// Z_r = (1 - alpha_r) S_r = S_r - S_{r-1}, and the whole-chunk decay.
-template <int SPT>
-struct SuffixGates {
-  float Z[SPT], dec[SPT];
-  __device__ __forceinline__ void compute(const GateRow<SPT>& g, bool valid, float inv_tau) {
-    float G[SPT];
-#pragma unroll
-    for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
-    wave_prefix_sums<SPT>(G);
-#pragma unroll
-    for (int s = 0; s < SPT; s++) {
-      const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
-      dec[s] = __builtin_amdgcn_exp2f(tot);
-      Z[s] = __builtin_amdgcn_exp2f(tot - G[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < SPT; s++) Z[s] -= prev_lane(Z[s], dec[s]);
-  }
-};
-
-// ------------------------------------------------------------ state tiles
-// W^T held in MFMA accumulators by NSW waves: wave sw owns column tiles
-// [sw*NCW, (sw+1)*NCW) of W (columns 0..DK-1 are Kt, DK.. are Vt) and all M
-// slots.  Lane l of tile (n, ct) holds W[16ct + l%16][16(sw*NCW+n) + 4(l/16) + i].
-template <int DK, int DV, int M, int NSW>
-struct StateTiles {
-  static constexpr int MT = M / 16;
-  static constexpr int NCT = (DK + DV) / 16;
-  static constexpr int NCW = NCT / NSW;
-  static_assert(NCT % NSW == 0 && NCW >= 1, "state columns must split evenly");
-  static_assert((DK / 16) % NCW == 0, "a wave's columns must lie in one of Kt / Vt");
-  f32x4 st[NCW][MT];
-
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) st[n][ct] = zero4();
-  }
-  __device__ __forceinline__ int col(int sw, int n, int lane) const {
-    return 16 * (sw * NCW + n) + 4 * (lane >> 4);
-  }
-  // src [M][DK+DV] fp32 (one map/state of the workspace)
-  __device__ __forceinline__ void load_w(const float* __restrict__ src, int sw, int lane) {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) {
-        const float4 x = *reinterpret_cast<const float4*>(
-            src + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane));
-        st[n][ct] = f32x4{x.x, x.y, x.z, x.w};
-      }
-  }
-  // one segment map (layout of load_w) into registers, and the segment step
-  // W <- Diag(dec) W + map with the scan kernel's operation order
-  typedef f32x4 MapRegs[NCW][MT];
-  __device__ __forceinline__ void load_map(MapRegs& x, const float* __restrict__ src, int sw,
-                                           int lane) const {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) {
-        const float4 v = *reinterpret_cast<const float4*>(
-            src + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane));
-        x[n][ct] = f32x4{v.x, v.y, v.z, v.w};
-      }
-  }
-  __device__ __forceinline__ void fold(const MapRegs& x, const float* __restrict__ dec, int lane) {
-#pragma unroll
-    for (int ct = 0; ct < MT; ct++) {
-      const float d = dec[16 * ct + (lane & 15)];
-#pragma unroll
-      for (int n = 0; n < NCW; n++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) st[n][ct][i] = d * st[n][ct][i] + x[n][ct][i];
-    }
-  }
-  // k0 [M][DK], v0 [M][DV], each nullable (zeros)
-  __device__ __forceinline__ void load_kv(const float* __restrict__ k0, const float* __restrict__ v0,
-                                          int sw, int lane) {
-#pragma unroll
-    for (int n = 0; n < NCW; n++) {
-      const int cl = col(sw, n, lane);
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) {
-        const int c = 16 * ct + (lane & 15);
-        const float* p = cl < DK ? (k0 ? k0 + (size_t)c * DK + cl : nullptr)
-                                 : (v0 ? v0 + (size_t)c * DV + cl - DK : nullptr);
-        if (p) {
-          const float4 x = *reinterpret_cast<const float4*>(p);
-          st[n][ct] = f32x4{x.x, x.y, x.z, x.w};
-        } else {
-          st[n][ct] = zero4();
-        }
-      }
-    }
-  }
-  __device__ __forceinline__ void store_w(float* __restrict__ dst, int sw, int lane) const {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++)
-        *reinterpret_cast<float4*>(dst + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane)) =
-            make_float4(st[n][ct][0], st[n][ct][1], st[n][ct][2], st[n][ct][3]);
-  }  // the same to global memory with streaming stores: a segment map is read
-  // only by the next launch, so its lines need not stay in L2 (less for the
-  // end of the kernel to write back)
-  __device__ __forceinline__ void store_w_nt(float* __restrict__ dst, int sw, int lane) const {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++)
-        __builtin_nontemporal_store(
-            st[n][ct], reinterpret_cast<f32x4*>(dst + (size_t)(16 * ct + (lane & 15)) * (DK + DV) + col(sw, n, lane)));
-  }
-
-  __device__ __forceinline__ void store_kv(float* __restrict__ kf, float* __restrict__ vf, int sw,
-                                           int lane) const {
-#pragma unroll
-    for (int n = 0; n < NCW; n++) {
-      const int cl = col(sw, n, lane);
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) {
-        const int c = 16 * ct + (lane & 15);
-        float* p = cl < DK ? (kf ? kf + (size_t)c * DK + cl : nullptr)
-                           : (vf ? vf + (size_t)c * DV + cl - DK : nullptr);
-        if (p) *reinterpret_cast<float4*>(p) = make_float4(st[n][ct][0], st[n][ct][1], st[n][ct][2], st[n][ct][3]);
-      }
-    }
-  }
-  // bf16 copy of W, row-major [M][ldw]
-  __device__ __forceinline__ void store_copy(bf16_t* sW, int ldw, int sw, int lane) const {
-#pragma unroll
-    for (int n = 0; n < NCW; n++)
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++)
-        *reinterpret_cast<bf16x4v*>(sW + (16 * ct + (lane & 15)) * ldw + col(sw, n, lane)) = pack4(st[n][ct]);
-  }
-  // one chunk: W^T <- W^T Diag(E_C) + [K|V]^T Z
-  __device__ __forceinline__ void carry(const bf16_t* sK, int ldk, const bf16_t* sV, int ldv,
-                                        const bf16_t* sZ, int ldz, const float* sDec, int sw,
-                                        int lane) {
-    const int L = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int ct = 0; ct < MT; ct++) {
-      const float d = sDec[16 * ct + L];
-#pragma unroll
-      for (int n = 0; n < NCW; n++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) st[n][ct][i] *= d;
-    }
-#pragma unroll
-    for (int r0 = 0; r0 < C; r0 += 32) {
-      bf16x8 zb[MT];
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) zb[ct] = ld_col(sZ, ldz, 16 * ct, r0 + 8 * g, r0 + 8 * g + 4, lane);
-#pragma unroll
-      for (int n = 0; n < NCW; n++) {
-        const int c0 = 16 * (sw * NCW + n);
-        const bf16x8 a = c0 < DK ? ld_col(sK, ldk, c0, r0 + 8 * g, r0 + 8 * g + 4, lane)
-                                 : ld_col(sV, ldv, c0 - DK, r0 + 8 * g, r0 + 8 * g + 4, lane);
-#pragma unroll
-        for (int ct = 0; ct < MT; ct++) st[n][ct] = mma(a, zb[ct], st[n][ct]);
-      }
-    }
-  }
-};
-
-// ------------------------------------------------------ chunk factors
-// SPT slots from slot0 of one chunk (token row = lane): X = (1-alpha)/E,
-// Z = (1-alpha) prod_{i>r} alpha_i and E into one factor set, the whole-chunk
-// decay into dec.  Returns whether any of these slots decays below the range
-// of the factorised form in this chunk.
-template <int SPT, int LDX, int LDE, class Row>
-__device__ __forceinline__ bool chunk_factors(const Row& g, bool valid, float inv_tau,
-                                              int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
-                                              float* sDec) {
-  LogGates<SPT> gt;
-  gt.compute(g, valid, inv_tau);
-  bool small = false;
-  float z[SPT];
-#pragma unroll
-  for (int s = 0; s < SPT; s++) {
-    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.G[s]), 63));
-    small |= !(gc >= kFastMinLog2Decay);
-    const float dc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.E[s]), 63));
-    z[s] = gt.X[s] * dc;
-    if (lane == 0) sDec[slot0 + s] = dc;
-  }
-  store_bf16_row<SPT>(sX + lane * LDX + slot0, gt.X);
-  store_bf16_row<SPT>(sZ + lane * LDX + slot0, z);
-  store_f32_row<SPT>(sE + lane * LDE + slot0, gt.E);
-  return small;
-}
 
 // -------------------------------------------------------- pass-wave chunk
 // Token rows 16J..16J+15 of the chunk: pass 1, the slot read non-linearity
@@ -967,6 +748,50 @@ static int launch_act(const GsaLaunch& a) {
 }
 
 }  // namespace bfk
+
+namespace bfk {
+// The segment start states of a dense batch, as the forward computes them:
+// state maps of segments 0 .. P-2 and the per-unit scan, so that ws_state[u][p]
+// (layout [units][P][M][DK+DV] fp32) holds the state at the start of segment p
+// (p = 0: the initial state).  ws_dec: [units][P][M] fp32.
+template <int DK, int DV, int M>
+static void segment_states(const void* k, const void* v, const void* g, const float* k0,
+                           const float* v0, float* ws_state, float* ws_dec, int units, int T, int S,
+                           int P, float tau, void* stream) {
+  using LS = StateLds<DK, DV, M>;
+  static const bool lds_set = [] {
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M, DenseSeqs>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
+    return true;
+  }();
+  (void)lds_set;
+  hipStream_t st = (hipStream_t)stream;
+  if (P > 1)
+    hipLaunchKernelGGL((gsa_bf16_state<DK, DV, M, DenseSeqs>), dim3(P - 1, units), dim3(NT), LS::total, st,
+                       (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, ws_state, ws_dec,
+                       DenseSeqs{T}, S, P, 1.0f / tau);
+  const long long ne = (long long)units * M * (DK + DV) / 4;
+  hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
+                     ws_state, (const float*)ws_dec, k0, v0, units, P);
+}
+}  // namespace bfk
+
+int gsa_bf16_segment_states(int dk, int dv, int m, const void* k, const void* v, const void* g,
+                            const float* k0, const float* v0, float* ws_state, float* ws_dec,
+                            int units, int T, int S, int P, float tau, void* stream) {
+#define SEG_CASE(DKC, DVC, MC)                                                                  \
+  if (dk == DKC && dv == DVC && m == MC) {                                                      \
+    bfk::segment_states<DKC, DVC, MC>(k, v, g, k0, v0, ws_state, ws_dec, units, T, S, P, tau,   \
+                                      stream);                                                  \
+    return 0;                                                                                   \
+  }
+  SEG_CASE(128, 128, 64)
+  SEG_CASE(128, 128, 32)
+  SEG_CASE(64, 64, 64)
+  SEG_CASE(64, 64, 32)
+#undef SEG_CASE
+  return -1;
+}
 
 #define GSA_BF16_CASE(DKC, DVC, MC)                                      \
   if (dk == DKC && dv == DVC && m == MC) {                                \

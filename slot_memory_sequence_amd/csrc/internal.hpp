@@ -95,9 +95,31 @@ struct GsaBwdLaunch {
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t around the two token-walk kernels
 };
+// The bf16 forward's segment start states of a dense batch (state maps of
+// segments 0 .. P-2, then the per-unit scan): ws_state [units][P][m][dk+dv]
+// fp32, slot p = the state at the start of segment p (S chunks each); ws_dec
+// [units][P][m] fp32.  Returns -1 if (dk, dv, m) is not compiled.
+int gsa_bf16_segment_states(int dk, int dv, int m, const void* k, const void* v, const void* g,
+                            const float* k0, const float* v0, float* ws_state, float* ws_dec,
+                            int units, int T, int S, int P, float tau, void* stream);
+
 // workspace of one launch sequence of `units` units of `chunks` chunks over
 // `rows` token rows in all
 size_t gsa_bwd_ws_bytes(size_t units, size_t chunks, size_t rows, int dk, int dv, int m);
 int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query);
+// The dense bf16 backward on the matrix cores (the chunk form): query ->
+// workspace bytes for `units` units of T tokens; launch -> 0; -1 if (dk, dv,
+// m) is not compiled for it.
+long long gsa_bwd_bf16_dispatch(int dk, int dv, int m, const GsaBwdLaunch* a, bool query, size_t units, int T);
+// Workspace bytes of the backward a call with these arguments runs: the
+// matrix-core path for a dense bf16 batch, the token-walk path otherwise
+// (float32, packed batches: `rows` token rows, `units` units of `chunks`
+// chunks per launch sequence).
+size_t gsa_bwd_need_bytes(int dtype, int act, bool packed, size_t units, size_t chunks, size_t rows, int T,
+                          int dk, int dv, int m);
+// Whether a call runs the matrix-core backward: dense bf16 batches of every
+// read but ReLU, whose derivative is a step at z = 0 -- there the token walk's
+// fp32 scores keep the step on the same side as the exact z, bf16 operands do not.
+inline bool gsa_bwd_on_mfma(int dtype, int act, bool packed) { return dtype == 1 && !packed && act != 3; }
 
 }  // namespace gsa

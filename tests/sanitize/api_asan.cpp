@@ -53,6 +53,11 @@ int gsa_bwd_dispatch(int, int dk, int dv, int m, const GsaBwdLaunch* a, bool que
 size_t gsa_bwd_ws_bytes(size_t units, size_t chunks, size_t rows, int dk, int dv, int m) {
   return (units * chunks * (size_t)m * (dk + dv) + rows * (size_t)m) * 4;
 }
+size_t gsa_bwd_need_bytes(int dtype, int act, bool packed, size_t units, size_t chunks, size_t rows, int T,
+                          int dk, int dv, int m) {
+  return gsa_bwd_ws_bytes(units, chunks, rows, dk, dv, m) / (gsa_bwd_on_mfma(dtype, act, packed) ? 2 : 1) +
+         (size_t)T * 0;
+}
 void state_copy(float*, const float*, size_t, void*) {}
 void record_event(void* const*, int, void*) {}
 }  // namespace gsa
@@ -142,8 +147,8 @@ int main() {
   // ---- backward
   void *dq = A(9 * 256 * MB), *dk = A(10 * 256 * MB), *dv = A(11 * 256 * MB), *dg = A(12 * 256 * MB);
   void* dO = A(13 * 256 * MB);
-  size_t nbw = gsa_bwd_workspace_bytes(B, H, T, d, d, m);
-  CHECK(nbw > 0);
+  size_t nbw = gsa_bwd_workspace_bytes_ex(B, H, T, d, d, m, GSA_DTYPE_BF16, GSA_SLOT_SOFTMAX);
+  CHECK(nbw > 0 && nbw < gsa_bwd_workspace_bytes(B, H, T, d, d, m));
   CHECK(gsa_bwd(q, k, v, g, dO, nullptr, nullptr, nullptr, nullptr, dq, dk, dv, dg, nullptr, nullptr, B,
                 H, T, d, d, m, 8.f, 1, ws, nbw, nullptr, nullptr) == GSA_OK);
   CHECK(g_bwd.ws == (float*)ws && g_bwd.T == T);

@@ -288,3 +288,23 @@ def test_autograd_double_backward_raises(gsa, torch):
     (gq,) = torch.autograd.grad(o.sum(), leaves["q"], create_graph=True)
     with pytest.raises(RuntimeError):
         torch.autograd.grad(gq.sum(), leaves["k"])
+
+
+def test_bwd_exact_chunks_inside_segments_sampled(gsa, torch):
+    """Segments of several chunks where most chunks leave the factorised range
+    (8 of 64 slots at logits N(-6, 1), about -48 of log-decay per chunk) and
+    one chunk in the middle of a segment holds gates at +-inf: the exact
+    token walks carry the state, the reverse map, the adjoint and the gate
+    sums across fast and exact chunks alike.  Sampled units against the
+    oracle."""
+    B, H, T = 8, 4, 1024  # 32 units of 16 chunks: segments of 2 chunks
+    inp = synth.gsa_inputs(B, H, T, 128, 128, 64, dtype="bf16", seed=81, init_std=0.1, fast_slots=8,
+                           fast_shift=-6.0)
+    x = inp["g"].f64.copy()
+    x[:, :, 70:90, 20:30] = np.inf
+    x[:, :, 75, 40:] = -np.inf
+    inp["g"] = synth.stored(x, "bf16")
+    gi = synth.gsa_grad_inputs(B, H, T, 128, 128, 64, dtype="bf16", seed=82, final_std=1.0)
+    got = _run(gsa, torch, inp, gi, 8.0)
+    units = [0, 13, 31]
+    _compare(got, _ref(inp, gi, 8.0, units=units), "bf16", "exact chunks inside segments", units=units)
