@@ -11,8 +11,13 @@ namespace bfk {
 constexpr int C = 64;   // chunk length
 constexpr int NW = 8;   // waves per workgroup
 constexpr int NT = NW * 64;
-// log2 of the smallest whole-chunk decay the factorised chunk form allows (e^-40)
-constexpr float kFastMinLog2Decay = -57.70780163555854f;
+// log2 of the smallest whole-chunk decay the factorised chunk form allows
+// (2^-90, about e^-62).  The forms divide by the chunk-local decay E, so
+// X = (1 - alpha) / E <= 2^90: a masked score times X stays about 2^38 below
+// the bf16 / fp32 overflow at 2^128 (no inf to meet a zero mask), E stays a
+// normal fp32 number, and every product that survives the causal mask is a
+// ratio E_j / E_r <= 1 formed from two factors of exact relative precision.
+constexpr float kFastMinLog2Decay = -90.0f;
 // Up to this many segment maps before the last segment, the output workgroups
 // build their start states from the maps themselves (no scan launch).
 constexpr int kMaxFoldedMaps = 3;

@@ -35,7 +35,7 @@
 //              two factor sets: the state waves before the chunk's first
 //              barrier (beside the pass waves' contractions), the pass waves
 //              after it (beside the state copy).
-// A chunk whose decay product falls below e^-40 in some key dimension runs as
+// A chunk whose decay product falls below 2^-90 in some key dimension runs as
 // the exact token recurrence instead (no division by a decay product).
 #include "bf16_common.hpp"
 #include "common.hpp"

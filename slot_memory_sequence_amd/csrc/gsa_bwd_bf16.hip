@@ -39,7 +39,7 @@
 //      gradients;
 //   4. bwd_bf16_rev: per segment, chunks in reverse from its end adjoint:
 //      the adjoint update (state waves), dk, dv, di and dg (pass waves).
-// A chunk where some slot's decay product falls below e^-40 (the factorised
+// A chunk where some slot's decay product falls below 2^-90 (the factorised
 // forms divide by E) runs as an exact token walk of the state waves over the
 // fp32 state / adjoint they hold in their accumulators.
 #include <type_traits>

@@ -31,7 +31,7 @@
 // the outputs (gsa_bf16_out).  With at most kMaxFoldedMaps maps before the last
 // segment there is no scan launch: each output workgroup folds the maps before
 // its segment into its start state (a dependent launch costs more than a few
-// such reads).  A chunk whose decay product falls below e^-40
+// such reads).  A chunk whose decay product falls below 2^-90
 // in some slot is run as the exact token recurrence instead (no division by a
 // decay product).
 #include <algorithm>

@@ -204,6 +204,12 @@ WORKLOADS = {
                                              C=64, tau=8.0, dtype="bf16",
                                              qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                                              init_std=None, fast_slots=8, fast_shift=-6.0),
+    # the same with logits N(-10, 1): log alpha ~ -1.25 per token, about -80
+    # over a 64-token chunk
+    "gsa_bf16_train_T2048_rapid_forget": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=64,
+                                              C=64, tau=8.0, dtype="bf16",
+                                              qkv_scale=1 / math.sqrt(128), g_shift=0.0,
+                                              init_std=None, fast_slots=8, fast_shift=-10.0),
     "gla_bf16_T4096": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64, tau=16.0,
                            dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                            init_std=None),

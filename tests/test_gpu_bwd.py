@@ -308,3 +308,14 @@ def test_bwd_exact_chunks_inside_segments_sampled(gsa, torch):
     got = _run(gsa, torch, inp, gi, 8.0)
     units = [0, 13, 31]
     _compare(got, _ref(inp, gi, 8.0, units=units), "bf16", "exact chunks inside segments", units=units)
+
+
+@pytest.mark.parametrize("mean", [-7.3, -8.0])
+def test_bwd_decay_near_the_floor(gsa, torch, mean):
+    """Gate logits N(mean, 0.05): 64-token decay products ~2^-84 (factorised
+    with X up to ~2^84) and ~2^-92 (around the 2^-90 floor: chunks of both
+    forms), through the forward and reverse sweeps."""
+    def mut(inp):
+        r = np.random.default_rng(6)
+        inp["g"] = synth.stored(mean + 0.05 * r.standard_normal(inp["g"].shape), "bf16")
+    _check(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, final=True, seed=83, edit=mut)

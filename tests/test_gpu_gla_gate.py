@@ -56,7 +56,8 @@ def test_gla_log_decay_segmentations(gsa, torch, cps):
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
 def test_gla_log_decay_exact_path(gsa, torch, dtype, d):
-    """Strong decays (a whole chunk far below e^-40), alpha = 0 (-inf) and
+    """Strong decays (a whole chunk far below the factorised
+    form's floor), alpha = 0 (-inf) and
     positive entries (taken as 0) send chunks through the exact recurrence."""
     inp = synth.gla_inputs(1, 2, 260, d, d, dtype=dtype, seed=9, init_std=0.1, log_decay_scale=0.06)
     x = inp["g"].f64.copy()

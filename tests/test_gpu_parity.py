@@ -110,7 +110,8 @@ def _extreme(inp):
 @pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
 def test_gsa_extreme_gates(gsa, torch, dtype, d, m):
     """alpha = 0 / alpha = 1 tokens (g = -inf / +inf, +-30): chunks whose decay
-    product falls below e^-40 take the exact token recurrence."""
+    product falls below the factorised form's floor (e^-40 in float32,
+    2^-90 in bfloat16) take the exact token recurrence."""
     for cps in (0, 1):
         _check_gsa(gsa, torch, 1, 2, 300, d, m, dtype, init=True, cps=cps, mutate=_extreme, seed=7)
 
@@ -322,22 +323,35 @@ def _shift_gates(shift):
     return mut
 
 
-@pytest.mark.parametrize("case", ["all", "mixed"])
+def _near_floor(x_mean, x_std):
+    """Gate logits N(x_mean, x_std) on every token (a decay regime chosen
+    relative to the factorised form's floor of 2^-90 per 64-token chunk)."""
+    def mut(inp):
+        r = np.random.default_rng(5)
+        inp["g"] = synth.stored(x_mean + x_std * r.standard_normal(inp["g"].shape), inp["g"].dtype)
+    return mut
+
+
+@pytest.mark.parametrize("case", ["all", "mixed", "near_floor"])
 def test_gsa_bf16_strong_decay(gsa, torch, case):
-    # alpha = sigmoid(g)^(1/8).  "all": g ~ N(-8, 1) makes every 64-token decay
-    # product ~e^-64, below the e^-40 floor of the factorised form, so every
-    # chunk runs the exact recurrence.  "mixed": g = -12 on chunks 1 and 3
-    # (product ~e^-96) and N(0, 1) elsewhere.
-    mut = _shift_gates(-8.0) if case == "all" else _decay_chunks((1, 3), -12.0)
+    # alpha = sigmoid(g)^(1/8).  "all": g ~ N(-8, 1) makes the 64-token decay
+    # products ~2^-92, around the 2^-90 floor of the factorised form, so
+    # chunks take either form.  "mixed": g = -12 on chunks 1 and 3 (product
+    # ~2^-138, exact recurrence) and N(0, 1) elsewhere.  "near_floor": g ~
+    # N(-7.3, 0.05), products ~2^-84: every chunk factorised with X up to ~2^84.
+    mut = {"all": _shift_gates(-8.0), "mixed": _decay_chunks((1, 3), -12.0),
+           "near_floor": _near_floor(-7.3, 0.05)}[case]
     for cps in (0, 1):
         _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, cps=cps, seed=21, mutate=mut)
 
 
-@pytest.mark.parametrize("case", ["all", "mixed"])
+@pytest.mark.parametrize("case", ["all", "mixed", "near_floor"])
 def test_gla_bf16_strong_decay(gsa, torch, case):
-    # tau = 16: g ~ N(-12, 1) makes every 64-token product ~e^-48 (exact
-    # recurrence everywhere); "mixed": g = -12 on chunks 1 and 3 only
-    mut = _shift_gates(-12.0) if case == "all" else _decay_chunks((1, 3), -12.0)
+    # tau = 16: g ~ N(-12, 1) makes every 64-token product ~2^-70 (factorised
+    # near the floor); "mixed": g = -12 on chunks 1 and 3 only; "near_floor":
+    # g ~ N(-15.5, 0.05), products ~2^-89
+    mut = {"all": _shift_gates(-12.0), "mixed": _decay_chunks((1, 3), -12.0),
+           "near_floor": _near_floor(-15.5, 0.05)}[case]
     for cps in (0, 1):
         _check_gla(gsa, torch, 1, 3, 64 * 5 + 11, 128, "bf16", init=True, cps=cps, seed=22, mutate=mut)
 
