@@ -85,14 +85,22 @@ const char* gsa_status_string(int status);
 
 /* 1 if the shape/dtype combination is compiled for the GPU, else 0.  The chunk
  * length C of the chunkwise form (App. A.1) is fixed at 64 tokens in this
- * build; the result of the method does not depend on C. */
+ * build; the result of the method does not depend on C.  Compiled: bf16 with
+ * d = dk = dv in {64, 128} and m in {32, 64, 128} (m = 128 as two groups of 64
+ * slots, each carried by its own chunk form, whose outputs are merged by the
+ * softmax read's log-sum-exp of each group: the slot rows of the states never
+ * mix, Sec. 3.2); float32 with d = 64, m in {16, 32, 64} and d = 128, m in
+ * {16, 32}.  Decode: bf16 with d in {64, 128}, m in {32, 64, 128}; float32
+ * with d = 128, m in {32, 64, 128} and d = 64, m in {16, 32, 64}. */
 int gsa_fwd_supported(int dk, int dv, int m, int C, int dtype);
 int gla_fwd_supported(int dk, int dv, int C, int dtype);
 int gsa_decode_supported(int dk, int dv, int m, int dtype);
 
 /* Bytes of device workspace gsa_fwd / gla_fwd need for this problem (the
- * segment state maps of the chunk-state scan).  chunks_per_segment = 0 picks
- * the library's default split; (size_t)-1 on invalid arguments. */
+ * segment state maps of the chunk-state scan; for bf16 GSA at m = 128 also the
+ * two slot groups' output rows and log-sum-exps, B*H*T*(2*dv*2 + 8) bytes).
+ * chunks_per_segment = 0 picks the library's default split; (size_t)-1 on
+ * invalid arguments. */
 size_t gsa_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int C, int dtype,
                                int chunks_per_segment);
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int dtype,
@@ -137,8 +145,8 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
  *   o        [H, total, dv]  bf16
  *   k_final, v_final [n_seqs, H, m, dk|dv] float32, NULL = not wanted (may
  *            equal k0 / v0)
- * Only bf16 storage and the softmax read are compiled for this entry point
- * (GSA_ERR_UNSUPPORTED otherwise); a bad cu_seqlens returns GSA_ERR_SHAPE.
+ * Only bf16 storage, m <= 64 and the softmax read are compiled for this entry
+ * point (GSA_ERR_UNSUPPORTED otherwise); a bad cu_seqlens returns GSA_ERR_SHAPE.
  * Workspace, aliasing, events and errors as for gsa_fwd_events; the workspace
  * size comes from gsa_fwd_varlen_workspace_bytes with the same cu_seqlens.
  * With more than 256 sequences the timing hooks stamp the whole call: events

@@ -75,6 +75,24 @@ size_t ws_bytes(long long units, int T, int cps, size_t state_elems, size_t dec_
   return ((st + 255) & ~(size_t)255) + dc;
 }
 
+// Workspace of a GSA forward over `units` (b, h) units of T tokens (c chunks
+// per segment): segment maps and decay products of units * G slot-group units
+// (G = slot_groups(dtype, m)), then with G > 1 the groups' output rows
+// ([units*T][G][dv], I/O dtype) at *part_off and log-sum-exps ([units*T][G]
+// fp32) at *lse_off.
+size_t fwd_ws_bytes(long long units, int T, int c, int dk, int dv, int m, int dtype,
+                    size_t* part_off = nullptr, size_t* lse_off = nullptr) {
+  const int G = gsa::slot_groups(dtype, m);
+  const size_t maps = ws_bytes(units * G, T, c, (size_t)(m / G) * (dk + dv), (size_t)(m / G));
+  if (G == 1 || T == 0 || units == 0) return maps;
+  const size_t rows = (size_t)units * T;
+  const size_t po = (maps + 255) & ~(size_t)255;
+  const size_t lo = (po + rows * G * dv * esize(dtype) + 255) & ~(size_t)255;
+  if (part_off) *part_off = po;
+  if (lse_off) *lse_off = lo;
+  return lo + rows * G * 4;
+}
+
 int hip_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? GSA_OK : GSA_ERR_HIP;
@@ -142,7 +160,10 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
     return GSA_ERR_ALIAS;
   for (Range in : {rq, rk, rv, rg, rk0, rv0})
     if (overlap(rws, in)) return GSA_ERR_ALIAS;
-  const size_t need = ws_bytes(ws_units, T, c, (size_t)m * (dk + dv), (size_t)m);
+  const int G = gsa::slot_groups(dtype, m);
+  if (cu && G > 1) return GSA_ERR_UNSUPPORTED;
+  size_t part_off = 0, lse_off = 0;
+  const size_t need = fwd_ws_bytes(ws_units, T, c, dk, dv, m, dtype, &part_off, &lse_off);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
 
   if (T == 0) {  // nothing to read: the final state is the initial state
@@ -161,6 +182,10 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
                        : nullptr;
   a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
   a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
+  if (G > 1) {
+    a.ws_part = (char*)workspace + part_off;
+    a.ws_lse = (float*)((char*)workspace + lse_off);
+  }
   a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
@@ -208,7 +233,8 @@ size_t gsa_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int C
   if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !dtype_ok(dtype))
     return (size_t)-1;
   const long long units = (long long)B * H;
-  return ws_bytes(units, T, resolve_cps(units, T, cps), (size_t)m * (dk + dv), (size_t)m);
+  const int G = gsa::slot_groups(dtype, m);
+  return fwd_ws_bytes(units, T, resolve_cps(units * G, T, cps), dk, dv, m, dtype);
 }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int dtype, int cps) {
@@ -243,10 +269,11 @@ int gsa_fwd_ex(const void* q, const void* k, const void* v, const void* g, const
     return GSA_ERR_SHAPE;
   if (!gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
-  if (units > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  const int G = gsa::slot_groups(dtype, m);
+  if (units * G > kMaxUnits) return GSA_ERR_UNSUPPORTED;
   if (units == 0) return GSA_OK;
   return gsa_run(q, k, v, g, k0, v0, o, kf, vf, B, H, T, (size_t)units * T,
-                 resolve_cps(units, T, cps), nullptr, dk, dv, m, tau, dtype, workspace,
+                 resolve_cps(units * G, T, cps), nullptr, dk, dv, m, tau, dtype, workspace,
                  workspace_bytes, nonlinearity, stream, events);
 }
 
@@ -272,7 +299,8 @@ int gsa_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
   if (H < 0 || dk < 1 || dv < 1 || m < 1 || C < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
       !dtype_ok(dtype) || !varlen_ok(cu_seqlens, n_seqs, &tmax, &total_chunks))
     return GSA_ERR_SHAPE;
-  if (dtype != GSA_DTYPE_BF16 || !gsa_fwd_supported(dk, dv, m, C, dtype)) return GSA_ERR_UNSUPPORTED;
+  if (dtype != GSA_DTYPE_BF16 || !gsa_fwd_supported(dk, dv, m, C, dtype) || gsa::slot_groups(dtype, m) > 1)
+    return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)n_seqs * H;
   if ((long long)std::min(n_seqs, gsa::kMaxVarSeqs) * H > kMaxUnits) return GSA_ERR_UNSUPPORTED;
   if (units == 0) return GSA_OK;

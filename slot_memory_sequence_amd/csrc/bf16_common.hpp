@@ -25,6 +25,7 @@ constexpr int kMaxFoldedMaps = 3;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4v;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -337,6 +338,7 @@ struct Span {
 // unit_of maps the launch order of the units to the units (here the identity).
 struct DenseSeqs {
   static constexpr bool kVar = false;
+  static constexpr int kGroups = 1;  // slot groups per (b, h): see SlotGroups
   int T;
   __device__ __forceinline__ Span span(int unit) const { return {(size_t)unit * T, T}; }
   __device__ __forceinline__ int unit_of(int i) const { return i; }
@@ -350,6 +352,7 @@ struct DenseSeqs {
 // length), so that the short ones fill the tail of the grid.
 struct VarSeqs {
   static constexpr bool kVar = true;
+  static constexpr int kGroups = 1;
   int H, total;
   int cu[kMaxVarSeqs + 1];
   int order[kMaxVarSeqs];
@@ -362,6 +365,29 @@ struct VarSeqs {
     return order[r] * H + (i - r * H);
   }
 };
+
+// A dense batch whose 2M slots run as two groups of M, each group its own unit
+// (the slot rows of K~ and V~ never mix in the recurrence, Sec. 3.2; only the
+// read's softmax spans both groups, and it is merged afterwards from each
+// group's log-sum-exp).  Unit 2u + h is group h of (b, h) unit u: it reads the
+// q, k, v rows of unit u and gate columns hM .. hM + M - 1 of its g rows (row
+// pitch 2M), and writes its normalised output rows and log-sum-exps
+// interleaved with the other group's ([rows][2][dv], [rows][2]).  Its states
+// are slot rows hM .. hM + M - 1 of unit u's, which sit where a unit 2u + h of
+// M slots would: no offset changes there.
+struct SlotGroups {
+  static constexpr bool kVar = false;
+  static constexpr int kGroups = 2;
+  int T;
+  __device__ __forceinline__ Span span(int unit) const { return {(size_t)(unit >> 1) * T, T}; }
+  __device__ __forceinline__ int unit_of(int i) const { return i; }
+};
+
+// First gate logit of a unit's rows (row pitch M * kGroups) and its group.
+template <class Seq, int M>
+__device__ __forceinline__ size_t gate_base(const Span& sp, int unit) {
+  return sp.base * (M * Seq::kGroups) + (size_t)(unit % Seq::kGroups) * M;
+}
 
 }  // namespace bfk
 }  // namespace gsa

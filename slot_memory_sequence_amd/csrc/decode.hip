@@ -201,10 +201,13 @@ static int launch_decode_act(const DecodeLaunch& a) {
   }
 
 int decode_dispatch(int dt, int dk, int dv, int m, const DecodeLaunch* a, bool query) {
+  DEC_CASE(bf16_t, 1, 128, 128, 128)
   DEC_CASE(bf16_t, 1, 128, 128, 64)
   DEC_CASE(bf16_t, 1, 128, 128, 32)
+  DEC_CASE(bf16_t, 1, 64, 64, 128)
   DEC_CASE(bf16_t, 1, 64, 64, 64)
   DEC_CASE(bf16_t, 1, 64, 64, 32)
+  DEC_CASE(float, 0, 128, 128, 128)
   DEC_CASE(float, 0, 128, 128, 64)
   DEC_CASE(float, 0, 128, 128, 32)
   DEC_CASE(float, 0, 64, 64, 64)

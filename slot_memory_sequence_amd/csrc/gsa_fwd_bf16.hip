@@ -97,11 +97,13 @@ struct StateLds {  // two buffers of everything a chunk needs (software pipeline
 // (ACT: the softmax, or an element-wise ablation function), pass 2 and the
 // output rows.  Reads sQ, sK, sV, sX, sE and the bf16 state copy sW.  J is a
 // template parameter so that every loop is static and independent
-// accumulators can be interleaved.
-template <int DK, int DV, int M, int J, int ACT>
+// accumulators can be interleaved.  G > 1 (slot groups): output rows have the
+// pitch G * DV, and the softmax's log-sum-exp of token j goes to lrow[j * G].
+template <int DK, int DV, int M, int J, int ACT, int G>
 __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf16_t* sK,
                                            const bf16_t* sV, const bf16_t* sW, const bf16_t* sX,
-                                           const float* sE, bf16_t* __restrict__ orow, int rv) {
+                                           const float* sE, bf16_t* __restrict__ orow,
+                                           float* __restrict__ lrow, int rv) {
   using Lds = OutLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, NP = M / 32, NVT = DV / 16;
   constexpr int NR = J + 1;         // score row tiles r <= j
@@ -170,6 +172,9 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
       }
     sm = group4_sum(sm);
     inv = 1.f / sm;
+    if constexpr (G > 1) {
+      if (g == 0 && j < rv) lrow[(size_t)j * G] = mx + __logf(sm);
+    }
   } else {
     // element-wise replacement of the softmax (Table 2 ablations)
 #pragma unroll
@@ -232,7 +237,7 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
       for (int u = 0; u < NG; u++)
         // streaming store: the outputs are not read again by this operation
         __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
-                                    reinterpret_cast<u32x2*>(orow + (size_t)j * DV + 16 * (n0 + u) + 4 * g));
+                                    reinterpret_cast<u32x2*>(orow + (size_t)j * (DV * G) + 16 * (n0 + u) + 4 * g));
     }
   }
 }
@@ -244,10 +249,11 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
 // for chunks whose decay product is too small for the factorised chunk form.
 // The state waves' accumulators W are written to LDS, advanced there by all
 // threads, and read back.  Contains workgroup barriers: all threads call it.
-template <int DK, int DV, int M, int ACT>
+// G as in pass_chunk.
+template <int DK, int DV, int M, int ACT, int G>
 __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
                                             const bf16_t* sQ, const bf16_t* sK, const bf16_t* sV,
-                                            bf16_t* __restrict__ orow, int tid) {
+                                            bf16_t* __restrict__ orow, float* __restrict__ lrow, int tid) {
   using Lds = OutLds<DK, DV, M>;
   constexpr int TPS = NT / M;            // threads per slot
   constexpr int KPT = DK / TPS, VPT = DV / TPS;
@@ -298,6 +304,9 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv,
       const float el = lane < M ? __expf(zl - mx) : 0.f;
       const float sm = sum64(el);
       sc = __shfl(el, c, 64) / sm;
+      if constexpr (G > 1) {
+        if (tid == 0) lrow[(size_t)jt * G] = mx + __logf(sm);
+      }
     } else {
       sc = slot_act<ACT>(sZs[c]);
     }
@@ -319,7 +328,7 @@ __device__ __forceinline__ void exact_chunk(StateTiles<DK, DV, M, 4>& W, int rv,
       float o = 0.f;
 #pragma unroll
       for (int w8 = 0; w8 < NW; w8++) o += sOp[w8 * DV + tid];
-      orow[(size_t)jt * DV + tid] = f2bf(o);
+      orow[(size_t)jt * (DV * G) + tid] = f2bf(o);
     }
   }
   (void)SPW;
@@ -360,7 +369,8 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
   const bf16_t* kb = kk + sp.base * DK;
   const bf16_t* vb = vv + sp.base * DV;
-  const bf16_t* gb = gg + sp.base * M + wv * SPT;
+  const bf16_t* gb = gg + gate_base<Seq, M>(sp, unit) + wv * SPT;
+  constexpr int GS = M * Seq::kGroups;  // gate row pitch
 
   StateTiles<DK, DV, M, NW> W;
   W.zero();
@@ -376,7 +386,7 @@ gsa_bf16_state(const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
     const int t0 = ch * C, rv = min(C, T_len - t0);
     pk.load(kb + (size_t)t0 * DK, rv, tid_);
     pv.load(vb + (size_t)t0 * DV, rv, tid_);
-    pg.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
+    pg.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * GS);
   };
   auto stage_chunk = [&](int ch, int b, bool count, int tid_, int lane_) {
     const int rv = min(C, T_len - ch * C);
@@ -474,7 +484,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
              const float* __restrict__ k0, const float* __restrict__ v0,
              const float* __restrict__ ws_state, bf16_t* __restrict__ oo, float* __restrict__ kf,
              float* __restrict__ vf, const float* __restrict__ ws_dec, Seq seq, int S, int P,
-             int units, int fold, float inv_tau) {
+             int units, int fold, float inv_tau, float* __restrict__ lse) {
   using Lds = OutLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   // Every wave computes the next chunk's gate factors of GPW slots (after its
@@ -513,8 +523,11 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
-  const bf16_t* gb = gg + ub * M + slot0;
-  bf16_t* ob = oo + ub * DV;
+  constexpr int G = Seq::kGroups, GS = M * G;  // slot groups, gate row pitch
+  const int grp = unit % G;
+  const bf16_t* gb = gg + gate_base<Seq, M>(sp, unit) + slot0;
+  bf16_t* ob = oo + (ub * G + grp) * DV;
+  float* lb = G > 1 ? lse + ub * G + grp : nullptr;
 
   // Gate logits, one row per owner: loaded at the top of a chunk for the next
   // chunk (after the exact path, if this chunk takes it, has read this
@@ -525,7 +538,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   typedef GateRow<GPW> Row;
   Row gr;
   auto load_gates = [&](Row& r, int t0, int rv, int lane_) {
-    r.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * M);
+    r.load(gb + (size_t)(t0 + min(lane_, rv - 1)) * GS);
   };
   // (the empty asm of pin() keeps the use of the logits, and so the wait for
   // their load, at the call)
@@ -607,14 +620,15 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     bool small;
     if (!slow) {
       if (!is_state) {
-        bf16_t* orow = ob + (size_t)t0 * DV;
+        bf16_t* orow = ob + (size_t)t0 * (DV * G);
+        float* lrow = G > 1 ? lb + (size_t)t0 * G : nullptr;
         // pass waves hold no state: dropping it frees these registers for the passes
         W.zero();
         switch (wv) {
-          case 0: pass_chunk<DK, DV, M, 0, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          case 1: pass_chunk<DK, DV, M, 1, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          case 2: pass_chunk<DK, DV, M, 2, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
-          default: pass_chunk<DK, DV, M, 3, ACT>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, rv); break;
+          case 0: pass_chunk<DK, DV, M, 0, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
+          case 1: pass_chunk<DK, DV, M, 1, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
+          case 2: pass_chunk<DK, DV, M, 2, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
+          default: pass_chunk<DK, DV, M, 3, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
         }
       } else {
         W.carry(sK, Lds::LDQ, sV, Lds::LDV, fZ(b), Lds::LDX, sDec0 + b * M, sw, lane_i);
@@ -625,7 +639,8 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       // ---- exact token recurrence (no division by a decay product), on an
       // fp32 copy of the state in LDS; thread t owns slot t / TPS and 1/TPS of
       // its columns for the whole chunk
-      exact_chunk<DK, DV, M, ACT>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * DV, tid_i);
+      exact_chunk<DK, DV, M, ACT, G>(W, rv, smem, sQ, sK, sV, ob + (size_t)t0 * (DV * G),
+                                     G > 1 ? lb + (size_t)t0 * G : nullptr, tid_i);
       small = factors(gr, rv1, b ^ 1, lane_i);
     }
     slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
@@ -635,6 +650,61 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
 
   if (seg == P - 1 && is_state)
     W.store_kv(kf ? kf + (size_t)unit * M * DK : nullptr, vf ? vf + (size_t)unit * M * DV : nullptr, sw, lane);
+}
+
+// ------------------------------------------------------ slot-group merge
+// The read of 2M slots from the two groups' normalised outputs o_h and
+// log-sum-exps l_h (SlotGroups).  The softmax over all the slots weighs group
+// h by w_h = exp(l_h - L), L = log(exp(l_0) + exp(l_1)), so o = w_0 o_0 +
+// w_1 o_1 (Sec. 3.2, the softmax read); an element-wise read adds the groups.
+// part [rows][2][DV] bf16, lse [rows][2] fp32.  Thread = 8 columns of one
+// token row.  Optional (non-null): L per row (lse_out), and delta = o . dO per
+// row from the fp32 o before rounding (delta, with d_o [rows][DV]).
+template <int DV, bool SOFTMAX>
+__global__ void __launch_bounds__(256)
+gsa_bf16_merge(const bf16_t* __restrict__ part, const float* __restrict__ lse, bf16_t* __restrict__ o,
+               size_t rows, float* __restrict__ lse_out, const bf16_t* __restrict__ d_o,
+               float* __restrict__ delta) {
+  constexpr int TPR = DV / 8;  // threads per row, a power of two dividing a wave
+  static_assert(DV % 8 == 0 && 64 % TPR == 0, "row width");
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / TPR;
+  const int c = (int)(gid % TPR) * 8;
+  if (row >= rows) return;  // whole rows leave together (TPR lanes, aligned)
+  float w0 = 1.f, w1 = 1.f;
+  if constexpr (SOFTMAX) {
+    const float2 l = *reinterpret_cast<const float2*>(lse + 2 * row);
+    const float mx = fmaxf(l.x, l.y);
+    const float e0 = __expf(l.x - mx), e1 = __expf(l.y - mx);
+    const float inv = 1.f / (e0 + e1);
+    w0 = e0 * inv;
+    w1 = e1 * inv;
+    if (lse_out && c == 0) lse_out[row] = mx + __logf(e0 + e1);
+  }
+  const uint4 a = *reinterpret_cast<const uint4*>(part + (2 * row) * DV + c);
+  const uint4 b = *reinterpret_cast<const uint4*>(part + (2 * row + 1) * DV + c);
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    r[2 * i] = w0 * __uint_as_float(aw[i] << 16) + w1 * __uint_as_float(bw[i] << 16);
+    r[2 * i + 1] = w0 * __uint_as_float(aw[i] & 0xffff0000u) + w1 * __uint_as_float(bw[i] & 0xffff0000u);
+  }
+  uint32_t ow[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) ow[i] = (uint32_t)f2bf(r[2 * i]) | ((uint32_t)f2bf(r[2 * i + 1]) << 16);
+  __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, reinterpret_cast<u32x4*>(o + row * DV + c));
+  if (delta) {
+    const uint4 d = *reinterpret_cast<const uint4*>(d_o + row * DV + c);
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      x += r[2 * i] * __uint_as_float(dw[i] << 16) + r[2 * i + 1] * __uint_as_float(dw[i] & 0xffff0000u);
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    if (c == 0) delta[row] = x;
+  }
 }
 
 // ------------------------------------------------------------ launcher
@@ -683,8 +753,37 @@ static int launch(const GsaLaunch& a, const Seq& seq) {
   launch_timed(gsa_bf16_out<DK, DV, M, ACT, Seq>, dim3(P * units), dim3(NT), LO::total, a.stream,
                a.events, 2, 3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                (const bf16_t*)a.g, a.k0, a.v0, (const float*)a.ws_state, (bf16_t*)a.o, a.kf, a.vf,
-               (const float*)a.ws_dec, seq, S, P, units, fold, inv_tau);
+               (const float*)a.ws_dec, seq, S, P, units, fold, inv_tau, a.ws_lse);
   return 0;
+}
+
+// 2M slots as two groups of M (SlotGroups): the group launches over 2BH units
+// (a.chunks_per_seg and the workspace sized for them), then the merge.
+template <int DK, int DV, int M, int ACT>
+static int launch_groups(const GsaLaunch& a) {
+  GsaLaunch b = a;
+  b.H = 2 * a.H;
+  b.o = a.ws_part;
+  if (launch<DK, DV, M, ACT, SlotGroups>(b, SlotGroups{a.T}) != 0) return -1;
+  const size_t rows = (size_t)a.B * a.H * a.T;
+  const size_t threads = rows * (DV / 8);
+  hipLaunchKernelGGL((gsa_bf16_merge<DV, ACT == kActSoftmax>), dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, (hipStream_t)a.stream, (const bf16_t*)a.ws_part, (const float*)a.ws_lse,
+                     (bf16_t*)a.o, rows, nullptr, nullptr, nullptr);
+  return 0;
+}
+
+template <int DK, int DV, int M>
+static int launch_act_groups(const GsaLaunch& a) {
+  if (a.cu_seqlens || !a.ws_part || !a.ws_lse) return -1;
+  switch (a.act) {
+    case kActSoftmax: return launch_groups<DK, DV, M, kActSoftmax>(a);
+    case kActIdentity: return launch_groups<DK, DV, M, kActIdentity>(a);
+    case kActSwish: return launch_groups<DK, DV, M, kActSwish>(a);
+    case kActRelu: return launch_groups<DK, DV, M, kActRelu>(a);
+    case kActRelu2: return launch_groups<DK, DV, M, kActRelu2>(a);
+    default: return -1;
+  }
 }
 
 template <int DK, int DV, int M>
@@ -800,8 +899,17 @@ int gsa_bf16_segment_states(int dk, int dv, int m, const void* k, const void* v,
     return bfk::launch_act<DKC, DVC, MC>(*a);                             \
   }
 
+// m = 2M as two slot groups of M (slot_groups(1, m) == 2)
+#define GSA_BF16_GROUPS_CASE(DKC, DVC, MC)                                \
+  if (dk == DKC && dv == DVC && m == 2 * MC) {                            \
+    if (query) return bfk::OutLds<DKC, DVC, MC>::total;                   \
+    return bfk::launch_act_groups<DKC, DVC, MC>(*a);                      \
+  }
+
 // Returns: query -> LDS bytes (>0) or -1 if unsupported; launch -> 0 or -1.
 int gsa_dispatch_bf16(int dk, int dv, int m, const GsaLaunch* a, bool query) {
+  GSA_BF16_GROUPS_CASE(128, 128, 64)
+  GSA_BF16_GROUPS_CASE(64, 64, 64)
   GSA_BF16_CASE(128, 128, 64)
   GSA_BF16_CASE(128, 128, 32)
   GSA_BF16_CASE(64, 64, 64)

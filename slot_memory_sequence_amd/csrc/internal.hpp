@@ -23,9 +23,18 @@ struct GsaLaunch {
   // cu_seqlens == nullptr: the dense [B, H, T, d] batch.
   const int* cu_seqlens;
   int n_seqs;
+  // two slot groups (slot_groups(dtype, m) == 2, dense batches only): the
+  // groups' output rows [B*H*T][2][dv] (I/O dtype) and log-sum-exps
+  // [B*H*T][2] fp32, in the workspace after the segment maps
+  void* ws_part;
+  float* ws_lse;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gsa_fwd_events
 };
+
+// Slot groups a GSA call with m slots runs as: 2 for bf16 at m = 128 (two
+// groups of 64 merged by the read's log-sum-exp), else 1.
+inline int slot_groups(int dtype, int m) { return dtype == 1 && m == 128 ? 2 : 1; }
 
 struct GlaLaunch {
   const void *q, *k, *v, *g;

@@ -47,6 +47,10 @@ def test_supported_sets(gsa):
     assert gsa.gla_fwd_supported(128, 128, 64, 1)
     assert gsa.gsa_decode_supported(128, 128, 64, 1)
     assert not gsa.gsa_decode_supported(96, 128, 64, 1)
+    # 128 slots: bf16 forward (two slot groups) and decode; not float32 at d 128
+    assert gsa.gsa_fwd_supported(128, 128, 128, 64, 1) and gsa.gsa_fwd_supported(64, 64, 128, 64, 1)
+    assert not gsa.gsa_fwd_supported(128, 128, 128, 64, 0)
+    assert gsa.gsa_decode_supported(128, 128, 128, 1) and gsa.gsa_decode_supported(128, 128, 128, 0)
 
 
 def test_workspace_query(gsa):
@@ -57,6 +61,16 @@ def test_workspace_query(gsa):
     state = 32 * P * 64 * 256 * 4
     assert nb == ((state + 255) // 256) * 256 + 32 * P * 64 * 4
     assert gsa.gsa_fwd_workspace_bytes(-1, 4, 16, 128, 128, 64, 64, 1, 0) == (1 << 64) - 1
+    # m = 128 in bf16: 64 slot-group units (default split: 4 segments of 8
+    # chunks each), then the groups' output rows [B*H*T][2][dv] bf16 and
+    # log-sum-exps [B*H*T][2] fp32, each 256-byte aligned
+    a256 = lambda x: (x + 255) // 256 * 256
+    rows, P2 = 32 * 2048, 4
+    maps = a256(64 * P2 * 64 * 256 * 4) + 64 * P2 * 64 * 4
+    assert gsa.gsa_fwd_workspace_bytes(8, 4, 2048, 128, 128, 128, 64, 1, 0) == \
+        a256(a256(maps) + rows * 2 * 128 * 2) + rows * 2 * 4
+    # one chunk: no segment maps, the group rows only
+    assert gsa.gsa_fwd_workspace_bytes(1, 1, 64, 128, 128, 128, 64, 1, 0) == a256(64 * 2 * 128 * 2) + 64 * 2 * 4
     assert gsa.gla_fwd_workspace_bytes(8, 16, 4096, 128, 128, 64, 1, 0) > 0
     # bf16 GLA: 64 units, 2 output segments, each split into 4 state-map
     # sub-segments -> max(P, (P-1)*4) = 4 slots per unit; fp32 keeps P = 2
