@@ -327,9 +327,14 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
  * No output may overlap an input, the workspace or another output
  * (GSA_ERR_ALIAS).  B * H <= 65535 and T <= 65535 * 64 (else
  * GSA_ERR_UNSUPPORTED).  Compiled for (dk = dv, m) in {(128, 64),
- * (128, 32), (64, 64), (64, 32)}, float32 and bf16 (gsa_bwd_supported).
- * events: NULL or 4 hipEvent_t: [0, 1] stamp the forward token-walk kernel's
- * dispatch, [2, 3] the reverse token-walk kernel's.
+ * (128, 32), (64, 64), (64, 32)}, float32 and bf16 (gsa_bwd_supported), and
+ * in bf16 for d in {64, 128} with m = 128 on dense batches and every read but
+ * ReLU (GSA_ERR_UNSUPPORTED for the packed batch or the ReLU read there): the
+ * slots run as two groups of 64 like gsa_fwd's, for the softmax read after a
+ * statistics pass that merges the groups' log-sum-exps and sums of s ds per
+ * token, and the groups' fp32 parts of d_q, d_k, d_v are added at the end.
+ * events: NULL or 4 hipEvent_t: [0, 1] stamp the forward sweep kernel's
+ * dispatch, [2, 3] the reverse sweep kernel's.
  * Asynchronous on stream; status as for gsa_fwd.
  */
 int gsa_bwd_supported(int dk, int dv, int m, int dtype);
@@ -337,7 +342,9 @@ int gsa_bwd_supported(int dk, int dv, int m, int dtype);
  * gsa_slot_nonlinearity code; 0 on invalid arguments or T = 0).  bf16 with
  * any read but ReLU runs the chunk form on the matrix cores and keeps
  * per-segment states, reverse maps and bf16 per-token read weights (59 MB at
- * B8 H4 T2048 d128 m64); float32, and bf16 with the ReLU read (whose
+ * B8 H4 T2048 d128 m64; with m = 128 those of the two slot groups plus the
+ * merge statistics and the groups' fp32 gradient parts, 6 * 4 * 2 * d + 24
+ * bytes per token); float32, and bf16 with the ReLU read (whose
  * derivative, a step at 0, needs fp32 scores), run fp32 token walks that
  * keep per-chunk states and five fp32 per-token arrays. */
 size_t gsa_bwd_workspace_bytes_ex(int B, int H, int T, int dk, int dv, int m, int dtype,

@@ -505,6 +505,8 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
                    void* workspace, size_t workspace_bytes, int nonlinearity, void* stream,
                    void* const* events) {
   if (!gsa_bwd_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
+  // two slot groups (bf16, m = 128): dense batches and the smooth reads only
+  if (gsa::slot_groups(dtype, m) > 1 && (cu || nonlinearity == GSA_SLOT_RELU)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
   if (units == 0) return GSA_OK;
   // one grid row per unit of a launch sequence (a packed batch launches groups)

@@ -877,6 +877,20 @@ size_t gsa_bwd_need_bytes(int dtype, int act, bool packed, size_t units, size_t 
     return query ? 0 : bwd::launch_act<TY, DK_, DV_, M_>(*a);
 
 int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bool query) {
+  // 128 slots: bf16 dense batches on the matrix cores as two slot groups (not
+  // the ReLU read, not packed batches: the caller rejects those)
+  if (slot_groups(dtype, m) == 2 && dk == dv && (dk == 128 || dk == 64)) {
+    if (query) return 0;
+    if (a->cu_seqlens || a->act == kActRelu) return -1;
+    if (a->T == 0) {
+      const size_t MK = (size_t)a->H * m * dk, MV = (size_t)a->H * m * dv;
+      state_copy(a->dk0, a->dkf, (size_t)a->B * MK, a->stream);
+      state_copy(a->dv0, a->dvf, (size_t)a->B * MV, a->stream);
+      for (int e = 0; e < 4; e++) record_event(a->events, e, a->stream);
+      return 0;
+    }
+    return gsa_bwd_bf16_dispatch(dk, dv, m, a, false, (size_t)a->B * a->H, a->T) == 0 ? 0 : -1;
+  }
   GSA_BWD_CASE(bf16_t, 1, 128, 128, 64)
   GSA_BWD_CASE(bf16_t, 1, 64, 64, 32)
   GSA_BWD_CASE(bf16_t, 1, 128, 128, 32)

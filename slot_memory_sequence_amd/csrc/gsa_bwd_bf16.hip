@@ -167,6 +167,23 @@ __device__ __forceinline__ float4 ld_bf16x4(const bf16_t* p) {
                      __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
 
+// Gradient rows of q, k, v: bf16 for one slot group; fp32 partials when the
+// slots run as G > 1 groups (the groups' parts of dq and dk are sums over
+// their own slots only and may nearly cancel, so they keep full precision
+// until they are added).
+template <int G>
+using GradT = typename std::conditional<(G > 1), float, bf16_t>::type;
+__device__ __forceinline__ void st_grad4(bf16_t* p, const f32x4& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(v)), reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_grad4(float* p, const f32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st_grad4(bf16_t* p, float a, float b, float c, float d) { store_bf16x4(p, a, b, c, d); }
+__device__ __forceinline__ void st_grad4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
 // A [C][D] bf16 chunk tile moved as 16-byte vectors by the NTH threads
 // 0 .. NTH-1 (the pass waves alone in the forward sweep, so that the state
 // waves hold no prefetch registers beside their two accumulator sets).  Rows
@@ -200,11 +217,19 @@ struct TileN {
 // 16J+15.  z and ds, the slot read, dz and h; s, dz and h to the per-token
 // workspace (rows < rv); s*E*D and dz*E*D rows to LDS for the reverse map;
 // (dz*E)^T as operands for the second half.
-template <int DK, int DV, int M, int J, int ACT>
+// G > 1 (one of G groups of M slots): the softmax read takes each token's
+// log-sum-exp over all the slots (lse_rows) and delta = sum over all slots of
+// s ds (dl_rows), so s = exp(z - lse) and dz = s (ds - delta).  STATS: only
+// the group's own softmax statistics of each token, its log-sum-exp and the
+// sum of s ds under its own softmax, to stat_rows[j * 2G + 0 / 1] (the pass
+// that the merged lse and delta come from: the same z and ds as the pass that
+// takes them, so that dz sums to zero over the slots).
+template <int DK, int DV, int M, int J, int ACT, int G, bool STATS>
 __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, bf16_t* sS, bf16_t* sDZ,
                                           const float* sSeg, bf16_t* __restrict__ s_rows,
                                           bf16_t* __restrict__ dz_rows, bf16_t* __restrict__ h_rows,
-                                          int rv, bf16x8 (&dzb)[M / 32]) {
+                                          const float* __restrict__ lse_rows, const float* __restrict__ dl_rows,
+                                          float* __restrict__ stat_rows, int rv, bf16x8 (&dzb)[M / 32]) {
   using Lds = BwdLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, KV = DV / 32, NP = M / 32;
   constexpr int NR = J + 1, NPR = J / 2 + 1;
@@ -280,7 +305,17 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
 
   // the slot read of token j (over (ct, i) in-lane and the four lane groups)
   f32x4 s[MT], dz[MT];
-  if constexpr (ACT == kActSoftmax) {
+  if constexpr (ACT == kActSoftmax && G > 1 && !STATS) {
+    const bool ok = j < rv;
+    const float lj = ok ? lse_rows[j] : 0.f, db = ok ? dl_rows[j] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        s[ct][i] = __builtin_amdgcn_exp2f((z[ct][i] - lj) * 1.4426950408889634f);
+        dz[ct][i] = s[ct][i] * (ds[ct][i] - db);
+      }
+  } else if constexpr (ACT == kActSoftmax) {
     float mx = z[0][0];
 #pragma unroll
     for (int ct = 0; ct < MT; ct++)
@@ -295,7 +330,8 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
         s[ct][i] = __builtin_amdgcn_exp2f((z[ct][i] - mx) * 1.4426950408889634f);
         sm += s[ct][i];
       }
-    const float inv = 1.f / group4_sum(sm);
+    const float smt = group4_sum(sm);
+    const float inv = 1.f / smt;
     float db = 0.f;
 #pragma unroll
     for (int ct = 0; ct < MT; ct++)
@@ -305,6 +341,13 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
         db += s[ct][i] * ds[ct][i];
       }
     db = group4_sum(db);
+    if constexpr (STATS) {
+      if (g == 0 && j < rv) {
+        stat_rows[(size_t)j * (2 * G)] = mx + __logf(smt);
+        stat_rows[(size_t)j * (2 * G) + 1] = db;
+      }
+      return;
+    }
 #pragma unroll
     for (int ct = 0; ct < MT; ct++)
 #pragma unroll
@@ -352,9 +395,9 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
 
 // Pass waves, second half: dq^T[n][j] = sum_c Wk[c][n] (dz*E)[j][c] +
 // sum_{r<=j} K[r][n] A3^T[r][j], A3^T[r][j] = sum_c X[r][c] (dz*E)[j][c].
-template <int DK, int DV, int M, int J>
+template <int DK, int DV, int M, int J, int G>
 __device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, const bf16x8 (&dzb)[M / 32],
-                                          bf16_t* __restrict__ dq_rows, int rv) {
+                                          GradT<G>* __restrict__ dq_rows, int rv) {
   using Lds = BwdLds<DK, DV, M>;
   constexpr int NP = M / 32, NKT = DK / 16;
   constexpr int NR = J + 1, NPR = J / 2 + 1;
@@ -399,8 +442,7 @@ __device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, c
     if (store) {
 #pragma unroll
       for (int u = 0; u < NG; u++)
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
-                                    reinterpret_cast<u32x2*>(dq_rows + (size_t)j * DK + 16 * (n0 + u) + 4 * g));
+        st_grad4(dq_rows + (size_t)j * (DK * G) + 16 * (n0 + u) + 4 * g, acc[u]);
     }
   }
 }
@@ -416,9 +458,9 @@ __device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, c
 // (over X, Z), the reductions over E.  Two workgroup barriers per token in
 // both halves (fwd_exact_state for the state waves, fwd_exact_pass for the
 // others).
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int G, bool STATS>
 __device__ __forceinline__ void fwd_exact_state(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
-                                                bf16_t* __restrict__ dq_rows, int lane, int sw) {
+                                                GradT<G>* __restrict__ dq_rows, int lane, int sw) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   constexpr int MT = M / 16, NCW = ST::NCW;
@@ -464,7 +506,7 @@ __device__ __forceinline__ void fwd_exact_state(StateTiles<DK, DV, M, 4>& W, int
     }
     __syncthreads();  // the token's scores are in LDS
     __syncthreads();  // its read weights are in LDS
-    if (khalf) {      // dq of token jt over this wave's Kt columns
+    if (!STATS && khalf) {  // dq of token jt over this wave's Kt columns
       float dz[MT];
 #pragma unroll
       for (int ct = 0; ct < MT; ct++) dz[ct] = rDZ[16 * ct + L];
@@ -478,16 +520,18 @@ __device__ __forceinline__ void fwd_exact_state(StateTiles<DK, DV, M, 4>& W, int
           for (int ct = 0; ct < MT; ct++) acc += W.st[n][ct][i] * dz[ct];
           x[i] = row_sum16(acc);
         }
-        if (L == 0) store_bf16x4(dq_rows + (size_t)jt * DK + W.col(sw, n, lane), x[0], x[1], x[2], x[3]);
+        if (L == 0) st_grad4(dq_rows + (size_t)jt * (DK * G) + W.col(sw, n, lane), x[0], x[1], x[2], x[3]);
       }
     }
   }
 }
 
-template <int DK, int DV, int M, int ACT>
+template <int DK, int DV, int M, int ACT, int G, bool STATS>
 __device__ __forceinline__ void fwd_exact_pass(int rv, unsigned char* smem, const float* sSeg,
                                                bf16_t* __restrict__ s_rows, bf16_t* __restrict__ dz_rows,
-                                               bf16_t* __restrict__ h_rows, int lane, int wv) {
+                                               bf16_t* __restrict__ h_rows, const float* __restrict__ lse_rows,
+                                               const float* __restrict__ dl_rows, float* __restrict__ stat_rows,
+                                               int lane, int wv) {
   using Lds = BwdLds<DK, DV, M>;
   const float* sLa = reinterpret_cast<const float*>(smem + Lds::oX);
   const float* part = reinterpret_cast<const float*>(smem + Lds::oE);
@@ -508,17 +552,27 @@ __device__ __forceinline__ void fwd_exact_pass(int rv, unsigned char* smem, cons
       const float z = on ? part[lane] + part[M + lane] : 0.f;
       const float ds = on ? part[2 * M + lane] + part[3 * M + lane] : 0.f;
       float s, dz;
-      if constexpr (ACT == kActSoftmax) {
+      if constexpr (ACT == kActSoftmax && G > 1 && !STATS) {
+        s = on ? __expf(z - lse_rows[jt]) : 0.f;
+        dz = s * (ds - dl_rows[jt]);
+      } else if constexpr (ACT == kActSoftmax) {
         const float mx = wave_max(on ? z : -INFINITY);
         const float e = on ? __expf(z - mx) : 0.f;
-        s = e / sum64(e);
+        const float smt = sum64(e);
+        s = e / smt;
         const float db = sum64(s * ds);
         dz = s * (ds - db);
+        if constexpr (STATS) {
+          if (lane == 0) {
+            stat_rows[(size_t)jt * (2 * G)] = mx + __logf(smt);
+            stat_rows[(size_t)jt * (2 * G) + 1] = db;
+          }
+        }
       } else {
         s = slot_act<ACT>(z);
         dz = slot_act_grad<ACT>(z) * ds;
       }
-      if (on) {
+      if (!STATS && on) {
         eseg *= __expf(sLa[jt * M + lane]);
         rDZ[lane] = dz;
         s_rows[(size_t)jt * M + lane] = f2bf(s);
@@ -536,13 +590,21 @@ __device__ __forceinline__ void fwd_exact_pass(int rv, unsigned char* smem, cons
 // separate loops (so that neither holds the other's registers) with the same
 // sequence of workgroup barriers: A (chunk staged), M (reverse-map operands
 // written), B (chunk done); an exact chunk replaces M by its per-token ones.
-template <int DK, int DV, int M, int ACT>
+// G slot groups (G > 1: unit 2u + h is group h of (b, h) unit u, as in the
+// forward's SlotGroups: q, k, v, dO rows of unit u; gate columns hM .. hM +
+// M - 1 of g rows of pitch G M; dq rows [rows][G][DK], one partial per group;
+// the per-token workspace rows are the group unit's own).
+// STATS (with G > 1, the softmax read): the statistics pass of fwd_pass1 only
+// (the state carried as usual; no dq, workspace rows, reverse maps or end
+// states: the segment start states stay for the pass that follows).
+template <int DK, int DV, int M, int ACT, int G, bool STATS>
 __global__ void __launch_bounds__(NT, 1)
 bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
              const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, float* __restrict__ st,
-             float* __restrict__ rm, float* __restrict__ rdec, bf16_t* __restrict__ dq,
+             float* __restrict__ rm, float* __restrict__ rdec, GradT<G>* __restrict__ dq,
              bf16_t* __restrict__ s_ws, bf16_t* __restrict__ dz_ws, bf16_t* __restrict__ h_ws, int T, int S,
-             int P, float inv_tau) {
+             int P, float inv_tau, const float* __restrict__ lse, const float* __restrict__ delta,
+             float* __restrict__ stats) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   constexpr int GPW = M / NW;
@@ -571,12 +633,15 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   const int seg = blockIdx.x % P, unit = blockIdx.x / P;
   const int nchunks = (T + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
-  const size_t ub = (size_t)unit * T;
+  constexpr int GS = M * G;                                 // gate row pitch
+  const int grp = unit % G;
+  const size_t ub = (size_t)(unit / G) * T, wb = (size_t)unit * T;  // token rows, workspace rows
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
   const bf16_t* db = dOo + ub * DV;
-  const bf16_t* gb = gg + ub * M + slot0;
+  const bf16_t* gb = gg + ub * GS + grp * M + slot0;
+  GradT<G>* dqb = dq + (ub * G + grp) * DK;
   float* stp = st + ((size_t)unit * P + seg) * NE;
   float* rmp = rm + ((size_t)unit * P + seg) * NE;
   auto rows_of = [&](int ch) { return min(C, T - ch * C); };
@@ -594,7 +659,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     pd.load(db + (size_t)t0 * DV, rv, tid_);
   };
   auto load_gates = [&](int ch, int lane_) {
-    gr.load(gb + (size_t)(ch * C + min(lane_, rows_of(ch) - 1)) * M);
+    gr.load(gb + (size_t)(ch * C + min(lane_, rows_of(ch) - 1)) * GS);
   };
   // stage chunk ch (the pass waves its tiles, every wave its factors),
   // barrier A, log alpha for an exact chunk, the loads of the next chunk
@@ -642,16 +707,18 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
         __syncthreads();  // M: the reverse-map operands are in LDS
       } else {
         __syncthreads();  // log alpha is in LDS
-        fwd_exact_state<DK, DV, M>(W, rv, smem, dq + (ub + ch * C) * DK, lane_i, sw);
+        fwd_exact_state<DK, DV, M, G, STATS>(W, rv, smem, dqb + (size_t)ch * C * (DK * G), lane_i, sw);
       }
       // the chunk's reverse map (operand rows from the passes or the walk)
-      R.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, nullptr, sw, lane_i);
+      if constexpr (!STATS) R.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, nullptr, sw, lane_i);
       __syncthreads();  // B: every reader of this chunk's tiles, factors and copies is done
     }
     // the segment's end state over its start state (only this workgroup reads
     // that slot), its reverse map beside it
-    W.store_w(stp, sw, lane);
-    R.store_w(rmp, sw, lane);
+    if constexpr (!STATS) {
+      W.store_w(stp, sw, lane);
+      R.store_w(rmp, sw, lane);
+    }
   } else {
     load_tiles(c_begin, tid);
     bf16x8 dzb[NP];
@@ -660,37 +727,41 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       asm volatile("" : "+v"(lane_i), "+v"(tid_i));
       const int t0 = ch * C, rv = rows_of(ch);
       const bool slow = stage(Pass{}, ch, ch - c_begin, lane_i, tid_i);
-      bf16_t* srow = s_ws + (ub + t0) * M;
-      bf16_t* dzrow = dz_ws + (ub + t0) * M;
-      bf16_t* hrow = h_ws + (ub + t0) * M;
+      bf16_t* srow = s_ws + (wb + t0) * M;
+      bf16_t* dzrow = dz_ws + (wb + t0) * M;
+      bf16_t* hrow = h_ws + (wb + t0) * M;
+      const float* lrow = G > 1 && !STATS ? lse + ub + t0 : nullptr;
+      const float* drow = G > 1 && !STATS ? delta + ub + t0 : nullptr;
+      float* strow = STATS ? stats + ((ub + t0) * G + grp) * 2 : nullptr;
       if (!slow) {
         switch (wv) {
-          case 0: fwd_pass1<DK, DV, M, 0, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
-          case 1: fwd_pass1<DK, DV, M, 1, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
-          case 2: fwd_pass1<DK, DV, M, 2, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
-          default: fwd_pass1<DK, DV, M, 3, ACT>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, rv, dzb); break;
+          case 0: fwd_pass1<DK, DV, M, 0, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
+          case 1: fwd_pass1<DK, DV, M, 1, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
+          case 2: fwd_pass1<DK, DV, M, 2, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
+          default: fwd_pass1<DK, DV, M, 3, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
         }
         __syncthreads();  // M
         // the decay from the segment start, advanced past this chunk (its
         // readers are all before M; E_C is rewritten only after B)
         if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];
-        bf16_t* dqrow = dq + (ub + t0) * DK;
+        GradT<G>* dqrow = dqb + (size_t)t0 * (DK * G);
+        if constexpr (!STATS)
         switch (wv) {
-          case 0: fwd_pass2<DK, DV, M, 0>(lane_i, smem, dzb, dqrow, rv); break;
-          case 1: fwd_pass2<DK, DV, M, 1>(lane_i, smem, dzb, dqrow, rv); break;
-          case 2: fwd_pass2<DK, DV, M, 2>(lane_i, smem, dzb, dqrow, rv); break;
-          default: fwd_pass2<DK, DV, M, 3>(lane_i, smem, dzb, dqrow, rv); break;
+          case 0: fwd_pass2<DK, DV, M, 0, G>(lane_i, smem, dzb, dqrow, rv); break;
+          case 1: fwd_pass2<DK, DV, M, 1, G>(lane_i, smem, dzb, dqrow, rv); break;
+          case 2: fwd_pass2<DK, DV, M, 2, G>(lane_i, smem, dzb, dqrow, rv); break;
+          default: fwd_pass2<DK, DV, M, 3, G>(lane_i, smem, dzb, dqrow, rv); break;
         }
       } else {
         __syncthreads();  // log alpha is in LDS
-        fwd_exact_pass<DK, DV, M, ACT>(rv, smem, sSeg, srow, dzrow, hrow, lane_i, wv);
+        fwd_exact_pass<DK, DV, M, ACT, G, STATS>(rv, smem, sSeg, srow, dzrow, hrow, lrow, drow, strow, lane_i, wv);
         if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];  // read by the walk before its first barrier
       }
       __syncthreads();  // B
     }
   }
   __syncthreads();
-  if (tid < M) rdec[((size_t)unit * P + seg) * M + tid] = sSeg[tid];
+  if (!STATS && tid < M) rdec[((size_t)unit * P + seg) * M + tid] = sSeg[tid];
 }
 
 // ======================================================== reverse scan
@@ -752,10 +823,10 @@ bwd_bf16_rscan(float* __restrict__ rm, const float* __restrict__ rdec, const flo
 // over the wave's rows from j on (pre), the wave's total per slot (sWt[J]).
 // The rest (later waves' totals and the carry from later chunks) is added
 // after the next barrier by rev_pass_finish.
-template <int DK, int DV, int M, int J>
+template <int DK, int DV, int M, int J, int G>
 __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, float* sWt,
                                          const bf16_t* __restrict__ h_rows, const bf16_t* __restrict__ g_rows,
-                                         bf16_t* __restrict__ dk_rows, bf16_t* __restrict__ dv_rows, int rv,
+                                         GradT<G>* __restrict__ dk_rows, GradT<G>* __restrict__ dv_rows, int rv,
                                          float inv_tau, float (&pre)[M / 16][4], float (&sn)[M / 16][4]) {
   using Lds = BwdLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, KV = DV / 32, NP = M / 32, NKT = DK / 16, NVT = DV / 16;
@@ -781,7 +852,7 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
 #pragma unroll
   for (int ct = 0; ct < MT; ct++) {
     hv[ct] = ld_bf16x4(h_rows + (size_t)jr * M + 16 * ct + 4 * g);
-    gv[ct] = ld_bf16x4(g_rows + (size_t)jr * M + 16 * ct + 4 * g);
+    gv[ct] = ld_bf16x4(g_rows + (size_t)jr * (M * G) + 16 * ct + 4 * g);
   }
 
   bf16x8 kf[KQ], vf[KV];
@@ -859,9 +930,8 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
     if (valid) {
 #pragma unroll
       for (int u = 0; u < NG; u++) {
-        bf16_t* dst = kpart ? dk_rows + (size_t)j * DK : dv_rows + (size_t)j * DV;
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x2, pack4(acc[u])),
-                                    reinterpret_cast<u32x2*>(dst + 16 * (nb + u) + 4 * g));
+        GradT<G>* dst = kpart ? dk_rows + (size_t)j * (DK * G) : dv_rows + (size_t)j * (DV * G);
+        st_grad4(dst + 16 * (nb + u) + 4 * g, acc[u]);
       }
     }
   }
@@ -923,7 +993,7 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
 // After the barrier that publishes every wave's totals: d log alpha = pre +
 // the totals of the later waves of this chunk + the carry from later chunks;
 // dg = that * sigmoid(-g) / tau.
-template <int M, int J>
+template <int M, int J, int G>
 __device__ __forceinline__ void rev_pass_finish(int lane, const float* sWt, const float* carry,
                                                 bf16_t* __restrict__ dg_rows, int rv,
                                                 const float (&pre)[M / 16][4], const float (&sn)[M / 16][4]) {
@@ -939,7 +1009,7 @@ __device__ __forceinline__ void rev_pass_finish(int lane, const float* sWt, cons
       add.x += t.x; add.y += t.y; add.z += t.z; add.w += t.w;
     }
     if (j < rv)
-      store_bf16x4(dg_rows + (size_t)j * M + c, (pre[ct][0] + add.x) * sn[ct][0], (pre[ct][1] + add.y) * sn[ct][1],
+      store_bf16x4(dg_rows + (size_t)j * (M * G) + c, (pre[ct][0] + add.x) * sn[ct][0], (pre[ct][1] + add.y) * sn[ct][1],
                    (pre[ct][2] + add.z) * sn[ct][2], (pre[ct][3] + add.w) * sn[ct][3]);
   }
 }
@@ -951,11 +1021,11 @@ __device__ __forceinline__ void rev_pass_finish(int lane, const float* sWt, cons
 // return the state waves' accumulators hold the adjoint at the chunk start
 // and sWt[0] the chunk's total of the gate terms (sWt[1..3] = 0).  One
 // workgroup barrier per token in both halves.
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int G>
 __device__ __forceinline__ void rev_exact_state(StateTiles<DK, DV, M, 4>& W, int rv, unsigned char* smem,
                                                 const bf16_t* __restrict__ s_rows,
-                                                const bf16_t* __restrict__ dz_rows, bf16_t* __restrict__ dk_rows,
-                                                bf16_t* __restrict__ dv_rows, int lane, int sw) {
+                                                const bf16_t* __restrict__ dz_rows, GradT<G>* __restrict__ dk_rows,
+                                                GradT<G>* __restrict__ dv_rows, int lane, int sw) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   constexpr int MT = M / 16, NCW = ST::NCW;
@@ -999,8 +1069,8 @@ __device__ __forceinline__ void rev_exact_state(StateTiles<DK, DV, M, 4>& W, int
         x[i] = row_sum16(acc);
       }
       if (L == 0) {
-        bf16_t* dst = khalf ? dk_rows + (size_t)jt * DK + c0 : dv_rows + (size_t)jt * DV + c0 - DK;
-        store_bf16x4(dst, x[0], x[1], x[2], x[3]);
+        GradT<G>* dst = khalf ? dk_rows + (size_t)jt * (DK * G) + c0 : dv_rows + (size_t)jt * (DV * G) + c0 - DK;
+        st_grad4(dst, x[0], x[1], x[2], x[3]);
       }
 #pragma unroll
       for (int i = 0; i < 4; i++)
@@ -1017,7 +1087,7 @@ __device__ __forceinline__ void rev_exact_state(StateTiles<DK, DV, M, 4>& W, int
   }
 }
 
-template <int M>
+template <int M, int G>
 __device__ __forceinline__ void rev_exact_pass(int rv, const unsigned char* smem, int oS, const float* carry,
                                                float* sWt, const bf16_t* __restrict__ h_rows,
                                                const bf16_t* __restrict__ g_rows, bf16_t* __restrict__ dg_rows,
@@ -1030,9 +1100,9 @@ __device__ __forceinline__ void rev_exact_pass(int rv, const unsigned char* smem
       const float* dp = dpart + (n & 1) * 4 * M;
       const float d = dp[lane] + dp[M + lane] + dp[2 * M + lane] + dp[3 * M + lane];
       float a, w, sn;
-      gate_terms(bf2f(g_rows[(size_t)jt * M + lane]), inv_tau, a, w, sn);
+      gate_terms(bf2f(g_rows[(size_t)jt * (M * G) + lane]), inv_tau, a, w, sn);
       run += bf2f(h_rows[(size_t)jt * M + lane]) - w * d;
-      dg_rows[(size_t)jt * M + lane] = f2bf((run + carry[lane] - a * d) * sn);
+      dg_rows[(size_t)jt * (M * G) + lane] = f2bf((run + carry[lane] - a * d) * sn);
     }
   }
   if (wv == 0 && lane < M) {
@@ -1045,12 +1115,12 @@ __device__ __forceinline__ void rev_exact_pass(int rv, const unsigned char* smem
 // forward sweep the two roles run separate loops with the same barriers: A
 // (chunk staged), B (chunk done, its gate totals published); an exact chunk
 // adds one barrier per token.
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int G>
 __global__ void __launch_bounds__(NT, 1)
 bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
              const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, const float* __restrict__ st,
              const float* __restrict__ rm, const bf16_t* __restrict__ s_ws, const bf16_t* __restrict__ dz_ws,
-             const bf16_t* __restrict__ h_ws, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv,
+             const bf16_t* __restrict__ h_ws, GradT<G>* __restrict__ dk, GradT<G>* __restrict__ dv,
              bf16_t* __restrict__ dg, int T, int S, int P, float inv_tau) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
@@ -1081,11 +1151,17 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   const int seg = blockIdx.x % P, unit = blockIdx.x / P;
   const int nchunks = (T + C - 1) / C;
   const int c_begin = seg * S, c_end = min(c_begin + S, nchunks);
-  const size_t ub = (size_t)unit * T;
+  constexpr int GS = M * G;  // gate row pitch (slot groups as in bwd_bf16_fwd)
+  const int grp = unit % G;
+  const size_t ub = (size_t)(unit / G) * T, wb = (size_t)unit * T;
   const bf16_t* qb = qq + ub * DK;
   const bf16_t* kb = kk + ub * DK;
   const bf16_t* vb = vv + ub * DV;
   const bf16_t* db = dOo + ub * DV;
+  const bf16_t* gb = gg + ub * GS + grp * M;
+  GradT<G>* dkb = dk + (ub * G + grp) * DK;
+  GradT<G>* dvb = dv + (ub * G + grp) * DV;
+  bf16_t* dgb = dg + ub * GS + grp * M;
   auto rows_of = [&](int ch) { return min(C, T - ch * C); };
 
   typedef GateRow<GPW> Row;
@@ -1098,10 +1174,10 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     pk.load(kb + (size_t)t0 * DK, rv, tid_);
     pv.load(vb + (size_t)t0 * DV, rv, tid_);
     pd.load(db + (size_t)t0 * DV, rv, tid_);
-    const size_t r = (ub + t0 + min(lane_, rv - 1)) * M + slot0;
-    gr.load(gg + r);
-    sr.load(s_ws + r);
-    zr.load(dz_ws + r);
+    const size_t tr = t0 + min(lane_, rv - 1);
+    gr.load(gb + tr * GS + slot0);
+    sr.load(s_ws + (wb + tr) * M + slot0);
+    zr.load(dz_ws + (wb + tr) * M + slot0);
   };
   // stage chunk ch: tiles, factors, s*E and dz*E (zero past the end); barrier
   // A; log alpha for an exact chunk; the loads of the chunk before
@@ -1172,8 +1248,8 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
         W.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sw, lane_i);
       } else {
         __syncthreads();  // log alpha is in LDS
-        rev_exact_state<DK, DV, M>(W, rv, smem, s_ws + (ub + t0) * M, dz_ws + (ub + t0) * M,
-                                   dk + (ub + t0) * DK, dv + (ub + t0) * DV, lane_i, sw);
+        rev_exact_state<DK, DV, M, G>(W, rv, smem, s_ws + (wb + t0) * M, dz_ws + (wb + t0) * M,
+                                      dkb + (size_t)t0 * (DK * G), dvb + (size_t)t0 * (DV * G), lane_i, sw);
       }
       __syncthreads();  // B
       if (sw == 0 && lane_i < M) {  // the carry into the chunk before
@@ -1191,29 +1267,29 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       const int t0 = ch * C, rv = rows_of(ch);
       const float* carry = sCarry + (it & 1) * M;
       const bool slow = stage(ch, it, lane_i, tid_i);
-      const bf16_t* hrow = h_ws + (ub + t0) * M;
-      const bf16_t* grow = gg + (ub + t0) * M;
-      bf16_t* dkrow = dk + (ub + t0) * DK;
-      bf16_t* dvrow = dv + (ub + t0) * DV;
-      bf16_t* dgrow = dg + (ub + t0) * M;
+      const bf16_t* hrow = h_ws + (wb + t0) * M;
+      const bf16_t* grow = gb + (size_t)t0 * GS;
+      GradT<G>* dkrow = dkb + (size_t)t0 * (DK * G);
+      GradT<G>* dvrow = dvb + (size_t)t0 * (DV * G);
+      bf16_t* dgrow = dgb + (size_t)t0 * GS;
       if (!slow) {
         switch (wv) {
-          case 0: rev_pass<DK, DV, M, 0>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          case 1: rev_pass<DK, DV, M, 1>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          case 2: rev_pass<DK, DV, M, 2>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          default: rev_pass<DK, DV, M, 3>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          case 0: rev_pass<DK, DV, M, 0, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          case 1: rev_pass<DK, DV, M, 1, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          case 2: rev_pass<DK, DV, M, 2, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+          default: rev_pass<DK, DV, M, 3, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
         }
       } else {
         __syncthreads();  // log alpha is in LDS
-        rev_exact_pass<M>(rv, smem, Lds::oS, carry, sWt, hrow, grow, dgrow, inv_tau, lane_i, wv);
+        rev_exact_pass<M, G>(rv, smem, Lds::oS, carry, sWt, hrow, grow, dgrow, inv_tau, lane_i, wv);
       }
       __syncthreads();  // B: every wave's gate totals are in LDS
       if (!slow) {
         switch (wv) {
-          case 0: rev_pass_finish<M, 0>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
-          case 1: rev_pass_finish<M, 1>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
-          case 2: rev_pass_finish<M, 2>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
-          default: rev_pass_finish<M, 3>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          case 0: rev_pass_finish<M, 0, G>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          case 1: rev_pass_finish<M, 1, G>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          case 2: rev_pass_finish<M, 2, G>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
+          default: rev_pass_finish<M, 3, G>(lane_i, sWt, carry, dgrow, rv, pre, sn); break;
         }
       }
     }
@@ -1275,47 +1351,158 @@ inline size_t ws_bytes(size_t U, int T, int dk, int dv, int m, Ws* w = nullptr, 
   return off;
 }
 
-template <int DK, int DV, int M, int ACT>
+// Two slot groups (m = 2M): besides the groups' own workspace (2U units), the
+// groups' softmax statistics per token ([rows][2][2] fp32), the merged
+// log-sum-exp and delta per token, and the groups' partial dq, dk, dv
+// ([rows][2][d] fp32).
+struct GroupWs {
+  float *dq, *dk, *dv;
+  float *stats, *lse, *delta;
+};
+
+inline size_t ws_bytes_groups(size_t U, int T, int dk, int dv, int m, Ws* w = nullptr, GroupWs* gw = nullptr,
+                              void* base = nullptr) {
+  size_t off = a256(ws_bytes(2 * U, T, dk, dv, m, w, base));
+  const size_t rows = U * (size_t)T;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += a256(bytes);
+    return o;
+  };
+  const size_t o_stats = take(rows * 4 * 4), o_lse = take(rows * 4), o_delta = take(rows * 4),
+               o_dq = take(rows * 2 * dk * 4), o_dk = take(rows * 2 * dk * 4), o_dv = take(rows * 2 * dv * 4);
+  if (gw) {
+    char* b = (char*)base;
+    gw->stats = (float*)(b + o_stats);
+    gw->lse = (float*)(b + o_lse);
+    gw->delta = (float*)(b + o_delta);
+    gw->dq = (float*)(b + o_dq);
+    gw->dk = (float*)(b + o_dk);
+    gw->dv = (float*)(b + o_dv);
+  }
+  return off;
+}
+
+// The softmax over all 2M slots from the two groups' own statistics per token
+// (l_h = log-sum-exp over group h, A_h = sum over group h of s ds under its own
+// softmax; stats [rows][2][2]): lse = log(e^{l_0} + e^{l_1}) and delta =
+// w_0 A_0 + w_1 A_1 with w_h = e^{l_h - lse}, the sum of s ds over all the
+// slots.  One thread per row.
+__global__ void __launch_bounds__(256)
+bwd_bf16_group_stats(const float* __restrict__ stats, float* __restrict__ lse, float* __restrict__ delta,
+                     size_t rows) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const float4 x = *reinterpret_cast<const float4*>(stats + 4 * row);
+  const float mx = fmaxf(x.x, x.z);
+  const float e0 = __expf(x.x - mx), e1 = __expf(x.z - mx);
+  const float inv = 1.f / (e0 + e1);
+  lse[row] = mx + __logf(e0 + e1);
+  delta[row] = (e0 * x.y + e1 * x.w) * inv;
+}
+
+// dx = x_0 + x_1 over the two slot groups' partial gradients: blockIdx.y
+// picks dq, dk or dv; p [rows][2][D] fp32 -> o [rows][D] bf16.  Thread = 4
+// columns of one row.
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_bf16_group_sum(const float* __restrict__ p0, bf16_t* __restrict__ o0, const float* __restrict__ p1,
+                   bf16_t* __restrict__ o1, const float* __restrict__ p2, bf16_t* __restrict__ o2, size_t rows) {
+  constexpr int TPR = D / 4;
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t row = gid / TPR;
+  const int c = (int)(gid % TPR) * 4;
+  if (row >= rows) return;
+  const float* p = blockIdx.y == 0 ? p0 : blockIdx.y == 1 ? p1 : p2;
+  bf16_t* o = blockIdx.y == 0 ? o0 : blockIdx.y == 1 ? o1 : o2;
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (2 * row) * D + c));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + (2 * row + 1) * D + c));
+  st_grad4(o + row * D + c, a + b);
+}
+
+// G = 1: the dense batch.  G = 2: m = 2M slots as two groups (unit 2u + h);
+// for the softmax read a statistics pass of the forward sweep and a merge
+// give the log-sum-exp over all slots and delta (the sum of s ds over all
+// slots) per token, which both groups' backward passes take, and the groups'
+// partial dq, dk, dv are summed last.
+template <int DK, int DV, int M, int ACT, int G>
 int launch(const GsaBwdLaunch& a) {
   using Lds = BwdLds<DK, DV, M>;
-  const int U = a.B * a.H, T = a.T;
+  const int U = a.B * a.H * G, T = a.T;  // (group) units
   const int nchunks = (T + C - 1) / C;
   const int S = chunks_per_segment(U, nchunks);
   const int P = (nchunks + S - 1) / S;
   Ws w;
-  ws_bytes((size_t)U, T, DK, DV, M, &w, a.ws);
+  GroupWs gw{};
+  if constexpr (G > 1)
+    ws_bytes_groups((size_t)a.B * a.H, T, DK, DV, M, &w, &gw, a.ws);
+  else
+    ws_bytes((size_t)U, T, DK, DV, M, &w, a.ws);
   const float inv_tau = 1.0f / a.tau;
   static const bool lds_set = [] {
-    (void)hipFuncSetAttribute((const void*)bwd_bf16_fwd<DK, DV, M, ACT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              Lds::total);
-    (void)hipFuncSetAttribute((const void*)bwd_bf16_rev<DK, DV, M>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_fwd<DK, DV, M, ACT, G, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds::total);
+    if constexpr (G > 1 && ACT == kActSoftmax)
+      (void)hipFuncSetAttribute((const void*)bwd_bf16_fwd<DK, DV, M, ACT, G, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, Lds::total);
+    (void)hipFuncSetAttribute((const void*)bwd_bf16_rev<DK, DV, M, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               Lds::total);
     return true;
   }();
   (void)lds_set;
-  if (gsa_bf16_segment_states(DK, DV, M, a.k, a.v, a.g, a.k0, a.v0, w.st, w.dec, U, T, S, P, a.tau, a.stream) != 0)
+  if (gsa_bf16_segment_states(DK, DV, M, G, a.k, a.v, a.g, a.k0, a.v0, w.st, w.dec, U, T, S, P, a.tau,
+                              a.stream) != 0)
     return -1;
   const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v, *g = (const bf16_t*)a.g,
                *dO = (const bf16_t*)a.d_o;
-  launch_timed(bwd_bf16_fwd<DK, DV, M, ACT>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 0, 1, q, k, v,
-               g, dO, w.st, w.rm, w.rdec, (bf16_t*)a.dq, w.s, w.dz, w.h, T, S, P, inv_tau);
+  if constexpr (G > 1 && ACT == kActSoftmax) {
+    hipLaunchKernelGGL((bwd_bf16_fwd<DK, DV, M, ACT, G, true>), dim3(P * U), dim3(NT), Lds::total,
+                       (hipStream_t)a.stream, q, k, v, g, dO, w.st, w.rm, w.rdec, (GradT<G>*)nullptr, w.s, w.dz, w.h,
+                       T, S, P, inv_tau, (const float*)nullptr, (const float*)nullptr, gw.stats);
+    const size_t rows = (size_t)a.B * a.H * T;
+    hipLaunchKernelGGL(bwd_bf16_group_stats, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       (hipStream_t)a.stream, (const float*)gw.stats, gw.lse, gw.delta, rows);
+  }
+  GradT<G>* dq;
+  GradT<G>* dk;
+  GradT<G>* dv;
+  if constexpr (G > 1) {
+    dq = gw.dq;
+    dk = gw.dk;
+    dv = gw.dv;
+  } else {
+    dq = (bf16_t*)a.dq;
+    dk = (bf16_t*)a.dk;
+    dv = (bf16_t*)a.dv;
+  }
+  launch_timed(bwd_bf16_fwd<DK, DV, M, ACT, G, false>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 0,
+               1, q, k, v, g, dO, w.st, w.rm, w.rdec, dq, w.s, w.dz, w.h, T, S, P, inv_tau, (const float*)gw.lse,
+               (const float*)gw.delta, (float*)nullptr);
   const long long ne = (long long)U * M * (DK + DV) / 4;
   hipLaunchKernelGGL((bwd_bf16_rscan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0,
                      (hipStream_t)a.stream, w.rm, (const float*)w.rdec, a.dkf, a.dvf, a.dk0, a.dv0, U, P);
-  launch_timed(bwd_bf16_rev<DK, DV, M>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 2, 3, q, k, v, g,
-               dO, (const float*)w.st, (const float*)w.rm, (const bf16_t*)w.s, (const bf16_t*)w.dz,
-               (const bf16_t*)w.h, (bf16_t*)a.dk, (bf16_t*)a.dv, (bf16_t*)a.dg, T, S, P, inv_tau);
+  launch_timed(bwd_bf16_rev<DK, DV, M, G>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 2, 3, q, k, v,
+               g, dO, (const float*)w.st, (const float*)w.rm, (const bf16_t*)w.s, (const bf16_t*)w.dz,
+               (const bf16_t*)w.h, dk, dv, (bf16_t*)a.dg, T, S, P, inv_tau);
+  if constexpr (G > 1) {
+    static_assert(DK == DV, "one row width for the three sums");
+    const size_t rows = (size_t)a.B * a.H * T;
+    const size_t threads = rows * (DK / 4);
+    hipLaunchKernelGGL((bwd_bf16_group_sum<DK>), dim3((unsigned)((threads + 255) / 256), 3), dim3(256), 0,
+                       (hipStream_t)a.stream, (const float*)gw.dq, (bf16_t*)a.dq, (const float*)gw.dk,
+                       (bf16_t*)a.dk, (const float*)gw.dv, (bf16_t*)a.dv, rows);
+  }
   return 0;
 }
 
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, int G>
 int launch_act(const GsaBwdLaunch& a) {
   switch (a.act) {
-    case kActSoftmax: return launch<DK, DV, M, kActSoftmax>(a);
-    case kActIdentity: return launch<DK, DV, M, kActIdentity>(a);
-    case kActSwish: return launch<DK, DV, M, kActSwish>(a);
-    case kActRelu: return launch<DK, DV, M, kActRelu>(a);
-    case kActRelu2: return launch<DK, DV, M, kActRelu2>(a);
+    case kActSoftmax: return launch<DK, DV, M, kActSoftmax, G>(a);
+    case kActIdentity: return launch<DK, DV, M, kActIdentity, G>(a);
+    case kActSwish: return launch<DK, DV, M, kActSwish, G>(a);
+    case kActRelu: return launch<DK, DV, M, kActRelu, G>(a);
+    case kActRelu2: return launch<DK, DV, M, kActRelu2, G>(a);
     default: return -1;
   }
 }
@@ -1327,12 +1514,19 @@ int launch_act(const GsaBwdLaunch& a) {
 long long gsa_bwd_bf16_dispatch(int dk, int dv, int m, const GsaBwdLaunch* a, bool query, size_t units, int T) {
 #define BWD_BF16_CASE(DKC, DVC, MC)                                                        \
   if (dk == DKC && dv == DVC && m == MC)                                                   \
-    return query ? (long long)bfb::ws_bytes(units, T, DKC, DVC, MC) : bfb::launch_act<DKC, DVC, MC>(*a);
+    return query ? (long long)bfb::ws_bytes(units, T, DKC, DVC, MC) : bfb::launch_act<DKC, DVC, MC, 1>(*a);
+  // m = 2 * 64 as two slot groups (slot_groups(1, 128) == 2)
+#define BWD_BF16_GROUPS_CASE(DKC, DVC, MC)                                                        \
+  if (dk == DKC && dv == DVC && m == 2 * MC)                                                      \
+    return query ? (long long)bfb::ws_bytes_groups(units, T, DKC, DVC, MC) : bfb::launch_act<DKC, DVC, MC, 2>(*a);
+  BWD_BF16_GROUPS_CASE(128, 128, 64)
+  BWD_BF16_GROUPS_CASE(64, 64, 64)
   BWD_BF16_CASE(128, 128, 64)
   BWD_BF16_CASE(128, 128, 32)
   BWD_BF16_CASE(64, 64, 64)
   BWD_BF16_CASE(64, 64, 32)
 #undef BWD_BF16_CASE
+#undef BWD_BF16_GROUPS_CASE
   return -1;
 }
 

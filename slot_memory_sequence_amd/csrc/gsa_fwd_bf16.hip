@@ -658,19 +658,17 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
 // h by w_h = exp(l_h - L), L = log(exp(l_0) + exp(l_1)), so o = w_0 o_0 +
 // w_1 o_1 (Sec. 3.2, the softmax read); an element-wise read adds the groups.
 // part [rows][2][DV] bf16, lse [rows][2] fp32.  Thread = 8 columns of one
-// token row.  Optional (non-null): L per row (lse_out), and delta = o . dO per
-// row from the fp32 o before rounding (delta, with d_o [rows][DV]).
+// token row.
 template <int DV, bool SOFTMAX>
 __global__ void __launch_bounds__(256)
 gsa_bf16_merge(const bf16_t* __restrict__ part, const float* __restrict__ lse, bf16_t* __restrict__ o,
-               size_t rows, float* __restrict__ lse_out, const bf16_t* __restrict__ d_o,
-               float* __restrict__ delta) {
+               size_t rows) {
   constexpr int TPR = DV / 8;  // threads per row, a power of two dividing a wave
   static_assert(DV % 8 == 0 && 64 % TPR == 0, "row width");
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t row = gid / TPR;
   const int c = (int)(gid % TPR) * 8;
-  if (row >= rows) return;  // whole rows leave together (TPR lanes, aligned)
+  if (row >= rows) return;
   float w0 = 1.f, w1 = 1.f;
   if constexpr (SOFTMAX) {
     const float2 l = *reinterpret_cast<const float2*>(lse + 2 * row);
@@ -679,7 +677,6 @@ gsa_bf16_merge(const bf16_t* __restrict__ part, const float* __restrict__ lse, b
     const float inv = 1.f / (e0 + e1);
     w0 = e0 * inv;
     w1 = e1 * inv;
-    if (lse_out && c == 0) lse_out[row] = mx + __logf(e0 + e1);
   }
   const uint4 a = *reinterpret_cast<const uint4*>(part + (2 * row) * DV + c);
   const uint4 b = *reinterpret_cast<const uint4*>(part + (2 * row + 1) * DV + c);
@@ -694,17 +691,6 @@ gsa_bf16_merge(const bf16_t* __restrict__ part, const float* __restrict__ lse, b
 #pragma unroll
   for (int i = 0; i < 4; i++) ow[i] = (uint32_t)f2bf(r[2 * i]) | ((uint32_t)f2bf(r[2 * i + 1]) << 16);
   __builtin_nontemporal_store(u32x4{ow[0], ow[1], ow[2], ow[3]}, reinterpret_cast<u32x4*>(o + row * DV + c));
-  if (delta) {
-    const uint4 d = *reinterpret_cast<const uint4*>(d_o + row * DV + c);
-    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-    float x = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-      x += r[2 * i] * __uint_as_float(dw[i] << 16) + r[2 * i + 1] * __uint_as_float(dw[i] & 0xffff0000u);
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    if (c == 0) delta[row] = x;
-  }
 }
 
 // ------------------------------------------------------------ launcher
@@ -769,7 +755,7 @@ static int launch_groups(const GsaLaunch& a) {
   const size_t threads = rows * (DV / 8);
   hipLaunchKernelGGL((gsa_bf16_merge<DV, ACT == kActSoftmax>), dim3((unsigned)((threads + 255) / 256)),
                      dim3(256), 0, (hipStream_t)a.stream, (const bf16_t*)a.ws_part, (const float*)a.ws_lse,
-                     (bf16_t*)a.o, rows, nullptr, nullptr, nullptr);
+                     (bf16_t*)a.o, rows);
   return 0;
 }
 
@@ -853,37 +839,42 @@ namespace bfk {
 // state maps of segments 0 .. P-2 and the per-unit scan, so that ws_state[u][p]
 // (layout [units][P][M][DK+DV] fp32) holds the state at the start of segment p
 // (p = 0: the initial state).  ws_dec: [units][P][M] fp32.
-template <int DK, int DV, int M>
+template <int DK, int DV, int M, class Seq>
 static void segment_states(const void* k, const void* v, const void* g, const float* k0,
                            const float* v0, float* ws_state, float* ws_dec, int units, int T, int S,
                            int P, float tau, void* stream) {
   using LS = StateLds<DK, DV, M>;
   static const bool lds_set = [] {
-    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M, DenseSeqs>,
+    (void)hipFuncSetAttribute((const void*)gsa_bf16_state<DK, DV, M, Seq>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, LS::total);
     return true;
   }();
   (void)lds_set;
   hipStream_t st = (hipStream_t)stream;
   if (P > 1)
-    hipLaunchKernelGGL((gsa_bf16_state<DK, DV, M, DenseSeqs>), dim3(P - 1, units), dim3(NT), LS::total, st,
+    hipLaunchKernelGGL((gsa_bf16_state<DK, DV, M, Seq>), dim3(P - 1, units), dim3(NT), LS::total, st,
                        (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)g, ws_state, ws_dec,
-                       DenseSeqs{T}, S, P, 1.0f / tau);
+                       Seq{T}, S, P, 1.0f / tau);
   const long long ne = (long long)units * M * (DK + DV) / 4;
   hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
                      ws_state, (const float*)ws_dec, k0, v0, units, P);
 }
 }  // namespace bfk
 
-int gsa_bf16_segment_states(int dk, int dv, int m, const void* k, const void* v, const void* g,
+int gsa_bf16_segment_states(int dk, int dv, int m, int groups, const void* k, const void* v, const void* g,
                             const float* k0, const float* v0, float* ws_state, float* ws_dec,
                             int units, int T, int S, int P, float tau, void* stream) {
-#define SEG_CASE(DKC, DVC, MC)                                                                  \
-  if (dk == DKC && dv == DVC && m == MC) {                                                      \
-    bfk::segment_states<DKC, DVC, MC>(k, v, g, k0, v0, ws_state, ws_dec, units, T, S, P, tau,   \
-                                      stream);                                                  \
-    return 0;                                                                                   \
+#define SEG_CASE(DKC, DVC, MC)                                                                        \
+  if (dk == DKC && dv == DVC && m == MC) {                                                            \
+    if (groups == 2)                                                                                  \
+      bfk::segment_states<DKC, DVC, MC, bfk::SlotGroups>(k, v, g, k0, v0, ws_state, ws_dec, units, T, \
+                                                         S, P, tau, stream);                          \
+    else                                                                                              \
+      bfk::segment_states<DKC, DVC, MC, bfk::DenseSeqs>(k, v, g, k0, v0, ws_state, ws_dec, units, T,  \
+                                                        S, P, tau, stream);                           \
+    return 0;                                                                                         \
   }
+  if (groups != 1 && !(groups == 2 && m == 64)) return -1;
   SEG_CASE(128, 128, 64)
   SEG_CASE(128, 128, 32)
   SEG_CASE(64, 64, 64)

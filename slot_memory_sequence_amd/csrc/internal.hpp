@@ -107,8 +107,10 @@ struct GsaBwdLaunch {
 // The bf16 forward's segment start states of a dense batch (state maps of
 // segments 0 .. P-2, then the per-unit scan): ws_state [units][P][m][dk+dv]
 // fp32, slot p = the state at the start of segment p (S chunks each); ws_dec
-// [units][P][m] fp32.  Returns -1 if (dk, dv, m) is not compiled.
-int gsa_bf16_segment_states(int dk, int dv, int m, const void* k, const void* v, const void* g,
+// [units][P][m] fp32.  groups = 2: the units are the slot groups of m = 64
+// each of a batch with 128 slots (unit 2u + h, gate row pitch 128).  Returns
+// -1 if (dk, dv, m, groups) is not compiled.
+int gsa_bf16_segment_states(int dk, int dv, int m, int groups, const void* k, const void* v, const void* g,
                             const float* k0, const float* v0, float* ws_state, float* ws_dec,
                             int units, int T, int S, int P, float tau, void* stream);
 

@@ -271,6 +271,15 @@ def test_bwd_validation(gsa):
     assert gsa.gsa_bwd_workspace_bytes(8, 4, 2048, 128, 128, 64, 1) == big < 64 * 10 ** 6
     assert gsa.gsa_bwd_supported(128, 128, 64, 1) and gsa.gsa_bwd_supported(64, 64, 32, 0)
     assert not gsa.gsa_bwd_supported(96, 96, 64, 1) and not gsa.gsa_bwd_supported(128, 128, 48, 1)
+    # 128 slots (bf16 only): two groups of 64 as 64 group units (4 segments of
+    # 8 chunks), then the groups' statistics [rows][2][2], the merged
+    # log-sum-exp and delta [rows], and fp32 partial dq, dk, dv [rows][2][128]
+    assert gsa.gsa_bwd_supported(128, 128, 128, 1) and gsa.gsa_bwd_supported(64, 64, 128, 1)
+    assert not gsa.gsa_bwd_supported(128, 128, 128, 0)
+    U2, nseg2, rows = 64, 4, 32 * 2048
+    own = 2 * a256(U2 * nseg2 * 64 * 256 * 4) + 2 * a256(U2 * nseg2 * 64 * 4) + 3 * a256(U2 * 2048 * 64 * 2)
+    grp = a256(rows * 16) + 2 * a256(rows * 4) + 3 * a256(rows * 2 * 128 * 4)
+    assert gsa.gsa_bwd_workspace_bytes(8, 4, 2048, 128, 128, 128, 1) == a256(own) + grp
 
     def call(**kw):
         a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, g=FAKE + 0x300000,
@@ -286,6 +295,7 @@ def test_bwd_validation(gsa):
     assert call(tau=0.0) == 2 and call(tau=float("inf")) == 2 and call(T=-1) == 2
     assert call(dtype=5) == 2
     assert call(d_k=96, d_v=96) == 4
+    assert call(m=128, dtype=0) == 4                    # 128 slots: bf16 only
     assert call(B=65536) == 4
     assert call(T=65535 * 64 + 1) == 4                  # more chunks than the grid takes
     assert call(B=0) == 0                               # nothing to do

@@ -159,3 +159,84 @@ def test_prefill_then_decode(gsa, torch):
     got = np.stack([to_np(x) for x in outs], axis=2)
     assert rel_err(got, ref["o"][:, :, T0:]) <= TOL["bf16"]
     assert rel_err(to_np(ks), ref["kf"]) <= TOL["bf16"] and rel_err(to_np(vs), ref["vf"]) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------- backward
+GRADS = ("dq", "dk", "dv", "dg", "dk0", "dv0")
+
+
+def _bwd_check(gsa, torch, B, H, T, d, init=True, final=True, seed=0, mutate=None, nl="softmax", units=None,
+               qkv_scale=None):
+    inp = synth.gsa_inputs(B, H, T, d, d, M, dtype="bf16", seed=seed, qkv_scale=qkv_scale,
+                           init_std=0.1 if init else None)
+    if mutate is not None:
+        mutate(inp)
+    gi = synth.gsa_grad_inputs(B, H, T, d, d, M, dtype="bf16", seed=seed + 1000,
+                               final_std=1.0 if final else None)
+    dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
+    ddev = {n: to_dev(gi[n], torch) for n in ("do", "dkf", "dvf")}
+    out = gsa.gsa_bwd(dev["q"], dev["k"], dev["v"], dev["g"], ddev["do"], dev["k0"], dev["v0"], ddev["dkf"],
+                      ddev["dvf"], state_grads=True, nonlinearity=nl)
+    torch.cuda.synchronize()
+    got = dict(zip(GRADS, out))
+
+    def sel(x):
+        if x is None:
+            return None
+        return x.f64 if units is None else x.f64.reshape(-1, *x.shape[2:])[units][:, None]
+    ref = oracle.gsa_bwd(*(sel(inp[n]) for n in "qkvg"), sel(gi["do"]), sel(inp["k0"]), sel(inp["v0"]),
+                         sel(gi["dkf"]), sel(gi["dvf"]), tau=8.0, nthreads=oracle.max_threads(), nonlinearity=nl)
+    errs = {}
+    for n in GRADS:
+        x = to_np(got[n])
+        if units is not None:
+            x = x.reshape(-1, *x.shape[2:])[units][:, None]
+        errs[n] = rel_err(x, ref[n])
+    print("m128 bwd B%d H%d T%d d%d %s: %s" % (B, H, T, d, nl, " ".join("%s %.2e" % kv for kv in errs.items())))
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("T", [1, 65, 200])
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_lengths(gsa, torch, T, d):
+    _bwd_check(gsa, torch, 2, 2, T, d, init=(T != 65), final=(T != 1), seed=T + d)
+
+
+@pytest.mark.parametrize("nl", ["identity", "swish", "relu2"])
+def test_bwd_elementwise_reads(gsa, torch, nl):
+    """Element-wise reads: each group's gradients are its own (no log-sum-exp)."""
+    _bwd_check(gsa, torch, 1, 2, 150, 128, nl=nl, seed=21)
+
+
+def test_bwd_relu_read_rejected(gsa, torch):
+    inp = synth.gsa_inputs(1, 1, 64, 128, 128, M, dtype="bf16", seed=22)
+    gi = synth.gsa_grad_inputs(1, 1, 64, 128, 128, M, dtype="bf16", seed=23)
+    dev = {n: to_dev(inp[n], torch) for n in "qkvg"}
+    with pytest.raises(RuntimeError):
+        gsa.gsa_bwd(dev["q"], dev["k"], dev["v"], dev["g"], to_dev(gi["do"], torch), nonlinearity="relu")
+
+
+def test_bwd_one_group_decays_fast(gsa, torch):
+    """Exact-recurrence chunks in the second group only, and +-inf gates."""
+    def mut(inp):
+        x = inp["g"].f64.copy()
+        x[..., 64:128, 64:] = -12.0
+        x[..., 10, 3] = -np.inf
+        x[..., 20, 100] = np.inf
+        inp["g"] = synth.stored(x, "bf16")
+    _bwd_check(gsa, torch, 1, 2, 64 * 3 + 11, 128, seed=24, mutate=mut)
+
+
+def test_bwd_skewed_groups(gsa, torch):
+    def mut(inp):
+        k0 = inp["k0"].f64.copy()
+        k0[:, :, :64] *= 40.0
+        inp["k0"] = synth.stored(k0, "f32")
+    _bwd_check(gsa, torch, 2, 1, 130, 128, seed=25, mutate=mut)
+
+
+def test_bwd_full_shape_sampled(gsa, torch):
+    """B8 H4 T2048 d128 m128 in the default launch configuration; three of
+    the 32 units against the oracle."""
+    _bwd_check(gsa, torch, 8, 4, 2048, 128, init=False, final=False, seed=26, units=[0, 13, 31],
+               qkv_scale=1 / np.sqrt(128))
