@@ -327,7 +327,7 @@ def bench_gla(torch, gsa, ev, w, steps, warmup, name="gla_bf16_T4096"):
             "_inp": inp, "_out": outs[0]}
 
 
-def bench_decode(torch, gsa, ev, w, steps, warmup):
+def bench_decode(torch, gsa, ev, w, steps, warmup, name="gsa_decode_N256"):
     import synth
     from synth import to_dev
     inp = synth.decode_inputs(w["N"], w["H"], w["dk"], w["dv"], w["m"], dtype=w["dtype"], seed=0,
@@ -356,7 +356,7 @@ def bench_decode(torch, gsa, ev, w, steps, warmup):
     units = w["N"] * w["H"]
     # both fp32 states read and written once, plus the bf16 token I/O (q, k, v, g in, o out)
     nbytes = units * (2 * 4 * w["m"] * (w["dk"] + w["dv"]) + 2 * (2 * w["dk"] + 2 * w["dv"] + w["m"]))
-    r = roofline(nbytes, t, "gsa_decode_kernel", "gsa_decode_N256")
+    r = roofline(nbytes, t, "gsa_decode_kernel", name)
     return {"value": r["achieved"], "unit": "GB/s", "ms_kernel": round(t, 4),
             "ms_kernel_stats": stats(tk), "steps_per_s": round(steps / wall, 1),
             "tokens_per_s": round(w["N"] * steps / wall, 1), "roofline": r, "_inp": inp}
@@ -840,6 +840,18 @@ def run_only(args, torch, gsa, ev):
                          args.warmup, cpu=False)
     if args.only == "gla_decode":
         return bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
+    if args.only == "m128":
+        r = bench_gsa(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_m128"], "gsa_bf16_train_T2048_m128",
+                      args.steps, args.warmup, args.sets, warm_too=False)
+        return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "bwd_m128":
+        return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_m128"], args.steps,
+                         args.warmup, name="gsa_bf16_train_T2048_m128_bwd", cpu=False)
+    if args.only == "decode_m128":
+        r = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256_m128"], args.steps, args.warmup,
+                         name="gsa_decode_N256_m128")
+        r.pop("_inp")
+        return r
     if args.only == "serve":
         return bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
                            args.warmup)
@@ -863,7 +875,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -925,6 +937,22 @@ def main():
                 "cpu_oracle": oracle_gsa_sample(wf, r["inp"], r["out"], ocpu) if ocpu else None}
             del r
         log("bench: fast-forgetting slots done")
+        # 128 slots: the forward (two slot groups and their merge), decode, backward
+        wm = synth.WORKLOADS["gsa_bf16_train_T2048_m128"]
+        r = bench_gsa(torch, gsa, ev, wm, "gsa_bf16_train_T2048_m128", args.steps, args.warmup, args.sets,
+                      warm_too=False)
+        comps["gsa_bf16_train_T2048_m128"] = {
+            "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+            "vs_m64": round(r["tokens_per_s"] / main_res["tokens_per_s"], 4),
+            "ms_per_step": round(r["ms_per_step"], 4), "ms_phases": r["ms_phases"],
+            "ms_op_stamped": r["ms_op_stamped"], "roofline": r["roofline"], "op_roofline": r["op_roofline"],
+            "alg_tflops": round(r["alg_tflops"], 2),
+            "cpu_oracle": oracle_gsa_sample(wm, r["inp"], r["out"], ocpu) if ocpu else None}
+        del r
+        comps["gsa_decode_N256_m128"] = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256_m128"],
+                                                     args.steps, args.warmup, name="gsa_decode_N256_m128")
+        comps["gsa_decode_N256_m128"].pop("_inp")
+        log("bench: 128 slots forward and decode done")
         r = bench_gla(torch, gsa, ev, synth.WORKLOADS["gla_bf16_T4096"], args.steps, args.warmup)
         gi, go = r.pop("_inp"), r.pop("_out")
         r["cpu_oracle"] = oracle_gla_sample(synth.WORKLOADS["gla_bf16_T4096"], gi, go, ocpu) if ocpu else None
@@ -956,6 +984,10 @@ def main():
             torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], max(1, args.steps // 4), args.warmup,
             name="gsa_bf16_long_T16384_bwd", cpu=False)
         log("bench: long-context backward done")
+        comps["gsa_bf16_train_T2048_m128_bwd"] = bench_bwd(
+            torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_m128"], max(1, args.steps // 4), args.warmup,
+            name="gsa_bf16_train_T2048_m128_bwd", cpu=False)
+        log("bench: 128-slot backward done")
         comps["gsa_bf16_serve_N256"] = bench_serve(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"],
                                                    max(1, args.steps // 2), args.warmup)
         log("bench: serving prefill + decode done")

@@ -210,6 +210,11 @@ WORKLOADS = {
                                               C=64, tau=8.0, dtype="bf16",
                                               qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                                               init_std=None, fast_slots=8, fast_shift=-10.0),
+    # the training shape with 128 slots (the largest slot count the pages
+    # measure training throughput at)
+    "gsa_bf16_train_T2048_m128": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=128, C=64,
+                                      tau=8.0, dtype="bf16", qkv_scale=1 / math.sqrt(128),
+                                      g_shift=0.0, init_std=None),
     "gla_bf16_T4096": dict(op="gla", B=8, H=16, T=4096, dk=128, dv=128, C=64, tau=16.0,
                            dtype="bf16", qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                            init_std=None),
@@ -223,6 +228,8 @@ WORKLOADS = {
                                  g_shift=2.0, init_std=0.1),
     "gsa_decode_N256": dict(op="decode", N=256, H=16, dk=128, dv=128, m=64, tau=8.0,
                             dtype="bf16", qkv_scale=1 / math.sqrt(128), state_std=0.1),
+    "gsa_decode_N256_m128": dict(op="decode", N=256, H=16, dk=128, dv=128, m=128, tau=8.0,
+                                 dtype="bf16", qkv_scale=1 / math.sqrt(128), state_std=0.1),
     # serving: the prefill of the decode batch's 256 sequences (prompt lengths
     # log-uniform in [16, 1024]) as one packed variable-length call, then decode
     # steps from its final states
