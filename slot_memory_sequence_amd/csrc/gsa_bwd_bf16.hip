@@ -600,11 +600,11 @@ __device__ __forceinline__ void fwd_exact_pass(int rv, unsigned char* smem, cons
 template <int DK, int DV, int M, int ACT, int G, bool STATS>
 __global__ void __launch_bounds__(NT, 1)
 bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
-             const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, float* __restrict__ st,
-             float* __restrict__ rm, float* __restrict__ rdec, GradT<G>* __restrict__ dq,
-             bf16_t* __restrict__ s_ws, bf16_t* __restrict__ dz_ws, bf16_t* __restrict__ h_ws, int T, int S,
-             int P, float inv_tau, const float* __restrict__ lse, const float* __restrict__ delta,
-             float* __restrict__ stats) {
+             const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, const float* __restrict__ st,
+             float* __restrict__ fin, float* __restrict__ rm, float* __restrict__ rdec,
+             GradT<G>* __restrict__ dq, bf16_t* __restrict__ s_ws, bf16_t* __restrict__ dz_ws,
+             bf16_t* __restrict__ h_ws, int T, int S, int P, float inv_tau, const float* __restrict__ lse,
+             const float* __restrict__ delta, float* __restrict__ stats) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   constexpr int GPW = M / NW;
@@ -642,7 +642,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   const bf16_t* db = dOo + ub * DV;
   const bf16_t* gb = gg + ub * GS + grp * M + slot0;
   GradT<G>* dqb = dq + (ub * G + grp) * DK;
-  float* stp = st + ((size_t)unit * P + seg) * NE;
+  const float* stp = st + ((size_t)unit * P + seg) * NE;
   float* rmp = rm + ((size_t)unit * P + seg) * NE;
   auto rows_of = [&](int ch) { return min(C, T - ch * C); };
 
@@ -713,10 +713,11 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       if constexpr (!STATS) R.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, nullptr, sw, lane_i);
       __syncthreads();  // B: every reader of this chunk's tiles, factors and copies is done
     }
-    // the segment's end state over its start state (only this workgroup reads
-    // that slot), its reverse map beside it
+    // the segment's reverse map; the last segment's end state (the final
+    // state: every other segment's end state is the next one's start state,
+    // which st already holds)
     if constexpr (!STATS) {
-      W.store_w(stp, sw, lane);
+      if (seg == P - 1) W.store_w(fin + (size_t)unit * NE, sw, lane);
       R.store_w(rmp, sw, lane);
     }
   } else {
@@ -1119,9 +1120,9 @@ template <int DK, int DV, int M, int G>
 __global__ void __launch_bounds__(NT, 1)
 bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const bf16_t* __restrict__ vv,
              const bf16_t* __restrict__ gg, const bf16_t* __restrict__ dOo, const float* __restrict__ st,
-             const float* __restrict__ rm, const bf16_t* __restrict__ s_ws, const bf16_t* __restrict__ dz_ws,
-             const bf16_t* __restrict__ h_ws, GradT<G>* __restrict__ dk, GradT<G>* __restrict__ dv,
-             bf16_t* __restrict__ dg, int T, int S, int P, float inv_tau) {
+             const float* __restrict__ fin, const float* __restrict__ rm, const bf16_t* __restrict__ s_ws,
+             const bf16_t* __restrict__ dz_ws, const bf16_t* __restrict__ h_ws, GradT<G>* __restrict__ dk,
+             GradT<G>* __restrict__ dv, bf16_t* __restrict__ dg, int T, int S, int P, float inv_tau) {
   using Lds = BwdLds<DK, DV, M>;
   using ST = StateTiles<DK, DV, M, 4>;
   constexpr int GPW = M / NW;
@@ -1216,10 +1217,11 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     ST W;  // the adjoint of the state at the end of the current chunk
     {
       // carry from the tokens after this segment: <dW_end, W_end> per slot
+      // (W_end: the next segment's start state, or the final state)
       const size_t o = ((size_t)unit * P + seg) * NE;
       W.load_w(rm + o, sw, lane);
       typename ST::MapRegs we;
-      W.load_map(we, st + o, sw, lane);
+      W.load_map(we, seg + 1 < P ? st + o + NE : fin + (size_t)unit * NE, sw, lane);
       float p[MT];
 #pragma unroll
       for (int ct = 0; ct < MT; ct++) {
@@ -1315,15 +1317,15 @@ inline int chunks_per_segment(long long units, int nchunks) {
 }
 
 struct Ws {
-  float *st, *dec, *rm, *rdec;
+  float *st, *dec, *fin, *rm, *rdec;
   bf16_t *s, *dz, *h;
 };
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of the dense bf16 backward (bytes) and its carving: segment
-// start/end states and reverse maps (fp32), segment decays, and s, dz, h per
-// token (bf16).
+// Workspace of the dense bf16 backward (bytes) and its carving: segment start
+// states, the final state and reverse maps (fp32), segment decays, and s, dz,
+// h per token (bf16).
 inline size_t ws_bytes(size_t U, int T, int dk, int dv, int m, Ws* w = nullptr, void* base = nullptr) {
   const int nchunks = (T + C - 1) / C;
   const int S = chunks_per_segment((long long)U, nchunks);
@@ -1335,13 +1337,15 @@ inline size_t ws_bytes(size_t U, int T, int dk, int dv, int m, Ws* w = nullptr, 
     off += a256(bytes);
     return o;
   };
-  const size_t o_st = take(U * P * NE * 4), o_dec = take(U * P * m * 4), o_rm = take(U * P * NE * 4),
+  const size_t o_st = take(U * P * NE * 4), o_dec = take(U * P * m * 4), o_fin = take(U * NE * 4),
+               o_rm = take(U * P * NE * 4),
                o_rdec = take(U * P * m * 4), o_s = take(U * T * (size_t)m * 2),
                o_dz = take(U * T * (size_t)m * 2), o_h = take(U * T * (size_t)m * 2);
   if (w) {
     char* b = (char*)base;
     w->st = (float*)(b + o_st);
     w->dec = (float*)(b + o_dec);
+    w->fin = (float*)(b + o_fin);
     w->rm = (float*)(b + o_rm);
     w->rdec = (float*)(b + o_rdec);
     w->s = (bf16_t*)(b + o_s);
@@ -1457,8 +1461,9 @@ int launch(const GsaBwdLaunch& a) {
                *dO = (const bf16_t*)a.d_o;
   if constexpr (G > 1 && ACT == kActSoftmax) {
     hipLaunchKernelGGL((bwd_bf16_fwd<DK, DV, M, ACT, G, true>), dim3(P * U), dim3(NT), Lds::total,
-                       (hipStream_t)a.stream, q, k, v, g, dO, w.st, w.rm, w.rdec, (GradT<G>*)nullptr, w.s, w.dz, w.h,
-                       T, S, P, inv_tau, (const float*)nullptr, (const float*)nullptr, gw.stats);
+                       (hipStream_t)a.stream, q, k, v, g, dO, (const float*)w.st, w.fin, w.rm, w.rdec,
+                       (GradT<G>*)nullptr, w.s, w.dz, w.h, T, S, P, inv_tau, (const float*)nullptr,
+                       (const float*)nullptr, gw.stats);
     const size_t rows = (size_t)a.B * a.H * T;
     hipLaunchKernelGGL(bwd_bf16_group_stats, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
                        (hipStream_t)a.stream, (const float*)gw.stats, gw.lse, gw.delta, rows);
@@ -1476,13 +1481,14 @@ int launch(const GsaBwdLaunch& a) {
     dv = (bf16_t*)a.dv;
   }
   launch_timed(bwd_bf16_fwd<DK, DV, M, ACT, G, false>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 0,
-               1, q, k, v, g, dO, w.st, w.rm, w.rdec, dq, w.s, w.dz, w.h, T, S, P, inv_tau, (const float*)gw.lse,
-               (const float*)gw.delta, (float*)nullptr);
+               1, q, k, v, g, dO, (const float*)w.st, w.fin, w.rm, w.rdec, dq, w.s, w.dz, w.h, T, S, P, inv_tau,
+               (const float*)gw.lse, (const float*)gw.delta, (float*)nullptr);
   const long long ne = (long long)U * M * (DK + DV) / 4;
   hipLaunchKernelGGL((bwd_bf16_rscan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0,
                      (hipStream_t)a.stream, w.rm, (const float*)w.rdec, a.dkf, a.dvf, a.dk0, a.dv0, U, P);
   launch_timed(bwd_bf16_rev<DK, DV, M, G>, dim3(P * U), dim3(NT), Lds::total, a.stream, a.events, 2, 3, q, k, v,
-               g, dO, (const float*)w.st, (const float*)w.rm, (const bf16_t*)w.s, (const bf16_t*)w.dz,
+               g, dO, (const float*)w.st, (const float*)w.fin, (const float*)w.rm, (const bf16_t*)w.s,
+               (const bf16_t*)w.dz,
                (const bf16_t*)w.h, dk, dv, (bf16_t*)a.dg, T, S, P, inv_tau);
   if constexpr (G > 1) {
     static_assert(DK == DV, "one row width for the three sums");

@@ -259,15 +259,16 @@ def test_bwd_validation(gsa):
     need = gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 1)  # the bf16 path's need
     assert gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 1, "relu") == \
         gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64, 0)  # ReLU: the token walks
-    assert 0 < need < gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64)  # < enough for either
+    assert 0 < need <= gsa.gsa_bwd_workspace_bytes(1, 1, 64, 128, 128, 64)  # <= enough for either
     assert gsa.gsa_bwd_workspace_bytes(1, 1, 0, 128, 128, 64) == 0       # T = 0: nothing kept
     assert gsa.gsa_bwd_workspace_bytes(-1, 1, 64, 128, 128, 64) == 0
     # the bf16 path at the training shape (B8 H4 T2048 d128 m64): segment
-    # states and reverse maps (8 segments of 4 chunks per unit, fp32) and bf16
-    # s, dz, h per token
+    # start states and reverse maps (8 segments of 4 chunks per unit, fp32),
+    # the final state per unit, and bf16 s, dz, h per token
     U, nseg = 32, 8
     a256 = lambda x: (x + 255) // 256 * 256
-    big = 2 * a256(U * nseg * 64 * 256 * 4) + 2 * a256(U * nseg * 64 * 4) + 3 * a256(U * 2048 * 64 * 2)
+    big = 2 * a256(U * nseg * 64 * 256 * 4) + 2 * a256(U * nseg * 64 * 4) + a256(U * 64 * 256 * 4) + \
+        3 * a256(U * 2048 * 64 * 2)
     assert gsa.gsa_bwd_workspace_bytes(8, 4, 2048, 128, 128, 64, 1) == big < 64 * 10 ** 6
     assert gsa.gsa_bwd_supported(128, 128, 64, 1) and gsa.gsa_bwd_supported(64, 64, 32, 0)
     assert not gsa.gsa_bwd_supported(96, 96, 64, 1) and not gsa.gsa_bwd_supported(128, 128, 48, 1)
@@ -277,7 +278,8 @@ def test_bwd_validation(gsa):
     assert gsa.gsa_bwd_supported(128, 128, 128, 1) and gsa.gsa_bwd_supported(64, 64, 128, 1)
     assert not gsa.gsa_bwd_supported(128, 128, 128, 0)
     U2, nseg2, rows = 64, 4, 32 * 2048
-    own = 2 * a256(U2 * nseg2 * 64 * 256 * 4) + 2 * a256(U2 * nseg2 * 64 * 4) + 3 * a256(U2 * 2048 * 64 * 2)
+    own = 2 * a256(U2 * nseg2 * 64 * 256 * 4) + 2 * a256(U2 * nseg2 * 64 * 4) + a256(U2 * 64 * 256 * 4) + \
+        3 * a256(U2 * 2048 * 64 * 2)
     grp = a256(rows * 16) + 2 * a256(rows * 4) + 3 * a256(rows * 2 * 128 * 4)
     assert gsa.gsa_bwd_workspace_bytes(8, 4, 2048, 128, 128, 128, 1) == a256(own) + grp
 
