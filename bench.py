@@ -451,25 +451,49 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
     al = gsa_bwd_chunk_alg(B, H, T, dk, dv, m, w["C"], 2)
     nbytes = al["bytes"]
-    # one training step of the op: the forward, then its backward (same inputs)
+    # one training step of the op as gsa_autograd runs it: the training forward
+    # (keeping the segment start states), then the backward reading them
     o_buf = [torch.empty_like(s_["v"]) for s_ in sets]
-    nbf = gsa.gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, w["C"], 1, 0)
+    nbf = int(gsa.lib.gsa_fwd_train_workspace_bytes(B, H, T, dk, dv, m, 1))
     wsf = torch.empty(max(nbf, 1), dtype=torch.uint8, device="cuda")
+    nst = gsa.gsa_train_states_bytes(B, H, T, dk, dv, m)
+    st_buf = [torch.empty(max(nst, 1), dtype=torch.uint8, device="cuda") for _ in sets]
+
+    def fwd_train(i):
+        s_ = sets[i % len(sets)]
+        gsa.gsa_fwd_train(s_["q"], s_["k"], s_["v"], s_["g"], s_.get("k0"), s_.get("v0"), tau=w["tau"],
+                          out=o_buf[i % len(sets)], workspace=wsf, states=st_buf[i % len(sets)])
+
+    def bwd_saved(i, events=None):
+        s_ = sets[i % len(sets)]
+        gsa.gsa_bwd_train(s_["q"], s_["k"], s_["v"], s_["g"], s_["do"], st_buf[i % len(sets)], s_.get("k0"),
+                          s_.get("v0"), s_.get("dkf"), s_.get("dvf"), tau=w["tau"], out=outs[i % len(sets)],
+                          workspace=ws, events=events)
 
     def train_step(i):
-        s_ = sets[i % len(sets)]
-        gsa.gsa_fwd(s_["q"], s_["k"], s_["v"], s_["g"], s_.get("k0"), s_.get("v0"), tau=w["tau"],
-                    out=o_buf[i % len(sets)], workspace=wsf)
-        call(s_, None)
+        fwd_train(i)
+        bwd_saved(i)
 
-    for i in range(warmup):
-        train_step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    wall_train = timed(train_step)
+    for i in range(len(sets)):  # states for every set, then the backward alone
+        fwd_train(i)
+    wall_saved = timed(bwd_saved)
+    evs = ev.create(4 * steps)
     for i in range(steps):
-        train_step(i)
+        bwd_saved(i, evs[4 * i: 4 * i + 4])
     torch.cuda.synchronize()
-    wall_train = time.perf_counter() - t0
+    saved_f = mean([ev.ms(evs[4 * i], evs[4 * i + 1]) for i in range(steps)])
+    saved_r = mean([ev.ms(evs[4 * i + 2], evs[4 * i + 3]) for i in range(steps)])
     kern, kb, t = ("bwd_bf16_fwd", al["bytes_fwd"], t_f) if t_f >= t_r else ("bwd_bf16_rev", al["bytes_rev"], t_r)
     t_op = wall / steps * 1e3
     fl = al["flops_fwd"] + al["flops_rev"]
@@ -487,11 +511,50 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
             "mfma": {"alg_tflops": round(fl / (t_op * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fl / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "basis": "the chunk form's algorithmic flops (causal halves) over the wall-clock step"},
+            "saved_states": {"value": round(B * T * steps / wall_saved, 1), "unit": "tokens/s",
+                             "ms_per_step": round(wall_saved / steps * 1e3, 4),
+                             "ms_kernels": {"bwd_bf16_fwd": round(saved_f, 4), "bwd_bf16_rev": round(saved_r, 4)},
+                             "op_roofline": op_roofline(nbytes, wall_saved / steps * 1e3),
+                             "states_bytes": nst,
+                             "what": "gsa_bwd_train: the backward reading the segment start states "
+                                     "gsa_fwd_train kept (no state maps or scan of its own)"},
             "train_step": {"value": round(B * T * steps / wall_train, 1), "unit": "tokens/s",
                            "ms_per_step": round(wall_train / steps * 1e3, 4),
-                           "what": "gsa_fwd then gsa_bwd on the same batch, per step"},
+                           "what": "gsa_fwd_train then gsa_bwd_train on the same batch, per step "
+                                   "(what gsa_autograd runs)"},
             "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None,
             "parity_rel_err": bwd_parity(torch, w, inp, outs[0]) if cpu else None}
+
+
+def bench_bwd_saved_only(torch, gsa, w, steps, warmup):
+    """The backward from a training forward's kept states alone (for profiler
+    runs: one gsa_fwd_train per input set, then only gsa_bwd_train)."""
+    import synth
+    B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
+    inp = synth.gsa_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=0, qkv_scale=w["qkv_scale"],
+                           g_shift=w["g_shift"], init_std=w["init_std"])
+    gi = synth.gsa_grad_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=1,
+                               final_std=1.0 if inp["k0"] is not None else None)
+    inp["do"], inp["dkf"], inp["dvf"] = gi["do"], gi["dkf"], gi["dvf"]
+    sets = dev_sets(torch, inp, ["q", "k", "v", "g", "do", "k0", "v0", "dkf", "dvf"], 2)
+    states = [gsa.gsa_fwd_train(s_["q"], s_["k"], s_["v"], s_["g"], s_.get("k0"), s_.get("v0"),
+                                tau=w["tau"])[3] for s_ in sets]
+    ws = torch.empty(gsa.gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, 1), dtype=torch.uint8, device="cuda")
+    outs = [tuple(torch.empty_like(s_[n]) for n in "qkvg") for s_ in sets]
+
+    def step(i):
+        s_ = sets[i % 2]
+        gsa.gsa_bwd_train(s_["q"], s_["k"], s_["v"], s_["g"], s_["do"], states[i % 2], s_.get("k0"),
+                          s_.get("v0"), s_.get("dkf"), s_.get("dvf"), tau=w["tau"], out=outs[i % 2], workspace=ws)
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s", "ms_per_step": round(wall / steps * 1e3, 4)}
 
 
 def bench_bwd_varlen(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_serve_N256_bwd"):
@@ -835,6 +898,10 @@ def run_only(args, torch, gsa, ev):
     if args.only == "bwd_serve":
         return bench_bwd_varlen(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
                                 args.warmup)
+    if args.only == "bwd_saved":
+        return bench_bwd_saved_only(torch, gsa, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps, args.warmup)
+    if args.only == "bwd_long_saved":
+        return bench_bwd_saved_only(torch, gsa, synth.WORKLOADS["gsa_bf16_long_T16384"], args.steps, args.warmup)
     if args.only == "bwd":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps,
                          args.warmup, cpu=False)
@@ -875,7 +942,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128", "bwd_saved", "bwd_long_saved"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

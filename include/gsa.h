@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define GSA_ABI_VERSION 4
+#define GSA_ABI_VERSION 5
 
 typedef enum {
   GSA_OK = 0,
@@ -367,6 +367,46 @@ int gsa_bwd_ex(const void* q, const void* k, const void* v, const void* g, const
                void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
                int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
                int nonlinearity, void* stream, void* const* events);
+
+/*
+ * Training pair: a forward that keeps the segment start states and a backward
+ * that reads them instead of recomputing them.  App. B's training scheme
+ * recomputes the per-chunk states in the backward (checkpointing, only pass
+ * 1's output saved); here the forward's own state maps and scan -- the same
+ * kernels the backward would run, on the backward's split of the sequence --
+ * leave the state at the start of every segment, O(N d m / segment length)
+ * floats, for the backward to read.  Compiled where the backward runs on the
+ * matrix cores: bf16, dense batches, every read but ReLU, and the shapes of
+ * gsa_bwd (m = 128 included); GSA_ERR_UNSUPPORTED otherwise.
+ *
+ * gsa_train_states_bytes: bytes of the kept states ((size_t)-1 on invalid
+ * arguments, 0 for T = 0 or an uncompiled combination).
+ * gsa_fwd_train_workspace_bytes: workspace of gsa_fwd_train (the decay
+ * products of the split, and for m = 128 the slot groups' rows).
+ * gsa_fwd_train: gsa_fwd_ex with C = 64 and the backward's split; in addition
+ *   states  device, float32, states_bytes >= gsa_train_states_bytes(...)
+ *           (written; owned by the caller; must not overlap any other
+ *           argument).  Errors as gsa_fwd_ex, GSA_ERR_NULL for a missing
+ *           states buffer, GSA_ERR_WORKSPACE for a short one.
+ * gsa_bwd_train: gsa_bwd_ex given the states that gsa_fwd_train wrote for the
+ *   same q, k, v, g, k0, v0, tau and slot read (the caller keeps them
+ *   unchanged in between; the library does not check that they match).  The
+ *   workspace query is gsa_bwd_workspace_bytes_ex's (an upper bound here).
+ *   The states are only read; outputs must not overlap them (GSA_ERR_ALIAS).
+ */
+size_t gsa_train_states_bytes(int B, int H, int T, int dk, int dv, int m, int dtype);
+size_t gsa_fwd_train_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int dtype);
+int gsa_fwd_train(const void* q, const void* k, const void* v, const void* g, const float* k0,
+                  const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T, int dk,
+                  int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+                  float* states, size_t states_bytes, int nonlinearity, void* stream,
+                  void* const* events);
+int gsa_bwd_train(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+                  const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+                  void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+                  int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+                  const float* states, size_t states_bytes, int nonlinearity, void* stream,
+                  void* const* events);
 
 /*
  * gsa_bwd over a packed batch of n_seqs variable-length sequences laid out as

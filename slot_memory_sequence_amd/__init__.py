@@ -20,7 +20,9 @@ __all__ = ["lib", "gsa_fwd", "gsa_fwd_varlen", "gla_fwd", "gsa_decode_step", "gl
            "GsaError", "LIB_PATH",
            "NONLINEARITIES", "gsa_fwd_varlen_workspace_bytes",
            "gsa_fwd_supported", "gla_fwd_supported", "gsa_decode_supported",
-           "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string"]
+           "gsa_fwd_workspace_bytes", "gla_fwd_workspace_bytes", "status_string",
+           "gsa_bwd", "gsa_bwd_varlen", "gsa_autograd", "gsa_fwd_train", "gsa_bwd_train",
+           "gsa_train_states_bytes", "gsa_train_supported"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -86,6 +88,14 @@ lib.gsa_bwd_ex.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _I, _P, _P]
 lib.gsa_bwd_varlen_workspace_bytes.argtypes = [_P] + [_I] * 5
 lib.gsa_bwd_varlen_workspace_bytes.restype = _S
 lib.gsa_bwd_varlen.argtypes = [_P] * 5 + [_P, _I, _I] + [_P] * 10 + [_I] * 3 + [_F, _I, _P, _S, _P, _P]
+lib.gsa_train_states_bytes.restype = _S
+lib.gsa_train_states_bytes.argtypes = [_I] * 7
+lib.gsa_fwd_train_workspace_bytes.restype = _S
+lib.gsa_fwd_train_workspace_bytes.argtypes = [_I] * 7
+lib.gsa_fwd_train.restype = _I
+lib.gsa_fwd_train.argtypes = [_P] * 9 + [_I] * 6 + [_F, _I, _P, _S, _P, _S, _I, _P, _P]
+lib.gsa_bwd_train.restype = _I
+lib.gsa_bwd_train.argtypes = [_P] * 15 + [_I] * 6 + [_F, _I, _P, _S, _P, _S, _I, _P, _P]
 lib.gsa_fwd_noalloc_scratch_bytes.restype = _S
 lib.gsa_fwd_noalloc_scratch_bytes.argtypes = []
 lib.gsa_fwd_noalloc.restype = _I
@@ -219,14 +229,9 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
-            chunks_per_segment=0, out=None, k_final=None, v_final=None, workspace=None,
-            stream=None, events=None, nonlinearity="softmax"):
-    """Chunkwise GSA forward.  q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m] (gate
-    logits); optional float32 initial slot states k0 [B,H,m,dk], v0 [B,H,m,dv].
-    nonlinearity: the slot read, "softmax" (GSA) or one of the element-wise
-    ablations "identity", "swish", "relu", "relu2".
-    Returns (o, k_final, v_final) -- the finals are None unless final_state."""
+def _fwd_prep(q, k, v, g, k0, v0, out, k_final, v_final, final_state):
+    """Shape and dtype checks of a GSA forward's tensors; allocates the
+    missing outputs.  Returns ((B, H, T, dk, dv, m), out, k_final, v_final)."""
     torch = _torch()
     _ndim(q, "q", 4)
     B, H, T, dk = q.shape
@@ -241,7 +246,6 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
         _check(t, n, q.dtype)
     for n, t in (("k0", k0), ("v0", v0), ("k_final", k_final), ("v_final", v_final)):
         _check(t, n, torch.float32)
-    dt = _dt(q)
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
     if final_state:
@@ -249,6 +253,21 @@ def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
             k_final = torch.empty((B, H, m, dk), dtype=torch.float32, device=q.device)
         if v_final is None:
             v_final = torch.empty((B, H, m, dv), dtype=torch.float32, device=q.device)
+    return (B, H, T, dk, dv, m), out, k_final, v_final
+
+
+def gsa_fwd(q, k, v, g, k0=None, v0=None, *, tau=8.0, C=64, final_state=False,
+            chunks_per_segment=0, out=None, k_final=None, v_final=None, workspace=None,
+            stream=None, events=None, nonlinearity="softmax"):
+    """Chunkwise GSA forward.  q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T,m] (gate
+    logits); optional float32 initial slot states k0 [B,H,m,dk], v0 [B,H,m,dv].
+    nonlinearity: the slot read, "softmax" (GSA) or one of the element-wise
+    ablations "identity", "swish", "relu", "relu2".
+    Returns (o, k_final, v_final) -- the finals are None unless final_state."""
+    torch = _torch()
+    (B, H, T, dk, dv, m), out, k_final, v_final = _fwd_prep(q, k, v, g, k0, v0, out, k_final, v_final,
+                                                             final_state)
+    dt = _dt(q)
     nbytes = gsa_fwd_workspace_bytes(B, H, T, dk, dv, m, C, dt, chunks_per_segment)
     if nbytes == (1 << 64) - 1:
         raise ValueError("invalid problem size")
@@ -459,16 +478,9 @@ def gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, dtype=None, nonlinearity="softma
     return int(lib.gsa_bwd_workspace_bytes_ex(B, H, T, dk, dv, m, int(dtype), _nl(nonlinearity)))
 
 
-def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
-            state_grads=False, out=None, workspace=None, stream=None, events=None,
-            nonlinearity="softmax"):
-    """GSA backward (softmax read): the gradients of gsa_fwd(q, k, v, g, k0,
-    v0, tau=tau) given d_o [B,H,T,dv] (the gradient of o) and optional float32
-    d_kf [B,H,m,dk] / d_vf [B,H,m,dv] (those of the final states).
-    Returns (d_q, d_k, d_v, d_g, d_k0, d_v0); d_k0 / d_v0 (float32) are None
-    unless state_grads.  out: optional (d_q, d_k, d_v, d_g) to write into.
-    nonlinearity: the slot read of the forward being differentiated, as for
-    gsa_fwd."""
+def _bwd_prep(q, k, v, g, d_o, k0, v0, d_kf, d_vf, out, state_grads):
+    """Shape and dtype checks of a GSA backward's tensors; allocates the
+    gradients.  Returns ((B, H, T, dk, dv, m), [d_q, d_k, d_v, d_g], [d_k0, d_v0])."""
     torch = _torch()
     _ndim(q, "q", 4)
     B, H, T, dk = q.shape
@@ -496,6 +508,21 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
     sg = [None, None]
     if state_grads:
         sg = [torch.empty((B, H, m, d), dtype=torch.float32, device=q.device) for d in (dk, dv)]
+    return (B, H, T, dk, dv, m), outs, sg
+
+
+def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
+            state_grads=False, out=None, workspace=None, stream=None, events=None,
+            nonlinearity="softmax"):
+    """GSA backward (softmax read): the gradients of gsa_fwd(q, k, v, g, k0,
+    v0, tau=tau) given d_o [B,H,T,dv] (the gradient of o) and optional float32
+    d_kf [B,H,m,dk] / d_vf [B,H,m,dv] (those of the final states).
+    Returns (d_q, d_k, d_v, d_g, d_k0, d_v0); d_k0 / d_v0 (float32) are None
+    unless state_grads.  out: optional (d_q, d_k, d_v, d_g) to write into.
+    nonlinearity: the slot read of the forward being differentiated, as for
+    gsa_fwd."""
+    torch = _torch()
+    (B, H, T, dk, dv, m), outs, sg = _bwd_prep(q, k, v, g, d_o, k0, v0, d_kf, d_vf, out, state_grads)
     nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, _dt(q), nonlinearity)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -506,6 +533,68 @@ def gsa_bwd(q, k, v, g, d_o, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
                         _stream(stream), _events(events))
     if st:
         raise GsaError("gsa_bwd", st)
+    return (*outs, sg[0], sg[1])
+
+
+def gsa_train_states_bytes(B, H, T, dk, dv, m, dtype=DTYPE_BF16) -> int:
+    """Bytes of the segment start states gsa_fwd_train keeps for
+    gsa_bwd_train (0: nothing to keep, or the pair is not compiled here)."""
+    return int(lib.gsa_train_states_bytes(B, H, T, dk, dv, m, dtype))
+
+
+def gsa_train_supported(q, v, g, nonlinearity="softmax") -> bool:
+    """Whether gsa_fwd_train / gsa_bwd_train run for these tensors and read
+    (bf16, the matrix-core backward's shapes, not ReLU)."""
+    dk, dv, m = q.shape[-1], v.shape[-1], g.shape[-1]
+    return (q.dtype == _torch().bfloat16 and _nl(nonlinearity) != NONLINEARITIES["relu"] and
+            gsa_fwd_supported(dk, dv, m, 64, DTYPE_BF16) and gsa_bwd_supported(dk, dv, m, DTYPE_BF16))
+
+
+def gsa_fwd_train(q, k, v, g, k0=None, v0=None, *, tau=8.0, final_state=False, out=None, k_final=None,
+                  v_final=None, states=None, workspace=None, stream=None, events=None,
+                  nonlinearity="softmax"):
+    """gsa_fwd that also keeps the segment start states of the backward's
+    split (a uint8 device tensor of gsa_train_states_bytes bytes, allocated
+    when `states` is None).  Returns (o, k_final, v_final, states)."""
+    torch = _torch()
+    (B, H, T, dk, dv, m), out, k_final, v_final = _fwd_prep(q, k, v, g, k0, v0, out, k_final, v_final,
+                                                             final_state)
+    dt = _dt(q)
+    sb = gsa_train_states_bytes(B, H, T, dk, dv, m, dt)
+    if sb == (1 << 64) - 1:
+        raise ValueError("invalid problem size")
+    if states is None:
+        states = torch.empty(max(sb, 1), dtype=torch.uint8, device=q.device)
+    nbytes = int(lib.gsa_fwd_train_workspace_bytes(B, H, T, dk, dv, m, dt))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_fwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(k0), _ptr(v0), _ptr(out),
+                           _ptr(k_final), _ptr(v_final), B, H, T, dk, dv, m, float(tau), dt,
+                           _ptr(workspace), _wsbytes(workspace), _ptr(states), _wsbytes(states),
+                           _nl(nonlinearity), _stream(stream), _events(events))
+    if st:
+        raise GsaError("gsa_fwd_train", st)
+    return out, k_final, v_final, states
+
+
+def gsa_bwd_train(q, k, v, g, d_o, states, k0=None, v0=None, d_kf=None, d_vf=None, *, tau=8.0,
+                  state_grads=False, out=None, workspace=None, stream=None, events=None,
+                  nonlinearity="softmax"):
+    """gsa_bwd given the states gsa_fwd_train kept for the same inputs (they
+    replace the backward's own recomputation of the segment start states).
+    Returns (d_q, d_k, d_v, d_g, d_k0, d_v0) as gsa_bwd."""
+    torch = _torch()
+    (B, H, T, dk, dv, m), outs, sg = _bwd_prep(q, k, v, g, d_o, k0, v0, d_kf, d_vf, out, state_grads)
+    nbytes = gsa_bwd_workspace_bytes(B, H, T, dk, dv, m, _dt(q), nonlinearity)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    st = lib.gsa_bwd_train(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(d_o), _ptr(k0), _ptr(v0),
+                           _ptr(d_kf), _ptr(d_vf), *(_ptr(x) for x in outs), _ptr(sg[0]), _ptr(sg[1]),
+                           B, H, T, dk, dv, m, float(tau), _dt(q), _ptr(workspace), _wsbytes(workspace),
+                           _ptr(states), _wsbytes(states), _nl(nonlinearity), _stream(stream),
+                           _events(events))
+    if st:
+        raise GsaError("gsa_bwd_train", st)
     return (*outs, sg[0], sg[1])
 
 
@@ -560,14 +649,23 @@ def _autograd_function():
     torch = _torch()
 
     class GsaFunction(torch.autograd.Function):
-        """gsa_fwd (final states returned) with gsa_bwd as its backward."""
+        """gsa_fwd (final states returned) with gsa_bwd as its backward (the
+        training pair gsa_fwd_train / gsa_bwd_train where it runs)."""
 
         @staticmethod
         def forward(ctx, q, k, v, g, k0, v0, tau, nonlinearity):
             ctx.set_materialize_grads(False)
-            o, kf, vf = gsa_fwd(q, k, v, g, k0, v0, tau=tau, final_state=True,
-                                nonlinearity=nonlinearity)
+            # where the training pair runs, the forward keeps the segment start
+            # states and the backward reads them instead of recomputing them
+            states = None
+            if gsa_train_supported(q, v, g, nonlinearity):
+                o, kf, vf, states = gsa_fwd_train(q, k, v, g, k0, v0, tau=tau, final_state=True,
+                                                  nonlinearity=nonlinearity)
+            else:
+                o, kf, vf = gsa_fwd(q, k, v, g, k0, v0, tau=tau, final_state=True,
+                                    nonlinearity=nonlinearity)
             ctx.save_for_backward(q, k, v, g, k0, v0)
+            ctx.states = states
             ctx.tau, ctx.nonlinearity = tau, nonlinearity
             return o, kf, vf
 
@@ -577,10 +675,15 @@ def _autograd_function():
             q, k, v, g, k0, v0 = ctx.saved_tensors
             if d_o is None:
                 d_o = torch.zeros_like(v)
-            grads = gsa_bwd(q, k, v, g, d_o.contiguous(), k0, v0,
-                            None if d_kf is None else d_kf.contiguous(),
-                            None if d_vf is None else d_vf.contiguous(), tau=ctx.tau,
-                            state_grads=True, nonlinearity=ctx.nonlinearity)
+            dkf = None if d_kf is None else d_kf.contiguous()
+            dvf = None if d_vf is None else d_vf.contiguous()
+            if ctx.states is not None:
+                grads = gsa_bwd_train(q, k, v, g, d_o.contiguous(), ctx.states, k0, v0, dkf, dvf,
+                                      tau=ctx.tau, state_grads=True, nonlinearity=ctx.nonlinearity)
+                ctx.states = None
+            else:
+                grads = gsa_bwd(q, k, v, g, d_o.contiguous(), k0, v0, dkf, dvf, tau=ctx.tau,
+                                state_grads=True, nonlinearity=ctx.nonlinearity)
             dk0 = grads[4] if k0 is not None and ctx.needs_input_grad[4] else None
             dv0 = grads[5] if v0 is not None and ctx.needs_input_grad[5] else None
             return grads[0], grads[1], grads[2], grads[3], dk0, dv0, None, None

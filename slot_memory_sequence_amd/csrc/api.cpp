@@ -80,10 +80,14 @@ size_t ws_bytes(long long units, int T, int cps, size_t state_elems, size_t dec_
 // (G = slot_groups(dtype, m)), then with G > 1 the groups' output rows
 // ([units*T][G][dv], I/O dtype) at *part_off and log-sum-exps ([units*T][G]
 // fp32) at *lse_off.
+// keep (the training forward): the start states live in the caller's buffer,
+// the workspace holds the decay products only (P >= 1 segments).
 size_t fwd_ws_bytes(long long units, int T, int c, int dk, int dv, int m, int dtype,
-                    size_t* part_off = nullptr, size_t* lse_off = nullptr) {
+                    size_t* part_off = nullptr, size_t* lse_off = nullptr, bool keep = false) {
   const int G = gsa::slot_groups(dtype, m);
-  const size_t maps = ws_bytes(units * G, T, c, (size_t)(m / G) * (dk + dv), (size_t)(m / G));
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const size_t maps = !keep ? ws_bytes(units * G, T, c, (size_t)(m / G) * (dk + dv), (size_t)(m / G))
+                            : (size_t)units * ((nchunks + c - 1) / c) * m * 4;
   if (G == 1 || T == 0 || units == 0) return maps;
   const size_t rows = (size_t)units * T;
   const size_t po = (maps + 255) & ~(size_t)255;
@@ -135,12 +139,13 @@ int resolve_cps_var(int H, int tmax, long long chunks_per_head, int cps) {
 int gsa_run(const void* q, const void* k, const void* v, const void* g, const float* k0,
             const float* v0, void* o, float* kf, float* vf, int B, int H, int T, size_t ntok, int c,
             const int* cu, int dk, int dv, int m, float tau, int dtype, void* workspace,
-            size_t workspace_bytes, int nonlinearity, void* stream, void* const* events) {
+            size_t workspace_bytes, int nonlinearity, void* stream, void* const* events,
+            float* keep = nullptr, size_t keep_bytes = 0) {
   const long long units = (long long)B * H;
   // units of one launch sequence (a packed batch runs in groups of sequences)
   const long long ws_units = cu ? (long long)std::min(B, gsa::kMaxVarSeqs) * H : units;
   if (ntok > 0 && (!q || !k || !v || !g || !o)) return GSA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace};
+  const void* ptrs[] = {q, k, v, g, k0, v0, o, kf, vf, workspace, keep};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GSA_ERR_ALIGN;
   const size_t es = esize(dtype);
@@ -160,10 +165,13 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
     return GSA_ERR_ALIAS;
   for (Range in : {rq, rk, rv, rg, rk0, rv0})
     if (overlap(rws, in)) return GSA_ERR_ALIAS;
+  const Range rkeep = rng(keep, keep_bytes);
+  for (Range in : {rq, rk, rv, rg, rk0, rv0, ro, rkf, rvf, rws})
+    if (overlap(rkeep, in)) return GSA_ERR_ALIAS;
   const int G = gsa::slot_groups(dtype, m);
   if (cu && G > 1) return GSA_ERR_UNSUPPORTED;
   size_t part_off = 0, lse_off = 0;
-  const size_t need = fwd_ws_bytes(ws_units, T, c, dk, dv, m, dtype, &part_off, &lse_off);
+  const size_t need = fwd_ws_bytes(ws_units, T, c, dk, dv, m, dtype, &part_off, &lse_off, keep != nullptr);
   if (need > 0 && (!workspace || workspace_bytes < need)) return GSA_ERR_WORKSPACE;
 
   if (T == 0) {  // nothing to read: the final state is the initial state
@@ -176,10 +184,16 @@ int gsa_run(const void* q, const void* k, const void* v, const void* g, const fl
   a.q = q; a.k = k; a.v = v; a.g = g; a.k0 = k0; a.v0 = v0; a.o = o; a.kf = kf; a.vf = vf;
   const int nchunks = (T + kChunk - 1) / kChunk;
   const long long P = (nchunks + c - 1) / c;
-  a.ws_state = (float*)workspace;
-  a.ws_dec = workspace ? (float*)((char*)workspace +
-                                  (((size_t)ws_units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
-                       : nullptr;
+  if (keep) {
+    a.ws_state = keep;
+    a.ws_dec = (float*)workspace;
+    a.keep_states = keep;
+  } else {
+    a.ws_state = (float*)workspace;
+    a.ws_dec = workspace ? (float*)((char*)workspace +
+                                    (((size_t)ws_units * P * m * (dk + dv) * 4 + 255) & ~(size_t)255))
+                         : nullptr;
+  }
   a.B = B; a.H = H; a.T = T; a.chunks_per_seg = c; a.tau = tau; a.act = nonlinearity;
   a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
   if (G > 1) {
@@ -503,8 +517,9 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
                    void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
                    size_t ntok, const int* cu, int dk, int dv, int m, float tau, int dtype,
                    void* workspace, size_t workspace_bytes, int nonlinearity, void* stream,
-                   void* const* events) {
+                   void* const* events, const float* saved = nullptr, size_t saved_bytes = 0) {
   if (!gsa_bwd_supported(dk, dv, m, dtype)) return GSA_ERR_UNSUPPORTED;
+  if (saved && !gsa::gsa_bwd_on_mfma(dtype, nonlinearity, cu != nullptr)) return GSA_ERR_UNSUPPORTED;
   // two slot groups (bf16, m = 128): dense batches and the smooth reads only
   if (gsa::slot_groups(dtype, m) > 1 && (cu || nonlinearity == GSA_SLOT_RELU)) return GSA_ERR_UNSUPPORTED;
   const long long units = (long long)B * H;
@@ -515,7 +530,7 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
   if (((long long)T + kChunk - 1) / kChunk > 65535) return GSA_ERR_UNSUPPORTED;  // chunks: grid y
   if (ntok > 0 && (!q || !k || !v || !g || !d_o || !d_q || !d_k || !d_v || !d_g))
     return GSA_ERR_NULL;
-  const void* ptrs[] = {q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, workspace};
+  const void* ptrs[] = {q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, workspace, saved};
   for (const void* p : ptrs)
     if (!aligned16(p)) return GSA_ERR_ALIGN;
   const size_t es = esize(dtype);
@@ -531,6 +546,9 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
                             : 0;
   const Range rws = rng(workspace, need);
   const Range outs[] = {rdq, rdk, rdv, rdg, rdk0, rdv0, rws};
+  const Range rsaved = rng(saved, saved_bytes);
+  for (Range out : outs)
+    if (overlap(out, rsaved)) return GSA_ERR_ALIAS;
   const Range ins[] = {rq, rk, rv, rg, rdo, rk0, rv0, rkf, rvf};
   for (int i = 0; i < 7; i++) {
     for (Range in : ins)
@@ -546,6 +564,7 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
   a.ws = (float*)workspace;
   a.B = B; a.H = H; a.T = T; a.tau = tau; a.act = nonlinearity;
   a.cu_seqlens = cu; a.n_seqs = cu ? B : 0;
+  a.saved_states = saved;
   a.stream = stream; a.events = events;
   (void)hipGetLastError();
   if (gsa::gsa_bwd_dispatch(dtype, dk, dv, m, &a, false) != 0) return GSA_ERR_UNSUPPORTED;
@@ -578,6 +597,75 @@ int gsa_bwd_varlen(const void* q, const void* k, const void* v, const void* g, c
   return bwd_run(q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, n_seqs, H, tmax,
                  (size_t)H * (size_t)cu_seqlens[n_seqs], cu_seqlens, dk, dv, m, tau, dtype, workspace,
                  workspace_bytes, GSA_SLOT_SOFTMAX, stream, events);
+}
+
+// ---------------------------------------------------------------- training pair
+// The chunks per segment of the training pair: the matrix-core backward's split
+// of this problem (units * groups units).
+static int train_cps(long long units, int T, int G) {
+  return gsa::gsa_bwd_chunks_per_segment(units * G, (T + kChunk - 1) / kChunk);
+}
+
+// The pair runs where the backward runs on the matrix cores: bf16, every read
+// but ReLU (dense batches only, checked by the entry points).
+static bool train_ok(int dk, int dv, int m, int dtype, int nonlinearity) {
+  return dtype == GSA_DTYPE_BF16 && gsa_fwd_supported(dk, dv, m, kChunk, dtype) &&
+         gsa_bwd_supported(dk, dv, m, dtype) && gsa::gsa_bwd_on_mfma(dtype, nonlinearity, false);
+}
+
+size_t gsa_train_states_bytes(int B, int H, int T, int dk, int dv, int m, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !dtype_ok(dtype)) return (size_t)-1;
+  if (!train_ok(dk, dv, m, dtype, GSA_SLOT_SOFTMAX) || T == 0) return 0;
+  const long long units = (long long)B * H;
+  const int G = gsa::slot_groups(dtype, m), c = train_cps(units, T, G);
+  const long long P = ((T + kChunk - 1) / kChunk + c - 1) / c;
+  return (size_t)units * P * m * (dk + dv) * 4;
+}
+
+size_t gsa_fwd_train_workspace_bytes(int B, int H, int T, int dk, int dv, int m, int dtype) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !dtype_ok(dtype)) return (size_t)-1;
+  const long long units = (long long)B * H;
+  const int G = gsa::slot_groups(dtype, m);
+  return fwd_ws_bytes(units, T, train_cps(units, T, G), dk, dv, m, dtype, nullptr, nullptr, true);
+}
+
+int gsa_fwd_train(const void* q, const void* k, const void* v, const void* g, const float* k0,
+                  const float* v0, void* o, float* kf, float* vf, int B, int H, int T, int dk, int dv,
+                  int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+                  float* states, size_t states_bytes, int nonlinearity, void* stream,
+                  void* const* events) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) || !std::isfinite(tau) ||
+      !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
+    return GSA_ERR_SHAPE;
+  if (!train_ok(dk, dv, m, dtype, nonlinearity)) return GSA_ERR_UNSUPPORTED;
+  const long long units = (long long)B * H;
+  const int G = gsa::slot_groups(dtype, m);
+  if (units * G > kMaxUnits) return GSA_ERR_UNSUPPORTED;
+  if (units == 0) return GSA_OK;
+  const size_t need = gsa_train_states_bytes(B, H, T, dk, dv, m, dtype);
+  if (need > 0 && !states) return GSA_ERR_NULL;
+  if (states_bytes < need) return GSA_ERR_WORKSPACE;
+  return gsa_run(q, k, v, g, k0, v0, o, kf, vf, B, H, T, (size_t)units * T, train_cps(units, T, G),
+                 nullptr, dk, dv, m, tau, dtype, workspace, workspace_bytes, nonlinearity, stream, events,
+                 need > 0 ? states : nullptr, need);
+}
+
+int gsa_bwd_train(const void* q, const void* k, const void* v, const void* g, const void* d_o,
+                  const float* k0, const float* v0, const float* d_kf, const float* d_vf, void* d_q,
+                  void* d_k, void* d_v, void* d_g, float* d_k0, float* d_v0, int B, int H, int T,
+                  int dk, int dv, int m, float tau, int dtype, void* workspace, size_t workspace_bytes,
+                  const float* states, size_t states_bytes, int nonlinearity, void* stream,
+                  void* const* events) {
+  if (B < 0 || H < 0 || T < 0 || dk < 1 || dv < 1 || m < 1 || !(tau > 0.f) ||
+      !std::isfinite(tau) || !dtype_ok(dtype) || !nonlinearity_ok(nonlinearity))
+    return GSA_ERR_SHAPE;
+  if (!train_ok(dk, dv, m, dtype, nonlinearity)) return GSA_ERR_UNSUPPORTED;
+  const size_t need = gsa_train_states_bytes(B, H, T, dk, dv, m, dtype);
+  if (need > 0 && !states) return GSA_ERR_NULL;
+  if (states_bytes < need) return GSA_ERR_WORKSPACE;
+  return bwd_run(q, k, v, g, d_o, k0, v0, d_kf, d_vf, d_q, d_k, d_v, d_g, d_k0, d_v0, B, H, T,
+                 (size_t)B * H * T, nullptr, dk, dv, m, tau, dtype, workspace, workspace_bytes,
+                 nonlinearity, stream, events, need > 0 ? states : nullptr, need);
 }
 
 int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const void* d_o,

@@ -1454,8 +1454,10 @@ int launch(const GsaBwdLaunch& a) {
     return true;
   }();
   (void)lds_set;
-  if (gsa_bf16_segment_states(DK, DV, M, G, a.k, a.v, a.g, a.k0, a.v0, w.st, w.dec, U, T, S, P, a.tau,
-                              a.stream) != 0)
+  if (a.saved_states)  // the training forward's start states (same split), read only
+    w.st = const_cast<float*>(a.saved_states);
+  else if (gsa_bf16_segment_states(DK, DV, M, G, a.k, a.v, a.g, a.k0, a.v0, w.st, w.dec, U, T, S, P, a.tau,
+                                   a.stream) != 0)
     return -1;
   const bf16_t *q = (const bf16_t*)a.q, *k = (const bf16_t*)a.k, *v = (const bf16_t*)a.v, *g = (const bf16_t*)a.g,
                *dO = (const bf16_t*)a.d_o;
@@ -1514,6 +1516,8 @@ int launch_act(const GsaBwdLaunch& a) {
 }
 
 }  // namespace bfb
+
+int gsa_bwd_chunks_per_segment(long long units, int nchunks) { return bfb::chunks_per_segment(units, nchunks); }
 
 // The dense bf16 backward on the matrix cores: returns the workspace bytes
 // (query) or launches (0); -1 if (dk, dv, m) is not compiled for it.

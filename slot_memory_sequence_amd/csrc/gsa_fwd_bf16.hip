@@ -722,7 +722,8 @@ static int launch(const GsaLaunch& a, const Seq& seq) {
   // output workgroup then reads k0 / v0, so not when the final state is written
   // over them (the last segment could finish before another one has started).
   const bool in_place = (a.kf && a.kf == a.k0) || (a.vf && a.vf == a.v0);
-  const int fold = P > 1 && P - 1 <= kMaxFoldedMaps && !in_place;
+  const bool keep = a.keep_states != nullptr;
+  const int fold = !keep && P > 1 && P - 1 <= kMaxFoldedMaps && !in_place;
   if (P > 1) {
     launch_timed(gsa_bf16_state<DK, DV, M, Seq>, dim3(P - 1, units), dim3(NT), LS::total, a.stream,
                  a.events, 0, 1, (const bf16_t*)a.k, (const bf16_t*)a.v, (const bf16_t*)a.g,
@@ -735,6 +736,11 @@ static int launch(const GsaLaunch& a, const Seq& seq) {
   } else {
     record_event(a.events, 0, a.stream);
     record_event(a.events, 1, a.stream);
+    if (keep) {  // one segment: its start state is the initial state
+      const long long ne = (long long)units * M * (DK + DV) / 4;
+      hipLaunchKernelGGL((gsa_bf16_scan<DK, DV, M>), dim3((unsigned)((ne + 255) / 256)), dim3(256), 0, st,
+                         a.ws_state, (const float*)a.ws_dec, a.k0, a.v0, units, P);
+    }
   }
   launch_timed(gsa_bf16_out<DK, DV, M, ACT, Seq>, dim3(P * units), dim3(NT), LO::total, a.stream,
                a.events, 2, 3, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,

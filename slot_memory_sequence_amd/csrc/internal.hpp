@@ -28,6 +28,11 @@ struct GsaLaunch {
   // [B*H*T][2] fp32, in the workspace after the segment maps
   void* ws_part;
   float* ws_lse;
+  // nullable: keep the segment start states for the backward.  ws_state is
+  // then this buffer ([units * groups][P][m / groups][dk+dv] fp32), the maps
+  // are never folded by the output kernel, and the scan also runs for P = 1
+  // (its one slot is the initial state).
+  float* keep_states;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t, see gsa_fwd_events
 };
@@ -101,6 +106,9 @@ struct GsaBwdLaunch {
   // (validated), B = n_seqs, T = the longest length, rows [H, total, d]
   const int* cu_seqlens;
   int n_seqs;
+  // nullable: the segment start states a training forward kept (the
+  // matrix-core path reads them instead of recomputing them)
+  const float* saved_states;
   void* stream;
   void* const* events;  // nullable: 4 hipEvent_t around the two token-walk kernels
 };
@@ -122,6 +130,9 @@ int gsa_bwd_dispatch(int dtype, int dk, int dv, int m, const GsaBwdLaunch* a, bo
 // workspace bytes for `units` units of T tokens; launch -> 0; -1 if (dk, dv,
 // m) is not compiled for it.
 long long gsa_bwd_bf16_dispatch(int dk, int dv, int m, const GsaBwdLaunch* a, bool query, size_t units, int T);
+// Chunks per segment of the matrix-core backward for `units` (group) units of
+// nchunks chunks: the split a training forward keeps its start states for.
+int gsa_bwd_chunks_per_segment(long long units, int nchunks);
 // Workspace bytes of the backward a call with these arguments runs: the
 // matrix-core path for a dense bf16 batch, the token-walk path otherwise
 // (float32, packed batches: `rows` token rows, `units` units of `chunks`

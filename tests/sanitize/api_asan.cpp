@@ -58,6 +58,11 @@ size_t gsa_bwd_need_bytes(int dtype, int act, bool packed, size_t units, size_t 
   return gsa_bwd_ws_bytes(units, chunks, rows, dk, dv, m) / (gsa_bwd_on_mfma(dtype, act, packed) ? 2 : 1) +
          (size_t)T * 0;
 }
+int gsa_bwd_chunks_per_segment(long long units, int nchunks) {
+  const long long p = units > 0 && units < 256 ? 256 / units : 1;
+  const long long s = (nchunks + p - 1) / p;
+  return (int)(s < 1 ? 1 : s > 8 ? 8 : s);
+}
 void state_copy(float*, const float*, size_t, void*) {}
 void record_event(void* const*, int, void*) {}
 }  // namespace gsa

@@ -29,7 +29,7 @@ def test_header_symbols_exported(gsa):
     assert {"gsa_fwd", "gla_fwd", "gsa_decode_step", "gsa_abi_version"} <= set(names)
     for n in names:
         assert hasattr(gsa.lib, n), "missing export: " + n
-    assert gsa.lib.gsa_abi_version() == 4
+    assert gsa.lib.gsa_abi_version() == 5
 
 
 def test_status_strings(gsa):
@@ -369,3 +369,54 @@ def test_noalloc_rejects_before_touching_the_device(gsa):
     assert f(*args, B, H, T, 128, 128, 64, 64, 8.0, 1, 1, 0, None, None) == 8
     assert gsa.status_string(8) != "unknown status"
     assert f(*args, -1, H, T, 128, 128, 64, 64, 8.0, 1, 0, 0, None, None) == 2
+
+
+def test_train_pair_validation(gsa):
+    """gsa_fwd_train / gsa_bwd_train: sizes, support and reject paths (every
+    call below fails validation before anything is enqueued)."""
+    P = ctypes.c_void_p
+    a256 = lambda x: (x + 255) // 256 * 256
+    # the backward's split at B8 H4 T2048: 8 segments of 4 chunks per unit
+    assert gsa.gsa_train_states_bytes(8, 4, 2048, 128, 128, 64) == 32 * 8 * 64 * 256 * 4
+    # 128 slots: 64 group units, 4 segments of 8 chunks, the same bytes per segment and slot
+    assert gsa.gsa_train_states_bytes(8, 4, 2048, 128, 128, 128) == 64 * 4 * 64 * 256 * 4
+    assert gsa.gsa_train_states_bytes(8, 4, 2048, 128, 128, 64, 0) == 0      # float32: not compiled
+    assert gsa.gsa_train_states_bytes(8, 4, 0, 128, 128, 64) == 0
+    assert gsa.gsa_train_states_bytes(-1, 4, 64, 128, 128, 64) == (1 << 64) - 1
+    # workspace of the training forward: the decay products only (m = 64)
+    assert gsa.lib.gsa_fwd_train_workspace_bytes(8, 4, 2048, 128, 128, 64, 1) == 32 * 8 * 64 * 4
+    assert gsa.lib.gsa_fwd_train_workspace_bytes(8, 4, 2048, 128, 128, 128, 1) == \
+        a256(a256(64 * 4 * 64 * 4) + 32 * 2048 * 2 * 128 * 2) + 32 * 2048 * 2 * 4
+
+    need = gsa.gsa_train_states_bytes(1, 1, 256, 128, 128, 64)
+    wsf = gsa.lib.gsa_fwd_train_workspace_bytes(1, 1, 256, 128, 128, 64, 1)
+
+    def fwd(**kw):
+        a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, g=FAKE + 0x300000, o=FAKE + 0x400000,
+                 ws=FAKE + 0x500000, wsb=wsf, st=FAKE + 0x600000, stb=need, nl=0, dtype=1, m=64)
+        a.update(kw)
+        return gsa.lib.gsa_fwd_train(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), None, None, P(a["o"]), None,
+                                     None, 1, 1, 256, 128, 128, a["m"], 8.0, a["dtype"], P(a["ws"]), a["wsb"],
+                                     P(a["st"]), a["stb"], a["nl"], None, None)
+
+    assert fwd(nl=3) == 4                      # ReLU: the backward keeps its token walks
+    assert fwd(dtype=0) == 4                   # float32
+    assert fwd(st=None) == 1                   # states buffer missing
+    assert fwd(stb=need - 4) == 5              # states buffer too small
+    assert fwd(st=FAKE + 0x400000) == 7        # states over the output
+    assert fwd(st=FAKE + 0x600004) == 3        # misaligned states
+    assert fwd(wsb=wsf - 4) == 5
+
+    def bwd(**kw):
+        a = dict(st=FAKE + 0x900000, stb=need, nl=0, dq=FAKE + 0x500000, ws=FAKE + 0xa00000)
+        a.update(kw)
+        return gsa.lib.gsa_bwd_train(P(FAKE), P(FAKE + 0x100000), P(FAKE + 0x200000), P(FAKE + 0x300000),
+                                     P(FAKE + 0x400000), None, None, None, None, P(a["dq"]),
+                                     P(FAKE + 0x600000), P(FAKE + 0x700000), P(FAKE + 0x800000), None, None,
+                                     1, 1, 256, 128, 128, 64, 8.0, 1, P(a["ws"]), 1 << 30, P(a["st"]),
+                                     a["stb"], a["nl"], None, None)
+
+    assert bwd(nl=3) == 4
+    assert bwd(st=None) == 1
+    assert bwd(stb=need - 4) == 5
+    assert bwd(dq=FAKE + 0x900000) == 7        # an output over the states
