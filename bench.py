@@ -426,7 +426,7 @@ def bwd_parity(torch, w, inp, grads):
                                for x, n in zip(grads, ("dq", "dk", "dv", "dg"))))
 
 
-def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd", cpu=True):
+def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd", cpu=True, pair=True):
     """The GSA backward at a workload's shape (the training shape B8 H4 T2048
     bf16 with zero states, or the long-context one with initial states and
     final-state gradients), dO ~ N(0, 1); two input sets rotated."""
@@ -451,6 +451,25 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     t_f, t_r = mean([p[0] for p in ph]), mean([p[2] for p in ph])
     al = gsa_bwd_chunk_alg(B, H, T, dk, dv, m, w["C"], 2)
     nbytes = al["bytes"]
+    kern, kb, t = ("bwd_bf16_fwd", al["bytes_fwd"], t_f) if t_f >= t_r else ("bwd_bf16_rev", al["bytes_rev"], t_r)
+    t_op = wall / steps * 1e3
+    fl = al["flops_fwd"] + al["flops_rev"]
+    res = {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
+           "ms_per_step": round(t_op, 4),
+           "ms_kernels": {"bwd_bf16_fwd": round(t_f, 4), "bwd_bf16_rev": round(t_r, 4)},
+           "ms_kernel_stats": {"bwd_bf16_fwd": stats([p[0] for p in ph]),
+                               "bwd_bf16_rev": stats([p[2] for p in ph])},
+           "kernel_alg_tflops": {"bwd_bf16_fwd": round(al["flops_fwd"] / (t_f * 1e-3) / 1e12, 2),
+                                 "bwd_bf16_rev": round(al["flops_rev"] / (t_r * 1e-3) / 1e12, 2)},
+           "roofline": dict(roofline(kb, t, kern, name),
+                            basis="this kernel's algorithmic bytes (q, k, v, g, dO read and its gradients "
+                                  "written once) over its mean dispatch time"),
+           "op_roofline": op_roofline(nbytes, t_op),
+           "mfma": {"alg_tflops": round(fl / (t_op * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(fl / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "basis": "the chunk form's algorithmic flops (causal halves) over the wall-clock step"}}
+    if not pair:
+        return res
     # one training step of the op as gsa_autograd runs it: the training forward
     # (keeping the segment start states), then the backward reading them
     o_buf = [torch.empty_like(s_["v"]) for s_ in sets]
@@ -494,23 +513,7 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     torch.cuda.synchronize()
     saved_f = mean([ev.ms(evs[4 * i], evs[4 * i + 1]) for i in range(steps)])
     saved_r = mean([ev.ms(evs[4 * i + 2], evs[4 * i + 3]) for i in range(steps)])
-    kern, kb, t = ("bwd_bf16_fwd", al["bytes_fwd"], t_f) if t_f >= t_r else ("bwd_bf16_rev", al["bytes_rev"], t_r)
-    t_op = wall / steps * 1e3
-    fl = al["flops_fwd"] + al["flops_rev"]
-    return {"value": round(B * T * steps / wall, 1), "unit": "tokens/s",
-            "ms_per_step": round(t_op, 4),
-            "ms_kernels": {"bwd_bf16_fwd": round(t_f, 4), "bwd_bf16_rev": round(t_r, 4)},
-            "ms_kernel_stats": {"bwd_bf16_fwd": stats([p[0] for p in ph]),
-                                "bwd_bf16_rev": stats([p[2] for p in ph])},
-            "kernel_alg_tflops": {"bwd_bf16_fwd": round(al["flops_fwd"] / (t_f * 1e-3) / 1e12, 2),
-                                  "bwd_bf16_rev": round(al["flops_rev"] / (t_r * 1e-3) / 1e12, 2)},
-            "roofline": dict(roofline(kb, t, kern, name),
-                             basis="this kernel's algorithmic bytes (q, k, v, g, dO read and its gradients "
-                                   "written once) over its mean dispatch time"),
-            "op_roofline": op_roofline(nbytes, t_op),
-            "mfma": {"alg_tflops": round(fl / (t_op * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(fl / (t_op * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "basis": "the chunk form's algorithmic flops (causal halves) over the wall-clock step"},
+    res.update({
             "saved_states": {"value": round(B * T * steps / wall_saved, 1), "unit": "tokens/s",
                              "ms_per_step": round(wall_saved / steps * 1e3, 4),
                              "ms_kernels": {"bwd_bf16_fwd": round(saved_f, 4), "bwd_bf16_rev": round(saved_r, 4)},
@@ -523,7 +526,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
                            "what": "gsa_fwd_train then gsa_bwd_train on the same batch, per step "
                                    "(what gsa_autograd runs)"},
             "cpu_oracle": bwd_cpu_oracle(w, inp) if cpu else None,
-            "parity_rel_err": bwd_parity(torch, w, inp, outs[0]) if cpu else None}
+            "parity_rel_err": bwd_parity(torch, w, inp, outs[0]) if cpu else None})
+    return res
 
 
 def bench_bwd_saved_only(torch, gsa, w, steps, warmup):
@@ -894,7 +898,7 @@ def run_only(args, torch, gsa, ev):
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
     if args.only == "bwd_long":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], args.steps,
-                         args.warmup, name="gsa_bf16_long_T16384_bwd", cpu=False)
+                         args.warmup, name="gsa_bf16_long_T16384_bwd", cpu=False, pair=False)
     if args.only == "bwd_serve":
         return bench_bwd_varlen(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_serve_N256"], args.steps,
                                 args.warmup)
@@ -904,7 +908,7 @@ def run_only(args, torch, gsa, ev):
         return bench_bwd_saved_only(torch, gsa, synth.WORKLOADS["gsa_bf16_long_T16384"], args.steps, args.warmup)
     if args.only == "bwd":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048"], args.steps,
-                         args.warmup, cpu=False)
+                         args.warmup, cpu=False, pair=False)
     if args.only == "gla_decode":
         return bench_gla_decode(torch, gsa, ev, args.steps, args.warmup)
     if args.only == "m128":
@@ -913,7 +917,7 @@ def run_only(args, torch, gsa, ev):
         return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
     if args.only == "bwd_m128":
         return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_m128"], args.steps,
-                         args.warmup, name="gsa_bf16_train_T2048_m128_bwd", cpu=False)
+                         args.warmup, name="gsa_bf16_train_T2048_m128_bwd", cpu=False, pair=False)
     if args.only == "decode_m128":
         r = bench_decode(torch, gsa, ev, synth.WORKLOADS["gsa_decode_N256_m128"], args.steps, args.warmup,
                          name="gsa_decode_N256_m128")
@@ -961,7 +965,10 @@ def main():
         sys.exit(1)
     ev = Events()
     if args.only is not None:
-        print(json.dumps(run_only(args, torch, gsa, ev)), flush=True)
+        rec = run_only(args, torch, gsa, ev)
+        if isinstance(rec, dict):  # the records' private entries (inputs, outputs) stay out
+            rec = {k: v for k, v in rec.items() if not k.startswith("_")}
+        print(json.dumps(rec), flush=True)
         return
     wname = "gsa_bf16_train_T2048"
     w = synth.WORKLOADS[wname]
