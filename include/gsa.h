@@ -341,7 +341,7 @@ int gsa_bwd_supported(int dk, int dv, int m, int dtype);
 /* Workspace bytes of gsa_bwd / gsa_bwd_ex for this dtype and slot read (a
  * gsa_slot_nonlinearity code; 0 on invalid arguments or T = 0).  bf16 with
  * any read but ReLU runs the chunk form on the matrix cores and keeps
- * per-segment states, reverse maps and bf16 per-token read weights (59 MB at
+ * per-segment states, reverse maps and bf16 per-token read weights (61 MB at
  * B8 H4 T2048 d128 m64; with m = 128 those of the two slot groups plus the
  * merge statistics and the groups' fp32 gradient parts, 6 * 4 * 2 * d + 24
  * bytes per token); float32, and bf16 with the ReLU read (whose
