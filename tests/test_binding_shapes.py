@@ -110,3 +110,20 @@ def test_bwd_shapes():
         gsa.gsa_bwd_varlen(q, q, q, g, q, [0, 20, 69])
     with pytest.raises(ValueError, match="k0"):
         gsa.gsa_bwd_varlen(q, q, q, g, q, cu, k0=f32(3, H, M, D))
+
+
+def test_training_pair_shapes():
+    a = fwd_args()
+    with pytest.raises(TypeError):  # shapes fine: stops at the device check
+        gsa.gsa_fwd_train(**a)
+    with pytest.raises(ValueError, match="g"):
+        gsa.gsa_fwd_train(a["q"], a["k"], a["v"], t(B, H, T - 1, M))
+    with pytest.raises(ValueError, match="v_final"):
+        gsa.gsa_fwd_train(**a, v_final=f32(B, H, M, D + 1))
+    st = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        gsa.gsa_bwd_train(a["q"], a["k"], a["v"], a["g"], t(B, H, T, D), st)
+    with pytest.raises(ValueError, match="d_o"):
+        gsa.gsa_bwd_train(a["q"], a["k"], a["v"], a["g"], t(B, H, T + 1, D), st)
+    with pytest.raises(ValueError, match="d_kf"):
+        gsa.gsa_bwd_train(a["q"], a["k"], a["v"], a["g"], t(B, H, T, D), st, d_kf=f32(B, H, M + 1, D))
