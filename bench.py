@@ -205,8 +205,8 @@ def stats(xs):
 
 
 def cpu_threads():
-    """Host threads the oracle runs on: the CPUs this process may use (the
-    GPU machine's CPU share), and os.cpu_count() beside it."""
+    """Host threads the oracle runs on: the CPUs this process may use (its
+    share of the host), and os.cpu_count() beside it."""
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
