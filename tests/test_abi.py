@@ -171,12 +171,12 @@ def test_varlen_validation(gsa):
     P = ctypes.c_void_p
     f = gsa.lib.gsa_fwd_varlen
 
-    def call(cu, n=None, H=2, dtype=1, q=FAKE, dk=128):
+    def call(cu, n=None, H=2, dtype=1, q=FAKE, dk=128, m=64):
         arr = (ctypes.c_int * len(cu))(*cu)
         n = len(cu) - 1 if n is None else n
         return f(P(q), P(FAKE + 0x1000000), P(FAKE + 0x2000000), P(FAKE + 0x3000000),
                  ctypes.cast(arr, P), n, H, None, None, P(FAKE + 0x4000000), None, None, dk, dk,
-                 64, 64, 8.0, dtype, None, 0, 0, None, None)
+                 m, 64, 8.0, dtype, None, 0, 0, None, None)
 
     assert call([1, 5]) == 2                       # cu[0] != 0
     assert call([0, 70, 60]) == 2                  # decreasing
@@ -185,6 +185,13 @@ def test_varlen_validation(gsa):
     assert f(P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 1, 2, None, None, P(FAKE), None, None,
              128, 128, 64, 64, 8.0, 1, None, 0, 0, None, None) == 2   # no offsets
     assert call([0, 5, 9], dtype=0) == 4           # bf16 only
+    assert call([0, 5, 9], m=128) == 4             # 128 slots: dense batches only
+    cu = (ctypes.c_int * 3)(0, 5, 9)
+    assert gsa.lib.gsa_bwd_varlen(P(FAKE), P(FAKE + 0x1000000), P(FAKE + 0x2000000), P(FAKE + 0x3000000),
+                                  P(FAKE + 0x4000000), ctypes.cast(cu, P), 2, 2, None, None, None, None,
+                                  P(FAKE + 0x5000000), P(FAKE + 0x6000000), P(FAKE + 0x7000000),
+                                  P(FAKE + 0x8000000), None, None, 128, 128, 128, 8.0, 1, P(FAKE + 0x9000000),
+                                  1 << 40, None, None) == 4
     assert call([0, 5, 9], dk=96) == 4
     assert call([0, 5, 9], q=FAKE + 8) == 3
     assert call([0, 5, 9], q=None) == 1
