@@ -247,3 +247,19 @@ def test_gla_split_handoff(oracle_mod):
     a = oracle_mod.gla_fwd(q[:, :, :11], k[:, :, :11], v[:, :, :11], g[:, :, :11])
     b = oracle_mod.gla_fwd(q[:, :, 11:], k[:, :, 11:], v[:, :, 11:], g[:, :, 11:], a["sf"])
     assert _rel(np.concatenate([a["o"], b["o"]], 2), full["o"]) < 1e-14
+
+
+# --------------------------------------------------- P10 128 slots
+def test_gsa_128_slots(oracle_mod):
+    """At m = 128 (the largest slot count of the pages' throughput table):
+    the recurrence equals the numpy chunk form, whose softmax spans all 128
+    slots at once, and permuting the slots (across the two 64-slot halves the
+    GPU path splits them into) permutes the states and leaves o unchanged."""
+    q, k, v, g, k0, v0 = _rand_gsa(1, 2, 150, 16, 12, 128, init=True, seed=12)
+    ref = oracle_mod.gsa_fwd(q, k, v, g, k0, v0, tau=8.0)
+    o, kf, vf = chunkwise.gsa_fwd(q, k, v, g, k0, v0, tau=8.0, C=64)
+    assert _rel(ref["o"], o) < 1e-12 and _rel(ref["kf"], kf) < 1e-12 and _rel(ref["vf"], vf) < 1e-12
+    perm = np.concatenate([np.arange(64, 128), np.arange(64)])[np.random.default_rng(1).permutation(128)]
+    b = oracle_mod.gsa_fwd(q, k, v, g[..., perm].copy(), k0[:, :, perm].copy(), v0[:, :, perm].copy())
+    assert _rel(b["o"], ref["o"]) < 1e-13
+    assert _rel(b["vf"], ref["vf"][:, :, perm]) < 1e-13

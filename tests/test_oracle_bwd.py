@@ -200,3 +200,10 @@ def test_chunk_form_backward_extreme_gates():
         den = max(np.max(np.abs(ref[n])), 1e-300)
         assert np.all(np.isfinite(got["d" + n])), n
         assert np.max(np.abs(got["d" + n] - ref[n])) / den < 1e-11, n
+
+
+def test_directional_derivatives_128_slots():
+    """The backward at m = 128, with states and final-state gradients."""
+    x, w = draw(1, 1, 40, 8, 6, 128, seed=17)
+    errs = directional_errors(fwd_oracle, bwd_oracle(x, w, 8.0), x, w, 8.0, seed=18)
+    assert max(errs.values()) < 1e-7, errs
