@@ -28,12 +28,14 @@
 // its segment end and sums only inside its own segment.
 //
 // Launches (one workgroup per (segment, unit); segments of S chunks):
-//   1. gsa_bf16_state + gsa_bf16_scan (the forward's): segment start states;
+//   1. gsa_bf16_state + gsa_bf16_scan (the forward's): segment start states
+//      (skipped when a training forward kept them);
 //   2. bwd_bf16_fwd: per segment, chunks in order from its start state: the
 //      state carry and the reverse map in MFMA accumulators (state waves),
 //      z, ds, s, dz, h = z dz + s ds and dq (pass waves); s, dz, h are kept
-//      per token (bf16) for the reverse sweep; the segment's end state is
-//      written over its start state, its reverse map and decay beside it;
+//      per token (bf16) for the reverse sweep, the segment's reverse map and
+//      decay beside them, and the last segment's end state (every other
+//      segment's end state is the next one's start state);
 //   3. bwd_bf16_rscan: the end adjoint of every segment (reverse scan of the
 //      reverse maps from the final-state gradients) and the initial-state
 //      gradients;
@@ -41,7 +43,10 @@
 //      the adjoint update (state waves), dk, dv, di and dg (pass waves).
 // A chunk where some slot's decay product falls below 2^-90 (the factorised
 // forms divide by E) runs as an exact token walk of the state waves over the
-// fp32 state / adjoint they hold in their accumulators.
+// fp32 state / adjoint they hold in their accumulators.  128 slots run as two
+// groups of 64 (G = 2): a statistics pass of step 2 gives each group's
+// softmax statistics, merged into the log-sum-exp and delta that both groups'
+// sweeps then take, and the groups' fp32 parts of dq, dk, dv are added last.
 #include <type_traits>
 
 #include "../../include/gsa.h"

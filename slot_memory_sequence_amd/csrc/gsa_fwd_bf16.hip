@@ -31,9 +31,12 @@
 // the outputs (gsa_bf16_out).  With at most kMaxFoldedMaps maps before the last
 // segment there is no scan launch: each output workgroup folds the maps before
 // its segment into its start state (a dependent launch costs more than a few
-// such reads).  A chunk whose decay product falls below 2^-90
-// in some slot is run as the exact token recurrence instead (no division by a
-// decay product).
+// such reads); a training forward that keeps its start states for the
+// backward always launches the scan (into the caller's buffer).  A chunk
+// whose decay product falls below 2^-90 in some slot is run as the exact
+// token recurrence instead (no division by a decay product).  128 slots run
+// as two groups of 64, each its own unit of these kernels (SlotGroups), and
+// gsa_bf16_merge combines the groups' outputs by their log-sum-exps.
 #include <algorithm>
 #include <type_traits>
 
