@@ -991,17 +991,17 @@ def main():
             "cpu_oracle": oracle_gsa_sample(wl, r["inp"], r["out"], ocpu) if ocpu else None}
         del r
         log("bench: long-context done")
-        for wname, what in (
+        for fname, what in (
                 ("gsa_bf16_train_T2048_fast_forget",
                  "the training shape with 8 of 64 slots at gate logits N(-6, 1): 64-token decay "
                  "products near 2^-69, inside the factorised range"),
                 ("gsa_bf16_train_T2048_rapid_forget",
                  "the training shape with 8 of 64 slots at gate logits N(-10, 1): 64-token decay "
                  "products near 2^-115, below the factorised range (every chunk an exact walk)")):
-            wf = synth.WORKLOADS[wname]
-            r = bench_gsa(torch, gsa, ev, wf, wname, args.steps, args.warmup, args.sets,
+            wf = synth.WORKLOADS[fname]
+            r = bench_gsa(torch, gsa, ev, wf, fname, args.steps, args.warmup, args.sets,
                           warm_too=False)
-            comps[wname] = {
+            comps[fname] = {
                 "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
                 "vs_headline": round(r["tokens_per_s"] / main_res["tokens_per_s"], 4),
                 "what": what,
