@@ -16,6 +16,7 @@ and the float64 CPU oracle timed on this host on the training-shape batch.
 """
 import argparse
 import ctypes
+import gc
 import hashlib
 import json
 import math
@@ -174,6 +175,7 @@ def time_op(torch, ev, call, sets, steps, warmup):
     for i in range(warmup):
         call(sets[i % len(sets)], None)
     torch.cuda.synchronize()
+    quiesce()
     t0 = time.perf_counter()
     for i in range(steps):
         call(sets[i % len(sets)], None)
@@ -187,6 +189,14 @@ def time_op(torch, ev, call, sets, steps, warmup):
         e = evs[4 * i: 4 * i + 4]
         phases.append((ev.ms(e[0], e[1]), ev.ms(e[1], e[2]), ev.ms(e[2], e[3]), ev.ms(e[0], e[3])))
     return wall, phases
+
+
+def quiesce():
+    """Start of a timed GPU region: run the cyclic garbage collector now.
+    Automatic collection is off in the benchmark process (main), because a
+    full pass over its heap took tens of milliseconds between two steps of a
+    timed loop."""
+    gc.collect()
 
 
 def mean(xs):
@@ -340,6 +350,7 @@ def bench_decode(torch, gsa, ev, w, steps, warmup, name="gsa_decode_N256"):
         ks, vs = states[i % 2]
         gsa.gsa_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], ks, vs, tau=w["tau"], out=out)
     torch.cuda.synchronize()
+    quiesce()
     t0 = time.perf_counter()
     for i in range(steps):
         ks, vs = states[i % 2]
@@ -377,6 +388,7 @@ def bench_gla_decode(torch, gsa, ev, steps, warmup):
     for i in range(warmup):
         gsa.gla_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], states[i % 2], out=out)
     torch.cuda.synchronize()
+    quiesce()
     t0 = time.perf_counter()
     for i in range(steps):
         gsa.gla_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], states[i % 2], out=out)
@@ -497,6 +509,7 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        quiesce()
         t0 = time.perf_counter()
         for i in range(steps):
             fn(i)
@@ -553,6 +566,7 @@ def bench_bwd_saved_only(torch, gsa, w, steps, warmup):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    quiesce()
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
@@ -882,8 +896,29 @@ def with_measured(rf, peaks):
     return rf
 
 
+# the training shape with a set of fast-forgetting slots, one decay regime each
+FORGET_WORKLOADS = (
+    ("gsa_bf16_train_T2048_fast_forget",
+     "the training shape with 8 of 64 slots at gate logits N(-6, 1): 64-token decay "
+     "products near 2^-69, inside the chunk form's range"),
+    ("gsa_bf16_train_T2048_rapid_forget",
+     "the training shape with 8 of 64 slots at gate logits N(-10, 1): 64-token decay "
+     "products near 2^-115, below the chunk form's range (every chunk in the 16-token "
+     "sub-chunk form)"),
+    ("gsa_bf16_train_T2048_extreme_forget",
+     "the training shape with 8 of 64 slots at gate logits N(-40, 1): 16-token decay "
+     "products near 2^-115, below the sub-chunk form's range too (every chunk an exact walk)"))
+
+
 def run_only(args, torch, gsa, ev):
     import synth
+    if args.only == "forget":
+        out = {}
+        for fname, _ in FORGET_WORKLOADS:
+            r = bench_gsa(torch, gsa, ev, synth.WORKLOADS[fname], fname, args.steps, args.warmup, args.sets,
+                          warm_too=False)
+            out[fname] = {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases")}
+        return out
     if args.only == "copy":
         return copy_calibration(torch, ev, args.steps)
     if args.only == "peaks":
@@ -946,7 +981,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128", "bwd_saved", "bwd_long_saved"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128", "bwd_saved", "bwd_long_saved", "forget"], default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -963,6 +998,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    gc.disable()  # collections run at the start of each timed region (quiesce)
     ev = Events()
     if args.only is not None:
         rec = run_only(args, torch, gsa, ev)
@@ -991,13 +1027,7 @@ def main():
             "cpu_oracle": oracle_gsa_sample(wl, r["inp"], r["out"], ocpu) if ocpu else None}
         del r
         log("bench: long-context done")
-        for fname, what in (
-                ("gsa_bf16_train_T2048_fast_forget",
-                 "the training shape with 8 of 64 slots at gate logits N(-6, 1): 64-token decay "
-                 "products near 2^-69, inside the factorised range"),
-                ("gsa_bf16_train_T2048_rapid_forget",
-                 "the training shape with 8 of 64 slots at gate logits N(-10, 1): 64-token decay "
-                 "products near 2^-115, below the factorised range (every chunk an exact walk)")):
+        for fname, what in FORGET_WORKLOADS:
             wf = synth.WORKLOADS[fname]
             r = bench_gsa(torch, gsa, ev, wf, fname, args.steps, args.warmup, args.sets,
                           warm_too=False)

@@ -11,9 +11,11 @@ namespace bfk {
 constexpr int C = 64;   // chunk length
 constexpr int NW = 8;   // waves per workgroup
 constexpr int NT = NW * 64;
-// log2 of the smallest whole-chunk decay the factorised chunk form allows
-// (2^-90, about e^-62).  The forms divide by the chunk-local decay E, so
-// X = (1 - alpha) / E <= 2^90: a masked score times X stays about 2^38 below
+// log2 of the smallest decay the factorised forms allow between a token and
+// its reference point: over a whole chunk in the chunk form, over a 16-token
+// sub-chunk in the forward's sub-chunk form (2^-90, about e^-62).  The forms
+// divide by the decay E from the reference point, so X = (1 - alpha) / E <=
+// 2^90: a masked score times X stays about 2^38 below
 // the bf16 / fp32 overflow at 2^128 (no inf to meet a zero mask), E stays a
 // normal fp32 number, and every product that survives the causal mask is a
 // ratio E_j / E_r <= 1 formed from two factors of exact relative precision.
@@ -29,6 +31,13 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+// 16x16x16 product (one 16-row sub-chunk as the contraction)
+__device__ __forceinline__ f32x4 mma16(const bf16x4v& a, const bf16x4v& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                   c, 0, 0, 0);
 }
 
 // two accumulator quads -> one operand fragment (round to nearest even)
@@ -54,6 +63,16 @@ __device__ __forceinline__ bf16x8 ld_row2(const bf16_t* base, int ld, int row0, 
   bf16x4v lo = *reinterpret_cast<const bf16x4v*>(p + klo);
   bf16x4v hi = *reinterpret_cast<const bf16x4v*>(p + khi);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Row-major [k][n] tile read column-wise, four k (k0 already includes the lane
+// group's offset): lane l gets tile[k0 + jj][n0 + l%16], jj = 0..3 (the
+// 16x16x16 operand order).
+__device__ __forceinline__ bf16x4v ld_col4(const bf16_t* base, int ld, int n0, int k0, int lane) {
+  const int L = lane & 15;
+  const bf16_t* p0 = base + (k0 + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  bf16x4_raw lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GSA_LDS bf16x4_raw*)(p0));
+  return bf16x4v{lo[0], lo[1], lo[2], lo[3]};
 }
 
 // Row-major [k][n] tile read column-wise with the LDS transpose read: lane l
@@ -164,8 +183,10 @@ __device__ __forceinline__ float dpp_zero(float x) {  // DPP lane move, 0 where 
 // values per lane, step-major so that every step issues N independent
 // operations: shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the last
 // lane of rows 0 / 2 into rows 1 / 3 and the last lane of row 1 into rows 2, 3.
+// wave_row_prefix_sums leaves the inclusive prefix sums inside each row of 16
+// lanes; wave_row_carry then adds the totals of the rows before.
 template <int N>
-__device__ __forceinline__ void wave_prefix_sums(float (&x)[N]) {
+__device__ __forceinline__ void wave_row_prefix_sums(float (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; i++) x[i] += dpp_zero<0x111, 0xf>(x[i]);  // row_shr:1
 #pragma unroll
@@ -174,10 +195,18 @@ __device__ __forceinline__ void wave_prefix_sums(float (&x)[N]) {
   for (int i = 0; i < N; i++) x[i] += dpp_zero<0x114, 0xf>(x[i]);  // row_shr:4
 #pragma unroll
   for (int i = 0; i < N; i++) x[i] += dpp_zero<0x118, 0xf>(x[i]);  // row_shr:8
+}
+template <int N>
+__device__ __forceinline__ void wave_row_carry(float (&x)[N]) {
 #pragma unroll
   for (int i = 0; i < N; i++) x[i] += dpp_zero<0x142, 0xa>(x[i]);  // row_bcast:15 into rows 1, 3
 #pragma unroll
   for (int i = 0; i < N; i++) x[i] += dpp_zero<0x143, 0xc>(x[i]);  // row_bcast:31 into rows 2, 3
+}
+template <int N>
+__device__ __forceinline__ void wave_prefix_sums(float (&x)[N]) {
+  wave_row_prefix_sums<N>(x);
+  wave_row_carry<N>(x);
 }
 
 // Value of the previous lane of the wave (a whole-wave shift by one lane);
@@ -275,6 +304,16 @@ __device__ __forceinline__ bool block_any(bool wave_flag, int* flags, int round,
   const int4 a = *reinterpret_cast<const int4*>(f);
   const int4 b = *reinterpret_cast<const int4*>(f + 4);
   return (a.x | a.y | a.z | a.w | b.x | b.y | b.z | b.w) != 0;
+}
+
+// Workgroup-wide OR of wave-uniform flag bits, as block_any.
+__device__ __forceinline__ int block_or(int wave_flags, int* flags, int round, int lane, int wv) {
+  int* f = flags + (round & 1) * NW;
+  if (lane == 0) f[wv] = wave_flags;
+  __syncthreads();
+  const int4 a = *reinterpret_cast<const int4*>(f);
+  const int4 b = *reinterpret_cast<const int4*>(f + 4);
+  return a.x | a.y | a.z | a.w | b.x | b.y | b.z | b.w;
 }
 
 // SPT consecutive floats -> bf16 / fp32 rows in LDS; dst is 4-byte (bf16) /

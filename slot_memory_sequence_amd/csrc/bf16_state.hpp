@@ -236,30 +236,79 @@ struct StateTiles {
 
 
 // ------------------------------------------------------ chunk factors
-// SPT slots from slot0 of one chunk (token row = lane): X = (1-alpha)/E,
-// Z = (1-alpha) prod_{i>r} alpha_i and E into one factor set, the whole-chunk
-// decay into dec.  Returns whether any of these slots decays below the range
-// of the factorised form in this chunk.
-template <int SPT, int LDX, int LDE, class Row>
-__device__ __forceinline__ bool chunk_factors(const Row& g, bool valid, float inv_tau,
-                                              int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
-                                              float* sDec) {
-  LogGates<SPT> gt;
-  gt.compute(g, valid, inv_tau);
-  bool small = false;
-  float z[SPT];
+// Regime bits of a chunk, OR-ed over its slots and then over the workgroup.
+constexpr int kNeedSub = 1;    // some slot decays below 2^-90 over the chunk
+constexpr int kNeedExact = 2;  // ... over one of its 16-token sub-chunks
+
+// SPT slots from slot0 of one chunk (token row = lane) into one factor set:
+// Z = (1-alpha_r) prod_{i>r} alpha_i, E and X = (1-alpha) / E, the decays
+// d[R-1] across sub-chunks R-1 = 0, 1, 2 (16 tokens each) and the whole-chunk
+// decay.  A slot whose chunk decay stays in the factorised range gets the
+// chunk-local E and X (cumulative from the chunk start) and d = 1.  Any other
+// slot gets sub-chunk reference points (GSA paper App. A.1, the secondary
+// chunking): E and X cumulative from the start of the token's own 16-token
+// sub-chunk, and the true d, so that a read at token j of sub-chunk J combines
+// a term of sub-chunk R <= J with the decay d[R] * ... * d[J-1] between the two
+// reference points; its Z comes from suffix products (no division).  Both
+// representations give the same reads under the sub-chunk form, and a chunk in
+// which no slot needs the second one can use the plain chunk form.  Returns
+// the regime bits of these slots.
+template <int SPT, int LDX, int LDE, int M, class Row>
+__device__ __forceinline__ int chunk_factors(const Row& g, bool valid, float inv_tau,
+                                             int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
+                                             float* sD, float* sDec) {
+  float G[SPT], Gl[SPT];
+#pragma unroll
+  for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
+  wave_row_prefix_sums<SPT>(G);
+#pragma unroll
+  for (int s = 0; s < SPT; s++) Gl[s] = G[s];  // sums inside the lane's sub-chunk
+  wave_row_carry<SPT>(G);
+  float E[SPT], X[SPT], z[SPT], gc[SPT];
+  bool any = false;
 #pragma unroll
   for (int s = 0; s < SPT; s++) {
-    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.G[s]), 63));
-    small |= !(gc >= kFastMinLog2Decay);
-    const float dc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.E[s]), 63));
-    z[s] = gt.X[s] * dc;
+    gc[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G[s]), 63));
+    any |= !(gc[s] >= kFastMinLog2Decay);
+    E[s] = __builtin_amdgcn_exp2f(G[s]);
+    X[s] = __builtin_amdgcn_exp2f(-G[s]);
+  }
+#pragma unroll
+  for (int s = 0; s < SPT; s++) X[s] -= prev_lane(X[s], 1.f);
+  float d[SPT];  // this lane's entry of the d rows (lanes 0..2)
+#pragma unroll
+  for (int s = 0; s < SPT; s++) {
+    const float dc = __builtin_amdgcn_exp2f(gc[s]);
+    z[s] = X[s] * dc;
+    d[s] = 1.f;
     if (lane == 0) sDec[slot0 + s] = dc;
   }
-  store_bf16_row<SPT>(sX + lane * LDX + slot0, gt.X);
+  int flags = 0;
+  if (any) {  // wave-uniform: some slot of this wave leaves the chunk-local range
+#pragma unroll
+    for (int s = 0; s < SPT; s++) {
+      if (gc[s] >= kFastMinLog2Decay) continue;  // uniform
+      flags |= kNeedSub;
+      const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gl[s]), 15));
+      const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gl[s]), 31));
+      const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gl[s]), 47));
+      const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gl[s]), 63));
+      if (!(fminf(fminf(r0, r1), fminf(r2, r3)) >= kFastMinLog2Decay)) flags |= kNeedExact;
+      E[s] = __builtin_amdgcn_exp2f(Gl[s]);
+      const float xi = __builtin_amdgcn_exp2f(-Gl[s]);
+      const float xp = prev_lane(xi, 1.f);
+      X[s] = xi - ((lane & 15) ? xp : 1.f);
+      // S_r = prod_{i>r} alpha_i = 2^(G_C - G_r); Z_r = S_r - S_{r-1}, S_{-1} = chunk decay
+      const float sr = __builtin_amdgcn_exp2f(gc[s] - G[s]);
+      z[s] = sr - prev_lane(sr, __builtin_amdgcn_exp2f(gc[s]));
+      d[s] = __builtin_amdgcn_exp2f(lane == 0 ? r0 : lane == 1 ? r1 : r2);
+    }
+  }
+  store_bf16_row<SPT>(sX + lane * LDX + slot0, X);
   store_bf16_row<SPT>(sZ + lane * LDX + slot0, z);
-  store_f32_row<SPT>(sE + lane * LDE + slot0, gt.E);
-  return small;
+  store_f32_row<SPT>(sE + lane * LDE + slot0, E);
+  if (lane < 3) store_f32_row<SPT>(sD + lane * M + slot0, d);
+  return flags;
 }
 
 }  // namespace bfk

@@ -33,8 +33,12 @@
 // its segment into its start state (a dependent launch costs more than a few
 // such reads); a training forward that keeps its start states for the
 // backward always launches the scan (into the caller's buffer).  A chunk
-// whose decay product falls below 2^-90 in some slot is run as the exact
-// token recurrence instead (no division by a decay product).  128 slots run
+// whose decay product falls below 2^-90 in some slot is run with 16-token
+// sub-chunk reference points (App. A.1, secondary chunking: the same
+// contractions, with the intra-chunk terms carried between the reference
+// points by the sub-chunk decays), and one in which a 16-token sub-chunk decays
+// below 2^-90 as the exact token recurrence (no division by a decay product).
+// 128 slots run
 // as two groups of 64, each its own unit of these kernels (SlotGroups), and
 // gsa_bf16_merge combines the groups' outputs by their log-sum-exps.
 #include <algorithm>
@@ -66,7 +70,8 @@ struct OutLds {
   static constexpr int fX = 0;                         // X [C][M] bf16
   static constexpr int fZ = fX + C * LDX * 2;          // Z [C][M] bf16
   static constexpr int fE = fZ + C * LDX * 2;          // E [C][M] fp32
-  static constexpr int szF = fE + C * LDE * 4;         // one factor set
+  static constexpr int fD = fE + C * LDE * 4;          // sub-chunk decays [3][M] fp32
+  static constexpr int szF = fD + 3 * M * 4;           // one factor set
   static constexpr int szFast = oF + 2 * szF - oR;
   // exact-recurrence path
   static constexpr int oWf = oR;                       // fp32 W [M][DK+DV]
@@ -78,7 +83,7 @@ struct OutLds {
   static constexpr int oFlag = oDec + 2 * M * 4;                         // 2 x NW ints
   static constexpr int total = oFlag + 2 * NW * 4;
   static_assert(oK % 16 == 0 && oV % 16 == 0 && oW % 16 == 0 && oF % 16 == 0 && szF % 16 == 0 &&
-                    fZ % 16 == 0 && fE % 16 == 0 && oLa % 16 == 0 && oOp % 16 == 0 && oDec % 16 == 0,
+                    fZ % 16 == 0 && fE % 16 == 0 && fD % 16 == 0 && oLa % 16 == 0 && oOp % 16 == 0 && oDec % 16 == 0,
                 "LDS tiles must stay 16-byte aligned");
 };
 
@@ -102,10 +107,16 @@ struct StateLds {  // two buffers of everything a chunk needs (software pipeline
 // template parameter so that every loop is static and independent
 // accumulators can be interleaved.  G > 1 (slot groups): output rows have the
 // pitch G * DV, and the softmax's log-sum-exp of token j goes to lrow[j * G].
-template <int DK, int DV, int M, int J, int ACT, int G>
+// SUB: the sub-chunk form of the reads (chunk_factors): the intra-chunk sums
+// run per 16-token sub-chunk R <= J, and a term of sub-chunk R is carried to
+// this wave's reference point by the decays sD[R] ... sD[J-1] between them --
+// in pass 1 by scaling the running slot scores before each sub-chunk is added
+// (the state read counts as the term before sub-chunk 0), in pass 2 by
+// scaling the weights s*E before the scores of each sub-chunk are formed.
+template <int DK, int DV, int M, int J, int ACT, int G, bool SUB>
 __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf16_t* sK,
                                            const bf16_t* sV, const bf16_t* sW, const bf16_t* sX,
-                                           const float* sE, bf16_t* __restrict__ orow,
+                                           const float* sE, const float* sD, bf16_t* __restrict__ orow,
                                            float* __restrict__ lrow, int rv) {
   using Lds = OutLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, NP = M / 32, NVT = DV / 16;
@@ -130,9 +141,6 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
 #pragma unroll
   for (int i = 0; i < 4; i++)
     if (4 * g + i > L) at[J][i] = 0.f;
-  bf16x8 af[2];
-  af[0] = pack8(at[0], at[1]);
-  af[1] = pack8(at[2], at[3]);
 
   // pass 1: o'^T[c][j] = E[j][c] (Wk[c].q_j + sum_r X[r][c] A^T[r][j])
   f32x4 op[MT];
@@ -142,11 +150,33 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
   for (int s = 0; s < KQ; s++)
 #pragma unroll
     for (int ct = 0; ct < MT; ct++) op[ct] = mma(ld_row(sW, Lds::LDW, 16 * ct, 32 * s, lane), qf[s], op[ct]);
+  if constexpr (!SUB) {
+    bf16x8 af[2];
+    af[0] = pack8(at[0], at[1]);
+    af[1] = pack8(at[2], at[3]);
 #pragma unroll
-  for (int pr = 0; pr < NPR; pr++)
+    for (int pr = 0; pr < NPR; pr++)
 #pragma unroll
-    for (int ct = 0; ct < MT; ct++)
-      op[ct] = mma(ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), af[pr], op[ct]);
+      for (int ct = 0; ct < MT; ct++)
+        op[ct] = mma(ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), af[pr], op[ct]);
+  } else {
+#pragma unroll
+    for (int R = 0; R < NR; R++) {
+      if (R > 0) {
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) {
+          const float4 dd = *reinterpret_cast<const float4*>(sD + (R - 1) * M + 16 * ct + 4 * g);
+          op[ct][0] *= dd.x;
+          op[ct][1] *= dd.y;
+          op[ct][2] *= dd.z;
+          op[ct][3] *= dd.w;
+        }
+      }
+      const bf16x4v ar = pack4(at[R]);
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) op[ct] = mma16(ld_col4(sX, Lds::LDX, 16 * ct, 16 * R + 4 * g, lane), ar, op[ct]);
+    }
+  }
 #pragma unroll
   for (int ct = 0; ct < MT; ct++) {
     const float4 e = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 16 * ct + 4 * g);
@@ -185,28 +215,59 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
 #pragma unroll
       for (int i = 0; i < 4; i++) op[ct][i] = slot_act<ACT>(op[ct][i]);
   }
-  // (s*E)^T as B operands over slot pairs (permuted slot index)
+  // (s*E)^T as B operands over slot pairs (permuted slot index), and the
+  // pass 2 scores A2^T[r][j] = sum_c X[r][c] (s*E)[j][c], r tiles R <= J
   bf16x8 sb[NP];
-#pragma unroll
-  for (int p = 0; p < NP; p++) {
-    const float4 ea = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 4 * g);
-    const float4 eb = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 16 + 4 * g);
-    const f32x4 a = {op[2 * p][0] * inv * ea.x, op[2 * p][1] * inv * ea.y, op[2 * p][2] * inv * ea.z,
-                     op[2 * p][3] * inv * ea.w};
-    const f32x4 b = {op[2 * p + 1][0] * inv * eb.x, op[2 * p + 1][1] * inv * eb.y,
-                     op[2 * p + 1][2] * inv * eb.z, op[2 * p + 1][3] * inv * eb.w};
-    sb[p] = pack8(a, b);
-  }
-
-  // pass 2 scores: A2^T[r][j] = sum_c X[r][c] (s*E)[j][c], r tiles R <= J
   f32x4 a2[4];
 #pragma unroll
   for (int R = 0; R < 4; R++) a2[R] = zero4();
+  if constexpr (!SUB) {
 #pragma unroll
-  for (int p = 0; p < NP; p++)
+    for (int p = 0; p < NP; p++) {
+      const float4 ea = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 4 * g);
+      const float4 eb = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 32 * p + 16 + 4 * g);
+      const f32x4 a = {op[2 * p][0] * inv * ea.x, op[2 * p][1] * inv * ea.y, op[2 * p][2] * inv * ea.z,
+                       op[2 * p][3] * inv * ea.w};
+      const f32x4 b = {op[2 * p + 1][0] * inv * eb.x, op[2 * p + 1][1] * inv * eb.y,
+                       op[2 * p + 1][2] * inv * eb.z, op[2 * p + 1][3] * inv * eb.w};
+      sb[p] = pack8(a, b);
+    }
 #pragma unroll
-    for (int R = 0; R < NR; R++)
-      a2[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], a2[R]);
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int R = 0; R < NR; R++)
+        a2[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], a2[R]);
+  } else {
+    // weights at this wave's reference point, then carried back one sub-chunk
+    // at a time: the last set (R = 0) is s*E from the chunk start, which the
+    // state read below takes as well
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const float4 e = *reinterpret_cast<const float4*>(sE + j * Lds::LDE + 16 * ct + 4 * g);
+      op[ct][0] *= inv * e.x;
+      op[ct][1] *= inv * e.y;
+      op[ct][2] *= inv * e.z;
+      op[ct][3] *= inv * e.w;
+    }
+#pragma unroll
+    for (int R = NR - 1; R >= 0; R--) {
+      if (R < J) {
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) {
+          const float4 dd = *reinterpret_cast<const float4*>(sD + R * M + 16 * ct + 4 * g);
+          op[ct][0] *= dd.x;
+          op[ct][1] *= dd.y;
+          op[ct][2] *= dd.z;
+          op[ct][3] *= dd.w;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NP; p++) sb[p] = pack8(op[2 * p], op[2 * p + 1]);
+#pragma unroll
+      for (int p = 0; p < NP; p++)
+        a2[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), sb[p], a2[R]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++)
     if (4 * g + i > L) a2[J][i] = 0.f;
@@ -249,7 +310,7 @@ __device__ __forceinline__ void pass_chunk(int lane, const bf16_t* sQ, const bf1
 // Runs one chunk token by token: Kt, Vt <- Diag(alpha) (.) + (1-alpha)[k|v]^T,
 // s = softmax over slots of Kt q (or the element-wise ACT), o = Vt^T s
 // (Sec. 3.2 recurrent form).  Used
-// for chunks whose decay product is too small for the factorised chunk form.
+// for chunks in which some slot decays too fast even for the sub-chunk form.
 // The state waves' accumulators W are written to LDS, advanced there by all
 // threads, and read back.  Contains workgroup barriers: all threads call it.
 // G as in pass_chunk.
@@ -506,6 +567,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   auto fX = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fX); };
   auto fZ = [&](int b) { return reinterpret_cast<bf16_t*>(smem + Lds::oF + b * Lds::szF + Lds::fZ); };
   auto fE = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oF + b * Lds::szF + Lds::fE); };
+  auto fD = [&](int b) { return reinterpret_cast<float*>(smem + Lds::oF + b * Lds::szF + Lds::fD); };
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool is_state = wv >= 4;
@@ -545,10 +607,10 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   };
   // (the empty asm of pin() keeps the use of the logits, and so the wait for
   // their load, at the call)
-  auto factors = [&](Row& r, int rv, int fb, int lane_) -> bool {
+  auto factors = [&](Row& r, int rv, int fb, int lane_) -> int {
     r.pin();
-    return chunk_factors<GPW, Lds::LDX, Lds::LDE>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
-                                                   fE(fb), sDec0 + fb * M);
+    return chunk_factors<GPW, Lds::LDX, Lds::LDE, M>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
+                                                      fE(fb), fD(fb), sDec0 + fb * M);
   };
   auto log_alpha = [&](const Row& r, int rv, int lane_) {  // natural log, exact path
 #pragma unroll
@@ -563,7 +625,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   Tile<DK> pq, pk;
   Tile<DV> pv;
   ST W;
-  bool slow;
+  int regime;  // the current chunk's kNeedSub / kNeedExact bits
   {
     const int t0 = c_begin * C, rv = rows_of(c_begin);
     if (!empty) {
@@ -597,7 +659,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
       }
       W.store_copy(sW, Lds::LDW, sw, lane);
     }
-    slow = empty ? false : block_any(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
+    regime = empty ? 0 : block_or(factors(gr, rv, 0, lane), sFlag, 0, lane, wv);
   }
 
   int b = 0;  // factor set of the current chunk
@@ -612,6 +674,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     pq.store(sQ, Lds::LDQ, rv, tid_i);
     pk.store(sK, Lds::LDQ, rv, tid_i);
     pv.store(sV, Lds::LDV, rv, tid_i);
+    const bool slow = regime & kNeedExact;
     if (slow) log_alpha(gr, rv, lane_i);
     load_gates(gr, t1, rv1, lane_i);
     __syncthreads();
@@ -620,18 +683,30 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
     pq.load(qb + (size_t)t1 * DK, rv1, tid_i);
     pk.load(kb + (size_t)t1 * DK, rv1, tid_i);
     pv.load(vb + (size_t)t1 * DV, rv1, tid_i);
-    bool small;
+    int small;
     if (!slow) {
       if (!is_state) {
         bf16_t* orow = ob + (size_t)t0 * (DV * G);
         float* lrow = G > 1 ? lb + (size_t)t0 * G : nullptr;
         // pass waves hold no state: dropping it frees these registers for the passes
         W.zero();
-        switch (wv) {
-          case 0: pass_chunk<DK, DV, M, 0, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
-          case 1: pass_chunk<DK, DV, M, 1, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
-          case 2: pass_chunk<DK, DV, M, 2, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
-          default: pass_chunk<DK, DV, M, 3, ACT, G>(lane_i, sQ, sK, sV, sW, fX(b), fE(b), orow, lrow, rv); break;
+        const bf16_t* x = fX(b);
+        const float* e = fE(b);
+        const float* d = fD(b);
+        if (!(regime & kNeedSub)) {
+          switch (wv) {
+            case 0: pass_chunk<DK, DV, M, 0, ACT, G, false>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            case 1: pass_chunk<DK, DV, M, 1, ACT, G, false>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            case 2: pass_chunk<DK, DV, M, 2, ACT, G, false>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            default: pass_chunk<DK, DV, M, 3, ACT, G, false>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+          }
+        } else {  // some slot decays out of the chunk form's range: sub-chunk reference points
+          switch (wv) {
+            case 0: pass_chunk<DK, DV, M, 0, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            case 1: pass_chunk<DK, DV, M, 1, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            case 2: pass_chunk<DK, DV, M, 2, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            default: pass_chunk<DK, DV, M, 3, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+          }
         }
       } else {
         W.carry(sK, Lds::LDQ, sV, Lds::LDV, fZ(b), Lds::LDX, sDec0 + b * M, sw, lane_i);
@@ -646,7 +721,7 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
                                      G > 1 ? lb + (size_t)t0 * G : nullptr, tid_i);
       small = factors(gr, rv1, b ^ 1, lane_i);
     }
-    slow = block_any(small, sFlag, ch - c_begin + 1, lane_i, wv);
+    regime = block_or(small, sFlag, ch - c_begin + 1, lane_i, wv);
     if (is_state) W.store_copy(sW, Lds::LDW, sw, lane_i);
     b ^= 1;
   }

@@ -210,6 +210,12 @@ WORKLOADS = {
                                               C=64, tau=8.0, dtype="bf16",
                                               qkv_scale=1 / math.sqrt(128), g_shift=0.0,
                                               init_std=None, fast_slots=8, fast_shift=-10.0),
+    # the same with logits N(-40, 1): log alpha ~ -5 per token, so that even a
+    # 16-token sub-chunk decays below the factorised range (the exact walk)
+    "gsa_bf16_train_T2048_extreme_forget": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=64,
+                                                C=64, tau=8.0, dtype="bf16",
+                                                qkv_scale=1 / math.sqrt(128), g_shift=0.0,
+                                                init_std=None, fast_slots=8, fast_shift=-40.0),
     # the training shape with 128 slots (the largest slot count the pages
     # measure training throughput at)
     "gsa_bf16_train_T2048_m128": dict(op="gsa", B=8, H=4, T=2048, dk=128, dv=128, m=128, C=64,

@@ -75,8 +75,9 @@ def test_fwd_elementwise_reads(gsa, torch, nl):
 
 def test_fwd_one_group_decays_fast(gsa, torch):
     """Gate logits -12 on every slot of the second group for chunks 1 and 3
-    (64-token decay products near 2^-138: those chunks run the exact
-    recurrence in that group's launch only), +-inf and +-30 tokens elsewhere."""
+    (64-token decay products near 2^-138: those chunks run the sub-chunk form
+    in that group's units only), +-inf tokens (the exact walk) and +-30
+    tokens elsewhere."""
     def mut(inp):
         x = inp["g"].f64.copy()
         x[..., 64:128, 64:] = -12.0

@@ -91,6 +91,18 @@ def test_gsa_nonlinearity_exact_path(gsa, torch, nl, dtype, d, m):
 
 
 @pytest.mark.parametrize("nl", ELEMENTWISE)
+def test_gsa_nonlinearity_subchunk_form(gsa, torch, nl):
+    """Chunks in the sub-chunk form (8 slots at g ~ N(-10, 1): 64-token decay
+    products ~2^-115, 16-token ~2^-29) apply the same read."""
+    inp = synth.gsa_inputs(1, 2, 64 * 4 + 9, 128, 128, 64, dtype="bf16", seed=9, init_std=0.1)
+    x = inp["g"].f64.copy()
+    x[..., :8] = -10.0 + np.random.default_rng(4).standard_normal(x[..., :8].shape)
+    inp["g"] = synth.stored(x, "bf16")
+    for cps in (0, 1):
+        _check(gsa, torch, inp, nl, "bf16", cps=cps, label="sub-chunk form")
+
+
+@pytest.mark.parametrize("nl", ELEMENTWISE)
 def test_gsa_nonlinearity_training_shape(gsa, torch, nl):
     """The training-shape workload (B8 H4 T2048 d128 m64, bf16) in the launch
     configuration the benchmark times, every unit against the oracle."""

@@ -110,8 +110,9 @@ def _extreme(inp):
 @pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64)])
 def test_gsa_extreme_gates(gsa, torch, dtype, d, m):
     """alpha = 0 / alpha = 1 tokens (g = -inf / +inf, +-30): chunks whose decay
-    product falls below the factorised form's floor (e^-40 in float32,
-    2^-90 in bfloat16) take the exact token recurrence."""
+    product falls below the factorised form's floor (e^-40 in float32; in
+    bfloat16 2^-90 over a 16-token sub-chunk) take the exact token
+    recurrence."""
     for cps in (0, 1):
         _check_gsa(gsa, torch, 1, 2, 300, d, m, dtype, init=True, cps=cps, mutate=_extreme, seed=7)
 
@@ -335,14 +336,59 @@ def _near_floor(x_mean, x_std):
 @pytest.mark.parametrize("case", ["all", "mixed", "near_floor"])
 def test_gsa_bf16_strong_decay(gsa, torch, case):
     # alpha = sigmoid(g)^(1/8).  "all": g ~ N(-8, 1) makes the 64-token decay
-    # products ~2^-92, around the 2^-90 floor of the factorised form, so
-    # chunks take either form.  "mixed": g = -12 on chunks 1 and 3 (product
-    # ~2^-138, exact recurrence) and N(0, 1) elsewhere.  "near_floor": g ~
-    # N(-7.3, 0.05), products ~2^-84: every chunk factorised with X up to ~2^84.
+    # products ~2^-92, around the 2^-90 floor of the chunk form, so chunks
+    # take either the chunk form or the sub-chunk form.  "mixed": g = -12 on
+    # chunks 1 and 3 (64-token products ~2^-138, 16-token ~2^-35: sub-chunk
+    # form) and N(0, 1) elsewhere.  "near_floor": g ~ N(-7.3, 0.05), products
+    # ~2^-84: every chunk in the chunk form with X up to ~2^84.
     mut = {"all": _shift_gates(-8.0), "mixed": _decay_chunks((1, 3), -12.0),
            "near_floor": _near_floor(-7.3, 0.05)}[case]
     for cps in (0, 1):
         _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, cps=cps, seed=21, mutate=mut)
+
+
+def _fast_slots(n, mean, std=1.0, seed=6):
+    """Gate logits N(mean, std) on the first n slots of every token (a few
+    slots forgetting fast), the stored N(0, 1) logits elsewhere."""
+    def mut(inp):
+        x = inp["g"].f64.copy()
+        r = np.random.default_rng(seed)
+        x[..., :n] = mean + std * r.standard_normal(x[..., :n].shape)
+        inp["g"] = synth.stored(x, inp["g"].dtype)
+    return mut
+
+
+def _regime_per_chunk(inp):
+    """One decay regime per 64-token chunk: 0 plain (chunk form); 1 g = -12 on
+    every slot (64-token products ~2^-138, 16-token ~2^-35: sub-chunk form);
+    2 g = -inf on one slot for three tokens (a 16-token product below 2^-90:
+    exact walk); 3 g ~ N(-10, 1) on 8 slots (sub-chunk form); 4 g = -30.5 on
+    4 slots (16-token products ~2^-88, the sub-chunk form near its floor);
+    the ragged tail plain."""
+    x = inp["g"].f64.copy()
+    m = x.shape[-1]
+    x[..., 64:128, :] = -12.0
+    x[..., 130:133, m // 2] = -np.inf
+    r = np.random.default_rng(8)
+    x[..., 192:256, :8] = -10.0 + r.standard_normal(x[..., 192:256, :8].shape)
+    x[..., 256:320, m - 4:] = -30.5
+    inp["g"] = synth.stored(x, inp["g"].dtype)
+
+
+@pytest.mark.parametrize("case", ["fast_slots", "sub_floor", "per_chunk"])
+@pytest.mark.parametrize("d,m", [(128, 64), (128, 32), (64, 64), (64, 32)])
+def test_gsa_bf16_subchunk_form(gsa, torch, case, d, m):
+    """Chunks whose 64-token decay product falls below the chunk form's 2^-90
+    floor in some slot run with 16-token sub-chunk reference points, and only
+    a sub-chunk product below 2^-90 sends a chunk to the exact walk.
+    "fast_slots": 8 slots at g ~ N(-10, 1) on every token (64-token products
+    ~2^-115, every chunk in the sub-chunk form).  "sub_floor": every slot at
+    g ~ N(-30.5, 0.05) (16-token products ~2^-88: X up to ~2^88).
+    "per_chunk": the plain, sub-chunk and exact regimes in turn."""
+    mut = {"fast_slots": _fast_slots(8, -10.0), "sub_floor": _near_floor(-30.5, 0.05),
+           "per_chunk": _regime_per_chunk}[case]
+    for cps in (0, 1):
+        _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, d, m, "bf16", init=True, cps=cps, seed=23, mutate=mut)
 
 
 @pytest.mark.parametrize("case", ["all", "mixed", "near_floor"])
