@@ -445,7 +445,8 @@ def bench_bwd(torch, gsa, ev, w, steps, warmup, name="gsa_bf16_train_T2048_bwd",
     import synth
     B, H, T, dk, dv, m = w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"]
     inp = synth.gsa_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=0, qkv_scale=w["qkv_scale"],
-                           g_shift=w["g_shift"], init_std=w["init_std"])
+                           g_shift=w["g_shift"], init_std=w["init_std"], fast_slots=w.get("fast_slots", 0),
+                           fast_shift=w.get("fast_shift", 0.0))
     states = inp["k0"] is not None
     gi = synth.gsa_grad_inputs(B, H, T, dk, dv, m, dtype=w["dtype"], seed=1,
                                final_std=1.0 if states else None)
