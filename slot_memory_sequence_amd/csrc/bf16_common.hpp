@@ -33,11 +33,18 @@ __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-// 16x16x16 product (one 16-row sub-chunk as the contraction)
+// 16x16x16 product (one 16-row sub-chunk as the contraction) as a 16x16x32
+// one whose second half of the contraction is zero on both operands (lane
+// group g's four values take contraction positions 8g .. 8g + 3).  The
+// 16x16x16 bf16 instruction itself (v_mfma_f32_16x16x16_bf16) was measured
+// to give wrong accumulators in one schedule of the backward kernel (its
+// first pass wave at dk = dv = 128, m = 64, where the product's result is
+// read soon after a 16x16x32 one), while this form gave the expected ones.
 __device__ __forceinline__ f32x4 mma16(const bf16x4v& a, const bf16x4v& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
-                                                   c, 0, 0, 0);
+  const __bf16 z = (__bf16)0.f;
+  const bf16x8 a8 = {a[0], a[1], a[2], a[3], z, z, z, z};
+  const bf16x8 b8 = {b[0], b[1], b[2], b[3], z, z, z, z};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
 }
 
 // two accumulator quads -> one operand fragment (round to nearest even)

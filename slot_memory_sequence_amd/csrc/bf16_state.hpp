@@ -6,29 +6,6 @@
 namespace gsa {
 namespace bfk {
 
-// Output-pass factors of SPT slots for token row = lane of a chunk, with
-// G = chunk-local inclusive cumulative sum of log2 alpha:
-//   E_j = exp2(G_j),  X_j = (1 - alpha_j) / E_j = 1/E_j - 1/E_{j-1}.
-// Rows past the end of the sequence are identity steps (log alpha = 0).
-template <int SPT>
-struct LogGates {
-  float G[SPT], E[SPT], X[SPT];
-  // g: a gate row holding at least SPT values
-  template <class Row>
-  __device__ __forceinline__ void compute(const Row& g, bool valid, float inv_tau) {
-#pragma unroll
-    for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
-    wave_prefix_sums<SPT>(G);
-#pragma unroll
-    for (int s = 0; s < SPT; s++) {
-      E[s] = __builtin_amdgcn_exp2f(G[s]);
-      X[s] = __builtin_amdgcn_exp2f(-G[s]);
-    }
-#pragma unroll
-    for (int s = 0; s < SPT; s++) X[s] -= prev_lane(X[s], 1.f);
-  }
-};
-
 // State-map factors: the decay from token r to the chunk end
 // S_r = prod_{i>r} alpha_i = exp2(G_C - G_r), the write term
 // Z_r = (1 - alpha_r) S_r = S_r - S_{r-1}, and the whole-chunk decay.
@@ -232,6 +209,40 @@ struct StateTiles {
       }
     }
   }
+  // update2 in the sub-chunk form (chunk_factors): Za, Zb hold weights at the
+  // reference point of each token's 16-token sub-chunk, and sD [4][M] the
+  // decays between reference points.  Horner's rule from the chunk end: for
+  // sub-chunks T = 3 .. 0, W^T <- W^T Diag(sD[T]) + [A | B]_T^T [Za | Zb]_T
+  // (one 16-token contraction each).
+  __device__ __forceinline__ void update2_sub(const bf16_t* sA, int lda, const bf16_t* sB, int ldb,
+                                              const bf16_t* sZa, const bf16_t* sZb, int ldz,
+                                              const float* sD, int sw, int lane) {
+    const int L = lane & 15, g = lane >> 4;
+    const bool khalf = 16 * (sw * NCW) < DK;
+    const bf16_t* sZ = khalf ? sZa : sZb;
+#pragma unroll
+    for (int T = 3; T >= 0; T--) {
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        const float d = sD[T * M + 16 * ct + L];
+#pragma unroll
+        for (int n = 0; n < NCW; n++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) st[n][ct][i] *= d;
+      }
+      bf16x4v zb[MT];
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) zb[ct] = ld_col4(sZ, ldz, 16 * ct, 16 * T + 4 * g, lane);
+#pragma unroll
+      for (int n = 0; n < NCW; n++) {
+        const int c0 = 16 * (sw * NCW + n);
+        const bf16x4v a = khalf ? ld_col4(sA, lda, c0, 16 * T + 4 * g, lane)
+                                : ld_col4(sB, ldb, c0 - DK, 16 * T + 4 * g, lane);
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) st[n][ct] = mma16(a, zb[ct], st[n][ct]);
+      }
+    }
+  }
 };
 
 
@@ -241,22 +252,25 @@ constexpr int kNeedSub = 1;    // some slot decays below 2^-90 over the chunk
 constexpr int kNeedExact = 2;  // ... over one of its 16-token sub-chunks
 
 // SPT slots from slot0 of one chunk (token row = lane) into one factor set:
-// Z = (1-alpha_r) prod_{i>r} alpha_i, E and X = (1-alpha) / E, the decays
-// d[R-1] across sub-chunks R-1 = 0, 1, 2 (16 tokens each) and the whole-chunk
-// decay.  A slot whose chunk decay stays in the factorised range gets the
-// chunk-local E and X (cumulative from the chunk start) and d = 1.  Any other
-// slot gets sub-chunk reference points (GSA paper App. A.1, the secondary
-// chunking): E and X cumulative from the start of the token's own 16-token
-// sub-chunk, and the true d, so that a read at token j of sub-chunk J combines
-// a term of sub-chunk R <= J with the decay d[R] * ... * d[J-1] between the two
-// reference points; its Z comes from suffix products (no division).  Both
-// representations give the same reads under the sub-chunk form, and a chunk in
-// which no slot needs the second one can use the plain chunk form.  Returns
-// the regime bits of these slots.
+// Z = (1-alpha_r) prod_{i>r} alpha_i, E and X = (1-alpha) / E, four decay rows
+// d[0..3] and the whole-chunk decay.  A slot whose chunk decay stays in the
+// factorised range gets the chunk-local E and X (cumulative from the chunk
+// start, the one reference point): d[0..2] = 1 between its coinciding
+// reference points and d[3] = the chunk decay after the last of them.  Any
+// other slot gets sub-chunk reference points (GSA paper App. A.1, the
+// secondary chunking) at tokens 0, 16, 32, 48: E and X cumulative from the
+// start of the token's own 16-token sub-chunk, and d[R] = the decay across
+// sub-chunk R.  A term between a token of sub-chunk R and a later one of
+// sub-chunk J then carries d[R] * ... * d[J-1] (the state at the chunk start
+// counts as reference point 0, the chunk end as the point after d[3]); its Z
+// comes from suffix products (no division).  Both representations give the
+// same results under the sub-chunk form, and a chunk in which no slot needs
+// the second one can use the plain chunk form.  E also returns this lane's E.
+// Returns the regime bits of these slots.
 template <int SPT, int LDX, int LDE, int M, class Row>
 __device__ __forceinline__ int chunk_factors(const Row& g, bool valid, float inv_tau,
                                              int lane, int slot0, bf16_t* sX, bf16_t* sZ, float* sE,
-                                             float* sD, float* sDec) {
+                                             float* sD, float* sDec, float (&E)[SPT]) {
   float G[SPT], Gl[SPT];
 #pragma unroll
   for (int s = 0; s < SPT; s++) G[s] = gate_log2_or_identity(g.at(s), valid, inv_tau);
@@ -264,7 +278,7 @@ __device__ __forceinline__ int chunk_factors(const Row& g, bool valid, float inv
 #pragma unroll
   for (int s = 0; s < SPT; s++) Gl[s] = G[s];  // sums inside the lane's sub-chunk
   wave_row_carry<SPT>(G);
-  float E[SPT], X[SPT], z[SPT], gc[SPT];
+  float X[SPT], z[SPT], gc[SPT];
   bool any = false;
 #pragma unroll
   for (int s = 0; s < SPT; s++) {
@@ -275,12 +289,12 @@ __device__ __forceinline__ int chunk_factors(const Row& g, bool valid, float inv
   }
 #pragma unroll
   for (int s = 0; s < SPT; s++) X[s] -= prev_lane(X[s], 1.f);
-  float d[SPT];  // this lane's entry of the d rows (lanes 0..2)
+  float d[SPT];  // this lane's entry of the d rows (lanes 0..3)
 #pragma unroll
   for (int s = 0; s < SPT; s++) {
     const float dc = __builtin_amdgcn_exp2f(gc[s]);
     z[s] = X[s] * dc;
-    d[s] = 1.f;
+    d[s] = lane == 3 ? dc : 1.f;
     if (lane == 0) sDec[slot0 + s] = dc;
   }
   int flags = 0;
@@ -301,13 +315,13 @@ __device__ __forceinline__ int chunk_factors(const Row& g, bool valid, float inv
       // S_r = prod_{i>r} alpha_i = 2^(G_C - G_r); Z_r = S_r - S_{r-1}, S_{-1} = chunk decay
       const float sr = __builtin_amdgcn_exp2f(gc[s] - G[s]);
       z[s] = sr - prev_lane(sr, __builtin_amdgcn_exp2f(gc[s]));
-      d[s] = __builtin_amdgcn_exp2f(lane == 0 ? r0 : lane == 1 ? r1 : r2);
+      d[s] = __builtin_amdgcn_exp2f(lane == 0 ? r0 : lane == 1 ? r1 : lane == 2 ? r2 : r3);
     }
   }
   store_bf16_row<SPT>(sX + lane * LDX + slot0, X);
   store_bf16_row<SPT>(sZ + lane * LDX + slot0, z);
   store_f32_row<SPT>(sE + lane * LDE + slot0, E);
-  if (lane < 3) store_f32_row<SPT>(sD + lane * M + slot0, d);
+  if (lane < 4) store_f32_row<SPT>(sD + lane * M + slot0, d);
   return flags;
 }
 

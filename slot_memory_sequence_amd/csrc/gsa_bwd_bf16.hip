@@ -85,7 +85,8 @@ struct BwdLds {
   static constexpr int oDec = oDZ + C * LDX * 2;  // chunk decay E_C [M] fp32
   static constexpr int oAux = oDec + M * 4;       // fwd: decay from the segment start [M]; rev: carry [2][M]
   static constexpr int oWt = oAux + 2 * M * 4;    // rev: per pass wave gate sums [4][M] fp32
-  static constexpr int oFlag = oWt + 4 * M * 4;   // 2 x NW ints
+  static constexpr int oD = oWt + 4 * M * 4;      // decays between reference points [4][M] fp32
+  static constexpr int oFlag = oD + 4 * M * 4;    // 2 x NW ints
   static constexpr int total = oFlag + 2 * NW * 4;
   static_assert(C * M * 4 <= 2 * C * LDX * 2, "log alpha fits over X and Z");
   static_assert(2 * 4 * M * 4 <= C * LDX * 2 && 6 * M * 4 <= C * LDE * 4, "exact-path reductions fit");
@@ -94,32 +95,6 @@ struct BwdLds {
                 "LDS tiles must stay 16-byte aligned");
   static_assert(total <= kLdsBytes, "LDS");
 };
-
-// The chunk's factors for GPW slots from slot0 (token row = lane): X, Z (bf16),
-// E (fp32), E_C; E is also returned.  Returns whether any of these slots
-// decays below the factorised form's range in this chunk.
-template <int GPW, int LDX, int LDE, class Row>
-__device__ __forceinline__ bool bwd_factors(const Row& g, bool valid, float inv_tau, int lane, int slot0,
-                                            bf16_t* sX, bf16_t* sZ, float* sE, float* sDec,
-                                            float (&E)[GPW]) {
-  LogGates<GPW> gt;
-  gt.compute(g, valid, inv_tau);
-  bool small = false;
-  float z[GPW];
-#pragma unroll
-  for (int s = 0; s < GPW; s++) {
-    const float gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.G[s]), 63));
-    small |= !(gc >= kFastMinLog2Decay);
-    const float dc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt.E[s]), 63));
-    z[s] = gt.X[s] * dc;
-    E[s] = gt.E[s];
-    if (lane == 0) sDec[slot0 + s] = dc;
-  }
-  store_bf16_row<GPW>(sX + lane * LDX + slot0, gt.X);
-  store_bf16_row<GPW>(sZ + lane * LDX + slot0, z);
-  store_f32_row<GPW>(sE + lane * LDE + slot0, gt.E);
-  return small;
-}
 
 // Natural log alpha of GPW slots of one token row (the exact path); 0 for a
 // row past the end of the sequence.
@@ -229,12 +204,18 @@ struct TileN {
 // sum of s ds under its own softmax, to stat_rows[j * 2G + 0 / 1] (the pass
 // that the merged lse and delta come from: the same z and ds as the pass that
 // takes them, so that dz sums to zero over the slots).
-template <int DK, int DV, int M, int J, int ACT, int G, bool STATS>
+// SUB: the sub-chunk form (chunk_factors): z and ds add the sub-chunks' terms
+// by Horner's rule over the decays sD between reference points, the
+// reverse-map rows take the decay from the chunk start (the product of the
+// rows of sD before this wave's sub-chunk), and the second half gets dz*E in
+// fp32 at this wave's reference point (dze) instead of the packed dzb.
+template <int DK, int DV, int M, int J, int ACT, int G, bool STATS, bool SUB>
 __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, bf16_t* sS, bf16_t* sDZ,
                                           const float* sSeg, bf16_t* __restrict__ s_rows,
                                           bf16_t* __restrict__ dz_rows, bf16_t* __restrict__ h_rows,
                                           const float* __restrict__ lse_rows, const float* __restrict__ dl_rows,
-                                          float* __restrict__ stat_rows, int rv, bf16x8 (&dzb)[M / 32]) {
+                                          float* __restrict__ stat_rows, int rv, bf16x8 (&dzb)[M / 32],
+                                          f32x4 (&dze)[M / 16]) {
   using Lds = BwdLds<DK, DV, M>;
   constexpr int MT = M / 16, KQ = DK / 32, KV = DV / 32, NP = M / 32;
   constexpr int NR = J + 1, NPR = J / 2 + 1;
@@ -245,6 +226,7 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
   const bf16_t* sW = reinterpret_cast<const bf16_t*>(smem + Lds::oW);
   const bf16_t* sX = reinterpret_cast<const bf16_t*>(smem + Lds::oX);
   const float* sE = reinterpret_cast<const float*>(smem + Lds::oE);
+  const float* sD = reinterpret_cast<const float*>(smem + Lds::oD);
   const int L = lane & 15, g = lane >> 4;
   const int j = 16 * J + L;
 
@@ -269,11 +251,6 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
 #pragma unroll
   for (int i = 0; i < 4; i++)
     if (4 * g + i > L) at[J][i] = bt[J][i] = 0.f;
-  bf16x8 af[2], bfr[2];
-  af[0] = pack8(at[0], at[1]);
-  af[1] = pack8(at[2], at[3]);
-  bfr[0] = pack8(bt[0], bt[1]);
-  bfr[1] = pack8(bt[2], bt[3]);
 
   // z^T[c][j] = E[j][c] (Wk[c].q_j + sum_r X[r][c] A^T[r][j]); ds^T likewise
   f32x4 z[MT], ds[MT];
@@ -288,14 +265,44 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
 #pragma unroll
     for (int ct = 0; ct < MT; ct++)
       ds[ct] = mma(ld_row(sW + DK, Lds::LDW, 16 * ct, 32 * s, lane), df[s], ds[ct]);
+  if constexpr (!SUB) {
+    bf16x8 af[2], bfr[2];
+    af[0] = pack8(at[0], at[1]);
+    af[1] = pack8(at[2], at[3]);
+    bfr[0] = pack8(bt[0], bt[1]);
+    bfr[1] = pack8(bt[2], bt[3]);
 #pragma unroll
-  for (int pr = 0; pr < NPR; pr++)
+    for (int pr = 0; pr < NPR; pr++)
 #pragma unroll
-    for (int ct = 0; ct < MT; ct++) {
-      const bf16x8 xa = ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane);
-      z[ct] = mma(xa, af[pr], z[ct]);
-      ds[ct] = mma(xa, bfr[pr], ds[ct]);
+      for (int ct = 0; ct < MT; ct++) {
+        const bf16x8 xa = ld_col(sX, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane);
+        z[ct] = mma(xa, af[pr], z[ct]);
+        ds[ct] = mma(xa, bfr[pr], ds[ct]);
+      }
+  } else {
+#pragma unroll
+    for (int R = 0; R < NR; R++) {
+      if (R > 0) {
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) {
+          const float4 dd = *reinterpret_cast<const float4*>(sD + (R - 1) * M + 16 * ct + 4 * g);
+          const float d4[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            z[ct][i] *= d4[i];
+            ds[ct][i] *= d4[i];
+          }
+        }
+      }
+      const bf16x4v ar = pack4(at[R]), br = pack4(bt[R]);
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        const bf16x4v xa = ld_col4(sX, Lds::LDX, 16 * ct, 16 * R + 4 * g, lane);
+        z[ct] = mma16(xa, ar, z[ct]);
+        ds[ct] = mma16(xa, br, ds[ct]);
+      }
     }
+  }
   float e[MT][4];
 #pragma unroll
   for (int ct = 0; ct < MT; ct++) {
@@ -371,7 +378,17 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
   for (int ct = 0; ct < MT; ct++) {
     const int c = 16 * ct + 4 * g;
     const float4 dd = *reinterpret_cast<const float4*>(sSeg + c);
-    const float d4[4] = {dd.x, dd.y, dd.z, dd.w};
+    float d4[4] = {dd.x, dd.y, dd.z, dd.w};
+    if constexpr (SUB) {  // and the decay from the chunk start to this wave's reference point
+#pragma unroll
+      for (int r = 0; r < J; r++) {
+        const float4 dr = *reinterpret_cast<const float4*>(sD + r * M + c);
+        d4[0] *= dr.x;
+        d4[1] *= dr.y;
+        d4[2] *= dr.z;
+        d4[3] *= dr.w;
+      }
+    }
     float h[4], sed[4], dzed[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -388,37 +405,75 @@ __device__ __forceinline__ void fwd_pass1(int lane, const unsigned char* smem, b
     store_bf16x4(sDZ + j * Lds::LDX + c, dzed[0], dzed[1], dzed[2], dzed[3]);
   }
   // (dz*E)^T as B operands over slot pairs (the permuted slot order of pass 2)
+  if constexpr (!SUB) {
 #pragma unroll
-  for (int p = 0; p < NP; p++) {
-    const f32x4 a = {dz[2 * p][0] * e[2 * p][0], dz[2 * p][1] * e[2 * p][1], dz[2 * p][2] * e[2 * p][2],
-                     dz[2 * p][3] * e[2 * p][3]};
-    const f32x4 b = {dz[2 * p + 1][0] * e[2 * p + 1][0], dz[2 * p + 1][1] * e[2 * p + 1][1],
-                     dz[2 * p + 1][2] * e[2 * p + 1][2], dz[2 * p + 1][3] * e[2 * p + 1][3]};
-    dzb[p] = pack8(a, b);
+    for (int p = 0; p < NP; p++) {
+      const f32x4 a = {dz[2 * p][0] * e[2 * p][0], dz[2 * p][1] * e[2 * p][1], dz[2 * p][2] * e[2 * p][2],
+                       dz[2 * p][3] * e[2 * p][3]};
+      const f32x4 b = {dz[2 * p + 1][0] * e[2 * p + 1][0], dz[2 * p + 1][1] * e[2 * p + 1][1],
+                       dz[2 * p + 1][2] * e[2 * p + 1][2], dz[2 * p + 1][3] * e[2 * p + 1][3]};
+      dzb[p] = pack8(a, b);
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) dze[ct][i] = dz[ct][i] * e[ct][i];
   }
 }
 
 // Pass waves, second half: dq^T[n][j] = sum_c Wk[c][n] (dz*E)[j][c] +
 // sum_{r<=j} K[r][n] A3^T[r][j], A3^T[r][j] = sum_c X[r][c] (dz*E)[j][c].
-template <int DK, int DV, int M, int J, int G>
-__device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, const bf16x8 (&dzb)[M / 32],
-                                          GradT<G>* __restrict__ dq_rows, int rv) {
+// SUB: from dze at this wave's reference point, carried back one sub-chunk at
+// a time (times sD[R]) before the scores of sub-chunk R; the last set (from
+// the chunk start) is the state read's operand.
+template <int DK, int DV, int M, int J, int G, bool SUB>
+__device__ __forceinline__ void fwd_pass2(int lane, const unsigned char* smem, const bf16x8 (&dzb_in)[M / 32],
+                                          const f32x4 (&dze_in)[M / 16], GradT<G>* __restrict__ dq_rows, int rv) {
   using Lds = BwdLds<DK, DV, M>;
-  constexpr int NP = M / 32, NKT = DK / 16;
+  constexpr int NP = M / 32, NKT = DK / 16, MT = M / 16;
   constexpr int NR = J + 1, NPR = J / 2 + 1;
   const bf16_t* sK = reinterpret_cast<const bf16_t*>(smem + Lds::oK);
   const bf16_t* sW = reinterpret_cast<const bf16_t*>(smem + Lds::oW);
   const bf16_t* sX = reinterpret_cast<const bf16_t*>(smem + Lds::oX);
+  const float* sD = reinterpret_cast<const float*>(smem + Lds::oD);
   const int L = lane & 15, g = lane >> 4;
   const int j = 16 * J + L;
   f32x4 a3[4];
 #pragma unroll
   for (int R = 0; R < 4; R++) a3[R] = zero4();
+  bf16x8 dzb[NP];
+  if constexpr (!SUB) {
 #pragma unroll
-  for (int p = 0; p < NP; p++)
+    for (int p = 0; p < NP; p++) dzb[p] = dzb_in[p];
 #pragma unroll
-    for (int R = 0; R < NR; R++)
-      a3[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), dzb[p], a3[R]);
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int R = 0; R < NR; R++)
+        a3[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), dzb[p], a3[R]);
+  } else {
+    f32x4 u[MT];
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) u[ct] = dze_in[ct];
+#pragma unroll
+    for (int R = NR - 1; R >= 0; R--) {
+      if (R < J) {
+#pragma unroll
+        for (int ct = 0; ct < MT; ct++) {
+          const float4 dd = *reinterpret_cast<const float4*>(sD + R * M + 16 * ct + 4 * g);
+          u[ct][0] *= dd.x;
+          u[ct][1] *= dd.y;
+          u[ct][2] *= dd.z;
+          u[ct][3] *= dd.w;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NP; p++) dzb[p] = pack8(u[2 * p], u[2 * p + 1]);
+#pragma unroll
+      for (int p = 0; p < NP; p++)
+        a3[R] = mma(ld_row2(sX, Lds::LDX, 16 * R, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), dzb[p], a3[R]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++)
     if (4 * g + i > L) a3[J][i] = 0.f;
@@ -628,6 +683,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   bf16_t* sDZ = reinterpret_cast<bf16_t*>(smem + Lds::oDZ);
   float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
   float* sSeg = reinterpret_cast<float*>(smem + Lds::oAux);
+  float* sD = reinterpret_cast<float*>(smem + Lds::oD);
   float* sLa = reinterpret_cast<float*>(smem + Lds::oX);
   int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
 
@@ -668,8 +724,8 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   };
   // stage chunk ch (the pass waves its tiles, every wave its factors),
   // barrier A, log alpha for an exact chunk, the loads of the next chunk
-  // (this one again at the end); returns whether ch is exact
-  auto stage = [&](auto pass, int ch, int it, int lane_, int tid_) -> bool {
+  // (this one again at the end); returns the chunk's regime bits
+  auto stage = [&](auto pass, int ch, int it, int lane_, int tid_) -> int {
     const int rv = rows_of(ch);
     if constexpr (decltype(pass)::value) {
       pq.store(sQ, Lds::LDQ, rv, tid_);
@@ -679,10 +735,10 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     }
     gr.pin();
     float E[GPW];
-    const bool small =
-        bwd_factors<GPW, Lds::LDX, Lds::LDE>(gr, lane_ < rv, inv_tau, lane_, slot0, sX, sZ, sE, sDec, E);
-    const bool slow = block_any(small, sFlag, it, lane_, wv);
-    if (slow) {  // every factor reader is past barrier A
+    const int small = chunk_factors<GPW, Lds::LDX, Lds::LDE, M>(gr, lane_ < rv, inv_tau, lane_, slot0, sX, sZ,
+                                                                 sE, sD, sDec, E);
+    const int regime = block_or(small, sFlag, it, lane_, wv);
+    if (regime & kNeedExact) {  // every factor reader is past barrier A
       float la[GPW];
       log_alpha_row<GPW>(gr, lane_ < rv, inv_tau, la);
       store_f32_row<GPW>(sLa + lane_ * M + slot0, la);
@@ -690,7 +746,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     const int cn = min(ch + 1, c_end - 1);
     load_gates(cn, lane_);
     if constexpr (decltype(pass)::value) load_tiles(cn, tid_);
-    return slow;
+    return regime;
   };
   using Pass = std::integral_constant<bool, true>;
   using State = std::integral_constant<bool, false>;
@@ -706,7 +762,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       asm volatile("" : "+v"(lane_i), "+v"(tid_i));
       const int rv = rows_of(ch);
       W.store_copy(sW, Lds::LDW, sw, lane_i);  // the chunk's start state for the pass waves
-      const bool slow = stage(State{}, ch, ch - c_begin, lane_i, tid_i);
+      const bool slow = stage(State{}, ch, ch - c_begin, lane_i, tid_i) & kNeedExact;
       if (!slow) {
         W.carry(sK, Lds::LDQ, sV, Lds::LDV, sZ, Lds::LDX, sDec, sw, lane_i);
         __syncthreads();  // M: the reverse-map operands are in LDS
@@ -729,10 +785,12 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     load_tiles(c_begin, tid);
     bf16x8 dzb[NP];
     for (int ch = c_begin; ch < c_end; ch++) {
+      f32x4 dze[M / 16];  // dz*E of the sub-chunk form (both halves before M)
       int lane_i = lane, tid_i = tid;
       asm volatile("" : "+v"(lane_i), "+v"(tid_i));
       const int t0 = ch * C, rv = rows_of(ch);
-      const bool slow = stage(Pass{}, ch, ch - c_begin, lane_i, tid_i);
+      const int regime = stage(Pass{}, ch, ch - c_begin, lane_i, tid_i);
+      const bool slow = regime & kNeedExact, sub = regime & kNeedSub;
       bf16_t* srow = s_ws + (wb + t0) * M;
       bf16_t* dzrow = dz_ws + (wb + t0) * M;
       bf16_t* hrow = h_ws + (wb + t0) * M;
@@ -740,23 +798,47 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       const float* drow = G > 1 && !STATS ? delta + ub + t0 : nullptr;
       float* strow = STATS ? stats + ((ub + t0) * G + grp) * 2 : nullptr;
       if (!slow) {
-        switch (wv) {
-          case 0: fwd_pass1<DK, DV, M, 0, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
-          case 1: fwd_pass1<DK, DV, M, 1, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
-          case 2: fwd_pass1<DK, DV, M, 2, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
-          default: fwd_pass1<DK, DV, M, 3, ACT, G, STATS>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, strow, rv, dzb); break;
+#define GSA_FWD_PASS1(JJ, SB)                                                                            \
+  fwd_pass1<DK, DV, M, JJ, ACT, G, STATS, SB>(lane_i, smem, sS, sDZ, sSeg, srow, dzrow, hrow, lrow, drow, \
+                                              strow, rv, dzb, dze)
+        if (!sub) {
+          switch (wv) {
+            case 0: GSA_FWD_PASS1(0, false); break;
+            case 1: GSA_FWD_PASS1(1, false); break;
+            case 2: GSA_FWD_PASS1(2, false); break;
+            default: GSA_FWD_PASS1(3, false); break;
+          }
+        } else {
+          // some slot decays out of the chunk form's range: sub-chunk
+          // reference points; both halves before M (dz*E stays in this
+          // branch's registers)
+          GradT<G>* dqrow = dqb + (size_t)t0 * (DK * G);
+#define GSA_FWD_SUB(JJ)                                                          \
+  GSA_FWD_PASS1(JJ, true);                                                       \
+  if constexpr (!STATS) fwd_pass2<DK, DV, M, JJ, G, true>(lane_i, smem, dzb, dze, dqrow, rv)
+          switch (wv) {
+            case 0: GSA_FWD_SUB(0); break;
+            case 1: GSA_FWD_SUB(1); break;
+            case 2: GSA_FWD_SUB(2); break;
+            default: GSA_FWD_SUB(3); break;
+          }
+#undef GSA_FWD_SUB
         }
+#undef GSA_FWD_PASS1
         __syncthreads();  // M
         // the decay from the segment start, advanced past this chunk (its
         // readers are all before M; E_C is rewritten only after B)
         if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];
         GradT<G>* dqrow = dqb + (size_t)t0 * (DK * G);
-        if constexpr (!STATS)
-        switch (wv) {
-          case 0: fwd_pass2<DK, DV, M, 0, G>(lane_i, smem, dzb, dqrow, rv); break;
-          case 1: fwd_pass2<DK, DV, M, 1, G>(lane_i, smem, dzb, dqrow, rv); break;
-          case 2: fwd_pass2<DK, DV, M, 2, G>(lane_i, smem, dzb, dqrow, rv); break;
-          default: fwd_pass2<DK, DV, M, 3, G>(lane_i, smem, dzb, dqrow, rv); break;
+        if constexpr (!STATS) {
+          if (!sub) {
+            switch (wv) {
+              case 0: fwd_pass2<DK, DV, M, 0, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
+              case 1: fwd_pass2<DK, DV, M, 1, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
+              case 2: fwd_pass2<DK, DV, M, 2, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
+              default: fwd_pass2<DK, DV, M, 3, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
+            }
+          }
         }
       } else {
         __syncthreads();  // log alpha is in LDS
@@ -829,7 +911,13 @@ bwd_bf16_rscan(float* __restrict__ rm, const float* __restrict__ rdec, const flo
 // over the wave's rows from j on (pre), the wave's total per slot (sWt[J]).
 // The rest (later waves' totals and the carry from later chunks) is added
 // after the next barrier by rev_pass_finish.
-template <int DK, int DV, int M, int J, int G>
+// SUB: the sub-chunk form (chunk_factors; s*E and dz*E staged at each token's
+// own reference point): the X rows of this wave are carried to the reference
+// point of each later read sub-chunk T (times sD[J] ... sD[T-1]) before its
+// scores, and di adds the read sub-chunks' terms by Horner's rule from the
+// chunk end (the adjoint term first, times sD[3], then each sub-chunk T = 3 ..
+// J after a scaling by sD[T]).
+template <int DK, int DV, int M, int J, int G, bool SUB>
 __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, float* sWt,
                                          const bf16_t* __restrict__ h_rows, const bf16_t* __restrict__ g_rows,
                                          GradT<G>* __restrict__ dk_rows, GradT<G>* __restrict__ dv_rows, int rv,
@@ -848,6 +936,7 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
   const bf16_t* sS = reinterpret_cast<const bf16_t*>(smem + Lds::oS);
   const bf16_t* sDZ = reinterpret_cast<const bf16_t*>(smem + Lds::oDZ);
   const float* sDec = reinterpret_cast<const float*>(smem + Lds::oDec);
+  const float* sD = reinterpret_cast<const float*>(smem + Lds::oD);
   const int L = lane & 15, g = lane >> 4;
   const int j = 16 * J + L;
   const bool valid = j < rv;
@@ -886,13 +975,38 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
   f32x4 ad[4], a2[4];
 #pragma unroll
   for (int T = 0; T < 4; T++) ad[T] = a2[T] = zero4();
+  if constexpr (!SUB) {
 #pragma unroll
-  for (int p = 0; p < NP; p++)
+    for (int p = 0; p < NP; p++)
+#pragma unroll
+      for (int T = J; T < 4; T++) {
+        ad[T] = mma(ld_row2(sDZ, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], ad[T]);
+        a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], a2[T]);
+      }
+  } else {
+    // X of this lane's row j in fp32 (slots 32p + 4g + 0..3 and 32p + 16 + 4g + 0..3)
+    f32x8 xr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; p++) xr[p] = __builtin_convertvector(xb[p], f32x8);
 #pragma unroll
     for (int T = J; T < 4; T++) {
-      ad[T] = mma(ld_row2(sDZ, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], ad[T]);
-      a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], a2[T]);
+      if (T > J) {
+#pragma unroll
+        for (int p = 0; p < NP; p++) {
+          const float4 lo = *reinterpret_cast<const float4*>(sD + (T - 1) * M + 32 * p + 4 * g);
+          const float4 hi = *reinterpret_cast<const float4*>(sD + (T - 1) * M + 32 * p + 16 + 4 * g);
+          xr[p][0] *= lo.x; xr[p][1] *= lo.y; xr[p][2] *= lo.z; xr[p][3] *= lo.w;
+          xr[p][4] *= hi.x; xr[p][5] *= hi.y; xr[p][6] *= hi.z; xr[p][7] *= hi.w;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < NP; p++) {
+        const bf16x8 xt = __builtin_convertvector(xr[p], bf16x8);
+        ad[T] = mma(ld_row2(sDZ, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xt, ad[T]);
+        a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xt, a2[T]);
+      }
     }
+  }
 #pragma unroll
   for (int i = 0; i < 4; i++)
     if (4 * g + i < L) s1[J][i] = s2[J][i] = ad[J][i] = a2[J][i] = 0.f;  // causal: t' >= j
@@ -956,21 +1070,41 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
 #pragma unroll
     for (int ct = 0; ct < MT; ct++)
       di[ct] = mma(ld_row(sW + DK, Lds::LDW, 16 * ct, 32 * s, lane), vf[s], di[ct]);
-#pragma unroll
-  for (int ct = 0; ct < MT; ct++) {
-    const float4 d = *reinterpret_cast<const float4*>(sDec + 16 * ct + 4 * g);
-    di[ct][0] *= d.x;
-    di[ct][1] *= d.y;
-    di[ct][2] *= d.z;
-    di[ct][3] *= d.w;
-  }
-#pragma unroll
-  for (int pr = PR0; pr < 2; pr++)
+  if constexpr (!SUB) {
 #pragma unroll
     for (int ct = 0; ct < MT; ct++) {
-      di[ct] = mma(ld_col(sDZ, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s1f[pr], di[ct]);
-      di[ct] = mma(ld_col(sS, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s2f[pr], di[ct]);
+      const float4 d = *reinterpret_cast<const float4*>(sDec + 16 * ct + 4 * g);
+      di[ct][0] *= d.x;
+      di[ct][1] *= d.y;
+      di[ct][2] *= d.z;
+      di[ct][3] *= d.w;
     }
+#pragma unroll
+    for (int pr = PR0; pr < 2; pr++)
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        di[ct] = mma(ld_col(sDZ, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s1f[pr], di[ct]);
+        di[ct] = mma(ld_col(sS, Lds::LDX, 16 * ct, 32 * pr + 4 * g, 32 * pr + 16 + 4 * g, lane), s2f[pr], di[ct]);
+      }
+  } else {
+#pragma unroll
+    for (int T = 3; T >= J; T--) {
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        const float4 d = *reinterpret_cast<const float4*>(sD + T * M + 16 * ct + 4 * g);
+        di[ct][0] *= d.x;
+        di[ct][1] *= d.y;
+        di[ct][2] *= d.z;
+        di[ct][3] *= d.w;
+      }
+      const bf16x4v b1 = pack4(s1[T]), b2 = pack4(s2[T]);
+#pragma unroll
+      for (int ct = 0; ct < MT; ct++) {
+        di[ct] = mma16(ld_col4(sDZ, Lds::LDX, 16 * ct, 16 * T + 4 * g, lane), b1, di[ct]);
+        di[ct] = mma16(ld_col4(sS, Lds::LDX, 16 * ct, 16 * T + 4 * g, lane), b2, di[ct]);
+      }
+    }
+  }
 
   // gate: u = h - (1 - alpha) di; sums over the wave's rows from j on (DPP
   // row shifts towards lower lanes), pre = that sum - alpha di
@@ -1147,6 +1281,7 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   float* sDec = reinterpret_cast<float*>(smem + Lds::oDec);
   float* sCarry = reinterpret_cast<float*>(smem + Lds::oAux);  // [2][M]
   float* sWt = reinterpret_cast<float*>(smem + Lds::oWt);      // [4][M]
+  float* sD = reinterpret_cast<float*>(smem + Lds::oD);
   float* sLa = reinterpret_cast<float*>(smem + Lds::oX);
   int* sFlag = reinterpret_cast<int*>(smem + Lds::oFlag);
 
@@ -1185,9 +1320,10 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     sr.load(s_ws + (wb + tr) * M + slot0);
     zr.load(dz_ws + (wb + tr) * M + slot0);
   };
-  // stage chunk ch: tiles, factors, s*E and dz*E (zero past the end); barrier
-  // A; log alpha for an exact chunk; the loads of the chunk before
-  auto stage = [&](int ch, int it, int lane_, int tid_) -> bool {
+  // stage chunk ch: tiles, factors, s*E and dz*E (zero past the end, E from
+  // each token's reference point); barrier A; log alpha for an exact chunk;
+  // the loads of the chunk before; returns the chunk's regime bits
+  auto stage = [&](int ch, int it, int lane_, int tid_) -> int {
     const int rv = rows_of(ch);
     pq.store(sQ, Lds::LDQ, rv, tid_);
     pk.store(sK, Lds::LDQ, rv, tid_);
@@ -1198,7 +1334,8 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     zr.pin();
     float E[GPW];
     const bool ok = lane_ < rv;
-    const bool small = bwd_factors<GPW, Lds::LDX, Lds::LDE>(gr, ok, inv_tau, lane_, slot0, sX, sZ, sE, sDec, E);
+    const int small = chunk_factors<GPW, Lds::LDX, Lds::LDE, M>(gr, ok, inv_tau, lane_, slot0, sX, sZ, sE, sD,
+                                                                 sDec, E);
     float se[GPW], ze[GPW];
 #pragma unroll
     for (int s = 0; s < GPW; s++) {
@@ -1207,14 +1344,14 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
     }
     store_bf16_row<GPW>(sS + lane_ * Lds::LDX + slot0, se);
     store_bf16_row<GPW>(sDZ + lane_ * Lds::LDX + slot0, ze);
-    const bool slow = block_any(small, sFlag, it, lane_, wv);
-    if (slow) {
+    const int regime = block_or(small, sFlag, it, lane_, wv);
+    if (regime & kNeedExact) {
       float la[GPW];
       log_alpha_row<GPW>(gr, ok, inv_tau, la);
       store_f32_row<GPW>(sLa + lane_ * M + slot0, la);
     }
     load_chunk(max(ch - 1, c_begin), lane_, tid_);  // the chunk before (this one again at the end)
-    return slow;
+    return regime;
   };
 
   load_chunk(c_end - 1, lane, tid);
@@ -1249,10 +1386,13 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       asm volatile("" : "+v"(lane_i), "+v"(tid_i));
       const int t0 = ch * C, rv = rows_of(ch);
       W.store_copy(sW, Lds::LDW, sw, lane_i);  // the adjoint at the chunk end, for the pass waves
-      const bool slow = stage(ch, it, lane_i, tid_i);
-      if (!slow) {
+      const int regime = stage(ch, it, lane_i, tid_i);
+      if (!(regime & kNeedExact)) {
         // the adjoint at the chunk start: Diag(E_C) dW + [Q | dO]^T [dz*E | s*E]
-        W.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sw, lane_i);
+        if (!(regime & kNeedSub))
+          W.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sw, lane_i);
+        else
+          W.update2_sub(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sD, sw, lane_i);
       } else {
         __syncthreads();  // log alpha is in LDS
         rev_exact_state<DK, DV, M, G>(W, rv, smem, s_ws + (wb + t0) * M, dz_ws + (wb + t0) * M,
@@ -1273,19 +1413,32 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
       asm volatile("" : "+v"(lane_i), "+v"(tid_i));
       const int t0 = ch * C, rv = rows_of(ch);
       const float* carry = sCarry + (it & 1) * M;
-      const bool slow = stage(ch, it, lane_i, tid_i);
+      const int regime = stage(ch, it, lane_i, tid_i);
+      const bool slow = regime & kNeedExact;
       const bf16_t* hrow = h_ws + (wb + t0) * M;
       const bf16_t* grow = gb + (size_t)t0 * GS;
       GradT<G>* dkrow = dkb + (size_t)t0 * (DK * G);
       GradT<G>* dvrow = dvb + (size_t)t0 * (DV * G);
       bf16_t* dgrow = dgb + (size_t)t0 * GS;
       if (!slow) {
-        switch (wv) {
-          case 0: rev_pass<DK, DV, M, 0, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          case 1: rev_pass<DK, DV, M, 1, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          case 2: rev_pass<DK, DV, M, 2, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
-          default: rev_pass<DK, DV, M, 3, G>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn); break;
+#define GSA_REV_PASS(JJ, SB) \
+  rev_pass<DK, DV, M, JJ, G, SB>(lane_i, smem, sWt, hrow, grow, dkrow, dvrow, rv, inv_tau, pre, sn)
+        if (!(regime & kNeedSub)) {
+          switch (wv) {
+            case 0: GSA_REV_PASS(0, false); break;
+            case 1: GSA_REV_PASS(1, false); break;
+            case 2: GSA_REV_PASS(2, false); break;
+            default: GSA_REV_PASS(3, false); break;
+          }
+        } else {  // sub-chunk reference points
+          switch (wv) {
+            case 0: GSA_REV_PASS(0, true); break;
+            case 1: GSA_REV_PASS(1, true); break;
+            case 2: GSA_REV_PASS(2, true); break;
+            default: GSA_REV_PASS(3, true); break;
+          }
         }
+#undef GSA_REV_PASS
       } else {
         __syncthreads();  // log alpha is in LDS
         rev_exact_pass<M, G>(rv, smem, Lds::oS, carry, sWt, hrow, grow, dgrow, inv_tau, lane_i, wv);

@@ -70,8 +70,8 @@ struct OutLds {
   static constexpr int fX = 0;                         // X [C][M] bf16
   static constexpr int fZ = fX + C * LDX * 2;          // Z [C][M] bf16
   static constexpr int fE = fZ + C * LDX * 2;          // E [C][M] fp32
-  static constexpr int fD = fE + C * LDE * 4;          // sub-chunk decays [3][M] fp32
-  static constexpr int szF = fD + 3 * M * 4;           // one factor set
+  static constexpr int fD = fE + C * LDE * 4;          // decays between reference points [4][M] fp32
+  static constexpr int szF = fD + 4 * M * 4;           // one factor set
   static constexpr int szFast = oF + 2 * szF - oR;
   // exact-recurrence path
   static constexpr int oWf = oR;                       // fp32 W [M][DK+DV]
@@ -609,8 +609,9 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
   // their load, at the call)
   auto factors = [&](Row& r, int rv, int fb, int lane_) -> int {
     r.pin();
+    float e_unused[GPW];
     return chunk_factors<GPW, Lds::LDX, Lds::LDE, M>(r, lane_ < rv, inv_tau, lane_, slot0, fX(fb), fZ(fb),
-                                                      fE(fb), fD(fb), sDec0 + fb * M);
+                                                      fE(fb), fD(fb), sDec0 + fb * M, e_unused);
   };
   auto log_alpha = [&](const Row& r, int rv, int lane_) {  // natural log, exact path
 #pragma unroll

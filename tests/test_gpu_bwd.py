@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import TOL, gates_fast_slots, gates_regime_per_chunk, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -291,15 +291,15 @@ def test_autograd_double_backward_raises(gsa, torch):
 
 
 def test_bwd_exact_chunks_inside_segments_sampled(gsa, torch):
-    """Segments of several chunks where most chunks leave the factorised range
-    (8 of 64 slots at logits N(-6, 1), about -48 of log-decay per chunk) and
-    one chunk in the middle of a segment holds gates at +-inf: the exact
-    token walks carry the state, the reverse map, the adjoint and the gate
-    sums across fast and exact chunks alike.  Sampled units against the
-    oracle."""
+    """Segments of several chunks where every chunk leaves the chunk form's
+    range (8 of 64 slots at logits N(-10, 1), 64-token decay products near
+    2^-115: the sub-chunk form) and one chunk in the middle of a segment
+    holds gates at +-inf (an exact walk): the state, the reverse map, the
+    adjoint and the gate sums carry across sub-chunk-form and exact chunks
+    alike.  Sampled units against the oracle."""
     B, H, T = 8, 4, 1024  # 32 units of 16 chunks: segments of 2 chunks
     inp = synth.gsa_inputs(B, H, T, 128, 128, 64, dtype="bf16", seed=81, init_std=0.1, fast_slots=8,
-                           fast_shift=-6.0)
+                           fast_shift=-10.0)
     x = inp["g"].f64.copy()
     x[:, :, 70:90, 20:30] = np.inf
     x[:, :, 75, 40:] = -np.inf
@@ -319,3 +319,25 @@ def test_bwd_decay_near_the_floor(gsa, torch, mean):
         r = np.random.default_rng(6)
         inp["g"] = synth.stored(mean + 0.05 * r.standard_normal(inp["g"].shape), "bf16")
     _check(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, final=True, seed=83, edit=mut)
+
+
+@pytest.mark.parametrize("case", ["fast_slots", "sub_floor", "per_chunk"])
+@pytest.mark.parametrize("d,m", [(128, 64), (64, 32), (128, 32), (64, 64)])
+def test_bwd_subchunk_form(gsa, torch, case, d, m):
+    """Chunks out of the chunk form's range run both sweeps with 16-token
+    sub-chunk reference points: 8 slots at g ~ N(-10, 1) everywhere
+    ("fast_slots"), 8 slots at g ~ N(-30.5, 0.05) everywhere (16-token
+    products ~2^-88, X up to ~2^88: "sub_floor"), and the chunk / sub-chunk
+    / exact regimes in turn ("per_chunk"); initial states and final-state
+    gradients on.  (With every slot near that floor all slot scores of a
+    token are nearly equal and dz = s (ds - s.ds) cancels to a few percent of
+    its terms, which bf16 operands do not resolve to this bar.)"""
+    edit = {"fast_slots": gates_fast_slots(8, -10.0), "sub_floor": gates_fast_slots(8, -30.5, 0.05),
+            "per_chunk": gates_regime_per_chunk}[case]
+    _check(gsa, torch, 2, 2, 64 * 5 + 11, d, m, "bf16", init=True, final=True, seed=84, edit=edit)
+
+
+@pytest.mark.parametrize("nl", ["identity", "swish", "relu2"])
+def test_bwd_subchunk_form_elementwise_reads(gsa, torch, nl):
+    _check(gsa, torch, 1, 2, 64 * 4 + 9, 128, 64, "bf16", init=True, final=True, seed=85,
+           edit=gates_fast_slots(8, -10.0), nl=nl)

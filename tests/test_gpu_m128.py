@@ -218,7 +218,8 @@ def test_bwd_relu_read_rejected(gsa, torch):
 
 
 def test_bwd_one_group_decays_fast(gsa, torch):
-    """Exact-recurrence chunks in the second group only, and +-inf gates."""
+    """Sub-chunk-form chunks in the second group only (g = -12 on its slots:
+    64-token products ~2^-138), and +-inf gates (exact walks)."""
     def mut(inp):
         x = inp["g"].f64.copy()
         x[..., 64:128, 64:] = -12.0

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import (TOL, gates_fast_slots, gates_normal, gates_regime_per_chunk, rel_err, to_dev,
+                                to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -324,15 +325,6 @@ def _shift_gates(shift):
     return mut
 
 
-def _near_floor(x_mean, x_std):
-    """Gate logits N(x_mean, x_std) on every token (a decay regime chosen
-    relative to the factorised form's floor of 2^-90 per 64-token chunk)."""
-    def mut(inp):
-        r = np.random.default_rng(5)
-        inp["g"] = synth.stored(x_mean + x_std * r.standard_normal(inp["g"].shape), inp["g"].dtype)
-    return mut
-
-
 @pytest.mark.parametrize("case", ["all", "mixed", "near_floor"])
 def test_gsa_bf16_strong_decay(gsa, torch, case):
     # alpha = sigmoid(g)^(1/8).  "all": g ~ N(-8, 1) makes the 64-token decay
@@ -342,37 +334,9 @@ def test_gsa_bf16_strong_decay(gsa, torch, case):
     # form) and N(0, 1) elsewhere.  "near_floor": g ~ N(-7.3, 0.05), products
     # ~2^-84: every chunk in the chunk form with X up to ~2^84.
     mut = {"all": _shift_gates(-8.0), "mixed": _decay_chunks((1, 3), -12.0),
-           "near_floor": _near_floor(-7.3, 0.05)}[case]
+           "near_floor": gates_normal(-7.3, 0.05)}[case]
     for cps in (0, 1):
         _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, 128, 64, "bf16", init=True, cps=cps, seed=21, mutate=mut)
-
-
-def _fast_slots(n, mean, std=1.0, seed=6):
-    """Gate logits N(mean, std) on the first n slots of every token (a few
-    slots forgetting fast), the stored N(0, 1) logits elsewhere."""
-    def mut(inp):
-        x = inp["g"].f64.copy()
-        r = np.random.default_rng(seed)
-        x[..., :n] = mean + std * r.standard_normal(x[..., :n].shape)
-        inp["g"] = synth.stored(x, inp["g"].dtype)
-    return mut
-
-
-def _regime_per_chunk(inp):
-    """One decay regime per 64-token chunk: 0 plain (chunk form); 1 g = -12 on
-    every slot (64-token products ~2^-138, 16-token ~2^-35: sub-chunk form);
-    2 g = -inf on one slot for three tokens (a 16-token product below 2^-90:
-    exact walk); 3 g ~ N(-10, 1) on 8 slots (sub-chunk form); 4 g = -30.5 on
-    4 slots (16-token products ~2^-88, the sub-chunk form near its floor);
-    the ragged tail plain."""
-    x = inp["g"].f64.copy()
-    m = x.shape[-1]
-    x[..., 64:128, :] = -12.0
-    x[..., 130:133, m // 2] = -np.inf
-    r = np.random.default_rng(8)
-    x[..., 192:256, :8] = -10.0 + r.standard_normal(x[..., 192:256, :8].shape)
-    x[..., 256:320, m - 4:] = -30.5
-    inp["g"] = synth.stored(x, inp["g"].dtype)
 
 
 @pytest.mark.parametrize("case", ["fast_slots", "sub_floor", "per_chunk"])
@@ -385,8 +349,8 @@ def test_gsa_bf16_subchunk_form(gsa, torch, case, d, m):
     ~2^-115, every chunk in the sub-chunk form).  "sub_floor": every slot at
     g ~ N(-30.5, 0.05) (16-token products ~2^-88: X up to ~2^88).
     "per_chunk": the plain, sub-chunk and exact regimes in turn."""
-    mut = {"fast_slots": _fast_slots(8, -10.0), "sub_floor": _near_floor(-30.5, 0.05),
-           "per_chunk": _regime_per_chunk}[case]
+    mut = {"fast_slots": gates_fast_slots(8, -10.0), "sub_floor": gates_normal(-30.5, 0.05),
+           "per_chunk": gates_regime_per_chunk}[case]
     for cps in (0, 1):
         _check_gsa(gsa, torch, 2, 2, 64 * 5 + 11, d, m, "bf16", init=True, cps=cps, seed=23, mutate=mut)
 
@@ -397,7 +361,7 @@ def test_gla_bf16_strong_decay(gsa, torch, case):
     # near the floor); "mixed": g = -12 on chunks 1 and 3 only; "near_floor":
     # g ~ N(-15.5, 0.05), products ~2^-89
     mut = {"all": _shift_gates(-12.0), "mixed": _decay_chunks((1, 3), -12.0),
-           "near_floor": _near_floor(-15.5, 0.05)}[case]
+           "near_floor": gates_normal(-15.5, 0.05)}[case]
     for cps in (0, 1):
         _check_gla(gsa, torch, 1, 3, 64 * 5 + 11, 128, "bf16", init=True, cps=cps, seed=22, mutate=mut)
 

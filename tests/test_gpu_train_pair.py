@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import TOL, gates_regime_per_chunk, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +27,11 @@ def gsa(torch):
     return m
 
 
-def _case(gsa, torch, B, H, T, d, m, init, final, seed, nl="softmax", qkv_scale=None):
+def _case(gsa, torch, B, H, T, d, m, init, final, seed, nl="softmax", qkv_scale=None, edit=None):
     inp = synth.gsa_inputs(B, H, T, d, d, m, dtype="bf16", seed=seed, qkv_scale=qkv_scale,
                            init_std=0.1 if init else None)
+    if edit is not None:
+        edit(inp)
     gi = synth.gsa_grad_inputs(B, H, T, d, d, m, dtype="bf16", seed=seed + 1000,
                                final_std=1.0 if final else None)
     dev = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "k0", "v0")}
@@ -61,6 +63,19 @@ def test_pair_gradients_and_forward(gsa, torch, T, d, m):
 @pytest.mark.parametrize("nl", ["swish", "relu2", "identity"])
 def test_pair_elementwise_reads(gsa, torch, nl):
     _case(gsa, torch, 1, 3, 300, 128, 64, init=True, final=False, seed=7, nl=nl)
+
+
+@pytest.mark.parametrize("m", [64, 128])
+def test_pair_subchunk_form(gsa, torch, m):
+    """The chunk / sub-chunk / exact regimes in turn through the kept-state
+    pair (bit-equal to gsa_bwd) and the forward against the oracle."""
+    inp, o, kf, vf = _case(gsa, torch, 2, 2, 64 * 5 + 11, 128, m, init=True, final=True, seed=31,
+                           edit=gates_regime_per_chunk)
+    opt = lambda x: None if x is None else x.f64
+    ref = oracle.gsa_fwd(*(inp[n].f64 for n in "qkvg"), opt(inp["k0"]), opt(inp["v0"]),
+                         nthreads=oracle.max_threads())
+    for x, y in ((o, ref["o"]), (kf, ref["kf"]), (vf, ref["vf"])):
+        assert rel_err(to_np(x), y) <= TOL["bf16"]
 
 
 def test_pair_training_shape(gsa, torch):
