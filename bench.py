@@ -913,6 +913,18 @@ FORGET_WORKLOADS = (
 
 def run_only(args, torch, gsa, ev):
     import synth
+    if args.only == "rapid":
+        w = synth.WORKLOADS["gsa_bf16_train_T2048_rapid_forget"]
+        r = bench_gsa(torch, gsa, ev, w, "gsa_bf16_train_T2048_rapid_forget", args.steps, args.warmup, args.sets,
+                      warm_too=False)
+        return {k: r[k] for k in ("tokens_per_s", "ms_per_step", "ms_phases", "roofline")}
+    if args.only == "bwd_rapid":
+        return bench_bwd(torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_rapid_forget"], args.steps,
+                         args.warmup, name="gsa_bf16_train_T2048_rapid_forget_bwd", cpu=False, pair=False)
+    if args.only == "bwd_forget":
+        return {fname + "_bwd": bench_bwd(torch, gsa, ev, synth.WORKLOADS[fname], args.steps, args.warmup,
+                                          name=fname + "_bwd", cpu=False)
+                for fname, _ in FORGET_WORKLOADS[1:]}
     if args.only == "forget":
         out = {}
         for fname, _ in FORGET_WORKLOADS:
@@ -982,7 +994,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["gsa", "long", "gla", "gla_log_decay", "decode", "copy", "ablations", "serve",
-                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128", "bwd_saved", "bwd_long_saved", "forget"], default=None,
+                             "peaks", "gla_decode", "bwd", "bwd_serve", "bwd_long", "m128", "bwd_m128", "decode_m128", "bwd_saved", "bwd_long_saved", "forget", "bwd_forget",
+                             "rapid", "bwd_rapid"],
+                    default=None,
                     help="run one workload and print its record (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -1089,6 +1103,12 @@ def main():
             torch, gsa, ev, synth.WORKLOADS["gsa_bf16_long_T16384"], max(1, args.steps // 4), args.warmup,
             name="gsa_bf16_long_T16384_bwd", cpu=False)
         log("bench: long-context backward done")
+        for fname, what in FORGET_WORKLOADS[1:]:
+            r = bench_bwd(torch, gsa, ev, synth.WORKLOADS[fname], max(1, args.steps // 4), args.warmup,
+                          name=fname + "_bwd", cpu=False)
+            r["what"] = "the backward (and a training step) on " + what
+            comps[fname + "_bwd"] = r
+        log("bench: fast-forgetting backward done")
         comps["gsa_bf16_train_T2048_m128_bwd"] = bench_bwd(
             torch, gsa, ev, synth.WORKLOADS["gsa_bf16_train_T2048_m128"], max(1, args.steps // 4), args.warmup,
             name="gsa_bf16_train_T2048_m128_bwd", cpu=False)

@@ -210,36 +210,46 @@ struct StateTiles {
     }
   }
   // update2 in the sub-chunk form (chunk_factors): Za, Zb hold weights at the
-  // reference point of each token's 16-token sub-chunk, and sD [4][M] the
-  // decays between reference points.  Horner's rule from the chunk end: for
-  // sub-chunks T = 3 .. 0, W^T <- W^T Diag(sD[T]) + [A | B]_T^T [Za | Zb]_T
-  // (one 16-token contraction each).
+  // reference point of each token's 16-token sub-chunk T, and sD [4][M] the
+  // decays between reference points.  A lane's eight contraction values (8
+  // consecutive tokens) lie in one sub-chunk T and one slot c, so its Z
+  // operand is carried to the chunk start by the one factor sD[0][c] * ... *
+  // sD[T-1][c] and the update is update2's.
   __device__ __forceinline__ void update2_sub(const bf16_t* sA, int lda, const bf16_t* sB, int ldb,
                                               const bf16_t* sZa, const bf16_t* sZb, int ldz,
-                                              const float* sD, int sw, int lane) {
+                                              const float* sDec, const float* sD, int sw, int lane) {
     const int L = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < MT; ct++) {
+      const float d = sDec[16 * ct + L];
+#pragma unroll
+      for (int n = 0; n < NCW; n++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) st[n][ct][i] *= d;
+    }
     const bool khalf = 16 * (sw * NCW) < DK;
     const bf16_t* sZ = khalf ? sZa : sZb;
 #pragma unroll
-    for (int T = 3; T >= 0; T--) {
+    for (int r0 = 0; r0 < C; r0 += 32) {
+      bf16x8 zb[MT];
 #pragma unroll
       for (int ct = 0; ct < MT; ct++) {
-        const float d = sD[T * M + 16 * ct + L];
+        // tokens r0 + 8g .. r0 + 8g + 7: sub-chunk T = r0 / 16 + g / 2
+        const int c = 16 * ct + L;
+        float f = g >= 2 ? sD[(r0 / 16) * M + c] : 1.f;
+        if (r0 == 32) f *= sD[c] * sD[M + c];
+        f32x8 z = __builtin_convertvector(ld_col(sZ, ldz, 16 * ct, r0 + 8 * g, r0 + 8 * g + 4, lane), f32x8);
 #pragma unroll
-        for (int n = 0; n < NCW; n++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) st[n][ct][i] *= d;
+        for (int i = 0; i < 8; i++) z[i] *= f;
+        zb[ct] = __builtin_convertvector(z, bf16x8);
       }
-      bf16x4v zb[MT];
-#pragma unroll
-      for (int ct = 0; ct < MT; ct++) zb[ct] = ld_col4(sZ, ldz, 16 * ct, 16 * T + 4 * g, lane);
 #pragma unroll
       for (int n = 0; n < NCW; n++) {
         const int c0 = 16 * (sw * NCW + n);
-        const bf16x4v a = khalf ? ld_col4(sA, lda, c0, 16 * T + 4 * g, lane)
-                                : ld_col4(sB, ldb, c0 - DK, 16 * T + 4 * g, lane);
+        const bf16x8 a = khalf ? ld_col(sA, lda, c0, r0 + 8 * g, r0 + 8 * g + 4, lane)
+                               : ld_col(sB, ldb, c0 - DK, r0 + 8 * g, r0 + 8 * g + 4, lane);
 #pragma unroll
-        for (int ct = 0; ct < MT; ct++) st[n][ct] = mma16(a, zb[ct], st[n][ct]);
+        for (int ct = 0; ct < MT; ct++) st[n][ct] = mma(a, zb[ct], st[n][ct]);
       }
     }
   }

@@ -817,7 +817,9 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
   GSA_FWD_PASS1(JJ, true);                                                       \
   if constexpr (!STATS) fwd_pass2<DK, DV, M, JJ, G, true>(lane_i, smem, dzb, dze, dqrow, rv)
           switch (wv) {
-            case 0: GSA_FWD_SUB(0); break;
+            // rows of sub-chunk 0: its reference point is the chunk start, so
+            // the sub-chunk form is the plain one (pass 2 after M as usual)
+            case 0: GSA_FWD_PASS1(0, false); break;
             case 1: GSA_FWD_SUB(1); break;
             case 2: GSA_FWD_SUB(2); break;
             default: GSA_FWD_SUB(3); break;
@@ -831,7 +833,7 @@ bwd_bf16_fwd(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
         if (tid_i < M) sSeg[tid_i] *= sDec[tid_i];
         GradT<G>* dqrow = dqb + (size_t)t0 * (DK * G);
         if constexpr (!STATS) {
-          if (!sub) {
+          if (!sub || wv == 0) {
             switch (wv) {
               case 0: fwd_pass2<DK, DV, M, 0, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
               case 1: fwd_pass2<DK, DV, M, 1, G, false>(lane_i, smem, dzb, dze, dqrow, rv); break;
@@ -984,24 +986,25 @@ __device__ __forceinline__ void rev_pass(int lane, const unsigned char* smem, fl
         a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xb[p], a2[T]);
       }
   } else {
-    // X of this lane's row j in fp32 (slots 32p + 4g + 0..3 and 32p + 16 + 4g + 0..3)
-    f32x8 xr[NP];
-#pragma unroll
-    for (int p = 0; p < NP; p++) xr[p] = __builtin_convertvector(xb[p], f32x8);
+    // X of this lane's row j (slots 32p + 4g + 0..3 and 32p + 16 + 4g + 0..3)
+    // carried to read sub-chunk T: times sD[J] ... sD[T-1], formed per T from
+    // the bf16 row (no fp32 copy held across the sub-chunks)
 #pragma unroll
     for (int T = J; T < 4; T++) {
-      if (T > J) {
-#pragma unroll
-        for (int p = 0; p < NP; p++) {
-          const float4 lo = *reinterpret_cast<const float4*>(sD + (T - 1) * M + 32 * p + 4 * g);
-          const float4 hi = *reinterpret_cast<const float4*>(sD + (T - 1) * M + 32 * p + 16 + 4 * g);
-          xr[p][0] *= lo.x; xr[p][1] *= lo.y; xr[p][2] *= lo.z; xr[p][3] *= lo.w;
-          xr[p][4] *= hi.x; xr[p][5] *= hi.y; xr[p][6] *= hi.z; xr[p][7] *= hi.w;
-        }
-      }
 #pragma unroll
       for (int p = 0; p < NP; p++) {
-        const bf16x8 xt = __builtin_convertvector(xr[p], bf16x8);
+        bf16x8 xt = xb[p];
+        if (T > J) {
+          f32x8 xr = __builtin_convertvector(xb[p], f32x8);
+#pragma unroll
+          for (int r = J; r < T; r++) {
+            const float4 lo = *reinterpret_cast<const float4*>(sD + r * M + 32 * p + 4 * g);
+            const float4 hi = *reinterpret_cast<const float4*>(sD + r * M + 32 * p + 16 + 4 * g);
+            xr[0] *= lo.x; xr[1] *= lo.y; xr[2] *= lo.z; xr[3] *= lo.w;
+            xr[4] *= hi.x; xr[5] *= hi.y; xr[6] *= hi.z; xr[7] *= hi.w;
+          }
+          xt = __builtin_convertvector(xr, bf16x8);
+        }
         ad[T] = mma(ld_row2(sDZ, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xt, ad[T]);
         a2[T] = mma(ld_row2(sS, Lds::LDX, 16 * T, 32 * p + 4 * g, 32 * p + 16 + 4 * g, lane), xt, a2[T]);
       }
@@ -1392,7 +1395,7 @@ bwd_bf16_rev(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk, const
         if (!(regime & kNeedSub))
           W.update2(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sw, lane_i);
         else
-          W.update2_sub(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sD, sw, lane_i);
+          W.update2_sub(sQ, Lds::LDQ, sDo, Lds::LDV, sDZ, sS, Lds::LDX, sDec, sD, sw, lane_i);
       } else {
         __syncthreads();  // log alpha is in LDS
         rev_exact_state<DK, DV, M, G>(W, rv, smem, s_ws + (wb + t0) * M, dz_ws + (wb + t0) * M,

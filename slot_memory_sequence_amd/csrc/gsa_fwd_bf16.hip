@@ -703,7 +703,9 @@ gsa_bf16_out(const bf16_t* __restrict__ qq, const bf16_t* __restrict__ kk,
           }
         } else {  // some slot decays out of the chunk form's range: sub-chunk reference points
           switch (wv) {
-            case 0: pass_chunk<DK, DV, M, 0, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
+            // rows of sub-chunk 0: its reference point is the chunk start, so
+            // the sub-chunk form is the plain one
+            case 0: pass_chunk<DK, DV, M, 0, ACT, G, false>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
             case 1: pass_chunk<DK, DV, M, 1, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
             case 2: pass_chunk<DK, DV, M, 2, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
             default: pass_chunk<DK, DV, M, 3, ACT, G, true>(lane_i, sQ, sK, sV, sW, x, e, d, orow, lrow, rv); break;
