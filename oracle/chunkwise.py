@@ -8,6 +8,8 @@ Source: "Gated Slot Attention for Efficient Linear-Time Sequence Modeling".
   chunks; within a chunk the output is an inter-chunk term read from the state
   at the chunk start plus an intra-chunk causal term, and the state is carried
   to the next chunk.  Element-wise gating keeps this rearrangement exact.
+* App. A.1 (the secondary chunking it points to; App. B runs it on 16-token
+  sub-chunks): see gla_*_secondary below.
 * App. B: GSA is two such GLA passes.  The first pass takes the queries and
   keys with the slot write intensities I = 1 - A as its values; a softmax over
   the slots of its output gives the queries of the second pass, whose keys are
@@ -78,6 +80,104 @@ def gla_value_decay(q, k, w, la, P0=None, C=64):
         o[sl] = inter + intra
         P = P * np.exp(Gf[-1])[None, :] + kc.T @ (wc * np.exp(D[-1]))
     return o, P
+
+
+# --------------------------------------------------- secondary chunking
+# App. A.1 points to a secondary chunking of each chunk (sub-chunks of Cs
+# tokens; App. B runs it with Cs = 16).  A query row j of sub-chunk J meets a
+# key row r of an earlier sub-chunk R through a matrix product whose two
+# factors are decays to and from a reference point, the first token of J:
+# exp(sum of log alpha over (ref, j]) <= 1 on the query side and
+# exp(sum over (r, ref]) <= 1 on the key side, so nothing is divided; rows of
+# the same sub-chunk meet through their pairwise decays directly.  The state
+# read and the carry are the chunk form's.
+
+def _span_logsum(lc, a, b):
+    """Sum of lc over rows (a, b] (0 when b <= a), per column, as an explicit
+    sum (so that log alpha = -inf never meets another -inf)."""
+    if b <= a:
+        return np.zeros(lc.shape[1])
+    return lc[a + 1:b + 1].sum(axis=0)
+
+
+def _sub_chunks(L, Cs):
+    return [(s0, min(s0 + Cs, L)) for s0 in range(0, L, Cs)]
+
+
+def gla_value_decay_secondary(q, k, w, la, P0=None, C=64, Cs=16):
+    """gla_value_decay with the intra-chunk term by secondary chunking."""
+    T, dk = q.shape
+    m = w.shape[1]
+    P = np.zeros((dk, m)) if P0 is None else np.array(P0, dtype=np.float64)
+    o = np.zeros((T, m))
+    for n0 in range(0, T, C):
+        n1 = min(n0 + C, T)
+        qc, kc, wc, lc = q[n0:n1], k[n0:n1], w[n0:n1], la[n0:n1]
+        L = n1 - n0
+        A = qc @ kc.T
+        for (j0, j1) in _sub_chunks(L, Cs):
+            ref = j0
+            # earlier sub-chunks: one product through the reference point
+            if j0 > 0:
+                kside = np.stack([wc[r] * np.exp(_span_logsum(lc, r, ref)) for r in range(j0)])
+                inner = A[j0:j1, :j0] @ kside                       # [rows, m]
+                qside = np.stack([np.exp(_span_logsum(lc, ref, j)) for j in range(j0, j1)])
+                o[n0 + j0:n0 + j1] += qside * inner
+            # the same sub-chunk: pairwise decays
+            for j in range(j0, j1):
+                for r in range(j0, j + 1):
+                    o[n0 + j] += A[j, r] * wc[r] * np.exp(_span_logsum(lc, r, j))
+        # the state read and the carry (chunk form)
+        Gf = np.stack([_span_logsum(lc, -1, j) for j in range(L)])
+        o[n0:n1] += np.exp(Gf) * (qc @ P)
+        P = P * np.exp(Gf[-1])[None, :] + kc.T @ (wc * np.exp(np.stack([_span_logsum(lc, r, L - 1) for r in range(L)])))
+    return o, P
+
+
+def gla_key_decay_secondary(q, k, v, la, S0=None, C=64, Cs=16):
+    """gla_key_decay with the intra-chunk term by secondary chunking."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for n0 in range(0, T, C):
+        n1 = min(n0 + C, T)
+        qc, kc, vc, lc = q[n0:n1], k[n0:n1], v[n0:n1], la[n0:n1]
+        L = n1 - n0
+        Acc = np.zeros((L, L))
+        for (j0, j1) in _sub_chunks(L, Cs):
+            ref = j0
+            if j0 > 0:
+                qside = np.stack([qc[j] * np.exp(_span_logsum(lc, ref, j)) for j in range(j0, j1)])
+                kside = np.stack([kc[r] * np.exp(_span_logsum(lc, r, ref)) for r in range(j0)])
+                Acc[j0:j1, :j0] = qside @ kside.T
+            for j in range(j0, j1):
+                for r in range(j0, j + 1):
+                    Acc[j, r] = np.sum(qc[j] * kc[r] * np.exp(_span_logsum(lc, r, j)))
+        Gf = np.stack([_span_logsum(lc, -1, j) for j in range(L)])
+        o[n0:n1] = (qc * np.exp(Gf)) @ S + Acc @ vc
+        S = np.exp(Gf[-1])[:, None] * S + (kc * np.exp(np.stack([_span_logsum(lc, r, L - 1) for r in range(L)]))).T @ vc
+    return o, S
+
+
+def gsa_fwd_secondary(q, k, v, g, k0=None, v0=None, tau=8.0, C=64, Cs=16, nonlinearity="softmax"):
+    """GSA (two passes) with both intra-chunk terms by secondary chunking."""
+    B, H, T, dk = q.shape
+    m = g.shape[-1]
+    o = np.zeros(v.shape)
+    kf = np.zeros((B, H, m, dk))
+    vf = np.zeros((B, H, m, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            la = log_sigmoid(g[b, h]) / tau
+            w = -np.expm1(la)
+            P0 = None if k0 is None else np.asarray(k0[b, h], dtype=np.float64).T
+            ok, P = gla_value_decay_secondary(q[b, h], k[b, h], w, la, P0, C, Cs)
+            s = slot_read(ok, nonlinearity)
+            o[b, h], vf[b, h] = gla_key_decay_secondary(s, w, v[b, h], la,
+                                                        None if v0 is None else v0[b, h], C, Cs)
+            kf[b, h] = P.T
+    return o, kf, vf
 
 
 def softmax_slots(x):

@@ -63,6 +63,25 @@ def test_gla_recurrent_equals_chunkwise(oracle_mod, C):
         assert _rel(ref["sf"], sf) < 1e-12
 
 
+@pytest.mark.parametrize("C,Cs", [(64, 16), (16, 4), (32, 5)])
+def test_gsa_secondary_chunking_equals_recurrence(oracle_mod, C, Cs):
+    """App. A.1's secondary chunking (sub-chunks of Cs tokens met through the
+    first token of the query's sub-chunk, pairwise decays inside a sub-chunk)
+    reproduces the recurrence, with alpha = 0 / 1 tokens and two slots at
+    g ~ N(-30, 1), whose 16-token decay (~2^-86) is far below what a single
+    64-token factorisation could hold."""
+    q, k, v, g, k0, v0 = _rand_gsa(1, 2, 3 * C + 11, 8, 6, 5, init=True, seed=C + Cs)
+    g[..., :2] -= 30.0
+    g[0, 0, 3, :] = -np.inf
+    g[0, 1, 10:14, 2] = np.inf
+    g[0, 0, C + 1, 1] = -np.inf
+    ref = oracle_mod.gsa_fwd(q, k, v, g, k0, v0, tau=8.0)
+    o, kf, vf = chunkwise.gsa_fwd_secondary(q, k, v, g, k0, v0, tau=8.0, C=C, Cs=Cs)
+    assert _rel(ref["o"], o) < 1e-12
+    assert _rel(ref["kf"], kf) < 1e-12
+    assert _rel(ref["vf"], vf) < 1e-12
+
+
 def test_gsa_chunkwise_extreme_gates(oracle_mod):
     """alpha = 0 and alpha = 1 tokens mixed in (g = -inf / +inf, and +-30)."""
     q, k, v, g, k0, v0 = _rand_gsa(1, 1, 70, 8, 8, 6, g_scale=3.0, init=True, seed=5)
