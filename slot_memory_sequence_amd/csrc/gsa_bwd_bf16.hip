@@ -42,8 +42,12 @@
 //   4. bwd_bf16_rev: per segment, chunks in reverse from its end adjoint:
 //      the adjoint update (state waves), dk, dv, di and dg (pass waves).
 // A chunk where some slot's decay product falls below 2^-90 (the factorised
-// forms divide by E) runs as an exact token walk of the state waves over the
-// fp32 state / adjoint they hold in their accumulators.  128 slots run as two
+// forms divide by E) runs with 16-token sub-chunk reference points
+// (chunk_factors; App. A.1's secondary chunking): the intra-chunk terms pass
+// between sub-chunks through the decays between their reference points, by
+// Horner's rule or by scaling one operand.  Only a chunk in which a 16-token
+// sub-chunk decays below 2^-90 runs as an exact token walk of the state waves
+// over the fp32 state / adjoint they hold in their accumulators.  128 slots run as two
 // groups of 64 (G = 2): a statistics pass of step 2 gives each group's
 // softmax statistics, merged into the log-sum-exp and delta that both groups'
 // sweeps then take, and the groups' fp32 parts of dq, dk, dv are added last.
