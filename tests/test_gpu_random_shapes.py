@@ -1,6 +1,7 @@
 """Seeded random cases over the compiled bf16 set, against the float64 oracle
 (bar 2e-2 per tensor): the forward (every read, any split, optional states,
-gate shifts), the backward and the training pair.  Each case prints its
+gate shifts, a random set of fast-forgetting slots that sends chunks to the
+sub-chunk form), the backward and the training pair.  Each case prints its
 parameters before it runs."""
 import numpy as np
 import pytest
@@ -21,9 +22,16 @@ def _draw(seed, bwd):
     nl = str(r.choice([x for x in READS if not (bwd and x == "relu")]))
     if m == 128 and bwd and nl == "relu":
         nl = "softmax"
-    return dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 4)), T=int(r.integers(1, 700)), d=d, m=m, nl=nl,
-                cps=int(r.choice([0, 0, 1, 2, 3, 5])), init=bool(r.integers(0, 2)), final=bool(r.integers(0, 2)),
-                shift=float(r.choice([0.0, 0.0, 2.0, -3.0])))
+    c = dict(B=int(r.integers(1, 3)), H=int(r.integers(1, 4)), T=int(r.integers(1, 700)), d=d, m=m, nl=nl,
+             cps=int(r.choice([0, 0, 1, 2, 3, 5])), init=bool(r.integers(0, 2)), final=bool(r.integers(0, 2)),
+             shift=float(r.choice([0.0, 0.0, 2.0, -3.0])))
+    # drawn last, so that the draws above are those of the earlier cases:
+    # n slots (a random subset) at logits N(mean, 1); at tau = 8, mean -10
+    # puts 64-token decays near 2^-115 (sub-chunk form), -25 near 2^-280 with
+    # 16-token ones near 2^-70
+    if r.integers(0, 2):
+        c["fast"] = (int(r.choice([4, 8, 16])), float(r.choice([-10.0, -14.0, -20.0, -25.0])))
+    return c
 
 
 @pytest.fixture(scope="module")
@@ -41,8 +49,16 @@ def gsa(torch):
 
 
 def _inputs(c, seed):
-    return synth.gsa_inputs(c["B"], c["H"], c["T"], c["d"], c["d"], c["m"], dtype="bf16", seed=seed,
-                            g_shift=c["shift"], init_std=0.1 if c["init"] else None)
+    inp = synth.gsa_inputs(c["B"], c["H"], c["T"], c["d"], c["d"], c["m"], dtype="bf16", seed=seed,
+                           g_shift=c["shift"], init_std=0.1 if c["init"] else None)
+    if "fast" in c:
+        n, mean = c["fast"]
+        r = np.random.default_rng(2000 + seed)
+        idx = r.choice(c["m"], size=n, replace=False)
+        x = inp["g"].f64.copy()
+        x[..., idx] = mean + r.standard_normal(x[..., idx].shape)
+        inp["g"] = synth.stored(x, "bf16")
+    return inp
 
 
 @pytest.mark.parametrize("seed", range(16))
@@ -62,7 +78,7 @@ def test_random_forward(gsa, torch, seed):
     assert max(errs) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_backward_and_pair(gsa, torch, seed):
     c = _draw(seed, bwd=True)
     print("random backward case", seed, c, flush=True)
