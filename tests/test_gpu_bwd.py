@@ -161,18 +161,23 @@ def test_bwd_matches_chunkwise_forward_outputs(gsa, torch):
     assert abs(ana - num) <= 5e-3 * abs(num)
 
 
-def test_bwd_training_shape_sampled(gsa, torch):
+@pytest.mark.parametrize("name", ["gsa_bf16_train_T2048", "gsa_bf16_train_T2048_rapid_forget",
+                                  "gsa_bf16_train_T2048_extreme_forget"])
+def test_bwd_training_shape_sampled(gsa, torch, name):
     """The training-shape workload (B8 H4 T2048 d128 m64, bf16) in the launch
-    configuration the benchmark times; five units against the oracle."""
-    w = synth.WORKLOADS["gsa_bf16_train_T2048"]
+    configuration the benchmark times, with its fast-forgetting variants (8
+    slots at logits N(-10, 1): sub-chunk form; N(-40, 1): exact walks); five
+    units against the oracle."""
+    w = synth.WORKLOADS[name]
     inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
                            seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
-                           init_std=w["init_std"])
+                           init_std=w["init_std"], fast_slots=w.get("fast_slots", 0),
+                           fast_shift=w.get("fast_shift", 0.0))
     gi = synth.gsa_grad_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
                                seed=1)
     got = _run(gsa, torch, inp, gi, w["tau"])
     units = [0, 7, 13, 22, w["B"] * w["H"] - 1]
-    _compare(got, _ref(inp, gi, w["tau"], units), "bf16", "B8 H4 T2048 sampled", units)
+    _compare(got, _ref(inp, gi, w["tau"], units), "bf16", name + " sampled", units)
 
 
 def test_bwd_long_context_sampled(gsa, torch):

@@ -32,12 +32,15 @@ def _units(x, idx):
     return a.reshape(-1, *a.shape[2:])[idx][:, None]
 
 
-@pytest.mark.parametrize("name", ["gsa_bf16_train_T2048", "gsa_bf16_long_T16384"])
+@pytest.mark.parametrize("name", ["gsa_bf16_train_T2048", "gsa_bf16_long_T16384",
+                                  "gsa_bf16_train_T2048_fast_forget", "gsa_bf16_train_T2048_rapid_forget",
+                                  "gsa_bf16_train_T2048_extreme_forget"])
 def test_gsa_full_workload(gsa, torch, name):
     w = synth.WORKLOADS[name]
     inp = synth.gsa_inputs(w["B"], w["H"], w["T"], w["dk"], w["dv"], w["m"], dtype=w["dtype"],
                            seed=0, qkv_scale=w["qkv_scale"], g_shift=w["g_shift"],
-                           init_std=w["init_std"])
+                           init_std=w["init_std"], fast_slots=w.get("fast_slots", 0),
+                           fast_shift=w.get("fast_shift", 0.0))
     q, k, v, g = (to_dev(inp[n], torch) for n in "qkvg")
     o, kf, vf = gsa.gsa_fwd(q, k, v, g, to_dev(inp["k0"], torch), to_dev(inp["v0"], torch),
                             tau=w["tau"], final_state=True)
