@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import RawEvents, TOL, rel_err, to_dev, to_np
+from tests.gpu_helpers import TOL, RawEvents, gates_fast_slots, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -68,9 +68,11 @@ def _run(gsa, torch, inp, cps=0, in_place=False):
     return o, kf, vf
 
 
-def _check(gsa, torch, lengths, H, d, m, init, cps=0, seed=0, in_place=False):
+def _check(gsa, torch, lengths, H, d, m, init, cps=0, seed=0, in_place=False, edit=None):
     inp = synth.varlen_inputs(lengths, H, d, d, m, dtype="bf16", seed=seed,
                               init_std=0.1 if init else None)
+    if edit is not None:
+        edit(inp)
     o, kf, vf = _run(gsa, torch, inp, cps, in_place)
     ro, rk, rv = _oracle_each(inp)
     errs = [rel_err(to_np(o), ro) if ro.size else 0.0, rel_err(to_np(kf), rk), rel_err(to_np(vf), rv)]
@@ -91,6 +93,20 @@ def test_varlen_mixed_lengths(gsa, torch, cps):
     sequences in one call, with initial states; every segment split (the
     scan, maps folded in the output kernel, one segment)."""
     _check(gsa, torch, MIX, 2, 128, 64, init=True, cps=cps, seed=cps + 1)
+
+
+@pytest.mark.parametrize("cps", [0, 1])
+def test_varlen_subchunk_form(gsa, torch, cps):
+    """The packed batch with 8 slots at logits N(-10, 1) on every token
+    (chunks in the 16-token sub-chunk form) and one slot at -inf for three
+    tokens of the 1000-token sequence (an exact chunk)."""
+    def edit(inp):
+        gates_fast_slots(8, -10.0)(inp)
+        x = inp["g"].f64.copy()
+        t = int(inp["cu_seqlens"][6]) + 70
+        x[:, t:t + 3, 20] = -np.inf
+        inp["g"] = synth.stored(x, "bf16")
+    _check(gsa, torch, MIX, 2, 128, 64, init=True, cps=cps, seed=cps + 11, edit=edit)
 
 
 @pytest.mark.parametrize("d,m", [(128, 64), (64, 32), (128, 32), (64, 64)])
