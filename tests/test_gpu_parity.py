@@ -81,6 +81,16 @@ def test_gsa_shapes(gsa, torch, T, dtype, d, m):
     _check_gsa(gsa, torch, 2, 2, T, d, m, dtype, init=(T % 2 == 1), seed=T)
 
 
+@pytest.mark.parametrize("tau", [1.0, 2.0, 32.0, 256.0])
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 64, 32)])
+def test_gsa_tau(gsa, torch, tau, dtype, d, m):
+    """The damping exponent 1/tau of the forget gate (Sec. 3.3) away from 8:
+    tau = 1 and 2 decay fast (sub-chunk reference points and exact chunks
+    among the logits N(0, 1)), tau = 32 and 256 keep 1 - alpha small, where
+    the telescoped factors difference nearly equal terms."""
+    _check_gsa(gsa, torch, 2, 2, 64 * 4 + 21, d, m, dtype, init=True, tau=tau, seed=11, cps=2)
+
+
 @pytest.mark.parametrize("cps", [1, 2, 3, 100])
 def test_gsa_segmentations(gsa, torch, cps):
     """The chunk-state scan must give the same result for any segment split."""
@@ -179,6 +189,13 @@ def _check_gla(gsa, torch, B, H, T, d, dtype, init=False, tau=16.0, cps=0, seed=
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64)])
 def test_gla_shapes(gsa, torch, T, dtype, d):
     _check_gla(gsa, torch, 2, 2, T, d, dtype, init=(T % 2 == 0), seed=T)
+
+
+@pytest.mark.parametrize("tau", [1.0, 4.0, 64.0])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_gla_tau(gsa, torch, tau, dtype, d):
+    """GLA's gate damping 1/tau away from the workload's 16."""
+    _check_gla(gsa, torch, 2, 2, 64 * 4 + 21, d, dtype, init=True, tau=tau, cps=2, seed=12)
 
 
 @pytest.mark.parametrize("cps", [1, 3])
