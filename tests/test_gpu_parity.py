@@ -252,6 +252,20 @@ def test_decode_step(gsa, torch, dtype, d, m):
     assert rel_err(to_np(ks), rk) <= 1e-5 and rel_err(to_np(vs), rv) <= 1e-5
 
 
+@pytest.mark.parametrize("tau", [1.0, 64.0])
+@pytest.mark.parametrize("dtype,d,m", [("bf16", 128, 64), ("f32", 64, 32)])
+def test_decode_step_tau(gsa, torch, tau, dtype, d, m):
+    """The decode step's gate damping 1/tau away from 8."""
+    inp = synth.decode_inputs(3, 5, d, d, m, dtype=dtype, seed=m + 7)
+    ks, vs = to_dev(inp["kstate"], torch), to_dev(inp["vstate"], torch)
+    o = gsa.gsa_decode_step(*(to_dev(inp[n], torch) for n in "qkvg"), ks, vs, tau=tau)
+    torch.cuda.synchronize()
+    ro, rk, rv = oracle.gsa_decode_step(inp["q"].f64, inp["k"].f64, inp["v"].f64, inp["g"].f64,
+                                        inp["kstate"].f64, inp["vstate"].f64, tau=tau)
+    assert rel_err(to_np(o), ro) <= TOL[dtype]
+    assert rel_err(to_np(ks), rk) <= 1e-5 and rel_err(to_np(vs), rv) <= 1e-5
+
+
 def test_decode_chain_equals_fwd(gsa, torch):
     """T chained decode steps reproduce the chunkwise forward (float32)."""
     inp = synth.gsa_inputs(2, 2, 70, 64, 64, 32, dtype="f32", seed=21, init_std=0.1)
