@@ -120,6 +120,8 @@ size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, int d
  *   chunks_per_segment: how many 64-token chunks one workgroup carries the
  *            state across (0 = default); the workspace must be sized for it.
  * k_final may equal k0 and v_final may equal v0 (in-place state advance).
+ * B * H <= 65535 (32767 at m = 128, whose two slot groups each count as a
+ * unit), else GSA_ERR_UNSUPPORTED.
  */
 int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* k0,
             const float* v0, void* o, float* k_final, float* v_final, int B, int H, int T, int dk,
@@ -325,8 +327,9 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
  *              dk, dv, m) bytes (else GSA_ERR_WORKSPACE), caller-owned; its
  *              contents on entry do not matter.
  * No output may overlap an input, the workspace or another output
- * (GSA_ERR_ALIAS).  B * H <= 65535 and T <= 65535 * 64 (else
- * GSA_ERR_UNSUPPORTED).  Compiled for (dk = dv, m) in {(128, 64),
+ * (GSA_ERR_ALIAS).  B * H <= 65535 (32767 at m = 128, whose two slot groups
+ * each count as a unit) and T <= 65535 * 64 (else GSA_ERR_UNSUPPORTED).
+ * Compiled for (dk = dv, m) in {(128, 64),
  * (128, 32), (64, 64), (64, 32)}, float32 and bf16 (gsa_bwd_supported), and
  * in bf16 for d in {64, 128} with m = 128 on dense batches and every read but
  * ReLU (GSA_ERR_UNSUPPORTED for the packed batch or the ReLU read there): the

@@ -526,7 +526,8 @@ static int bwd_run(const void* q, const void* k, const void* v, const void* g, c
   if (units == 0) return GSA_OK;
   // one grid row per unit of a launch sequence (a packed batch launches groups)
   const long long launch_units = cu ? (long long)std::min(B, gsa::kMaxVarSeqs) * H : units;
-  if (launch_units > 65535) return GSA_ERR_UNSUPPORTED;
+  // 128 slots run as two groups of 64, each group a unit of the launches
+  if (launch_units * gsa::slot_groups(dtype, m) > 65535) return GSA_ERR_UNSUPPORTED;
   if (((long long)T + kChunk - 1) / kChunk > 65535) return GSA_ERR_UNSUPPORTED;  // chunks: grid y
   if (ntok > 0 && (!q || !k || !v || !g || !d_o || !d_q || !d_k || !d_v || !d_g))
     return GSA_ERR_NULL;

@@ -113,6 +113,11 @@ def test_gsa_fwd_validation(gsa):
     assert _gsa_call(gsa, T=4096, cps=1) == 5
     assert _gsa_call(gsa, T=4096, cps=1, ws=FAKE + 0x10000000, wsb=16) == 5
     assert _gsa_call(gsa, B=70000) == 4
+    # 128 slots run as two groups of 64, each group a unit of the grid: at most
+    # 32767 (batch, head) pairs (the next step at the limit is the workspace check)
+    far = dict(k=FAKE + (1 << 30), v=FAKE + (2 << 30), g=FAKE + (3 << 30), o=FAKE + (4 << 30))
+    assert _gsa_call(gsa, B=32768, m=128, **far) == 4
+    assert _gsa_call(gsa, B=32767, m=128, **far) == 5
 
 
 def test_gla_and_decode_validation(gsa):
@@ -306,6 +311,9 @@ def test_bwd_validation(gsa):
     assert call(d_k=96, d_v=96) == 4
     assert call(m=128, dtype=0) == 4                    # 128 slots: bf16 only
     assert call(B=65536) == 4
+    far = {n: FAKE + (i << 30) for i, n in enumerate(("k", "v", "g", "do", "dq", "dk", "dv", "dg"), 1)}
+    assert call(B=32768, m=128, ws=FAKE + (9 << 30), **far) == 4   # two slot groups per (batch, head)
+    assert call(B=32767, m=128, ws=FAKE + (9 << 30), **far) == 5   # within the grid: the workspace check
     assert call(T=65535 * 64 + 1) == 4                  # more chunks than the grid takes
     assert call(B=0) == 0                               # nothing to do
     assert call(q=None) == 1 and call(do=None) == 1 and call(dg=None) == 1
