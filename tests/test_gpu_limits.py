@@ -1,5 +1,5 @@
 """GPU parity at the size limits: the largest unit count the launch grid takes
-(65535 (batch, head) units), tensors of more than 2^31 elements (64-bit
+(65535 (batch, head) units, 32767 with 128 slots), tensors of more than 2^31 elements (64-bit
 offsets everywhere), and a decode batch of 131072 units; the same limits for
 the backward.  The inputs are drawn
 on the device with a seeded torch generator; sampled units are copied back and
@@ -156,6 +156,16 @@ def _bwd_sampled(gsa, torch, B, H, T, d, m, units, seed):
 def test_bwd_max_units(gsa, torch):
     B = 65535
     assert _bwd_sampled(gsa, torch, B, 1, 70, 64, 32, [0, 1, 32768, B - 1], seed=5) <= TOL["bf16"]
+
+
+def test_m128_max_units(gsa, torch):
+    """128 slots run as two groups of 64, each group a unit of the launches:
+    32767 (batch, head) pairs are 65534 group units, the most the grid takes
+    (one pair more is rejected on the host); forward and backward."""
+    B = 32767
+    units = [0, 1, 16384, B - 1]
+    assert _gsa_sampled(gsa, torch, B, 1, 70, 64, 128, units, seed=7) <= TOL["bf16"]
+    assert _bwd_sampled(gsa, torch, B, 1, 70, 64, 128, units, seed=8) <= TOL["bf16"]
 
 
 def test_bwd_over_2g_elements(gsa, torch):
