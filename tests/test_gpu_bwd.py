@@ -103,6 +103,16 @@ def test_bwd_optional_states(gsa, torch, init, final):
     _check(gsa, torch, 2, 2, 130, 128, 64, "bf16", init=init, final=final, seed=7)
 
 
+@pytest.mark.parametrize("which", ["k0", "v0"])
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 128, 128)])
+def test_bwd_one_initial_state(gsa, torch, which, dtype, d, m):
+    """Only one of the two initial slot states given: the other is zero and its
+    gradient is still written."""
+    def drop(inp):
+        inp["v0" if which == "k0" else "k0"] = None
+    _check(gsa, torch, 2, 2, 64 * 3 + 11, d, m, dtype, True, True, seed=14, edit=drop)
+
+
 @pytest.mark.parametrize("tau", [1.0, 16.0])
 def test_bwd_tau(gsa, torch, tau):
     _check(gsa, torch, 1, 2, 100, 64, 32, "f32", init=True, final=True, tau=tau, seed=9)

@@ -81,6 +81,16 @@ def test_gsa_shapes(gsa, torch, T, dtype, d, m):
     _check_gsa(gsa, torch, 2, 2, T, d, m, dtype, init=(T % 2 == 1), seed=T)
 
 
+@pytest.mark.parametrize("which", ["k0", "v0"])
+@pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 128, 128)])
+def test_gsa_one_initial_state(gsa, torch, which, dtype, d, m):
+    """Only one of the two initial slot states given (the other zero), across
+    several segments: each start state is loaded on its own."""
+    def drop(inp):
+        inp["v0" if which == "k0" else "k0"] = None
+    _check_gsa(gsa, torch, 2, 2, 64 * 5 + 7, d, m, dtype, init=True, cps=2, seed=13, mutate=drop)
+
+
 @pytest.mark.parametrize("tau", [1.0, 2.0, 32.0, 256.0])
 @pytest.mark.parametrize("dtype,d,m", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 64, 32)])
 def test_gsa_tau(gsa, torch, tau, dtype, d, m):
