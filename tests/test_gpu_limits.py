@@ -168,6 +168,30 @@ def test_m128_max_units(gsa, torch):
     assert _bwd_sampled(gsa, torch, B, 1, 70, 64, 128, units, seed=8) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("m,B", [(64, 65535), (128, 32767)])
+def test_pair_max_units(gsa, torch, m, B):
+    """The training pair at the largest unit count: its kept states give
+    gsa_bwd's gradients bit for bit, and its forward matches gsa_fwd's."""
+    T, d = 70, 64
+    gen = torch.Generator(device="cuda").manual_seed(9 + m)
+    sc = 1.0 / np.sqrt(d)
+    q = _randn(torch, gen, (B, 1, T, d), sc)
+    k = _randn(torch, gen, (B, 1, T, d), sc)
+    v = _randn(torch, gen, (B, 1, T, d), sc)
+    g = _randn(torch, gen, (B, 1, T, m), 1.0)
+    do = _randn(torch, gen, (B, 1, T, d), 1.0)
+    o, _, _, states = gsa.gsa_fwd_train(q, k, v, g)
+    o_ref, _, _ = gsa.gsa_fwd(q, k, v, g)
+    a = gsa.gsa_bwd_train(q, k, v, g, do, states)
+    b = gsa.gsa_bwd(q, k, v, g, do)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv", "dg"), a[:4], b[:4]):
+        assert torch.equal(x, y), name
+    assert rel_err(to_np(o), to_np(o_ref)) <= TOL["bf16"]
+    del q, k, v, g, do, o, o_ref, states, a, b
+    torch.cuda.empty_cache()
+
+
 def test_bwd_over_2g_elements(gsa, torch):
     """q, k, v, dO and the gradients of 2^31 + elements each (about 90 GB of
     device memory with the workspace)."""
