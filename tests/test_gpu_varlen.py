@@ -219,3 +219,51 @@ def test_varlen_more_than_256_sequences(gsa, torch, cps):
     print("600 sequences cps=%d: o %.2e kf %.2e vf %.2e" % (cps, *errs))
     assert max(errs) <= TOL["bf16"]
     assert np.array_equal(to_np(kf)[256:512], inp["k0"].f64[256:512])
+
+
+def test_varlen_at_the_unit_limit(gsa, torch):
+    """257 sequences x 255 heads: a first group of 256 sequences fills 65280
+    grid rows (at most 65535 are taken), the last sequence runs alone; the
+    forward and the backward of the packed batch, checked on sampled
+    sequences (every head); one head more is rejected on the host."""
+    r = np.random.default_rng(41)
+    lengths = [int(x) for x in r.integers(0, 41, size=257)]
+    lengths[0], lengths[255], lengths[256] = 40, 1, 70
+    H, d, m = 255, 64, 32
+    inp = synth.varlen_inputs(lengths, H, d, d, m, dtype="bf16", seed=42, init_std=0.1)
+    o, kf, vf = _run(gsa, torch, inp)
+    cu = inp["cu_seqlens"]
+    worst = 0.0
+    for s_ in (0, 128, 255, 256):
+        k0, v0 = inp["k0"].f64[s_:s_ + 1], inp["v0"].f64[s_:s_ + 1]
+        ref = oracle.gsa_fwd(*(_seq(inp[x].f64, cu, s_) for x in "qkvg"), k0, v0, tau=8.0,
+                             nthreads=oracle.max_threads())
+        if lengths[s_]:
+            worst = max(worst, rel_err(_seq(to_np(o), cu, s_), ref["o"]))
+        worst = max(worst, rel_err(to_np(kf)[s_:s_ + 1], ref["kf"]), rel_err(to_np(vf)[s_:s_ + 1], ref["vf"]))
+    print("varlen 257 sequences x H255: forward worst rel err %.2e" % worst)
+    assert worst <= TOL["bf16"]
+    # the backward of the same packed batch
+    gi = synth.varlen_grad_inputs(lengths, H, d, d, m, dtype="bf16", seed=43)
+    dev = {x: to_dev(inp[x], torch) for x in ("q", "k", "v", "g", "k0", "v0")}
+    grads = gsa.gsa_bwd_varlen(dev["q"], dev["k"], dev["v"], dev["g"], to_dev(gi["do"], torch), cu,
+                               dev["k0"], dev["v0"])
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s_ in (0, 128, 255, 256):
+        if not lengths[s_]:
+            continue
+        k0, v0 = inp["k0"].f64[s_:s_ + 1], inp["v0"].f64[s_:s_ + 1]
+        ref = oracle.gsa_bwd(*(_seq(inp[x].f64, cu, s_) for x in "qkvg"), _seq(gi["do"].f64, cu, s_),
+                             k0, v0, tau=8.0, nthreads=oracle.max_threads())
+        for name, x in zip(("dq", "dk", "dv", "dg"), grads[:4]):
+            worst = max(worst, rel_err(_seq(to_np(x), cu, s_), ref[name]))
+    print("varlen 257 sequences x H255: backward worst rel err %.2e" % worst)
+    assert worst <= TOL["bf16"]
+    # one head more and the first group would need 65536 grid rows: rejected on
+    # the host before anything is launched
+    n = 257
+    x = torch.zeros((H + 1, n, d), dtype=torch.bfloat16, device="cuda")
+    gx = torch.zeros((H + 1, n, m), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gsa.GsaError):
+        gsa.gsa_fwd_varlen(x, x, x, gx, np.arange(n + 1, dtype=np.int32))
